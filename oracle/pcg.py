@@ -1,0 +1,107 @@
+"""Preconditioned conjugate gradients in fp64.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+The pages solve A x = b with preconditioned CG and M ~ A^{-1} ("Hierarchical
+Transformer Preconditioning for Interactive Physics Simulation", project page,
+Introduction and Background, eq. (1)), stopping when ||r_k||_2 / ||r_0||_2 falls
+to the tolerance (Supplementary section 1, "Convergence criterion"; main text
+section 7.1).  The pages print no listing of the loop, so this is the textbook
+preconditioned CG (Saad, "Iterative Methods for Sparse Linear Systems", the
+preconditioned CG algorithm in section 9.2) with x_0 = 0, so r_0 = b:
+
+    z = M r,  p = z,  rz = r.z
+    repeat:  q = A p;  alpha = rz / p.q;  x += alpha p;  r -= alpha q
+             stop if ||r|| / ||b|| <= tol
+             z = M r;  beta = (r.z) / rz;  p = z + beta p
+
+Readings taken where the pages are silent: the iteration count is the number
+of products q = A p done when the test first passes; the test uses the
+recursively updated r; a non-positive or non-finite p.q or r.z stops the loop
+as a breakdown.  Everything here is fp64 (the pages keep only scalars in fp64;
+the GPU path's vectors are fp32, which is what the iteration-count tolerance
+absorbs).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from .hmatrix import apply_M
+from .sparse import spmv, true_relres
+
+
+@dataclass
+class PCGResult:
+    x: np.ndarray
+    iterations: int
+    status: str                  # "converged" | "not_converged" | "breakdown"
+    relres: float                # recursive ||r|| / ||b|| at exit
+    true_relres: float           # ||b - A x|| / ||b|| from the returned x
+    history: list = field(default_factory=list)   # ||r_k|| / ||b|| for k = 1 ..
+
+
+def pcg(row_ptr, col, val, b, precond, tol: float, maxit: int) -> PCGResult:
+    """Solve A x = b.  precond is either a callable r -> M r or a tuple (U, W, g)
+    of preconditioner factors applied with the structured apply."""
+    if callable(precond):
+        apply = precond
+    else:
+        U, W, g = precond
+
+        def apply(v):
+            return apply_M(U, W, g, v)
+
+    b = np.asarray(b, dtype=np.float64)
+    x = np.zeros_like(b)
+    r = b.copy()
+    bnorm = float(np.linalg.norm(b))
+    if bnorm == 0.0:
+        return PCGResult(x, 0, "converged", 0.0, 0.0, [])
+    z = np.asarray(apply(r), dtype=np.float64)
+    p = z.copy()
+    rz = float(r @ z)
+    history = []
+    if not (np.isfinite(rz) and rz > 0.0):
+        return PCGResult(x, 0, "breakdown", 1.0, 1.0, history)
+    for it in range(1, maxit + 1):
+        q = spmv(row_ptr, col, val, p)
+        pq = float(p @ q)
+        if not (np.isfinite(pq) and pq > 0.0):
+            rel = float(np.linalg.norm(r)) / bnorm
+            return PCGResult(x, it, "breakdown", rel,
+                             true_relres(row_ptr, col, val, b, x), history)
+        alpha = rz / pq
+        x += alpha * p
+        r -= alpha * q
+        rel = float(np.linalg.norm(r)) / bnorm
+        history.append(rel)
+        if rel <= tol:
+            return PCGResult(x, it, "converged", rel,
+                             true_relres(row_ptr, col, val, b, x), history)
+        z = np.asarray(apply(r), dtype=np.float64)
+        rz_new = float(r @ z)
+        if not (np.isfinite(rz_new) and rz_new > 0.0):
+            return PCGResult(x, it, "breakdown", rel,
+                             true_relres(row_ptr, col, val, b, x), history)
+        beta = rz_new / rz
+        p = z + beta * p
+        rz = rz_new
+    rel = float(np.linalg.norm(r)) / bnorm
+    return PCGResult(x, maxit, "not_converged", rel,
+                     true_relres(row_ptr, col, val, b, x), history)
+
+
+def pcg_batch(batch, tol: float | None = None, maxit: int | None = None,
+              systems=None) -> list:
+    """Independent PCG per system of a workloads.Batch (or the listed systems)."""
+    tol = batch.tol if tol is None else tol
+    maxit = batch.maxit if maxit is None else maxit
+    idx = range(batch.batch) if systems is None else systems
+    out = []
+    for s in idx:
+        sy = batch.system(s)
+        out.append(pcg(sy.row_ptr, sy.col, sy.val, sy.b, (sy.U, sy.W, sy.g), tol, maxit))
+    return out

@@ -1,0 +1,132 @@
+"""Pins for the oracle's PCG loop.
+
+scipy.sparse.linalg.cg is an independent textbook (P)CG loop: with M = I and
+with M given as a LinearOperator it must take the same number of steps and
+return the same x.  Exact preconditioners finish in one step; PCG is invariant
+under M -> cM (the scale invariance the pages build their loss on, project
+page, Training, Proposition 1); CG ends within n steps in exact arithmetic.
+"""
+
+import numpy as np
+import pytest
+import scipy.sparse
+import scipy.sparse.linalg as spla
+
+import oracle
+from workloads import make_config
+from workloads.generate import random_system
+
+
+def _scipy_cg(A, b, tol, maxit, M=None):
+    count = [0]
+
+    def cb(_x):
+        count[0] += 1
+
+    x, info = spla.cg(A, b, rtol=tol, atol=0.0, maxiter=maxit, M=M, callback=cb)
+    return x, count[0], info
+
+
+@pytest.mark.parametrize("name", ["N1k", "tet4k"])
+def test_identity_preconditioner_is_textbook_cg(name):
+    b = make_config(name)
+    sy = b.system(0)
+    A = scipy.sparse.csr_matrix((sy.val.astype(np.float64), sy.col, sy.row_ptr), shape=(b.n, b.n))
+    rhs = sy.b.astype(np.float64)
+    res = oracle.pcg(sy.row_ptr, sy.col, sy.val, rhs, lambda v: v.copy(), 1e-6, 5000)
+    xs, its, info = _scipy_cg(A, rhs, 1e-6, 5000)
+    assert info == 0 and res.status == "converged"
+    assert res.iterations == its
+    np.testing.assert_allclose(res.x, xs, rtol=1e-9, atol=1e-9 * np.abs(xs).max())
+
+
+def test_hmatrix_preconditioner_matches_scipy_pcg():
+    b = make_config("N1k")
+    sy = b.system(0)
+    A = scipy.sparse.csr_matrix((sy.val.astype(np.float64), sy.col, sy.row_ptr), shape=(b.n, b.n))
+    Mop = spla.LinearOperator((b.n, b.n), matvec=lambda v: oracle.apply_M(sy.U, sy.W, sy.g, v))
+    rhs = sy.b.astype(np.float64)
+    res = oracle.pcg(sy.row_ptr, sy.col, sy.val, rhs, (sy.U, sy.W, sy.g), 1e-6, 1000)
+    xs, its, info = _scipy_cg(A, rhs, 1e-6, 1000, M=Mop)
+    assert info == 0 and res.status == "converged"
+    assert res.iterations == its
+    np.testing.assert_allclose(res.x, xs, rtol=1e-9, atol=1e-9 * np.abs(xs).max())
+    assert res.true_relres <= 1.01e-6
+
+
+def test_exact_inverse_takes_one_step():
+    b = random_system(256, seed=4, leaf=32, rank=4)
+    sy = b.system(0)
+    Ainv = np.linalg.inv(oracle.dense_A(sy.row_ptr, sy.col, sy.val))
+    res = oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b, lambda v: Ainv @ v, 1e-10, 50)
+    assert res.status == "converged" and res.iterations == 1
+    assert res.true_relres < 1e-11
+
+
+def test_format_exact_block_diagonal_inverse():
+    # keep only the in-leaf couplings of A; U_k = chol(A_kk)^{-T} gives M = A^{-1}
+    b = random_system(512, seed=8, leaf=64, rank=4)
+    sy = b.system(0)
+    L = 64
+    A = oracle.dense_A(sy.row_ptr, sy.col, sy.val)
+    K = sy.n // L
+    Ab = np.zeros_like(A)
+    U = np.zeros((K, L, L))
+    for k in range(K):
+        blk = A[k * L:(k + 1) * L, k * L:(k + 1) * L]
+        Ab[k * L:(k + 1) * L, k * L:(k + 1) * L] = blk
+        U[k] = np.linalg.inv(np.linalg.cholesky(blk)).T
+    S = scipy.sparse.csr_matrix(Ab)
+    W = np.zeros((3, K, L, 4))
+    res = oracle.pcg(S.indptr, S.indices, S.data, sy.b, (U, W, np.zeros(sy.n)), 1e-10, 50)
+    assert res.status == "converged" and res.iterations == 1
+
+
+def test_scale_invariance():
+    b = make_config("N1k")
+    sy = b.system(0)
+    r1 = oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b, (sy.U, sy.W, sy.g), 1e-6, 1000)
+    c = 37.5
+    r2 = oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b,
+                    lambda v: c * oracle.apply_M(sy.U, sy.W, sy.g, v), 1e-6, 1000)
+    assert r1.iterations == r2.iterations
+    np.testing.assert_allclose(r1.x, r2.x, rtol=1e-8, atol=1e-8 * np.abs(r1.x).max())
+
+
+def test_finite_termination_small_system():
+    rng = np.random.default_rng(12)
+    n = 48
+    Q = np.linalg.qr(rng.standard_normal((n, n)))[0]
+    A = Q @ np.diag(np.linspace(1.0, 4.0, n)) @ Q.T
+    A = (A + A.T) / 2
+    S = scipy.sparse.csr_matrix(A)
+    rhs = rng.standard_normal(n)
+    res = oracle.pcg(S.indptr, S.indices, S.data, rhs, lambda v: v.copy(), 1e-12, 500)
+    assert res.status == "converged" and res.iterations <= n
+    # two distinct eigenvalues: CG converges in two steps
+    A2 = Q @ np.diag(np.where(np.arange(n) < n // 2, 1.0, 3.0)) @ Q.T
+    S2 = scipy.sparse.csr_matrix((A2 + A2.T) / 2)
+    res2 = oracle.pcg(S2.indptr, S2.indices, S2.data, rhs, lambda v: v.copy(), 1e-10, 500)
+    assert res2.iterations == 2
+
+
+def test_edge_cases():
+    b = make_config("N1k")
+    sy = b.system(0)
+    zero = oracle.pcg(sy.row_ptr, sy.col, sy.val, np.zeros(sy.n), (sy.U, sy.W, sy.g), 1e-6, 10)
+    assert zero.status == "converged" and zero.iterations == 0 and not zero.x.any()
+    one = oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b, (sy.U, sy.W, sy.g), 1e-6, 1)
+    assert one.status == "not_converged" and one.iterations == 1 and one.x.any()
+    bad = oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b,
+                     (0 * sy.U, sy.W, np.full(sy.n, -10.0)), 1e-6, 10)
+    assert bad.status == "breakdown"
+
+
+def test_batch_equals_per_system():
+    b = make_config("batch64x2k", batch=2)
+    res = oracle.pcg_batch(b)
+    for s in range(2):
+        sy = b.system(s)
+        r = oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b, (sy.U, sy.W, sy.g), b.tol, b.maxit)
+        assert r.iterations == res[s].iterations
+        np.testing.assert_array_equal(r.x, res[s].x)
