@@ -1,0 +1,199 @@
+/*
+ * hpcg.h - C ABI of the MI355X (gfx950) H-matrix-preconditioned conjugate
+ * gradient solver.
+ *
+ * The library solves A x = b for sparse SPD A (CSR, nodes in space-filling-curve
+ * order) with preconditioned CG, where the preconditioner M is a
+ * weak-admissibility H-matrix approximate inverse applied every iteration
+ * without ever being assembled:
+ *
+ *   M = blockdiag_k(U_k U_k^T)                      dense leaf blocks, L = 128
+ *     + sum over tiles (l, j) of  U_{l,j} V_{l,j}^T   and its mirror V U^T
+ *     + diag(g)                                     per-node gate
+ *
+ * Sources for the operations (cited by page title and section):
+ *  - "Hierarchical Transformer Preconditioning for Interactive Physics
+ *    Simulation" (arXiv 2605.13343 v1/v2), section 5 "Preconditioner
+ *    Application": the diagonal stage y_k = F_k r_k as one batched product over
+ *    leaves, the off-diagonal restriction / strip aggregation / coupling /
+ *    prolongation chain of eqs. (2)-(5), and the CSR SpMV as the only sparse
+ *    operation of the loop; section 5 "Single-graph capture": the whole
+ *    iteration without host dispatch; Supplementary section 2 "Apply-path
+ *    tensor layout": the partition with K - 1 unique tiles at eta = 1;
+ *    Supplementary section 7: fp32 apply and vectors, fp64 scalar accumulators.
+ *  - "A Neural Hierarchical-Matrix Preconditioner for Real-Time GPU Solves"
+ *    (v3), section 2 "Preconditioner": leaf blocks F_k = U_k U_k^T, symmetric
+ *    mirrored off-diagonal tiles.
+ *
+ * Partition.  n unknowns per system are cut into K = n / L leaves (L = 128,
+ * K a power of two).  Tile j of level l (S = 2^l leaves per side, l = 0 ..
+ * levels-1, j = 0 .. K/(2S)-1) couples row leaves [2jS, 2jS+S) with column
+ * leaves [2jS+S, 2jS+2S).  Its factors are stacks of per-leaf slabs:
+ * U_{l,j} stacks W_l[k] over the row leaves, V_{l,j} over the column leaves,
+ * each slab L x R with R = 32, and the coupling core is the identity.
+ *
+ * Batching.  `batch` independent systems of equal n are solved in lockstep,
+ * one launch per phase across the whole batch.  The CSR of a batch is
+ * block-diagonal with global indices (system s owns rows and columns
+ * [s*n, (s+1)*n)); factors and vectors carry a leading batch axis.
+ *
+ * Memory and ownership.  Every pointer named d_* is device memory on the
+ * current HIP device; h_* pointers are host memory.  The caller owns all
+ * device memory, including the workspace: the library never allocates device
+ * memory and keeps only a host-side handle (plus an instantiated HIP graph and
+ * a few bytes of pinned host memory for convergence polling).  hpcg_create and
+ * hpcg_set_factors copy their inputs into the workspace in stream order, so the
+ * caller may reuse those buffers once the stream has passed the call.  The
+ * workspace must stay allocated until hpcg_destroy.
+ *
+ * Streams and threads.  All work is enqueued on the stream given to
+ * hpcg_create.  hpcg_apply_M and hpcg_spmv are asynchronous; hpcg_solve returns
+ * after its final synchronization.  A handle is not thread-safe; different
+ * handles are independent.
+ *
+ * Errors.  Every call returns an hpcg_status; nothing throws across the ABI.
+ * Arguments are validated before any launch.  HIP failures return
+ * HPCG_ERR_HIP with text in hpcg_last_error.
+ */
+#ifndef HPCG_H
+#define HPCG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct hpcg_ctx* hpcg_handle;
+
+typedef enum {
+    HPCG_OK = 0,
+    HPCG_ERR_INVALID_ARG = 1,   /* null pointer, bad tolerance, bad option       */
+    HPCG_ERR_SHAPE = 2,         /* partition or CSR sizes not supported          */
+    HPCG_ERR_HIP = 3,           /* a HIP runtime call failed                     */
+    HPCG_ERR_BREAKDOWN = 4,     /* p.Ap or r.Mr not positive and finite          */
+    HPCG_ERR_NOT_CONVERGED = 5, /* maxit reached before the tolerance            */
+    HPCG_ERR_WORKSPACE = 6,     /* workspace too small or misaligned             */
+    HPCG_ERR_STATE = 7          /* call order violated (e.g. solve before factors) */
+} hpcg_status;
+
+/* Per-system outcome of the last hpcg_solve (see hpcg_last_solve_status). */
+typedef enum {
+    HPCG_SYS_RUNNING = 0,
+    HPCG_SYS_CONVERGED = 1,
+    HPCG_SYS_NOT_CONVERGED = 2,
+    HPCG_SYS_BREAKDOWN = 3
+} hpcg_system_status;
+
+typedef struct {
+    int32_t n;       /* unknowns per system; n % leaf == 0, n / leaf a power of 2 */
+    int32_t leaf;    /* L, must be 128                                            */
+    int32_t rank;    /* R, columns of every off-diagonal slab, must be 32         */
+    int32_t levels;  /* tile levels present, 0 .. log2(n / leaf); 0 = leaves only */
+    int32_t batch;   /* B >= 1 independent systems                                */
+} hpcg_partition;
+
+/* Solve engines (hpcg_set_option(HPCG_OPT_ENGINE, ...)). */
+typedef enum {
+    HPCG_ENGINE_AUTO = 0,       /* persistent when co-residency allows, else graph */
+    HPCG_ENGINE_GRAPH = 1,      /* per-phase kernels, unrolled iterations replayed
+                                   as one hipGraph, host polls a pinned flag      */
+    HPCG_ENGINE_PERSISTENT = 2  /* one cooperative launch runs the whole solve with
+                                   device-wide barriers between phases            */
+} hpcg_engine;
+
+typedef enum {
+    HPCG_OPT_ENGINE = 1,        /* an hpcg_engine value                          */
+    HPCG_OPT_GRAPH_UNROLL = 2,  /* iterations per graph replay, 1 .. 64 (default 8) */
+    HPCG_OPT_RESIDENT = 3       /* persistent engine keeps M in LDS when it fits:
+                                   1 = yes (default), 0 = stream M every iteration */
+} hpcg_option;
+
+/* Bytes of device workspace hpcg_create needs for this partition and a CSR of
+ * nnz_total stored entries (all systems together).  Returns 0 when the
+ * partition is invalid.  The workspace must be 256-byte aligned. */
+size_t hpcg_workspace_bytes(const hpcg_partition* part, int64_t nnz_total);
+
+/* Create a solver for one sparsity pattern and value set of A.
+ *  part        partition and batch size (validated: HPCG_ERR_SHAPE).
+ *  d_row_ptr   int32 [batch*n + 1], d_row_ptr[0] == 0, nondecreasing,
+ *              d_row_ptr[batch*n] == nnz_total.
+ *  d_col       int32 [nnz_total] global column indices; row i of system s must
+ *              only reference columns of system s.
+ *  d_val       float32 [nnz_total].
+ *  d_workspace at least hpcg_workspace_bytes(part, nnz_total) bytes.
+ *  stream      a hipStream_t, or NULL for the null stream.
+ *  out         receives the handle; untouched on error.
+ * The CSR is copied into the workspace (stream-ordered).  The row pointer is
+ * checked on the host after one synchronous copy; column indices are trusted. */
+hpcg_status hpcg_create(const hpcg_partition* part, const int32_t* d_row_ptr,
+                        const int32_t* d_col, const float* d_val, int64_t nnz_total,
+                        void* d_workspace, size_t ws_bytes, void* stream,
+                        hpcg_handle* out);
+
+/* Replace the matrix values (same pattern) without rebuilding the handle.
+ * d_val float32 [nnz_total], copied in stream order. */
+hpcg_status hpcg_set_values(hpcg_handle h, const float* d_val);
+
+/* Load the preconditioner factors (the stand-in for the pages' network output),
+ * copied into the workspace in stream order:
+ *  d_leafU  float32 [batch][K][L][L]            U_k, row-major, row = node in leaf
+ *  d_tileW  float32 [batch][levels][K][L][R]    slab of leaf k at level l: a slab
+ *           of U_{l,j} when (k >> l) is even, of V_{l,j} when it is odd
+ *           (may be NULL when levels == 0)
+ *  d_gate   float32 [batch][n]                  g, added as diag(g)
+ * M is symmetric by construction; it must also be positive definite for PCG
+ * (not checked here; a non-positive r.Mr is reported as HPCG_ERR_BREAKDOWN). */
+hpcg_status hpcg_set_factors(hpcg_handle h, const float* d_leafU, const float* d_tileW,
+                             const float* d_gate);
+
+/* y = M r for every system of the batch (asynchronous, stream-ordered).
+ * d_r, d_y float32 [batch*n], must not alias. */
+hpcg_status hpcg_apply_M(hpcg_handle h, const float* d_r, float* d_y);
+
+/* y = A x for every system of the batch (asynchronous, stream-ordered).
+ * d_x, d_y float32 [batch*n], must not alias. */
+hpcg_status hpcg_spmv(hpcg_handle h, const float* d_x, float* d_y);
+
+/* Solve A x = b for every system with x_0 = 0, stopping a system when its
+ * recursively updated residual satisfies ||r_k||_2 <= tol * ||b||_2 (the pages'
+ * ||r_k|| / ||r_0|| with r_0 = b), or after maxit iterations.
+ *  d_b      float32 [batch*n]
+ *  d_x      float64 [batch*n]  solution (written also when not converged)
+ *  tol      > 0;  maxit >= 1
+ *  h_iters  int32 [batch] or NULL: products q = A p done when the test passed
+ *           (maxit when not converged; the iteration of the failure on breakdown)
+ *  h_relres float64 [batch] or NULL: ||r||/||b|| of the recursive residual at exit
+ * Vectors are fp32, scalars (dot products, norms, step sizes) fp64, x fp64.
+ * Returns HPCG_OK when every system converged, HPCG_ERR_BREAKDOWN when any
+ * system broke down, else HPCG_ERR_NOT_CONVERGED when any system ran out of
+ * iterations.  Synchronizes the handle's stream before returning. */
+hpcg_status hpcg_solve(hpcg_handle h, const float* d_b, double* d_x, double tol,
+                       int32_t maxit, int32_t* h_iters, double* h_relres);
+
+/* Per-system hpcg_system_status values of the last hpcg_solve, int32 [batch]. */
+hpcg_status hpcg_last_solve_status(hpcg_handle h, int32_t* h_status);
+
+/* Engine and tuning options (see hpcg_option). */
+hpcg_status hpcg_set_option(hpcg_handle h, int32_t option, int32_t value);
+
+/* Engine the last hpcg_solve actually ran (an hpcg_engine value), or 0. */
+int32_t hpcg_last_engine(hpcg_handle h);
+
+/* Static text for a status code. */
+const char* hpcg_status_string(hpcg_status s);
+
+/* Text of the last error on this handle ("" when none); NULL handle gives the
+ * last error of a failed hpcg_create on this thread. */
+const char* hpcg_last_error(hpcg_handle h);
+
+/* Release the handle (and its graph / pinned host memory).  Does not free the
+ * caller's workspace.  NULL is ignored. */
+void hpcg_destroy(hpcg_handle h);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HPCG_H */

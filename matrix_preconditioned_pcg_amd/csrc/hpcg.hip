@@ -1,0 +1,524 @@
+// Host side of the C ABI declared in include/hpcg.h: argument checks, workspace
+// carving, engine selection and the solve loop.  All device work is in
+// hpcg_kernels.hpp / hpcg_device.hpp.
+#include "hpcg.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <chrono>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "hpcg_kernels.hpp"
+
+using namespace hpcg;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  size_t row_ptr, col, val, U, W, g, b, r, z, q, p0, p1, x, tpart, ppart, pq, rr, rz, st, ctl, total;
+};
+
+// control words, each on its own 256-byte line
+constexpr size_t kCtlBarrier = 0, kCtlAbort = 256, kCtlItbase = 512, kCtlReplays = 768, kCtlBytes = 1024;
+
+bool make_geom(const hpcg_partition* p, Geom& G, std::string& why) {
+  if (!p) { why = "partition is NULL"; return false; }
+  if (p->leaf != LEAF) { why = "leaf size must be 128"; return false; }
+  if (p->rank != RANK) { why = "off-diagonal rank must be 32"; return false; }
+  if (p->n <= 0 || p->n % LEAF) { why = "n must be a positive multiple of 128"; return false; }
+  const int K = p->n / LEAF;
+  if (K & (K - 1)) { why = "n/128 must be a power of two"; return false; }
+  int full = 0;
+  while ((1 << full) < K) ++full;
+  if (p->levels < 0 || p->levels > full) { why = "levels must lie in [0, log2(n/128)]"; return false; }
+  if (p->levels > MAX_LEVELS) { why = "too many levels"; return false; }
+  if (p->batch < 1) { why = "batch must be >= 1"; return false; }
+  if ((int64_t)p->batch * p->n >= (int64_t)1 << 30) { why = "batch*n too large"; return false; }
+  G.n = p->n;
+  G.K = K;
+  G.levels = p->levels;
+  G.B = p->batch;
+  int bpl = 1;
+  while ((int64_t)G.B * K * bpl < 256 && bpl < 8) bpl *= 2;
+  G.bpl = bpl;
+  G.RB = LEAF / bpl;
+  G.nblk_sys = K * bpl;
+  G.nblk = G.B * G.nblk_sys;
+  return true;
+}
+
+Layout make_layout(const Geom& G, int64_t nnz) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+  const size_t N = (size_t)G.B * G.n;
+  L.row_ptr = take((N + 1) * 4);
+  L.col = take((size_t)nnz * 4);
+  L.val = take((size_t)nnz * 4);
+  L.U = take((size_t)G.B * G.K * LEAF * LEAF * 4);
+  L.W = take((size_t)G.B * G.levels * G.K * LEAF * RANK * 4);
+  L.g = take(N * 4);
+  L.b = take(N * 4);
+  L.r = take(N * 4);
+  L.z = take(N * 4);
+  L.q = take(N * 4);
+  L.p0 = take(N * 4);
+  L.p1 = take(N * 4);
+  L.x = take(N * 8);
+  L.tpart = take((size_t)G.B * G.K * G.bpl * LEAF * 4);
+  L.ppart = take((size_t)G.B * G.levels * G.K * G.bpl * RANK * 4 + 4);
+  L.pq = take((size_t)G.nblk * 8);
+  L.rr = take((size_t)G.nblk * 8);
+  L.rz = take((size_t)G.nblk * 8);
+  L.st = take((size_t)G.B * sizeof(SysState));
+  L.ctl = take(kCtlBytes);
+  L.total = off;
+  return L;
+}
+
+thread_local std::string g_create_error;
+
+}  // namespace
+
+struct hpcg_ctx {
+  hpcg_partition part{};
+  int64_t nnz = 0;
+  Geom G{};
+  Bufs B{};
+  Layout lay{};
+  hipStream_t stream = nullptr;
+  hipStream_t cap_stream = nullptr;
+  char* ws = nullptr;
+  bool factors_set = false;
+  int engine_opt = HPCG_ENGINE_AUTO;
+  int unroll = 8;
+  int resident = 1;
+  int last_engine = 0;
+  int num_cu = 0;
+  int coop = 0;
+  size_t max_lds = 0;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t gexec = nullptr;
+  int graph_unroll = 0;
+  double graph_tol = -1.0;
+  int graph_maxit = -1;
+  int* h_flag = nullptr;   // pinned, device-mapped
+  int* d_flag = nullptr;
+  SysState* h_st = nullptr;
+  int* h_ctl = nullptr;    // pinned copy of the abort flag
+  std::vector<int32_t> last_status;
+  std::string err;
+};
+
+namespace {
+
+hpcg_status fail(hpcg_ctx* h, hpcg_status s, const std::string& msg) {
+  if (h) h->err = msg; else g_create_error = msg;
+  return s;
+}
+
+hpcg_status hip_fail(hpcg_ctx* h, hipError_t e, const char* what) {
+  std::string m = std::string(what) + ": " + hipGetErrorString(e);
+  return fail(h, HPCG_ERR_HIP, m);
+}
+
+#define HIP_OR_FAIL(h, call)                                  \
+  do {                                                        \
+    hipError_t e_ = (call);                                   \
+    if (e_ != hipSuccess) return hip_fail((h), e_, #call);    \
+  } while (0)
+
+hpcg_status check_launch(hpcg_ctx* h, const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(h, e, what);
+  return HPCG_OK;
+}
+
+size_t res_lds_bytes(const Geom& G) {
+  return ((size_t)G.RB * LEAF + (size_t)G.levels * G.RB * RANK) * sizeof(float);
+}
+
+void destroy_graph(hpcg_ctx* h) {
+  if (h->gexec) (void)hipGraphExecDestroy(h->gexec);
+  if (h->graph) (void)hipGraphDestroy(h->graph);
+  h->gexec = nullptr;
+  h->graph = nullptr;
+  h->graph_unroll = 0;
+}
+
+hpcg_status build_graph(hpcg_ctx* h) {
+  destroy_graph(h);
+  const Geom G = h->G;
+  const Bufs B = h->B;
+  HIP_OR_FAIL(h, hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal));
+  for (int j = 0; j < h->unroll; ++j) {
+    hipLaunchKernelGGL(k_phase_A, dim3(G.nblk), dim3(NT), 0, h->cap_stream, G, B, j);
+    hipLaunchKernelGGL(k_phase_B, dim3(G.nblk), dim3(NT), 0, h->cap_stream, G, B, j);
+    hipLaunchKernelGGL(k_phase_C, dim3(G.nblk), dim3(NT), 0, h->cap_stream, G, B, j, -1);
+  }
+  hipLaunchKernelGGL(k_advance, dim3(1), dim3(64), 0, h->cap_stream, G, B, h->unroll, h->d_flag);
+  hipError_t e = hipStreamEndCapture(h->cap_stream, &h->graph);
+  if (e != hipSuccess) return hip_fail(h, e, "hipStreamEndCapture");
+  e = hipGraphInstantiate(&h->gexec, h->graph, nullptr, nullptr, 0);
+  if (e != hipSuccess) return hip_fail(h, e, "hipGraphInstantiate");
+  h->graph_unroll = h->unroll;
+  h->graph_tol = B.tol;
+  h->graph_maxit = B.maxit;
+  return HPCG_OK;
+}
+
+hpcg_status run_graph(hpcg_ctx* h) {
+  const Geom G = h->G;
+  const Bufs B = h->B;
+  if (!h->gexec || h->graph_unroll != h->unroll || h->graph_tol != B.tol || h->graph_maxit != B.maxit) {
+    hpcg_status s = build_graph(h);
+    if (s != HPCG_OK) return s;
+  }
+  hipLaunchKernelGGL(k_reset, dim3(1), dim3(64), 0, h->stream, B, 1, h->d_flag);
+  hipLaunchKernelGGL(k_init, dim3(G.nblk), dim3(NT), 0, h->stream, G, B);
+  hipLaunchKernelGGL(k_phase_C, dim3(G.nblk), dim3(NT), 0, h->stream, G, B, 0, 0);
+  hpcg_status s = check_launch(h, "graph engine setup launch");
+  if (s != HPCG_OK) return s;
+  __atomic_store_n(h->h_flag, 0, __ATOMIC_RELEASE);
+  const int max_replays = (B.maxit + h->unroll - 1) / h->unroll;
+  const int lookahead = 2;
+  int launched = 0, seen = 0;
+  bool done = false;
+  while (!done) {
+    while (launched < max_replays && launched - seen < lookahead) {
+      HIP_OR_FAIL(h, hipGraphLaunch(h->gexec, h->stream));
+      ++launched;
+    }
+    // wait until the next replay has published its flag
+    unsigned spins = 0;
+    for (;;) {
+      const int f = __atomic_load_n(h->h_flag, __ATOMIC_ACQUIRE);
+      if ((f >> 1) > seen) {
+        seen = f >> 1;
+        done = (f & 1) != 0 || seen >= max_replays;
+        break;
+      }
+      if ((++spins & 1023u) == 0) {
+        hipError_t q = hipStreamQuery(h->stream);
+        if (q == hipSuccess) {
+          const int f2 = __atomic_load_n(h->h_flag, __ATOMIC_ACQUIRE);
+          if ((f2 >> 1) <= seen) return fail(h, HPCG_ERR_HIP, "graph engine: stream drained without progress flag");
+        } else if (q != hipErrorNotReady) {
+          return hip_fail(h, q, "hipStreamQuery");
+        }
+      }
+    }
+  }
+  return HPCG_OK;
+}
+
+hpcg_status run_persistent(hpcg_ctx* h, bool& ran) {
+  ran = false;
+  const Geom G = h->G;
+  const Bufs B = h->B;
+  if (!h->coop) return HPCG_OK;
+  int per_cu = 0;
+  bool res = false;
+  size_t dyn = 0;
+  const void* fn = nullptr;
+  int grid = 0;
+  if (h->resident && res_lds_bytes(G) + sizeof(Smem) <= h->max_lds) {
+    dyn = res_lds_bytes(G);
+    fn = reinterpret_cast<const void*>(&k_persistent<true>);
+    HIP_OR_FAIL(h, hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn));
+    HIP_OR_FAIL(h, hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NT, dyn));
+    if ((int64_t)per_cu * h->num_cu >= G.nblk) {
+      res = true;
+      grid = G.nblk;
+    }
+  }
+  if (!res) {
+    dyn = 0;
+    fn = reinterpret_cast<const void*>(&k_persistent<false>);
+    HIP_OR_FAIL(h, hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NT, 0));
+    const int64_t cap = (int64_t)per_cu * h->num_cu;
+    if (cap <= 0) return HPCG_OK;
+    grid = (int)std::min<int64_t>(cap, G.nblk);
+  }
+  hipLaunchKernelGGL(k_reset, dim3(1), dim3(64), 0, h->stream, B, 0, (int*)nullptr);
+  Geom Ga = G;
+  Bufs Ba = B;
+  void* args[] = {&Ga, &Ba};
+  HIP_OR_FAIL(h, hipLaunchCooperativeKernel(fn, dim3(grid), dim3(NT), args, (unsigned)dyn, h->stream));
+  ran = true;
+  return HPCG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hpcg_workspace_bytes(const hpcg_partition* part, int64_t nnz_total) {
+  Geom G;
+  std::string why;
+  if (!make_geom(part, G, why) || nnz_total < 0) return 0;
+  return make_layout(G, nnz_total).total;
+}
+
+hpcg_status hpcg_create(const hpcg_partition* part, const int32_t* d_row_ptr, const int32_t* d_col,
+                        const float* d_val, int64_t nnz_total, void* d_workspace, size_t ws_bytes,
+                        void* stream, hpcg_handle* out) {
+  g_create_error.clear();
+  if (!out) return fail(nullptr, HPCG_ERR_INVALID_ARG, "out is NULL");
+  Geom G;
+  std::string why;
+  if (!make_geom(part, G, why)) return fail(nullptr, HPCG_ERR_SHAPE, why);
+  if (nnz_total < 0 || nnz_total >= ((int64_t)1 << 31)) return fail(nullptr, HPCG_ERR_SHAPE, "nnz_total out of range");
+  if (!d_row_ptr || (nnz_total > 0 && (!d_col || !d_val)))
+    return fail(nullptr, HPCG_ERR_INVALID_ARG, "CSR pointer is NULL");
+  if (!d_workspace) return fail(nullptr, HPCG_ERR_INVALID_ARG, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(d_workspace) % kAlign)
+    return fail(nullptr, HPCG_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const Layout lay = make_layout(G, nnz_total);
+  if (ws_bytes < lay.total) return fail(nullptr, HPCG_ERR_WORKSPACE, "workspace too small");
+
+  hpcg_ctx* h = new hpcg_ctx();
+  h->part = *part;
+  h->nnz = nnz_total;
+  h->G = G;
+  h->lay = lay;
+  h->stream = reinterpret_cast<hipStream_t>(stream);
+  h->ws = reinterpret_cast<char*>(d_workspace);
+  auto cleanup_fail = [&](hpcg_status s) {
+    g_create_error = h->err;
+    hpcg_destroy(h);
+    return s;
+  };
+#define CREATE_HIP(call)                                              \
+  do {                                                                \
+    hipError_t e_ = (call);                                           \
+    if (e_ != hipSuccess) return cleanup_fail(hip_fail(h, e_, #call)); \
+  } while (0)
+
+  int dev = 0;
+  CREATE_HIP(hipGetDevice(&dev));
+  hipDeviceProp_t prop;
+  CREATE_HIP(hipGetDeviceProperties(&prop, dev));
+  h->num_cu = prop.multiProcessorCount;
+  h->max_lds = prop.sharedMemPerMultiprocessor ? prop.sharedMemPerMultiprocessor : 65536;
+  int coop = 0;
+  CREATE_HIP(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev));
+  h->coop = coop;
+  CREATE_HIP(hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking));
+  CREATE_HIP(hipHostMalloc(reinterpret_cast<void**>(&h->h_flag), 256, hipHostMallocMapped));
+  CREATE_HIP(hipHostGetDevicePointer(reinterpret_cast<void**>(&h->d_flag), h->h_flag, 0));
+  CREATE_HIP(hipHostMalloc(reinterpret_cast<void**>(&h->h_st), (size_t)G.B * sizeof(SysState), hipHostMallocDefault));
+  CREATE_HIP(hipHostMalloc(reinterpret_cast<void**>(&h->h_ctl), 256, hipHostMallocDefault));
+  *h->h_flag = 0;
+
+  char* w = h->ws;
+  Bufs& B = h->B;
+  B.row_ptr = reinterpret_cast<const int*>(w + lay.row_ptr);
+  B.col = reinterpret_cast<const int*>(w + lay.col);
+  B.val = reinterpret_cast<const float*>(w + lay.val);
+  B.U = reinterpret_cast<const float*>(w + lay.U);
+  B.W = reinterpret_cast<const float*>(w + lay.W);
+  B.g = reinterpret_cast<const float*>(w + lay.g);
+  B.b = reinterpret_cast<const float*>(w + lay.b);
+  B.r = reinterpret_cast<float*>(w + lay.r);
+  B.z = reinterpret_cast<float*>(w + lay.z);
+  B.q = reinterpret_cast<float*>(w + lay.q);
+  B.p0 = reinterpret_cast<float*>(w + lay.p0);
+  B.p1 = reinterpret_cast<float*>(w + lay.p1);
+  B.x = reinterpret_cast<double*>(w + lay.x);
+  B.tpart = reinterpret_cast<float*>(w + lay.tpart);
+  B.ppart = reinterpret_cast<float*>(w + lay.ppart);
+  B.pq_part = reinterpret_cast<double*>(w + lay.pq);
+  B.rr_part = reinterpret_cast<double*>(w + lay.rr);
+  B.rz_part = reinterpret_cast<double*>(w + lay.rz);
+  B.st = reinterpret_cast<SysState*>(w + lay.st);
+  B.barrier = reinterpret_cast<unsigned*>(w + lay.ctl + kCtlBarrier);
+  B.abort_flag = reinterpret_cast<int*>(w + lay.ctl + kCtlAbort);
+  B.itbase = reinterpret_cast<int*>(w + lay.ctl + kCtlItbase);
+  B.replays = reinterpret_cast<int*>(w + lay.ctl + kCtlReplays);
+  B.tol = 1e-6;
+  B.maxit = 1000;
+
+  const size_t N = (size_t)G.B * G.n;
+  CREATE_HIP(hipMemcpyAsync(w + lay.row_ptr, d_row_ptr, (N + 1) * 4, hipMemcpyDeviceToDevice, h->stream));
+  if (nnz_total > 0) {
+    CREATE_HIP(hipMemcpyAsync(w + lay.col, d_col, (size_t)nnz_total * 4, hipMemcpyDeviceToDevice, h->stream));
+    CREATE_HIP(hipMemcpyAsync(w + lay.val, d_val, (size_t)nnz_total * 4, hipMemcpyDeviceToDevice, h->stream));
+  }
+  // host-side structural checks of the CSR (create time only)
+  std::vector<int32_t> rp(N + 1), cols((size_t)nnz_total);
+  CREATE_HIP(hipMemcpyAsync(rp.data(), w + lay.row_ptr, (N + 1) * 4, hipMemcpyDeviceToHost, h->stream));
+  if (nnz_total > 0)
+    CREATE_HIP(hipMemcpyAsync(cols.data(), w + lay.col, (size_t)nnz_total * 4, hipMemcpyDeviceToHost, h->stream));
+  CREATE_HIP(hipStreamSynchronize(h->stream));
+  if (rp[0] != 0 || rp[N] != nnz_total) return cleanup_fail(fail(h, HPCG_ERR_SHAPE, "row_ptr must start at 0 and end at nnz_total"));
+  for (size_t i = 0; i < N; ++i) {
+    if (rp[i + 1] < rp[i]) return cleanup_fail(fail(h, HPCG_ERR_SHAPE, "row_ptr must be nondecreasing"));
+    const int64_t lo = (int64_t)(i / G.n) * G.n, hi = lo + G.n;
+    for (int32_t e = rp[i]; e < rp[i + 1]; ++e)
+      if (cols[e] < lo || cols[e] >= hi)
+        return cleanup_fail(fail(h, HPCG_ERR_SHAPE, "column index outside its system's block"));
+  }
+#undef CREATE_HIP
+  h->last_status.assign(G.B, HPCG_SYS_RUNNING);
+  *out = h;
+  return HPCG_OK;
+}
+
+hpcg_status hpcg_set_values(hpcg_handle h, const float* d_val) {
+  if (!h) return fail(nullptr, HPCG_ERR_INVALID_ARG, "handle is NULL");
+  if (h->nnz > 0 && !d_val) return fail(h, HPCG_ERR_INVALID_ARG, "d_val is NULL");
+  if (h->nnz > 0)
+    HIP_OR_FAIL(h, hipMemcpyAsync(h->ws + h->lay.val, d_val, (size_t)h->nnz * 4, hipMemcpyDeviceToDevice, h->stream));
+  return HPCG_OK;
+}
+
+hpcg_status hpcg_set_factors(hpcg_handle h, const float* d_leafU, const float* d_tileW, const float* d_gate) {
+  if (!h) return fail(nullptr, HPCG_ERR_INVALID_ARG, "handle is NULL");
+  const Geom& G = h->G;
+  if (!d_leafU || !d_gate || (G.levels > 0 && !d_tileW)) return fail(h, HPCG_ERR_INVALID_ARG, "factor pointer is NULL");
+  HIP_OR_FAIL(h, hipMemcpyAsync(h->ws + h->lay.U, d_leafU, (size_t)G.B * G.K * LEAF * LEAF * 4,
+                                hipMemcpyDeviceToDevice, h->stream));
+  if (G.levels > 0)
+    HIP_OR_FAIL(h, hipMemcpyAsync(h->ws + h->lay.W, d_tileW, (size_t)G.B * G.levels * G.K * LEAF * RANK * 4,
+                                  hipMemcpyDeviceToDevice, h->stream));
+  HIP_OR_FAIL(h, hipMemcpyAsync(h->ws + h->lay.g, d_gate, (size_t)G.B * G.n * 4, hipMemcpyDeviceToDevice, h->stream));
+  h->factors_set = true;
+  return HPCG_OK;
+}
+
+hpcg_status hpcg_apply_M(hpcg_handle h, const float* d_r, float* d_y) {
+  if (!h) return fail(nullptr, HPCG_ERR_INVALID_ARG, "handle is NULL");
+  if (!d_r || !d_y) return fail(h, HPCG_ERR_INVALID_ARG, "vector pointer is NULL");
+  if (d_r == d_y) return fail(h, HPCG_ERR_INVALID_ARG, "d_r and d_y must not alias");
+  if (!h->factors_set) return fail(h, HPCG_ERR_STATE, "hpcg_set_factors has not been called");
+  const Geom& G = h->G;
+  hipLaunchKernelGGL(k_apply_restrict, dim3(G.nblk), dim3(NT), 0, h->stream, G, h->B, d_r);
+  hipLaunchKernelGGL(k_apply_prolong, dim3(G.nblk), dim3(NT), 0, h->stream, G, h->B, d_r, d_y);
+  return check_launch(h, "hpcg_apply_M launch");
+}
+
+hpcg_status hpcg_spmv(hpcg_handle h, const float* d_x, float* d_y) {
+  if (!h) return fail(nullptr, HPCG_ERR_INVALID_ARG, "handle is NULL");
+  if (!d_x || !d_y) return fail(h, HPCG_ERR_INVALID_ARG, "vector pointer is NULL");
+  if (d_x == d_y) return fail(h, HPCG_ERR_INVALID_ARG, "d_x and d_y must not alias");
+  const int N = h->G.B * h->G.n;
+  const int grid = (N + SPMV_ROWS - 1) / SPMV_ROWS;
+  hipLaunchKernelGGL(k_spmv, dim3(grid), dim3(NT), 0, h->stream, h->B.row_ptr, h->B.col, h->B.val, d_x, d_y, N);
+  return check_launch(h, "hpcg_spmv launch");
+}
+
+hpcg_status hpcg_solve(hpcg_handle h, const float* d_b, double* d_x, double tol, int32_t maxit,
+                       int32_t* h_iters, double* h_relres) {
+  if (!h) return fail(nullptr, HPCG_ERR_INVALID_ARG, "handle is NULL");
+  if (!d_b || !d_x) return fail(h, HPCG_ERR_INVALID_ARG, "vector pointer is NULL");
+  if (!(tol > 0.0) || !(tol < 1e300)) return fail(h, HPCG_ERR_INVALID_ARG, "tol must be positive and finite");
+  if (maxit < 1) return fail(h, HPCG_ERR_INVALID_ARG, "maxit must be >= 1");
+  if (!h->factors_set) return fail(h, HPCG_ERR_STATE, "hpcg_set_factors has not been called");
+  const Geom G = h->G;
+  const size_t N = (size_t)G.B * G.n;
+  h->B.tol = tol;
+  h->B.maxit = maxit;
+  HIP_OR_FAIL(h, hipMemcpyAsync(h->ws + h->lay.b, d_b, N * 4, hipMemcpyDeviceToDevice, h->stream));
+  hpcg_status s = HPCG_OK;
+  bool ran = false;
+  if (h->engine_opt != HPCG_ENGINE_GRAPH) {
+    s = run_persistent(h, ran);
+    if (s != HPCG_OK) return s;
+    if (!ran && h->engine_opt == HPCG_ENGINE_PERSISTENT)
+      return fail(h, HPCG_ERR_SHAPE, "persistent engine: device does not support a co-resident grid for this partition");
+    if (ran) h->last_engine = HPCG_ENGINE_PERSISTENT;
+  }
+  if (!ran) {
+    s = run_graph(h);
+    if (s != HPCG_OK) return s;
+    h->last_engine = HPCG_ENGINE_GRAPH;
+  }
+  hipLaunchKernelGGL(k_copy_x, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, h->stream, h->B.x, d_x, (int)N);
+  s = check_launch(h, "copy-out launch");
+  if (s != HPCG_OK) return s;
+  HIP_OR_FAIL(h, hipMemcpyAsync(h->h_st, h->B.st, (size_t)G.B * sizeof(SysState), hipMemcpyDeviceToHost, h->stream));
+  HIP_OR_FAIL(h, hipMemcpyAsync(h->h_ctl, h->B.abort_flag, sizeof(int), hipMemcpyDeviceToHost, h->stream));
+  HIP_OR_FAIL(h, hipStreamSynchronize(h->stream));
+  if (*h->h_ctl) return fail(h, HPCG_ERR_HIP, "device-wide barrier timed out (workgroups not co-resident)");
+  bool any_break = false, any_nc = false;
+  for (int i = 0; i < G.B; ++i) {
+    const SysState& st = h->h_st[i];
+    h->last_status[i] = st.status;
+    if (h_iters) h_iters[i] = st.iters;
+    if (h_relres) h_relres[i] = st.relres;
+    if (st.status == ST_BREAKDOWN) any_break = true;
+    else if (st.status != ST_CONVERGED) any_nc = true;
+  }
+  if (any_break) return fail(h, HPCG_ERR_BREAKDOWN, "breakdown: p.Ap or r.Mr not positive and finite");
+  if (any_nc) return fail(h, HPCG_ERR_NOT_CONVERGED, "maxit reached before the tolerance");
+  return HPCG_OK;
+}
+
+hpcg_status hpcg_last_solve_status(hpcg_handle h, int32_t* h_status) {
+  if (!h) return fail(nullptr, HPCG_ERR_INVALID_ARG, "handle is NULL");
+  if (!h_status) return fail(h, HPCG_ERR_INVALID_ARG, "h_status is NULL");
+  for (int i = 0; i < h->G.B; ++i) h_status[i] = h->last_status[i];
+  return HPCG_OK;
+}
+
+hpcg_status hpcg_set_option(hpcg_handle h, int32_t option, int32_t value) {
+  if (!h) return fail(nullptr, HPCG_ERR_INVALID_ARG, "handle is NULL");
+  switch (option) {
+    case HPCG_OPT_ENGINE:
+      if (value < HPCG_ENGINE_AUTO || value > HPCG_ENGINE_PERSISTENT) return fail(h, HPCG_ERR_INVALID_ARG, "bad engine");
+      h->engine_opt = value;
+      return HPCG_OK;
+    case HPCG_OPT_GRAPH_UNROLL:
+      if (value < 1 || value > 64) return fail(h, HPCG_ERR_INVALID_ARG, "graph unroll must lie in [1, 64]");
+      h->unroll = value;
+      return HPCG_OK;
+    case HPCG_OPT_RESIDENT:
+      if (value != 0 && value != 1) return fail(h, HPCG_ERR_INVALID_ARG, "resident must be 0 or 1");
+      h->resident = value;
+      return HPCG_OK;
+    default:
+      return fail(h, HPCG_ERR_INVALID_ARG, "unknown option");
+  }
+}
+
+int32_t hpcg_last_engine(hpcg_handle h) { return h ? h->last_engine : 0; }
+
+const char* hpcg_status_string(hpcg_status s) {
+  switch (s) {
+    case HPCG_OK: return "ok";
+    case HPCG_ERR_INVALID_ARG: return "invalid argument";
+    case HPCG_ERR_SHAPE: return "unsupported shape";
+    case HPCG_ERR_HIP: return "HIP runtime error";
+    case HPCG_ERR_BREAKDOWN: return "PCG breakdown";
+    case HPCG_ERR_NOT_CONVERGED: return "not converged";
+    case HPCG_ERR_WORKSPACE: return "workspace error";
+    case HPCG_ERR_STATE: return "call order error";
+  }
+  return "unknown status";
+}
+
+const char* hpcg_last_error(hpcg_handle h) {
+  if (!h) return g_create_error.c_str();
+  return h->err.c_str();
+}
+
+void hpcg_destroy(hpcg_handle h) {
+  if (!h) return;
+  destroy_graph(h);
+  if (h->cap_stream) (void)hipStreamDestroy(h->cap_stream);
+  if (h->h_flag) (void)hipHostFree(h->h_flag);
+  if (h->h_st) (void)hipHostFree(h->h_st);
+  if (h->h_ctl) (void)hipHostFree(h->h_ctl);
+  delete h;
+}
+
+}  // extern "C"

@@ -1,0 +1,334 @@
+"""GPU parity: the HIP library against the CPU oracle, through the C ABI.
+
+Bars (fp32 vectors and apply, fp64 scalars and x):
+  * SpMV and M-apply: relative L2 error <= 1e-5 against the fp64 oracle on the
+    same fp32 inputs, and elementwise |y - y_ref| <= 1e-5 * (|M| |r|)_i (the
+    magnitude fp32 rounding scales with; the same with |A| |x| for the SpMV).
+  * PCG: same outcome, iteration count within 2 of the oracle's, recursive
+    residual <= tol and true residual ||b - A x||/||b|| <= 1.05 tol, both engines.
+The workloads are the five benchmark systems at full size plus small edge
+cases (one leaf, two leaves, levels below the maximum, odd batch sizes).
+"""
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from workloads import CONFIGS, make_config  # noqa: E402
+from workloads.generate import build_batch, random_system  # noqa: E402
+
+from matrix_preconditioned_pcg_amd import hpcg  # noqa: E402
+
+APPLY_TOL = 1e-5
+ITER_TOL = 2
+NAMES = list(CONFIGS)
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def cfg():
+    cache = {}
+
+    def get(name):
+        if name not in cache:
+            cache[name] = make_config(name)
+        return cache[name]
+    return get
+
+
+@pytest.fixture(scope="module")
+def oracle_solves():
+    cache = {}
+
+    def get(batch):
+        if batch.name not in cache:
+            cache[batch.name] = oracle.pcg_batch(batch)
+        return cache[batch.name]
+    return get
+
+
+def _solver(batch, levels=None):
+    s = hpcg.Solver(batch.n, batch.row_ptr, batch.col, batch.val, batch=batch.batch,
+                    levels=batch.levels if levels is None else levels)
+    s.set_factors(batch.U, batch.W if batch.levels else None, batch.g)
+    return s
+
+
+def _abs_apply(batch, r):
+    return np.stack([oracle.apply_M(np.abs(batch.U[s]), np.abs(batch.W[s]), np.abs(batch.g[s]), np.abs(r[s]))
+                     for s in range(batch.batch)])
+
+
+def _check_apply(batch, solver, r):
+    y = solver.apply_M(r.reshape(-1)).cpu().numpy().astype(np.float64).reshape(batch.batch, batch.n)
+    ref = oracle.apply_M_batch(batch.U, batch.W, batch.g, r)
+    mag = _abs_apply(batch, r)
+    rel = np.linalg.norm(y - ref) / np.linalg.norm(ref)
+    assert rel <= APPLY_TOL, rel
+    bad = np.abs(y - ref) > APPLY_TOL * mag + 1e-30
+    assert not bad.any(), (np.argwhere(bad)[:5], y[bad][:5], ref[bad][:5])
+    return rel
+
+
+def _check_spmv(batch, solver, x):
+    y = solver.spmv(x.reshape(-1)).cpu().numpy().astype(np.float64)
+    ref = oracle.spmv(batch.row_ptr, batch.col, batch.val, x.reshape(-1))
+    mag = oracle.spmv(batch.row_ptr, batch.col, np.abs(batch.val), np.abs(x.reshape(-1)))
+    rel = np.linalg.norm(y - ref) / np.linalg.norm(ref)
+    assert rel <= APPLY_TOL, rel
+    bad = np.abs(y - ref) > APPLY_TOL * mag + 1e-30
+    assert not bad.any(), (np.argwhere(bad)[:5],)
+    return rel
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_spmv_parity(cfg, name):
+    batch = cfg(name)
+    _log(f"spmv parity {name}")
+    s = _solver(batch)
+    x = np.random.default_rng(11).standard_normal((batch.batch, batch.n)).astype(np.float32)
+    _check_spmv(batch, s, x)
+    s.close()
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_apply_parity(cfg, name):
+    batch = cfg(name)
+    _log(f"apply parity {name}")
+    s = _solver(batch)
+    r = np.random.default_rng(12).standard_normal((batch.batch, batch.n)).astype(np.float32)
+    _check_apply(batch, s, r)
+    # a second call with another vector reuses the same scratch
+    _check_apply(batch, s, (r[:, ::-1] * 0.5).copy())
+    s.close()
+
+
+@pytest.mark.parametrize("n,levels,batch", [(128, 0, 1), (256, 1, 1), (512, 1, 1), (1024, 2, 1),
+                                            (2048, 4, 3), (4096, 0, 2), (256, 1, 5)])
+def test_apply_spmv_small_and_ragged(n, levels, batch):
+    _log(f"apply small n={n} levels={levels} batch={batch}")
+    systems = [random_system(n, seed=100 + s, levels=levels).system(0) for s in range(batch)]
+    b = build_batch(systems, name=f"small{n}_{levels}_{batch}")
+    s = _solver(b)
+    rng = np.random.default_rng(n + levels)
+    r = rng.standard_normal((batch, n)).astype(np.float32)
+    _check_apply(b, s, r)
+    _check_spmv(b, s, r)
+    z = np.zeros((batch, n), dtype=np.float32)
+    assert not s.apply_M(z.reshape(-1)).any().item()
+    s.close()
+
+
+def _check_solve(batch, res, refs):
+    for i, ref in enumerate(refs):
+        sy = batch.system(i)
+        assert res.system_status[i] == hpcg.HPCG_SYS_CONVERGED, (i, res.system_status[i])
+        assert ref.status == "converged"
+        assert abs(res.iterations[i] - ref.iterations) <= ITER_TOL, (i, res.iterations[i], ref.iterations)
+        assert res.relres[i] <= batch.tol
+        x = res.x[i].cpu().numpy()
+        tr = oracle.true_relres(sy.row_ptr, sy.col, sy.val, sy.b, x)
+        assert tr <= 1.05 * batch.tol, (i, tr)
+
+
+@pytest.mark.parametrize("engine", [hpcg.HPCG_ENGINE_PERSISTENT, hpcg.HPCG_ENGINE_GRAPH])
+@pytest.mark.parametrize("name", NAMES)
+def test_solve_parity(cfg, oracle_solves, name, engine):
+    batch = cfg(name)
+    _log(f"solve parity {name} engine={engine}")
+    refs = oracle_solves(batch)
+    s = _solver(batch)
+    s.set_option(hpcg.HPCG_OPT_ENGINE, engine)
+    res = s.solve(batch.b.reshape(-1), tol=batch.tol, maxit=batch.maxit)
+    assert s.last_engine == engine
+    assert res.status == hpcg.HPCG_OK, (res.status, hpcg.hpcg_last_error(s.handle))
+    _check_solve(batch, res, refs)
+    s.close()
+
+
+def test_persistent_streaming_matches_resident(cfg):
+    batch = cfg("N8k")
+    _log("persistent streaming vs resident N8k")
+    s = _solver(batch)
+    s.set_option(hpcg.HPCG_OPT_ENGINE, hpcg.HPCG_ENGINE_PERSISTENT)
+    a = s.solve(batch.b.reshape(-1))
+    s.set_option(hpcg.HPCG_OPT_RESIDENT, 0)
+    b = s.solve(batch.b.reshape(-1))
+    assert a.iterations == b.iterations
+    assert torch.equal(a.x, b.x)
+    s.close()
+
+
+def test_engines_agree_bitwise(cfg):
+    batch = cfg("N1k")
+    _log("graph vs persistent bitwise N1k")
+    s = _solver(batch)
+    out = []
+    for eng in (hpcg.HPCG_ENGINE_GRAPH, hpcg.HPCG_ENGINE_PERSISTENT, hpcg.HPCG_ENGINE_GRAPH):
+        s.set_option(hpcg.HPCG_OPT_ENGINE, eng)
+        out.append(s.solve(batch.b.reshape(-1)))
+    for o in out[1:]:
+        assert o.iterations == out[0].iterations
+        assert torch.equal(o.x, out[0].x)
+    s.close()
+
+
+@pytest.mark.parametrize("unroll", [1, 3, 8])
+def test_graph_unroll_independent(cfg, unroll):
+    batch = cfg("tet4k")
+    _log(f"graph unroll {unroll}")
+    s = _solver(batch)
+    s.set_option(hpcg.HPCG_OPT_ENGINE, hpcg.HPCG_ENGINE_GRAPH)
+    s.set_option(hpcg.HPCG_OPT_GRAPH_UNROLL, unroll)
+    res = s.solve(batch.b.reshape(-1))
+    s.set_option(hpcg.HPCG_OPT_ENGINE, hpcg.HPCG_ENGINE_PERSISTENT)
+    ref = s.solve(batch.b.reshape(-1))
+    assert res.iterations == ref.iterations
+    assert torch.equal(res.x, ref.x)
+    s.close()
+
+
+def test_identity_preconditioner_is_plain_cg(cfg):
+    batch = cfg("N1k")
+    _log("identity preconditioner")
+    sy = batch.system(0)
+    U = np.broadcast_to(np.eye(128, dtype=np.float32), batch.U.shape).copy()
+    W = np.zeros_like(batch.W)
+    g = np.zeros_like(batch.g)
+    s = _solver(batch)
+    s.set_factors(U, W, g)
+    res = s.solve(batch.b.reshape(-1), tol=1e-6, maxit=2000)
+    ref = oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b, lambda v: v.copy(), 1e-6, 2000)
+    assert res.status == hpcg.HPCG_OK
+    assert abs(res.iterations[0] - ref.iterations) <= ITER_TOL
+    s.close()
+
+
+def test_format_exact_inverse_converges_at_once():
+    _log("format-exact block-diagonal inverse")
+    # block-diagonal SPD A (in-leaf couplings only), U_k = chol(A_kk)^{-T}: M = A^{-1}
+    b = random_system(1024, seed=21)
+    sy = b.system(0)
+    A = oracle.dense_A(sy.row_ptr, sy.col, sy.val)
+    K, L = 8, 128
+    Ab = np.zeros_like(A)
+    U = np.zeros((1, K, L, L), dtype=np.float32)
+    for k in range(K):
+        sl = slice(k * L, (k + 1) * L)
+        Ab[sl, sl] = A[sl, sl]
+        U[0, k] = np.linalg.inv(np.linalg.cholesky(A[sl, sl])).T
+    import scipy.sparse
+    S = scipy.sparse.csr_matrix(Ab.astype(np.float32))
+    S.sort_indices()
+    s = hpcg.Solver(1024, S.indptr.astype(np.int32), S.indices.astype(np.int32), S.data, levels=3)
+    s.set_factors(U, np.zeros((1, 3, K, L, 32), np.float32), np.zeros((1, 1024), np.float32))
+    res = s.solve(sy.b, tol=1e-5, maxit=50)
+    assert res.status == hpcg.HPCG_OK and res.iterations[0] <= 2, res
+    s.close()
+
+
+def test_scale_invariance_exact(cfg):
+    # scaling U and W by 2 and g by 4 scales M by exactly 4: every iterate is bitwise equal
+    batch = cfg("N1k")
+    _log("scale invariance")
+    s = _solver(batch)
+    a = s.solve(batch.b.reshape(-1))
+    s.set_factors(2 * batch.U, 2 * batch.W, 4 * batch.g)
+    b = s.solve(batch.b.reshape(-1))
+    assert a.iterations == b.iterations
+    assert torch.equal(a.x, b.x)
+    s.close()
+
+
+@pytest.mark.parametrize("engine", [hpcg.HPCG_ENGINE_PERSISTENT, hpcg.HPCG_ENGINE_GRAPH])
+def test_edge_outcomes(cfg, engine):
+    batch = cfg("N1k")
+    _log(f"edge outcomes engine={engine}")
+    sy = batch.system(0)
+    s = _solver(batch)
+    s.set_option(hpcg.HPCG_OPT_ENGINE, engine)
+    # maxit = 1: one step, not converged, x = alpha z0 as in the oracle
+    one = s.solve(batch.b.reshape(-1), maxit=1)
+    ref1 = oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b, (sy.U, sy.W, sy.g), 1e-6, 1)
+    assert one.status == hpcg.HPCG_ERR_NOT_CONVERGED and one.iterations == [1]
+    assert one.system_status == [hpcg.HPCG_SYS_NOT_CONVERGED]
+    x1 = one.x[0].cpu().numpy()
+    assert np.linalg.norm(x1 - ref1.x) <= 1e-5 * np.linalg.norm(ref1.x)
+    assert abs(one.relres[0] - ref1.relres) <= 1e-5 * ref1.relres
+    # zero right-hand side: converged at once with x = 0
+    zero = s.solve(np.zeros(batch.n, np.float32))
+    assert zero.status == hpcg.HPCG_OK and zero.iterations == [0] and not zero.x.any().item()
+    # an indefinite M breaks down at the first r.Mr
+    s.set_factors(0 * batch.U, 0 * batch.W, np.full_like(batch.g, -10.0))
+    bad = s.solve(batch.b.reshape(-1))
+    assert bad.status == hpcg.HPCG_ERR_BREAKDOWN
+    assert bad.system_status == [hpcg.HPCG_SYS_BREAKDOWN] and bad.iterations == [0]
+    s.close()
+
+
+def test_batch_mixed_outcomes():
+    _log("batch mixed outcomes")
+    b = make_config("batch64x2k", batch=3)
+    b.b[1] = 0.0                      # system 1: zero rhs
+    s = _solver(b)
+    res = s.solve(b.b.reshape(-1))
+    refs = oracle.pcg_batch(b)
+    assert res.status == hpcg.HPCG_OK
+    assert res.iterations[1] == 0
+    for i in (0, 2):
+        assert abs(res.iterations[i] - refs[i].iterations) <= ITER_TOL
+    s.close()
+
+
+def test_deterministic(cfg):
+    batch = cfg("N16k")
+    _log("determinism N16k")
+    s = _solver(batch)
+    a = s.solve(batch.b.reshape(-1))
+    b = s.solve(batch.b.reshape(-1))
+    assert a.iterations == b.iterations and torch.equal(a.x, b.x)
+    s.close()
+
+
+def test_set_values_refreshes_matrix(cfg):
+    batch = cfg("N1k")
+    _log("set_values")
+    s = _solver(batch)
+    x = np.random.default_rng(3).standard_normal(batch.n).astype(np.float32)
+    s.set_values(batch.val * 2)
+    y = s.spmv(x).cpu().numpy()
+    ref = oracle.spmv(batch.row_ptr, batch.col, batch.val * 2, x)
+    assert np.linalg.norm(y - ref) <= APPLY_TOL * np.linalg.norm(ref)
+    s.close()
+
+
+def test_argument_errors(cfg):
+    batch = cfg("N1k")
+    _log("argument errors")
+    s = _solver(batch)
+    with pytest.raises(hpcg.HPCGError):
+        s.solve(batch.b.reshape(-1), tol=0.0)
+    with pytest.raises(hpcg.HPCGError):
+        s.solve(batch.b.reshape(-1), maxit=0)
+    with pytest.raises(hpcg.HPCGError):
+        s.set_option(hpcg.HPCG_OPT_GRAPH_UNROLL, 0)
+    with pytest.raises(ValueError):
+        s.apply_M(np.zeros(batch.n + 1, np.float32))
+    s.close()
+    # a column index outside its system is rejected at create time
+    bad_col = batch.col.copy()
+    bad_col[5] = batch.n + 3
+    with pytest.raises(hpcg.HPCGError):
+        hpcg.Solver(batch.n, batch.row_ptr, bad_col, batch.val)
+    # an apply before any factors is a call-order error
+    s2 = hpcg.Solver(batch.n, batch.row_ptr, batch.col, batch.val)
+    with pytest.raises(hpcg.HPCGError):
+        s2.apply_M(np.zeros(batch.n, np.float32))
+    s2.close()
