@@ -106,9 +106,17 @@ typedef enum {
 typedef enum {
     HPCG_OPT_ENGINE = 1,        /* an hpcg_engine value                          */
     HPCG_OPT_GRAPH_UNROLL = 2,  /* iterations per graph replay, 1 .. 64 (default 8) */
-    HPCG_OPT_RESIDENT = 3       /* persistent engine keeps M in LDS when it fits:
+    HPCG_OPT_RESIDENT = 3,      /* persistent engine keeps M in LDS when it fits:
                                    1 = yes (default), 0 = stream M every iteration */
+    HPCG_OPT_PRECISION = 4      /* an hpcg_precision value                        */
 } hpcg_option;
+
+/* Arithmetic of the solve's vectors (hpcg_set_option(HPCG_OPT_PRECISION, ...)).
+ * Factors and matrix values are fp32 and scalars and x are fp64 in both modes. */
+typedef enum {
+    HPCG_PREC_VEC64 = 0,        /* r, z, p, q and every accumulation in fp64 (default) */
+    HPCG_PREC_VEC32 = 1         /* the pages' split: fp32 vectors and apply arithmetic */
+} hpcg_precision;
 
 /* Bytes of device workspace hpcg_create needs for this partition and a CSR of
  * nnz_total stored entries (all systems together).  Returns 0 when the
@@ -125,8 +133,9 @@ size_t hpcg_workspace_bytes(const hpcg_partition* part, int64_t nnz_total);
  *  d_workspace at least hpcg_workspace_bytes(part, nnz_total) bytes.
  *  stream      a hipStream_t, or NULL for the null stream.
  *  out         receives the handle; untouched on error.
- * The CSR is copied into the workspace (stream-ordered).  The row pointer is
- * checked on the host after one synchronous copy; column indices are trusted. */
+ * The CSR is copied into the workspace (stream-ordered), then copied back once
+ * (synchronously) so the host can check the row pointer and that every column
+ * index stays inside its system's block: HPCG_ERR_SHAPE otherwise. */
 hpcg_status hpcg_create(const hpcg_partition* part, const int32_t* d_row_ptr,
                         const int32_t* d_col, const float* d_val, int64_t nnz_total,
                         void* d_workspace, size_t ws_bytes, void* stream,
@@ -165,7 +174,8 @@ hpcg_status hpcg_spmv(hpcg_handle h, const float* d_x, float* d_y);
  *  h_iters  int32 [batch] or NULL: products q = A p done when the test passed
  *           (maxit when not converged; the iteration of the failure on breakdown)
  *  h_relres float64 [batch] or NULL: ||r||/||b|| of the recursive residual at exit
- * Vectors are fp32, scalars (dot products, norms, step sizes) fp64, x fp64.
+ * Scalars (dot products, norms, step sizes) and x are fp64; vectors follow
+ * HPCG_OPT_PRECISION.
  * Returns HPCG_OK when every system converged, HPCG_ERR_BREAKDOWN when any
  * system broke down, else HPCG_ERR_NOT_CONVERGED when any system ran out of
  * iterations.  Synchronizes the handle's stream before returning. */
@@ -180,6 +190,10 @@ hpcg_status hpcg_set_option(hpcg_handle h, int32_t option, int32_t value);
 
 /* Engine the last hpcg_solve actually ran (an hpcg_engine value), or 0. */
 int32_t hpcg_last_engine(hpcg_handle h);
+
+/* Launch shape of the last persistent solve: *grid workgroups, and whether the
+ * factors were LDS-resident (*resident = 1).  Either pointer may be NULL. */
+hpcg_status hpcg_last_launch_info(hpcg_handle h, int32_t* grid, int32_t* resident);
 
 /* Static text for a status code. */
 const char* hpcg_status_string(hpcg_status s);

@@ -67,14 +67,15 @@ Layout make_layout(const Geom& G, int64_t nnz) {
   L.W = take((size_t)G.B * G.levels * G.K * LEAF * RANK * 4);
   L.g = take(N * 4);
   L.b = take(N * 4);
-  L.r = take(N * 4);
-  L.z = take(N * 4);
-  L.q = take(N * 4);
-  L.p0 = take(N * 4);
-  L.p1 = take(N * 4);
+  // solve vectors and restriction partials are sized for the fp64 vector mode
+  L.r = take(N * 8);
+  L.z = take(N * 8);
+  L.q = take(N * 8);
+  L.p0 = take(N * 8);
+  L.p1 = take(N * 8);
   L.x = take(N * 8);
-  L.tpart = take((size_t)G.B * G.K * G.bpl * LEAF * 4);
-  L.ppart = take((size_t)G.B * G.levels * G.K * G.bpl * RANK * 4 + 4);
+  L.tpart = take((size_t)G.B * G.K * G.bpl * LEAF * 8);
+  L.ppart = take((size_t)G.B * G.levels * G.K * G.bpl * RANK * 8 + 8);
   L.pq = take((size_t)G.nblk * 8);
   L.rr = take((size_t)G.nblk * 8);
   L.rz = take((size_t)G.nblk * 8);
@@ -101,6 +102,7 @@ struct hpcg_ctx {
   int engine_opt = HPCG_ENGINE_AUTO;
   int unroll = 8;
   int resident = 1;
+  int prec = HPCG_PREC_VEC64;
   int last_engine = 0;
   int num_cu = 0;
   int coop = 0;
@@ -108,8 +110,11 @@ struct hpcg_ctx {
   hipGraph_t graph = nullptr;
   hipGraphExec_t gexec = nullptr;
   int graph_unroll = 0;
+  int graph_prec = -1;
   double graph_tol = -1.0;
   int graph_maxit = -1;
+  int last_resident = 0;
+  int last_grid = 0;
   int* h_flag = nullptr;   // pinned, device-mapped
   int* d_flag = nullptr;
   SysState* h_st = nullptr;
@@ -146,6 +151,9 @@ size_t res_lds_bytes(const Geom& G) {
   return ((size_t)G.RB * LEAF + (size_t)G.levels * G.RB * RANK) * sizeof(float);
 }
 
+// Clear the HIP runtime's sticky last error after a call whose failure we handle.
+void clear_hip_error() { (void)hipGetLastError(); }
+
 void destroy_graph(hpcg_ctx* h) {
   if (h->gexec) (void)hipGraphExecDestroy(h->gexec);
   if (h->graph) (void)hipGraphDestroy(h->graph);
@@ -154,15 +162,16 @@ void destroy_graph(hpcg_ctx* h) {
   h->graph_unroll = 0;
 }
 
+template <typename T>
 hpcg_status build_graph(hpcg_ctx* h) {
   destroy_graph(h);
   const Geom G = h->G;
   const Bufs B = h->B;
   HIP_OR_FAIL(h, hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal));
   for (int j = 0; j < h->unroll; ++j) {
-    hipLaunchKernelGGL(k_phase_A, dim3(G.nblk), dim3(NT), 0, h->cap_stream, G, B, j);
-    hipLaunchKernelGGL(k_phase_B, dim3(G.nblk), dim3(NT), 0, h->cap_stream, G, B, j);
-    hipLaunchKernelGGL(k_phase_C, dim3(G.nblk), dim3(NT), 0, h->cap_stream, G, B, j, -1);
+    hipLaunchKernelGGL(k_phase_A<T>, dim3(G.nblk), dim3(NT), 0, h->cap_stream, G, B, j);
+    hipLaunchKernelGGL(k_phase_B<T>, dim3(G.nblk), dim3(NT), 0, h->cap_stream, G, B, j);
+    hipLaunchKernelGGL(k_phase_C<T>, dim3(G.nblk), dim3(NT), 0, h->cap_stream, G, B, j, -1);
   }
   hipLaunchKernelGGL(k_advance, dim3(1), dim3(64), 0, h->cap_stream, G, B, h->unroll, h->d_flag);
   hipError_t e = hipStreamEndCapture(h->cap_stream, &h->graph);
@@ -170,24 +179,27 @@ hpcg_status build_graph(hpcg_ctx* h) {
   e = hipGraphInstantiate(&h->gexec, h->graph, nullptr, nullptr, 0);
   if (e != hipSuccess) return hip_fail(h, e, "hipGraphInstantiate");
   h->graph_unroll = h->unroll;
+  h->graph_prec = h->prec;
   h->graph_tol = B.tol;
   h->graph_maxit = B.maxit;
   return HPCG_OK;
 }
 
+template <typename T>
 hpcg_status run_graph(hpcg_ctx* h) {
   const Geom G = h->G;
   const Bufs B = h->B;
-  if (!h->gexec || h->graph_unroll != h->unroll || h->graph_tol != B.tol || h->graph_maxit != B.maxit) {
-    hpcg_status s = build_graph(h);
+  if (!h->gexec || h->graph_unroll != h->unroll || h->graph_prec != h->prec || h->graph_tol != B.tol ||
+      h->graph_maxit != B.maxit) {
+    hpcg_status s = build_graph<T>(h);
     if (s != HPCG_OK) return s;
   }
+  __atomic_store_n(h->h_flag, 0, __ATOMIC_RELEASE);
   hipLaunchKernelGGL(k_reset, dim3(1), dim3(64), 0, h->stream, B, 1, h->d_flag);
-  hipLaunchKernelGGL(k_init, dim3(G.nblk), dim3(NT), 0, h->stream, G, B);
-  hipLaunchKernelGGL(k_phase_C, dim3(G.nblk), dim3(NT), 0, h->stream, G, B, 0, 0);
+  hipLaunchKernelGGL(k_init<T>, dim3(G.nblk), dim3(NT), 0, h->stream, G, B);
+  hipLaunchKernelGGL(k_phase_C<T>, dim3(G.nblk), dim3(NT), 0, h->stream, G, B, 0, 0);
   hpcg_status s = check_launch(h, "graph engine setup launch");
   if (s != HPCG_OK) return s;
-  __atomic_store_n(h->h_flag, 0, __ATOMIC_RELEASE);
   const int max_replays = (B.maxit + h->unroll - 1) / h->unroll;
   const int lookahead = 2;
   int launched = 0, seen = 0;
@@ -220,6 +232,10 @@ hpcg_status run_graph(hpcg_ctx* h) {
   return HPCG_OK;
 }
 
+// Pick the persistent variant that fits: LDS-resident factors with one row
+// block per workgroup when LDS and occupancy allow, otherwise factors streamed
+// from memory with workgroups looping over row blocks.
+template <typename T>
 hpcg_status run_persistent(hpcg_ctx* h, bool& ran) {
   ran = false;
   const Geom G = h->G;
@@ -230,19 +246,20 @@ hpcg_status run_persistent(hpcg_ctx* h, bool& ran) {
   size_t dyn = 0;
   const void* fn = nullptr;
   int grid = 0;
-  if (h->resident && res_lds_bytes(G) + sizeof(Smem) <= h->max_lds) {
+  if (h->resident && res_lds_bytes(G) + sizeof(Smem<T>) <= h->max_lds) {
     dyn = res_lds_bytes(G);
-    fn = reinterpret_cast<const void*>(&k_persistent<true>);
-    HIP_OR_FAIL(h, hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn));
-    HIP_OR_FAIL(h, hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NT, dyn));
-    if ((int64_t)per_cu * h->num_cu >= G.nblk) {
+    fn = reinterpret_cast<const void*>(&k_persistent<T, true>);
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NT, dyn) == hipSuccess &&
+        (int64_t)per_cu * h->num_cu >= G.nblk) {
       res = true;
       grid = G.nblk;
     }
+    clear_hip_error();
   }
   if (!res) {
     dyn = 0;
-    fn = reinterpret_cast<const void*>(&k_persistent<false>);
+    fn = reinterpret_cast<const void*>(&k_persistent<T, false>);
     HIP_OR_FAIL(h, hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NT, 0));
     const int64_t cap = (int64_t)per_cu * h->num_cu;
     if (cap <= 0) return HPCG_OK;
@@ -253,6 +270,8 @@ hpcg_status run_persistent(hpcg_ctx* h, bool& ran) {
   Bufs Ba = B;
   void* args[] = {&Ga, &Ba};
   HIP_OR_FAIL(h, hipLaunchCooperativeKernel(fn, dim3(grid), dim3(NT), args, (unsigned)dyn, h->stream));
+  h->last_resident = res ? 1 : 0;
+  h->last_grid = grid;
   ran = true;
   return HPCG_OK;
 }
@@ -308,7 +327,9 @@ hpcg_status hpcg_create(const hpcg_partition* part, const int32_t* d_row_ptr, co
   hipDeviceProp_t prop;
   CREATE_HIP(hipGetDeviceProperties(&prop, dev));
   h->num_cu = prop.multiProcessorCount;
-  h->max_lds = prop.sharedMemPerMultiprocessor ? prop.sharedMemPerMultiprocessor : 65536;
+  int max_lds = 0;
+  CREATE_HIP(hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev));
+  h->max_lds = max_lds > 0 ? (size_t)max_lds : 65536;
   int coop = 0;
   CREATE_HIP(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev));
   h->coop = coop;
@@ -328,14 +349,14 @@ hpcg_status hpcg_create(const hpcg_partition* part, const int32_t* d_row_ptr, co
   B.W = reinterpret_cast<const float*>(w + lay.W);
   B.g = reinterpret_cast<const float*>(w + lay.g);
   B.b = reinterpret_cast<const float*>(w + lay.b);
-  B.r = reinterpret_cast<float*>(w + lay.r);
-  B.z = reinterpret_cast<float*>(w + lay.z);
-  B.q = reinterpret_cast<float*>(w + lay.q);
-  B.p0 = reinterpret_cast<float*>(w + lay.p0);
-  B.p1 = reinterpret_cast<float*>(w + lay.p1);
+  B.r = w + lay.r;
+  B.z = w + lay.z;
+  B.q = w + lay.q;
+  B.p0 = w + lay.p0;
+  B.p1 = w + lay.p1;
   B.x = reinterpret_cast<double*>(w + lay.x);
-  B.tpart = reinterpret_cast<float*>(w + lay.tpart);
-  B.ppart = reinterpret_cast<float*>(w + lay.ppart);
+  B.tpart = w + lay.tpart;
+  B.ppart = w + lay.ppart;
   B.pq_part = reinterpret_cast<double*>(w + lay.pq);
   B.rr_part = reinterpret_cast<double*>(w + lay.rr);
   B.rz_part = reinterpret_cast<double*>(w + lay.rz);
@@ -430,15 +451,16 @@ hpcg_status hpcg_solve(hpcg_handle h, const float* d_b, double* d_x, double tol,
   HIP_OR_FAIL(h, hipMemcpyAsync(h->ws + h->lay.b, d_b, N * 4, hipMemcpyDeviceToDevice, h->stream));
   hpcg_status s = HPCG_OK;
   bool ran = false;
+  const bool f32 = (h->prec == HPCG_PREC_VEC32);
   if (h->engine_opt != HPCG_ENGINE_GRAPH) {
-    s = run_persistent(h, ran);
+    s = f32 ? run_persistent<float>(h, ran) : run_persistent<double>(h, ran);
     if (s != HPCG_OK) return s;
     if (!ran && h->engine_opt == HPCG_ENGINE_PERSISTENT)
       return fail(h, HPCG_ERR_SHAPE, "persistent engine: device does not support a co-resident grid for this partition");
     if (ran) h->last_engine = HPCG_ENGINE_PERSISTENT;
   }
   if (!ran) {
-    s = run_graph(h);
+    s = f32 ? run_graph<float>(h) : run_graph<double>(h);
     if (s != HPCG_OK) return s;
     h->last_engine = HPCG_ENGINE_GRAPH;
   }
@@ -485,12 +507,23 @@ hpcg_status hpcg_set_option(hpcg_handle h, int32_t option, int32_t value) {
       if (value != 0 && value != 1) return fail(h, HPCG_ERR_INVALID_ARG, "resident must be 0 or 1");
       h->resident = value;
       return HPCG_OK;
+    case HPCG_OPT_PRECISION:
+      if (value != HPCG_PREC_VEC64 && value != HPCG_PREC_VEC32) return fail(h, HPCG_ERR_INVALID_ARG, "bad precision");
+      h->prec = value;
+      return HPCG_OK;
     default:
       return fail(h, HPCG_ERR_INVALID_ARG, "unknown option");
   }
 }
 
 int32_t hpcg_last_engine(hpcg_handle h) { return h ? h->last_engine : 0; }
+
+hpcg_status hpcg_last_launch_info(hpcg_handle h, int32_t* grid, int32_t* resident) {
+  if (!h) return fail(nullptr, HPCG_ERR_INVALID_ARG, "handle is NULL");
+  if (grid) *grid = h->last_grid;
+  if (resident) *resident = h->last_resident;
+  return HPCG_OK;
+}
 
 const char* hpcg_status_string(hpcg_status s) {
   switch (s) {

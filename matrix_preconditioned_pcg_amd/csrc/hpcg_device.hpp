@@ -17,9 +17,15 @@
 //   C  convergence test on sum r.r;  z = M r from the restriction sums:
 //      z_k = U_k t_k + sum_l W_l[k] P_l[partner half] + g r_k  (eqs. (3)-(5),
 //      coupling core = identity);  partial r.z
-// Scalars are accumulated in fp64, vectors are fp32, x is fp64.  Every sum of
-// partials is evaluated by every workgroup that needs it in one fixed order, so
-// all workgroups agree bit for bit and a solve is deterministic.
+//
+// Precision.  Factors and matrix values are always fp32 (they are the bytes
+// that bound the apply).  The vector type T of the solve is a template
+// parameter: T = float is the pages' split (fp32 vectors and apply arithmetic,
+// fp64 scalars; Supplementary section 7), T = double carries r, z, p, q, the
+// restriction partials and all accumulations in fp64.  Scalars and x are fp64
+// in both.  Every sum of partials is evaluated by every workgroup that needs it
+// in one fixed order, so all workgroups agree bit for bit and a solve is
+// deterministic.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -60,6 +66,8 @@ struct Geom {
   int nblk;      // B * nblk_sys
 };
 
+// Device buffers.  Vector buffers are sized for double; with T = float only the
+// first half of each is used.
 struct Bufs {
   const int* row_ptr;
   const int* col;
@@ -68,14 +76,14 @@ struct Bufs {
   const float* W;      // [B][levels][K][LEAF][RANK]
   const float* g;      // [B*n]
   const float* b;      // [B*n]
-  float* r;
-  float* z;
-  float* q;
-  float* p0;
-  float* p1;
+  void* r;
+  void* z;
+  void* q;
+  void* p0;
+  void* p1;
   double* x;
-  float* tpart;        // [B][K][bpl][LEAF]
-  float* ppart;        // [B][levels][K][bpl][RANK]
+  void* tpart;         // [B][K][bpl][LEAF]
+  void* ppart;         // [B][levels][K][bpl][RANK]
   double* pq_part;     // [nblk]
   double* rr_part;
   double* rz_part;
@@ -88,18 +96,20 @@ struct Bufs {
   int maxit;
 };
 
+template <typename T>
 struct alignas(16) Smem {
-  float r[LEAF];                       // the block's rows of r
-  float t[LEAF];                       // t_k = U_k^T r_k (whole leaf)
-  float P[MAX_LEVELS * RANK];          // partner-half sums per level
+  T r[LEAF];                         // the block's rows of r
+  T t[LEAF];                         // t_k = U_k^T r_k (whole leaf)
+  T P[MAX_LEVELS * RANK];            // partner-half sums per level
   union {
-    float redA[8][LEAF];               // restriction: U partials per row group
-    float redP[8][MAX_LEVELS * RANK];  // prolongation: partner-sum partials
+    struct {
+      T redA[NWAVE][LEAF];           // restriction: U partials per wave
+      T redB[NWAVE][MAX_LEVELS * RANK];  // restriction: slab partials per wave
+    };
+    T redP[NWAVE][MAX_LEVELS * RANK];    // prolongation: partner-sum partials per wave
   };
-  float redB[NWAVE][MAX_LEVELS * RANK];  // restriction: slab partials per wave
-  float redU[LEAF][33];                // prolongation: per-row, per-column-slot dots
-  float yoff[LEAF];
-  float y[LEAF];
+  T yleaf[LEAF];
+  T yoff[LEAF];
   double dred[NWAVE];
   int flag;
 };
@@ -122,16 +132,39 @@ __device__ __forceinline__ Blk decode(const Geom& G, int b) {
   return o;
 }
 
-__device__ __forceinline__ float dot4(float4 a, float4 b) {
-  return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
-}
-
 __device__ __forceinline__ float4 ld4(const float* p) {
   return *reinterpret_cast<const float4*>(p);
 }
 
+template <typename T>
+struct Vec4 { T x, y, z, w; };
+
+template <typename T>
+__device__ __forceinline__ Vec4<T> lds4(const T* p) {
+  Vec4<T> v;
+  v.x = p[0]; v.y = p[1]; v.z = p[2]; v.w = p[3];
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T dot4(float4 a, const Vec4<T>& b) {
+  T s = (T)a.x * b.x;
+  s = fma((T)a.y, b.y, s);
+  s = fma((T)a.z, b.z, s);
+  return fma((T)a.w, b.w, s);
+}
+
+template <typename T>
+__device__ __forceinline__ void axpy4(Vec4<T>& acc, float4 u, T s) {
+  acc.x = fma((T)u.x, s, acc.x);
+  acc.y = fma((T)u.y, s, acc.y);
+  acc.z = fma((T)u.z, s, acc.z);
+  acc.w = fma((T)u.w, s, acc.w);
+}
+
 // Sum over the whole workgroup in a fixed tree order (deterministic).
-__device__ __forceinline__ double wg_sum(double v, Smem& sm) {
+template <typename T>
+__device__ __forceinline__ double wg_sum(double v, Smem<T>& sm) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   const int tid = threadIdx.x;
@@ -145,7 +178,8 @@ __device__ __forceinline__ double wg_sum(double v, Smem& sm) {
 }
 
 // Sum of one system's per-block partials, identical in every workgroup.
-__device__ __forceinline__ double sys_sum(const double* part, int s, int nblk_sys, Smem& sm) {
+template <typename T>
+__device__ __forceinline__ double sys_sum(const double* part, int s, int nblk_sys, Smem<T>& sm) {
   double v = 0.0;
   for (int j = threadIdx.x; j < nblk_sys; j += NT) v += part[(size_t)s * nblk_sys + j];
   return wg_sum(v, sm);
@@ -153,7 +187,8 @@ __device__ __forceinline__ double sys_sum(const double* part, int s, int nblk_sy
 
 // Broadcast a system's status through LDS so the whole workgroup branches alike.
 // Returns ST_RUNNING, a final status, or -1 when a breakdown is pending.
-__device__ __forceinline__ int read_status(const SysState* st, Smem& sm) {
+template <typename T>
+__device__ __forceinline__ int read_status(const SysState* st, Smem<T>& sm) {
   if (threadIdx.x == 0) {
     int v = __hip_atomic_load(&st->status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (v == ST_RUNNING && __hip_atomic_load(&st->brk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) v = -1;
@@ -195,52 +230,57 @@ __device__ __forceinline__ FactorView global_view(const Geom& G, const Bufs& B, 
 // ---------------------------------------------------------------------------
 // Restriction (eq. (2) per leaf and level): from sm.r (block rows) write the
 // block's partial t = U_blk^T r_blk and, for every level, W_l,blk^T r_blk.
+// U: lane = 4-column slot (32 per row), 8 row groups; W: 8 slots per row, 32
+// row groups.  Row groups are summed across lanes, then across waves in LDS.
 // ---------------------------------------------------------------------------
+template <typename T>
 __device__ __forceinline__ void restrict_block(const Geom& G, const Bufs& B, const Blk& bk,
-                                               const FactorView& fv, Smem& sm) {
-  const int tid = threadIdx.x;
+                                               const FactorView& fv, Smem<T>& sm) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int RB = G.RB;
+  T* tpart = reinterpret_cast<T*>(B.tpart);
+  T* ppart = reinterpret_cast<T*>(B.ppart);
   {
     const int cs = tid & 31, rg = tid >> 5;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int i = rg; i < RB; i += 8) {
-      const float4 u = ld4(fv.Ub + (size_t)i * LEAF + 4 * cs);
-      const float ri = sm.r[i];
-      acc.x += u.x * ri; acc.y += u.y * ri; acc.z += u.z * ri; acc.w += u.w * ri;
+    Vec4<T> acc{0, 0, 0, 0};
+    for (int i = rg; i < RB; i += 8) axpy4(acc, ld4(fv.Ub + (size_t)i * LEAF + 4 * cs), sm.r[i]);
+    acc.x += __shfl_xor(acc.x, 32); acc.y += __shfl_xor(acc.y, 32);
+    acc.z += __shfl_xor(acc.z, 32); acc.w += __shfl_xor(acc.w, 32);
+    if (lane < 32) {
+      T* d = &sm.redA[wave][4 * cs];
+      d[0] = acc.x; d[1] = acc.y; d[2] = acc.z; d[3] = acc.w;
     }
-    *reinterpret_cast<float4*>(&sm.redA[rg][4 * cs]) = acc;
   }
   {
-    const int cs = tid & 7, rg = tid >> 3, lane = tid & 63, wave = tid >> 6;
+    const int cs = tid & 7, rg = tid >> 3;
     for (int l = 0; l < G.levels; ++l) {
       const float* Wl = fv.Wb + (size_t)l * fv.wstride;
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int i = rg; i < RB; i += 32) {
-        const float4 w = ld4(Wl + (size_t)i * RANK + 4 * cs);
-        const float ri = sm.r[i];
-        acc.x += w.x * ri; acc.y += w.y * ri; acc.z += w.z * ri; acc.w += w.w * ri;
-      }
+      Vec4<T> acc{0, 0, 0, 0};
+      for (int i = rg; i < RB; i += 32) axpy4(acc, ld4(Wl + (size_t)i * RANK + 4 * cs), sm.r[i]);
 #pragma unroll
       for (int o = 8; o < 64; o <<= 1) {
         acc.x += __shfl_xor(acc.x, o); acc.y += __shfl_xor(acc.y, o);
         acc.z += __shfl_xor(acc.z, o); acc.w += __shfl_xor(acc.w, o);
       }
-      if (lane < 8) *reinterpret_cast<float4*>(&sm.redB[wave][l * RANK + 4 * cs]) = acc;
+      if (lane < 8) {
+        T* d = &sm.redB[wave][l * RANK + 4 * cs];
+        d[0] = acc.x; d[1] = acc.y; d[2] = acc.z; d[3] = acc.w;
+      }
     }
   }
   __syncthreads();
   if (tid < LEAF) {
-    float s = 0.f;
+    T s = sm.redA[0][tid];
 #pragma unroll
-    for (int g = 0; g < 8; ++g) s += sm.redA[g][tid];
-    B.tpart[(((size_t)bk.s * G.K + bk.k) * G.bpl + bk.sub) * LEAF + tid] = s;
+    for (int w = 1; w < NWAVE; ++w) s += sm.redA[w][tid];
+    tpart[(((size_t)bk.s * G.K + bk.k) * G.bpl + bk.sub) * LEAF + tid] = s;
   }
   for (int e = tid; e < G.levels * RANK; e += NT) {
-    float s = sm.redB[0][e];
+    T s = sm.redB[0][e];
 #pragma unroll
     for (int w = 1; w < NWAVE; ++w) s += sm.redB[w][e];
     const int l = e / RANK, c = e - l * RANK;
-    B.ppart[((((size_t)bk.s * G.levels + l) * G.K + bk.k) * G.bpl + bk.sub) * RANK + c] = s;
+    ppart[((((size_t)bk.s * G.levels + l) * G.K + bk.k) * G.bpl + bk.sub) * RANK + c] = s;
   }
   __syncthreads();
 }
@@ -248,17 +288,20 @@ __device__ __forceinline__ void restrict_block(const Geom& G, const Bufs& B, con
 // ---------------------------------------------------------------------------
 // Prolongation and assembly of y = M r on the block's rows (eqs. (3)-(5) and
 // the diagonal stage), reading the restriction partials of every block of the
-// system.  Needs sm.r; leaves y in sm.y[0..RB).
+// system.  Needs sm.r; returns y for row tid (tid < RB).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void prolong_block(const Geom& G, const Bufs& B, const Blk& bk,
-                                              const FactorView& fv, Smem& sm) {
-  const int tid = threadIdx.x;
+template <typename T>
+__device__ __forceinline__ T prolong_block(const Geom& G, const Bufs& B, const Blk& bk,
+                                           const FactorView& fv, Smem<T>& sm) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int RB = G.RB;
+  const T* tpart = reinterpret_cast<const T*>(B.tpart);
+  const T* ppart = reinterpret_cast<const T*>(B.ppart);
   // t_k: sum of the leaf's block partials
   if (tid < LEAF) {
-    const float* tp = B.tpart + ((size_t)bk.s * G.K + bk.k) * G.bpl * LEAF + tid;
-    float s = 0.f;
-    for (int j = 0; j < G.bpl; ++j) s += tp[(size_t)j * LEAF];
+    const T* tp = tpart + ((size_t)bk.s * G.K + bk.k) * G.bpl * LEAF + tid;
+    T s = tp[0];
+    for (int j = 1; j < G.bpl; ++j) s += tp[(size_t)j * LEAF];
     sm.t[tid] = s;
   }
   // strip aggregation: partner-half sums per level (eq. (3))
@@ -267,36 +310,49 @@ __device__ __forceinline__ void prolong_block(const Geom& G, const Bufs& B, cons
     for (int l = 0; l < G.levels; ++l) {
       const int kp0 = ((bk.k >> l) ^ 1) << l;
       const int cnt = (1 << l) * G.bpl;
-      const float* base = B.ppart + (((size_t)bk.s * G.levels + l) * G.K + kp0) * G.bpl * RANK + c;
-      float acc = 0.f;
+      const T* base = ppart + (((size_t)bk.s * G.levels + l) * G.K + kp0) * G.bpl * RANK + c;
+      T acc = 0;
       for (int v = j0; v < cnt; v += 8) acc += base[(size_t)v * RANK];
-      sm.redP[j0][l * RANK + c] = acc;
+      acc += __shfl_xor(acc, 32);
+      if (lane < 32) sm.redP[wave][l * RANK + c] = acc;
     }
   }
   __syncthreads();
   for (int e = tid; e < G.levels * RANK; e += NT) {
-    float s = sm.redP[0][e];
+    T s = sm.redP[0][e];
 #pragma unroll
-    for (int j = 1; j < 8; ++j) s += sm.redP[j][e];
+    for (int w = 1; w < NWAVE; ++w) s += sm.redP[w][e];
     sm.P[e] = s;
   }
   __syncthreads();
-  // diagonal stage: per row, dot of U row and t, split over 32 column slots
+  // diagonal stage: row i's dot with t is split over 32 lanes (4 columns each);
+  // two rows at a time are folded with a transpose-reduce (5 shuffles per pair)
   {
     const int cs = tid & 31, rg = tid >> 5;
-    const float4 t4 = *reinterpret_cast<const float4*>(&sm.t[4 * cs]);
-    for (int i = rg; i < RB; i += 8) sm.redU[i][cs] = dot4(ld4(fv.Ub + (size_t)i * LEAF + 4 * cs), t4);
+    const Vec4<T> t4 = lds4(&sm.t[4 * cs]);
+    const bool hi = (cs & 16) != 0;
+    for (int i0 = rg; i0 < RB; i0 += 16) {
+      const int i1 = i0 + 8;
+      const T v0 = dot4(ld4(fv.Ub + (size_t)i0 * LEAF + 4 * cs), t4);
+      const T v1 = (i1 < RB) ? dot4(ld4(fv.Ub + (size_t)i1 * LEAF + 4 * cs), t4) : T(0);
+      T keep = hi ? v1 : v0;
+      const T send = hi ? v0 : v1;
+      keep += __shfl_xor(send, 16);
+      keep += __shfl_xor(keep, 8);
+      keep += __shfl_xor(keep, 4);
+      keep += __shfl_xor(keep, 2);
+      keep += __shfl_xor(keep, 1);
+      if (cs == 0) sm.yleaf[i0] = keep;
+      if (cs == 16 && i1 < RB) sm.yleaf[i1] = keep;
+    }
   }
   // prolongation (eq. (5)): per row, sum over levels of slab row . P_l
   {
     const int cs = tid & 7, rg = tid >> 3;
     for (int i = rg; i < RB; i += 32) {
-      float acc = 0.f;
-      for (int l = 0; l < G.levels; ++l) {
-        const float4 w = ld4(fv.Wb + (size_t)l * fv.wstride + (size_t)i * RANK + 4 * cs);
-        const float4 p4 = *reinterpret_cast<const float4*>(&sm.P[l * RANK + 4 * cs]);
-        acc += dot4(w, p4);
-      }
+      T acc = 0;
+      for (int l = 0; l < G.levels; ++l)
+        acc += dot4(ld4(fv.Wb + (size_t)l * fv.wstride + (size_t)i * RANK + 4 * cs), lds4(&sm.P[l * RANK + 4 * cs]));
       acc += __shfl_xor(acc, 1);
       acc += __shfl_xor(acc, 2);
       acc += __shfl_xor(acc, 4);
@@ -304,33 +360,31 @@ __device__ __forceinline__ void prolong_block(const Geom& G, const Bufs& B, cons
     }
   }
   __syncthreads();
-  if (tid < RB) {
-    float s = 0.f;
-#pragma unroll
-    for (int c = 0; c < 32; ++c) s += sm.redU[tid][c];
-    const int grow = bk.grow0 + tid;
-    sm.y[tid] = s + sm.yoff[tid] + B.g[grow] * sm.r[tid];
-  }
-  __syncthreads();
+  T y = 0;
+  if (tid < RB) y = sm.yleaf[tid] + sm.yoff[tid] + (T)B.g[bk.grow0 + tid] * sm.r[tid];
+  return y;
 }
 
 // p_new = z + beta p_old, evaluated identically wherever it is needed so that
 // the stored p and the p the SpMV multiplies are the same numbers.
-__device__ __forceinline__ float pdir(float z, float pold, double beta) {
-  return (float)((double)z + beta * (double)pold);
+template <typename T>
+__device__ __forceinline__ T pdir(T z, T pold, double beta) {
+  return (T)((double)z + beta * (double)pold);
 }
 
 // ---------------------------------------------------------------------------
 // Phases.  b = global block index; it = iteration (1-based; 0 = initial apply).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void phase_init(const Geom& G, const Bufs& B, int b, const FactorView& fv, Smem& sm) {
+template <typename T>
+__device__ __forceinline__ void phase_init(const Geom& G, const Bufs& B, int b, const FactorView& fv, Smem<T>& sm) {
   const Blk bk = decode(G, b);
   const int tid = threadIdx.x;
+  T* r = reinterpret_cast<T*>(B.r);
   double loc = 0.0;
   if (tid < G.RB) {
     const int grow = bk.grow0 + tid;
-    const float bv = B.b[grow];
-    B.r[grow] = bv;
+    const T bv = (T)B.b[grow];
+    r[grow] = bv;
     B.x[grow] = 0.0;
     sm.r[tid] = bv;
     loc = (double)bv * (double)bv;
@@ -350,7 +404,8 @@ __device__ __forceinline__ void phase_init(const Geom& G, const Bufs& B, int b, 
   }
 }
 
-__device__ __forceinline__ void phase_A(const Geom& G, const Bufs& B, int b, int it, Smem& sm) {
+template <typename T>
+__device__ __forceinline__ void phase_A(const Geom& G, const Bufs& B, int b, int it, Smem<T>& sm) {
   const Blk bk = decode(G, b);
   SysState* st = B.st + bk.s;
   if (read_status(st, sm) != ST_RUNNING) return;
@@ -363,33 +418,36 @@ __device__ __forceinline__ void phase_A(const Geom& G, const Bufs& B, int b, int
   double beta = 0.0;
   if (it > 1) beta = rz / st->rz[(it - 2) & 1];
   if (tid == 0 && bk.lb == 0) st->rz[(it - 1) & 1] = rz;
-  const float* pold = (it & 1) ? B.p0 : B.p1;
-  float* pnew = (it & 1) ? B.p1 : B.p0;
+  const T* z = reinterpret_cast<const T*>(B.z);
+  const T* pold = reinterpret_cast<const T*>((it & 1) ? B.p0 : B.p1);
+  T* pnew = reinterpret_cast<T*>((it & 1) ? B.p1 : B.p0);
+  T* q = reinterpret_cast<T*>(B.q);
   const bool first = (it == 1);
   // SpMV on the fly of p_new: TPR threads per row
   const int TPR = NT / G.RB;
   const int i = tid / TPR, lr = tid - i * TPR;
   const int grow = bk.grow0 + i;
   const int e0 = B.row_ptr[grow], e1 = B.row_ptr[grow + 1];
-  float acc = 0.f;
+  T acc = 0;
   for (int e = e0 + lr; e < e1; e += TPR) {
     const int c = B.col[e];
-    const float v = first ? B.z[c] : pdir(B.z[c], pold[c], beta);
-    acc = fmaf(B.val[e], v, acc);
+    const T v = first ? z[c] : pdir<T>(z[c], pold[c], beta);
+    acc = fma((T)B.val[e], v, acc);
   }
   for (int o = 1; o < TPR; o <<= 1) acc += __shfl_xor(acc, o);
   double loc = 0.0;
   if (lr == 0) {
-    const float pn = first ? B.z[grow] : pdir(B.z[grow], pold[grow], beta);
+    const T pn = first ? z[grow] : pdir<T>(z[grow], pold[grow], beta);
     pnew[grow] = pn;
-    B.q[grow] = acc;
+    q[grow] = acc;
     loc = (double)pn * (double)acc;
   }
   const double pq = wg_sum(loc, sm);
   if (tid == 0) B.pq_part[b] = pq;
 }
 
-__device__ __forceinline__ void phase_B(const Geom& G, const Bufs& B, int b, int it, const FactorView& fv, Smem& sm) {
+template <typename T>
+__device__ __forceinline__ void phase_B(const Geom& G, const Bufs& B, int b, int it, const FactorView& fv, Smem<T>& sm) {
   const Blk bk = decode(G, b);
   SysState* st = B.st + bk.s;
   if (read_status(st, sm) != ST_RUNNING) return;
@@ -400,12 +458,14 @@ __device__ __forceinline__ void phase_B(const Geom& G, const Bufs& B, int b, int
     return;
   }
   const double alpha = st->rz[(it - 1) & 1] / pq;
-  const float* pnew = (it & 1) ? B.p1 : B.p0;
+  const T* pnew = reinterpret_cast<const T*>((it & 1) ? B.p1 : B.p0);
+  const T* q = reinterpret_cast<const T*>(B.q);
+  T* r = reinterpret_cast<T*>(B.r);
   double loc = 0.0;
   if (tid < G.RB) {
     const int grow = bk.grow0 + tid;
-    const float rn = (float)((double)B.r[grow] - alpha * (double)B.q[grow]);
-    B.r[grow] = rn;
+    const T rn = (T)((double)r[grow] - alpha * (double)q[grow]);
+    r[grow] = rn;
     B.x[grow] += alpha * (double)pnew[grow];
     sm.r[tid] = rn;
     loc = (double)rn * (double)rn;
@@ -416,7 +476,8 @@ __device__ __forceinline__ void phase_B(const Geom& G, const Bufs& B, int b, int
   if (tid == 0) B.rr_part[b] = rr;
 }
 
-__device__ __forceinline__ void phase_C(const Geom& G, const Bufs& B, int b, int it, const FactorView& fv, Smem& sm) {
+template <typename T>
+__device__ __forceinline__ void phase_C(const Geom& G, const Bufs& B, int b, int it, const FactorView& fv, Smem<T>& sm) {
   const Blk bk = decode(G, b);
   SysState* st = B.st + bk.s;
   const int tid = threadIdx.x;
@@ -446,13 +507,14 @@ __device__ __forceinline__ void phase_C(const Geom& G, const Bufs& B, int b, int
       return;
     }
   }
-  if (tid < G.RB) sm.r[tid] = B.r[bk.grow0 + tid];
+  const T* r = reinterpret_cast<const T*>(B.r);
+  T* z = reinterpret_cast<T*>(B.z);
+  if (tid < G.RB) sm.r[tid] = r[bk.grow0 + tid];
   __syncthreads();
-  prolong_block(G, B, bk, fv, sm);
+  const T zv = prolong_block(G, B, bk, fv, sm);
   double loc = 0.0;
   if (tid < G.RB) {
-    const float zv = sm.y[tid];
-    B.z[bk.grow0 + tid] = zv;
+    z[bk.grow0 + tid] = zv;
     loc = (double)sm.r[tid] * (double)zv;
   }
   const double rz = wg_sum(loc, sm);

@@ -50,25 +50,29 @@ __device__ __forceinline__ bool grid_barrier(unsigned* ctr, int* abort_flag, uns
 // ---------------------------------------------------------------------------
 // graph-engine kernels (one workgroup per row block)
 // ---------------------------------------------------------------------------
+template <typename T>
 __global__ __launch_bounds__(NT) void k_init(Geom G, Bufs B) {
-  __shared__ Smem sm;
+  __shared__ Smem<T> sm;
   const int b = blockIdx.x;
   phase_init(G, B, b, global_view(G, B, decode(G, b)), sm);
 }
 
+template <typename T>
 __global__ __launch_bounds__(NT) void k_phase_A(Geom G, Bufs B, int off) {
-  __shared__ Smem sm;
+  __shared__ Smem<T> sm;
   phase_A(G, B, blockIdx.x, *B.itbase + off, sm);
 }
 
+template <typename T>
 __global__ __launch_bounds__(NT) void k_phase_B(Geom G, Bufs B, int off) {
-  __shared__ Smem sm;
+  __shared__ Smem<T> sm;
   const int b = blockIdx.x;
   phase_B(G, B, b, *B.itbase + off, global_view(G, B, decode(G, b)), sm);
 }
 
+template <typename T>
 __global__ __launch_bounds__(NT) void k_phase_C(Geom G, Bufs B, int off, int absolute) {
-  __shared__ Smem sm;
+  __shared__ Smem<T> sm;
   const int b = blockIdx.x;
   const int it = absolute >= 0 ? absolute : *B.itbase + off;
   phase_C(G, B, b, it, global_view(G, B, decode(G, b)), sm);
@@ -103,12 +107,12 @@ __global__ void k_reset(Bufs B, int itbase, int* host_flag) {
 // ---------------------------------------------------------------------------
 // RES: each workgroup owns exactly one row block and copies its rows of U_k and
 // of the level slabs into dynamic LDS once; every later apply reads them there.
-template <bool RES>
+template <typename T, bool RES>
 __global__ __launch_bounds__(NT) void k_persistent(Geom G, Bufs B) {
-  __shared__ Smem sm;
+  __shared__ Smem<T> sm;
   extern __shared__ float4 dyn4[];
   unsigned target = 0;
-  FactorView fres;
+  FactorView fres{};
   if constexpr (RES) {
     const Blk bk = decode(G, blockIdx.x);
     const FactorView gv = global_view(G, B, bk);
@@ -151,14 +155,11 @@ __global__ __launch_bounds__(NT) void k_persistent(Geom G, Bufs B) {
   }
 }
 
-template __global__ void k_persistent<true>(Geom, Bufs);
-template __global__ void k_persistent<false>(Geom, Bufs);
-
 // ---------------------------------------------------------------------------
 // standalone apply and SpMV
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(NT) void k_apply_restrict(Geom G, Bufs B, const float* __restrict__ rin) {
-  __shared__ Smem sm;
+  __shared__ Smem<float> sm;
   const Blk bk = decode(G, blockIdx.x);
   if (threadIdx.x < G.RB) sm.r[threadIdx.x] = rin[bk.grow0 + threadIdx.x];
   __syncthreads();
@@ -167,12 +168,12 @@ __global__ __launch_bounds__(NT) void k_apply_restrict(Geom G, Bufs B, const flo
 
 __global__ __launch_bounds__(NT) void k_apply_prolong(Geom G, Bufs B, const float* __restrict__ rin,
                                                        float* __restrict__ yout) {
-  __shared__ Smem sm;
+  __shared__ Smem<float> sm;
   const Blk bk = decode(G, blockIdx.x);
   if (threadIdx.x < G.RB) sm.r[threadIdx.x] = rin[bk.grow0 + threadIdx.x];
   __syncthreads();
-  prolong_block(G, B, bk, global_view(G, B, bk), sm);
-  if (threadIdx.x < G.RB) yout[bk.grow0 + threadIdx.x] = sm.y[threadIdx.x];
+  const float y = prolong_block(G, B, bk, global_view(G, B, bk), sm);
+  if (threadIdx.x < G.RB) yout[bk.grow0 + threadIdx.x] = y;
 }
 
 // y = A x; SPMV_TPR consecutive lanes share a row and stride over its entries.

@@ -42,6 +42,10 @@ HPCG_ENGINE_PERSISTENT = 2
 HPCG_OPT_ENGINE = 1
 HPCG_OPT_GRAPH_UNROLL = 2
 HPCG_OPT_RESIDENT = 3
+HPCG_OPT_PRECISION = 4
+
+HPCG_PREC_VEC64 = 0
+HPCG_PREC_VEC32 = 1
 
 LEAF = 128
 RANK = 32
@@ -86,6 +90,7 @@ def lib() -> ctypes.CDLL:
         "hpcg_last_solve_status": (i32, [vp, P(i32)]),
         "hpcg_set_option": (i32, [vp, i32, i32]),
         "hpcg_last_engine": (i32, [vp]),
+        "hpcg_last_launch_info": (i32, [vp, P(i32), P(i32)]),
         "hpcg_status_string": (ctypes.c_char_p, [i32]),
         "hpcg_last_error": (ctypes.c_char_p, [vp]),
         "hpcg_destroy": (None, [vp]),
@@ -218,6 +223,13 @@ def hpcg_set_option(h, option: int, value: int):
 
 def hpcg_last_engine(h) -> int:
     return int(lib().hpcg_last_engine(h))
+
+
+def hpcg_last_launch_info(h) -> tuple:
+    """(grid, resident) of the last persistent solve."""
+    grid, res = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().hpcg_last_launch_info(h, ctypes.byref(grid), ctypes.byref(res)), h)
+    return grid.value, res.value
 
 
 def hpcg_status_string(status: int) -> str:
