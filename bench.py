@@ -119,6 +119,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="N8k")
     ap.add_argument("--engine", type=int, default=0, help="0 auto, 1 graph, 2 persistent")
+    ap.add_argument("--prec", type=int, default=0, help="0 fp64 vectors (default), 1 fp32 vectors")
+    ap.add_argument("--no-variants", action="store_true", help="skip the engine/precision variants")
     ap.add_argument("--reps", type=int, default=300, help="calls per apply/SpMV timing")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-others", action="store_true", help="skip ms/solve of the other workloads")
@@ -137,13 +139,16 @@ def main(argv=None):
     torch.cuda.set_device(0)
     dev_name = torch.cuda.get_device_name(0)
 
-    def run_config(name, steps, warmup, with_roofline):
+    def run_config(name, steps, warmup, with_roofline, engine=None, prec=None):
         batch = make_config(name)
         solver = hpcg.Solver(batch.n, batch.row_ptr, batch.col, batch.val, batch=batch.batch,
                              levels=batch.levels)
         solver.set_factors(batch.U, batch.W, batch.g)
-        if args.engine:
-            solver.set_option(hpcg.HPCG_OPT_ENGINE, args.engine)
+        engine = args.engine if engine is None else engine
+        prec = args.prec if prec is None else prec
+        if engine:
+            solver.set_option(hpcg.HPCG_OPT_ENGINE, engine)
+        solver.set_option(hpcg.HPCG_OPT_PRECISION, prec)
         b = torch.as_tensor(batch.b.reshape(-1)).cuda()
         ms, iters, res = time_solves(solver, b, batch.tol, batch.maxit, steps, warmup, torch)
         out = {"ms_per_solve": ms, "iterations": iters, "status": res.status,
@@ -184,6 +189,13 @@ def main(argv=None):
                             if len(o["iterations"]) <= 4 else
                             {"min": min(o["iterations"]), "max": max(o["iterations"])},
                             "engine": o["engine"]}
+    variants = {}
+    if not args.no_variants:
+        for label, eng, prec in (("persistent_vec64", 2, 0), ("persistent_vec32", 2, 1),
+                                 ("graph_vec64", 1, 0), ("graph_vec32", 1, 1)):
+            log(f"bench: variant {label}")
+            _b, o = run_config(args.config, max(3, args.steps // 2), 1, False, eng, prec)
+            variants[label] = {"ms_per_solve": round(o["ms_per_solve"], 4), "iterations": o["iterations"][0]}
     cpu = None if args.no_cpu else cpu_baseline(batch)
     iters = main_out["iterations"][0]
     line = {
@@ -197,12 +209,13 @@ def main(argv=None):
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f64" if args.prec == 0 else "f32",
         "data": "synthetic",
         "config": {
             "workload": f"{args.config}: 3D 7-point variable-coefficient Poisson, Morton order, "
                         f"n={batch.n}, K={batch.K} leaves of 128, {batch.levels} tile levels of rank 32, "
                         f"nnz={batch.nnz}, tol={batch.tol}",
+            "vectors": "f64" if args.prec == 0 else "f32", "factors_and_matrix": "f32",
             "scalars": "f64", "x": "f64", "engine": main_out["engine"],
             "iterations": iters, "device": dev_name,
         },
@@ -223,6 +236,7 @@ def main(argv=None):
         },
         "cpu_baseline": cpu,
         "ms_per_solve_by_config": others,
+        "variants_at_workload": variants,
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -90,13 +90,13 @@ typedef struct {
     int32_t n;       /* unknowns per system; n % leaf == 0, n / leaf a power of 2 */
     int32_t leaf;    /* L, must be 128                                            */
     int32_t rank;    /* R, columns of every off-diagonal slab, must be 32         */
-    int32_t levels;  /* tile levels present, 0 .. log2(n / leaf); 0 = leaves only */
+    int32_t levels;  /* tile levels present, 0 .. min(8, log2(n / leaf)); 0 = leaves only */
     int32_t batch;   /* B >= 1 independent systems                                */
 } hpcg_partition;
 
 /* Solve engines (hpcg_set_option(HPCG_OPT_ENGINE, ...)). */
 typedef enum {
-    HPCG_ENGINE_AUTO = 0,       /* persistent when co-residency allows, else graph */
+    HPCG_ENGINE_AUTO = 0,       /* the graph engine (the faster one on gfx950)    */
     HPCG_ENGINE_GRAPH = 1,      /* per-phase kernels, unrolled iterations replayed
                                    as one hipGraph, host polls a pinned flag      */
     HPCG_ENGINE_PERSISTENT = 2  /* one cooperative launch runs the whole solve with
@@ -106,8 +106,6 @@ typedef enum {
 typedef enum {
     HPCG_OPT_ENGINE = 1,        /* an hpcg_engine value                          */
     HPCG_OPT_GRAPH_UNROLL = 2,  /* iterations per graph replay, 1 .. 64 (default 8) */
-    HPCG_OPT_RESIDENT = 3,      /* persistent engine keeps M in LDS when it fits:
-                                   1 = yes (default), 0 = stream M every iteration */
     HPCG_OPT_PRECISION = 4      /* an hpcg_precision value                        */
 } hpcg_option;
 
@@ -191,9 +189,9 @@ hpcg_status hpcg_set_option(hpcg_handle h, int32_t option, int32_t value);
 /* Engine the last hpcg_solve actually ran (an hpcg_engine value), or 0. */
 int32_t hpcg_last_engine(hpcg_handle h);
 
-/* Launch shape of the last persistent solve: *grid workgroups, and whether the
- * factors were LDS-resident (*resident = 1).  Either pointer may be NULL. */
-hpcg_status hpcg_last_launch_info(hpcg_handle h, int32_t* grid, int32_t* resident);
+/* Launch shape of the last hpcg_solve: *grid workgroups per phase launch and
+ * the largest dynamic LDS a phase used, in bytes.  Either pointer may be NULL. */
+hpcg_status hpcg_last_launch_info(hpcg_handle h, int32_t* grid, int32_t* lds_bytes);
 
 /* Static text for a status code. */
 const char* hpcg_status_string(hpcg_status s);

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <chrono>
 #include <cstdio>
@@ -23,8 +24,11 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t row_ptr, col, val, U, W, g, b, r, z, q, p0, p1, x, tpart, ppart, pq, rr, rz, st, ctl, total;
+  size_t row_ptr, col, val, U, W, g, b, r, z, q, p0, p1, x, tleaf, pleaf, pq, rr, rz, st, ctl, total;
 };
+
+// LDS of one gfx950 compute unit: a workgroup's static and dynamic LDS must fit.
+constexpr size_t kMaxLds = 160 * 1024;
 
 // control words, each on its own 256-byte line
 constexpr size_t kCtlBarrier = 0, kCtlAbort = 256, kCtlItbase = 512, kCtlReplays = 768, kCtlBytes = 1024;
@@ -39,17 +43,27 @@ bool make_geom(const hpcg_partition* p, Geom& G, std::string& why) {
   int full = 0;
   while ((1 << full) < K) ++full;
   if (p->levels < 0 || p->levels > full) { why = "levels must lie in [0, log2(n/128)]"; return false; }
-  if (p->levels > MAX_LEVELS) { why = "too many levels"; return false; }
+  if (p->levels > MAX_LEVELS) { why = "at most 8 tile levels (256 leaves) per system"; return false; }
   if (p->batch < 1) { why = "batch must be >= 1"; return false; }
   if ((int64_t)p->batch * p->n >= (int64_t)1 << 30) { why = "batch*n too large"; return false; }
   G.n = p->n;
   G.K = K;
   G.levels = p->levels;
   G.B = p->batch;
+  // workgroups per leaf: enough to give every CU a workgroup, and enough that
+  // the restriction and prolongation stages fit LDS in fp64 mode
   int bpl = 1;
   while ((int64_t)G.B * K * bpl < 256 && bpl < 8) bpl *= 2;
-  G.bpl = bpl;
-  G.RB = LEAF / bpl;
+  for (;;) {
+    G.bpl = bpl;
+    G.RB = LEAF / bpl;
+    const size_t need = sizeof(Smem<double>) + std::max(restrict_lds_bytes(G), prolong_lds_bytes<double>(G));
+    if (need <= kMaxLds || bpl == 8) {
+      if (need > kMaxLds) { why = "partition needs more LDS than a compute unit has"; return false; }
+      break;
+    }
+    bpl *= 2;
+  }
   G.nblk_sys = K * bpl;
   G.nblk = G.B * G.nblk_sys;
   return true;
@@ -74,8 +88,8 @@ Layout make_layout(const Geom& G, int64_t nnz) {
   L.p0 = take(N * 8);
   L.p1 = take(N * 8);
   L.x = take(N * 8);
-  L.tpart = take((size_t)G.B * G.K * G.bpl * LEAF * 8);
-  L.ppart = take((size_t)G.B * G.levels * G.K * G.bpl * RANK * 8 + 8);
+  L.tleaf = take((size_t)G.B * G.K * LEAF * 8);
+  L.pleaf = take((size_t)G.B * G.levels * G.K * RANK * 8 + 16);
   L.pq = take((size_t)G.nblk * 8);
   L.rr = take((size_t)G.nblk * 8);
   L.rz = take((size_t)G.nblk * 8);
@@ -101,7 +115,6 @@ struct hpcg_ctx {
   bool factors_set = false;
   int engine_opt = HPCG_ENGINE_AUTO;
   int unroll = 8;
-  int resident = 1;
   int prec = HPCG_PREC_VEC64;
   int last_engine = 0;
   int num_cu = 0;
@@ -113,8 +126,8 @@ struct hpcg_ctx {
   int graph_prec = -1;
   double graph_tol = -1.0;
   int graph_maxit = -1;
-  int last_resident = 0;
   int last_grid = 0;
+  int last_lds = 0;
   int* h_flag = nullptr;   // pinned, device-mapped
   int* d_flag = nullptr;
   SysState* h_st = nullptr;
@@ -124,6 +137,9 @@ struct hpcg_ctx {
 };
 
 namespace {
+
+// Clear the HIP runtime's sticky last error after a call whose failure we handle.
+void clear_hip_error_fn() { (void)hipGetLastError(); }
 
 hpcg_status fail(hpcg_ctx* h, hpcg_status s, const std::string& msg) {
   if (h) h->err = msg; else g_create_error = msg;
@@ -147,12 +163,18 @@ hpcg_status check_launch(hpcg_ctx* h, const char* what) {
   return HPCG_OK;
 }
 
-size_t res_lds_bytes(const Geom& G) {
-  return ((size_t)G.RB * LEAF + (size_t)G.levels * G.RB * RANK) * sizeof(float);
+// Raise a kernel's dynamic-LDS limit when it needs more than the default.
+hpcg_status allow_lds(hpcg_ctx* h, const void* fn, size_t bytes) {
+  if (bytes <= 48 * 1024) return HPCG_OK;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e != hipSuccess) {
+    clear_hip_error_fn();
+    return hip_fail(h, e, "hipFuncSetAttribute(MaxDynamicSharedMemorySize)");
+  }
+  return HPCG_OK;
 }
 
-// Clear the HIP runtime's sticky last error after a call whose failure we handle.
-void clear_hip_error() { (void)hipGetLastError(); }
+
 
 void destroy_graph(hpcg_ctx* h) {
   if (h->gexec) (void)hipGraphExecDestroy(h->gexec);
@@ -167,11 +189,15 @@ hpcg_status build_graph(hpcg_ctx* h) {
   destroy_graph(h);
   const Geom G = h->G;
   const Bufs B = h->B;
+  const size_t lds_b = restrict_lds_bytes(G), lds_c = prolong_lds_bytes<T>(G);
+  hpcg_status s = allow_lds(h, reinterpret_cast<const void*>(&k_phase_B<T>), lds_b);
+  if (s == HPCG_OK) s = allow_lds(h, reinterpret_cast<const void*>(&k_phase_C<T>), lds_c);
+  if (s != HPCG_OK) return s;
   HIP_OR_FAIL(h, hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal));
   for (int j = 0; j < h->unroll; ++j) {
     hipLaunchKernelGGL(k_phase_A<T>, dim3(G.nblk), dim3(NT), 0, h->cap_stream, G, B, j);
-    hipLaunchKernelGGL(k_phase_B<T>, dim3(G.nblk), dim3(NT), 0, h->cap_stream, G, B, j);
-    hipLaunchKernelGGL(k_phase_C<T>, dim3(G.nblk), dim3(NT), 0, h->cap_stream, G, B, j, -1);
+    hipLaunchKernelGGL(k_phase_B<T>, dim3(G.nblk), dim3(NT), lds_b, h->cap_stream, G, B, j, -1);
+    hipLaunchKernelGGL(k_phase_C<T>, dim3(G.nblk), dim3(NT), lds_c, h->cap_stream, G, B, j, -1);
   }
   hipLaunchKernelGGL(k_advance, dim3(1), dim3(64), 0, h->cap_stream, G, B, h->unroll, h->d_flag);
   hipError_t e = hipStreamEndCapture(h->cap_stream, &h->graph);
@@ -196,8 +222,8 @@ hpcg_status run_graph(hpcg_ctx* h) {
   }
   __atomic_store_n(h->h_flag, 0, __ATOMIC_RELEASE);
   hipLaunchKernelGGL(k_reset, dim3(1), dim3(64), 0, h->stream, B, 1, h->d_flag);
-  hipLaunchKernelGGL(k_init<T>, dim3(G.nblk), dim3(NT), 0, h->stream, G, B);
-  hipLaunchKernelGGL(k_phase_C<T>, dim3(G.nblk), dim3(NT), 0, h->stream, G, B, 0, 0);
+  hipLaunchKernelGGL(k_phase_B<T>, dim3(G.nblk), dim3(NT), restrict_lds_bytes(G), h->stream, G, B, 0, 0);
+  hipLaunchKernelGGL(k_phase_C<T>, dim3(G.nblk), dim3(NT), prolong_lds_bytes<T>(G), h->stream, G, B, 0, 0);
   hpcg_status s = check_launch(h, "graph engine setup launch");
   if (s != HPCG_OK) return s;
   const int max_replays = (B.maxit + h->unroll - 1) / h->unroll;
@@ -229,49 +255,35 @@ hpcg_status run_graph(hpcg_ctx* h) {
       }
     }
   }
+  h->last_grid = G.nblk;
+  h->last_lds = (int)std::max(restrict_lds_bytes(G), prolong_lds_bytes<T>(G));
   return HPCG_OK;
 }
 
-// Pick the persistent variant that fits: LDS-resident factors with one row
-// block per workgroup when LDS and occupancy allow, otherwise factors streamed
-// from memory with workgroups looping over row blocks.
+// One cooperative launch for the whole solve; the grid is as many workgroups
+// as can be co-resident (at most one per (leaf, slot) item).
 template <typename T>
 hpcg_status run_persistent(hpcg_ctx* h, bool& ran) {
   ran = false;
   const Geom G = h->G;
   const Bufs B = h->B;
   if (!h->coop) return HPCG_OK;
+  const size_t dyn = std::max(restrict_lds_bytes(G), prolong_lds_bytes<T>(G));
+  const void* fn = reinterpret_cast<const void*>(&k_persistent<T>);
+  hpcg_status s = allow_lds(h, fn, dyn);
+  if (s != HPCG_OK) return s;
   int per_cu = 0;
-  bool res = false;
-  size_t dyn = 0;
-  const void* fn = nullptr;
-  int grid = 0;
-  if (h->resident && res_lds_bytes(G) + sizeof(Smem<T>) <= h->max_lds) {
-    dyn = res_lds_bytes(G);
-    fn = reinterpret_cast<const void*>(&k_persistent<T, true>);
-    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NT, dyn) == hipSuccess &&
-        (int64_t)per_cu * h->num_cu >= G.nblk) {
-      res = true;
-      grid = G.nblk;
-    }
-    clear_hip_error();
-  }
-  if (!res) {
-    dyn = 0;
-    fn = reinterpret_cast<const void*>(&k_persistent<T, false>);
-    HIP_OR_FAIL(h, hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NT, 0));
-    const int64_t cap = (int64_t)per_cu * h->num_cu;
-    if (cap <= 0) return HPCG_OK;
-    grid = (int)std::min<int64_t>(cap, G.nblk);
-  }
+  HIP_OR_FAIL(h, hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NT, dyn));
+  const int64_t cap = (int64_t)per_cu * h->num_cu;
+  if (cap <= 0) return HPCG_OK;
+  const int grid = (int)std::min<int64_t>(cap, G.nblk);
   hipLaunchKernelGGL(k_reset, dim3(1), dim3(64), 0, h->stream, B, 0, (int*)nullptr);
   Geom Ga = G;
   Bufs Ba = B;
   void* args[] = {&Ga, &Ba};
   HIP_OR_FAIL(h, hipLaunchCooperativeKernel(fn, dim3(grid), dim3(NT), args, (unsigned)dyn, h->stream));
-  h->last_resident = res ? 1 : 0;
   h->last_grid = grid;
+  h->last_lds = (int)dyn;
   ran = true;
   return HPCG_OK;
 }
@@ -355,8 +367,8 @@ hpcg_status hpcg_create(const hpcg_partition* part, const int32_t* d_row_ptr, co
   B.p0 = w + lay.p0;
   B.p1 = w + lay.p1;
   B.x = reinterpret_cast<double*>(w + lay.x);
-  B.tpart = w + lay.tpart;
-  B.ppart = w + lay.ppart;
+  B.tleaf = w + lay.tleaf;
+  B.pleaf = w + lay.pleaf;
   B.pq_part = reinterpret_cast<double*>(w + lay.pq);
   B.rr_part = reinterpret_cast<double*>(w + lay.rr);
   B.rz_part = reinterpret_cast<double*>(w + lay.rz);
@@ -422,8 +434,12 @@ hpcg_status hpcg_apply_M(hpcg_handle h, const float* d_r, float* d_y) {
   if (d_r == d_y) return fail(h, HPCG_ERR_INVALID_ARG, "d_r and d_y must not alias");
   if (!h->factors_set) return fail(h, HPCG_ERR_STATE, "hpcg_set_factors has not been called");
   const Geom& G = h->G;
-  hipLaunchKernelGGL(k_apply_restrict, dim3(G.nblk), dim3(NT), 0, h->stream, G, h->B, d_r);
-  hipLaunchKernelGGL(k_apply_prolong, dim3(G.nblk), dim3(NT), 0, h->stream, G, h->B, d_r, d_y);
+  const size_t lds_r = restrict_lds_bytes(G), lds_p = prolong_lds_bytes<float>(G);
+  hpcg_status s = allow_lds(h, reinterpret_cast<const void*>(&k_apply_restrict), lds_r);
+  if (s == HPCG_OK) s = allow_lds(h, reinterpret_cast<const void*>(&k_apply_prolong), lds_p);
+  if (s != HPCG_OK) return s;
+  hipLaunchKernelGGL(k_apply_restrict, dim3(G.nblk), dim3(NT), lds_r, h->stream, G, h->B, d_r);
+  hipLaunchKernelGGL(k_apply_prolong, dim3(G.nblk), dim3(NT), lds_p, h->stream, G, h->B, d_r, d_y);
   return check_launch(h, "hpcg_apply_M launch");
 }
 
@@ -452,7 +468,11 @@ hpcg_status hpcg_solve(hpcg_handle h, const float* d_b, double* d_x, double tol,
   hpcg_status s = HPCG_OK;
   bool ran = false;
   const bool f32 = (h->prec == HPCG_PREC_VEC32);
-  if (h->engine_opt != HPCG_ENGINE_GRAPH) {
+  // AUTO runs the graph engine: on gfx950 a kernel boundary inside a graph
+  // (about 2 us) is cheaper than an agent-scope device-wide barrier over a
+  // full grid (about 10 us at 256 workgroups, dominated by the per-workgroup
+  // L2 writeback and invalidate of the release/acquire fences).
+  if (h->engine_opt == HPCG_ENGINE_PERSISTENT) {
     s = f32 ? run_persistent<float>(h, ran) : run_persistent<double>(h, ran);
     if (s != HPCG_OK) return s;
     if (!ran && h->engine_opt == HPCG_ENGINE_PERSISTENT)
@@ -503,10 +523,6 @@ hpcg_status hpcg_set_option(hpcg_handle h, int32_t option, int32_t value) {
       if (value < 1 || value > 64) return fail(h, HPCG_ERR_INVALID_ARG, "graph unroll must lie in [1, 64]");
       h->unroll = value;
       return HPCG_OK;
-    case HPCG_OPT_RESIDENT:
-      if (value != 0 && value != 1) return fail(h, HPCG_ERR_INVALID_ARG, "resident must be 0 or 1");
-      h->resident = value;
-      return HPCG_OK;
     case HPCG_OPT_PRECISION:
       if (value != HPCG_PREC_VEC64 && value != HPCG_PREC_VEC32) return fail(h, HPCG_ERR_INVALID_ARG, "bad precision");
       h->prec = value;
@@ -518,10 +534,10 @@ hpcg_status hpcg_set_option(hpcg_handle h, int32_t option, int32_t value) {
 
 int32_t hpcg_last_engine(hpcg_handle h) { return h ? h->last_engine : 0; }
 
-hpcg_status hpcg_last_launch_info(hpcg_handle h, int32_t* grid, int32_t* resident) {
+hpcg_status hpcg_last_launch_info(hpcg_handle h, int32_t* grid, int32_t* lds_bytes) {
   if (!h) return fail(nullptr, HPCG_ERR_INVALID_ARG, "handle is NULL");
   if (grid) *grid = h->last_grid;
-  if (resident) *resident = h->last_resident;
+  if (lds_bytes) *lds_bytes = h->last_lds;
   return HPCG_OK;
 }
 

@@ -1,10 +1,14 @@
 // Device-side building blocks of the H-matrix-preconditioned CG solve on gfx950.
 //
 // Work decomposition.  Every system's n rows are cut into leaves of LEAF = 128
-// rows, and every leaf into `bpl` row blocks of RB = LEAF / bpl rows.  One
-// workgroup of NT = 256 threads (four wave64 wavefronts) owns one row block in
-// every phase, so the same rows, the same rows of U_k and the same rows of the
-// level slabs W_l[k] stay with the same workgroup through the whole iteration.
+// rows, and every leaf is served by `bpl` workgroups of NT = 256 threads (four
+// wave64 wavefronts).  Workgroup j of leaf k
+//   * restricts by columns: it computes the complete slice j of t_k = U_k^T r_k
+//     (columns [j*CW, (j+1)*CW), CW = LEAF/bpl) and the complete per-leaf
+//     restriction W_l[k]^T r_k of the levels l with l % bpl == j; so every
+//     restriction result exists once per leaf, with no partial sums;
+//   * prolongs and does the vector work by rows: rows [j*RB, (j+1)*RB) of the
+//     leaf, RB = LEAF/bpl.
 //
 // One PCG iteration is three phases with a device-wide dependency between them
 // ("Hierarchical Transformer Preconditioning for Interactive Physics
@@ -12,20 +16,23 @@
 // inner loop):
 //   A  beta = (r.z)/(r.z)_old;  p = z + beta p;  q = A p;  partial p.q
 //   B  alpha = (r.z)/(p.q);  x += alpha p;  r -= alpha q;  partial r.r;
-//      restriction of the new r: t_k partial = U_k^T r_k over the block's rows,
-//      and per level the slab partial W_l[k]^T r_k          (eq. (2))
-//   C  convergence test on sum r.r;  z = M r from the restriction sums:
-//      z_k = U_k t_k + sum_l W_l[k] P_l[partner half] + g r_k  (eqs. (3)-(5),
-//      coupling core = identity);  partial r.z
+//      restriction of the new r (eq. (2)): t_k = U_k^T r_k, W_l[k]^T r_k
+//   C  convergence test on r.r;  strip aggregation over the partner half of
+//      every level (eq. (3)), then z_k = U_k t_k + sum_l W_l[k] P_l + g r_k
+//      (eqs. (4)-(5) with the coupling core equal to the identity);  partial r.z
 //
-// Precision.  Factors and matrix values are always fp32 (they are the bytes
-// that bound the apply).  The vector type T of the solve is a template
-// parameter: T = float is the pages' split (fp32 vectors and apply arithmetic,
-// fp64 scalars; Supplementary section 7), T = double carries r, z, p, q, the
-// restriction partials and all accumulations in fp64.  Scalars and x are fp64
-// in both.  Every sum of partials is evaluated by every workgroup that needs it
-// in one fixed order, so all workgroups agree bit for bit and a solve is
-// deterministic.
+// Memory traffic.  Each phase issues all of its loads in one batch: the factor
+// rows it needs go straight from global memory into LDS with gfx950's
+// global_load_lds_dwordx4 (no register staging), next to the scalar partials
+// and vector slices, so a phase costs about one memory round trip.
+//
+// Precision.  Factors and matrix values are fp32 (the bytes that bound the
+// apply).  The vector type T is a template parameter: T = float is the pages'
+// split (fp32 vectors and apply arithmetic, fp64 scalars; Supplementary
+// section 7), T = double carries r, z, p, q, the restriction results and all
+// accumulations in fp64.  Scalars and x are fp64 in both.  Every sum of
+// partials is evaluated in one fixed order wherever it is needed, so all
+// workgroups agree bit for bit and a solve is deterministic.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -37,14 +44,15 @@ constexpr int LEAF = 128;
 constexpr int RANK = 32;
 constexpr int NT = 256;
 constexpr int NWAVE = NT / 64;
-constexpr int MAX_LEVELS = 12;
+constexpr int MAX_LEVELS = 8;      // K <= 256 leaves per system
 
 enum : int { ST_RUNNING = 0, ST_CONVERGED = 1, ST_NOT_CONVERGED = 2, ST_BREAKDOWN = 3 };
 
 // `status` changes only in phase C (and at init): a breakdown found in phase A
 // or B is parked in `brk`/`brk_it` and turned into a status by the next phase C.
-// Every status a workgroup reads after a phase-C barrier is therefore final for
-// that iteration, and all workgroups take the same loop-exit decision.
+// A breakdown is parked only when the scalar that every workgroup of the system
+// computes identically is bad, so within a phase every workgroup reaches the
+// same decision, and every status read after a phase-C boundary is final.
 struct SysState {
   double rz[2];     // (r.z) after phase C of iteration j lives in rz[j & 1]
   double bnorm;     // ||b||_2
@@ -60,14 +68,14 @@ struct Geom {
   int K;         // leaves per system
   int levels;    // tile levels
   int B;         // systems
-  int bpl;       // row blocks per leaf
-  int RB;        // rows per block (LEAF / bpl)
+  int bpl;       // workgroups per leaf
+  int RB;        // rows per workgroup (LEAF / bpl), also the column-slice width CW
   int nblk_sys;  // K * bpl
   int nblk;      // B * nblk_sys
 };
 
-// Device buffers.  Vector buffers are sized for double; with T = float only the
-// first half of each is used.
+// Device buffers.  Vector and restriction buffers are sized for double; with
+// T = float only the first half of each is used.
 struct Bufs {
   const int* row_ptr;
   const int* col;
@@ -82,8 +90,8 @@ struct Bufs {
   void* p0;
   void* p1;
   double* x;
-  void* tpart;         // [B][K][bpl][LEAF]
-  void* ppart;         // [B][levels][K][bpl][RANK]
+  void* tleaf;         // [B][K][LEAF]        t_k = U_k^T r_k
+  void* pleaf;         // [B][levels][K][RANK] W_l[k]^T r_k
   double* pq_part;     // [nblk]
   double* rr_part;
   double* rz_part;
@@ -98,46 +106,91 @@ struct Bufs {
 
 template <typename T>
 struct alignas(16) Smem {
-  T r[LEAF];                         // the block's rows of r
-  T t[LEAF];                         // t_k = U_k^T r_k (whole leaf)
-  T P[MAX_LEVELS * RANK];            // partner-half sums per level
+  T r[LEAF];                          // phase B: r (then r_new) of the whole leaf; C: block rows
+  T t[LEAF];                          // phase C: t_k
+  T P[MAX_LEVELS * RANK];             // phase C: partner-half sums per level
   union {
     struct {
-      T redA[NWAVE][LEAF];           // restriction: U partials per wave
-      T redB[NWAVE][MAX_LEVELS * RANK];  // restriction: slab partials per wave
+      T redT[4 * NT];                 // phase B: U restriction partials [row group][column]
+      T redW[NWAVE][MAX_LEVELS * RANK];  // phase B: slab restriction partials per wave
     };
-    T redP[NWAVE][MAX_LEVELS * RANK];    // prolongation: partner-sum partials per wave
+    T redP[8][MAX_LEVELS * RANK];     // phase C: strip-aggregation partials
   };
   T yleaf[LEAF];
   T yoff[LEAF];
-  double dred[NWAVE];
-  int flag;
+  double dred[NWAVE];                 // workgroup sums
+  double dsc;                         // broadcast scalar
+  int flag;                           // broadcast state
 };
 
 struct Blk {
+  int item;   // item index (workgroup index after the XCD-aware permutation)
   int s;      // system
-  int lb;     // block within system
+  int lb;     // workgroup within system
   int k;      // leaf
-  int sub;    // row block within leaf
-  int grow0;  // first global row
+  int j;      // slot within leaf (column slice in B, row block in C and A)
+  int lrow0;  // first row of the row block within the leaf
+  int grow0;  // first global row of the row block
+  int leaf0;  // first global row of the leaf
 };
 
-__device__ __forceinline__ Blk decode(const Geom& G, int b) {
+// XCD-aware placement.  Workgroups are dispatched to the eight XCDs round-robin
+// (workgroup b runs on XCD b % 8), and each XCD has its own L2.  The item a
+// workgroup serves is chosen so that XCD x gets the contiguous item range
+// [x*nblk/8, (x+1)*nblk/8): every workgroup that touches leaf k in any phase
+// runs on the same XCD, so leaf k's factor rows and vector slices can stay in
+// that XCD's L2 from one kernel and one iteration to the next.
+constexpr int NXCD = 8;
+
+__device__ __forceinline__ int item_of(const Geom& G, int b) {
+  if (G.nblk % NXCD) return b;
+  return (b % NXCD) * (G.nblk / NXCD) + b / NXCD;
+}
+
+__device__ __forceinline__ Blk decode(const Geom& G, int wg) {
   Blk o;
+  const int b = item_of(G, wg);
+  o.item = b;
   o.s = b / G.nblk_sys;
   o.lb = b - o.s * G.nblk_sys;
   o.k = o.lb / G.bpl;
-  o.sub = o.lb - o.k * G.bpl;
-  o.grow0 = o.s * G.n + o.k * LEAF + o.sub * G.RB;
+  o.j = o.lb - o.k * G.bpl;
+  o.lrow0 = o.j * G.RB;
+  o.leaf0 = o.s * G.n + o.k * LEAF;
+  o.grow0 = o.leaf0 + o.lrow0;
   return o;
 }
 
-__device__ __forceinline__ float4 ld4(const float* p) {
-  return *reinterpret_cast<const float4*>(p);
+// ---------------------------------------------------------------------------
+// LDS helpers
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void* lds_vptr;
+
+// Copy `nchunks` 16-byte chunks into LDS at `dst` (16-byte aligned), packed in
+// chunk order; chunk c comes from global address addr(c) (16-byte aligned).
+// Each wave moves 64 consecutive chunks (1 KB) per global_load_lds_dwordx4; the
+// caller waits with lds_dma_wait() before reading.
+template <typename AddrFn>
+__device__ __forceinline__ void dma_to_lds(void* dst, int nchunks, AddrFn addr) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int q = wave; q * 64 < nchunks; q += NWAVE) {
+    const int c = q * 64 + lane;
+    lds_vptr l = (lds_vptr)((__attribute__((address_space(3))) char*)dst + q * 1024);
+    if (c < nchunks) __builtin_amdgcn_global_load_lds(addr(c), l, 16, 0, 0);
+  }
+}
+
+// All outstanding global loads (including the DMAs into LDS) of every wave
+// have landed after this.
+__device__ __forceinline__ void lds_dma_wait() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 }
 
 template <typename T>
 struct Vec4 { T x, y, z, w; };
+
+__device__ __forceinline__ float4 lds4f(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
 template <typename T>
 __device__ __forceinline__ Vec4<T> lds4(const T* p) {
@@ -162,42 +215,34 @@ __device__ __forceinline__ void axpy4(Vec4<T>& acc, float4 u, T s) {
   acc.w = fma((T)u.w, s, acc.w);
 }
 
-// Sum over the whole workgroup in a fixed tree order (deterministic).
-template <typename T>
-__device__ __forceinline__ double wg_sum(double v, Smem<T>& sm) {
+// Sum of a system's per-workgroup partials, computed by every wave in the same
+// order (xor butterflies add commutative pairs), hence bitwise identical in
+// every wave and every workgroup.  Loads are issued by the caller's batch.
+__device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ double load_partials(const double* part, int s, int nblk_sys) {
+  double v = 0.0;
+  const double* p = part + (size_t)s * nblk_sys;
+  for (int j = threadIdx.x & 63; j < nblk_sys; j += 64) v += p[j];
+  return v;
+}
+
+// Workgroup sum in a fixed order (deterministic).
+template <typename T>
+__device__ __forceinline__ double wg_sum(double v, double* red) {
+  v = wave_sum(v);
   const int tid = threadIdx.x;
-  if ((tid & 63) == 0) sm.dred[tid >> 6] = v;
+  if ((tid & 63) == 0) red[tid >> 6] = v;
   __syncthreads();
-  double s = sm.dred[0];
+  double s = red[0];
 #pragma unroll
-  for (int w = 1; w < NWAVE; ++w) s += sm.dred[w];
+  for (int w = 1; w < NWAVE; ++w) s += red[w];
   __syncthreads();
   return s;
-}
-
-// Sum of one system's per-block partials, identical in every workgroup.
-template <typename T>
-__device__ __forceinline__ double sys_sum(const double* part, int s, int nblk_sys, Smem<T>& sm) {
-  double v = 0.0;
-  for (int j = threadIdx.x; j < nblk_sys; j += NT) v += part[(size_t)s * nblk_sys + j];
-  return wg_sum(v, sm);
-}
-
-// Broadcast a system's status through LDS so the whole workgroup branches alike.
-// Returns ST_RUNNING, a final status, or -1 when a breakdown is pending.
-template <typename T>
-__device__ __forceinline__ int read_status(const SysState* st, Smem<T>& sm) {
-  if (threadIdx.x == 0) {
-    int v = __hip_atomic_load(&st->status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (v == ST_RUNNING && __hip_atomic_load(&st->brk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) v = -1;
-    sm.flag = v;
-  }
-  __syncthreads();
-  const int v = sm.flag;
-  __syncthreads();
-  return v;
 }
 
 __device__ __forceinline__ void park_breakdown(SysState* st, int it) {
@@ -210,131 +255,170 @@ __device__ __forceinline__ void set_state(SysState* st, int status, int iters) {
   __hip_atomic_store(&st->status, status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Where a block's rows of U_k and of its level slabs are read from: global
-// memory (row stride LEAF for U; slab level stride K*LEAF*RANK) or a resident
-// copy in LDS (level stride RB*RANK).
-struct FactorView {
-  const float* Ub;   // first row of the block in U_k, rows LEAF floats apart
-  const float* Wb;   // first row of the block in W_0[k], rows RANK floats apart
-  size_t wstride;    // floats between consecutive levels
-};
-
-__device__ __forceinline__ FactorView global_view(const Geom& G, const Bufs& B, const Blk& bk) {
-  FactorView v;
-  v.Ub = B.U + ((size_t)bk.s * G.K + bk.k) * LEAF * LEAF + (size_t)bk.sub * G.RB * LEAF;
-  v.Wb = B.W + ((size_t)bk.s * G.levels * G.K + bk.k) * LEAF * RANK + (size_t)bk.sub * G.RB * RANK;
-  v.wstride = (size_t)G.K * LEAF * RANK;
+// Thread 0 reads the system state; the value reaches the whole workgroup through
+// LDS.  Returns ST_RUNNING, a final status, or -1 when a breakdown is pending.
+__device__ __forceinline__ int load_state(const SysState* st) {
+  int v = __hip_atomic_load(&st->status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (v == ST_RUNNING && __hip_atomic_load(&st->brk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) v = -1;
   return v;
 }
 
+// Dynamic-LDS bytes of the restriction and prolongation stages.
+__host__ __device__ inline int levels_of_slot(const Geom& G, int j) {
+  return j < G.levels ? (G.levels - 1 - j) / G.bpl + 1 : 0;
+}
+__host__ __device__ inline size_t restrict_lds_bytes(const Geom& G) {
+  return (size_t)4 * ((size_t)LEAF * G.RB + (size_t)levels_of_slot(G, 0) * LEAF * RANK);
+}
+template <typename T>
+__host__ __device__ inline size_t prolong_lds_bytes(const Geom& G) {
+  const size_t factors = (size_t)4 * ((size_t)G.RB * LEAF + (size_t)G.levels * G.RB * RANK);
+  return factors + (size_t)(G.K - 1) * RANK * sizeof(T);
+}
+
 // ---------------------------------------------------------------------------
-// Restriction (eq. (2) per leaf and level): from sm.r (block rows) write the
-// block's partial t = U_blk^T r_blk and, for every level, W_l,blk^T r_blk.
-// U: lane = 4-column slot (32 per row), 8 row groups; W: 8 slots per row, 32
-// row groups.  Row groups are summed across lanes, then across waves in LDS.
+// Restriction (eq. (2)): from sm.r (the leaf's r, all LEAF rows) compute the
+// workgroup's column slice of t_k and the per-leaf restriction of its levels.
+// Factors were DMA'd to dyn: U slice [LEAF][CW], then each owned level's slab
+// [LEAF][RANK].  Writes tleaf and pleaf.
 // ---------------------------------------------------------------------------
 template <typename T>
-__device__ __forceinline__ void restrict_block(const Geom& G, const Bufs& B, const Blk& bk,
-                                               const FactorView& fv, Smem<T>& sm) {
+__device__ __forceinline__ void issue_restrict_dma(const Geom& G, const Bufs& B, const Blk& bk, float* dyn) {
+  const int CW = G.RB;
+  const float* Uk = B.U + ((size_t)bk.s * G.K + bk.k) * LEAF * LEAF + (size_t)bk.j * CW;
+  const int cpr = CW / 4;  // chunks per row of the slice
+  dma_to_lds(dyn, LEAF * cpr, [&](int c) { return Uk + (size_t)(c / cpr) * LEAF + 4 * (c % cpr); });
+  float* dw = dyn + LEAF * CW;
+  const int nl = levels_of_slot(G, bk.j);
+  for (int m = 0; m < nl; ++m) {
+    const int l = bk.j + m * G.bpl;
+    const float* Wl = B.W + (((size_t)bk.s * G.levels + l) * G.K + bk.k) * LEAF * RANK;
+    dma_to_lds(dw + (size_t)m * LEAF * RANK, LEAF * RANK / 4, [&](int c) { return Wl + 4 * c; });
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void restrict_leaf(const Geom& G, const Bufs& B, const Blk& bk, const float* dyn,
+                                              Smem<T>& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int RB = G.RB;
-  T* tpart = reinterpret_cast<T*>(B.tpart);
-  T* ppart = reinterpret_cast<T*>(B.ppart);
+  const int CW = G.RB;
+  T* tleaf = reinterpret_cast<T*>(B.tleaf);
+  T* pleaf = reinterpret_cast<T*>(B.pleaf);
   {
-    const int cs = tid & 31, rg = tid >> 5;
+    // U slice: thread = (4-column slot c4, row group rg); RG row groups
+    const int slots = CW / 4, RG = NT / slots;
+    const int c4 = tid % slots, rg = tid / slots;
     Vec4<T> acc{0, 0, 0, 0};
-    for (int i = rg; i < RB; i += 8) axpy4(acc, ld4(fv.Ub + (size_t)i * LEAF + 4 * cs), sm.r[i]);
-    acc.x += __shfl_xor(acc.x, 32); acc.y += __shfl_xor(acc.y, 32);
-    acc.z += __shfl_xor(acc.z, 32); acc.w += __shfl_xor(acc.w, 32);
-    if (lane < 32) {
-      T* d = &sm.redA[wave][4 * cs];
-      d[0] = acc.x; d[1] = acc.y; d[2] = acc.z; d[3] = acc.w;
-    }
+    for (int i = rg; i < LEAF; i += RG) axpy4(acc, lds4f(dyn + i * CW + 4 * c4), sm.r[i]);
+    T* d = &sm.redT[rg * CW + 4 * c4];
+    d[0] = acc.x; d[1] = acc.y; d[2] = acc.z; d[3] = acc.w;
   }
   {
+    // owned levels: thread = (4-column slot cs of 8, row group rg of 32)
     const int cs = tid & 7, rg = tid >> 3;
-    for (int l = 0; l < G.levels; ++l) {
-      const float* Wl = fv.Wb + (size_t)l * fv.wstride;
+    const int nl = levels_of_slot(G, bk.j);
+    const float* dw = dyn + LEAF * CW;
+    for (int m = 0; m < nl; ++m) {
+      const float* Wm = dw + (size_t)m * LEAF * RANK;
       Vec4<T> acc{0, 0, 0, 0};
-      for (int i = rg; i < RB; i += 32) axpy4(acc, ld4(Wl + (size_t)i * RANK + 4 * cs), sm.r[i]);
+#pragma unroll
+      for (int i = rg; i < LEAF; i += 32) axpy4(acc, lds4f(Wm + i * RANK + 4 * cs), sm.r[i]);
 #pragma unroll
       for (int o = 8; o < 64; o <<= 1) {
         acc.x += __shfl_xor(acc.x, o); acc.y += __shfl_xor(acc.y, o);
         acc.z += __shfl_xor(acc.z, o); acc.w += __shfl_xor(acc.w, o);
       }
       if (lane < 8) {
-        T* d = &sm.redB[wave][l * RANK + 4 * cs];
+        T* d = &sm.redW[wave][m * RANK + 4 * cs];
         d[0] = acc.x; d[1] = acc.y; d[2] = acc.z; d[3] = acc.w;
       }
     }
   }
   __syncthreads();
-  if (tid < LEAF) {
-    T s = sm.redA[0][tid];
+  {
+    const int RG = NT / (CW / 4);
+    if (tid < CW) {
+      T s = sm.redT[tid];
+      for (int g = 1; g < RG; ++g) s += sm.redT[g * CW + tid];
+      tleaf[((size_t)bk.s * G.K + bk.k) * LEAF + bk.j * CW + tid] = s;
+    }
+    const int nl = levels_of_slot(G, bk.j);
+    for (int e = tid; e < nl * RANK; e += NT) {
+      T s = sm.redW[0][e];
 #pragma unroll
-    for (int w = 1; w < NWAVE; ++w) s += sm.redA[w][tid];
-    tpart[(((size_t)bk.s * G.K + bk.k) * G.bpl + bk.sub) * LEAF + tid] = s;
+      for (int w = 1; w < NWAVE; ++w) s += sm.redW[w][e];
+      const int m = e / RANK, c = e - m * RANK;
+      const int l = bk.j + m * G.bpl;
+      pleaf[(((size_t)bk.s * G.levels + l) * G.K + bk.k) * RANK + c] = s;
+    }
   }
-  for (int e = tid; e < G.levels * RANK; e += NT) {
-    T s = sm.redB[0][e];
-#pragma unroll
-    for (int w = 1; w < NWAVE; ++w) s += sm.redB[w][e];
-    const int l = e / RANK, c = e - l * RANK;
-    ppart[((((size_t)bk.s * G.levels + l) * G.K + bk.k) * G.bpl + bk.sub) * RANK + c] = s;
-  }
-  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
-// Prolongation and assembly of y = M r on the block's rows (eqs. (3)-(5) and
-// the diagonal stage), reading the restriction partials of every block of the
-// system.  Needs sm.r; returns y for row tid (tid < RB).
+// Prolongation (eqs. (3)-(5) and the diagonal stage) on the workgroup's row
+// block.  DMA: U rows [RB][LEAF], slab rows [levels][RB][RANK], the partner
+// half's per-leaf restrictions of every level (stage, level l at row 2^l - 1),
+// t_k.  Needs sm.r (block rows) and g; returns y for row tid (tid < RB).
 // ---------------------------------------------------------------------------
 template <typename T>
-__device__ __forceinline__ T prolong_block(const Geom& G, const Bufs& B, const Blk& bk,
-                                           const FactorView& fv, Smem<T>& sm) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__device__ __forceinline__ void issue_prolong_dma(const Geom& G, const Bufs& B, const Blk& bk, float* dyn,
+                                                  Smem<T>& sm) {
   const int RB = G.RB;
-  const T* tpart = reinterpret_cast<const T*>(B.tpart);
-  const T* ppart = reinterpret_cast<const T*>(B.ppart);
-  // t_k: sum of the leaf's block partials
-  if (tid < LEAF) {
-    const T* tp = tpart + ((size_t)bk.s * G.K + bk.k) * G.bpl * LEAF + tid;
-    T s = tp[0];
-    for (int j = 1; j < G.bpl; ++j) s += tp[(size_t)j * LEAF];
-    sm.t[tid] = s;
+  const float* Ub = B.U + ((size_t)bk.s * G.K + bk.k) * LEAF * LEAF + (size_t)bk.lrow0 * LEAF;
+  dma_to_lds(dyn, RB * LEAF / 4, [&](int c) { return Ub + 4 * c; });
+  float* dw = dyn + RB * LEAF;
+  for (int l = 0; l < G.levels; ++l) {
+    const float* Wl = B.W + (((size_t)bk.s * G.levels + l) * G.K + bk.k) * LEAF * RANK + (size_t)bk.lrow0 * RANK;
+    dma_to_lds(dw + (size_t)l * RB * RANK, RB * RANK / 4, [&](int c) { return Wl + 4 * c; });
   }
-  // strip aggregation: partner-half sums per level (eq. (3))
+  T* stage = reinterpret_cast<T*>(dw + (size_t)G.levels * RB * RANK);
+  const T* pleaf = reinterpret_cast<const T*>(B.pleaf);
+  constexpr int CPV = RANK * sizeof(T) / 16;   // chunks per restriction vector
+  for (int l = 0; l < G.levels; ++l) {
+    const int kp0 = ((bk.k >> l) ^ 1) << l;
+    const T* src = pleaf + (((size_t)bk.s * G.levels + l) * G.K + kp0) * RANK;
+    dma_to_lds(stage + (size_t)((1 << l) - 1) * RANK, (1 << l) * CPV,
+               [&](int c) { return reinterpret_cast<const char*>(src) + 16 * c; });
+  }
+  const T* tl = reinterpret_cast<const T*>(B.tleaf) + ((size_t)bk.s * G.K + bk.k) * LEAF;
+  dma_to_lds(sm.t, LEAF * (int)sizeof(T) / 16, [&](int c) { return reinterpret_cast<const char*>(tl) + 16 * c; });
+}
+
+template <typename T>
+__device__ __forceinline__ T prolong_rows(const Geom& G, const Bufs& B, const Blk& bk, const float* dyn,
+                                          Smem<T>& sm) {
+  const int tid = threadIdx.x;
+  const int RB = G.RB;
+  const float* dw = dyn + RB * LEAF;
+  const T* stage = reinterpret_cast<const T*>(dw + (size_t)G.levels * RB * RANK);
+  // strip aggregation (eq. (3)): P_l[c] = sum over the 2^l partner leaves
   {
-    const int c = tid & 31, j0 = tid >> 5;
+    const int c = tid & 31, g = tid >> 5;
     for (int l = 0; l < G.levels; ++l) {
-      const int kp0 = ((bk.k >> l) ^ 1) << l;
-      const int cnt = (1 << l) * G.bpl;
-      const T* base = ppart + (((size_t)bk.s * G.levels + l) * G.K + kp0) * G.bpl * RANK + c;
+      const T* v = stage + (size_t)((1 << l) - 1) * RANK + c;
       T acc = 0;
-      for (int v = j0; v < cnt; v += 8) acc += base[(size_t)v * RANK];
-      acc += __shfl_xor(acc, 32);
-      if (lane < 32) sm.redP[wave][l * RANK + c] = acc;
+      for (int i = g; i < (1 << l); i += 8) acc += v[i * RANK];
+      sm.redP[g][l * RANK + c] = acc;
     }
   }
   __syncthreads();
   for (int e = tid; e < G.levels * RANK; e += NT) {
     T s = sm.redP[0][e];
 #pragma unroll
-    for (int w = 1; w < NWAVE; ++w) s += sm.redP[w][e];
+    for (int g = 1; g < 8; ++g) s += sm.redP[g][e];
     sm.P[e] = s;
   }
   __syncthreads();
-  // diagonal stage: row i's dot with t is split over 32 lanes (4 columns each);
-  // two rows at a time are folded with a transpose-reduce (5 shuffles per pair)
+  // diagonal stage: row i's dot with t_k over 32 lanes (4 columns each); two
+  // rows at a time are folded with a transpose-reduce (5 shuffles per pair)
   {
     const int cs = tid & 31, rg = tid >> 5;
     const Vec4<T> t4 = lds4(&sm.t[4 * cs]);
     const bool hi = (cs & 16) != 0;
     for (int i0 = rg; i0 < RB; i0 += 16) {
       const int i1 = i0 + 8;
-      const T v0 = dot4(ld4(fv.Ub + (size_t)i0 * LEAF + 4 * cs), t4);
-      const T v1 = (i1 < RB) ? dot4(ld4(fv.Ub + (size_t)i1 * LEAF + 4 * cs), t4) : T(0);
+      const T v0 = dot4(lds4f(dyn + i0 * LEAF + 4 * cs), t4);
+      const T v1 = (i1 < RB) ? dot4(lds4f(dyn + i1 * LEAF + 4 * cs), t4) : T(0);
       T keep = hi ? v1 : v0;
       const T send = hi ? v0 : v1;
       keep += __shfl_xor(send, 16);
@@ -352,7 +436,7 @@ __device__ __forceinline__ T prolong_block(const Geom& G, const Bufs& B, const B
     for (int i = rg; i < RB; i += 32) {
       T acc = 0;
       for (int l = 0; l < G.levels; ++l)
-        acc += dot4(ld4(fv.Wb + (size_t)l * fv.wstride + (size_t)i * RANK + 4 * cs), lds4(&sm.P[l * RANK + 4 * cs]));
+        acc += dot4(lds4f(dw + ((size_t)l * RB + i) * RANK + 4 * cs), lds4(&sm.P[l * RANK + 4 * cs]));
       acc += __shfl_xor(acc, 1);
       acc += __shfl_xor(acc, 2);
       acc += __shfl_xor(acc, 4);
@@ -373,29 +457,69 @@ __device__ __forceinline__ T pdir(T z, T pold, double beta) {
 }
 
 // ---------------------------------------------------------------------------
-// Phases.  b = global block index; it = iteration (1-based; 0 = initial apply).
+// Phases.  b = workgroup index (mapped to an item by decode); it = iteration
+// (1-based; 0 = initial).
 // ---------------------------------------------------------------------------
+
+// Phase B (and the initial restriction when it == 0: r = b, x = 0).
 template <typename T>
-__device__ __forceinline__ void phase_init(const Geom& G, const Bufs& B, int b, const FactorView& fv, Smem<T>& sm) {
+__device__ __forceinline__ void phase_B(const Geom& G, const Bufs& B, int b, int it, Smem<T>& sm, float* dyn) {
   const Blk bk = decode(G, b);
   const int tid = threadIdx.x;
+  SysState* st = B.st + bk.s;
+  const bool init = (it == 0);
   T* r = reinterpret_cast<T*>(B.r);
+  // ---- one batch of loads ----
+  issue_restrict_dma<T>(G, B, bk, dyn);
+  const double pqv = init ? 0.0 : load_partials(B.pq_part, bk.s, G.nblk_sys);
+  int state = ST_RUNNING;
+  double rzv = 0.0;
+  if (tid == 0 && !init) {
+    state = load_state(st);
+    rzv = st->rz[(it - 1) & 1];
+  }
+  T rv = 0, qv = 0, pv = 0;
+  double xv = 0.0;
+  const bool own = (tid >= bk.lrow0 && tid < bk.lrow0 + G.RB);
+  if (tid < LEAF) {
+    if (init) {
+      rv = (T)B.b[bk.leaf0 + tid];
+    } else {
+      rv = r[bk.leaf0 + tid];
+      qv = reinterpret_cast<const T*>(B.q)[bk.leaf0 + tid];
+      if (own) {
+        pv = reinterpret_cast<const T*>((it & 1) ? B.p1 : B.p0)[bk.leaf0 + tid];
+        xv = B.x[bk.leaf0 + tid];
+      }
+    }
+  }
+  const double pq = wave_sum(pqv);
+  if (tid == 0) { sm.flag = state; sm.dsc = rzv; }
+  lds_dma_wait();
+  if (!init) {
+    if (sm.flag != ST_RUNNING) return;
+    if (!(pq > 0.0) || !isfinite(pq)) {
+      if (tid == 0 && bk.lb == 0) park_breakdown(st, it);
+      return;
+    }
+  }
+  const double alpha = init ? 0.0 : sm.dsc / pq;
   double loc = 0.0;
-  if (tid < G.RB) {
-    const int grow = bk.grow0 + tid;
-    const T bv = (T)B.b[grow];
-    r[grow] = bv;
-    B.x[grow] = 0.0;
-    sm.r[tid] = bv;
-    loc = (double)bv * (double)bv;
+  if (tid < LEAF) {
+    const T rn = init ? rv : (T)((double)rv - alpha * (double)qv);
+    sm.r[tid] = rn;
+    if (own) {
+      r[bk.leaf0 + tid] = rn;
+      B.x[bk.leaf0 + tid] = init ? 0.0 : xv + alpha * (double)pv;
+      loc = (double)rn * (double)rn;
+    }
   }
   __syncthreads();
-  restrict_block(G, B, bk, fv, sm);
-  const double rr = wg_sum(loc, sm);
+  restrict_leaf(G, B, bk, dyn, sm);
+  const double rr = wg_sum<T>(loc, sm.dred);
   if (tid == 0) {
-    B.rr_part[b] = rr;
-    if (bk.lb == 0) {
-      SysState* st = B.st + bk.s;
+    B.rr_part[bk.item] = rr;
+    if (init && bk.lb == 0) {
       st->relres = 1.0;
       st->brk = 0;
       st->brk_it = 0;
@@ -405,90 +529,33 @@ __device__ __forceinline__ void phase_init(const Geom& G, const Bufs& B, int b, 
 }
 
 template <typename T>
-__device__ __forceinline__ void phase_A(const Geom& G, const Bufs& B, int b, int it, Smem<T>& sm) {
+__device__ __forceinline__ void phase_C(const Geom& G, const Bufs& B, int b, int it, Smem<T>& sm, float* dyn) {
   const Blk bk = decode(G, b);
-  SysState* st = B.st + bk.s;
-  if (read_status(st, sm) != ST_RUNNING) return;
   const int tid = threadIdx.x;
-  const double rz = sys_sum(B.rz_part, bk.s, G.nblk_sys, sm);
-  if (!(rz > 0.0) || !isfinite(rz)) {
-    if (tid == 0 && bk.lb == 0) park_breakdown(st, it - 1);
-    return;
-  }
-  double beta = 0.0;
-  if (it > 1) beta = rz / st->rz[(it - 2) & 1];
-  if (tid == 0 && bk.lb == 0) st->rz[(it - 1) & 1] = rz;
-  const T* z = reinterpret_cast<const T*>(B.z);
-  const T* pold = reinterpret_cast<const T*>((it & 1) ? B.p0 : B.p1);
-  T* pnew = reinterpret_cast<T*>((it & 1) ? B.p1 : B.p0);
-  T* q = reinterpret_cast<T*>(B.q);
-  const bool first = (it == 1);
-  // SpMV on the fly of p_new: TPR threads per row
-  const int TPR = NT / G.RB;
-  const int i = tid / TPR, lr = tid - i * TPR;
-  const int grow = bk.grow0 + i;
-  const int e0 = B.row_ptr[grow], e1 = B.row_ptr[grow + 1];
-  T acc = 0;
-  for (int e = e0 + lr; e < e1; e += TPR) {
-    const int c = B.col[e];
-    const T v = first ? z[c] : pdir<T>(z[c], pold[c], beta);
-    acc = fma((T)B.val[e], v, acc);
-  }
-  for (int o = 1; o < TPR; o <<= 1) acc += __shfl_xor(acc, o);
-  double loc = 0.0;
-  if (lr == 0) {
-    const T pn = first ? z[grow] : pdir<T>(z[grow], pold[grow], beta);
-    pnew[grow] = pn;
-    q[grow] = acc;
-    loc = (double)pn * (double)acc;
-  }
-  const double pq = wg_sum(loc, sm);
-  if (tid == 0) B.pq_part[b] = pq;
-}
-
-template <typename T>
-__device__ __forceinline__ void phase_B(const Geom& G, const Bufs& B, int b, int it, const FactorView& fv, Smem<T>& sm) {
-  const Blk bk = decode(G, b);
   SysState* st = B.st + bk.s;
-  if (read_status(st, sm) != ST_RUNNING) return;
-  const int tid = threadIdx.x;
-  const double pq = sys_sum(B.pq_part, bk.s, G.nblk_sys, sm);
-  if (!(pq > 0.0) || !isfinite(pq)) {
-    if (tid == 0 && bk.lb == 0) park_breakdown(st, it);
-    return;
-  }
-  const double alpha = st->rz[(it - 1) & 1] / pq;
-  const T* pnew = reinterpret_cast<const T*>((it & 1) ? B.p1 : B.p0);
-  const T* q = reinterpret_cast<const T*>(B.q);
-  T* r = reinterpret_cast<T*>(B.r);
-  double loc = 0.0;
-  if (tid < G.RB) {
-    const int grow = bk.grow0 + tid;
-    const T rn = (T)((double)r[grow] - alpha * (double)q[grow]);
-    r[grow] = rn;
-    B.x[grow] += alpha * (double)pnew[grow];
-    sm.r[tid] = rn;
-    loc = (double)rn * (double)rn;
-  }
-  __syncthreads();
-  restrict_block(G, B, bk, fv, sm);
-  const double rr = wg_sum(loc, sm);
-  if (tid == 0) B.rr_part[b] = rr;
-}
-
-template <typename T>
-__device__ __forceinline__ void phase_C(const Geom& G, const Bufs& B, int b, int it, const FactorView& fv, Smem<T>& sm) {
-  const Blk bk = decode(G, b);
-  SysState* st = B.st + bk.s;
-  const int tid = threadIdx.x;
   const bool lead = (tid == 0 && bk.lb == 0);
-  const int cur = read_status(st, sm);
+  // ---- one batch of loads ----
+  issue_prolong_dma<T>(G, B, bk, dyn, sm);
+  const double rrv = load_partials(B.rr_part, bk.s, G.nblk_sys);
+  int state = ST_RUNNING;
+  double bnorm = 0.0;
+  if (tid == 0) {
+    state = (it == 0) ? ST_RUNNING : load_state(st);
+    bnorm = st->bnorm;
+  }
+  const T* r = reinterpret_cast<const T*>(B.r);
+  T rv = 0;
+  if (tid < G.RB) rv = r[bk.grow0 + tid];
+  const double rr = wave_sum(rrv);
+  if (tid == 0) { sm.flag = state; sm.dsc = bnorm; }
+  if (tid < G.RB) sm.r[tid] = rv;
+  lds_dma_wait();
+  const int cur = sm.flag;
   if (cur == -1) {
     if (lead) set_state(st, ST_BREAKDOWN, st->brk_it);
     return;
   }
   if (cur != ST_RUNNING) return;
-  const double rr = sys_sum(B.rr_part, bk.s, G.nblk_sys, sm);
   if (it == 0) {
     if (lead) st->bnorm = sqrt(rr);
     if (rr == 0.0) {
@@ -496,7 +563,7 @@ __device__ __forceinline__ void phase_C(const Geom& G, const Bufs& B, int b, int
       return;
     }
   } else {
-    const double rel = sqrt(rr) / st->bnorm;
+    const double rel = sqrt(rr) / sm.dsc;
     if (lead) st->relres = rel;
     if (rel <= B.tol) {
       if (lead) set_state(st, ST_CONVERGED, it);
@@ -507,18 +574,80 @@ __device__ __forceinline__ void phase_C(const Geom& G, const Bufs& B, int b, int
       return;
     }
   }
-  const T* r = reinterpret_cast<const T*>(B.r);
-  T* z = reinterpret_cast<T*>(B.z);
-  if (tid < G.RB) sm.r[tid] = r[bk.grow0 + tid];
-  __syncthreads();
-  const T zv = prolong_block(G, B, bk, fv, sm);
+  const T zv = prolong_rows(G, B, bk, dyn, sm);
   double loc = 0.0;
   if (tid < G.RB) {
-    z[bk.grow0 + tid] = zv;
+    reinterpret_cast<T*>(B.z)[bk.grow0 + tid] = zv;
     loc = (double)sm.r[tid] * (double)zv;
   }
-  const double rz = wg_sum(loc, sm);
-  if (tid == 0) B.rz_part[b] = rz;
+  const double rz = wg_sum<T>(loc, sm.dred);
+  if (tid == 0) B.rz_part[bk.item] = rz;
+}
+
+// Phase A: beta, p = z + beta p, q = A p (row block), partial p.q.
+template <typename T>
+__device__ __forceinline__ void phase_A(const Geom& G, const Bufs& B, int b, int it, Smem<T>& sm) {
+  const Blk bk = decode(G, b);
+  const int tid = threadIdx.x;
+  SysState* st = B.st + bk.s;
+  const T* z = reinterpret_cast<const T*>(B.z);
+  const T* pold = reinterpret_cast<const T*>((it & 1) ? B.p0 : B.p1);
+  T* pnew = reinterpret_cast<T*>((it & 1) ? B.p1 : B.p0);
+  const bool first = (it == 1);
+  // ---- loads: scalars, own row, row extent ----
+  const double rzv = load_partials(B.rz_part, bk.s, G.nblk_sys);
+  int state = ST_RUNNING;
+  double rzold = 1.0;
+  if (tid == 0) {
+    state = load_state(st);
+    if (!first) rzold = st->rz[(it - 2) & 1];
+  }
+  const int TPR = NT / G.RB;
+  const int i = tid / TPR, lr = tid - i * TPR;
+  const int grow = bk.grow0 + i;
+  const int e0 = B.row_ptr[grow], e1 = B.row_ptr[grow + 1];
+  T zown = 0, pown = 0;
+  if (lr == 0) {
+    zown = z[grow];
+    if (!first) pown = pold[grow];
+  }
+  const double rz = wave_sum(rzv);
+  if (tid == 0) { sm.flag = state; sm.dsc = rzold; }
+  __syncthreads();
+  if (sm.flag != ST_RUNNING) return;
+  if (!(rz > 0.0) || !isfinite(rz)) {
+    if (tid == 0 && bk.lb == 0) park_breakdown(st, it - 1);
+    return;
+  }
+  const double beta = first ? 0.0 : rz / sm.dsc;
+  if (tid == 0 && bk.lb == 0) st->rz[(it - 1) & 1] = rz;
+  // ---- SpMV of p_new on the fly: entries in passes of 4 per thread ----
+  T acc = 0;
+  for (int e = e0 + lr; e < e1; e += 4 * TPR) {
+    int c[4];
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int eu = e + u * TPR;
+      c[u] = eu < e1 ? B.col[eu] : grow;
+      v[u] = eu < e1 ? B.val[eu] : 0.f;
+    }
+    T pz[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) pz[u] = first ? z[c[u]] : pdir<T>(z[c[u]], pold[c[u]], beta);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc = fma((T)v[u], pz[u], acc);
+  }
+  for (int o = 1; o < TPR; o <<= 1) acc += __shfl_xor(acc, o);
+  double loc = 0.0;
+  if (lr == 0) {
+    const T pn = first ? zown : pdir<T>(zown, pown, beta);
+    pnew[grow] = pn;
+    reinterpret_cast<T*>(B.q)[grow] = acc;
+    loc = (double)pn * (double)acc;
+  }
+  const double pq = wg_sum<T>(loc, sm.dred);
+  if (tid == 0) B.pq_part[bk.item] = pq;
 }
 
 }  // namespace hpcg

@@ -4,9 +4,9 @@
 //  * graph engine: one kernel per phase, G unrolled iterations captured in a
 //    hipGraph and replayed; the host reads a pinned flag between replays.
 //  * persistent engine: a single cooperative launch runs the whole solve; phases
-//    are separated by a device-wide barrier, and each workgroup can keep its rows
-//    of the factors resident in LDS for every iteration.
-// Standalone kernels serve hpcg_apply_M and hpcg_spmv.
+//    are separated by a device-wide barrier.
+// Standalone kernels serve hpcg_apply_M (restriction, then prolongation) and
+// hpcg_spmv.
 #pragma once
 #include "hpcg_device.hpp"
 
@@ -17,9 +17,11 @@ namespace hpcg {
 // ---------------------------------------------------------------------------
 // Every workgroup arrives once per barrier on a monotonically increasing
 // counter; barrier number m completes when the counter reaches m * gridDim.x.
-// The wait is bounded: after ~2^26 polls (seconds) the workgroup raises the
-// abort flag and leaves, so a broken co-residency assumption ends the kernel
-// with an error instead of hanging the device.
+// Arrival is an agent-scope release, the wait an agent-scope acquire, so the
+// data written before the barrier is visible after it on every XCD.  The wait
+// is bounded: after ~2^26 polls the workgroup raises the abort flag and
+// leaves, so a broken co-residency assumption ends the kernel with an error
+// instead of hanging the device.
 __device__ __forceinline__ bool grid_barrier(unsigned* ctr, int* abort_flag, unsigned& target) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -48,34 +50,29 @@ __device__ __forceinline__ bool grid_barrier(unsigned* ctr, int* abort_flag, uns
 }
 
 // ---------------------------------------------------------------------------
-// graph-engine kernels (one workgroup per row block)
+// graph-engine kernels (one workgroup per (leaf, slot))
 // ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(NT) void k_init(Geom G, Bufs B) {
-  __shared__ Smem<T> sm;
-  const int b = blockIdx.x;
-  phase_init(G, B, b, global_view(G, B, decode(G, b)), sm);
-}
-
 template <typename T>
 __global__ __launch_bounds__(NT) void k_phase_A(Geom G, Bufs B, int off) {
   __shared__ Smem<T> sm;
   phase_A(G, B, blockIdx.x, *B.itbase + off, sm);
 }
 
+// absolute >= 0 selects a fixed iteration (0 = initial restriction of b).
 template <typename T>
-__global__ __launch_bounds__(NT) void k_phase_B(Geom G, Bufs B, int off) {
+__global__ __launch_bounds__(NT) void k_phase_B(Geom G, Bufs B, int off, int absolute) {
   __shared__ Smem<T> sm;
-  const int b = blockIdx.x;
-  phase_B(G, B, b, *B.itbase + off, global_view(G, B, decode(G, b)), sm);
+  extern __shared__ float4 dyn4[];
+  const int it = absolute >= 0 ? absolute : *B.itbase + off;
+  phase_B(G, B, blockIdx.x, it, sm, reinterpret_cast<float*>(dyn4));
 }
 
 template <typename T>
 __global__ __launch_bounds__(NT) void k_phase_C(Geom G, Bufs B, int off, int absolute) {
   __shared__ Smem<T> sm;
-  const int b = blockIdx.x;
+  extern __shared__ float4 dyn4[];
   const int it = absolute >= 0 ? absolute : *B.itbase + off;
-  phase_C(G, B, b, it, global_view(G, B, decode(G, b)), sm);
+  phase_C(G, B, blockIdx.x, it, sm, reinterpret_cast<float*>(dyn4));
 }
 
 // End of a replay: advance the iteration base and publish (replay count, all
@@ -103,41 +100,18 @@ __global__ void k_reset(Bufs B, int itbase, int* host_flag) {
 }
 
 // ---------------------------------------------------------------------------
-// persistent engine
+// persistent engine: workgroups loop over (leaf, slot) items, device-wide
+// barriers separate the phases
 // ---------------------------------------------------------------------------
-// RES: each workgroup owns exactly one row block and copies its rows of U_k and
-// of the level slabs into dynamic LDS once; every later apply reads them there.
-template <typename T, bool RES>
+template <typename T>
 __global__ __launch_bounds__(NT) void k_persistent(Geom G, Bufs B) {
   __shared__ Smem<T> sm;
   extern __shared__ float4 dyn4[];
+  float* dyn = reinterpret_cast<float*>(dyn4);
   unsigned target = 0;
-  FactorView fres{};
-  if constexpr (RES) {
-    const Blk bk = decode(G, blockIdx.x);
-    const FactorView gv = global_view(G, B, bk);
-    float* dyn = reinterpret_cast<float*>(dyn4);
-    const int RB = G.RB;
-    float4* du = reinterpret_cast<float4*>(dyn);
-    for (int e = threadIdx.x; e < RB * LEAF / 4; e += NT) du[e] = ld4(gv.Ub + 4 * e);
-    float* dw = dyn + RB * LEAF;
-    for (int l = 0; l < G.levels; ++l) {
-      float4* d = reinterpret_cast<float4*>(dw + (size_t)l * RB * RANK);
-      const float* src = gv.Wb + (size_t)l * gv.wstride;
-      for (int e = threadIdx.x; e < RB * RANK / 4; e += NT) d[e] = ld4(src + 4 * e);
-    }
-    fres.Ub = dyn;
-    fres.Wb = dw;
-    fres.wstride = (size_t)RB * RANK;
-    __syncthreads();
-  }
-  auto view = [&](int b) -> FactorView {
-    if constexpr (RES) return fres;
-    else return global_view(G, B, decode(G, b));
-  };
-  for (int b = blockIdx.x; b < G.nblk; b += gridDim.x) phase_init(G, B, b, view(b), sm);
+  for (int b = blockIdx.x; b < G.nblk; b += gridDim.x) { phase_B(G, B, b, 0, sm, dyn); __syncthreads(); }
   if (grid_barrier(B.barrier, B.abort_flag, target)) return;
-  for (int b = blockIdx.x; b < G.nblk; b += gridDim.x) phase_C(G, B, b, 0, view(b), sm);
+  for (int b = blockIdx.x; b < G.nblk; b += gridDim.x) { phase_C(G, B, b, 0, sm, dyn); __syncthreads(); }
   if (grid_barrier(B.barrier, B.abort_flag, target)) return;
   for (int it = 1; it <= B.maxit; ++it) {
     // Statuses change only in phase C, before the barrier just passed, so every
@@ -146,33 +120,41 @@ __global__ __launch_bounds__(NT) void k_persistent(Geom G, Bufs B) {
     for (int s = threadIdx.x; s < G.B; s += NT)
       running |= (__hip_atomic_load(&B.st[s].status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ST_RUNNING);
     if (!__syncthreads_or(running)) break;
-    for (int b = blockIdx.x; b < G.nblk; b += gridDim.x) phase_A(G, B, b, it, sm);
+    for (int b = blockIdx.x; b < G.nblk; b += gridDim.x) { phase_A(G, B, b, it, sm); __syncthreads(); }
     if (grid_barrier(B.barrier, B.abort_flag, target)) return;
-    for (int b = blockIdx.x; b < G.nblk; b += gridDim.x) phase_B(G, B, b, it, view(b), sm);
+    for (int b = blockIdx.x; b < G.nblk; b += gridDim.x) { phase_B(G, B, b, it, sm, dyn); __syncthreads(); }
     if (grid_barrier(B.barrier, B.abort_flag, target)) return;
-    for (int b = blockIdx.x; b < G.nblk; b += gridDim.x) phase_C(G, B, b, it, view(b), sm);
+    for (int b = blockIdx.x; b < G.nblk; b += gridDim.x) { phase_C(G, B, b, it, sm, dyn); __syncthreads(); }
     if (grid_barrier(B.barrier, B.abort_flag, target)) return;
   }
 }
 
 // ---------------------------------------------------------------------------
-// standalone apply and SpMV
+// standalone apply (fp32 in and out) and SpMV
 // ---------------------------------------------------------------------------
+// Restriction of r: per leaf slot, the t_k slice and the owned levels' W^T r_k.
 __global__ __launch_bounds__(NT) void k_apply_restrict(Geom G, Bufs B, const float* __restrict__ rin) {
   __shared__ Smem<float> sm;
+  extern __shared__ float4 dyn4[];
+  float* dyn = reinterpret_cast<float*>(dyn4);
   const Blk bk = decode(G, blockIdx.x);
-  if (threadIdx.x < G.RB) sm.r[threadIdx.x] = rin[bk.grow0 + threadIdx.x];
-  __syncthreads();
-  restrict_block(G, B, bk, global_view(G, B, bk), sm);
+  issue_restrict_dma<float>(G, B, bk, dyn);
+  if (threadIdx.x < LEAF) sm.r[threadIdx.x] = rin[bk.leaf0 + threadIdx.x];
+  lds_dma_wait();
+  restrict_leaf(G, B, bk, dyn, sm);
 }
 
+// Prolongation and assembly of y on the workgroup's rows.
 __global__ __launch_bounds__(NT) void k_apply_prolong(Geom G, Bufs B, const float* __restrict__ rin,
                                                        float* __restrict__ yout) {
   __shared__ Smem<float> sm;
+  extern __shared__ float4 dyn4[];
+  float* dyn = reinterpret_cast<float*>(dyn4);
   const Blk bk = decode(G, blockIdx.x);
+  issue_prolong_dma<float>(G, B, bk, dyn, sm);
   if (threadIdx.x < G.RB) sm.r[threadIdx.x] = rin[bk.grow0 + threadIdx.x];
-  __syncthreads();
-  const float y = prolong_block(G, B, bk, global_view(G, B, bk), sm);
+  lds_dma_wait();
+  const float y = prolong_rows(G, B, bk, dyn, sm);
   if (threadIdx.x < G.RB) yout[bk.grow0 + threadIdx.x] = y;
 }
 

@@ -41,7 +41,6 @@ HPCG_ENGINE_PERSISTENT = 2
 
 HPCG_OPT_ENGINE = 1
 HPCG_OPT_GRAPH_UNROLL = 2
-HPCG_OPT_RESIDENT = 3
 HPCG_OPT_PRECISION = 4
 
 HPCG_PREC_VEC64 = 0
@@ -226,10 +225,10 @@ def hpcg_last_engine(h) -> int:
 
 
 def hpcg_last_launch_info(h) -> tuple:
-    """(grid, resident) of the last persistent solve."""
-    grid, res = ctypes.c_int32(), ctypes.c_int32()
-    _check(lib().hpcg_last_launch_info(h, ctypes.byref(grid), ctypes.byref(res)), h)
-    return grid.value, res.value
+    """(workgroups per phase launch, largest dynamic LDS bytes) of the last solve."""
+    grid, lds = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().hpcg_last_launch_info(h, ctypes.byref(grid), ctypes.byref(lds)), h)
+    return grid.value, lds.value
 
 
 def hpcg_status_string(status: int) -> str:

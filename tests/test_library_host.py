@@ -59,8 +59,8 @@ def test_workspace_bytes_covers_the_buffers(hp):
     factors = 128 * 128 * 128 * 4 + 7 * 128 * 128 * 32 * 4
     csr = (16385 + 2 * nnz) * 4
     vectors = 16384 * (2 * 4 + 6 * 8)            # g, b fp32; r, z, q, p0, p1, x fp64
-    partials = (128 * 2 * 128 + 7 * 128 * 2 * 32) * 8
-    need = factors + csr + vectors + partials
+    restrictions = (128 * 128 + 7 * 128 * 32) * 8  # t_k and W_l[k]^T r_k per leaf, fp64
+    need = factors + csr + vectors + restrictions
     assert need <= nbytes <= need + (1 << 20)
     assert hp.hpcg_workspace_bytes(hp.partition(2048, batch=64), 851968) > 64 * hp.hpcg_workspace_bytes(
         hp.partition(2048), 13312) * 0.9
