@@ -13,7 +13,7 @@
 #include <string>
 #include <vector>
 
-#include "hpcg_kernels.hpp"
+#include "hpcg_resident.hpp"
 
 using namespace hpcg;
 
@@ -88,8 +88,11 @@ Layout make_layout(const Geom& G, int64_t nnz) {
   L.p0 = take(N * 8);
   L.p1 = take(N * 8);
   L.x = take(N * 8);
-  L.tleaf = take((size_t)G.B * G.K * LEAF * 8);
-  L.pleaf = take((size_t)G.B * G.levels * G.K * RANK * 8 + 16);
+  // t_k per leaf (streaming engines) also holds W^T q (resident engine): both
+  // need at most B*K*max(LEAF, levels*RANK) values; pleaf holds two copies of
+  // W^T r for the resident engine's ping-pong
+  L.tleaf = take((size_t)G.B * G.K * std::max(LEAF, G.levels * RANK) * 8 + 16);
+  L.pleaf = take(2 * (size_t)G.B * G.levels * G.K * RANK * 8 + 16);
   L.pq = take((size_t)G.nblk * 8);
   L.rr = take((size_t)G.nblk * 8);
   L.rz = take((size_t)G.nblk * 8);
@@ -128,6 +131,7 @@ struct hpcg_ctx {
   int graph_maxit = -1;
   int last_grid = 0;
   int last_lds = 0;
+  int max_leaf_nnz = 0;
   int* h_flag = nullptr;   // pinned, device-mapped
   int* d_flag = nullptr;
   SysState* h_st = nullptr;
@@ -257,6 +261,54 @@ hpcg_status run_graph(hpcg_ctx* h) {
   }
   h->last_grid = G.nblk;
   h->last_lds = (int)std::max(restrict_lds_bytes(G), prolong_lds_bytes<T>(G));
+  return HPCG_OK;
+}
+
+template <typename T>
+const void* resident_kernel(int levels) {
+  switch (levels) {
+    case 0: return reinterpret_cast<const void*>(&k_resident<T, 0>);
+    case 1: return reinterpret_cast<const void*>(&k_resident<T, 1>);
+    case 2: return reinterpret_cast<const void*>(&k_resident<T, 2>);
+    case 3: return reinterpret_cast<const void*>(&k_resident<T, 3>);
+    case 4: return reinterpret_cast<const void*>(&k_resident<T, 4>);
+    case 5: return reinterpret_cast<const void*>(&k_resident<T, 5>);
+    case 6: return reinterpret_cast<const void*>(&k_resident<T, 6>);
+    case 7: return reinterpret_cast<const void*>(&k_resident<T, 7>);
+    case 8: return reinterpret_cast<const void*>(&k_resident<T, 8>);
+    default: return nullptr;
+  }
+}
+
+// Register-resident persistent solve: one 1024-thread workgroup per leaf, all
+// co-resident (one per CU).  Declines (ran = false) when the batch has more
+// leaves than the device has CUs.
+template <typename T>
+hpcg_status run_resident(hpcg_ctx* h, bool& ran) {
+  ran = false;
+  const Geom G = h->G;
+  const Bufs B = h->B;
+  const int items = G.B * G.K;
+  if (!h->coop || items > h->num_cu) return HPCG_OK;
+  const void* fn = resident_kernel<T>(G.levels);
+  if (!fn) return HPCG_OK;
+  const size_t dyn = ((size_t)h->max_leaf_nnz * 8 + (LEAF + 1) * 4 + 15) / 16 * 16 +
+                     2 * (size_t)std::max(G.K - 1, 1) * RANK * sizeof(T);
+  if (dyn + sizeof(RSmem<T>) > kMaxLds) return HPCG_OK;
+  hpcg_status s = allow_lds(h, fn, dyn);
+  if (s != HPCG_OK) return s;
+  int per_cu = 0;
+  HIP_OR_FAIL(h, hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NTR, dyn));
+  if ((int64_t)per_cu * h->num_cu < items) return HPCG_OK;
+  hipLaunchKernelGGL(k_reset, dim3(1), dim3(64), 0, h->stream, B, 0, (int*)nullptr);
+  Geom Ga = G;
+  Bufs Ba = B;
+  int mln = h->max_leaf_nnz;
+  void* args[] = {&Ga, &Ba, &mln};
+  HIP_OR_FAIL(h, hipLaunchCooperativeKernel(fn, dim3(items), dim3(NTR), args, (unsigned)dyn, h->stream));
+  h->last_grid = items;
+  h->last_lds = (int)dyn;
+  ran = true;
   return HPCG_OK;
 }
 
@@ -401,6 +453,8 @@ hpcg_status hpcg_create(const hpcg_partition* part, const int32_t* d_row_ptr, co
         return cleanup_fail(fail(h, HPCG_ERR_SHAPE, "column index outside its system's block"));
   }
 #undef CREATE_HIP
+  for (size_t i0 = 0; i0 < N; i0 += LEAF)
+    h->max_leaf_nnz = std::max(h->max_leaf_nnz, rp[i0 + LEAF] - rp[i0]);
   h->last_status.assign(G.B, HPCG_SYS_RUNNING);
   *out = h;
   return HPCG_OK;
@@ -473,7 +527,9 @@ hpcg_status hpcg_solve(hpcg_handle h, const float* d_b, double* d_x, double tol,
   // full grid (about 10 us at 256 workgroups, dominated by the per-workgroup
   // L2 writeback and invalidate of the release/acquire fences).
   if (h->engine_opt == HPCG_ENGINE_PERSISTENT) {
-    s = f32 ? run_persistent<float>(h, ran) : run_persistent<double>(h, ran);
+    s = f32 ? run_resident<float>(h, ran) : run_resident<double>(h, ran);
+    if (s != HPCG_OK) return s;
+    if (!ran) s = f32 ? run_persistent<float>(h, ran) : run_persistent<double>(h, ran);
     if (s != HPCG_OK) return s;
     if (!ran && h->engine_opt == HPCG_ENGINE_PERSISTENT)
       return fail(h, HPCG_ERR_SHAPE, "persistent engine: device does not support a co-resident grid for this partition");

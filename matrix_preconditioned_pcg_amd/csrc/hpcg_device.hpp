@@ -180,6 +180,17 @@ __device__ __forceinline__ void dma_to_lds(void* dst, int nchunks, AddrFn addr) 
   }
 }
 
+// dma_to_lds for a workgroup of NW waves.
+template <int NW, typename AddrFn>
+__device__ __forceinline__ void dma_to_lds_n(void* dst, int nchunks, AddrFn addr) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int q = wave; q * 64 < nchunks; q += NW) {
+    const int c = q * 64 + lane;
+    lds_vptr l = (lds_vptr)((__attribute__((address_space(3))) char*)dst + q * 1024);
+    if (c < nchunks) __builtin_amdgcn_global_load_lds(addr(c), l, 16, 0, 0);
+  }
+}
+
 // All outstanding global loads (including the DMAs into LDS) of every wave
 // have landed after this.
 __device__ __forceinline__ void lds_dma_wait() {

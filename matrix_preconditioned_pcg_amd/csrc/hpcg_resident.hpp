@@ -1,0 +1,467 @@
+// Register-resident persistent solve for gfx950.
+//
+// One workgroup of NTR = 512 threads (8 wave64 wavefronts, one workgroup per
+// CU, up to 256 VGPRs per lane) owns one leaf of one system for the whole solve:
+//   * its factors live in VGPRs: U_k as eight float4 per thread (rows rg + 16m,
+//     columns 4cs..4cs+3 with cs = tid % 32, rg = tid / 32) and, per level l,
+//     two rows of W_l[k] as float4 (rows tid/8 and tid/8 + 64, columns
+//     4(tid % 8)..);
+//   * its rows of r, q, z and p and its CSR rows live in LDS, x in registers;
+//   * only what other leaves need crosses workgroups: z and p (the SpMV halo),
+//     the per-leaf restrictions W_l[k]^T r_k and W_l[k]^T q_k, and the scalar
+//     partials.
+//
+// Two device-wide barriers per iteration.  The restriction is linear, so
+// W^T r_new = W^T r - alpha W^T q: phase A, which owns the whole leaf's q,
+// restricts q right after the SpMV, and the next phase forms the partner-half
+// sums of (W^T r - alpha W^T q) and applies M to r_new without another
+// barrier.  W^T r is recomputed exactly from r_new every iteration (into the
+// other of two buffers), so the recurrence never accumulates rounding drift.
+//   A(it):  convergence test on ||r_{it-1}||; beta; p = z + beta p;
+//           q = A p; t_q = U_k^T q, W_l[k]^T q; partial p.q
+//   BC(it): alpha; x += alpha p; r -= alpha q; partial r.r;
+//           z = U_k (t_r - alpha t_q) + sum_l W_l[k] P_l + g r with
+//           P_l = partner-half sum of (W^T r - alpha W^T q);  partial r.z;
+//           t_r = U_k^T r, W_l[k]^T r for the next iteration
+// Per iteration the factors are never reloaded.
+#pragma once
+#include "hpcg_kernels.hpp"
+
+namespace hpcg {
+
+constexpr int NTR = 512;
+constexpr int NWR = NTR / 64;
+
+template <typename T>
+struct alignas(16) RSmem {
+  T r[LEAF];
+  T q[LEAF];
+  T z[LEAF];
+  T p[LEAF];                         // p of the current iteration (own rows)
+  T tr[LEAF];                        // U_k^T r
+  T tq[LEAF];                        // U_k^T q
+  T t[LEAF];                         // U_k^T r_new = tr - alpha tq
+  T P[MAX_LEVELS * RANK];            // partner-half sums
+  T yleaf[LEAF];
+  T yoff[LEAF];
+  T red[NWR][LEAF];                  // cross-wave reductions of t
+  T redW[NWR][2 * MAX_LEVELS * RANK];  // cross-wave reductions (restriction, strip sums)
+  double dred[NWR];
+  double dsc[4];
+  int flag[4];
+};
+
+// Sum over the workgroup in a fixed order.
+template <typename T>
+__device__ __forceinline__ double wg_sum_r(double v, RSmem<T>& sm) {
+  v = wave_sum(v);
+  const int tid = threadIdx.x;
+  if ((tid & 63) == 0) sm.dred[tid >> 6] = v;
+  __syncthreads();
+  double s = sm.dred[0];
+#pragma unroll
+  for (int w = 1; w < NWR; ++w) s += sm.dred[w];
+  __syncthreads();
+  return s;
+}
+
+// Every wave reads the system's K partials and sums them in the same order.
+__device__ __forceinline__ double sum_partials_r(const double* part, int s, int K) {
+  double v = 0.0;
+  const double* p = part + (size_t)s * K;
+  for (int j = threadIdx.x & 63; j < K; j += 64) v += p[j];
+  return wave_sum(v);
+}
+
+template <typename T, int LEV>
+struct Resident {
+  float4 u[8];
+  float4 w[LEV > 0 ? LEV : 1][2];
+};
+
+// Restriction of the LDS vector v: U_k^T v into tout (LDS, complete) and
+// W_l[k]^T v into pout (global, [levels][K][RANK] of system s).
+template <typename T, int LEV>
+__device__ __forceinline__ void r_restrict(const Geom& G, int s, int k, const Resident<T, LEV>& F,
+                                           const T* v, T* tout, T* pout, RSmem<T>& sm) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  {
+    const int cs = tid & 31, rg = tid >> 5;
+    Vec4<T> acc{0, 0, 0, 0};
+#pragma unroll
+    for (int m = 0; m < 8; ++m) axpy4(acc, F.u[m], v[rg + 16 * m]);
+    acc.x += __shfl_xor(acc.x, 32); acc.y += __shfl_xor(acc.y, 32);
+    acc.z += __shfl_xor(acc.z, 32); acc.w += __shfl_xor(acc.w, 32);
+    if (lane < 32) {
+      T* d = &sm.red[wave][4 * cs];
+      d[0] = acc.x; d[1] = acc.y; d[2] = acc.z; d[3] = acc.w;
+    }
+  }
+  if constexpr (LEV > 0) {
+    // thread = (4-column slot cs of 8, rows row and row + 64); the eight rows of
+    // a wave (lane bits 3..5) are folded per pair of levels with a
+    // transpose-reduce: 8 values -> 1 per lane in 4 + 2 + 1 shuffles
+    const int cs = tid & 7, row = tid >> 3;
+    const T r0 = v[row], r1 = v[row + 64];
+    const bool b5 = (lane & 32) != 0, b4 = (lane & 16) != 0, b3 = (lane & 8) != 0;
+    const int which = (b5 ? 4 : 0) + (b4 ? 2 : 0) + (b3 ? 1 : 0);   // value index a lane ends with
+#pragma unroll
+    for (int l0 = 0; l0 < LEV; l0 += 2) {
+      T x[8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        Vec4<T> acc{0, 0, 0, 0};
+        if (l0 + h < LEV) {
+          axpy4(acc, F.w[l0 + h < LEV ? l0 + h : 0][0], r0);
+          axpy4(acc, F.w[l0 + h < LEV ? l0 + h : 0][1], r1);
+        }
+        x[4 * h + 0] = acc.x; x[4 * h + 1] = acc.y; x[4 * h + 2] = acc.z; x[4 * h + 3] = acc.w;
+      }
+      T a[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const T keep = b5 ? x[4 + i] : x[i], send = b5 ? x[i] : x[4 + i];
+        a[i] = keep + __shfl_xor(send, 32);
+      }
+      T bb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const T keep = b4 ? a[2 + i] : a[i], send = b4 ? a[i] : a[2 + i];
+        bb[i] = keep + __shfl_xor(send, 16);
+      }
+      T kk = b3 ? bb[1] : bb[0];
+      kk += __shfl_xor(b3 ? bb[0] : bb[1], 8);
+      // value index `which` = 4h + component: level l0 + which/4, column 4cs + which%4
+      const int l = l0 + (which >> 2);
+      if (l < LEV) sm.redW[wave][l * RANK + 4 * cs + (which & 3)] = kk;
+    }
+  }
+  __syncthreads();
+  if (tid < LEAF) {
+    T a = sm.red[0][tid];
+#pragma unroll
+    for (int w = 1; w < NWR; ++w) a += sm.red[w][tid];
+    tout[tid] = a;
+  }
+  if constexpr (LEV > 0) {
+    if (tid < LEV * RANK) {
+      T a = sm.redW[0][tid];
+#pragma unroll
+      for (int w = 1; w < NWR; ++w) a += sm.redW[w][tid];
+      const int l = tid / RANK, c = tid - l * RANK;
+      pout[(((size_t)s * G.levels + l) * G.K + k) * RANK + c] = a;
+    }
+  }
+  __syncthreads();
+}
+
+// Issue the DMA of the partner halves' per-leaf restrictions of every level
+// from src ([B][levels][K][RANK]) into `stage` (level l at row 2^l - 1); the
+// caller waits with lds_dma_wait().
+template <typename T, int LEV>
+__device__ __forceinline__ void r_stage_partners(const Geom& G, const T* src, int s, int k, T* stage) {
+  constexpr int CPV = RANK * sizeof(T) / 16;
+#pragma unroll
+  for (int l = 0; l < LEV; ++l) {
+    const int kp0 = ((k >> l) ^ 1) << l;
+    const T* from = src + (((size_t)s * G.levels + l) * G.K + kp0) * RANK;
+    dma_to_lds_n<NWR>(stage + (size_t)((1 << l) - 1) * RANK, (1 << l) * CPV,
+                      [&](int c) { return reinterpret_cast<const char*>(from) + 16 * c; });
+  }
+}
+
+// z = M r_new on the leaf's rows into sm.z.  Needs sm.t (= U_k^T r_new), sm.r
+// (= r_new) and the staged partner restrictions of r (stR) and q (stQ):
+// P_l = sum(stR) - alpha sum(stQ).  With stQ == nullptr, P_l = sum(stR).
+template <typename T, int LEV>
+__device__ __forceinline__ void r_prolong(const Resident<T, LEV>& F, RSmem<T>& sm, const T* stR, const T* stQ,
+                                          double alpha, float gate) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if constexpr (LEV > 0) {
+    // strip aggregation (eq. (3)) from the staged partner restrictions (level l
+    // at stage row 2^l - 1): 16 groups of threads per column, then across waves
+    const int c = tid & 31, g = tid >> 5;
+#pragma unroll
+    for (int l = 0; l < LEV; ++l) {
+      const T* vr = stR + (size_t)((1 << l) - 1) * RANK + c;
+      T a = 0, b = 0;
+#pragma unroll
+      for (int m = 0; m < ((1 << l) + 15) / 16; ++m) {
+        const int i = g + 16 * m;
+        if (i < (1 << l)) {
+          a += vr[i * RANK];
+          if (stQ) b += stQ[(size_t)((1 << l) - 1) * RANK + c + i * RANK];
+        }
+      }
+      a += __shfl_xor(a, 32);
+      b += __shfl_xor(b, 32);
+      if (lane < 32) {
+        sm.redW[wave][l * RANK + c] = a;
+        sm.redW[wave][(MAX_LEVELS + l) * RANK + c] = b;
+      }
+    }
+    __syncthreads();
+    if (tid < LEV * RANK) {
+      T a = sm.redW[0][tid], b = sm.redW[0][MAX_LEVELS * RANK + tid];
+#pragma unroll
+      for (int w = 1; w < NWR; ++w) { a += sm.redW[w][tid]; b += sm.redW[w][MAX_LEVELS * RANK + tid]; }
+      sm.P[tid] = stQ ? (T)((double)a - alpha * (double)b) : a;
+    }
+    __syncthreads();
+  }
+  // diagonal stage: rows rg + 16m (m < 8), dots over 32 column slots; the eight
+  // rows of a lane are folded with a transpose-reduce (7 + 2 shuffles)
+  {
+    const int cs = tid & 31, rg = tid >> 5;
+    const Vec4<T> t4 = lds4(&sm.t[4 * cs]);
+    T v[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) v[m] = dot4(F.u[m], t4);
+    const bool b4 = (cs & 16) != 0, b3 = (cs & 8) != 0, b2 = (cs & 4) != 0;
+    T a[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {           // xor 16: keep the upper four rows if b4
+      const T keep = b4 ? v[4 + i] : v[i], send = b4 ? v[i] : v[4 + i];
+      a[i] = keep + __shfl_xor(send, 16);
+    }
+    T bb[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {           // xor 8
+      const T keep = b3 ? a[2 + i] : a[i], send = b3 ? a[i] : a[2 + i];
+      bb[i] = keep + __shfl_xor(send, 8);
+    }
+    T kk = b2 ? bb[1] : bb[0];              // xor 4
+    kk += __shfl_xor(b2 ? bb[0] : bb[1], 4);
+    kk += __shfl_xor(kk, 2);
+    kk += __shfl_xor(kk, 1);
+    if ((cs & 3) == 0) sm.yleaf[rg + 16 * ((b4 ? 4 : 0) + (b3 ? 2 : 0) + (b2 ? 1 : 0))] = kk;
+  }
+  if constexpr (LEV > 0) {
+    const int cs = tid & 7, row = tid >> 3;
+    T o0 = 0, o1 = 0;
+#pragma unroll
+    for (int l = 0; l < LEV; ++l) {
+      const Vec4<T> p4 = lds4(&sm.P[l * RANK + 4 * cs]);
+      o0 += dot4(F.w[l][0], p4);
+      o1 += dot4(F.w[l][1], p4);
+    }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) { o0 += __shfl_xor(o0, o); o1 += __shfl_xor(o1, o); }
+    if (cs == 0) { sm.yoff[row] = o0; sm.yoff[row + 64] = o1; }
+  } else {
+    if (tid < LEAF) sm.yoff[tid] = 0;
+  }
+  __syncthreads();
+  if (tid < LEAF) sm.z[tid] = sm.yleaf[tid] + sm.yoff[tid] + (T)gate * sm.r[tid];
+  __syncthreads();
+}
+
+template <typename T, int LEV>
+__global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_nnz) {
+  __shared__ RSmem<T> sm;
+  extern __shared__ int4 rdyn4[];
+  int* colL = reinterpret_cast<int*>(rdyn4);
+  float* valL = reinterpret_cast<float*>(colL + max_leaf_nnz);
+  int* rpL = reinterpret_cast<int*>(valL + max_leaf_nnz);
+  const int stage_rows = G.K > 1 ? G.K - 1 : 1;
+  T* stR = reinterpret_cast<T*>(rdyn4 + (2 * max_leaf_nnz + LEAF + 1 + 3) / 4);
+  T* stQ = stR + (size_t)stage_rows * RANK;
+  const int tid = threadIdx.x;
+  const int item = blockIdx.x;
+  const int s = item / G.K, k = item - s * G.K;
+  const int leaf0 = s * G.n + k * LEAF;
+  SysState* st = B.st + s;
+  const bool lead = (tid == 0 && k == 0);
+  unsigned target = 0;
+  // restriction buffers: W^T r in two halves of pleaf (ping-pong), W^T q in tleaf
+  const size_t half = (size_t)G.B * G.levels * G.K * RANK;
+  T* pR[2] = {reinterpret_cast<T*>(B.pleaf), reinterpret_cast<T*>(B.pleaf) + half};
+  T* pQ = reinterpret_cast<T*>(B.tleaf);
+  int rbuf = 0;
+
+  // ---- factors into registers, CSR rows into LDS ----
+  Resident<T, LEV> F;
+  {
+    const int cs = tid & 31, rg = tid >> 5;
+    const float* Uk = B.U + ((size_t)s * G.K + k) * LEAF * LEAF;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) F.u[m] = *reinterpret_cast<const float4*>(Uk + (rg + 16 * m) * LEAF + 4 * cs);
+    if constexpr (LEV > 0) {
+      const int c8 = tid & 7, row = tid >> 3;
+#pragma unroll
+      for (int l = 0; l < LEV; ++l) {
+        const float* Wl = B.W + (((size_t)s * G.levels + l) * G.K + k) * LEAF * RANK;
+        F.w[l][0] = *reinterpret_cast<const float4*>(Wl + row * RANK + 4 * c8);
+        F.w[l][1] = *reinterpret_cast<const float4*>(Wl + (row + 64) * RANK + 4 * c8);
+      }
+    }
+  }
+  const int e_begin = B.row_ptr[leaf0];
+  if (tid <= LEAF) rpL[tid] = B.row_ptr[leaf0 + tid] - e_begin;
+  const int leaf_nnz = B.row_ptr[leaf0 + LEAF] - e_begin;
+  for (int e = tid; e < leaf_nnz; e += NTR) {
+    colL[e] = B.col[e_begin + e];
+    valL[e] = B.val[e_begin + e];
+  }
+  const float gate = (tid < LEAF) ? B.g[leaf0 + tid] : 0.f;
+  double x = 0.0;                      // x of row tid (tid < LEAF)
+  T* zg = reinterpret_cast<T*>(B.z);
+
+  // ---- r = b, its restriction (t_r, W^T r), ||b||^2 ----
+  double loc = 0.0;
+  if (tid < LEAF) {
+    const T bv = (T)B.b[leaf0 + tid];
+    sm.r[tid] = bv;
+    loc = (double)bv * (double)bv;
+  }
+  __syncthreads();
+  r_restrict<T, LEV>(G, s, k, F, sm.r, sm.tr, pR[0], sm);
+  double part = wg_sum_r(loc, sm);
+  if (tid == 0) {
+    B.rr_part[item] = part;
+    if (k == 0) {
+      st->relres = 1.0;
+      st->brk = 0;
+      st->brk_it = 0;
+      set_state(st, ST_RUNNING, 0);
+    }
+  }
+  if (grid_barrier(B.barrier, B.abort_flag, target)) return;
+
+  // ---- z0 = M r0 ----
+  bool done = false;                   // this system has finished (decided locally)
+  double bnorm = 1.0, rz_old = 1.0;
+  {
+    if constexpr (LEV > 0) r_stage_partners<T, LEV>(G, pR[0], s, k, stR);
+    const double rr = sum_partials_r(B.rr_part, s, G.K);
+    lds_dma_wait();
+    bnorm = sqrt(rr);
+    if (rr == 0.0) {
+      done = true;
+      if (lead) { st->bnorm = 0.0; st->relres = 0.0; set_state(st, ST_CONVERGED, 0); }
+    } else {
+      if (lead) st->bnorm = bnorm;
+      if (tid < LEAF) sm.t[tid] = sm.tr[tid];
+      __syncthreads();
+      r_prolong<T, LEV>(F, sm, stR, (const T*)nullptr, 0.0, gate);
+      loc = 0.0;
+      if (tid < LEAF) {
+        zg[leaf0 + tid] = sm.z[tid];
+        loc = (double)sm.r[tid] * (double)sm.z[tid];
+      }
+      part = wg_sum_r(loc, sm);
+      if (tid == 0) B.rz_part[item] = part;
+    }
+  }
+  if (grid_barrier(B.barrier, B.abort_flag, target)) return;
+
+  // Statuses are written by each system's lead only in the second phase of an
+  // iteration and read by everyone only in the first, so every workgroup sees
+  // the same values and leaves the loop together.
+  int pend_status = ST_RUNNING, pend_iters = 0;
+  double pend_rel = 0.0;
+  for (int it = 1; it <= B.maxit + 2; ++it) {
+    // ---------------- phase A (it) ----------------
+    {
+      int running = 0;
+      for (int q = tid; q < G.B; q += NTR)
+        running |= (__hip_atomic_load(&B.st[q].status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ST_RUNNING);
+      const double rr = sum_partials_r(B.rr_part, s, G.K);
+      const double rz = sum_partials_r(B.rz_part, s, G.K);
+      if (!__syncthreads_or(running)) break;
+      if (!done && it >= 2) {
+        const double rel = sqrt(rr) / bnorm;
+        if (rel <= B.tol) {
+          done = true; pend_status = ST_CONVERGED; pend_iters = it - 1; pend_rel = rel;
+        } else if (it - 1 >= B.maxit) {
+          done = true; pend_status = ST_NOT_CONVERGED; pend_iters = B.maxit; pend_rel = rel;
+        } else {
+          pend_rel = rel;
+        }
+      }
+      if (!done && (!(rz > 0.0) || !isfinite(rz))) {
+        done = true; pend_status = ST_BREAKDOWN; pend_iters = it - 1;
+      }
+      if (!done) {
+        const bool first = (it == 1);
+        const double beta = first ? 0.0 : rz / rz_old;
+        rz_old = rz;
+        sm.dsc[0] = rz;
+        const T* pold = reinterpret_cast<const T*>((it & 1) ? B.p0 : B.p1);
+        T* pnew = reinterpret_cast<T*>((it & 1) ? B.p1 : B.p0);
+        // SpMV: 4 threads per row, CSR rows from LDS, z and p gathered globally
+        const int row = tid >> 2, lr = tid & 3;
+        const int e0 = rpL[row], e1 = rpL[row + 1];
+        T acc = 0;
+        for (int e = e0 + lr; e < e1; e += 4) {
+          const int c = colL[e];
+          const T v = first ? zg[c] : pdir<T>(zg[c], pold[c], beta);
+          acc = fma((T)valL[e], v, acc);
+        }
+        acc += __shfl_xor(acc, 1);
+        acc += __shfl_xor(acc, 2);
+        loc = 0.0;
+        if (lr == 0) {
+          const T pn = first ? sm.z[row] : pdir<T>(sm.z[row], sm.p[row], beta);
+          sm.p[row] = pn;
+          sm.q[row] = acc;
+          pnew[leaf0 + row] = pn;
+          loc = (double)pn * (double)acc;
+        }
+        __syncthreads();
+        r_restrict<T, LEV>(G, s, k, F, sm.q, sm.tq, pQ, sm);
+        part = wg_sum_r(loc, sm);
+        if (tid == 0) B.pq_part[item] = part;
+      }
+    }
+    if (grid_barrier(B.barrier, B.abort_flag, target)) return;
+    // ---------------- phase BC (it) ----------------
+    {
+      if (lead && pend_status != ST_RUNNING) {
+        st->relres = pend_rel;
+        set_state(st, pend_status, pend_iters);
+        pend_status = ST_RUNNING;   // written once
+      }
+      if (!done) {
+        if constexpr (LEV > 0) {
+          r_stage_partners<T, LEV>(G, pR[rbuf], s, k, stR);
+          r_stage_partners<T, LEV>(G, pQ, s, k, stQ);
+        }
+        const double pq = sum_partials_r(B.pq_part, s, G.K);
+        lds_dma_wait();
+        if (!(pq > 0.0) || !isfinite(pq)) {
+          done = true;
+          if (lead) set_state(st, ST_BREAKDOWN, it);
+        } else {
+          const double alpha = rz_old / pq;
+          loc = 0.0;
+          if (tid < LEAF) {
+            const T rn = (T)((double)sm.r[tid] - alpha * (double)sm.q[tid]);
+            sm.r[tid] = rn;
+            x += alpha * (double)sm.p[tid];
+            loc = (double)rn * (double)rn;
+            sm.t[tid] = (T)((double)sm.tr[tid] - alpha * (double)sm.tq[tid]);
+          }
+          part = wg_sum_r(loc, sm);
+          if (tid == 0) B.rr_part[item] = part;
+          r_prolong<T, LEV>(F, sm, stR, stQ, alpha, gate);
+          loc = 0.0;
+          if (tid < LEAF) {
+            zg[leaf0 + tid] = sm.z[tid];
+            loc = (double)sm.r[tid] * (double)sm.z[tid];
+          }
+          part = wg_sum_r(loc, sm);
+          if (tid == 0) B.rz_part[item] = part;
+          // exact restriction of the new r for the next iteration
+          rbuf ^= 1;
+          r_restrict<T, LEV>(G, s, k, F, sm.r, sm.tr, pR[rbuf], sm);
+        }
+      }
+    }
+    if (grid_barrier(B.barrier, B.abort_flag, target)) return;
+  }
+  // ---- the solution of the leaf's rows ----
+  if (tid < LEAF) B.x[leaf0 + tid] = x;
+}
+
+}  // namespace hpcg
