@@ -96,11 +96,16 @@ typedef struct {
 
 /* Solve engines (hpcg_set_option(HPCG_OPT_ENGINE, ...)). */
 typedef enum {
-    HPCG_ENGINE_AUTO = 0,       /* the graph engine (the faster one on gfx950)    */
+    HPCG_ENGINE_AUTO = 0,       /* persistent (register-resident) when every leaf
+                                   of the batch gets a CU, else graph            */
     HPCG_ENGINE_GRAPH = 1,      /* per-phase kernels, unrolled iterations replayed
                                    as one hipGraph, host polls a pinned flag      */
     HPCG_ENGINE_PERSISTENT = 2  /* one cooperative launch runs the whole solve with
-                                   device-wide barriers between phases            */
+                                   device-wide barriers between phases: one
+                                   512-thread workgroup per leaf with the factors
+                                   in VGPRs when B*K <= #CUs (two barriers per
+                                   iteration), else workgroups streaming the
+                                   factors (three barriers per iteration)        */
 } hpcg_engine;
 
 typedef enum {

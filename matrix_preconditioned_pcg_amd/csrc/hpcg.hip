@@ -522,14 +522,18 @@ hpcg_status hpcg_solve(hpcg_handle h, const float* d_b, double* d_x, double tol,
   hpcg_status s = HPCG_OK;
   bool ran = false;
   const bool f32 = (h->prec == HPCG_PREC_VEC32);
-  // AUTO runs the graph engine: on gfx950 a kernel boundary inside a graph
-  // (about 2 us) is cheaper than an agent-scope device-wide barrier over a
-  // full grid (about 10 us at 256 workgroups, dominated by the per-workgroup
-  // L2 writeback and invalidate of the release/acquire fences).
-  if (h->engine_opt == HPCG_ENGINE_PERSISTENT) {
+  // AUTO runs the register-resident persistent engine when every leaf of the
+  // batch gets its own CU (B*K <= #CUs): the factors then never leave VGPRs
+  // and an iteration costs two device-wide barriers.  Larger batches run the
+  // graph engine: a kernel boundary inside a graph (about 2 us) is cheaper
+  // than an agent-scope barrier over a full grid of streaming workgroups
+  // (about 10 us at 256 workgroups, dominated by the per-workgroup L2
+  // writeback and invalidate of the release/acquire fences).
+  if (h->engine_opt == HPCG_ENGINE_PERSISTENT || h->engine_opt == HPCG_ENGINE_AUTO) {
     s = f32 ? run_resident<float>(h, ran) : run_resident<double>(h, ran);
     if (s != HPCG_OK) return s;
-    if (!ran) s = f32 ? run_persistent<float>(h, ran) : run_persistent<double>(h, ran);
+    if (!ran && h->engine_opt == HPCG_ENGINE_PERSISTENT)
+      s = f32 ? run_persistent<float>(h, ran) : run_persistent<double>(h, ran);
     if (s != HPCG_OK) return s;
     if (!ran && h->engine_opt == HPCG_ENGINE_PERSISTENT)
       return fail(h, HPCG_ERR_SHAPE, "persistent engine: device does not support a co-resident grid for this partition");

@@ -226,13 +226,67 @@ __device__ __forceinline__ void axpy4(Vec4<T>& acc, float4 u, T s) {
   acc.w = fma((T)u.w, s, acc.w);
 }
 
+// ---------------------------------------------------------------------------
+// Cross-lane exchanges without the LDS crossbar.  gfx950 maps xor-32 and
+// xor-16 partners with v_permlane32_swap / v_permlane16_swap (the swapped
+// half is selected by lane bit 5 / 4), xor 8 with DPP row_ror:8, xor 2 and
+// xor 1 with DPP quad_perm, and pairs lane j with 7 - j inside each group of
+// eight with DPP row_half_mirror (a perfect matching between the lower and
+// upper four lanes, which is all a reduction over those lanes needs).
+// 64-bit values are exchanged word by word.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ int dpp_word(int w) {
+  return __builtin_amdgcn_update_dpp(0, w, CTRL, 0xf, 0xf, false);
+}
+
+template <typename T, typename Fn>
+__device__ __forceinline__ T per_word(T v, Fn fn) {
+  if constexpr (sizeof(T) == 4) {
+    return __int_as_float(fn(__float_as_int(v)));
+  } else {
+    const int lo = __double2loint(v), hi = __double2hiint(v);
+    return __hiloint2double(fn(hi), fn(lo));
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ T lane_x1(T v) { return per_word(v, [](int w) { return dpp_word<0xb1>(w); }); }
+template <typename T>
+__device__ __forceinline__ T lane_x2(T v) { return per_word(v, [](int w) { return dpp_word<0x4e>(w); }); }
+template <typename T>
+__device__ __forceinline__ T lane_m4(T v) { return per_word(v, [](int w) { return dpp_word<0x141>(w); }); }
+template <typename T>
+__device__ __forceinline__ T lane_x8(T v) { return per_word(v, [](int w) { return dpp_word<0x128>(w); }); }
+template <typename T>
+__device__ __forceinline__ T lane_x16(T v) {
+  return per_word(v, [](int w) {
+    const auto p = __builtin_amdgcn_permlane16_swap((unsigned)w, (unsigned)w, false, false);
+    return (int)((threadIdx.x & 16) ? p[0] : p[1]);
+  });
+}
+template <typename T>
+__device__ __forceinline__ T lane_x32(T v) {
+  return per_word(v, [](int w) {
+    const auto p = __builtin_amdgcn_permlane32_swap((unsigned)w, (unsigned)w, false, false);
+    return (int)((threadIdx.x & 32) ? p[0] : p[1]);
+  });
+}
+
+// Sum over groups of 4 / 8 consecutive lanes (every lane of the group gets it).
+template <typename T>
+__device__ __forceinline__ T group4_sum(T v) { v += lane_x1(v); return v + lane_x2(v); }
+template <typename T>
+__device__ __forceinline__ T group8_sum(T v) { v = group4_sum(v); return v + lane_m4(v); }
+
 // Sum of a system's per-workgroup partials, computed by every wave in the same
 // order (xor butterflies add commutative pairs), hence bitwise identical in
 // every wave and every workgroup.  Loads are issued by the caller's batch.
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v = group8_sum(v);
+  v += lane_x8(v);
+  v += lane_x16(v);
+  return v + lane_x32(v);
 }
 
 __device__ __forceinline__ double load_partials(const double* part, int s, int nblk_sys) {

@@ -90,8 +90,8 @@ __device__ __forceinline__ void r_restrict(const Geom& G, int s, int k, const Re
     Vec4<T> acc{0, 0, 0, 0};
 #pragma unroll
     for (int m = 0; m < 8; ++m) axpy4(acc, F.u[m], v[rg + 16 * m]);
-    acc.x += __shfl_xor(acc.x, 32); acc.y += __shfl_xor(acc.y, 32);
-    acc.z += __shfl_xor(acc.z, 32); acc.w += __shfl_xor(acc.w, 32);
+    acc.x += lane_x32(acc.x); acc.y += lane_x32(acc.y);
+    acc.z += lane_x32(acc.z); acc.w += lane_x32(acc.w);
     if (lane < 32) {
       T* d = &sm.red[wave][4 * cs];
       d[0] = acc.x; d[1] = acc.y; d[2] = acc.z; d[3] = acc.w;
@@ -121,16 +121,16 @@ __device__ __forceinline__ void r_restrict(const Geom& G, int s, int k, const Re
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const T keep = b5 ? x[4 + i] : x[i], send = b5 ? x[i] : x[4 + i];
-        a[i] = keep + __shfl_xor(send, 32);
+        a[i] = keep + lane_x32(send);
       }
       T bb[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const T keep = b4 ? a[2 + i] : a[i], send = b4 ? a[i] : a[2 + i];
-        bb[i] = keep + __shfl_xor(send, 16);
+        bb[i] = keep + lane_x16(send);
       }
       T kk = b3 ? bb[1] : bb[0];
-      kk += __shfl_xor(b3 ? bb[0] : bb[1], 8);
+      kk += lane_x8(b3 ? bb[0] : bb[1]);
       // value index `which` = 4h + component: level l0 + which/4, column 4cs + which%4
       const int l = l0 + (which >> 2);
       if (l < LEV) sm.redW[wave][l * RANK + 4 * cs + (which & 3)] = kk;
@@ -193,8 +193,8 @@ __device__ __forceinline__ void r_prolong(const Resident<T, LEV>& F, RSmem<T>& s
           if (stQ) b += stQ[(size_t)((1 << l) - 1) * RANK + c + i * RANK];
         }
       }
-      a += __shfl_xor(a, 32);
-      b += __shfl_xor(b, 32);
+      a += lane_x32(a);
+      b += lane_x32(b);
       if (lane < 32) {
         sm.redW[wave][l * RANK + c] = a;
         sm.redW[wave][(MAX_LEVELS + l) * RANK + c] = b;
@@ -222,18 +222,17 @@ __device__ __forceinline__ void r_prolong(const Resident<T, LEV>& F, RSmem<T>& s
 #pragma unroll
     for (int i = 0; i < 4; ++i) {           // xor 16: keep the upper four rows if b4
       const T keep = b4 ? v[4 + i] : v[i], send = b4 ? v[i] : v[4 + i];
-      a[i] = keep + __shfl_xor(send, 16);
+      a[i] = keep + lane_x16(send);
     }
     T bb[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {           // xor 8
       const T keep = b3 ? a[2 + i] : a[i], send = b3 ? a[i] : a[2 + i];
-      bb[i] = keep + __shfl_xor(send, 8);
+      bb[i] = keep + lane_x8(send);
     }
-    T kk = b2 ? bb[1] : bb[0];              // xor 4
-    kk += __shfl_xor(b2 ? bb[0] : bb[1], 4);
-    kk += __shfl_xor(kk, 2);
-    kk += __shfl_xor(kk, 1);
+    T kk = b2 ? bb[1] : bb[0];              // bit 2 (lane j pairs with 7 - j)
+    kk += lane_m4(b2 ? bb[0] : bb[1]);
+    kk = group4_sum(kk);
     if ((cs & 3) == 0) sm.yleaf[rg + 16 * ((b4 ? 4 : 0) + (b3 ? 2 : 0) + (b2 ? 1 : 0))] = kk;
   }
   if constexpr (LEV > 0) {
@@ -245,8 +244,8 @@ __device__ __forceinline__ void r_prolong(const Resident<T, LEV>& F, RSmem<T>& s
       o0 += dot4(F.w[l][0], p4);
       o1 += dot4(F.w[l][1], p4);
     }
-#pragma unroll
-    for (int o = 1; o < 8; o <<= 1) { o0 += __shfl_xor(o0, o); o1 += __shfl_xor(o1, o); }
+    o0 = group8_sum(o0);
+    o1 = group8_sum(o1);
     if (cs == 0) { sm.yoff[row] = o0; sm.yoff[row + 64] = o1; }
   } else {
     if (tid < LEAF) sm.yoff[tid] = 0;
@@ -398,8 +397,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
           const T v = first ? zg[c] : pdir<T>(zg[c], pold[c], beta);
           acc = fma((T)valL[e], v, acc);
         }
-        acc += __shfl_xor(acc, 1);
-        acc += __shfl_xor(acc, 2);
+        acc = group4_sum(acc);
         loc = 0.0;
         if (lr == 0) {
           const T pn = first ? sm.z[row] : pdir<T>(sm.z[row], sm.p[row], beta);
