@@ -59,16 +59,17 @@ def tile_count(K: int, levels: int | None = None) -> int:
     return len(tiles(K, levels))
 
 
-def apply_M(U, W, g, r):
+def apply_M(U, W, g, r, dtype=np.float64):
     """y = M r for one system, structured (M is never formed).
 
     U: [K, L, L] leaf factors; W: [levels, K, L, R] per-level slabs;
-    g: [N] gate; r: [N].  Everything is promoted to fp64.
+    g: [N] gate; r: [N].  Everything is promoted to fp64 (or to `dtype`, e.g.
+    np.longdouble for an extended-precision reference run).
     """
-    U = np.asarray(U, dtype=np.float64)
-    W = np.asarray(W, dtype=np.float64)
-    g = np.asarray(g, dtype=np.float64)
-    r = np.asarray(r, dtype=np.float64)
+    U = np.asarray(U, dtype=dtype)
+    W = np.asarray(W, dtype=dtype)
+    g = np.asarray(g, dtype=dtype)
+    r = np.asarray(r, dtype=dtype)
     K, L, _ = U.shape
     levels = W.shape[0]
     R = W.shape[3] if levels else 0

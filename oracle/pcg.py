@@ -18,9 +18,11 @@ preconditioned CG algorithm in section 9.2) with x_0 = 0, so r_0 = b:
 Readings taken where the pages are silent: the iteration count is the number
 of products q = A p done when the test first passes; the test uses the
 recursively updated r; a non-positive or non-finite p.q or r.z stops the loop
-as a breakdown.  Everything here is fp64 (the pages keep only scalars in fp64;
-the GPU path's vectors are fp32, which is what the iteration-count tolerance
-absorbs).
+as a breakdown.  Everything here is fp64 by default.  The same loop also runs
+in extended precision (dtype=np.longdouble, 64-bit significand): CG's
+iteration count on a badly conditioned system drifts with rounding, and the
+extended run is the near-exact count that a fp64 run with any summation order
+should not undercut by much.
 """
 
 from __future__ import annotations
@@ -43,55 +45,57 @@ class PCGResult:
     history: list = field(default_factory=list)   # ||r_k|| / ||b|| for k = 1 ..
 
 
-def pcg(row_ptr, col, val, b, precond, tol: float, maxit: int) -> PCGResult:
+def pcg(row_ptr, col, val, b, precond, tol: float, maxit: int, dtype=np.float64) -> PCGResult:
     """Solve A x = b.  precond is either a callable r -> M r or a tuple (U, W, g)
-    of preconditioner factors applied with the structured apply."""
+    of preconditioner factors applied with the structured apply.  Vectors and
+    scalars are carried in `dtype` (fp64 unless asked otherwise)."""
     if callable(precond):
         apply = precond
     else:
         U, W, g = precond
 
         def apply(v):
-            return apply_M(U, W, g, v)
+            return apply_M(U, W, g, v, dtype)
 
-    b = np.asarray(b, dtype=np.float64)
+    def norm(v):
+        return dtype(np.linalg.norm(v))
+
+    b = np.asarray(b, dtype=dtype)
     x = np.zeros_like(b)
     r = b.copy()
-    bnorm = float(np.linalg.norm(b))
+    bnorm = norm(b)
     if bnorm == 0.0:
         return PCGResult(x, 0, "converged", 0.0, 0.0, [])
-    z = np.asarray(apply(r), dtype=np.float64)
+
+    def out(it, status, rel):
+        return PCGResult(x, it, status, float(rel), true_relres(row_ptr, col, val, b, x, dtype), history)
+
+    z = np.asarray(apply(r), dtype=dtype)
     p = z.copy()
-    rz = float(r @ z)
+    rz = dtype(r @ z)
     history = []
     if not (np.isfinite(rz) and rz > 0.0):
         return PCGResult(x, 0, "breakdown", 1.0, 1.0, history)
     for it in range(1, maxit + 1):
-        q = spmv(row_ptr, col, val, p)
-        pq = float(p @ q)
+        q = spmv(row_ptr, col, val, p, dtype)
+        pq = dtype(p @ q)
         if not (np.isfinite(pq) and pq > 0.0):
-            rel = float(np.linalg.norm(r)) / bnorm
-            return PCGResult(x, it, "breakdown", rel,
-                             true_relres(row_ptr, col, val, b, x), history)
+            return out(it, "breakdown", norm(r) / bnorm)
         alpha = rz / pq
         x += alpha * p
         r -= alpha * q
-        rel = float(np.linalg.norm(r)) / bnorm
-        history.append(rel)
+        rel = norm(r) / bnorm
+        history.append(float(rel))
         if rel <= tol:
-            return PCGResult(x, it, "converged", rel,
-                             true_relres(row_ptr, col, val, b, x), history)
-        z = np.asarray(apply(r), dtype=np.float64)
-        rz_new = float(r @ z)
+            return out(it, "converged", rel)
+        z = np.asarray(apply(r), dtype=dtype)
+        rz_new = dtype(r @ z)
         if not (np.isfinite(rz_new) and rz_new > 0.0):
-            return PCGResult(x, it, "breakdown", rel,
-                             true_relres(row_ptr, col, val, b, x), history)
+            return out(it, "breakdown", rel)
         beta = rz_new / rz
         p = z + beta * p
         rz = rz_new
-    rel = float(np.linalg.norm(r)) / bnorm
-    return PCGResult(x, maxit, "not_converged", rel,
-                     true_relres(row_ptr, col, val, b, x), history)
+    return out(maxit, "not_converged", norm(r) / bnorm)
 
 
 def pcg_batch(batch, tol: float | None = None, maxit: int | None = None,

@@ -14,13 +14,18 @@ from __future__ import annotations
 import numpy as np
 
 
-def spmv(row_ptr, col, val, x):
-    """y = A x for a CSR matrix (row_ptr [n+1], col [nnz], val [nnz]), in fp64."""
+def spmv(row_ptr, col, val, x, dtype=np.float64):
+    """y = A x for a CSR matrix (row_ptr [n+1], col [nnz], val [nnz]), in fp64
+    (or in `dtype`; each row is summed in storage order either way)."""
     row_ptr = np.asarray(row_ptr, dtype=np.int64)
     n = row_ptr.size - 1
     rows = np.repeat(np.arange(n), np.diff(row_ptr))
-    prods = np.asarray(val, dtype=np.float64) * np.asarray(x, dtype=np.float64)[np.asarray(col)]
-    return np.bincount(rows, weights=prods, minlength=n)
+    prods = np.asarray(val, dtype=dtype) * np.asarray(x, dtype=dtype)[np.asarray(col)]
+    if np.dtype(dtype) == np.float64:
+        return np.bincount(rows, weights=prods, minlength=n)
+    y = np.zeros(n, dtype=dtype)
+    np.add.at(y, rows, prods)
+    return y
 
 
 def spmv_batch(row_ptr, col, val, x):
@@ -40,9 +45,9 @@ def dense_A(row_ptr, col, val):
     return A
 
 
-def true_relres(row_ptr, col, val, b, x) -> float:
-    """||b - A x||_2 / ||b||_2 in fp64."""
-    b = np.asarray(b, dtype=np.float64)
-    res = b - spmv(row_ptr, col, val, x)
+def true_relres(row_ptr, col, val, b, x, dtype=np.float64) -> float:
+    """||b - A x||_2 / ||b||_2 in fp64 (or in `dtype`)."""
+    b = np.asarray(b, dtype=dtype)
+    res = b - spmv(row_ptr, col, val, x, dtype)
     nb = np.linalg.norm(b)
     return float(np.linalg.norm(res) / nb) if nb > 0 else float(np.linalg.norm(res))

@@ -1,11 +1,17 @@
 """GPU parity: the HIP library against the CPU oracle, through the C ABI.
 
-Bars (fp32 vectors and apply, fp64 scalars and x):
-  * SpMV and M-apply: relative L2 error <= 1e-5 against the fp64 oracle on the
-    same fp32 inputs, and elementwise |y - y_ref| <= 1e-5 * (|M| |r|)_i (the
-    magnitude fp32 rounding scales with; the same with |A| |x| for the SpMV).
-  * PCG: same outcome, iteration count within 2 of the oracle's, recursive
-    residual <= tol and true residual ||b - A x||/||b|| <= 1.05 tol, both engines.
+The library's default arithmetic: fp32 matrix and factors, fp64 vectors,
+scalars and x (fp32 vectors are an option, checked separately).  Bars:
+  * SpMV and M-apply (fp32 in and out): relative L2 error <= 1e-5 against the
+    fp64 oracle on the same fp32 inputs, and elementwise
+    |y - y_ref| <= 1e-5 * (|M| |r|)_i (the magnitude fp32 rounding scales with;
+    the same with |A| |x| for the SpMV).
+  * Truncated PCG (a fixed number of steps, before rounding differences have
+    grown): x and the residual agree with the fp64 oracle's to 1e-9 relative.
+  * PCG to the tolerance: same outcome, iteration count within 2 of the
+    oracle's (on the tetrahedral system, within 2 of the band that rounding
+    alone produces), recursive residual <= tol and true residual
+    ||b - A x||/||b|| <= 1.05 tol, both engines.
 The workloads are the five benchmark systems at full size plus small edge
 cases (one leaf, two leaves, levels below the maximum, odd batch sizes).
 """
@@ -52,6 +58,44 @@ def oracle_solves():
             cache[batch.name] = oracle.pcg_batch(batch)
         return cache[batch.name]
     return get
+
+
+def rounding_band(sy, tol, maxit, eps=1e-15, runs=4, seed=0):
+    """Range of CG iteration counts that rounding alone produces on one system.
+
+    Low end: the oracle run in extended precision (64-bit significand), the
+    near-exact count.  High end: the fp64 oracle with every apply of M
+    perturbed by relative noise of size eps (rounding level), the largest of a
+    few runs.  On the tetrahedral system the first differences of 1e-16 grow by
+    about four orders of magnitude every ten steps, so the count of a fp64 run
+    depends on its summation order (extended 499, fp64 517, perturbed fp64
+    515-523); a GPU run with its own order is held to this band widened by 2.
+    """
+    ext = oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b, (sy.U, sy.W, sy.g), tol, maxit,
+                     dtype=np.longdouble).iterations
+    rng = np.random.default_rng(seed)
+    counts = []
+    for _ in range(runs):
+        res = oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b,
+                         lambda v: oracle.apply_M(sy.U, sy.W, sy.g, v) * (1 + eps * rng.standard_normal(v.size)),
+                         tol, maxit)
+        counts.append(res.iterations)
+    return min([ext] + counts), max([ext] + counts)
+
+
+_BANDS = {}
+
+
+def _iter_band(batch, i, ref):
+    """Allowed iteration range: oracle +-2; on the tetrahedral system the
+    rounding band (rounding_band) widened by 2 on each side."""
+    lo, hi = ref.iterations, ref.iterations
+    if batch.meta.get("n_tets"):
+        key = (batch.name, i)
+        if key not in _BANDS:
+            _BANDS[key] = rounding_band(batch.system(i), batch.tol, batch.maxit)
+        lo, hi = min(lo, _BANDS[key][0]), max(hi, _BANDS[key][1])
+    return lo - ITER_TOL, hi + ITER_TOL
 
 
 def _solver(batch, levels=None):
@@ -131,7 +175,8 @@ def _check_solve(batch, res, refs):
         sy = batch.system(i)
         assert res.system_status[i] == hpcg.HPCG_SYS_CONVERGED, (i, res.system_status[i])
         assert ref.status == "converged"
-        assert abs(res.iterations[i] - ref.iterations) <= ITER_TOL, (i, res.iterations[i], ref.iterations)
+        lo, hi = _iter_band(batch, i, ref)
+        assert lo <= res.iterations[i] <= hi, (i, res.iterations[i], ref.iterations, lo, hi)
         assert res.relres[i] <= batch.tol
         x = res.x[i].cpu().numpy()
         tr = oracle.true_relres(sy.row_ptr, sy.col, sy.val, sy.b, x)
@@ -150,6 +195,33 @@ def test_solve_parity(cfg, oracle_solves, name, engine):
     assert s.last_engine == engine
     assert res.status == hpcg.HPCG_OK, (res.status, hpcg.hpcg_last_error(s.handle))
     _check_solve(batch, res, refs)
+    s.close()
+
+
+# Steps before rounding differences grow: the grid systems keep fp64 and
+# extended-precision runs within 1e-14 for the first ~75 steps, the tetrahedral
+# one for the first ~10.
+TRUNC_STEPS = {"tet4k": 8}
+
+
+@pytest.mark.parametrize("engine", [hpcg.HPCG_ENGINE_PERSISTENT, hpcg.HPCG_ENGINE_GRAPH])
+@pytest.mark.parametrize("name", NAMES)
+def test_truncated_solve_parity(cfg, name, engine):
+    batch = cfg(name)
+    steps = TRUNC_STEPS.get(name, 40)
+    _log(f"truncated solve {name} engine={engine} steps={steps}")
+    s = _solver(batch)
+    s.set_option(hpcg.HPCG_OPT_ENGINE, engine)
+    res = s.solve(batch.b.reshape(-1), tol=batch.tol, maxit=steps)
+    assert res.status == hpcg.HPCG_ERR_NOT_CONVERGED, (res.status, hpcg.hpcg_last_error(s.handle))
+    for i in range(batch.batch):
+        sy = batch.system(i)
+        ref = oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b, (sy.U, sy.W, sy.g), batch.tol, steps)
+        assert ref.status == "not_converged" and res.iterations[i] == steps
+        x = res.x[i].cpu().numpy()
+        scale = np.abs(ref.x).max()
+        assert np.abs(x - ref.x).max() <= 1e-9 * scale, (i, np.abs(x - ref.x).max() / scale)
+        assert abs(res.relres[i] - ref.relres) <= 1e-9 * ref.relres, (i, res.relres[i], ref.relres)
     s.close()
 
 

@@ -130,3 +130,38 @@ def test_batch_equals_per_system():
         r = oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b, (sy.U, sy.W, sy.g), b.tol, b.maxit)
         assert r.iterations == res[s].iterations
         np.testing.assert_array_equal(r.x, res[s].x)
+
+
+def test_extended_precision_run():
+    # The same loop carried in np.longdouble: on a well-conditioned system it
+    # agrees with fp64 (count and x); it really runs in the wider type.
+    sy = make_config("N1k").system(0)
+    d = oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b, (sy.U, sy.W, sy.g), 1e-6, 1000)
+    e = oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b, (sy.U, sy.W, sy.g), 1e-6, 1000, dtype=np.longdouble)
+    assert e.x.dtype == np.longdouble and e.status == "converged"
+    assert e.iterations == d.iterations
+    # rounding differences stay at 1e-15 for the first ~50 steps, then grow
+    d = oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b, (sy.U, sy.W, sy.g), 1e-6, 40)
+    e = oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b, (sy.U, sy.W, sy.g), 1e-6, 40, dtype=np.longdouble)
+    np.testing.assert_allclose(e.x.astype(np.float64), d.x, rtol=0, atol=1e-12 * np.abs(d.x).max())
+    assert not np.array_equal(e.x, d.x.astype(np.longdouble))
+    # exact preconditioner: one step in either precision
+    b = random_system(256, seed=4, leaf=32, rank=4)
+    sy = b.system(0)
+    Ainv = np.linalg.inv(oracle.dense_A(sy.row_ptr, sy.col, sy.val))
+    e1 = oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b, lambda v: (Ainv @ v.astype(np.float64)).astype(np.longdouble),
+                    1e-10, 50, dtype=np.longdouble)
+    assert e1.iterations == 1
+
+
+def test_rounding_sensitivity_of_iteration_counts():
+    # On the tetrahedral system (a 100:1 coefficient jump) rounding differences
+    # grow by orders of magnitude within tens of steps, so the iteration count
+    # depends on the arithmetic: fewer steps in extended precision than in fp64.
+    # The first steps still agree closely.
+    sy = make_config("tet4k").system(0)
+    d = oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b, (sy.U, sy.W, sy.g), 1e-6, 2000)
+    e = oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b, (sy.U, sy.W, sy.g), 1e-6, 2000, dtype=np.longdouble)
+    assert d.status == e.status == "converged"
+    assert e.iterations < d.iterations - 2
+    np.testing.assert_allclose(d.history[:5], e.history[:5], rtol=1e-12)
