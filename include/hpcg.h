@@ -111,7 +111,12 @@ typedef enum {
 typedef enum {
     HPCG_OPT_ENGINE = 1,        /* an hpcg_engine value                          */
     HPCG_OPT_GRAPH_UNROLL = 2,  /* iterations per graph replay, 1 .. 64 (default 8) */
-    HPCG_OPT_PRECISION = 4      /* an hpcg_precision value                        */
+    HPCG_OPT_PRECISION = 4,     /* an hpcg_precision value                        */
+    HPCG_OPT_LEAF_SPLIT = 8     /* workgroups per leaf in the apply kernels and the
+                                   graph and streaming engines: 0 = automatic
+                                   (default), else 1, 2, 4 or 8; a split whose LDS
+                                   need exceeds a compute unit is raised to the
+                                   next that fits                                 */
 } hpcg_option;
 
 /* Arithmetic of the solve's vectors (hpcg_set_option(HPCG_OPT_PRECISION, ...)).

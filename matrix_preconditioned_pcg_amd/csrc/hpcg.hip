@@ -33,7 +33,10 @@ constexpr size_t kMaxLds = 160 * 1024;
 // control words, each on its own 256-byte line
 constexpr size_t kCtlBarrier = 0, kCtlAbort = 256, kCtlItbase = 512, kCtlReplays = 768, kCtlBytes = 1024;
 
-bool make_geom(const hpcg_partition* p, Geom& G, std::string& why) {
+constexpr int kMaxSplit = 8;   // workgroups per leaf in the streaming kernels
+
+// split = 0 picks the workgroups per leaf automatically, else 1, 2, 4 or 8.
+bool make_geom(const hpcg_partition* p, Geom& G, std::string& why, int split = 0) {
   if (!p) { why = "partition is NULL"; return false; }
   if (p->leaf != LEAF) { why = "leaf size must be 128"; return false; }
   if (p->rank != RANK) { why = "off-diagonal rank must be 32"; return false; }
@@ -52,13 +55,13 @@ bool make_geom(const hpcg_partition* p, Geom& G, std::string& why) {
   G.B = p->batch;
   // workgroups per leaf: enough to give every CU a workgroup, and enough that
   // the restriction and prolongation stages fit LDS in fp64 mode
-  int bpl = 1;
-  while ((int64_t)G.B * K * bpl < 256 && bpl < 8) bpl *= 2;
+  int bpl = split > 0 ? split : 1;
+  while (split == 0 && (int64_t)G.B * K * bpl < 256 && bpl < kMaxSplit) bpl *= 2;
   for (;;) {
     G.bpl = bpl;
     G.RB = LEAF / bpl;
     const size_t need = sizeof(Smem<double>) + std::max(restrict_lds_bytes(G), prolong_lds_bytes<double>(G));
-    if (need <= kMaxLds || bpl == 8) {
+    if (need <= kMaxLds || bpl == kMaxSplit) {
       if (need > kMaxLds) { why = "partition needs more LDS than a compute unit has"; return false; }
       break;
     }
@@ -82,20 +85,21 @@ Layout make_layout(const Geom& G, int64_t nnz) {
   L.g = take(N * 4);
   L.b = take(N * 4);
   // solve vectors and restriction partials are sized for the fp64 vector mode
-  L.r = take(N * 8);
+  L.r = take(2 * N * 8);
   L.z = take(N * 8);
   L.q = take(N * 8);
   L.p0 = take(N * 8);
   L.p1 = take(N * 8);
   L.x = take(N * 8);
-  // t_k per leaf (streaming engines) also holds W^T q (resident engine): both
-  // need at most B*K*max(LEAF, levels*RANK) values; pleaf holds two copies of
-  // W^T r for the resident engine's ping-pong
-  L.tleaf = take((size_t)G.B * G.K * std::max(LEAF, G.levels * RANK) * 8 + 16);
+  // pleaf holds two copies of W^T r for the resident engine's ping-pong
+  // diagonal shares per (leaf, slot) (streaming engines) also hold W^T q
+  // (resident engine); sized for the largest leaf split, like the partials
+  const size_t items = (size_t)G.B * G.K * kMaxSplit;
+  L.tleaf = take((size_t)G.B * G.K * std::max(kMaxSplit * LEAF, G.levels * RANK) * 8 + 16);
   L.pleaf = take(2 * (size_t)G.B * G.levels * G.K * RANK * 8 + 16);
-  L.pq = take((size_t)G.nblk * 8);
-  L.rr = take((size_t)G.nblk * 8);
-  L.rz = take((size_t)G.nblk * 8);
+  L.pq = take(items * 8);
+  L.rr = take(items * 8);
+  L.rz = take(items * 8);
   L.st = take((size_t)G.B * sizeof(SysState));
   L.ctl = take(kCtlBytes);
   L.total = off;
@@ -127,6 +131,8 @@ struct hpcg_ctx {
   hipGraphExec_t gexec = nullptr;
   int graph_unroll = 0;
   int graph_prec = -1;
+  int graph_bpl = 0;
+  int split = 0;
   double graph_tol = -1.0;
   int graph_maxit = -1;
   int last_grid = 0;
@@ -210,6 +216,7 @@ hpcg_status build_graph(hpcg_ctx* h) {
   if (e != hipSuccess) return hip_fail(h, e, "hipGraphInstantiate");
   h->graph_unroll = h->unroll;
   h->graph_prec = h->prec;
+  h->graph_bpl = G.bpl;
   h->graph_tol = B.tol;
   h->graph_maxit = B.maxit;
   return HPCG_OK;
@@ -220,7 +227,7 @@ hpcg_status run_graph(hpcg_ctx* h) {
   const Geom G = h->G;
   const Bufs B = h->B;
   if (!h->gexec || h->graph_unroll != h->unroll || h->graph_prec != h->prec || h->graph_tol != B.tol ||
-      h->graph_maxit != B.maxit) {
+      h->graph_maxit != B.maxit || h->graph_bpl != G.bpl) {
     hpcg_status s = build_graph<T>(h);
     if (s != HPCG_OK) return s;
   }
@@ -587,6 +594,16 @@ hpcg_status hpcg_set_option(hpcg_handle h, int32_t option, int32_t value) {
       if (value != HPCG_PREC_VEC64 && value != HPCG_PREC_VEC32) return fail(h, HPCG_ERR_INVALID_ARG, "bad precision");
       h->prec = value;
       return HPCG_OK;
+    case HPCG_OPT_LEAF_SPLIT: {
+      if (value != 0 && value != 1 && value != 2 && value != 4 && value != 8)
+        return fail(h, HPCG_ERR_INVALID_ARG, "leaf split must be 0 (automatic), 1, 2, 4 or 8");
+      Geom G;
+      std::string why;
+      if (!make_geom(&h->part, G, why, value)) return fail(h, HPCG_ERR_SHAPE, why);
+      h->G = G;
+      h->split = value;
+      return HPCG_OK;
+    }
     default:
       return fail(h, HPCG_ERR_INVALID_ARG, "unknown option");
   }

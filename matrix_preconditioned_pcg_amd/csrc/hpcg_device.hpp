@@ -3,12 +3,14 @@
 // Work decomposition.  Every system's n rows are cut into leaves of LEAF = 128
 // rows, and every leaf is served by `bpl` workgroups of NT = 256 threads (four
 // wave64 wavefronts).  Workgroup j of leaf k
-//   * restricts by columns: it computes the complete slice j of t_k = U_k^T r_k
-//     (columns [j*CW, (j+1)*CW), CW = LEAF/bpl) and the complete per-leaf
-//     restriction W_l[k]^T r_k of the levels l with l % bpl == j; so every
-//     restriction result exists once per leaf, with no partial sums;
+//   * restricts by columns: with the column slice U_k[:, C_j] (C_j = columns
+//     [j*CW, (j+1)*CW), CW = LEAF/bpl) it forms the slice t_j = U_k[:, C_j]^T r_k
+//     and at once the slot's share U_k[:, C_j] t_j of the diagonal-block product
+//     U_k U_k^T r_k = sum_j U_k[:, C_j] t_j, so each U_k byte is read once per
+//     apply; it also forms the complete per-leaf restriction W_l[k]^T r_k of the
+//     levels l with l % bpl == j;
 //   * prolongs and does the vector work by rows: rows [j*RB, (j+1)*RB) of the
-//     leaf, RB = LEAF/bpl.
+//     leaf, RB = LEAF/bpl, adding the bpl diagonal-block shares in slot order.
 //
 // One PCG iteration is three phases with a device-wide dependency between them
 // ("Hierarchical Transformer Preconditioning for Interactive Physics
@@ -16,10 +18,12 @@
 // inner loop):
 //   A  beta = (r.z)/(r.z)_old;  p = z + beta p;  q = A p;  partial p.q
 //   B  alpha = (r.z)/(p.q);  x += alpha p;  r -= alpha q;  partial r.r;
-//      restriction of the new r (eq. (2)): t_k = U_k^T r_k, W_l[k]^T r_k
+//      diagonal stage U_k U_k^T r_k by column slices and the restriction of the
+//      new r (eq. (2)), W_l[k]^T r_k
 //   C  convergence test on r.r;  strip aggregation over the partner half of
-//      every level (eq. (3)), then z_k = U_k t_k + sum_l W_l[k] P_l + g r_k
-//      (eqs. (4)-(5) with the coupling core equal to the identity);  partial r.z
+//      every level (eq. (3)), then z_k = (diagonal shares) + sum_l W_l[k] P_l
+//      + g r_k (eqs. (4)-(5) with the coupling core equal to the identity);
+//      partial r.z
 //
 // Memory traffic.  Each phase issues all of its loads in one batch: the factor
 // rows it needs go straight from global memory into LDS with gfx950's
@@ -84,13 +88,13 @@ struct Bufs {
   const float* W;      // [B][levels][K][LEAF][RANK]
   const float* g;      // [B*n]
   const float* b;      // [B*n]
-  void* r;
+  void* r;             // [2][B*n]: r of even and odd iterations
   void* z;
   void* q;
   void* p0;
   void* p1;
   double* x;
-  void* tleaf;         // [B][K][LEAF]        t_k = U_k^T r_k
+  void* tleaf;         // [B][K][bpl][LEAF]   diagonal-block shares U_k[:, C_j] U_k[:, C_j]^T r_k
   void* pleaf;         // [B][levels][K][RANK] W_l[k]^T r_k
   double* pq_part;     // [nblk]
   double* rr_part;
@@ -107,7 +111,7 @@ struct Bufs {
 template <typename T>
 struct alignas(16) Smem {
   T r[LEAF];                          // phase B: r (then r_new) of the whole leaf; C: block rows
-  T t[LEAF];                          // phase C: t_k
+  T t[LEAF];                          // phase B: the slot's slice of U_k^T r_k; C: diagonal shares
   T P[MAX_LEVELS * RANK];             // phase C: partner-half sums per level
   union {
     struct {
@@ -337,15 +341,16 @@ __host__ __device__ inline size_t restrict_lds_bytes(const Geom& G) {
 }
 template <typename T>
 __host__ __device__ inline size_t prolong_lds_bytes(const Geom& G) {
-  const size_t factors = (size_t)4 * ((size_t)G.RB * LEAF + (size_t)G.levels * G.RB * RANK);
+  const size_t factors = (size_t)4 * (size_t)G.levels * G.RB * RANK;
   return factors + (size_t)(G.K - 1) * RANK * sizeof(T);
 }
 
 // ---------------------------------------------------------------------------
-// Restriction (eq. (2)): from sm.r (the leaf's r, all LEAF rows) compute the
-// workgroup's column slice of t_k and the per-leaf restriction of its levels.
-// Factors were DMA'd to dyn: U slice [LEAF][CW], then each owned level's slab
-// [LEAF][RANK].  Writes tleaf and pleaf.
+// Restriction (eq. (2)) and the diagonal stage by column slices: from sm.r (the
+// leaf's r, all LEAF rows) compute t_j = U_k[:, C_j]^T r_k, the slot's share
+// U_k[:, C_j] t_j of the diagonal-block product, and the per-leaf restriction
+// of the slot's levels.  Factors were DMA'd to dyn: U slice [LEAF][CW], then
+// each owned level's slab [LEAF][RANK].  Writes tleaf (shares) and pleaf.
 // ---------------------------------------------------------------------------
 template <typename T>
 __device__ __forceinline__ void issue_restrict_dma(const Geom& G, const Bufs& B, const Blk& bk, float* dyn) {
@@ -362,16 +367,27 @@ __device__ __forceinline__ void issue_restrict_dma(const Geom& G, const Bufs& B,
   }
 }
 
+// Sum over groups of `width` consecutive lanes (width = 4, 8, 16 or 32).
+template <typename T>
+__device__ __forceinline__ T group_sum(T v, int width) {
+  v = group4_sum(v);
+  if (width > 4) v += lane_m4(v);
+  if (width > 8) v += lane_x8(v);
+  if (width > 16) v += lane_x16(v);
+  return v;
+}
+
 template <typename T>
 __device__ __forceinline__ void restrict_leaf(const Geom& G, const Bufs& B, const Blk& bk, const float* dyn,
                                               Smem<T>& sm) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, wave = tid >> 6;
   const int CW = G.RB;
-  T* tleaf = reinterpret_cast<T*>(B.tleaf);
+  const int slots = CW / 4;              // 4-column slots of the slice
+  T* share = reinterpret_cast<T*>(B.tleaf) + (((size_t)bk.s * G.K + bk.k) * G.bpl + bk.j) * LEAF;
   T* pleaf = reinterpret_cast<T*>(B.pleaf);
   {
-    // U slice: thread = (4-column slot c4, row group rg); RG row groups
-    const int slots = CW / 4, RG = NT / slots;
+    // t_j: thread = (4-column slot c4, row group rg); RG row groups
+    const int RG = NT / slots;
     const int c4 = tid % slots, rg = tid / slots;
     Vec4<T> acc{0, 0, 0, 0};
     for (int i = rg; i < LEAF; i += RG) axpy4(acc, lds4f(dyn + i * CW + 4 * c4), sm.r[i]);
@@ -379,7 +395,8 @@ __device__ __forceinline__ void restrict_leaf(const Geom& G, const Bufs& B, cons
     d[0] = acc.x; d[1] = acc.y; d[2] = acc.z; d[3] = acc.w;
   }
   {
-    // owned levels: thread = (4-column slot cs of 8, row group rg of 32)
+    // owned levels: thread = (4-column slot cs of 8, row group rg of 32); the
+    // rows of a wave (lane bits 3..5) are summed with xor 8, 16, 32
     const int cs = tid & 7, rg = tid >> 3;
     const int nl = levels_of_slot(G, bk.j);
     const float* dw = dyn + LEAF * CW;
@@ -388,12 +405,10 @@ __device__ __forceinline__ void restrict_leaf(const Geom& G, const Bufs& B, cons
       Vec4<T> acc{0, 0, 0, 0};
 #pragma unroll
       for (int i = rg; i < LEAF; i += 32) axpy4(acc, lds4f(Wm + i * RANK + 4 * cs), sm.r[i]);
-#pragma unroll
-      for (int o = 8; o < 64; o <<= 1) {
-        acc.x += __shfl_xor(acc.x, o); acc.y += __shfl_xor(acc.y, o);
-        acc.z += __shfl_xor(acc.z, o); acc.w += __shfl_xor(acc.w, o);
-      }
-      if (lane < 8) {
+      acc.x += lane_x8(acc.x); acc.y += lane_x8(acc.y); acc.z += lane_x8(acc.z); acc.w += lane_x8(acc.w);
+      acc.x += lane_x16(acc.x); acc.y += lane_x16(acc.y); acc.z += lane_x16(acc.z); acc.w += lane_x16(acc.w);
+      acc.x += lane_x32(acc.x); acc.y += lane_x32(acc.y); acc.z += lane_x32(acc.z); acc.w += lane_x32(acc.w);
+      if ((tid & 63) < 8) {
         T* d = &sm.redW[wave][m * RANK + 4 * cs];
         d[0] = acc.x; d[1] = acc.y; d[2] = acc.z; d[3] = acc.w;
       }
@@ -401,37 +416,46 @@ __device__ __forceinline__ void restrict_leaf(const Geom& G, const Bufs& B, cons
   }
   __syncthreads();
   {
-    const int RG = NT / (CW / 4);
+    const int RG = NT / slots;
     if (tid < CW) {
-      T s = sm.redT[tid];
-      for (int g = 1; g < RG; ++g) s += sm.redT[g * CW + tid];
-      tleaf[((size_t)bk.s * G.K + bk.k) * LEAF + bk.j * CW + tid] = s;
+      T a = sm.redT[tid];
+      for (int g = 1; g < RG; ++g) a += sm.redT[g * CW + tid];
+      sm.t[tid] = a;
     }
     const int nl = levels_of_slot(G, bk.j);
     for (int e = tid; e < nl * RANK; e += NT) {
-      T s = sm.redW[0][e];
+      T a = sm.redW[0][e];
 #pragma unroll
-      for (int w = 1; w < NWAVE; ++w) s += sm.redW[w][e];
+      for (int w = 1; w < NWAVE; ++w) a += sm.redW[w][e];
       const int m = e / RANK, c = e - m * RANK;
       const int l = bk.j + m * G.bpl;
-      pleaf[(((size_t)bk.s * G.levels + l) * G.K + bk.k) * RANK + c] = s;
+      pleaf[(((size_t)bk.s * G.levels + l) * G.K + bk.k) * RANK + c] = a;
+    }
+  }
+  __syncthreads();
+  {
+    // the slot's diagonal share: row i's dot of U_k[i, C_j] with t_j, `slots`
+    // lanes per row (4 columns each), NT / slots rows per pass
+    const int c4 = tid % slots, ri = tid / slots, rows = NT / slots;
+    const Vec4<T> t4 = lds4(&sm.t[4 * c4]);
+    for (int i = ri; i < LEAF; i += rows) {
+      const T v = group_sum(dot4(lds4f(dyn + i * CW + 4 * c4), t4), slots);
+      if (c4 == 0) share[i] = v;
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Prolongation (eqs. (3)-(5) and the diagonal stage) on the workgroup's row
-// block.  DMA: U rows [RB][LEAF], slab rows [levels][RB][RANK], the partner
-// half's per-leaf restrictions of every level (stage, level l at row 2^l - 1),
-// t_k.  Needs sm.r (block rows) and g; returns y for row tid (tid < RB).
+// Prolongation (eqs. (3)-(5)) and assembly on the workgroup's row block.  DMA:
+// slab rows [levels][RB][RANK], the partner half's per-leaf restrictions of
+// every level (stage, level l at row 2^l - 1), the bpl diagonal shares of the
+// block rows.  Needs sm.r (block rows) and g; returns y for row tid (tid < RB).
 // ---------------------------------------------------------------------------
 template <typename T>
 __device__ __forceinline__ void issue_prolong_dma(const Geom& G, const Bufs& B, const Blk& bk, float* dyn,
                                                   Smem<T>& sm) {
   const int RB = G.RB;
-  const float* Ub = B.U + ((size_t)bk.s * G.K + bk.k) * LEAF * LEAF + (size_t)bk.lrow0 * LEAF;
-  dma_to_lds(dyn, RB * LEAF / 4, [&](int c) { return Ub + 4 * c; });
-  float* dw = dyn + RB * LEAF;
+  float* dw = dyn;
   for (int l = 0; l < G.levels; ++l) {
     const float* Wl = B.W + (((size_t)bk.s * G.levels + l) * G.K + bk.k) * LEAF * RANK + (size_t)bk.lrow0 * RANK;
     dma_to_lds(dw + (size_t)l * RB * RANK, RB * RANK / 4, [&](int c) { return Wl + 4 * c; });
@@ -445,8 +469,13 @@ __device__ __forceinline__ void issue_prolong_dma(const Geom& G, const Bufs& B, 
     dma_to_lds(stage + (size_t)((1 << l) - 1) * RANK, (1 << l) * CPV,
                [&](int c) { return reinterpret_cast<const char*>(src) + 16 * c; });
   }
-  const T* tl = reinterpret_cast<const T*>(B.tleaf) + ((size_t)bk.s * G.K + bk.k) * LEAF;
-  dma_to_lds(sm.t, LEAF * (int)sizeof(T) / 16, [&](int c) { return reinterpret_cast<const char*>(tl) + 16 * c; });
+  // shares: slot j' rows [lrow0, lrow0 + RB) into sm.t[j' * RB ...]
+  const T* sh = reinterpret_cast<const T*>(B.tleaf) + ((size_t)bk.s * G.K + bk.k) * G.bpl * LEAF + bk.lrow0;
+  const int cps = RB * (int)sizeof(T) / 16;    // chunks per slot
+  dma_to_lds(sm.t, G.bpl * cps, [&](int c) {
+    const int j = c / cps;
+    return reinterpret_cast<const char*>(sh + (size_t)j * LEAF) + 16 * (c - j * cps);
+  });
 }
 
 template <typename T>
@@ -454,7 +483,7 @@ __device__ __forceinline__ T prolong_rows(const Geom& G, const Bufs& B, const Bl
                                           Smem<T>& sm) {
   const int tid = threadIdx.x;
   const int RB = G.RB;
-  const float* dw = dyn + RB * LEAF;
+  const float* dw = dyn;
   const T* stage = reinterpret_cast<const T*>(dw + (size_t)G.levels * RB * RANK);
   // strip aggregation (eq. (3)): P_l[c] = sum over the 2^l partner leaves
   {
@@ -468,33 +497,12 @@ __device__ __forceinline__ T prolong_rows(const Geom& G, const Bufs& B, const Bl
   }
   __syncthreads();
   for (int e = tid; e < G.levels * RANK; e += NT) {
-    T s = sm.redP[0][e];
+    T a = sm.redP[0][e];
 #pragma unroll
-    for (int g = 1; g < 8; ++g) s += sm.redP[g][e];
-    sm.P[e] = s;
+    for (int g = 1; g < 8; ++g) a += sm.redP[g][e];
+    sm.P[e] = a;
   }
   __syncthreads();
-  // diagonal stage: row i's dot with t_k over 32 lanes (4 columns each); two
-  // rows at a time are folded with a transpose-reduce (5 shuffles per pair)
-  {
-    const int cs = tid & 31, rg = tid >> 5;
-    const Vec4<T> t4 = lds4(&sm.t[4 * cs]);
-    const bool hi = (cs & 16) != 0;
-    for (int i0 = rg; i0 < RB; i0 += 16) {
-      const int i1 = i0 + 8;
-      const T v0 = dot4(lds4f(dyn + i0 * LEAF + 4 * cs), t4);
-      const T v1 = (i1 < RB) ? dot4(lds4f(dyn + i1 * LEAF + 4 * cs), t4) : T(0);
-      T keep = hi ? v1 : v0;
-      const T send = hi ? v0 : v1;
-      keep += __shfl_xor(send, 16);
-      keep += __shfl_xor(keep, 8);
-      keep += __shfl_xor(keep, 4);
-      keep += __shfl_xor(keep, 2);
-      keep += __shfl_xor(keep, 1);
-      if (cs == 0) sm.yleaf[i0] = keep;
-      if (cs == 16 && i1 < RB) sm.yleaf[i1] = keep;
-    }
-  }
   // prolongation (eq. (5)): per row, sum over levels of slab row . P_l
   {
     const int cs = tid & 7, rg = tid >> 3;
@@ -502,16 +510,24 @@ __device__ __forceinline__ T prolong_rows(const Geom& G, const Bufs& B, const Bl
       T acc = 0;
       for (int l = 0; l < G.levels; ++l)
         acc += dot4(lds4f(dw + ((size_t)l * RB + i) * RANK + 4 * cs), lds4(&sm.P[l * RANK + 4 * cs]));
-      acc += __shfl_xor(acc, 1);
-      acc += __shfl_xor(acc, 2);
-      acc += __shfl_xor(acc, 4);
+      acc = group8_sum(acc);
       if (cs == 0) sm.yoff[i] = acc;
     }
   }
   __syncthreads();
   T y = 0;
-  if (tid < RB) y = sm.yleaf[tid] + sm.yoff[tid] + (T)B.g[bk.grow0 + tid] * sm.r[tid];
+  if (tid < RB) {
+    T d = sm.t[tid];
+    for (int j = 1; j < G.bpl; ++j) d += sm.t[j * RB + tid];
+    y = d + sm.yoff[tid] + (T)B.g[bk.grow0 + tid] * sm.r[tid];
+  }
   return y;
+}
+
+// r after iteration it (0 = initial) lives in half it & 1 of the r buffer.
+template <typename T>
+__device__ __forceinline__ T* r_buf(const Geom& G, const Bufs& B, int it) {
+  return reinterpret_cast<T*>(B.r) + ((it & 1) ? (size_t)G.B * G.n : 0);
 }
 
 // p_new = z + beta p_old, evaluated identically wherever it is needed so that
@@ -533,7 +549,10 @@ __device__ __forceinline__ void phase_B(const Geom& G, const Bufs& B, int b, int
   const int tid = threadIdx.x;
   SysState* st = B.st + bk.s;
   const bool init = (it == 0);
-  T* r = reinterpret_cast<T*>(B.r);
+  // every slot of a leaf reads the leaf's whole old r while each writes only
+  // its own rows of the new r, so old and new live in different buffers
+  const T* rold = r_buf<T>(G, B, it - 1);
+  T* rnew = r_buf<T>(G, B, it);
   // ---- one batch of loads ----
   issue_restrict_dma<T>(G, B, bk, dyn);
   const double pqv = init ? 0.0 : load_partials(B.pq_part, bk.s, G.nblk_sys);
@@ -550,7 +569,7 @@ __device__ __forceinline__ void phase_B(const Geom& G, const Bufs& B, int b, int
     if (init) {
       rv = (T)B.b[bk.leaf0 + tid];
     } else {
-      rv = r[bk.leaf0 + tid];
+      rv = rold[bk.leaf0 + tid];
       qv = reinterpret_cast<const T*>(B.q)[bk.leaf0 + tid];
       if (own) {
         pv = reinterpret_cast<const T*>((it & 1) ? B.p1 : B.p0)[bk.leaf0 + tid];
@@ -574,7 +593,7 @@ __device__ __forceinline__ void phase_B(const Geom& G, const Bufs& B, int b, int
     const T rn = init ? rv : (T)((double)rv - alpha * (double)qv);
     sm.r[tid] = rn;
     if (own) {
-      r[bk.leaf0 + tid] = rn;
+      rnew[bk.leaf0 + tid] = rn;
       B.x[bk.leaf0 + tid] = init ? 0.0 : xv + alpha * (double)pv;
       loc = (double)rn * (double)rn;
     }
@@ -608,7 +627,7 @@ __device__ __forceinline__ void phase_C(const Geom& G, const Bufs& B, int b, int
     state = (it == 0) ? ST_RUNNING : load_state(st);
     bnorm = st->bnorm;
   }
-  const T* r = reinterpret_cast<const T*>(B.r);
+  const T* r = r_buf<T>(G, B, it);
   T rv = 0;
   if (tid < G.RB) rv = r[bk.grow0 + tid];
   const double rr = wave_sum(rrv);

@@ -42,6 +42,7 @@ HPCG_ENGINE_PERSISTENT = 2
 HPCG_OPT_ENGINE = 1
 HPCG_OPT_GRAPH_UNROLL = 2
 HPCG_OPT_PRECISION = 4
+HPCG_OPT_LEAF_SPLIT = 8
 
 HPCG_PREC_VEC64 = 0
 HPCG_PREC_VEC32 = 1

@@ -154,6 +154,19 @@ def test_apply_parity(cfg, name):
     s.close()
 
 
+@pytest.mark.parametrize("split", [1, 2, 4, 8])
+@pytest.mark.parametrize("name", ["N8k", "batch64x2k"])
+def test_apply_parity_leaf_split(cfg, name, split):
+    # every workgroups-per-leaf split of the apply kernels gives the same M r
+    batch = cfg(name)
+    _log(f"apply parity {name} split={split}")
+    s = _solver(batch)
+    s.set_option(hpcg.HPCG_OPT_LEAF_SPLIT, split)
+    r = np.random.default_rng(13).standard_normal((batch.batch, batch.n)).astype(np.float32)
+    _check_apply(batch, s, r)
+    s.close()
+
+
 @pytest.mark.parametrize("n,levels,batch", [(128, 0, 1), (256, 1, 1), (512, 1, 1), (1024, 2, 1),
                                             (2048, 4, 3), (4096, 0, 2), (256, 1, 5)])
 def test_apply_spmv_small_and_ragged(n, levels, batch):
@@ -299,6 +312,43 @@ def test_graph_unroll_independent(cfg, unroll):
     s.close()
 
 
+@pytest.mark.parametrize("split", [1, 8])
+def test_graph_solve_leaf_split(cfg, oracle_solves, split):
+    batch = cfg("N8k")
+    _log(f"graph solve N8k split={split}")
+    refs = oracle_solves(batch)
+    s = _solver(batch)
+    s.set_option(hpcg.HPCG_OPT_ENGINE, hpcg.HPCG_ENGINE_GRAPH)
+    s.set_option(hpcg.HPCG_OPT_LEAF_SPLIT, split)
+    res = s.solve(batch.b.reshape(-1))
+    assert res.status == hpcg.HPCG_OK, (res.status, hpcg.hpcg_last_error(s.handle))
+    _check_solve(batch, res, refs)
+    s.close()
+
+
+# Many more workgroups than compute units, several per leaf: slots of one leaf
+# run at different times, so any buffer that one slot writes while another
+# still reads it would show here.
+@pytest.mark.parametrize("engine,split", [(hpcg.HPCG_ENGINE_GRAPH, 2), (hpcg.HPCG_ENGINE_GRAPH, 8),
+                                          (hpcg.HPCG_ENGINE_PERSISTENT, 4)])
+def test_streaming_solve_leaf_split_batch(cfg, engine, split):
+    batch = cfg("batch64x2k")
+    steps = 40
+    _log(f"streaming solve batch64 engine={engine} split={split}")
+    s = _solver(batch)
+    s.set_option(hpcg.HPCG_OPT_ENGINE, engine)
+    s.set_option(hpcg.HPCG_OPT_LEAF_SPLIT, split)
+    res = s.solve(batch.b.reshape(-1), maxit=steps)
+    assert s.last_engine == engine
+    for i in range(0, batch.batch, 7):
+        sy = batch.system(i)
+        ref = oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b, (sy.U, sy.W, sy.g), batch.tol, steps)
+        x = res.x[i].cpu().numpy()
+        scale = np.abs(ref.x).max()
+        assert np.abs(x - ref.x).max() <= 1e-9 * scale, (i, np.abs(x - ref.x).max() / scale)
+    s.close()
+
+
 def test_identity_preconditioner_is_plain_cg(cfg):
     batch = cfg("N1k")
     _log("identity preconditioner")
@@ -423,6 +473,8 @@ def test_argument_errors(cfg):
         s.solve(batch.b.reshape(-1), maxit=0)
     with pytest.raises(hpcg.HPCGError):
         s.set_option(hpcg.HPCG_OPT_GRAPH_UNROLL, 0)
+    with pytest.raises(hpcg.HPCGError):
+        s.set_option(hpcg.HPCG_OPT_LEAF_SPLIT, 3)
     with pytest.raises(ValueError):
         s.apply_M(np.zeros(batch.n + 1, np.float32))
     s.close()

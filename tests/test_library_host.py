@@ -58,8 +58,9 @@ def test_workspace_bytes_covers_the_buffers(hp):
     nbytes = hp.hpcg_workspace_bytes(part, nnz)
     factors = 128 * 128 * 128 * 4 + 7 * 128 * 128 * 32 * 4
     csr = (16385 + 2 * nnz) * 4
-    vectors = 16384 * (2 * 4 + 6 * 8)            # g, b fp32; r, z, q, p0, p1, x fp64
-    restrictions = (128 * 128 + 7 * 128 * 32) * 8  # t_k and W_l[k]^T r_k per leaf, fp64
+    vectors = 16384 * (2 * 4 + 7 * 8)            # g, b fp32; r (two), z, q, p0, p1, x fp64
+    # per leaf: diagonal shares of up to 8 slots and two copies of W_l[k]^T r_k, fp64
+    restrictions = 128 * (8 * 128 + 2 * 7 * 32) * 8
     need = factors + csr + vectors + restrictions
     assert need <= nbytes <= need + (1 << 20)
     assert hp.hpcg_workspace_bytes(hp.partition(2048, batch=64), 851968) > 64 * hp.hpcg_workspace_bytes(
