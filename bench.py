@@ -9,9 +9,10 @@ workload is the N = 8,192 system (3D 7-point variable-coefficient Poisson on a
 16 x 16 x 32 Morton-ordered grid, K = 64 leaves, 6 tile levels).
 
 Printed: one JSON line on stdout.  `value` is ms per solve (lower is better).
-`roofline` covers the M-apply + SpMV pair, timed per call with HIP events on
-the library's stream, against MI355X's 8 TB/s HBM peak, using algorithmic bytes
-(each factor, matrix entry and vector read or written once per call).
+`roofline` covers the M-apply + SpMV pair: `reps` pairs are captured into one
+graph on the library's stream and replayed between HIP events on that stream;
+achieved = algorithmic bytes (each factor, matrix entry and vector read or
+written once per call) / GPU time per pair, against MI355X's 8 TB/s HBM peak.
 `cpu_baseline` times the fp64 numpy oracle on a bounded sample on host cores.
 """
 
@@ -44,6 +45,31 @@ def spmv_bytes(n: int, nnz: int, B: int = 1) -> int:
     return 8 * nnz + 4 * (B * n + 1) + 8 * B * n
 
 
+def kernel_source_digest() -> str:
+    """Digest of the HIP sources, so that recorded counters go stale with them."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "matrix_preconditioned_pcg_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(config: str):
+    """HBM bytes per apply+SpMV pair from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, scaled by a copy kernel's reading), or
+    None when there is none for this workload or the kernels changed since."""
+    path = os.path.join(ROOT, "profiles", f"apply_spmv_traffic_{config}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return rec.get("bytes_per_pair")
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -61,9 +87,9 @@ def time_solves(solver, b, tol, maxit, steps, warmup, torch):
     return (time.perf_counter() - t0) * 1e3 / steps, iters, res
 
 
-def time_calls(fn, reps, torch):
-    """Average duration of fn() with a HIP event pair around every call."""
-    stream = torch.cuda.current_stream()
+def time_calls(fn, reps, stream, torch):
+    """Eager timing: mean and median duration of fn() with a HIP event pair
+    around every call on `stream` (includes host launch latency)."""
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for _ in range(5):
         fn()
@@ -77,18 +103,28 @@ def time_calls(fn, reps, torch):
     return float(np.mean(ms)) * 1e3, float(np.median(ms)) * 1e3   # microseconds
 
 
-def time_back_to_back(fn, reps, torch):
-    stream = torch.cuda.current_stream()
-    a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for _ in range(5):
-        fn()
+def time_graph(fn, reps, stream, torch, replays=5):
+    """GPU time per fn() call: `reps` calls captured into one graph on `stream`
+    (the library's stream), replayed `replays` times between HIP events on that
+    stream; the median replay is reported.  Free of host launch overhead."""
+    fn()
     torch.cuda.synchronize()
-    a.record(stream)
-    for _ in range(reps):
-        fn()
-    e.record(stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(reps):
+            fn()
+    g.replay()
     torch.cuda.synchronize()
-    return a.elapsed_time(e) * 1e3 / reps
+    out = []
+    for _ in range(replays):
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        e.record(stream)
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(e) * 1e3 / reps)
+    del g
+    return float(np.median(out))
 
 
 def cpu_baseline(batch, budget_s=12.0):
@@ -124,6 +160,8 @@ def main(argv=None):
     ap.add_argument("--reps", type=int, default=300, help="calls per apply/SpMV timing")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-others", action="store_true", help="skip ms/solve of the other workloads")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run three 256 MiB device-to-device copies (calibrates HBM byte counters)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this solver path is built and measured on a single "
@@ -139,10 +177,41 @@ def main(argv=None):
     torch.cuda.set_device(0)
     dev_name = torch.cuda.get_device_name(0)
 
+    # one non-default stream for the library: solves, applies and the graphs
+    # that time them all run on it
+    stream = torch.cuda.Stream()
+
+    def measure_apply_spmv(batch, solver):
+        r = torch.randn(batch.batch * batch.n, device="cuda", dtype=torch.float32)
+        y = torch.empty_like(r)
+        q = torch.empty_like(r)
+
+        def apply():
+            hpcg.hpcg_apply_M(solver.handle, solver.part, r, y)
+
+        def spmv():
+            hpcg.hpcg_spmv(solver.handle, solver.part, r, q)
+
+        def pair():
+            spmv()
+            apply()
+        ab = apply_bytes(batch.n, batch.K, batch.levels, batch.batch)
+        sb = spmv_bytes(batch.n, batch.nnz, batch.batch)
+        with torch.cuda.stream(stream):
+            out = {"apply_us": time_graph(apply, args.reps, stream, torch),
+                   "spmv_us": time_graph(spmv, args.reps, stream, torch),
+                   "pair_us": time_graph(pair, args.reps, stream, torch)}
+            out["apply_us_eager"], _ = time_calls(apply, args.reps, stream, torch)
+        out.update(apply_bytes=ab, spmv_bytes=sb,
+                   apply_gbs=ab / out["apply_us"] / 1e3, spmv_gbs=sb / out["spmv_us"] / 1e3,
+                   pair_gbs=(ab + sb) / out["pair_us"] / 1e3)
+        out["pair_frac"] = out["pair_gbs"] / HBM_PEAK_GBS
+        return out
+
     def run_config(name, steps, warmup, with_roofline, engine=None, prec=None):
         batch = make_config(name)
         solver = hpcg.Solver(batch.n, batch.row_ptr, batch.col, batch.val, batch=batch.batch,
-                             levels=batch.levels)
+                             levels=batch.levels, stream=stream)
         solver.set_factors(batch.U, batch.W, batch.g)
         engine = args.engine if engine is None else engine
         prec = args.prec if prec is None else prec
@@ -150,45 +219,40 @@ def main(argv=None):
             solver.set_option(hpcg.HPCG_OPT_ENGINE, engine)
         solver.set_option(hpcg.HPCG_OPT_PRECISION, prec)
         b = torch.as_tensor(batch.b.reshape(-1)).cuda()
+        torch.cuda.synchronize()
         ms, iters, res = time_solves(solver, b, batch.tol, batch.maxit, steps, warmup, torch)
         out = {"ms_per_solve": ms, "iterations": iters, "status": res.status,
                "engine": solver.last_engine, "batch": batch.batch, "n": batch.n}
         if with_roofline:
-            r = torch.randn(batch.batch * batch.n, device="cuda", dtype=torch.float32)
-            y = torch.empty_like(r)
-            q = torch.empty_like(r)
-            t_apply, t_apply_med = time_calls(lambda: hpcg.hpcg_apply_M(solver.handle, solver.part, r, y),
-                                              args.reps, torch)
-            t_spmv, t_spmv_med = time_calls(lambda: hpcg.hpcg_spmv(solver.handle, solver.part, r, q),
-                                            args.reps, torch)
-
-            def pair():
-                hpcg.hpcg_spmv(solver.handle, solver.part, r, q)
-                hpcg.hpcg_apply_M(solver.handle, solver.part, r, y)
-            t_pair = time_back_to_back(pair, args.reps, torch)
-            ab = apply_bytes(batch.n, batch.K, batch.levels, batch.batch)
-            sb = spmv_bytes(batch.n, batch.nnz, batch.batch)
-            out.update(apply_us=t_apply, apply_us_median=t_apply_med, spmv_us=t_spmv,
-                       spmv_us_median=t_spmv_med, pair_back_to_back_us=t_pair,
-                       apply_bytes=ab, spmv_bytes=sb)
+            out.update(measure_apply_spmv(batch, solver))
         solver.close()
         return batch, out
 
+    if args.copy_probe:
+        src = torch.ones(64 << 20, device="cuda", dtype=torch.float32)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     batch, main_out = run_config(args.config, args.steps, args.warmup, True)
     ab, sb = main_out["apply_bytes"], main_out["spmv_bytes"]
-    t_sum = main_out["apply_us"] + main_out["spmv_us"]
-    achieved = (ab + sb) / (t_sum * 1e-6) / 1e9
+    achieved = main_out["pair_gbs"]
     others = {}
     if not args.no_others:
         for name in CONFIGS:
             if name == args.config:
                 continue
             log(f"bench: {name}")
-            _b, o = run_config(name, max(3, args.steps // 4), 1, False)
+            _b, o = run_config(name, max(3, args.steps // 4), 1, True)
             others[name] = {"ms_per_solve": round(o["ms_per_solve"], 4), "iterations": o["iterations"]
                             if len(o["iterations"]) <= 4 else
                             {"min": min(o["iterations"]), "max": max(o["iterations"])},
-                            "engine": o["engine"]}
+                            "engine": o["engine"],
+                            "apply_us": round(o["apply_us"], 3), "spmv_us": round(o["spmv_us"], 3),
+                            "apply_spmv_us": round(o["pair_us"], 3),
+                            "apply_spmv_gbs": round(o["pair_gbs"], 1),
+                            "apply_spmv_frac": round(o["pair_frac"], 4)}
     variants = {}
     if not args.no_variants:
         for label, eng, prec in (("persistent_vec64", 2, 0), ("persistent_vec32", 2, 1),
@@ -223,19 +287,23 @@ def main(argv=None):
         "us_per_iteration": round(main_out["ms_per_solve"] * 1e3 / max(iters, 1), 3),
         "apply_us": round(main_out["apply_us"], 3),
         "spmv_us": round(main_out["spmv_us"], 3),
-        "apply_spmv_back_to_back_us": round(main_out["pair_back_to_back_us"], 3),
+        "apply_spmv_us": round(main_out["pair_us"], 3),
+        "apply_us_eager": round(main_out["apply_us_eager"], 3),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "kernel": "M-apply (restrict + prolong) + CSR SpMV, per call",
+            "traffic": traffic_record(args.config),
+            "kernel": "M-apply (k_apply_restrict + k_apply_prolong) + CSR SpMV (k_spmv), one pair per "
+                      "launch group, graph-replayed back to back on the library stream",
             "algorithmic_bytes": ab + sb,
+            "apply_gbs": round(main_out["apply_gbs"], 1),
+            "spmv_gbs": round(main_out["spmv_gbs"], 1),
         },
         "cpu_baseline": cpu,
-        "ms_per_solve_by_config": others,
+        "by_config": others,
         "variants_at_workload": variants,
     }
     print(json.dumps(line), flush=True)

@@ -10,6 +10,7 @@
 #include <chrono>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -174,13 +175,21 @@ hpcg_status check_launch(hpcg_ctx* h, const char* what) {
 }
 
 // Raise a kernel's dynamic-LDS limit when it needs more than the default.
+// The limit is a per-kernel, per-process setting: remember what was granted so
+// that repeated calls cost no runtime call.
 hpcg_status allow_lds(hpcg_ctx* h, const void* fn, size_t bytes) {
   if (bytes <= 48 * 1024) return HPCG_OK;
+  static std::mutex mu;
+  static std::vector<std::pair<const void*, size_t>> granted;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto& g : granted)
+    if (g.first == fn && g.second >= bytes) return HPCG_OK;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (e != hipSuccess) {
     clear_hip_error_fn();
     return hip_fail(h, e, "hipFuncSetAttribute(MaxDynamicSharedMemorySize)");
   }
+  granted.emplace_back(fn, bytes);
   return HPCG_OK;
 }
 
