@@ -42,6 +42,8 @@ struct alignas(16) RSmem {
   T tq[LEAF];                        // U_k^T q
   T t[LEAF];                         // U_k^T r_new = tr - alpha tq
   T P[MAX_LEVELS * RANK];            // partner-half sums
+  T ownR[MAX_LEVELS * RANK];         // this leaf's W_l[k]^T r
+  T ownQ[MAX_LEVELS * RANK];         // this leaf's W_l[k]^T q
   T yleaf[LEAF];
   T yoff[LEAF];
   T red[NWR][LEAF];                  // cross-wave reductions of t
@@ -73,6 +75,12 @@ __device__ __forceinline__ double sum_partials_r(const double* part, int s, int 
   return wave_sum(v);
 }
 
+// Iterations between exact restrictions of r (the others use the linear
+// update).  fp64 drift over 8 updates stays near 1e-15 of |r|; fp32 vectors
+// refresh every iteration.
+template <typename T>
+constexpr int kRefresh = sizeof(T) == 8 ? 8 : 1;
+
 template <typename T, int LEV>
 struct Resident {
   float4 u[8];
@@ -80,10 +88,10 @@ struct Resident {
 };
 
 // Restriction of the LDS vector v: U_k^T v into tout (LDS, complete) and
-// W_l[k]^T v into pout (global, [levels][K][RANK] of system s).
+// W_l[k]^T v into pout (global, [levels][K][RANK] of system s) and own (LDS).
 template <typename T, int LEV>
 __device__ __forceinline__ void r_restrict(const Geom& G, int s, int k, const Resident<T, LEV>& F,
-                                           const T* v, T* tout, T* pout, RSmem<T>& sm) {
+                                           const T* v, T* tout, T* pout, T* own, RSmem<T>& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   {
     const int cs = tid & 31, rg = tid >> 5;
@@ -150,6 +158,7 @@ __device__ __forceinline__ void r_restrict(const Geom& G, int s, int k, const Re
       for (int w = 1; w < NWR; ++w) a += sm.redW[w][tid];
       const int l = tid / RANK, c = tid - l * RANK;
       pout[(((size_t)s * G.levels + l) * G.K + k) * RANK + c] = a;
+      own[tid] = a;
     }
   }
   __syncthreads();
@@ -314,7 +323,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
     loc = (double)bv * (double)bv;
   }
   __syncthreads();
-  r_restrict<T, LEV>(G, s, k, F, sm.r, sm.tr, pR[0], sm);
+  r_restrict<T, LEV>(G, s, k, F, sm.r, sm.tr, pR[0], sm.ownR, sm);
   double part = wg_sum_r(loc, sm);
   if (tid == 0) {
     B.rr_part[item] = part;
@@ -362,6 +371,28 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
   for (int it = 1; it <= B.maxit + 2; ++it) {
     // ---------------- phase A (it) ----------------
     {
+      // the SpMV's first gathers go out together with the scalar loads
+      const T* pold = reinterpret_cast<const T*>((it & 1) ? B.p0 : B.p1);
+      T* pnew = reinterpret_cast<T*>((it & 1) ? B.p1 : B.p0);
+      const bool first = (it == 1);
+      const int row = tid >> 2, lr = tid & 3;
+      const int e0 = rpL[row], e1 = rpL[row + 1];
+      constexpr int PF = 2;
+      T zc[PF], pc[PF];
+      float vv[PF];
+#pragma unroll
+      for (int u = 0; u < PF; ++u) {
+        const int e = e0 + lr + 4 * u;
+        zc[u] = 0;
+        pc[u] = 0;
+        vv[u] = 0.f;
+        if (e < e1) {
+          const int c = colL[e];
+          vv[u] = valL[e];
+          zc[u] = zg[c];
+          if (!first) pc[u] = pold[c];
+        }
+      }
       int running = 0;
       for (int q = tid; q < G.B; q += NTR)
         running |= (__hip_atomic_load(&B.st[q].status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ST_RUNNING);
@@ -382,17 +413,14 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
         done = true; pend_status = ST_BREAKDOWN; pend_iters = it - 1;
       }
       if (!done) {
-        const bool first = (it == 1);
         const double beta = first ? 0.0 : rz / rz_old;
         rz_old = rz;
         sm.dsc[0] = rz;
-        const T* pold = reinterpret_cast<const T*>((it & 1) ? B.p0 : B.p1);
-        T* pnew = reinterpret_cast<T*>((it & 1) ? B.p1 : B.p0);
         // SpMV: 4 threads per row, CSR rows from LDS, z and p gathered globally
-        const int row = tid >> 2, lr = tid & 3;
-        const int e0 = rpL[row], e1 = rpL[row + 1];
         T acc = 0;
-        for (int e = e0 + lr; e < e1; e += 4) {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) acc = fma((T)vv[u], first ? zc[u] : pdir<T>(zc[u], pc[u], beta), acc);
+        for (int e = e0 + lr + 4 * PF; e < e1; e += 4) {
           const int c = colL[e];
           const T v = first ? zg[c] : pdir<T>(zg[c], pold[c], beta);
           acc = fma((T)valL[e], v, acc);
@@ -407,7 +435,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
           loc = (double)pn * (double)acc;
         }
         __syncthreads();
-        r_restrict<T, LEV>(G, s, k, F, sm.q, sm.tq, pQ, sm);
+        r_restrict<T, LEV>(G, s, k, F, sm.q, sm.tq, pQ, sm.ownQ, sm);
         part = wg_sum_r(loc, sm);
         if (tid == 0) B.pq_part[item] = part;
       }
@@ -450,9 +478,22 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
           }
           part = wg_sum_r(loc, sm);
           if (tid == 0) B.rz_part[item] = part;
-          // exact restriction of the new r for the next iteration
+          // restriction of the new r for the next iteration: exact every
+          // kRefresh iterations, else by the same linear update the partners
+          // used above (its rounding drift is bounded by the exact refreshes)
           rbuf ^= 1;
-          r_restrict<T, LEV>(G, s, k, F, sm.r, sm.tr, pR[rbuf], sm);
+          if (it % kRefresh<T> == 0) {
+            r_restrict<T, LEV>(G, s, k, F, sm.r, sm.tr, pR[rbuf], sm.ownR, sm);
+          } else {
+            if (tid < LEAF) sm.tr[tid] = sm.t[tid];
+            if (tid < LEV * RANK) {
+              const T v = (T)((double)sm.ownR[tid] - alpha * (double)sm.ownQ[tid]);
+              sm.ownR[tid] = v;
+              const int l = tid / RANK, c = tid - l * RANK;
+              pR[rbuf][(((size_t)s * G.levels + l) * G.K + k) * RANK + c] = v;
+            }
+            __syncthreads();
+          }
         }
       }
     }
