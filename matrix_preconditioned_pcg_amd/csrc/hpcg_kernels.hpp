@@ -49,6 +49,40 @@ __device__ __forceinline__ bool grid_barrier(unsigned* ctr, int* abort_flag, uns
   return aborted != 0;
 }
 
+// Split form of the same barrier: arrive once this workgroup's writes for the
+// other workgroups are done, do work nobody waits for, then wait.
+__device__ __forceinline__ void grid_arrive(unsigned* ctr, unsigned& target) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    target += gridDim.x;
+    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+__device__ __forceinline__ bool grid_wait(unsigned* ctr, int* abort_flag, unsigned target) {
+  __shared__ int aborted_w;
+  if (threadIdx.x == 0) {
+    unsigned polls = 0;
+    int ab = 0;
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(1);
+      if (((++polls) & 1023u) == 0) {
+        if (__hip_atomic_load(abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) { ab = 1; break; }
+        if (polls > (1u << 26)) {
+          __hip_atomic_store(abort_flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ab = 1;
+          break;
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    aborted_w = ab;
+  }
+  __syncthreads();
+  return aborted_w != 0;
+}
+
 // ---------------------------------------------------------------------------
 // graph-engine kernels (one workgroup per (leaf, slot))
 // ---------------------------------------------------------------------------

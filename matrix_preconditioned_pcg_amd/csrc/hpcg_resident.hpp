@@ -368,6 +368,8 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
   // the same values and leaves the loop together.
   int pend_status = ST_RUNNING, pend_iters = 0;
   double pend_rel = 0.0;
+  bool restrict_next = false;
+  double next_alpha = 0.0;
   for (int it = 1; it <= B.maxit + 2; ++it) {
     // ---------------- phase A (it) ----------------
     {
@@ -478,26 +480,34 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
           }
           part = wg_sum_r(loc, sm);
           if (tid == 0) B.rz_part[item] = part;
-          // restriction of the new r for the next iteration: exact every
-          // kRefresh iterations, else by the same linear update the partners
-          // used above (its rounding drift is bounded by the exact refreshes)
-          rbuf ^= 1;
-          if (it % kRefresh<T> == 0) {
-            r_restrict<T, LEV>(G, s, k, F, sm.r, sm.tr, pR[rbuf], sm.ownR, sm);
-          } else {
-            if (tid < LEAF) sm.tr[tid] = sm.t[tid];
-            if (tid < LEV * RANK) {
-              const T v = (T)((double)sm.ownR[tid] - alpha * (double)sm.ownQ[tid]);
-              sm.ownR[tid] = v;
-              const int l = tid / RANK, c = tid - l * RANK;
-              pR[rbuf][(((size_t)s * G.levels + l) * G.K + k) * RANK + c] = v;
-            }
-            __syncthreads();
-          }
+          next_alpha = alpha;
+          restrict_next = true;
         }
       }
     }
-    if (grid_barrier(B.barrier, B.abort_flag, target)) return;
+    // Everything the next phase A reads (z, the partials, the statuses) is
+    // written: arrive now.  The restriction of the new r is read by the
+    // partners only after the following barrier, so it overlaps the wait.
+    grid_arrive(B.barrier, target);
+    if (restrict_next) {
+      // exact every kRefresh iterations, else by the same linear update the
+      // partners used above (its rounding drift is bounded by the refreshes)
+      restrict_next = false;
+      rbuf ^= 1;
+      if (it % kRefresh<T> == 0) {
+        r_restrict<T, LEV>(G, s, k, F, sm.r, sm.tr, pR[rbuf], sm.ownR, sm);
+      } else {
+        if (tid < LEAF) sm.tr[tid] = sm.t[tid];
+        if (tid < LEV * RANK) {
+          const T v = (T)((double)sm.ownR[tid] - next_alpha * (double)sm.ownQ[tid]);
+          sm.ownR[tid] = v;
+          const int l = tid / RANK, c = tid - l * RANK;
+          pR[rbuf][(((size_t)s * G.levels + l) * G.K + k) * RANK + c] = v;
+        }
+        __syncthreads();
+      }
+    }
+    if (grid_wait(B.barrier, B.abort_flag, target)) return;
   }
   // ---- the solution of the leaf's rows ----
   if (tid < LEAF) B.x[leaf0 + tid] = x;
