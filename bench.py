@@ -31,6 +31,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+FP32_MFMA_PEAK_TFLOPS = 157.3
 METRIC = "PCG ms/solve and M-apply+SpMV HBM GB/s (fraction of peak) at N=8,192"
 
 
@@ -38,6 +39,14 @@ def apply_bytes(n: int, K: int, levels: int, B: int = 1) -> int:
     """Algorithmic bytes of one M-apply: leaf factors, level slabs, gate, r in, y out."""
     L, R = 128, 32
     return B * 4 * (n * L + n * R * levels + n) + B * 8 * n
+
+
+def block_apply_flops(n: int, levels: int, nrhs: int, B: int = 1) -> int:
+    """Algorithmic flops of one block apply: per column the leaf stage (two
+    n x 128 products), restriction and prolongation (two n x 32 products per
+    level) and the gate."""
+    L, R = 128, 32
+    return B * nrhs * (4 * n * L + 4 * n * R * levels + 2 * n)
 
 
 def spmv_bytes(n: int, nnz: int, B: int = 1) -> int:
@@ -160,6 +169,7 @@ def main(argv=None):
     ap.add_argument("--reps", type=int, default=300, help="calls per apply/SpMV timing")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-others", action="store_true", help="skip ms/solve of the other workloads")
+    ap.add_argument("--no-block", action="store_true", help="skip the block (probe) apply timing")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run three 256 MiB device-to-device copies (calibrates HBM byte counters)")
     args = ap.parse_args(argv)
@@ -207,6 +217,32 @@ def main(argv=None):
                    pair_gbs=(ab + sb) / out["pair_us"] / 1e3)
         out["pair_frac"] = out["pair_gbs"] / HBM_PEAK_GBS
         return out
+
+    def measure_block(name):
+        """Block apply M R on the matrix cores with the pages' probe width
+        K_z = max(64, ceil(sqrt(N))) rounded up to 16."""
+        batch = make_config(name)
+        solver = hpcg.Solver(batch.n, batch.row_ptr, batch.col, batch.val, batch=batch.batch,
+                             levels=batch.levels, stream=stream)
+        solver.set_factors(batch.U, batch.W, batch.g)
+        kz = max(64, int(np.ceil(np.sqrt(batch.n))))
+        nrhs = (kz + 15) // 16 * 16
+        R = torch.randn(batch.batch * batch.n * nrhs, device="cuda", dtype=torch.float32)
+        Y = torch.empty_like(R)
+        X = torch.empty_like(R)
+        work = torch.empty(hpcg.hpcg_block_workspace_bytes(solver.handle, nrhs), dtype=torch.uint8, device="cuda")
+        with torch.cuda.stream(stream):
+            t_apply = time_graph(lambda: hpcg.hpcg_apply_M_block(solver.handle, solver.part, R, Y, nrhs, work),
+                                 max(20, args.reps // 10), stream, torch)
+            t_spmv = time_graph(lambda: hpcg.hpcg_spmv_block(solver.handle, solver.part, R, X, nrhs),
+                                max(20, args.reps // 10), stream, torch)
+        fl = block_apply_flops(batch.n, batch.levels, nrhs, batch.batch)
+        solver.close()
+        tf = fl / t_apply / 1e6
+        return {"workload": name, "nrhs": nrhs, "probe_columns": kz, "apply_us": round(t_apply, 3),
+                "tflops": round(tf, 2), "peak_tflops": FP32_MFMA_PEAK_TFLOPS,
+                "frac": round(tf / FP32_MFMA_PEAK_TFLOPS, 4), "flops": fl, "dtype": "f32 (mfma 16x16x4)",
+                "spmv_block_us": round(t_spmv, 3)}
 
     def run_config(name, steps, warmup, with_roofline, engine=None, prec=None):
         batch = make_config(name)
@@ -260,6 +296,11 @@ def main(argv=None):
             log(f"bench: variant {label}")
             _b, o = run_config(args.config, max(3, args.steps // 2), 1, False, eng, prec)
             variants[label] = {"ms_per_solve": round(o["ms_per_solve"], 4), "iterations": o["iterations"][0]}
+    block = []
+    if not args.no_block:
+        for name in ("N8k", "N16k"):
+            log(f"bench: block apply {name}")
+            block.append(measure_block(name))
     cpu = None if args.no_cpu else cpu_baseline(batch)
     iters = main_out["iterations"][0]
     line = {
@@ -305,6 +346,7 @@ def main(argv=None):
         "cpu_baseline": cpu,
         "by_config": others,
         "variants_at_workload": variants,
+        "block_apply": block,
     }
     print(json.dumps(line), flush=True)
     return 0

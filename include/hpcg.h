@@ -173,6 +173,33 @@ hpcg_status hpcg_apply_M(hpcg_handle h, const float* d_r, float* d_y);
  * d_x, d_y float32 [batch*n], must not alias. */
 hpcg_status hpcg_spmv(hpcg_handle h, const float* d_x, float* d_y);
 
+/* Block products for a block of right-hand sides, e.g. the pages' probe block
+ * Z of N x K_z with K_z = max(64, ceil(sqrt(N))) whose M A Z the training
+ * objective needs ("Hierarchical Transformer Preconditioning for Interactive
+ * Physics Simulation", project page, "Cosine Hutchinson Probe Loss" and
+ * "Training Setup"; Supplementary section 3, "Probe vectors").  Every stage of
+ * the apply (section 5, stages (i)-(ii), eqs. (2)-(5)) becomes a dense product
+ * run on the matrix cores.
+ *
+ * Layout: node-major, float32 [batch*n][nrhs] (the nrhs values of one node are
+ * contiguous), 16-byte aligned; nrhs a multiple of 16 in [16, 1024] (pad the
+ * block with zero columns otherwise: HPCG_ERR_SHAPE).  Asynchronous on the
+ * handle's stream.
+ *
+ * hpcg_block_workspace_bytes: scratch that hpcg_apply_M_block needs for a given
+ * nrhs (the per-leaf restrictions and their half sums), 0 for a bad nrhs or
+ * handle.  The caller owns it; it may be reused once the stream has passed.
+ *
+ * hpcg_apply_M_block: Y = M R for every system and column.  d_R and d_Y must
+ * not alias.  d_work may be NULL when levels == 0.
+ *
+ * hpcg_spmv_block: Y = A X for every system and column.  d_X and d_Y must not
+ * alias. */
+size_t hpcg_block_workspace_bytes(hpcg_handle h, int32_t nrhs);
+hpcg_status hpcg_apply_M_block(hpcg_handle h, const float* d_R, float* d_Y, int32_t nrhs,
+                               void* d_work, size_t work_bytes);
+hpcg_status hpcg_spmv_block(hpcg_handle h, const float* d_X, float* d_Y, int32_t nrhs);
+
 /* Solve A x = b for every system with x_0 = 0, stopping a system when its
  * recursively updated residual satisfies ||r_k||_2 <= tol * ||b||_2 (the pages'
  * ||r_k|| / ||r_0|| with r_0 = b), or after maxit iterations.

@@ -15,6 +15,7 @@
 #include <vector>
 
 #include "hpcg_resident.hpp"
+#include "hpcg_block.hpp"
 
 using namespace hpcg;
 
@@ -521,6 +522,75 @@ hpcg_status hpcg_spmv(hpcg_handle h, const float* d_x, float* d_y) {
   const int grid = (N + SPMV_ROWS - 1) / SPMV_ROWS;
   hipLaunchKernelGGL(k_spmv, dim3(grid), dim3(NT), 0, h->stream, h->B.row_ptr, h->B.col, h->B.val, d_x, d_y, N);
   return check_launch(h, "hpcg_spmv launch");
+}
+
+namespace {
+
+bool block_nrhs_ok(int32_t nrhs) { return nrhs >= BNC && nrhs <= 1024 && nrhs % BNC == 0; }
+
+BlockGeom block_geom(const hpcg_ctx* h, int32_t nrhs) {
+  BlockGeom bg;
+  bg.n = h->G.n;
+  bg.K = h->G.K;
+  bg.levels = h->G.levels;
+  bg.B = h->G.B;
+  bg.nrhs = nrhs;
+  bg.tiles = nrhs / BNC;
+  return bg;
+}
+
+size_t block_half_bytes(const hpcg_ctx* h, int32_t nrhs) {
+  return align_up((size_t)h->G.B * h->G.levels * h->G.K * RANK * nrhs * 4);
+}
+
+}  // namespace
+
+size_t hpcg_block_workspace_bytes(hpcg_handle h, int32_t nrhs) {
+  if (!h || !block_nrhs_ok(nrhs)) return 0;
+  return 2 * block_half_bytes(h, nrhs) + kAlign;
+}
+
+hpcg_status hpcg_apply_M_block(hpcg_handle h, const float* d_R, float* d_Y, int32_t nrhs, void* d_work,
+                               size_t work_bytes) {
+  if (!h) return fail(nullptr, HPCG_ERR_INVALID_ARG, "handle is NULL");
+  if (!d_R || !d_Y) return fail(h, HPCG_ERR_INVALID_ARG, "block pointer is NULL");
+  if (d_R == d_Y) return fail(h, HPCG_ERR_INVALID_ARG, "d_R and d_Y must not alias");
+  if (!block_nrhs_ok(nrhs)) return fail(h, HPCG_ERR_SHAPE, "nrhs must be a multiple of 16 in [16, 1024]");
+  if ((reinterpret_cast<uintptr_t>(d_R) | reinterpret_cast<uintptr_t>(d_Y)) % 16)
+    return fail(h, HPCG_ERR_INVALID_ARG, "d_R and d_Y must be 16-byte aligned");
+  if (!h->factors_set) return fail(h, HPCG_ERR_STATE, "hpcg_set_factors has not been called");
+  const size_t half = block_half_bytes(h, nrhs);
+  if (h->G.levels > 0) {
+    if (!d_work) return fail(h, HPCG_ERR_INVALID_ARG, "d_work is NULL");
+    if (work_bytes < hpcg_block_workspace_bytes(h, nrhs)) return fail(h, HPCG_ERR_WORKSPACE, "block workspace too small");
+  }
+  const BlockGeom bg = block_geom(h, nrhs);
+  char* wk = reinterpret_cast<char*>(align_up(reinterpret_cast<uintptr_t>(d_work)));
+  float* Q = reinterpret_cast<float*>(wk);
+  float* H = reinterpret_cast<float*>(wk + half);
+  const int grid = h->G.B * h->G.K * bg.tiles;
+  hipLaunchKernelGGL(k_block_restrict, dim3(grid), dim3(BNT), 0, h->stream, bg, h->B.U, h->B.W, h->B.g, d_R, d_Y, Q);
+  if (h->G.levels > 0) {
+    size_t sys_total = 0;
+    for (int l = 0; l < h->G.levels; ++l) sys_total += (size_t)(h->G.K >> l) * RANK * nrhs;
+    const size_t total = sys_total * h->G.B;
+    hipLaunchKernelGGL(k_block_halfsum, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, h->stream, bg, Q, H);
+    hipLaunchKernelGGL(k_block_prolong, dim3(grid), dim3(BNT), 0, h->stream, bg, h->B.W, H, d_Y);
+  }
+  return check_launch(h, "hpcg_apply_M_block launch");
+}
+
+hpcg_status hpcg_spmv_block(hpcg_handle h, const float* d_X, float* d_Y, int32_t nrhs) {
+  if (!h) return fail(nullptr, HPCG_ERR_INVALID_ARG, "handle is NULL");
+  if (!d_X || !d_Y) return fail(h, HPCG_ERR_INVALID_ARG, "block pointer is NULL");
+  if (d_X == d_Y) return fail(h, HPCG_ERR_INVALID_ARG, "d_X and d_Y must not alias");
+  if (!block_nrhs_ok(nrhs)) return fail(h, HPCG_ERR_SHAPE, "nrhs must be a multiple of 16 in [16, 1024]");
+  if ((reinterpret_cast<uintptr_t>(d_X) | reinterpret_cast<uintptr_t>(d_Y)) % 16)
+    return fail(h, HPCG_ERR_INVALID_ARG, "d_X and d_Y must be 16-byte aligned");
+  const size_t threads = (size_t)h->G.B * h->G.n * (nrhs / 4);
+  hipLaunchKernelGGL(k_spmv_block, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, h->stream, h->B.row_ptr,
+                     h->B.col, h->B.val, d_X, d_Y, h->G.B * h->G.n, nrhs);
+  return check_launch(h, "hpcg_spmv_block launch");
 }
 
 hpcg_status hpcg_solve(hpcg_handle h, const float* d_b, double* d_x, double tol, int32_t maxit,

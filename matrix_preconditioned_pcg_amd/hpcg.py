@@ -86,6 +86,9 @@ def lib() -> ctypes.CDLL:
         "hpcg_set_factors": (i32, [vp, vp, vp, vp]),
         "hpcg_apply_M": (i32, [vp, vp, vp]),
         "hpcg_spmv": (i32, [vp, vp, vp]),
+        "hpcg_block_workspace_bytes": (sz, [vp, i32]),
+        "hpcg_apply_M_block": (i32, [vp, vp, vp, i32, vp, sz]),
+        "hpcg_spmv_block": (i32, [vp, vp, vp, i32]),
         "hpcg_solve": (i32, [vp, vp, vp, dbl, i32, P(i32), P(dbl)]),
         "hpcg_last_solve_status": (i32, [vp, P(i32)]),
         "hpcg_set_option": (i32, [vp, i32, i32]),
@@ -196,6 +199,26 @@ def hpcg_apply_M(h, part: hpcg_partition, r, y):
 def hpcg_spmv(h, part: hpcg_partition, x, y):
     N = part.n * part.batch
     _check(lib().hpcg_spmv(h, _ptr(x, torch.float32, N, "x"), _ptr(y, torch.float32, N, "y")), h)
+
+
+def hpcg_block_workspace_bytes(h, nrhs: int) -> int:
+    return int(lib().hpcg_block_workspace_bytes(h, int(nrhs)))
+
+
+def hpcg_apply_M_block(h, part: hpcg_partition, R, Y, nrhs: int, work=None):
+    """R, Y: float32 device tensors of batch*n*nrhs elements, node-major; work:
+    uint8 device tensor of hpcg_block_workspace_bytes(h, nrhs) bytes (or None
+    when levels == 0)."""
+    N = part.n * part.batch
+    wp, wb = (None, 0) if work is None else (work.data_ptr(), work.numel())
+    _check(lib().hpcg_apply_M_block(h, _ptr(R, torch.float32, N * nrhs, "R"), _ptr(Y, torch.float32, N * nrhs, "Y"),
+                                    int(nrhs), wp, wb), h)
+
+
+def hpcg_spmv_block(h, part: hpcg_partition, X, Y, nrhs: int):
+    N = part.n * part.batch
+    _check(lib().hpcg_spmv_block(h, _ptr(X, torch.float32, N * nrhs, "X"), _ptr(Y, torch.float32, N * nrhs, "Y"),
+                                 int(nrhs)), h)
 
 
 def hpcg_solve(h, part: hpcg_partition, b, x, tol: float, maxit: int):
@@ -313,6 +336,33 @@ class Solver:
         y = torch.empty_like(x) if y is None else y
         hpcg_spmv(self.handle, self.part, x, y)
         return y
+
+    def _block(self, V, nrhs):
+        V = torch.as_tensor(V, dtype=torch.float32).to(self.device).contiguous()
+        if V.numel() != self.batch * self.n * nrhs:
+            raise ValueError(f"block must have batch*n*nrhs = {self.batch * self.n * nrhs} elements")
+        return V
+
+    def apply_M_block(self, R, nrhs: int, Y=None):
+        """Y = M R for a node-major block [batch*n, nrhs]."""
+        R = self._block(R, nrhs)
+        Y = torch.empty_like(R) if Y is None else Y
+        nbytes = hpcg_block_workspace_bytes(self.handle, nrhs)
+        if nbytes == 0:
+            raise HPCGError(HPCG_ERR_SHAPE, "nrhs must be a multiple of 16 in [16, 1024]")
+        work = getattr(self, "_bwork", None)
+        if work is None or work.numel() < nbytes:
+            work = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+            self._bwork = work
+        hpcg_apply_M_block(self.handle, self.part, R, Y, nrhs, work)
+        return Y
+
+    def spmv_block(self, X, nrhs: int, Y=None):
+        """Y = A X for a node-major block [batch*n, nrhs]."""
+        X = self._block(X, nrhs)
+        Y = torch.empty_like(X) if Y is None else Y
+        hpcg_spmv_block(self.handle, self.part, X, Y, nrhs)
+        return Y
 
     def solve(self, b, tol: float = 1e-6, maxit: int = 1000, x=None) -> SolveResult:
         b = self._vec(b)

@@ -22,9 +22,10 @@ from .hmatrix import (  # noqa: F401
     tile_count,
     apply_M,
     apply_M_batch,
+    apply_M_block,
     dense_M,
     dense_M_entry,
     weyl_lower_bound,
 )
-from .sparse import spmv, spmv_batch, true_relres, dense_A  # noqa: F401
+from .sparse import spmv, spmv_batch, spmv_block, true_relres, dense_A  # noqa: F401
 from .pcg import pcg, pcg_batch, PCGResult  # noqa: F401

@@ -97,6 +97,14 @@ def apply_M_batch(U, W, g, r):
     return np.stack([apply_M(U[s], W[s], g[s], r[s]) for s in range(U.shape[0])])
 
 
+def apply_M_block(U, W, g, R):
+    """Y = M R for a block R of shape [N, nrhs]: M applied to every column
+    (the probe-block product of the pages' training objective, project page,
+    "Cosine Hutchinson Probe Loss")."""
+    R = np.asarray(R, dtype=np.float64)
+    return np.stack([apply_M(U, W, g, R[:, j]) for j in range(R.shape[1])], axis=1)
+
+
 def dense_M_entry(U, W, g, i: int, j: int) -> float:
     """One entry M[i, j], written from the partition's geometry rather than its tiles.
 

@@ -28,6 +28,12 @@ def spmv(row_ptr, col, val, x, dtype=np.float64):
     return y
 
 
+def spmv_block(row_ptr, col, val, X):
+    """Y = A X for a block X of shape [n, nrhs], column by column."""
+    X = np.asarray(X, dtype=np.float64)
+    return np.stack([spmv(row_ptr, col, val, X[:, j]) for j in range(X.shape[1])], axis=1)
+
+
 def spmv_batch(row_ptr, col, val, x):
     """Block-diagonal batch: global CSR over B*n rows, x of shape [B, n]."""
     x = np.asarray(x, dtype=np.float64)

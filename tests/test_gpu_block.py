@@ -1,0 +1,132 @@
+"""GPU parity of the block (multi-right-hand-side) apply and SpMV, through the C ABI.
+
+Bar: per column, relative L2 error <= 1e-5 against the fp64 oracle on the same
+fp32 inputs, and elementwise |Y - Y_ref| <= 1e-5 (|M| |R|) (fp32 arithmetic on
+the matrix cores, fp32 accumulation).
+"""
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from workloads import make_config  # noqa: E402
+from workloads.generate import build_batch, random_system  # noqa: E402
+
+from matrix_preconditioned_pcg_amd import hpcg  # noqa: E402
+
+TOL = 1e-5
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _solver(batch):
+    s = hpcg.Solver(batch.n, batch.row_ptr, batch.col, batch.val, batch=batch.batch, levels=batch.levels)
+    s.set_factors(batch.U, batch.W if batch.levels else None, batch.g)
+    return s
+
+
+def _check_block_apply(batch, s, R):
+    nrhs = R.shape[-1]
+    Y = s.apply_M_block(R.reshape(-1), nrhs).cpu().numpy().astype(np.float64).reshape(batch.batch, batch.n, nrhs)
+    for i in range(batch.batch):
+        sy = batch.system(i)
+        ref = oracle.apply_M_block(sy.U, sy.W, sy.g, R[i])
+        mag = oracle.apply_M_block(np.abs(sy.U), np.abs(sy.W), np.abs(sy.g), np.abs(R[i]))
+        rel = np.linalg.norm(Y[i] - ref, axis=0) / np.linalg.norm(ref, axis=0)
+        assert rel.max() <= TOL, (i, rel.max(), int(rel.argmax()))
+        bad = np.abs(Y[i] - ref) > TOL * mag + 1e-30
+        assert not bad.any(), (i, np.argwhere(bad)[:5])
+    return Y
+
+
+@pytest.mark.parametrize("name,nrhs", [("N1k", 16), ("N1k", 64), ("N8k", 64), ("N16k", 128), ("tet4k", 48),
+                                       ("batch64x2k", 16)])
+def test_block_apply_parity(name, nrhs):
+    batch = make_config(name, batch=8 if name == "batch64x2k" else None)
+    _log(f"block apply {name} nrhs={nrhs}")
+    s = _solver(batch)
+    R = np.random.default_rng(nrhs).standard_normal((batch.batch, batch.n, nrhs)).astype(np.float32)
+    _check_block_apply(batch, s, R)
+    s.close()
+
+
+@pytest.mark.parametrize("n,levels,batch", [(128, 0, 1), (256, 1, 2), (1024, 2, 1), (2048, 4, 3)])
+def test_block_apply_small(n, levels, batch):
+    _log(f"block apply small n={n} levels={levels} batch={batch}")
+    systems = [random_system(n, seed=200 + s, levels=levels).system(0) for s in range(batch)]
+    b = build_batch(systems, name=f"blk{n}_{levels}_{batch}")
+    s = _solver(b)
+    R = np.random.default_rng(n).standard_normal((batch, n, 32)).astype(np.float32)
+    _check_block_apply(b, s, R)
+    s.close()
+
+
+def test_block_apply_columns_match_single_apply():
+    batch = make_config("N8k")
+    _log("block apply vs single apply N8k")
+    s = _solver(batch)
+    R = np.random.default_rng(3).standard_normal((batch.n, 32)).astype(np.float32)
+    Y = s.apply_M_block(R.reshape(-1), 32).cpu().numpy().reshape(batch.n, 32)
+    for j in (0, 13, 31):
+        y = s.apply_M(R[:, j].copy()).cpu().numpy()
+        assert np.linalg.norm(Y[:, j] - y) <= 1e-6 * np.linalg.norm(y)
+    s.close()
+
+
+@pytest.mark.parametrize("name,nrhs", [("N8k", 64), ("tet4k", 16), ("batch64x2k", 32)])
+def test_block_spmv_parity(name, nrhs):
+    batch = make_config(name)
+    _log(f"block spmv {name} nrhs={nrhs}")
+    s = _solver(batch)
+    X = np.random.default_rng(9).standard_normal((batch.batch * batch.n, nrhs)).astype(np.float32)
+    Y = s.spmv_block(X.reshape(-1), nrhs).cpu().numpy().astype(np.float64).reshape(-1, nrhs)
+    ref = oracle.spmv_block(batch.row_ptr, batch.col, batch.val, X)
+    mag = oracle.spmv_block(batch.row_ptr, batch.col, np.abs(batch.val), np.abs(X))
+    rel = np.linalg.norm(Y - ref, axis=0) / np.linalg.norm(ref, axis=0)
+    assert rel.max() <= TOL, rel.max()
+    assert not (np.abs(Y - ref) > TOL * mag + 1e-30).any()
+    s.close()
+
+
+def test_probe_block_MAZ():
+    # the pages' probe product M A Z with K_z = max(64, ceil(sqrt(N))) padded to 16
+    batch = make_config("N8k")
+    kz = max(64, int(np.ceil(np.sqrt(batch.n))))
+    nrhs = (kz + 15) // 16 * 16
+    _log(f"probe block M A Z N8k nrhs={nrhs}")
+    s = _solver(batch)
+    Z = np.zeros((batch.n, nrhs), dtype=np.float32)
+    Z[:, :kz] = np.random.default_rng(21).standard_normal((batch.n, kz))
+    AZ = s.spmv_block(Z.reshape(-1), nrhs)
+    MAZ = s.apply_M_block(AZ, nrhs).cpu().numpy().astype(np.float64).reshape(batch.n, nrhs)
+    sy = batch.system(0)
+    ref = oracle.apply_M_block(sy.U, sy.W, sy.g, oracle.spmv_block(sy.row_ptr, sy.col, sy.val, Z))
+    rel = np.linalg.norm(MAZ[:, :kz] - ref[:, :kz]) / np.linalg.norm(ref[:, :kz])
+    assert rel <= 2 * TOL, rel
+    assert not MAZ[:, kz:].any()
+    s.close()
+
+
+def test_block_argument_errors():
+    batch = make_config("N1k")
+    s = _solver(batch)
+    for bad in (0, 8, 20, 2048):
+        assert hpcg.hpcg_block_workspace_bytes(s.handle, bad) == 0
+    R = torch.zeros(batch.n * 24, device="cuda")
+    with pytest.raises(hpcg.HPCGError):
+        hpcg.hpcg_apply_M_block(s.handle, s.part, R, torch.empty_like(R), 24, None)
+    R = torch.zeros(batch.n * 16, device="cuda")
+    with pytest.raises(hpcg.HPCGError):
+        hpcg.hpcg_apply_M_block(s.handle, s.part, R, torch.empty_like(R), 16, None)   # no workspace
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(hpcg.HPCGError):
+        hpcg.hpcg_apply_M_block(s.handle, s.part, R, torch.empty_like(R), 16, small)
+    with pytest.raises(hpcg.HPCGError):
+        hpcg.hpcg_spmv_block(s.handle, s.part, R, R, 16)
+    s.close()

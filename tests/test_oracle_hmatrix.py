@@ -125,3 +125,12 @@ def test_weyl_bound_is_a_true_lower_bound_on_rough_factors():
     U, W, g = _factors(8, 6, 3, 3, seed=5)
     M = oracle.dense_M(U, W, g)
     assert oracle.weyl_lower_bound(U, W, g) <= np.linalg.eigvalsh(M)[0] + 1e-10
+
+
+@pytest.mark.parametrize("K,L,R,levels", [(4, 6, 2, 2), (8, 4, 3, 3)])
+def test_block_apply_is_dense_product(K, L, R, levels):
+    # the block apply against the dense closed form times the whole block
+    U, W, g = _factors(K, L, R, levels, seed=31 + K)
+    R_blk = np.random.default_rng(5).standard_normal((K * L, 7))
+    np.testing.assert_allclose(oracle.apply_M_block(U, W, g, R_blk), oracle.dense_M(U, W, g) @ R_blk,
+                               rtol=1e-12, atol=1e-12 * np.abs(R_blk).max())

@@ -97,3 +97,11 @@ def test_tet_stiffness_kills_constants_away_from_dirichlet():
     np.testing.assert_allclose(rowsum[free], 0.0, atol=1e-10 * np.abs(A).max())
     assert np.all(np.linalg.eigvalsh(A) > 0)                # SPD after elimination
     assert info["n_tets"] == 6 * 5 ** 3
+
+
+def test_spmv_block_matches_scipy():
+    b = make_config("N1k")
+    A = scipy.sparse.csr_matrix((b.val.astype(np.float64), b.col, b.row_ptr), shape=(b.n, b.n))
+    X = np.random.default_rng(1).standard_normal((b.n, 5))
+    np.testing.assert_allclose(oracle.spmv_block(b.row_ptr, b.col, b.val, X), A @ X,
+                               rtol=1e-13, atol=1e-13 * np.abs(A).sum(axis=1).max() * np.abs(X).max())
