@@ -569,13 +569,33 @@ hpcg_status hpcg_apply_M_block(hpcg_handle h, const float* d_R, float* d_Y, int3
   float* Q = reinterpret_cast<float*>(wk);
   float* H = reinterpret_cast<float*>(wk + half);
   const int grid = h->G.B * h->G.K * bg.tiles;
-  hipLaunchKernelGGL(k_block_restrict, dim3(grid), dim3(BNT), 0, h->stream, bg, h->B.U, h->B.W, h->B.g, d_R, d_Y, Q);
+  switch (h->G.levels) {
+#define HPCG_BLOCK_RESTRICT(LV)                                                                          \
+    case LV:                                                                                             \
+      hipLaunchKernelGGL(k_block_restrict<LV>, dim3(grid), dim3(BNT), 0, h->stream, bg, h->B.U, h->B.W, \
+                         h->B.g, d_R, d_Y, Q);                                                           \
+      break;
+    HPCG_BLOCK_RESTRICT(0) HPCG_BLOCK_RESTRICT(1) HPCG_BLOCK_RESTRICT(2) HPCG_BLOCK_RESTRICT(3)
+    HPCG_BLOCK_RESTRICT(4) HPCG_BLOCK_RESTRICT(5) HPCG_BLOCK_RESTRICT(6) HPCG_BLOCK_RESTRICT(7)
+    HPCG_BLOCK_RESTRICT(8)
+#undef HPCG_BLOCK_RESTRICT
+    default: return fail(h, HPCG_ERR_SHAPE, "levels out of range");
+  }
   if (h->G.levels > 0) {
     size_t sys_total = 0;
     for (int l = 0; l < h->G.levels; ++l) sys_total += (size_t)(h->G.K >> l) * RANK * nrhs;
     const size_t total = sys_total * h->G.B;
     hipLaunchKernelGGL(k_block_halfsum, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, h->stream, bg, Q, H);
-    hipLaunchKernelGGL(k_block_prolong, dim3(grid), dim3(BNT), 0, h->stream, bg, h->B.W, H, d_Y);
+    switch (h->G.levels) {
+#define HPCG_BLOCK_PROLONG(LV)                                                                          \
+      case LV:                                                                                          \
+        hipLaunchKernelGGL(k_block_prolong<LV>, dim3(grid), dim3(BNT), 0, h->stream, bg, h->B.W, H, d_Y); \
+        break;
+      HPCG_BLOCK_PROLONG(1) HPCG_BLOCK_PROLONG(2) HPCG_BLOCK_PROLONG(3) HPCG_BLOCK_PROLONG(4)
+      HPCG_BLOCK_PROLONG(5) HPCG_BLOCK_PROLONG(6) HPCG_BLOCK_PROLONG(7) HPCG_BLOCK_PROLONG(8)
+#undef HPCG_BLOCK_PROLONG
+      default: return fail(h, HPCG_ERR_SHAPE, "levels out of range");
+    }
   }
   return check_launch(h, "hpcg_apply_M_block launch");
 }

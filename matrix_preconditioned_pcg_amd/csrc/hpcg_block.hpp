@@ -47,11 +47,16 @@ struct BlockGeom {
   int tiles;             // nrhs / BNC
 };
 
-// Workgroup -> (system, leaf, column tile).
+// Workgroup -> (system, leaf, column tile).  Workgroups are dispatched to the
+// eight XCDs round-robin; the items are dealt so that each XCD gets a
+// contiguous item range, i.e. all column tiles of a leaf run on one XCD and
+// read that leaf's factors through the same L2.
 struct BItem { int s, k, ct, leaf0; };
 __device__ __forceinline__ BItem bitem(const BlockGeom& G) {
   BItem o;
-  const int b = blockIdx.x;
+  const int nblk = G.B * G.K * G.tiles;
+  const int b = (nblk % NXCD) ? (int)blockIdx.x
+                              : (int)(blockIdx.x % NXCD) * (nblk / NXCD) + (int)(blockIdx.x / NXCD);
   o.ct = b % G.tiles;
   const int lk = b / G.tiles;
   o.s = lk / G.K;
@@ -65,7 +70,9 @@ __device__ __forceinline__ size_t q_index(const BlockGeom& G, int s, int l, int 
   return ((((size_t)s * G.levels + l) * G.K + k) * RANK + row) * G.nrhs;
 }
 
-// (1) leaf stage, gate and restriction.
+// (1) leaf stage, gate and restriction.  All global operand loads of a stage
+// are issued before its products, and the next level's before this level's.
+template <int LEV>
 __global__ __launch_bounds__(BNT) void k_block_restrict(BlockGeom G, const float* __restrict__ U,
                                                         const float* __restrict__ W, const float* __restrict__ g,
                                                         const float* __restrict__ R, float* __restrict__ Y,
@@ -77,15 +84,25 @@ __global__ __launch_bounds__(BNT) void k_block_restrict(BlockGeom G, const float
   const int q = lane >> 4, r = lane & 15;
   const int c0 = it.ct * BNC;
   const float* Uk = U + ((size_t)it.s * G.K + it.k) * LEAF * LEAF;
+  // restriction work of this wave: rank tile (w & 1) of levels (w >> 1), +2, ...
+  const int mt = w & 1;
+  auto wlev = [&](int l) {
+    return W + (((size_t)it.s * LEV + l) * G.K + it.k) * LEAF * RANK + 16 * mt + r;
+  };
   // R tile: 128 rows x 64 bytes, straight into LDS
   dma_to_lds(Rs, LEAF * BNC / 4, [&](int c) { return R + (size_t)(it.leaf0 + (c >> 2)) * G.nrhs + c0 + 4 * (c & 3); });
   // GEMM 1 A operands: U[4s + q][32w + r] and U[4s + q][32w + 16 + r], s = 0..31
-  float ua[32], ub[32];
+  float ua[32], ub[32], wa[32];
 #pragma unroll
   for (int s = 0; s < 32; ++s) {
     const float* row = Uk + (size_t)(4 * s + q) * LEAF + 32 * w + r;
     ua[s] = row[0];
     ub[s] = row[16];
+  }
+  if (LEV > (w >> 1)) {
+    const float* Wl = wlev(w >> 1);
+#pragma unroll
+    for (int s = 0; s < 32; ++s) wa[s] = Wl[(size_t)(4 * s + q) * RANK];
   }
   lds_dma_wait();
   // T = U_k^T R_k: this wave's rows [32w, 32w + 32) of T
@@ -99,34 +116,51 @@ __global__ __launch_bounds__(BNT) void k_block_restrict(BlockGeom G, const float
   // T^T into LDS: lane holds T[32w + 4q + v][r] (and + 16)
   *reinterpret_cast<mf4*>(&Ts[r * TS_STRIDE + 32 * w + 4 * q]) = ta;
   *reinterpret_cast<mf4*>(&Ts[r * TS_STRIDE + 32 * w + 16 + 4 * q]) = tb;
-  // restriction Q_l = W_l[k]^T R_k: wave w takes rank tile (w & 1) of the levels
-  // l = (w >> 1), (w >> 1) + 2, ...
-  for (int l = w >> 1; l < G.levels; l += 2) {
-    const float* Wl = W + (((size_t)it.s * G.levels + l) * G.K + it.k) * LEAF * RANK + 16 * (w & 1) + r;
-    float wa[32];
+  // restriction Q_l = W_l[k]^T R_k, two accumulation chains (even / odd k
+  // steps) summed at the end
 #pragma unroll
-    for (int s = 0; s < 32; ++s) wa[s] = Wl[(size_t)(4 * s + q) * RANK];
-    mf4 acc = {0, 0, 0, 0};
+  for (int l = 0; l < LEV; ++l) {
+    if ((l & 1) != (w >> 1)) continue;
+    float wn[32];
+    if (l + 2 < LEV) {
+      const float* Wn = wlev(l + 2);
 #pragma unroll
-    for (int s = 0; s < 32; ++s) acc = mfma4(wa[s], Rs[(4 * s + q) * BNC + r], acc);
-    float* Qo = Q + q_index(G, it.s, l, it.k, 16 * (w & 1) + 4 * q) + c0 + r;
+      for (int s = 0; s < 32; ++s) wn[s] = Wn[(size_t)(4 * s + q) * RANK];
+    }
+    mf4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < 32; s += 2) {
+      a0 = mfma4(wa[s], Rs[(4 * s + q) * BNC + r], a0);
+      a1 = mfma4(wa[s + 1], Rs[(4 * s + 4 + q) * BNC + r], a1);
+    }
+    const mf4 acc = a0 + a1;
+    float* Qo = Q + q_index(G, it.s, l, it.k, 16 * mt + 4 * q) + c0 + r;
 #pragma unroll
     for (int v = 0; v < 4; ++v) Qo[(size_t)v * G.nrhs] = acc[v];
+    if (l + 2 < LEV) {
+#pragma unroll
+      for (int s = 0; s < 32; ++s) wa[s] = wn[s];
+    }
+  }
+  // GEMM 2 operands: rows 32w + r and 32w + 16 + r of U_k (L2-resident by now)
+  const float* Ua = Uk + (size_t)(32 * w + r) * LEAF + 4 * q;
+  const float* Ub = Ua + 16 * LEAF;
+  mf4 au[LEAF / 16], bu[LEAF / 16];
+#pragma unroll
+  for (int ch = 0; ch < LEAF / 16; ++ch) {
+    au[ch] = *reinterpret_cast<const mf4*>(Ua + 16 * ch);
+    bu[ch] = *reinterpret_cast<const mf4*>(Ub + 16 * ch);
   }
   __syncthreads();
   // Y = U_k T + g R: this wave's rows [32w, 32w + 32)
   mf4 ya = {0, 0, 0, 0}, yb = {0, 0, 0, 0};
-  const float* Ua = Uk + (size_t)(32 * w + r) * LEAF + 4 * q;
-  const float* Ub = Ua + 16 * LEAF;
 #pragma unroll
   for (int ch = 0; ch < LEAF / 16; ++ch) {
-    const mf4 au = *reinterpret_cast<const mf4*>(Ua + 16 * ch);
-    const mf4 bu = *reinterpret_cast<const mf4*>(Ub + 16 * ch);
     const mf4 bt = *reinterpret_cast<const mf4*>(&Ts[r * TS_STRIDE + 16 * ch + 4 * q]);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      ya = mfma4(au[t], bt[t], ya);
-      yb = mfma4(bu[t], bt[t], yb);
+      ya = mfma4(au[ch][t], bt[t], ya);
+      yb = mfma4(bu[ch][t], bt[t], yb);
     }
   }
 #pragma unroll
@@ -161,25 +195,39 @@ __global__ void k_block_halfsum(BlockGeom G, const float* __restrict__ Q, float*
   const size_t e = rem - (size_t)h * per;
   const int span = 1 << l;
   const float* src = Q + q_index(G, s, l, h * span, 0) + e;
-  float a = src[0];
-  for (int i = 1; i < span; ++i) a += src[(size_t)i * per];
+  // loads in batches of 8 in flight; the sum keeps leaf order
+  float a = 0.f;
+  int i = 0;
+  for (; i + 8 <= span; i += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = src[(size_t)(i + u) * per];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a += v[u];
+  }
+  for (; i < span; ++i) a += src[(size_t)i * per];
   H[q_index(G, s, l, h, 0) + e] = a;
 }
 
-// (3) prolongation: Y_k += sum_l W_l[k] H_l[(k >> l) ^ 1].
+// (3) prolongation: Y_k += sum_l W_l[k] H_l[(k >> l) ^ 1].  Every level's slab
+// rows are loaded in one batch up front.
+template <int LEV>
 __global__ __launch_bounds__(BNT) void k_block_prolong(BlockGeom G, const float* __restrict__ W,
                                                        const float* __restrict__ H, float* __restrict__ Y) {
-  __shared__ __attribute__((aligned(16))) float Ps[MAX_LEVELS * BNC * PS_STRIDE];   // [l][col][rank]
+  __shared__ __attribute__((aligned(16))) float Ps[(LEV > 0 ? LEV : 1) * BNC * PS_STRIDE];   // [l][col][rank]
   const BItem it = bitem(G);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int q = lane >> 4, r = lane & 15;
   const int c0 = it.ct * BNC;
-  // partner half sums, transposed into LDS
-  for (int e = tid; e < G.levels * RANK * BNC; e += BNT) {
-    const int l = e / (RANK * BNC), rem = e - l * RANK * BNC;
-    const int row = rem / BNC, col = rem - row * BNC;
-    const int hp = (it.k >> l) ^ 1;
-    Ps[(l * BNC + col) * PS_STRIDE + row] = H[q_index(G, it.s, l, hp, row) + c0 + col];
+  mf4 aw[LEV > 0 ? LEV : 1][2], bw[LEV > 0 ? LEV : 1][2];
+#pragma unroll
+  for (int l = 0; l < LEV; ++l) {
+    const float* Wa = W + ((((size_t)it.s * LEV + l) * G.K + it.k) * LEAF + 32 * w + r) * RANK + 4 * q;
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+      aw[l][ch] = *reinterpret_cast<const mf4*>(Wa + 16 * ch);
+      bw[l][ch] = *reinterpret_cast<const mf4*>(Wa + 16 * RANK + 16 * ch);
+    }
   }
   // accumulators start from the leaf stage's Y
   mf4 ya, yb;
@@ -188,19 +236,33 @@ __global__ __launch_bounds__(BNT) void k_block_prolong(BlockGeom G, const float*
     ya[v] = Y[(size_t)(it.leaf0 + 32 * w + 4 * q + v) * G.nrhs + c0 + r];
     yb[v] = Y[(size_t)(it.leaf0 + 32 * w + 16 + 4 * q + v) * G.nrhs + c0 + r];
   }
+  // partner half sums, transposed into LDS: all loads first, then the stores
+  constexpr int PER = (LEV > 0 ? LEV : 1) * RANK * BNC / BNT;   // elements per thread
+  float hv[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int e = tid + u * BNT;
+    const int l = e / (RANK * BNC), rem = e - l * RANK * BNC;
+    const int row = rem / BNC, col = rem - row * BNC;
+    hv[u] = H[q_index(G, it.s, l, (it.k >> l) ^ 1, row) + c0 + col];
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int e = tid + u * BNT;
+    const int l = e / (RANK * BNC), rem = e - l * RANK * BNC;
+    const int row = rem / BNC, col = rem - row * BNC;
+    Ps[(l * BNC + col) * PS_STRIDE + row] = hv[u];
+  }
   __syncthreads();
-  for (int l = 0; l < G.levels; ++l) {
-    const float* Wa = W + ((((size_t)it.s * G.levels + l) * G.K + it.k) * LEAF + 32 * w + r) * RANK + 4 * q;
-    const float* Wb = Wa + 16 * RANK;
+#pragma unroll
+  for (int l = 0; l < LEV; ++l) {
 #pragma unroll
     for (int ch = 0; ch < RANK / 16; ++ch) {
-      const mf4 aw = *reinterpret_cast<const mf4*>(Wa + 16 * ch);
-      const mf4 bw = *reinterpret_cast<const mf4*>(Wb + 16 * ch);
       const mf4 bp = *reinterpret_cast<const mf4*>(&Ps[(l * BNC + r) * PS_STRIDE + 16 * ch + 4 * q]);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        ya = mfma4(aw[t], bp[t], ya);
-        yb = mfma4(bw[t], bp[t], yb);
+        ya = mfma4(aw[l][ch][t], bp[t], ya);
+        yb = mfma4(bw[l][ch][t], bp[t], yb);
       }
     }
   }
