@@ -33,7 +33,8 @@ struct Layout {
 constexpr size_t kMaxLds = 160 * 1024;
 
 // control words, each on its own 256-byte line
-constexpr size_t kCtlBarrier = 0, kCtlAbort = 256, kCtlItbase = 512, kCtlReplays = 768, kCtlBytes = 1024;
+constexpr size_t kCtlBarrier = 0, kCtlAbort = 256, kCtlItbase = 512, kCtlReplays = 768, kCtlFlag = 1024,
+                 kCtlBytes = 1280;
 
 constexpr int kMaxSplit = 8;   // workgroups per leaf in the streaming kernels
 
@@ -446,6 +447,7 @@ hpcg_status hpcg_create(const hpcg_partition* part, const int32_t* d_row_ptr, co
   B.abort_flag = reinterpret_cast<int*>(w + lay.ctl + kCtlAbort);
   B.itbase = reinterpret_cast<int*>(w + lay.ctl + kCtlItbase);
   B.replays = reinterpret_cast<int*>(w + lay.ctl + kCtlReplays);
+  B.bflag = reinterpret_cast<unsigned*>(w + lay.ctl + kCtlFlag);
   B.tol = 1e-6;
   B.maxit = 1000;
 

@@ -101,6 +101,7 @@ struct Bufs {
   double* rz_part;
   SysState* st;        // [B]
   unsigned* barrier;   // device-wide barrier arrival counter
+  unsigned* bflag;     // resident engine: number of the last completed barrier
   int* abort_flag;     // set when a barrier wait exceeds its bound
   int* itbase;         // graph engine: absolute iteration of the replay's first step
   int* replays;        // graph engine: replays finished
@@ -184,14 +185,17 @@ __device__ __forceinline__ void dma_to_lds(void* dst, int nchunks, AddrFn addr) 
   }
 }
 
-// dma_to_lds for a workgroup of NW waves.
-template <int NW, typename AddrFn>
+// dma_to_lds for a workgroup of NW waves.  CPOL is the load's cache policy:
+// 0 = default, CPOL_AGENT = agent-scope coherent (sc1: never served from a
+// stale copy in another XCD's L2).
+constexpr int CPOL_AGENT = 16;
+template <int NW, int CPOL = 0, typename AddrFn>
 __device__ __forceinline__ void dma_to_lds_n(void* dst, int nchunks, AddrFn addr) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int q = wave; q * 64 < nchunks; q += NW) {
     const int c = q * 64 + lane;
     lds_vptr l = (lds_vptr)((__attribute__((address_space(3))) char*)dst + q * 1024);
-    if (c < nchunks) __builtin_amdgcn_global_load_lds(addr(c), l, 16, 0, 0);
+    if (c < nchunks) __builtin_amdgcn_global_load_lds(addr(c), l, 16, 0, CPOL);
   }
 }
 

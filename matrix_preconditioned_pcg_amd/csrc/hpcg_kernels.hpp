@@ -127,6 +127,7 @@ __global__ void k_advance(Geom G, Bufs B, int unroll, int* host_flag) {
 __global__ void k_reset(Bufs B, int itbase, int* host_flag) {
   if (threadIdx.x != 0 || blockIdx.x != 0) return;
   *B.barrier = 0u;
+  *B.bflag = 0u;
   *B.abort_flag = 0;
   *B.itbase = itbase;
   *B.replays = 0;

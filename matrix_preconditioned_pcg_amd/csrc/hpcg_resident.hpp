@@ -24,6 +24,14 @@
 //           P_l = partner-half sum of (W^T r - alpha W^T q);  partial r.z;
 //           t_r = U_k^T r, W_l[k]^T r for the next iteration
 // Per iteration the factors are never reloaded.
+//
+// Coherence without cache maintenance.  Every value one workgroup writes for
+// another (z and p, the restrictions, the scalar partials, the statuses) is
+// stored and loaded with agent-scope accesses (sc1: written through to, and
+// read from, the point where all XCDs agree), so the device-wide barrier needs
+// no L2 write-back or invalidation: arriving waits until this workgroup's
+// stores are acknowledged, then bumps the counter; the last arrival publishes
+// the barrier number on a line of its own that the others poll.
 #pragma once
 #include "hpcg_kernels.hpp"
 
@@ -53,6 +61,58 @@ struct alignas(16) RSmem {
   int flag[4];
 };
 
+// Agent-scope (XCD-coherent) load and store of one value.
+template <typename T>
+__device__ __forceinline__ T ld_c(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ void st_c(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Device-wide barrier over agent-coherent data (see the header).  `epoch`
+// counts this workgroup's barriers; the flag holds the last completed one.
+__device__ __forceinline__ void cgrid_arrive(const Bufs& B, unsigned& target, unsigned& epoch) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  target += gridDim.x;
+  ++epoch;
+  if (threadIdx.x == 0) {
+    const unsigned old = __hip_atomic_fetch_add(B.barrier, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old + 1 == target) st_c(B.bflag, epoch);
+  }
+}
+
+__device__ __forceinline__ bool cgrid_wait(const Bufs& B, unsigned epoch) {
+  __shared__ int aborted_c;
+  if (threadIdx.x == 0) {
+    unsigned polls = 0;
+    int ab = 0;
+    while (ld_c(B.bflag) < epoch) {
+      __builtin_amdgcn_s_sleep(1);
+      if (((++polls) & 1023u) == 0) {
+        if (ld_c(B.abort_flag)) { ab = 1; break; }
+        if (polls > (1u << 26)) {
+          st_c(B.abort_flag, 1);
+          ab = 1;
+          break;
+        }
+      }
+    }
+    aborted_c = ab;
+  }
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  return aborted_c != 0;
+}
+
+__device__ __forceinline__ bool cgrid_barrier(const Bufs& B, unsigned& target, unsigned& epoch) {
+  cgrid_arrive(B, target, epoch);
+  return cgrid_wait(B, epoch);
+}
+
 // Sum over the workgroup in a fixed order.
 template <typename T>
 __device__ __forceinline__ double wg_sum_r(double v, RSmem<T>& sm) {
@@ -71,7 +131,7 @@ __device__ __forceinline__ double wg_sum_r(double v, RSmem<T>& sm) {
 __device__ __forceinline__ double sum_partials_r(const double* part, int s, int K) {
   double v = 0.0;
   const double* p = part + (size_t)s * K;
-  for (int j = threadIdx.x & 63; j < K; j += 64) v += p[j];
+  for (int j = threadIdx.x & 63; j < K; j += 64) v += ld_c(p + j);
   return wave_sum(v);
 }
 
@@ -157,7 +217,7 @@ __device__ __forceinline__ void r_restrict(const Geom& G, int s, int k, const Re
 #pragma unroll
       for (int w = 1; w < NWR; ++w) a += sm.redW[w][tid];
       const int l = tid / RANK, c = tid - l * RANK;
-      pout[(((size_t)s * G.levels + l) * G.K + k) * RANK + c] = a;
+      st_c(pout + (((size_t)s * G.levels + l) * G.K + k) * RANK + c, a);
       own[tid] = a;
     }
   }
@@ -174,7 +234,7 @@ __device__ __forceinline__ void r_stage_partners(const Geom& G, const T* src, in
   for (int l = 0; l < LEV; ++l) {
     const int kp0 = ((k >> l) ^ 1) << l;
     const T* from = src + (((size_t)s * G.levels + l) * G.K + kp0) * RANK;
-    dma_to_lds_n<NWR>(stage + (size_t)((1 << l) - 1) * RANK, (1 << l) * CPV,
+    dma_to_lds_n<NWR, CPOL_AGENT>(stage + (size_t)((1 << l) - 1) * RANK, (1 << l) * CPV,
                       [&](int c) { return reinterpret_cast<const char*>(from) + 16 * c; });
   }
 }
@@ -280,7 +340,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
   const int leaf0 = s * G.n + k * LEAF;
   SysState* st = B.st + s;
   const bool lead = (tid == 0 && k == 0);
-  unsigned target = 0;
+  unsigned target = 0, epoch = 0;
   // restriction buffers: W^T r in two halves of pleaf (ping-pong), W^T q in tleaf
   const size_t half = (size_t)G.B * G.levels * G.K * RANK;
   T* pR[2] = {reinterpret_cast<T*>(B.pleaf), reinterpret_cast<T*>(B.pleaf) + half};
@@ -326,7 +386,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
   r_restrict<T, LEV>(G, s, k, F, sm.r, sm.tr, pR[0], sm.ownR, sm);
   double part = wg_sum_r(loc, sm);
   if (tid == 0) {
-    B.rr_part[item] = part;
+    st_c(B.rr_part + item, part);
     if (k == 0) {
       st->relres = 1.0;
       st->brk = 0;
@@ -334,7 +394,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
       set_state(st, ST_RUNNING, 0);
     }
   }
-  if (grid_barrier(B.barrier, B.abort_flag, target)) return;
+  if (cgrid_barrier(B, target, epoch)) return;
 
   // ---- z0 = M r0 ----
   bool done = false;                   // this system has finished (decided locally)
@@ -354,14 +414,14 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
       r_prolong<T, LEV>(F, sm, stR, (const T*)nullptr, 0.0, gate);
       loc = 0.0;
       if (tid < LEAF) {
-        zg[leaf0 + tid] = sm.z[tid];
+        st_c(zg + leaf0 + tid, sm.z[tid]);
         loc = (double)sm.r[tid] * (double)sm.z[tid];
       }
       part = wg_sum_r(loc, sm);
-      if (tid == 0) B.rz_part[item] = part;
+      if (tid == 0) st_c(B.rz_part + item, part);
     }
   }
-  if (grid_barrier(B.barrier, B.abort_flag, target)) return;
+  if (cgrid_barrier(B, target, epoch)) return;
 
   // Statuses are written by each system's lead only in the second phase of an
   // iteration and read by everyone only in the first, so every workgroup sees
@@ -391,8 +451,8 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
         if (e < e1) {
           const int c = colL[e];
           vv[u] = valL[e];
-          zc[u] = zg[c];
-          if (!first) pc[u] = pold[c];
+          zc[u] = ld_c(zg + c);
+          if (!first) pc[u] = ld_c(pold + c);
         }
       }
       int running = 0;
@@ -424,7 +484,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
         for (int u = 0; u < PF; ++u) acc = fma((T)vv[u], first ? zc[u] : pdir<T>(zc[u], pc[u], beta), acc);
         for (int e = e0 + lr + 4 * PF; e < e1; e += 4) {
           const int c = colL[e];
-          const T v = first ? zg[c] : pdir<T>(zg[c], pold[c], beta);
+          const T v = first ? ld_c(zg + c) : pdir<T>(ld_c(zg + c), ld_c(pold + c), beta);
           acc = fma((T)valL[e], v, acc);
         }
         acc = group4_sum(acc);
@@ -433,16 +493,16 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
           const T pn = first ? sm.z[row] : pdir<T>(sm.z[row], sm.p[row], beta);
           sm.p[row] = pn;
           sm.q[row] = acc;
-          pnew[leaf0 + row] = pn;
+          st_c(pnew + leaf0 + row, pn);
           loc = (double)pn * (double)acc;
         }
         __syncthreads();
         r_restrict<T, LEV>(G, s, k, F, sm.q, sm.tq, pQ, sm.ownQ, sm);
         part = wg_sum_r(loc, sm);
-        if (tid == 0) B.pq_part[item] = part;
+        if (tid == 0) st_c(B.pq_part + item, part);
       }
     }
-    if (grid_barrier(B.barrier, B.abort_flag, target)) return;
+    if (cgrid_barrier(B, target, epoch)) return;
     // ---------------- phase BC (it) ----------------
     {
       if (lead && pend_status != ST_RUNNING) {
@@ -471,15 +531,15 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
             sm.t[tid] = (T)((double)sm.tr[tid] - alpha * (double)sm.tq[tid]);
           }
           part = wg_sum_r(loc, sm);
-          if (tid == 0) B.rr_part[item] = part;
+          if (tid == 0) st_c(B.rr_part + item, part);
           r_prolong<T, LEV>(F, sm, stR, stQ, alpha, gate);
           loc = 0.0;
           if (tid < LEAF) {
-            zg[leaf0 + tid] = sm.z[tid];
+            st_c(zg + leaf0 + tid, sm.z[tid]);
             loc = (double)sm.r[tid] * (double)sm.z[tid];
           }
           part = wg_sum_r(loc, sm);
-          if (tid == 0) B.rz_part[item] = part;
+          if (tid == 0) st_c(B.rz_part + item, part);
           next_alpha = alpha;
           restrict_next = true;
         }
@@ -488,7 +548,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
     // Everything the next phase A reads (z, the partials, the statuses) is
     // written: arrive now.  The restriction of the new r is read by the
     // partners only after the following barrier, so it overlaps the wait.
-    grid_arrive(B.barrier, target);
+    cgrid_arrive(B, target, epoch);
     if (restrict_next) {
       // exact every kRefresh iterations, else by the same linear update the
       // partners used above (its rounding drift is bounded by the refreshes)
@@ -502,12 +562,12 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
           const T v = (T)((double)sm.ownR[tid] - next_alpha * (double)sm.ownQ[tid]);
           sm.ownR[tid] = v;
           const int l = tid / RANK, c = tid - l * RANK;
-          pR[rbuf][(((size_t)s * G.levels + l) * G.K + k) * RANK + c] = v;
+          st_c(pR[rbuf] + (((size_t)s * G.levels + l) * G.K + k) * RANK + c, v);
         }
         __syncthreads();
       }
     }
-    if (grid_wait(B.barrier, B.abort_flag, target)) return;
+    if (cgrid_wait(B, epoch)) return;
   }
   // ---- the solution of the leaf's rows ----
   if (tid < LEAF) B.x[leaf0 + tid] = x;
