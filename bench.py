@@ -54,12 +54,17 @@ def spmv_bytes(n: int, nnz: int, B: int = 1) -> int:
     return 8 * nnz + 4 * (B * n + 1) + 8 * B * n
 
 
+# sources of the single-vector apply and SpMV kernels and of their launch code
+APPLY_SPMV_SOURCES = ("hpcg_device.hpp", "hpcg_kernels.hpp", "hpcg.hip")
+
+
 def kernel_source_digest() -> str:
-    """Digest of the HIP sources, so that recorded counters go stale with them."""
+    """Digest of the apply / SpMV kernel sources, so that recorded counters go
+    stale as soon as those kernels or their launch code change."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "matrix_preconditioned_pcg_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in APPLY_SPMV_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]

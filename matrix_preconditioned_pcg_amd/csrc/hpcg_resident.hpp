@@ -496,10 +496,11 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
           st_c(pnew + leaf0 + row, pn);
           loc = (double)pn * (double)acc;
         }
-        __syncthreads();
-        r_restrict<T, LEV>(G, s, k, F, sm.q, sm.tq, pQ, sm.ownQ, sm);
+        // the partial p.q goes out first, so that its store is acknowledged
+        // while the restriction of q runs
         part = wg_sum_r(loc, sm);
         if (tid == 0) st_c(B.pq_part + item, part);
+        r_restrict<T, LEV>(G, s, k, F, sm.q, sm.tq, pQ, sm.ownQ, sm);
       }
     }
     if (cgrid_barrier(B, target, epoch)) return;
