@@ -175,6 +175,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-others", action="store_true", help="skip ms/solve of the other workloads")
     ap.add_argument("--no-block", action="store_true", help="skip the block (probe) apply timing")
+    ap.add_argument("--no-fused", action="store_true", help="skip the single-launch (cooperative) apply timing")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run three 256 MiB device-to-device copies (calibrates HBM byte counters)")
     args = ap.parse_args(argv)
@@ -212,12 +213,23 @@ def main(argv=None):
             apply()
         ab = apply_bytes(batch.n, batch.K, batch.levels, batch.batch)
         sb = spmv_bytes(batch.n, batch.nnz, batch.batch)
+        fused_us = None
+        if not args.no_fused and batch.batch * batch.K <= 256:
+            # the single-launch apply (reads every factor byte once) for comparison
+            solver.set_option(hpcg.HPCG_OPT_APPLY_PATH, hpcg.HPCG_APPLY_FUSED)
+            with torch.cuda.stream(stream):
+                fused_us = time_graph(apply, args.reps, stream, torch)
+            solver.set_option(hpcg.HPCG_OPT_APPLY_PATH, hpcg.HPCG_APPLY_AUTO)
         with torch.cuda.stream(stream):
+            apply()
+            torch.cuda.synchronize()
+            path = {hpcg.HPCG_APPLY_FUSED: "fused", hpcg.HPCG_APPLY_STREAMING: "streaming"}.get(
+                hpcg.hpcg_last_apply_path(solver.handle), "?")
             out = {"apply_us": time_graph(apply, args.reps, stream, torch),
                    "spmv_us": time_graph(spmv, args.reps, stream, torch),
                    "pair_us": time_graph(pair, args.reps, stream, torch)}
             out["apply_us_eager"], _ = time_calls(apply, args.reps, stream, torch)
-        out.update(apply_bytes=ab, spmv_bytes=sb,
+        out.update(apply_path=path, apply_fused_us=fused_us, apply_bytes=ab, spmv_bytes=sb,
                    apply_gbs=ab / out["apply_us"] / 1e3, spmv_gbs=sb / out["spmv_us"] / 1e3,
                    pair_gbs=(ab + sb) / out["pair_us"] / 1e3)
         out["pair_frac"] = out["pair_gbs"] / HBM_PEAK_GBS
@@ -290,6 +302,7 @@ def main(argv=None):
                             if len(o["iterations"]) <= 4 else
                             {"min": min(o["iterations"]), "max": max(o["iterations"])},
                             "engine": o["engine"],
+                            "apply_path": o["apply_path"],
                             "apply_us": round(o["apply_us"], 3), "spmv_us": round(o["spmv_us"], 3),
                             "apply_spmv_us": round(o["pair_us"], 3),
                             "apply_spmv_gbs": round(o["pair_gbs"], 1),
@@ -335,6 +348,7 @@ def main(argv=None):
         "spmv_us": round(main_out["spmv_us"], 3),
         "apply_spmv_us": round(main_out["pair_us"], 3),
         "apply_us_eager": round(main_out["apply_us_eager"], 3),
+        "apply_fused_us": None if main_out["apply_fused_us"] is None else round(main_out["apply_fused_us"], 3),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),
@@ -342,8 +356,9 @@ def main(argv=None):
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_record(args.config),
-            "kernel": "M-apply (k_apply_restrict + k_apply_prolong) + CSR SpMV (k_spmv), one pair per "
-                      "launch group, graph-replayed back to back on the library stream",
+            "kernel": ("M-apply (k_apply_fused: one cooperative launch)" if main_out["apply_path"] == "fused"
+                       else "M-apply (k_apply_restrict + k_apply_prolong)")
+                      + " + CSR SpMV (k_spmv), pairs graph-replayed back to back on the library stream",
             "algorithmic_bytes": ab + sb,
             "apply_gbs": round(main_out["apply_gbs"], 1),
             "spmv_gbs": round(main_out["spmv_gbs"], 1),

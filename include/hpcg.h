@@ -112,12 +112,28 @@ typedef enum {
     HPCG_OPT_ENGINE = 1,        /* an hpcg_engine value                          */
     HPCG_OPT_GRAPH_UNROLL = 2,  /* iterations per graph replay, 1 .. 64 (default 8) */
     HPCG_OPT_PRECISION = 4,     /* an hpcg_precision value                        */
+    HPCG_OPT_APPLY_PATH = 16,   /* an hpcg_apply_path value                       */
     HPCG_OPT_LEAF_SPLIT = 8     /* workgroups per leaf in the apply kernels and the
                                    graph and streaming engines: 0 = automatic
                                    (default), else 1, 2, 4 or 8; a split whose LDS
                                    need exceeds a compute unit is raised to the
                                    next that fits                                 */
 } hpcg_option;
+
+/* How hpcg_apply_M runs (hpcg_set_option(HPCG_OPT_APPLY_PATH, ...)).
+ * STREAMING: two launches (restriction, then prolongation), any batch size;
+ * the prolongation reads the level slabs a second time.  FUSED: one
+ * cooperative launch in which the workgroup of each leaf keeps U_k and its
+ * slabs in registers from the restriction to the prolongation, across one
+ * device-wide barrier, so every factor byte is read once; needs one compute
+ * unit per leaf of the batch (HPCG_ERR_SHAPE otherwise).  A cooperative launch
+ * costs far more than it saves for a single apply on this hardware (about 25 us
+ * against 10 us at n = 8192), so AUTO (default) means STREAMING. */
+typedef enum {
+    HPCG_APPLY_AUTO = 0,
+    HPCG_APPLY_STREAMING = 1,
+    HPCG_APPLY_FUSED = 2
+} hpcg_apply_path;
 
 /* Arithmetic of the solve's vectors (hpcg_set_option(HPCG_OPT_PRECISION, ...)).
  * Factors and matrix values are fp32 and scalars and x are fp64 in both modes. */
@@ -222,6 +238,9 @@ hpcg_status hpcg_last_solve_status(hpcg_handle h, int32_t* h_status);
 
 /* Engine and tuning options (see hpcg_option). */
 hpcg_status hpcg_set_option(hpcg_handle h, int32_t option, int32_t value);
+
+/* Path the last hpcg_apply_M call took (an hpcg_apply_path; 0 before any). */
+int32_t hpcg_last_apply_path(hpcg_handle h);
 
 /* Engine the last hpcg_solve actually ran (an hpcg_engine value), or 0. */
 int32_t hpcg_last_engine(hpcg_handle h);

@@ -34,7 +34,7 @@ constexpr size_t kMaxLds = 160 * 1024;
 
 // control words, each on its own 256-byte line
 constexpr size_t kCtlBarrier = 0, kCtlAbort = 256, kCtlItbase = 512, kCtlReplays = 768, kCtlFlag = 1024,
-                 kCtlBytes = 1280;
+                 kCtlApplyCtr = 1280, kCtlApplyGen = 1536, kCtlBytes = 1792;
 
 constexpr int kMaxSplit = 8;   // workgroups per leaf in the streaming kernels
 
@@ -136,6 +136,9 @@ struct hpcg_ctx {
   int graph_prec = -1;
   int graph_bpl = 0;
   int split = 0;
+  int apply_path = HPCG_APPLY_AUTO;
+  int last_apply_path = 0;
+  int fused_per_cu = -1;
   double graph_tol = -1.0;
   int graph_maxit = -1;
   int last_grid = 0;
@@ -298,7 +301,7 @@ const void* resident_kernel(int levels) {
   }
 }
 
-// Register-resident persistent solve: one 1024-thread workgroup per leaf, all
+// Register-resident persistent solve: one 512-thread workgroup per leaf, all
 // co-resident (one per CU).  Declines (ran = false) when the batch has more
 // leaves than the device has CUs.
 template <typename T>
@@ -448,10 +451,13 @@ hpcg_status hpcg_create(const hpcg_partition* part, const int32_t* d_row_ptr, co
   B.itbase = reinterpret_cast<int*>(w + lay.ctl + kCtlItbase);
   B.replays = reinterpret_cast<int*>(w + lay.ctl + kCtlReplays);
   B.bflag = reinterpret_cast<unsigned*>(w + lay.ctl + kCtlFlag);
+  B.actr = reinterpret_cast<unsigned*>(w + lay.ctl + kCtlApplyCtr);
+  B.agen = reinterpret_cast<unsigned*>(w + lay.ctl + kCtlApplyGen);
   B.tol = 1e-6;
   B.maxit = 1000;
 
   const size_t N = (size_t)G.B * G.n;
+  CREATE_HIP(hipMemsetAsync(w + lay.ctl, 0, kCtlBytes, h->stream));
   CREATE_HIP(hipMemcpyAsync(w + lay.row_ptr, d_row_ptr, (N + 1) * 4, hipMemcpyDeviceToDevice, h->stream));
   if (nnz_total > 0) {
     CREATE_HIP(hipMemcpyAsync(w + lay.col, d_col, (size_t)nnz_total * 4, hipMemcpyDeviceToDevice, h->stream));
@@ -501,11 +507,63 @@ hpcg_status hpcg_set_factors(hpcg_handle h, const float* d_leafU, const float* d
   return HPCG_OK;
 }
 
+const void* fused_apply_kernel(int levels) {
+  switch (levels) {
+    case 0: return reinterpret_cast<const void*>(&k_apply_fused<0>);
+    case 1: return reinterpret_cast<const void*>(&k_apply_fused<1>);
+    case 2: return reinterpret_cast<const void*>(&k_apply_fused<2>);
+    case 3: return reinterpret_cast<const void*>(&k_apply_fused<3>);
+    case 4: return reinterpret_cast<const void*>(&k_apply_fused<4>);
+    case 5: return reinterpret_cast<const void*>(&k_apply_fused<5>);
+    case 6: return reinterpret_cast<const void*>(&k_apply_fused<6>);
+    case 7: return reinterpret_cast<const void*>(&k_apply_fused<7>);
+    case 8: return reinterpret_cast<const void*>(&k_apply_fused<8>);
+    default: return nullptr;
+  }
+}
+
+// Single cooperative launch of the apply when every leaf gets its own CU;
+// ran = false when it does not fit (the caller then uses the two launches).
+hpcg_status run_fused_apply(hpcg_ctx* h, const float* d_r, float* d_y, bool& ran) {
+  ran = false;
+  const Geom G = h->G;
+  const int items = G.B * G.K;
+  if (!h->coop || items > h->num_cu) return HPCG_OK;
+  const void* fn = fused_apply_kernel(G.levels);
+  if (!fn) return HPCG_OK;
+  const size_t dyn = (size_t)std::max(G.K - 1, 1) * RANK * sizeof(float);
+  if (dyn + sizeof(RSmem<float>) > kMaxLds) return HPCG_OK;
+  hpcg_status s = allow_lds(h, fn, dyn);
+  if (s != HPCG_OK) return s;
+  if (h->fused_per_cu < 0)
+    HIP_OR_FAIL(h, hipOccupancyMaxActiveBlocksPerMultiprocessor(&h->fused_per_cu, fn, NTR, dyn));
+  if ((int64_t)h->fused_per_cu * h->num_cu < items) return HPCG_OK;
+  Geom Ga = G;
+  Bufs Ba = h->B;
+  const float* ra = d_r;
+  float* ya = d_y;
+  void* args[] = {&Ga, &Ba, &ra, &ya};
+  HIP_OR_FAIL(h, hipLaunchCooperativeKernel(fn, dim3(items), dim3(NTR), args, (unsigned)dyn, h->stream));
+  ran = true;
+  return HPCG_OK;
+}
+
 hpcg_status hpcg_apply_M(hpcg_handle h, const float* d_r, float* d_y) {
   if (!h) return fail(nullptr, HPCG_ERR_INVALID_ARG, "handle is NULL");
   if (!d_r || !d_y) return fail(h, HPCG_ERR_INVALID_ARG, "vector pointer is NULL");
   if (d_r == d_y) return fail(h, HPCG_ERR_INVALID_ARG, "d_r and d_y must not alias");
   if (!h->factors_set) return fail(h, HPCG_ERR_STATE, "hpcg_set_factors has not been called");
+  if (h->apply_path == HPCG_APPLY_FUSED) {
+    bool ran = false;
+    hpcg_status s = run_fused_apply(h, d_r, d_y, ran);
+    if (s != HPCG_OK) return s;
+    if (ran) {
+      h->last_apply_path = HPCG_APPLY_FUSED;
+      return HPCG_OK;
+    }
+    return fail(h, HPCG_ERR_SHAPE, "fused apply: the batch has more leaves than co-resident workgroups");
+  }
+  h->last_apply_path = HPCG_APPLY_STREAMING;
   const Geom& G = h->G;
   const size_t lds_r = restrict_lds_bytes(G), lds_p = prolong_lds_bytes<float>(G);
   hpcg_status s = allow_lds(h, reinterpret_cast<const void*>(&k_apply_restrict), lds_r);
@@ -695,6 +753,10 @@ hpcg_status hpcg_set_option(hpcg_handle h, int32_t option, int32_t value) {
       if (value != HPCG_PREC_VEC64 && value != HPCG_PREC_VEC32) return fail(h, HPCG_ERR_INVALID_ARG, "bad precision");
       h->prec = value;
       return HPCG_OK;
+    case HPCG_OPT_APPLY_PATH:
+      if (value < HPCG_APPLY_AUTO || value > HPCG_APPLY_FUSED) return fail(h, HPCG_ERR_INVALID_ARG, "bad apply path");
+      h->apply_path = value;
+      return HPCG_OK;
     case HPCG_OPT_LEAF_SPLIT: {
       if (value != 0 && value != 1 && value != 2 && value != 4 && value != 8)
         return fail(h, HPCG_ERR_INVALID_ARG, "leaf split must be 0 (automatic), 1, 2, 4 or 8");
@@ -711,6 +773,8 @@ hpcg_status hpcg_set_option(hpcg_handle h, int32_t option, int32_t value) {
 }
 
 int32_t hpcg_last_engine(hpcg_handle h) { return h ? h->last_engine : 0; }
+
+int32_t hpcg_last_apply_path(hpcg_handle h) { return h ? h->last_apply_path : 0; }
 
 hpcg_status hpcg_last_launch_info(hpcg_handle h, int32_t* grid, int32_t* lds_bytes) {
   if (!h) return fail(nullptr, HPCG_ERR_INVALID_ARG, "handle is NULL");

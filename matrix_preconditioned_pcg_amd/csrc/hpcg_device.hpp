@@ -102,6 +102,8 @@ struct Bufs {
   SysState* st;        // [B]
   unsigned* barrier;   // device-wide barrier arrival counter
   unsigned* bflag;     // resident engine: number of the last completed barrier
+  unsigned* actr;      // fused apply: arrivals at its barrier (returns to 0 after each)
+  unsigned* agen;      // fused apply: barrier generation
   int* abort_flag;     // set when a barrier wait exceeds its bound
   int* itbase;         // graph engine: absolute iteration of the replay's first step
   int* replays;        // graph engine: replays finished

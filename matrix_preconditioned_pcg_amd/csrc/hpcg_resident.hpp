@@ -324,6 +324,76 @@ __device__ __forceinline__ void r_prolong(const Resident<T, LEV>& F, RSmem<T>& s
   __syncthreads();
 }
 
+// U_k and the leaf's level slabs into the register layout of Resident.
+template <typename T, int LEV>
+__device__ __forceinline__ void load_factors(const Geom& G, const Bufs& B, int s, int k, Resident<T, LEV>& F) {
+  const int tid = threadIdx.x;
+  const int cs = tid & 31, rg = tid >> 5;
+  const float* Uk = B.U + ((size_t)s * G.K + k) * LEAF * LEAF;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) F.u[m] = *reinterpret_cast<const float4*>(Uk + (rg + 16 * m) * LEAF + 4 * cs);
+  if constexpr (LEV > 0) {
+    const int c8 = tid & 7, row = tid >> 3;
+#pragma unroll
+    for (int l = 0; l < LEV; ++l) {
+      const float* Wl = B.W + (((size_t)s * G.levels + l) * G.K + k) * LEAF * RANK;
+      F.w[l][0] = *reinterpret_cast<const float4*>(Wl + row * RANK + 4 * c8);
+      F.w[l][1] = *reinterpret_cast<const float4*>(Wl + (row + 64) * RANK + 4 * c8);
+    }
+  }
+}
+
+// Single-launch apply y = M r (fp32 in and out) for batches whose leaves all
+// get a compute unit: the workgroup of leaf k loads U_k and its slabs into
+// registers once, restricts (eq. (2)), meets the others at one device-wide
+// barrier, and prolongs (eqs. (3)-(5)) and adds the diagonal stage and the gate
+// with the same registers, so every factor byte crosses HBM once per apply.
+// The barrier is self-resetting (the arrival counter wraps to zero, the last
+// arrival advances a generation word), so the launch can be replayed from a
+// captured graph.
+template <int LEV>
+__global__ __launch_bounds__(NTR) void k_apply_fused(Geom G, Bufs B, const float* __restrict__ rin,
+                                                     float* __restrict__ yout) {
+  __shared__ RSmem<float> sm;
+  extern __shared__ int4 fdyn4[];
+  float* stR = reinterpret_cast<float*>(fdyn4);
+  const int tid = threadIdx.x;
+  const int item = blockIdx.x;
+  const int s = item / G.K, k = item - s * G.K;
+  const int leaf0 = s * G.n + k * LEAF;
+  __shared__ unsigned gen0;
+  if (tid == 0) gen0 = ld_c(B.agen);
+  Resident<float, LEV> F;
+  load_factors(G, B, s, k, F);
+  const float gate = (tid < LEAF) ? B.g[leaf0 + tid] : 0.f;
+  if (tid < LEAF) sm.r[tid] = rin[leaf0 + tid];
+  __syncthreads();
+  float* pR = reinterpret_cast<float*>(B.pleaf);
+  r_restrict<float, LEV>(G, s, k, F, sm.r, sm.t, pR, sm.ownR, sm);
+  // device-wide barrier
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned old = __builtin_amdgcn_atomic_inc32(B.actr, gridDim.x - 1, __ATOMIC_RELAXED, "agent");
+    if (old == gridDim.x - 1) st_c(B.agen, gen0 + 1);
+    unsigned polls = 0;
+    while (ld_c(B.agen) == gen0) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++polls > (1u << 26)) {
+        st_c(B.abort_flag, 1);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  if constexpr (LEV > 0) r_stage_partners<float, LEV>(G, pR, s, k, stR);
+  lds_dma_wait();
+  r_prolong<float, LEV>(F, sm, stR, (const float*)nullptr, 0.0, gate);
+  if (tid < LEAF) yout[leaf0 + tid] = sm.z[tid];
+}
+
 template <typename T, int LEV>
 __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_nnz) {
   __shared__ RSmem<T> sm;
@@ -349,21 +419,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
 
   // ---- factors into registers, CSR rows into LDS ----
   Resident<T, LEV> F;
-  {
-    const int cs = tid & 31, rg = tid >> 5;
-    const float* Uk = B.U + ((size_t)s * G.K + k) * LEAF * LEAF;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) F.u[m] = *reinterpret_cast<const float4*>(Uk + (rg + 16 * m) * LEAF + 4 * cs);
-    if constexpr (LEV > 0) {
-      const int c8 = tid & 7, row = tid >> 3;
-#pragma unroll
-      for (int l = 0; l < LEV; ++l) {
-        const float* Wl = B.W + (((size_t)s * G.levels + l) * G.K + k) * LEAF * RANK;
-        F.w[l][0] = *reinterpret_cast<const float4*>(Wl + row * RANK + 4 * c8);
-        F.w[l][1] = *reinterpret_cast<const float4*>(Wl + (row + 64) * RANK + 4 * c8);
-      }
-    }
-  }
+  load_factors(G, B, s, k, F);
   const int e_begin = B.row_ptr[leaf0];
   if (tid <= LEAF) rpL[tid] = B.row_ptr[leaf0 + tid] - e_begin;
   const int leaf_nnz = B.row_ptr[leaf0 + LEAF] - e_begin;

@@ -43,6 +43,11 @@ HPCG_OPT_ENGINE = 1
 HPCG_OPT_GRAPH_UNROLL = 2
 HPCG_OPT_PRECISION = 4
 HPCG_OPT_LEAF_SPLIT = 8
+HPCG_OPT_APPLY_PATH = 16
+
+HPCG_APPLY_AUTO = 0
+HPCG_APPLY_STREAMING = 1
+HPCG_APPLY_FUSED = 2
 
 HPCG_PREC_VEC64 = 0
 HPCG_PREC_VEC32 = 1
@@ -93,6 +98,7 @@ def lib() -> ctypes.CDLL:
         "hpcg_last_solve_status": (i32, [vp, P(i32)]),
         "hpcg_set_option": (i32, [vp, i32, i32]),
         "hpcg_last_engine": (i32, [vp]),
+        "hpcg_last_apply_path": (i32, [vp]),
         "hpcg_last_launch_info": (i32, [vp, P(i32), P(i32)]),
         "hpcg_status_string": (ctypes.c_char_p, [i32]),
         "hpcg_last_error": (ctypes.c_char_p, [vp]),
@@ -246,6 +252,10 @@ def hpcg_set_option(h, option: int, value: int):
 
 def hpcg_last_engine(h) -> int:
     return int(lib().hpcg_last_engine(h))
+
+
+def hpcg_last_apply_path(h) -> int:
+    return int(lib().hpcg_last_apply_path(h))
 
 
 def hpcg_last_launch_info(h) -> tuple:

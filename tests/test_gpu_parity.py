@@ -154,6 +154,75 @@ def test_apply_parity(cfg, name):
     s.close()
 
 
+@pytest.mark.parametrize("path", [hpcg.HPCG_APPLY_STREAMING, hpcg.HPCG_APPLY_FUSED])
+@pytest.mark.parametrize("name", ["N1k", "N8k", "N16k", "tet4k"])
+def test_apply_paths(cfg, name, path):
+    # the two-launch and the single cooperative launch apply give the same M r
+    batch = cfg(name)
+    _log(f"apply path {path} {name}")
+    s = _solver(batch)
+    s.set_option(hpcg.HPCG_OPT_APPLY_PATH, path)
+    r = np.random.default_rng(14).standard_normal((batch.batch, batch.n)).astype(np.float32)
+    _check_apply(batch, s, r)
+    assert hpcg.hpcg_last_apply_path(s.handle) == path
+    _check_apply(batch, s, (0.25 * r[:, ::-1]).copy())
+    s.close()
+
+
+def test_apply_auto_path_and_fused_refusal(cfg):
+    big = cfg("batch64x2k")        # 1024 leaves: more than one compute unit each
+    s = _solver(big)
+    r = np.random.default_rng(15).standard_normal((big.batch, big.n)).astype(np.float32)
+    _check_apply(big, s, r)
+    assert hpcg.hpcg_last_apply_path(s.handle) == hpcg.HPCG_APPLY_STREAMING
+    s.set_option(hpcg.HPCG_OPT_APPLY_PATH, hpcg.HPCG_APPLY_FUSED)
+    with pytest.raises(hpcg.HPCGError):
+        s.apply_M(r.reshape(-1))
+    s.close()
+    small = cfg("N8k")
+    s = _solver(small)
+    s.apply_M(np.ones(small.n, np.float32))
+    assert hpcg.hpcg_last_apply_path(s.handle) == hpcg.HPCG_APPLY_STREAMING
+    s.close()
+
+
+def test_fused_apply_graph_replays(cfg):
+    # the fused apply's barrier resets itself: captured calls replay correctly,
+    # with eager work and synchronizations between the replays
+    batch = cfg("N8k")
+    _log("fused apply graph replays")
+    stream = torch.cuda.Stream()
+    s = hpcg.Solver(batch.n, batch.row_ptr, batch.col, batch.val, batch=batch.batch, levels=batch.levels,
+                    stream=stream)
+    s.set_factors(batch.U, batch.W, batch.g)
+    s.set_option(hpcg.HPCG_OPT_APPLY_PATH, hpcg.HPCG_APPLY_FUSED)
+    rng = np.random.default_rng(16)
+    rs = [torch.as_tensor(rng.standard_normal(batch.n).astype(np.float32)).cuda() for _ in range(3)]
+    ys = [torch.empty_like(rs[0]) for _ in range(3)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for r, y in zip(rs, ys):
+            hpcg.hpcg_apply_M(s.handle, s.part, r, y)
+    torch.cuda.synchronize()
+    ref = [y.clone() for y in ys]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for r, y in zip(rs, ys):
+            hpcg.hpcg_apply_M(s.handle, s.part, r, y)
+    for rep in range(4):
+        for y in ys:
+            y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for y, y0 in zip(ys, ref):
+            assert torch.equal(y, y0), rep
+        s.apply_M(rs[0].cpu().numpy())      # eager call between replays
+        torch.cuda.synchronize()
+    assert hpcg.hpcg_last_apply_path(s.handle) == hpcg.HPCG_APPLY_FUSED
+    s.close()
+
+
 @pytest.mark.parametrize("split", [1, 2, 4, 8])
 @pytest.mark.parametrize("name", ["N8k", "batch64x2k"])
 def test_apply_parity_leaf_split(cfg, name, split):
@@ -161,6 +230,7 @@ def test_apply_parity_leaf_split(cfg, name, split):
     batch = cfg(name)
     _log(f"apply parity {name} split={split}")
     s = _solver(batch)
+    s.set_option(hpcg.HPCG_OPT_APPLY_PATH, hpcg.HPCG_APPLY_STREAMING)
     s.set_option(hpcg.HPCG_OPT_LEAF_SPLIT, split)
     r = np.random.default_rng(13).standard_normal((batch.batch, batch.n)).astype(np.float32)
     _check_apply(batch, s, r)
