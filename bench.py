@@ -314,6 +314,24 @@ def main(argv=None):
             log(f"bench: variant {label}")
             _b, o = run_config(args.config, max(3, args.steps // 2), 1, False, eng, prec)
             variants[label] = {"ms_per_solve": round(o["ms_per_solve"], 4), "iterations": o["iterations"][0]}
+    bridge = None
+    if not args.no_variants:
+        # the pages' own factor format: bridges + cores, expanded on the device
+        from workloads.generate import bridge_factors_for
+        log("bench: bridge-format factors")
+        bb = make_config(args.config)
+        Ub, Vb, Bc = bridge_factors_for(bb)
+        solver = hpcg.Solver(bb.n, bb.row_ptr, bb.col, bb.val, batch=bb.batch, levels=bb.levels, stream=stream)
+        dev = [torch.as_tensor(a).cuda() for a in (bb.U, Ub, Vb, Bc, bb.g)]
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            t_exp = time_graph(lambda: hpcg.hpcg_set_factors_bridge(solver.handle, solver.part, *dev), 20,
+                               stream, torch)
+        bvec = torch.as_tensor(bb.b.reshape(-1)).cuda()
+        ms, its, _res = time_solves(solver, bvec, bb.tol, bb.maxit, max(3, args.steps // 2), 1, torch)
+        bridge = {"expand_us": round(t_exp, 3), "ms_per_solve": round(ms, 4), "iterations": its[0],
+                  "factor_bytes": int(sum(a.numel() * 4 for a in dev))}
+        solver.close()
     block = []
     if not args.no_block:
         for name in ("N8k", "N16k"):
@@ -367,6 +385,7 @@ def main(argv=None):
         "by_config": others,
         "variants_at_workload": variants,
         "block_apply": block,
+        "bridge_format": bridge,
     }
     print(json.dumps(line), flush=True)
     return 0

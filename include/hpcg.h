@@ -181,6 +181,24 @@ hpcg_status hpcg_set_values(hpcg_handle h, const float* d_val);
 hpcg_status hpcg_set_factors(hpcg_handle h, const float* d_leafU, const float* d_tileW,
                              const float* d_gate);
 
+/* Load the preconditioner in the pages' own off-diagonal format: per-leaf
+ * bridges U~_k, V~_k of L x R and one R x R core B_m per tile ("Hierarchical
+ * Transformer Preconditioning for Interactive Physics Simulation", section 4.4
+ * decoder heads and section 5 eqs. (2)-(5); packed width of Supplementary
+ * Table 3).  Tile m of level l contributes U~_R B_m V~_C^T and its mirror.
+ *  d_leafF    float32 [batch][K][L][L]   F_k (block F_k F_k^T), as d_leafU above
+ *  d_bridgeU  float32 [batch][K][L][R]   U~_k
+ *  d_bridgeV  float32 [batch][K][L][R]   V~_k
+ *  d_cores    float32 [batch][M_H][R][R] B_m, M_H = sum over levels l of K/2^(l+1),
+ *             tiles in level order, j ascending within a level
+ *  d_gate     float32 [batch][n]
+ * (the three off-diagonal pointers may be NULL when levels == 0).  The library
+ * expands the format on the device into its per-level slabs (W_l[k] = U~_k B_m
+ * for the row half of a tile, V~_k for the column half; fp32 products), after
+ * which every call behaves as with hpcg_set_factors.  Stream-ordered. */
+hpcg_status hpcg_set_factors_bridge(hpcg_handle h, const float* d_leafF, const float* d_bridgeU,
+                                    const float* d_bridgeV, const float* d_cores, const float* d_gate);
+
 /* y = M r for every system of the batch (asynchronous, stream-ordered).
  * d_r, d_y float32 [batch*n], must not alias. */
 hpcg_status hpcg_apply_M(hpcg_handle h, const float* d_r, float* d_y);

@@ -548,6 +548,24 @@ hpcg_status run_fused_apply(hpcg_ctx* h, const float* d_r, float* d_y, bool& ran
   return HPCG_OK;
 }
 
+hpcg_status hpcg_set_factors_bridge(hpcg_handle h, const float* d_leafF, const float* d_bridgeU,
+                                    const float* d_bridgeV, const float* d_cores, const float* d_gate) {
+  if (!h) return fail(nullptr, HPCG_ERR_INVALID_ARG, "handle is NULL");
+  const Geom& G = h->G;
+  if (!d_leafF || !d_gate || (G.levels > 0 && (!d_bridgeU || !d_bridgeV || !d_cores)))
+    return fail(h, HPCG_ERR_INVALID_ARG, "factor pointer is NULL");
+  HIP_OR_FAIL(h, hipMemcpyAsync(h->ws + h->lay.U, d_leafF, (size_t)G.B * G.K * LEAF * LEAF * 4,
+                                hipMemcpyDeviceToDevice, h->stream));
+  if (G.levels > 0)
+    hipLaunchKernelGGL(k_expand_bridge, dim3(G.B * G.levels * G.K), dim3(NT), 0, h->stream, G, d_bridgeU, d_bridgeV,
+                       d_cores, reinterpret_cast<float*>(h->ws + h->lay.W));
+  HIP_OR_FAIL(h, hipMemcpyAsync(h->ws + h->lay.g, d_gate, (size_t)G.B * G.n * 4, hipMemcpyDeviceToDevice, h->stream));
+  hpcg_status s = check_launch(h, "bridge expansion launch");
+  if (s != HPCG_OK) return s;
+  h->factors_set = true;
+  return HPCG_OK;
+}
+
 hpcg_status hpcg_apply_M(hpcg_handle h, const float* d_r, float* d_y) {
   if (!h) return fail(nullptr, HPCG_ERR_INVALID_ARG, "handle is NULL");
   if (!d_r || !d_y) return fail(h, HPCG_ERR_INVALID_ARG, "vector pointer is NULL");

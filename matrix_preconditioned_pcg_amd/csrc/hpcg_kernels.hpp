@@ -213,6 +213,42 @@ __global__ __launch_bounds__(NT) void k_spmv(const int* __restrict__ row_ptr, co
   if (row < nrows && lr == 0) y[row] = acc;
 }
 
+// Bridge format -> per-level slabs: for tile m of level l, a row-half leaf k
+// gets W_l[k] = U~_k B_m and a column-half leaf gets W_l[k] = V~_k, which gives
+// the same M with the identity core ("Hierarchical Transformer Preconditioning
+// for Interactive Physics Simulation", section 5, eqs. (2)-(5): the row strip
+// is prolonged through U~ B, the column strip restricted through V~).  One
+// workgroup per (system, level, leaf); fp32 products.
+__global__ __launch_bounds__(NT) void k_expand_bridge(Geom G, const float* __restrict__ Ub,
+                                                      const float* __restrict__ Vb, const float* __restrict__ Bc,
+                                                      float* __restrict__ W) {
+  __shared__ float Bs[RANK * RANK];
+  const int b = blockIdx.x;
+  const int k = b % G.K, l = (b / G.K) % G.levels, s = b / (G.K * G.levels);
+  const size_t slab = (size_t)LEAF * RANK;
+  float* out = W + (((size_t)s * G.levels + l) * G.K + k) * slab;
+  const size_t leaf_off = ((size_t)s * G.K + k) * slab;
+  if (((k >> l) & 1) != 0) {                     // column half: V~_k
+    for (int e = threadIdx.x; e < LEAF * RANK; e += NT) out[e] = Vb[leaf_off + e];
+    return;
+  }
+  int m = 0;                                     // tile index: level-major, j ascending
+  for (int ll = 0; ll < l; ++ll) m += G.K >> (ll + 1);
+  m += k >> (l + 1);
+  const int cores = [&] { int c = 0; for (int ll = 0; ll < G.levels; ++ll) c += G.K >> (ll + 1); return c; }();
+  const float* B = Bc + ((size_t)s * cores + m) * RANK * RANK;
+  for (int e = threadIdx.x; e < RANK * RANK; e += NT) Bs[e] = B[e];
+  __syncthreads();
+  const float* Uk = Ub + leaf_off;
+  for (int e = threadIdx.x; e < LEAF * RANK; e += NT) {
+    const int i = e / RANK, c = e - i * RANK;
+    float a = 0.f;
+#pragma unroll 8
+    for (int t = 0; t < RANK; ++t) a = fmaf(Uk[i * RANK + t], Bs[t * RANK + c], a);
+    out[e] = a;
+  }
+}
+
 __global__ void k_copy_x(const double* __restrict__ src, double* __restrict__ dst, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) dst[i] = src[i];

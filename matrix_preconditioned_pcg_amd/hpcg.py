@@ -89,6 +89,7 @@ def lib() -> ctypes.CDLL:
         "hpcg_create": (i32, [P(hpcg_partition), vp, vp, vp, i64, vp, sz, vp, P(vp)]),
         "hpcg_set_values": (i32, [vp, vp]),
         "hpcg_set_factors": (i32, [vp, vp, vp, vp]),
+        "hpcg_set_factors_bridge": (i32, [vp, vp, vp, vp, vp, vp]),
         "hpcg_apply_M": (i32, [vp, vp, vp]),
         "hpcg_spmv": (i32, [vp, vp, vp]),
         "hpcg_block_workspace_bytes": (sz, [vp, i32]),
@@ -195,6 +196,18 @@ def hpcg_set_factors(h, part: hpcg_partition, U, W, g):
     wp = _ptr(W, torch.float32, part.batch * part.levels * K * LEAF * RANK, "W", allow_none=part.levels == 0)
     gp = _ptr(g, torch.float32, part.batch * part.n, "g")
     _check(lib().hpcg_set_factors(h, up, wp, gp), h)
+
+
+def hpcg_set_factors_bridge(h, part: hpcg_partition, F, Ub, Vb, Bc, g):
+    K = part.n // LEAF
+    cores = sum(K >> (l + 1) for l in range(part.levels))
+    none_ok = part.levels == 0
+    fp = _ptr(F, torch.float32, part.batch * K * LEAF * LEAF, "F")
+    up = _ptr(Ub, torch.float32, part.batch * K * LEAF * RANK, "Ub", allow_none=none_ok)
+    vq = _ptr(Vb, torch.float32, part.batch * K * LEAF * RANK, "Vb", allow_none=none_ok)
+    bp = _ptr(Bc, torch.float32, part.batch * cores * RANK * RANK, "Bc", allow_none=none_ok)
+    gp = _ptr(g, torch.float32, part.batch * part.n, "g")
+    _check(lib().hpcg_set_factors_bridge(h, fp, up, vq, bp, gp), h)
 
 
 def hpcg_apply_M(h, part: hpcg_partition, r, y):
@@ -331,6 +344,13 @@ class Solver:
             None if a is None else torch.as_tensor(a, dtype=torch.float32).to(self.device).contiguous()
             for a in (U, W, g))
         hpcg_set_factors(self.handle, self.part, *self._factors)
+
+    def set_factors_bridge(self, F, Ub, Vb, Bc, g):
+        """Bridge-format factors (per-leaf bridges and per-tile cores)."""
+        self._factors = tuple(
+            None if a is None else torch.as_tensor(a, dtype=torch.float32).to(self.device).contiguous()
+            for a in (F, Ub, Vb, Bc, g))
+        hpcg_set_factors_bridge(self.handle, self.part, *self._factors)
 
     def _vec(self, v):
         return torch.as_tensor(v, dtype=torch.float32).to(self.device).contiguous().reshape(-1)

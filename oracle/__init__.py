@@ -12,6 +12,7 @@ Modules
            a dense assembly of M by its entries, and an SPD certificate
   sparse   CSR matrix-vector product and the true residual
   pcg      preconditioned conjugate gradients
+  bridge   the pages' bridge-and-core off-diagonal format and its apply
 
 Every function in this package is pinned by a CPU test against something other
 than itself (printed values, closed forms, library routines, brute force).
@@ -29,3 +30,11 @@ from .hmatrix import (  # noqa: F401
 )
 from .sparse import spmv, spmv_batch, spmv_block, true_relres, dense_A  # noqa: F401
 from .pcg import pcg, pcg_batch, PCGResult  # noqa: F401
+from .bridge import (  # noqa: F401
+    apply_M_bridge,
+    dense_M_bridge_entry,
+    to_slabs,
+    pack_bridge,
+    weyl_lower_bound_bridge,
+    core_count,
+)

@@ -324,6 +324,31 @@ def make_factors(rng, n: int, diag_a: np.ndarray, leaf: int = LEAF, rank: int = 
     return U.astype(np.float32), W.astype(np.float32), g.astype(np.float32)
 
 
+def make_bridge_factors(rng, K: int, levels: int, leaf: int = LEAF, rank: int = RANK,
+                        bridge_scale: float = 1.0, core_scale: float = 0.005):
+    """Off-diagonal factors in the pages' bridge format for one system: per-leaf
+    bridges U~_k, V~_k [K, L, Ls] with entries N(0,1) bridge_scale/sqrt(L), and
+    one Ls x Ls core per tile (tile order: level by level, j ascending) with
+    entries N(0,1) core_scale/(sqrt(Ls) 2^l) at level l, so that every level's
+    tiles have about the same operator norm."""
+    Ub = bridge_scale * rng.standard_normal((K, leaf, rank)) / np.sqrt(leaf)
+    Vb = bridge_scale * rng.standard_normal((K, leaf, rank)) / np.sqrt(leaf)
+    cores = [core_scale * rng.standard_normal((rank, rank)) / (np.sqrt(rank) * (1 << lev))
+             for lev in range(levels) for _j in range(K >> (lev + 1))]
+    Bc = np.stack(cores) if cores else np.zeros((0, rank, rank))
+    return Ub.astype(np.float32), Vb.astype(np.float32), Bc.astype(np.float32)
+
+
+def bridge_factors_for(batch: "Batch", seed: int = 7):
+    """Bridge-format off-diagonal factors for every system of a batch (its leaf
+    factors and gate stay as they are): Ub, Vb [B, K, L, Ls], Bc [B, M_H, Ls, Ls]."""
+    out = []
+    for s in range(batch.batch):
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, s, batch.n])))
+        out.append(make_bridge_factors(rng, batch.K, batch.levels))
+    return tuple(np.stack([o[i] for o in out]) for i in range(3))
+
+
 def _diag_of(row_ptr, col, val):
     n = row_ptr.size - 1
     rows = np.repeat(np.arange(n), np.diff(row_ptr))
