@@ -39,7 +39,20 @@ constexpr size_t kCtlBarrier = 0, kCtlAbort = 256, kCtlItbase = 512, kCtlReplays
 constexpr int kMaxSplit = 8;   // workgroups per leaf in the streaming kernels
 
 // split = 0 picks the workgroups per leaf automatically, else 1, 2, 4 or 8.
-bool make_geom(const hpcg_partition* p, Geom& G, std::string& why, int split = 0) {
+bool make_geom(const hpcg_partition* p, Geom& G, std::string& why, int split);
+
+// The standalone apply on large batches (B K >= 512 leaves, more than two per
+// compute unit) runs 4 workgroups per leaf: 32 KB of LDS each instead of up to
+// 128 KB, so several share a compute unit and their loads overlap.
+Geom apply_geom(const hpcg_partition* p, const Geom& G, int split) {
+  if (split != 0 || (int64_t)G.B * G.K < 512 || G.bpl >= 4) return G;
+  Geom A;
+  std::string why;
+  return make_geom(p, A, why, 4) ? A : G;
+}
+
+// split = 0 picks the workgroups per leaf automatically, else 1, 2, 4 or 8.
+bool make_geom(const hpcg_partition* p, Geom& G, std::string& why, int split) {
   if (!p) { why = "partition is NULL"; return false; }
   if (p->leaf != LEAF) { why = "leaf size must be 128"; return false; }
   if (p->rank != RANK) { why = "off-diagonal rank must be 32"; return false; }
@@ -137,6 +150,7 @@ struct hpcg_ctx {
   int graph_bpl = 0;
   int split = 0;
   int apply_path = HPCG_APPLY_AUTO;
+  Geom Gapply{};           // geometry of the standalone apply kernels
   int last_apply_path = 0;
   int fused_per_cu = -1;
   double graph_tol = -1.0;
@@ -368,7 +382,7 @@ extern "C" {
 size_t hpcg_workspace_bytes(const hpcg_partition* part, int64_t nnz_total) {
   Geom G;
   std::string why;
-  if (!make_geom(part, G, why) || nnz_total < 0) return 0;
+  if (!make_geom(part, G, why, 0) || nnz_total < 0) return 0;
   return make_layout(G, nnz_total).total;
 }
 
@@ -379,7 +393,7 @@ hpcg_status hpcg_create(const hpcg_partition* part, const int32_t* d_row_ptr, co
   if (!out) return fail(nullptr, HPCG_ERR_INVALID_ARG, "out is NULL");
   Geom G;
   std::string why;
-  if (!make_geom(part, G, why)) return fail(nullptr, HPCG_ERR_SHAPE, why);
+  if (!make_geom(part, G, why, 0)) return fail(nullptr, HPCG_ERR_SHAPE, why);
   if (nnz_total < 0 || nnz_total >= ((int64_t)1 << 31)) return fail(nullptr, HPCG_ERR_SHAPE, "nnz_total out of range");
   if (!d_row_ptr || (nnz_total > 0 && (!d_col || !d_val)))
     return fail(nullptr, HPCG_ERR_INVALID_ARG, "CSR pointer is NULL");
@@ -393,6 +407,7 @@ hpcg_status hpcg_create(const hpcg_partition* part, const int32_t* d_row_ptr, co
   h->part = *part;
   h->nnz = nnz_total;
   h->G = G;
+  h->Gapply = apply_geom(part, G, 0);
   h->lay = lay;
   h->stream = reinterpret_cast<hipStream_t>(stream);
   h->ws = reinterpret_cast<char*>(d_workspace);
@@ -582,7 +597,7 @@ hpcg_status hpcg_apply_M(hpcg_handle h, const float* d_r, float* d_y) {
     return fail(h, HPCG_ERR_SHAPE, "fused apply: the batch has more leaves than co-resident workgroups");
   }
   h->last_apply_path = HPCG_APPLY_STREAMING;
-  const Geom& G = h->G;
+  const Geom& G = h->Gapply;
   const size_t lds_r = restrict_lds_bytes(G), lds_p = prolong_lds_bytes<float>(G);
   hpcg_status s = allow_lds(h, reinterpret_cast<const void*>(&k_apply_restrict), lds_r);
   if (s == HPCG_OK) s = allow_lds(h, reinterpret_cast<const void*>(&k_apply_prolong), lds_p);
@@ -783,6 +798,7 @@ hpcg_status hpcg_set_option(hpcg_handle h, int32_t option, int32_t value) {
       if (!make_geom(&h->part, G, why, value)) return fail(h, HPCG_ERR_SHAPE, why);
       h->G = G;
       h->split = value;
+      h->Gapply = apply_geom(&h->part, G, value);
       return HPCG_OK;
     }
     default:
