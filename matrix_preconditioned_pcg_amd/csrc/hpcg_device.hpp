@@ -373,6 +373,16 @@ __device__ __forceinline__ void issue_restrict_dma(const Geom& G, const Bufs& B,
   }
 }
 
+// Sum over the lanes of a wave that share lane % slots (slots = 4, 8, 16 or
+// 32): xor partners at distances slots .. 32.
+template <typename T>
+__device__ __forceinline__ T rowgroup_sum(T v, int slots) {
+  if (slots <= 4) v += __shfl_xor(v, 4);
+  if (slots <= 8) v += lane_x8(v);
+  if (slots <= 16) v += lane_x16(v);
+  return v + lane_x32(v);
+}
+
 // Sum over groups of `width` consecutive lanes (width = 4, 8, 16 or 32).
 template <typename T>
 __device__ __forceinline__ T group_sum(T v, int width) {
@@ -392,13 +402,19 @@ __device__ __forceinline__ void restrict_leaf(const Geom& G, const Bufs& B, cons
   T* share = reinterpret_cast<T*>(B.tleaf) + (((size_t)bk.s * G.K + bk.k) * G.bpl + bk.j) * LEAF;
   T* pleaf = reinterpret_cast<T*>(B.pleaf);
   {
-    // t_j: thread = (4-column slot c4, row group rg); RG row groups
+    // t_j: thread = (4-column slot c4, row group rg); RG row groups.  The row
+    // groups of a wave (lane bits log2(slots) .. 5) are summed across lanes,
+    // then the four waves through LDS.
     const int RG = NT / slots;
     const int c4 = tid % slots, rg = tid / slots;
     Vec4<T> acc{0, 0, 0, 0};
     for (int i = rg; i < LEAF; i += RG) axpy4(acc, lds4f(dyn + i * CW + 4 * c4), sm.r[i]);
-    T* d = &sm.redT[rg * CW + 4 * c4];
-    d[0] = acc.x; d[1] = acc.y; d[2] = acc.z; d[3] = acc.w;
+    acc.x = rowgroup_sum(acc.x, slots); acc.y = rowgroup_sum(acc.y, slots);
+    acc.z = rowgroup_sum(acc.z, slots); acc.w = rowgroup_sum(acc.w, slots);
+    if ((tid & 63) < slots) {
+      T* d = &sm.redT[wave * CW + 4 * c4];
+      d[0] = acc.x; d[1] = acc.y; d[2] = acc.z; d[3] = acc.w;
+    }
   }
   {
     // owned levels: thread = (4-column slot cs of 8, row group rg of 32); the
@@ -422,10 +438,10 @@ __device__ __forceinline__ void restrict_leaf(const Geom& G, const Bufs& B, cons
   }
   __syncthreads();
   {
-    const int RG = NT / slots;
     if (tid < CW) {
       T a = sm.redT[tid];
-      for (int g = 1; g < RG; ++g) a += sm.redT[g * CW + tid];
+#pragma unroll
+      for (int w = 1; w < NWAVE; ++w) a += sm.redT[w * CW + tid];
       sm.t[tid] = a;
     }
     const int nl = levels_of_slot(G, bk.j);
