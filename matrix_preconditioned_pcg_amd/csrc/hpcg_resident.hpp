@@ -57,6 +57,7 @@ struct alignas(16) RSmem {
   T red[NWR][LEAF];                  // cross-wave reductions of t
   T redW[NWR][2 * MAX_LEVELS * RANK];  // cross-wave reductions (restriction, strip sums)
   double dred[NWR];
+  double dred2[NWR];
   double dsc[4];
   int flag[4];
 };
@@ -127,6 +128,28 @@ __device__ __forceinline__ double wg_sum_r(double v, RSmem<T>& sm) {
   return s;
 }
 
+// Two workgroup sums with one pair of barriers.
+template <typename T>
+__device__ __forceinline__ void wg_sum2_r(double& a, double& b, RSmem<T>& sm) {
+  a = wave_sum(a);
+  b = wave_sum(b);
+  const int tid = threadIdx.x;
+  if ((tid & 63) == 0) {
+    sm.dred[tid >> 6] = a;
+    sm.dred2[tid >> 6] = b;
+  }
+  __syncthreads();
+  double sa = sm.dred[0], sb = sm.dred2[0];
+#pragma unroll
+  for (int w = 1; w < NWR; ++w) {
+    sa += sm.dred[w];
+    sb += sm.dred2[w];
+  }
+  __syncthreads();
+  a = sa;
+  b = sb;
+}
+
 // Every wave reads the system's K partials and sums them in the same order.
 __device__ __forceinline__ double sum_partials_r(const double* part, int s, int K) {
   double v = 0.0;
@@ -149,10 +172,17 @@ struct Resident {
 
 // Restriction of the LDS vector v: U_k^T v into tout (LDS, complete) and
 // W_l[k]^T v into pout (global, [levels][K][RANK] of system s) and own (LDS).
+// With part_dst, the workgroup sum of `loc` is stored there as well (sharing
+// the restriction's barriers).
 template <typename T, int LEV>
 __device__ __forceinline__ void r_restrict(const Geom& G, int s, int k, const Resident<T, LEV>& F,
-                                           const T* v, T* tout, T* pout, T* own, RSmem<T>& sm) {
+                                           const T* v, T* tout, T* pout, T* own, RSmem<T>& sm,
+                                           double loc = 0.0, double* part_dst = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (part_dst) {
+    loc = wave_sum(loc);
+    if (lane == 0) sm.dred[wave] = loc;
+  }
   {
     const int cs = tid & 31, rg = tid >> 5;
     Vec4<T> acc{0, 0, 0, 0};
@@ -205,6 +235,12 @@ __device__ __forceinline__ void r_restrict(const Geom& G, int s, int k, const Re
     }
   }
   __syncthreads();
+  if (part_dst && tid == 0) {
+    double p = sm.dred[0];
+#pragma unroll
+    for (int w = 1; w < NWR; ++w) p += sm.dred[w];
+    st_c(part_dst, p);
+  }
   if (tid < LEAF) {
     T a = sm.red[0][tid];
 #pragma unroll
@@ -278,6 +314,7 @@ __device__ __forceinline__ void r_prolong(const Resident<T, LEV>& F, RSmem<T>& s
     }
     __syncthreads();
   }
+  if constexpr (LEV == 0) __syncthreads();   // sm.t and sm.r of the caller
   // diagonal stage: rows rg + 16m (m < 8), dots over 32 column slots; the eight
   // rows of a lane are folded with a transpose-reduce (7 + 2 shuffles)
   {
@@ -552,11 +589,9 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
           st_c(pnew + leaf0 + row, pn);
           loc = (double)pn * (double)acc;
         }
-        // the partial p.q goes out first, so that its store is acknowledged
-        // while the restriction of q runs
-        part = wg_sum_r(loc, sm);
-        if (tid == 0) st_c(B.pq_part + item, part);
-        r_restrict<T, LEV>(G, s, k, F, sm.q, sm.tq, pQ, sm.ownQ, sm);
+        __syncthreads();
+        // the restriction of q also sums and stores the partial p.q
+        r_restrict<T, LEV>(G, s, k, F, sm.q, sm.tq, pQ, sm.ownQ, sm, loc, B.pq_part + item);
       }
     }
     if (cgrid_barrier(B, target, epoch)) return;
@@ -579,24 +614,26 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
           if (lead) set_state(st, ST_BREAKDOWN, it);
         } else {
           const double alpha = rz_old / pq;
-          loc = 0.0;
+          double loc_rr = 0.0;
           if (tid < LEAF) {
             const T rn = (T)((double)sm.r[tid] - alpha * (double)sm.q[tid]);
             sm.r[tid] = rn;
             x += alpha * (double)sm.p[tid];
-            loc = (double)rn * (double)rn;
+            loc_rr = (double)rn * (double)rn;
             sm.t[tid] = (T)((double)sm.tr[tid] - alpha * (double)sm.tq[tid]);
           }
-          part = wg_sum_r(loc, sm);
-          if (tid == 0) st_c(B.rr_part + item, part);
+          // (r_prolong synchronizes before it reads sm.r and sm.t)
           r_prolong<T, LEV>(F, sm, stR, stQ, alpha, gate);
-          loc = 0.0;
+          double loc_rz = 0.0;
           if (tid < LEAF) {
             st_c(zg + leaf0 + tid, sm.z[tid]);
-            loc = (double)sm.r[tid] * (double)sm.z[tid];
+            loc_rz = (double)sm.r[tid] * (double)sm.z[tid];
           }
-          part = wg_sum_r(loc, sm);
-          if (tid == 0) st_c(B.rz_part + item, part);
+          wg_sum2_r(loc_rr, loc_rz, sm);
+          if (tid == 0) {
+            st_c(B.rr_part + item, loc_rr);
+            st_c(B.rz_part + item, loc_rz);
+          }
           next_alpha = alpha;
           restrict_next = true;
         }
