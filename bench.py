@@ -332,6 +332,28 @@ def main(argv=None):
         bridge = {"expand_us": round(t_exp, 3), "ms_per_solve": round(ms, 4), "iterations": its[0],
                   "factor_bytes": int(sum(a.numel() * 4 for a in dev))}
         solver.close()
+    tight = None
+    if not args.no_variants:
+        # rtol 1e-10: fp64 vectors directly, and the outer refinement around
+        # fp32-vector inner solves (inner tolerance 1e-5)
+        log("bench: tight tolerance")
+        bt = make_config(args.config)
+        solver = hpcg.Solver(bt.n, bt.row_ptr, bt.col, bt.val, batch=bt.batch, levels=bt.levels, stream=stream)
+        solver.set_factors(bt.U, bt.W, bt.g)
+        bvec = torch.as_tensor(bt.b.reshape(-1)).cuda()
+        ms_d, its_d, _r = time_solves(solver, bvec, 1e-10, 5000, 3, 1, torch)
+        solver.set_option(hpcg.HPCG_OPT_PRECISION, hpcg.HPCG_PREC_VEC32)
+        solver.solve_refined(bvec, tol=1e-10, maxit=20000, inner_tol=1e-5)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(3):
+            res_r, outer = solver.solve_refined(bvec, tol=1e-10, maxit=20000, inner_tol=1e-5)
+        torch.cuda.synchronize()
+        ms_r = (time.perf_counter() - t0) * 1e3 / 3
+        tight = {"tol": 1e-10, "vec64_ms_per_solve": round(ms_d, 4), "vec64_iterations": its_d[0],
+                 "refined_vec32_ms_per_solve": round(ms_r, 4), "refined_inner_iterations": res_r.iterations[0],
+                 "refined_outer_steps": outer[0], "refined_true_relres": res_r.relres[0]}
+        solver.close()
     block = []
     if not args.no_block:
         for name in ("N8k", "N16k"):
@@ -386,6 +408,7 @@ def main(argv=None):
         "variants_at_workload": variants,
         "block_apply": block,
         "bridge_format": bridge,
+        "tight_tolerance": tight,
     }
     print(json.dumps(line), flush=True)
     return 0

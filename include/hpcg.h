@@ -251,6 +251,29 @@ hpcg_status hpcg_spmv_block(hpcg_handle h, const float* d_X, float* d_Y, int32_t
 hpcg_status hpcg_solve(hpcg_handle h, const float* d_b, double* d_x, double tol,
                        int32_t maxit, int32_t* h_iters, double* h_relres);
 
+/* Solve to a tight tolerance with an outer iterative refinement in fp64
+ * around the configured solve ("Hierarchical Transformer Preconditioning for
+ * Interactive Physics Simulation", Supplementary section 7: for rtol <= 1e-10
+ * the pages propose an outer refinement loop that keeps the float32 apply as
+ * the inner preconditioner):
+ *   x = 0;  repeat:  r = b - A x (fp64);  stop when ||r|| <= tol ||b||;
+ *                    solve A d = r / ||r|| to inner_tol (engine and vector
+ *                    precision as set by hpcg_set_option);  x += ||r|| d.
+ *  d_b, d_x   as for hpcg_solve (x is overwritten, fp64)
+ *  tol        outer tolerance on the true residual ||b - A x|| / ||b||
+ *  maxit      budget of inner iterations per system, summed over the outer steps
+ *  inner_tol  in (0, 1), e.g. 1e-5 with fp32 vectors
+ *  max_outer  >= 1
+ *  h_iters    [batch] inner iterations summed (may be NULL)
+ *  h_outer    [batch] outer steps taken (may be NULL)
+ *  h_relres   [batch] final true relative residual, fp64 (may be NULL)
+ * Statuses as for hpcg_solve; scratch lives in the workspace.  Synchronizes
+ * with the host once per outer step. */
+hpcg_status hpcg_solve_refined(hpcg_handle h, const float* d_b, double* d_x, double tol, int32_t maxit,
+                               double inner_tol, int32_t max_outer, int32_t* h_iters, int32_t* h_outer,
+                               double* h_relres);
+
+
 /* Per-system hpcg_system_status values of the last hpcg_solve, int32 [batch]. */
 hpcg_status hpcg_last_solve_status(hpcg_handle h, int32_t* h_status);
 

@@ -9,6 +9,7 @@
 #include <atomic>
 #include <chrono>
 #include <cstdio>
+#include <cmath>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -26,7 +27,9 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t row_ptr, col, val, U, W, g, b, r, z, q, p0, p1, x, tleaf, pleaf, pq, rr, rz, st, ctl, total;
+  size_t row_ptr, col, val, U, W, g, b, r, z, q, p0, p1, x, tleaf, pleaf, pq, rr, rz, st, ctl;
+  size_t fr, fd, frhs, fsc;   // outer refinement: residual, correction, scaled rhs, per-system scalars
+  size_t total;
 };
 
 // LDS of one gfx950 compute unit: a workgroup's static and dynamic LDS must fit.
@@ -118,6 +121,10 @@ Layout make_layout(const Geom& G, int64_t nnz) {
   L.rz = take(items * 8);
   L.st = take((size_t)G.B * sizeof(SysState));
   L.ctl = take(kCtlBytes);
+  L.fr = take(N * 8);
+  L.fd = take(N * 8);
+  L.frhs = take(N * 4);
+  L.fsc = take((size_t)G.B * 8 * 3);
   L.total = off;
   return L;
 }
@@ -706,13 +713,11 @@ hpcg_status hpcg_spmv_block(hpcg_handle h, const float* d_X, float* d_Y, int32_t
   return check_launch(h, "hpcg_spmv_block launch");
 }
 
-hpcg_status hpcg_solve(hpcg_handle h, const float* d_b, double* d_x, double tol, int32_t maxit,
-                       int32_t* h_iters, double* h_relres) {
-  if (!h) return fail(nullptr, HPCG_ERR_INVALID_ARG, "handle is NULL");
-  if (!d_b || !d_x) return fail(h, HPCG_ERR_INVALID_ARG, "vector pointer is NULL");
-  if (!(tol > 0.0) || !(tol < 1e300)) return fail(h, HPCG_ERR_INVALID_ARG, "tol must be positive and finite");
-  if (maxit < 1) return fail(h, HPCG_ERR_INVALID_ARG, "maxit must be >= 1");
-  if (!h->factors_set) return fail(h, HPCG_ERR_STATE, "hpcg_set_factors has not been called");
+namespace {
+
+// One PCG solve with the configured engine; fills the per-system state copy
+// h->h_st (status, iterations, recursive residual) and returns the call status.
+hpcg_status solve_core(hpcg_ctx* h, const float* d_b, double* d_x, double tol, int32_t maxit) {
   const Geom G = h->G;
   const size_t N = (size_t)G.B * G.n;
   h->B.tol = tol;
@@ -750,8 +755,28 @@ hpcg_status hpcg_solve(hpcg_handle h, const float* d_b, double* d_x, double tol,
   HIP_OR_FAIL(h, hipMemcpyAsync(h->h_ctl, h->B.abort_flag, sizeof(int), hipMemcpyDeviceToHost, h->stream));
   HIP_OR_FAIL(h, hipStreamSynchronize(h->stream));
   if (*h->h_ctl) return fail(h, HPCG_ERR_HIP, "device-wide barrier timed out (workgroups not co-resident)");
+  return HPCG_OK;
+}
+
+hpcg_status check_solve_args(hpcg_ctx* h, const float* d_b, double* d_x, double tol, int32_t maxit) {
+  if (!h) return fail(nullptr, HPCG_ERR_INVALID_ARG, "handle is NULL");
+  if (!d_b || !d_x) return fail(h, HPCG_ERR_INVALID_ARG, "vector pointer is NULL");
+  if (!(tol > 0.0) || !(tol < 1e300)) return fail(h, HPCG_ERR_INVALID_ARG, "tol must be positive and finite");
+  if (maxit < 1) return fail(h, HPCG_ERR_INVALID_ARG, "maxit must be >= 1");
+  if (!h->factors_set) return fail(h, HPCG_ERR_STATE, "hpcg_set_factors has not been called");
+  return HPCG_OK;
+}
+
+}  // namespace
+
+hpcg_status hpcg_solve(hpcg_handle h, const float* d_b, double* d_x, double tol, int32_t maxit,
+                       int32_t* h_iters, double* h_relres) {
+  hpcg_status s = check_solve_args(h, d_b, d_x, tol, maxit);
+  if (s != HPCG_OK) return s;
+  s = solve_core(h, d_b, d_x, tol, maxit);
+  if (s != HPCG_OK) return s;
   bool any_break = false, any_nc = false;
-  for (int i = 0; i < G.B; ++i) {
+  for (int i = 0; i < h->G.B; ++i) {
     const SysState& st = h->h_st[i];
     h->last_status[i] = st.status;
     if (h_iters) h_iters[i] = st.iters;
@@ -761,6 +786,80 @@ hpcg_status hpcg_solve(hpcg_handle h, const float* d_b, double* d_x, double tol,
   }
   if (any_break) return fail(h, HPCG_ERR_BREAKDOWN, "breakdown: p.Ap or r.Mr not positive and finite");
   if (any_nc) return fail(h, HPCG_ERR_NOT_CONVERGED, "maxit reached before the tolerance");
+  return HPCG_OK;
+}
+
+hpcg_status hpcg_solve_refined(hpcg_handle h, const float* d_b, double* d_x, double tol, int32_t maxit,
+                               double inner_tol, int32_t max_outer, int32_t* h_iters, int32_t* h_outer,
+                               double* h_relres) {
+  hpcg_status s = check_solve_args(h, d_b, d_x, tol, maxit);
+  if (s != HPCG_OK) return s;
+  if (!(inner_tol > 0.0) || !(inner_tol < 1.0)) return fail(h, HPCG_ERR_INVALID_ARG, "inner_tol must lie in (0, 1)");
+  if (max_outer < 1) return fail(h, HPCG_ERR_INVALID_ARG, "max_outer must be >= 1");
+  const Geom G = h->G;
+  const int N = G.B * G.n;
+  const unsigned grid = (unsigned)((N + 255) / 256);
+  double* r = reinterpret_cast<double*>(h->ws + h->lay.fr);
+  double* d = reinterpret_cast<double*>(h->ws + h->lay.fd);
+  float* rhs = reinterpret_cast<float*>(h->ws + h->lay.frhs);
+  double* sumsq = reinterpret_cast<double*>(h->ws + h->lay.fsc);
+  double* inv = sumsq + G.B;
+  double* scale = inv + G.B;
+  std::vector<double> hs(G.B), bn2(G.B), hinv(G.B), hscale(G.B), rel(G.B, 1.0);
+  std::vector<int> its(G.B, 0), outer(G.B, 0), status(G.B, ST_RUNNING);
+  const Bufs& B = h->B;
+  HIP_OR_FAIL(h, hipMemsetAsync(d_x, 0, (size_t)N * 8, h->stream));
+  bool any_break = false;
+  for (int o = 0;; ++o) {
+    // true residual of the current x, in fp64
+    hipLaunchKernelGGL(k_residual64, dim3(grid), dim3(256), 0, h->stream, B.row_ptr, B.col, B.val, d_b, d_x, r, N);
+    hipLaunchKernelGGL(k_sys_sumsq, dim3(G.B), dim3(NT), 0, h->stream, r, G.n, sumsq);
+    s = check_launch(h, "refinement residual launch");
+    if (s != HPCG_OK) return s;
+    HIP_OR_FAIL(h, hipMemcpyAsync(hs.data(), sumsq, (size_t)G.B * 8, hipMemcpyDeviceToHost, h->stream));
+    HIP_OR_FAIL(h, hipStreamSynchronize(h->stream));
+    if (o == 0) bn2 = hs;
+    bool all_done = true;
+    for (int i = 0; i < G.B; ++i) {
+      if (status[i] != ST_RUNNING) { hinv[i] = 0.0; continue; }
+      rel[i] = bn2[i] > 0.0 ? std::sqrt(hs[i] / bn2[i]) : 0.0;
+      if (rel[i] <= tol) { status[i] = ST_CONVERGED; hinv[i] = 0.0; continue; }
+      if (o >= max_outer || its[i] >= maxit) { status[i] = ST_NOT_CONVERGED; hinv[i] = 0.0; continue; }
+      all_done = false;
+      hscale[i] = std::sqrt(hs[i]);
+      hinv[i] = 1.0 / hscale[i];
+    }
+    if (all_done) break;
+    // inner solve of A d = r / ||r|| with the configured engine and precision
+    HIP_OR_FAIL(h, hipMemcpyAsync(inv, hinv.data(), (size_t)G.B * 8, hipMemcpyHostToDevice, h->stream));
+    hipLaunchKernelGGL(k_scale_rhs, dim3(grid), dim3(256), 0, h->stream, r, inv, rhs, G.n, N);
+    int budget = 0;
+    for (int i = 0; i < G.B; ++i)
+      if (status[i] == ST_RUNNING) budget = std::max(budget, maxit - its[i]);
+    s = solve_core(h, rhs, d, inner_tol, std::max(budget, 1));
+    if (s != HPCG_OK) return s;
+    for (int i = 0; i < G.B; ++i) {
+      if (status[i] != ST_RUNNING) { hscale[i] = 0.0; continue; }
+      const SysState& st = h->h_st[i];
+      its[i] += st.iters;
+      outer[i] = o + 1;
+      if (st.status == ST_BREAKDOWN) { status[i] = ST_BREAKDOWN; any_break = true; hscale[i] = 0.0; }
+    }
+    HIP_OR_FAIL(h, hipMemcpyAsync(scale, hscale.data(), (size_t)G.B * 8, hipMemcpyHostToDevice, h->stream));
+    hipLaunchKernelGGL(k_add_scaled, dim3(grid), dim3(256), 0, h->stream, d_x, d, scale, G.n, N);
+    s = check_launch(h, "refinement update launch");
+    if (s != HPCG_OK) return s;
+  }
+  bool any_nc = false;
+  for (int i = 0; i < G.B; ++i) {
+    h->last_status[i] = status[i];
+    if (h_iters) h_iters[i] = its[i];
+    if (h_outer) h_outer[i] = outer[i];
+    if (h_relres) h_relres[i] = rel[i];
+    if (status[i] == ST_NOT_CONVERGED) any_nc = true;
+  }
+  if (any_break) return fail(h, HPCG_ERR_BREAKDOWN, "breakdown in an inner solve");
+  if (any_nc) return fail(h, HPCG_ERR_NOT_CONVERGED, "outer or inner iteration budget reached before the tolerance");
   return HPCG_OK;
 }
 

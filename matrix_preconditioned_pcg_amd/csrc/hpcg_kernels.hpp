@@ -249,6 +249,50 @@ __global__ __launch_bounds__(NT) void k_expand_bridge(Geom G, const float* __res
   }
 }
 
+// ---------------------------------------------------------------------------
+// outer refinement (fp64 residual of the fp32 matrix, per-system scaling)
+// ---------------------------------------------------------------------------
+// r = b - A x in fp64 (thread per row).
+__global__ void k_residual64(const int* __restrict__ row_ptr, const int* __restrict__ col,
+                             const float* __restrict__ val, const float* __restrict__ b,
+                             const double* __restrict__ x, double* __restrict__ r, int nrows) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nrows) return;
+  double acc = 0.0;
+  for (int e = row_ptr[i]; e < row_ptr[i + 1]; ++e) acc = fma((double)val[e], x[col[e]], acc);
+  r[i] = (double)b[i] - acc;
+}
+
+// Per-system sum of squares of v (one workgroup per system, fixed order).
+__global__ __launch_bounds__(NT) void k_sys_sumsq(const double* __restrict__ v, int n, double* __restrict__ out) {
+  __shared__ double red[NWAVE];
+  const double* p = v + (size_t)blockIdx.x * n;
+  double a = 0.0;
+  for (int i = threadIdx.x; i < n; i += NT) a = fma(p[i], p[i], a);
+  a = wave_sum(a);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double s = red[0];
+    for (int w = 1; w < NWAVE; ++w) s += red[w];
+    out[blockIdx.x] = s;
+  }
+}
+
+// rhs = r * inv[s] rounded to fp32 (inv = 0 for a finished system).
+__global__ void k_scale_rhs(const double* __restrict__ r, const double* __restrict__ inv, float* __restrict__ rhs,
+                            int n, int N) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < N) rhs[i] = (float)(r[i] * inv[i / n]);
+}
+
+// x += scale[s] * d.
+__global__ void k_add_scaled(double* __restrict__ x, const double* __restrict__ d, const double* __restrict__ scale,
+                             int n, int N) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < N) x[i] = fma(scale[i / n], d[i], x[i]);
+}
+
 __global__ void k_copy_x(const double* __restrict__ src, double* __restrict__ dst, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) dst[i] = src[i];

@@ -97,6 +97,7 @@ def lib() -> ctypes.CDLL:
         "hpcg_spmv_block": (i32, [vp, vp, vp, i32]),
         "hpcg_solve": (i32, [vp, vp, vp, dbl, i32, P(i32), P(dbl)]),
         "hpcg_last_solve_status": (i32, [vp, P(i32)]),
+        "hpcg_solve_refined": (i32, [vp, vp, vp, dbl, i32, dbl, i32, P(i32), P(i32), P(dbl)]),
         "hpcg_set_option": (i32, [vp, i32, i32]),
         "hpcg_last_engine": (i32, [vp]),
         "hpcg_last_apply_path": (i32, [vp]),
@@ -253,6 +254,19 @@ def hpcg_solve(h, part: hpcg_partition, b, x, tol: float, maxit: int):
     return st, list(iters), list(rel)
 
 
+def hpcg_solve_refined(h, part: hpcg_partition, b, x, tol: float, maxit: int, inner_tol: float, max_outer: int):
+    """Returns (status, inner iterations[list], outer steps[list], true relres[list])."""
+    N = part.n * part.batch
+    iters = (ctypes.c_int32 * part.batch)()
+    outer = (ctypes.c_int32 * part.batch)()
+    rel = (ctypes.c_double * part.batch)()
+    st = lib().hpcg_solve_refined(h, _ptr(b, torch.float32, N, "b"), _ptr(x, torch.float64, N, "x"),
+                                  float(tol), int(maxit), float(inner_tol), int(max_outer), iters, outer, rel)
+    if st not in (HPCG_OK, HPCG_ERR_NOT_CONVERGED, HPCG_ERR_BREAKDOWN):
+        _check(st, h)
+    return st, list(iters), list(outer), list(rel)
+
+
 def hpcg_last_solve_status(h, batch: int) -> list:
     out = (ctypes.c_int32 * batch)()
     _check(lib().hpcg_last_solve_status(h, out), h)
@@ -400,6 +414,16 @@ class Solver:
         st, iters, rel = hpcg_solve(self.handle, self.part, b, x, tol, maxit)
         sys_st = hpcg_last_solve_status(self.handle, self.batch)
         return SolveResult(x.reshape(self.batch, self.n), iters, rel, st, sys_st)
+
+    def solve_refined(self, b, tol: float = 1e-10, maxit: int = 5000, inner_tol: float = 1e-5,
+                      max_outer: int = 10, x=None):
+        """Outer fp64 refinement around the configured solve; returns
+        (SolveResult with the true relative residual, outer steps per system)."""
+        b = self._vec(b)
+        x = torch.empty(b.numel(), dtype=torch.float64, device=self.device) if x is None else x
+        st, iters, outer, rel = hpcg_solve_refined(self.handle, self.part, b, x, tol, maxit, inner_tol, max_outer)
+        sys_st = hpcg_last_solve_status(self.handle, self.batch)
+        return SolveResult(x.reshape(self.batch, self.n), iters, rel, st, sys_st), outer
 
     @property
     def last_engine(self) -> int:

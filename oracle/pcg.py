@@ -98,6 +98,32 @@ def pcg(row_ptr, col, val, b, precond, tol: float, maxit: int, dtype=np.float64)
     return out(maxit, "not_converged", norm(r) / bnorm)
 
 
+def pcg_refined(row_ptr, col, val, b, precond, tol: float, maxit: int, inner_tol: float, max_outer: int):
+    """Outer iterative refinement around PCG ("Hierarchical Transformer
+    Preconditioning for Interactive Physics Simulation", Supplementary section 7,
+    the loop proposed for rtol <= 1e-10): x = 0; repeat r = b - A x; stop when
+    ||r|| <= tol ||b||; solve A d = r / ||r|| to inner_tol; x += ||r|| d.
+    Returns (x, inner iterations summed, outer steps, status, true relres)."""
+    b = np.asarray(b, dtype=np.float64)
+    x = np.zeros_like(b)
+    bnorm = float(np.linalg.norm(b))
+    iters, outer = 0, 0
+    while True:
+        r = b - spmv(row_ptr, col, val, x)
+        rn = float(np.linalg.norm(r))
+        rel = rn / bnorm if bnorm > 0 else 0.0
+        if rel <= tol:
+            return x, iters, outer, "converged", rel
+        if outer >= max_outer or iters >= maxit:
+            return x, iters, outer, "not_converged", rel
+        inner = pcg(row_ptr, col, val, r / rn, precond, inner_tol, maxit - iters)
+        iters += inner.iterations
+        outer += 1
+        if inner.status == "breakdown":
+            return x, iters, outer, "breakdown", rel
+        x = x + rn * inner.x
+
+
 def pcg_batch(batch, tol: float | None = None, maxit: int | None = None,
               systems=None) -> list:
     """Independent PCG per system of a workloads.Batch (or the listed systems)."""

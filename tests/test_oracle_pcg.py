@@ -165,3 +165,23 @@ def test_rounding_sensitivity_of_iteration_counts():
     assert d.status == e.status == "converged"
     assert e.iterations < d.iterations - 2
     np.testing.assert_allclose(d.history[:5], e.history[:5], rtol=1e-12)
+
+
+def test_refinement_reaches_tight_tolerance():
+    # outer refinement with a loose inner tolerance reaches 1e-10 on the true
+    # residual; the number of outer steps is about log(tol) / log(inner_tol)
+    sy = make_config("N1k").system(0)
+    x, its, outer, status, rel = oracle.pcg_refined(sy.row_ptr, sy.col, sy.val, sy.b, (sy.U, sy.W, sy.g),
+                                                    1e-10, 5000, 1e-4, 10)
+    assert status == "converged" and rel <= 1e-10
+    assert 3 <= outer <= 4
+    assert rel == pytest.approx(oracle.true_relres(sy.row_ptr, sy.col, sy.val, sy.b, x), rel=1e-12)
+    # with the inner tolerance at the outer one, one step is plain PCG
+    x1, its1, outer1, status1, _ = oracle.pcg_refined(sy.row_ptr, sy.col, sy.val, sy.b, (sy.U, sy.W, sy.g),
+                                                      1e-6, 1000, 1e-6, 10)
+    plain = oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b, (sy.U, sy.W, sy.g), 1e-6, 1000)
+    assert its1 >= plain.iterations and outer1 >= 1
+    # against a direct solve: the refined x is the solution to ~ cond(A) * 1e-10
+    A = oracle.dense_A(sy.row_ptr, sy.col, sy.val)
+    xs = np.linalg.solve(A, sy.b.astype(np.float64))
+    assert np.linalg.norm(x - xs) <= 1e-6 * np.linalg.norm(xs)
