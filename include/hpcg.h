@@ -113,12 +113,35 @@ typedef enum {
     HPCG_OPT_GRAPH_UNROLL = 2,  /* iterations per graph replay, 1 .. 64 (default 8) */
     HPCG_OPT_PRECISION = 4,     /* an hpcg_precision value                        */
     HPCG_OPT_APPLY_PATH = 16,   /* an hpcg_apply_path value                       */
+    HPCG_OPT_FORM = 32,         /* an hpcg_form value                             */
+    HPCG_OPT_FALLBACK = 64,     /* 1: an hpcg_solve in which some system breaks
+                                   down (M not SPD) solves the whole batch again
+                                   from x = 0 with M = diag(A)^-1 and reports
+                                   that solve; 0 (default): report the breakdown */
     HPCG_OPT_LEAF_SPLIT = 8     /* workgroups per leaf in the apply kernels and the
                                    graph and streaming engines: 0 = automatic
                                    (default), else 1, 2, 4 or 8; a split whose LDS
                                    need exceeds a compute unit is raised to the
                                    next that fits                                 */
 } hpcg_option;
+
+/* Which preconditioner the apply and the solve use (hpcg_set_option(
+ * HPCG_OPT_FORM, ...)), with H the H-matrix of the factors:
+ *  DIRECT   M = H (default; "Hierarchical Transformer Preconditioning for
+ *           Interactive Physics Simulation", section 5);
+ *  SQUARED  M = H H, SPD whenever the symmetric H is nonsingular ("A Neural
+ *           Hierarchical-Matrix Preconditioner for Real-Time GPU Solves",
+ *           section 2, "SPD by construction"); two applications of H per
+ *           iteration;
+ *  JACOBI   M = diag(A)^-1, the fallback those pages name; needs no factors.
+ * SQUARED and JACOBI solves run on the graph engine (AUTO selects it; the
+ * persistent engines return HPCG_ERR_SHAPE); the block apply runs DIRECT only
+ * (HPCG_ERR_STATE otherwise). */
+typedef enum {
+    HPCG_FORM_DIRECT = 0,
+    HPCG_FORM_SQUARED = 1,
+    HPCG_FORM_JACOBI = 2
+} hpcg_form;
 
 /* How hpcg_apply_M runs (hpcg_set_option(HPCG_OPT_APPLY_PATH, ...)).
  * STREAMING: two launches (restriction, then prolongation), any batch size;
@@ -279,6 +302,21 @@ hpcg_status hpcg_last_solve_status(hpcg_handle h, int32_t* h_status);
 
 /* Engine and tuning options (see hpcg_option). */
 hpcg_status hpcg_set_option(hpcg_handle h, int32_t option, int32_t value);
+
+/* Extreme eigenvalues of H, the factor operator (M itself in the direct form,
+ * M = H H in the squared form), whatever the form option says: the monitor of
+ * lambda_min(H) that "A Neural Hierarchical-Matrix Preconditioner for
+ * Real-Time GPU Solves", section 2, pairs with a Jacobi fallback.  `steps`
+ * Lanczos steps (2 .. 200) on the host in fp64, with full reorthogonalization,
+ * around the device apply, from a fixed pseudo-random start vector over the
+ * whole batch (so the result covers every system of the batch).  Ritz values
+ * lie inside the spectrum: *h_lmin <= 0 shows that H is not positive definite
+ * (up to the fp32 apply's rounding); a positive value is an upper estimate of
+ * lambda_min.  Requires factors.  Synchronous; uses the workspace as scratch. */
+hpcg_status hpcg_estimate_spectrum(hpcg_handle h, int32_t steps, double* h_lmin, double* h_lmax);
+
+/* 1 if the last hpcg_solve fell back to Jacobi (HPCG_OPT_FALLBACK), else 0. */
+int32_t hpcg_last_fallback(hpcg_handle h);
 
 /* Path the last hpcg_apply_M call took (an hpcg_apply_path; 0 before any). */
 int32_t hpcg_last_apply_path(hpcg_handle h);

@@ -29,6 +29,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   size_t row_ptr, col, val, U, W, g, b, r, z, q, p0, p1, x, tleaf, pleaf, pq, rr, rz, st, ctl;
   size_t fr, fd, frhs, fsc;   // outer refinement: residual, correction, scaled rhs, per-system scalars
+  size_t w, dinv, ftmp;       // squared form: H r; Jacobi: 1 / A_ii; apply scratch
   size_t total;
 };
 
@@ -125,6 +126,9 @@ Layout make_layout(const Geom& G, int64_t nnz) {
   L.fd = take(N * 8);
   L.frhs = take(N * 4);
   L.fsc = take((size_t)G.B * 8 * 3);
+  L.w = take(N * 8);
+  L.dinv = take(N * 8);
+  L.ftmp = take(N * 4);
   L.total = off;
   return L;
 }
@@ -155,6 +159,9 @@ struct hpcg_ctx {
   int graph_unroll = 0;
   int graph_prec = -1;
   int graph_bpl = 0;
+  int graph_form = -1;
+  int fallback = 0;
+  int last_fallback = 0;
   int split = 0;
   int apply_path = HPCG_APPLY_AUTO;
   Geom Gapply{};           // geometry of the standalone apply kernels
@@ -241,8 +248,14 @@ hpcg_status build_graph(hpcg_ctx* h) {
   HIP_OR_FAIL(h, hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal));
   for (int j = 0; j < h->unroll; ++j) {
     hipLaunchKernelGGL(k_phase_A<T>, dim3(G.nblk), dim3(NT), 0, h->cap_stream, G, B, j);
-    hipLaunchKernelGGL(k_phase_B<T>, dim3(G.nblk), dim3(NT), lds_b, h->cap_stream, G, B, j, -1);
-    hipLaunchKernelGGL(k_phase_C<T>, dim3(G.nblk), dim3(NT), lds_c, h->cap_stream, G, B, j, -1);
+    hipLaunchKernelGGL(k_phase_B<T>, dim3(G.nblk), dim3(NT), lds_b, h->cap_stream, G, B, j, -1, 0);
+    if (B.form == FORM_SQUARED) {
+      hipLaunchKernelGGL(k_phase_C<T>, dim3(G.nblk), dim3(NT), lds_c, h->cap_stream, G, B, j, -1, 1);
+      hipLaunchKernelGGL(k_phase_B<T>, dim3(G.nblk), dim3(NT), lds_b, h->cap_stream, G, B, j, -1, 1);
+      hipLaunchKernelGGL(k_phase_C<T>, dim3(G.nblk), dim3(NT), lds_c, h->cap_stream, G, B, j, -1, 2);
+    } else {
+      hipLaunchKernelGGL(k_phase_C<T>, dim3(G.nblk), dim3(NT), lds_c, h->cap_stream, G, B, j, -1, 0);
+    }
   }
   hipLaunchKernelGGL(k_advance, dim3(1), dim3(64), 0, h->cap_stream, G, B, h->unroll, h->d_flag);
   hipError_t e = hipStreamEndCapture(h->cap_stream, &h->graph);
@@ -252,6 +265,7 @@ hpcg_status build_graph(hpcg_ctx* h) {
   h->graph_unroll = h->unroll;
   h->graph_prec = h->prec;
   h->graph_bpl = G.bpl;
+  h->graph_form = B.form;
   h->graph_tol = B.tol;
   h->graph_maxit = B.maxit;
   return HPCG_OK;
@@ -262,14 +276,20 @@ hpcg_status run_graph(hpcg_ctx* h) {
   const Geom G = h->G;
   const Bufs B = h->B;
   if (!h->gexec || h->graph_unroll != h->unroll || h->graph_prec != h->prec || h->graph_tol != B.tol ||
-      h->graph_maxit != B.maxit || h->graph_bpl != G.bpl) {
+      h->graph_maxit != B.maxit || h->graph_bpl != G.bpl || h->graph_form != B.form) {
     hpcg_status s = build_graph<T>(h);
     if (s != HPCG_OK) return s;
   }
   __atomic_store_n(h->h_flag, 0, __ATOMIC_RELEASE);
   hipLaunchKernelGGL(k_reset, dim3(1), dim3(64), 0, h->stream, B, 1, h->d_flag);
-  hipLaunchKernelGGL(k_phase_B<T>, dim3(G.nblk), dim3(NT), restrict_lds_bytes(G), h->stream, G, B, 0, 0);
-  hipLaunchKernelGGL(k_phase_C<T>, dim3(G.nblk), dim3(NT), prolong_lds_bytes<T>(G), h->stream, G, B, 0, 0);
+  hipLaunchKernelGGL(k_phase_B<T>, dim3(G.nblk), dim3(NT), restrict_lds_bytes(G), h->stream, G, B, 0, 0, 0);
+  if (B.form == FORM_SQUARED) {
+    hipLaunchKernelGGL(k_phase_C<T>, dim3(G.nblk), dim3(NT), prolong_lds_bytes<T>(G), h->stream, G, B, 0, 0, 1);
+    hipLaunchKernelGGL(k_phase_B<T>, dim3(G.nblk), dim3(NT), restrict_lds_bytes(G), h->stream, G, B, 0, 0, 1);
+    hipLaunchKernelGGL(k_phase_C<T>, dim3(G.nblk), dim3(NT), prolong_lds_bytes<T>(G), h->stream, G, B, 0, 0, 2);
+  } else {
+    hipLaunchKernelGGL(k_phase_C<T>, dim3(G.nblk), dim3(NT), prolong_lds_bytes<T>(G), h->stream, G, B, 0, 0, 0);
+  }
   hpcg_status s = check_launch(h, "graph engine setup launch");
   if (s != HPCG_OK) return s;
   const int max_replays = (B.maxit + h->unroll - 1) / h->unroll;
@@ -331,7 +351,7 @@ hpcg_status run_resident(hpcg_ctx* h, bool& ran) {
   const Geom G = h->G;
   const Bufs B = h->B;
   const int items = G.B * G.K;
-  if (!h->coop || items > h->num_cu) return HPCG_OK;
+  if (!h->coop || items > h->num_cu || B.form != FORM_DIRECT) return HPCG_OK;
   const void* fn = resident_kernel<T>(G.levels);
   if (!fn) return HPCG_OK;
   const size_t dyn = ((size_t)h->max_leaf_nnz * 8 + (LEAF + 1) * 4 + 15) / 16 * 16 +
@@ -361,7 +381,7 @@ hpcg_status run_persistent(hpcg_ctx* h, bool& ran) {
   ran = false;
   const Geom G = h->G;
   const Bufs B = h->B;
-  if (!h->coop) return HPCG_OK;
+  if (!h->coop || B.form != FORM_DIRECT) return HPCG_OK;
   const size_t dyn = std::max(restrict_lds_bytes(G), prolong_lds_bytes<T>(G));
   const void* fn = reinterpret_cast<const void*>(&k_persistent<T>);
   hpcg_status s = allow_lds(h, fn, dyn);
@@ -474,6 +494,9 @@ hpcg_status hpcg_create(const hpcg_partition* part, const int32_t* d_row_ptr, co
   B.replays = reinterpret_cast<int*>(w + lay.ctl + kCtlReplays);
   B.bflag = reinterpret_cast<unsigned*>(w + lay.ctl + kCtlFlag);
   B.actr = reinterpret_cast<unsigned*>(w + lay.ctl + kCtlApplyCtr);
+  B.w = w + lay.w;
+  B.dinv = reinterpret_cast<const double*>(w + lay.dinv);
+  B.form = FORM_DIRECT;
   B.agen = reinterpret_cast<unsigned*>(w + lay.ctl + kCtlApplyGen);
   B.tol = 1e-6;
   B.maxit = 1000;
@@ -499,6 +522,9 @@ hpcg_status hpcg_create(const hpcg_partition* part, const int32_t* d_row_ptr, co
       if (cols[e] < lo || cols[e] >= hi)
         return cleanup_fail(fail(h, HPCG_ERR_SHAPE, "column index outside its system's block"));
   }
+  hipLaunchKernelGGL(k_diag_inv, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, h->stream, h->B.row_ptr, h->B.col,
+                     h->B.val, reinterpret_cast<double*>(h->ws + h->lay.dinv), (int)N, G.n);
+  CREATE_HIP(hipGetLastError());
 #undef CREATE_HIP
   for (size_t i0 = 0; i0 < N; i0 += LEAF)
     h->max_leaf_nnz = std::max(h->max_leaf_nnz, rp[i0 + LEAF] - rp[i0]);
@@ -512,7 +538,10 @@ hpcg_status hpcg_set_values(hpcg_handle h, const float* d_val) {
   if (h->nnz > 0 && !d_val) return fail(h, HPCG_ERR_INVALID_ARG, "d_val is NULL");
   if (h->nnz > 0)
     HIP_OR_FAIL(h, hipMemcpyAsync(h->ws + h->lay.val, d_val, (size_t)h->nnz * 4, hipMemcpyDeviceToDevice, h->stream));
-  return HPCG_OK;
+  const int N = h->G.B * h->G.n;
+  hipLaunchKernelGGL(k_diag_inv, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, h->stream, h->B.row_ptr, h->B.col,
+                     h->B.val, reinterpret_cast<double*>(h->ws + h->lay.dinv), N, h->G.n);
+  return check_launch(h, "diagonal launch");
 }
 
 hpcg_status hpcg_set_factors(hpcg_handle h, const float* d_leafU, const float* d_tileW, const float* d_gate) {
@@ -588,11 +617,33 @@ hpcg_status hpcg_set_factors_bridge(hpcg_handle h, const float* d_leafF, const f
   return HPCG_OK;
 }
 
+namespace {
+hpcg_status apply_H(hpcg_ctx* h, const float* d_r, float* d_y);
+}
+
 hpcg_status hpcg_apply_M(hpcg_handle h, const float* d_r, float* d_y) {
   if (!h) return fail(nullptr, HPCG_ERR_INVALID_ARG, "handle is NULL");
   if (!d_r || !d_y) return fail(h, HPCG_ERR_INVALID_ARG, "vector pointer is NULL");
   if (d_r == d_y) return fail(h, HPCG_ERR_INVALID_ARG, "d_r and d_y must not alias");
+  if (h->B.form == FORM_JACOBI) {
+    const int N = h->G.B * h->G.n;
+    hipLaunchKernelGGL(k_jacobi_apply, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, h->stream, d_r, h->B.dinv,
+                       d_y, N);
+    return check_launch(h, "hpcg_apply_M launch");
+  }
   if (!h->factors_set) return fail(h, HPCG_ERR_STATE, "hpcg_set_factors has not been called");
+  if (h->B.form == FORM_SQUARED) {
+    float* tmp = reinterpret_cast<float*>(h->ws + h->lay.ftmp);
+    hpcg_status s = apply_H(h, d_r, tmp);
+    if (s != HPCG_OK) return s;
+    return apply_H(h, tmp, d_y);
+  }
+  return apply_H(h, d_r, d_y);
+}
+
+namespace {
+// y = H r with the H-matrix factors (the apply paths of hpcg_apply_M).
+hpcg_status apply_H(hpcg_ctx* h, const float* d_r, float* d_y) {
   if (h->apply_path == HPCG_APPLY_FUSED) {
     bool ran = false;
     hpcg_status s = run_fused_apply(h, d_r, d_y, ran);
@@ -613,6 +664,7 @@ hpcg_status hpcg_apply_M(hpcg_handle h, const float* d_r, float* d_y) {
   hipLaunchKernelGGL(k_apply_prolong, dim3(G.nblk), dim3(NT), lds_p, h->stream, G, h->B, d_r, d_y);
   return check_launch(h, "hpcg_apply_M launch");
 }
+}  // namespace
 
 hpcg_status hpcg_spmv(hpcg_handle h, const float* d_x, float* d_y) {
   if (!h) return fail(nullptr, HPCG_ERR_INVALID_ARG, "handle is NULL");
@@ -659,6 +711,7 @@ hpcg_status hpcg_apply_M_block(hpcg_handle h, const float* d_R, float* d_Y, int3
   if ((reinterpret_cast<uintptr_t>(d_R) | reinterpret_cast<uintptr_t>(d_Y)) % 16)
     return fail(h, HPCG_ERR_INVALID_ARG, "d_R and d_Y must be 16-byte aligned");
   if (!h->factors_set) return fail(h, HPCG_ERR_STATE, "hpcg_set_factors has not been called");
+  if (h->B.form != FORM_DIRECT) return fail(h, HPCG_ERR_STATE, "the block apply runs the direct form (M = H) only");
   const size_t half = block_half_bytes(h, nrhs);
   if (h->G.levels > 0) {
     if (!d_work) return fail(h, HPCG_ERR_INVALID_ARG, "d_work is NULL");
@@ -740,7 +793,9 @@ hpcg_status solve_core(hpcg_ctx* h, const float* d_b, double* d_x, double tol, i
       s = f32 ? run_persistent<float>(h, ran) : run_persistent<double>(h, ran);
     if (s != HPCG_OK) return s;
     if (!ran && h->engine_opt == HPCG_ENGINE_PERSISTENT)
-      return fail(h, HPCG_ERR_SHAPE, "persistent engine: device does not support a co-resident grid for this partition");
+      return fail(h, HPCG_ERR_SHAPE, h->B.form != FORM_DIRECT
+                                         ? "persistent engines run the direct form only"
+                                         : "persistent engine: device does not support a co-resident grid for this partition");
     if (ran) h->last_engine = HPCG_ENGINE_PERSISTENT;
   }
   if (!ran) {
@@ -763,7 +818,8 @@ hpcg_status check_solve_args(hpcg_ctx* h, const float* d_b, double* d_x, double 
   if (!d_b || !d_x) return fail(h, HPCG_ERR_INVALID_ARG, "vector pointer is NULL");
   if (!(tol > 0.0) || !(tol < 1e300)) return fail(h, HPCG_ERR_INVALID_ARG, "tol must be positive and finite");
   if (maxit < 1) return fail(h, HPCG_ERR_INVALID_ARG, "maxit must be >= 1");
-  if (!h->factors_set) return fail(h, HPCG_ERR_STATE, "hpcg_set_factors has not been called");
+  if (!h->factors_set && h->B.form != FORM_JACOBI)
+    return fail(h, HPCG_ERR_STATE, "hpcg_set_factors has not been called");
   return HPCG_OK;
 }
 
@@ -773,8 +829,25 @@ hpcg_status hpcg_solve(hpcg_handle h, const float* d_b, double* d_x, double tol,
                        int32_t* h_iters, double* h_relres) {
   hpcg_status s = check_solve_args(h, d_b, d_x, tol, maxit);
   if (s != HPCG_OK) return s;
+  h->last_fallback = 0;
   s = solve_core(h, d_b, d_x, tol, maxit);
   if (s != HPCG_OK) return s;
+  if (h->fallback && h->B.form != FORM_JACOBI) {
+    bool broke = false;
+    for (int i = 0; i < h->G.B; ++i) broke |= (h->h_st[i].status == ST_BREAKDOWN);
+    if (broke) {
+      // the preconditioner is not SPD for some system: solve again with Jacobi
+      // (the persistent engines run the direct form only)
+      const int form = h->B.form, engine = h->engine_opt;
+      h->B.form = FORM_JACOBI;
+      if (engine == HPCG_ENGINE_PERSISTENT) h->engine_opt = HPCG_ENGINE_AUTO;
+      s = solve_core(h, d_b, d_x, tol, maxit);
+      h->B.form = form;
+      h->engine_opt = engine;
+      if (s != HPCG_OK) return s;
+      h->last_fallback = 1;
+    }
+  }
   bool any_break = false, any_nc = false;
   for (int i = 0; i < h->G.B; ++i) {
     const SysState& st = h->h_st[i];
@@ -863,6 +936,92 @@ hpcg_status hpcg_solve_refined(hpcg_handle h, const float* d_b, double* d_x, dou
   return HPCG_OK;
 }
 
+namespace {
+
+// Number of eigenvalues below x of the symmetric tridiagonal matrix with
+// diagonal a and off-diagonal b (Sturm sequence of the LDL^T pivots).
+int sturm_count(const std::vector<double>& a, const std::vector<double>& b, double x) {
+  int count = 0;
+  double d = 1.0;
+  for (size_t i = 0; i < a.size(); ++i) {
+    const double off = i ? b[i - 1] * b[i - 1] : 0.0;
+    d = a[i] - x - (i ? off / d : 0.0);
+    if (d == 0.0) d = -1e-300;
+    if (d < 0.0) ++count;
+  }
+  return count;
+}
+
+// k-th smallest eigenvalue (0-based) by bisection inside the Gershgorin interval.
+double tridiag_eig(const std::vector<double>& a, const std::vector<double>& b, int k) {
+  double lo = 0.0, hi = 0.0;
+  for (size_t i = 0; i < a.size(); ++i) {
+    const double r = (i ? std::fabs(b[i - 1]) : 0.0) + (i + 1 < a.size() ? std::fabs(b[i]) : 0.0);
+    lo = i ? std::min(lo, a[i] - r) : a[i] - r;
+    hi = i ? std::max(hi, a[i] + r) : a[i] + r;
+  }
+  for (int iter = 0; iter < 200 && hi - lo > 1e-15 * std::max(std::fabs(lo), std::fabs(hi)); ++iter) {
+    const double mid = 0.5 * (lo + hi);
+    if (sturm_count(a, b, mid) > k) hi = mid;
+    else lo = mid;
+  }
+  return 0.5 * (lo + hi);
+}
+
+}  // namespace
+
+hpcg_status hpcg_estimate_spectrum(hpcg_handle h, int32_t steps, double* h_lmin, double* h_lmax) {
+  if (!h) return fail(nullptr, HPCG_ERR_INVALID_ARG, "handle is NULL");
+  if (steps < 2 || steps > 200) return fail(h, HPCG_ERR_INVALID_ARG, "steps must lie in [2, 200]");
+  if (!h->factors_set) return fail(h, HPCG_ERR_STATE, "hpcg_set_factors has not been called");
+  const size_t N = (size_t)h->G.B * h->G.n;
+  float* d_in = reinterpret_cast<float*>(h->ws + h->lay.frhs);
+  float* d_out = reinterpret_cast<float*>(h->ws + h->lay.w);
+  std::vector<std::vector<double>> V;
+  std::vector<double> alpha, beta, v(N), w(N);
+  std::vector<float> buf(N);
+  // seeded start vector (xorshift, uniform in [-1, 1))
+  uint64_t st = 0x9e3779b97f4a7c15ULL;
+  double nrm = 0.0;
+  for (size_t i = 0; i < N; ++i) {
+    st ^= st << 13; st ^= st >> 7; st ^= st << 17;
+    v[i] = (double)(st >> 11) * (1.0 / 4503599627370496.0) - 1.0;
+    nrm += v[i] * v[i];
+  }
+  nrm = std::sqrt(nrm);
+  for (auto& e : v) e /= nrm;
+  for (int j = 0; j < steps; ++j) {
+    V.push_back(v);
+    for (size_t i = 0; i < N; ++i) buf[i] = (float)v[i];
+    HIP_OR_FAIL(h, hipMemcpyAsync(d_in, buf.data(), N * 4, hipMemcpyHostToDevice, h->stream));
+    hpcg_status s = apply_H(h, d_in, d_out);
+    if (s != HPCG_OK) return s;
+    HIP_OR_FAIL(h, hipMemcpyAsync(buf.data(), d_out, N * 4, hipMemcpyDeviceToHost, h->stream));
+    HIP_OR_FAIL(h, hipStreamSynchronize(h->stream));
+    for (size_t i = 0; i < N; ++i) w[i] = buf[i];
+    double a = 0.0;
+    for (size_t i = 0; i < N; ++i) a += w[i] * v[i];
+    alpha.push_back(a);
+    // full reorthogonalization against every Lanczos vector, twice
+    for (int pass = 0; pass < 2; ++pass)
+      for (const auto& u : V) {
+        double c = 0.0;
+        for (size_t i = 0; i < N; ++i) c += w[i] * u[i];
+        for (size_t i = 0; i < N; ++i) w[i] -= c * u[i];
+      }
+    double bn = 0.0;
+    for (size_t i = 0; i < N; ++i) bn += w[i] * w[i];
+    bn = std::sqrt(bn);
+    if (j + 1 == steps || bn <= 1e-12 * std::fabs(a)) break;
+    beta.push_back(bn);
+    for (size_t i = 0; i < N; ++i) v[i] = w[i] / bn;
+  }
+  beta.resize(alpha.size() > 0 ? alpha.size() - 1 : 0);
+  if (h_lmin) *h_lmin = tridiag_eig(alpha, beta, 0);
+  if (h_lmax) *h_lmax = tridiag_eig(alpha, beta, (int)alpha.size() - 1);
+  return HPCG_OK;
+}
+
 hpcg_status hpcg_last_solve_status(hpcg_handle h, int32_t* h_status) {
   if (!h) return fail(nullptr, HPCG_ERR_INVALID_ARG, "handle is NULL");
   if (!h_status) return fail(h, HPCG_ERR_INVALID_ARG, "h_status is NULL");
@@ -884,6 +1043,14 @@ hpcg_status hpcg_set_option(hpcg_handle h, int32_t option, int32_t value) {
     case HPCG_OPT_PRECISION:
       if (value != HPCG_PREC_VEC64 && value != HPCG_PREC_VEC32) return fail(h, HPCG_ERR_INVALID_ARG, "bad precision");
       h->prec = value;
+      return HPCG_OK;
+    case HPCG_OPT_FALLBACK:
+      if (value != 0 && value != 1) return fail(h, HPCG_ERR_INVALID_ARG, "fallback must be 0 or 1");
+      h->fallback = value;
+      return HPCG_OK;
+    case HPCG_OPT_FORM:
+      if (value < HPCG_FORM_DIRECT || value > HPCG_FORM_JACOBI) return fail(h, HPCG_ERR_INVALID_ARG, "bad form");
+      h->B.form = value;
       return HPCG_OK;
     case HPCG_OPT_APPLY_PATH:
       if (value < HPCG_APPLY_AUTO || value > HPCG_APPLY_FUSED) return fail(h, HPCG_ERR_INVALID_ARG, "bad apply path");
@@ -908,6 +1075,8 @@ hpcg_status hpcg_set_option(hpcg_handle h, int32_t option, int32_t value) {
 int32_t hpcg_last_engine(hpcg_handle h) { return h ? h->last_engine : 0; }
 
 int32_t hpcg_last_apply_path(hpcg_handle h) { return h ? h->last_apply_path : 0; }
+
+int32_t hpcg_last_fallback(hpcg_handle h) { return h ? h->last_fallback : 0; }
 
 hpcg_status hpcg_last_launch_info(hpcg_handle h, int32_t* grid, int32_t* lds_bytes) {
   if (!h) return fail(nullptr, HPCG_ERR_INVALID_ARG, "handle is NULL");

@@ -52,6 +52,9 @@ constexpr int MAX_LEVELS = 8;      // K <= 256 leaves per system
 
 enum : int { ST_RUNNING = 0, ST_CONVERGED = 1, ST_NOT_CONVERGED = 2, ST_BREAKDOWN = 3 };
 
+// Preconditioner forms: M = H (the H-matrix itself), M = H H, M = diag(A)^-1.
+enum : int { FORM_DIRECT = 0, FORM_SQUARED = 1, FORM_JACOBI = 2 };
+
 // `status` changes only in phase C (and at init): a breakdown found in phase A
 // or B is parked in `brk`/`brk_it` and turned into a status by the next phase C.
 // A breakdown is parked only when the scalar that every workgroup of the system
@@ -107,6 +110,9 @@ struct Bufs {
   int* abort_flag;     // set when a barrier wait exceeds its bound
   int* itbase;         // graph engine: absolute iteration of the replay's first step
   int* replays;        // graph engine: replays finished
+  void* w;             // [B*n] H r in the squared form
+  const double* dinv;  // [B*n] 1 / A_ii
+  int form;            // FORM_*
   double tol;
   int maxit;
 };
@@ -565,18 +571,31 @@ __device__ __forceinline__ T pdir(T z, T pold, double beta) {
 // ---------------------------------------------------------------------------
 
 // Phase B (and the initial restriction when it == 0: r = b, x = 0).
+// Phase B (and the initial restriction when it == 0: r = b, x = 0).  stage 1
+// (squared form only): restriction of w = H r for the second factor.
 template <typename T>
-__device__ __forceinline__ void phase_B(const Geom& G, const Bufs& B, int b, int it, Smem<T>& sm, float* dyn) {
+__device__ __forceinline__ void phase_B(const Geom& G, const Bufs& B, int b, int it, Smem<T>& sm, float* dyn,
+                                        int stage = 0) {
   const Blk bk = decode(G, b);
   const int tid = threadIdx.x;
   SysState* st = B.st + bk.s;
   const bool init = (it == 0);
+  if (stage == 1) {
+    issue_restrict_dma<T>(G, B, bk, dyn);
+    if (tid == 0) sm.flag = load_state(st);
+    if (tid < LEAF) sm.r[tid] = reinterpret_cast<const T*>(B.w)[bk.leaf0 + tid];
+    lds_dma_wait();
+    if (sm.flag != ST_RUNNING) return;
+    restrict_leaf(G, B, bk, dyn, sm);
+    return;
+  }
+  const bool restrict_r = (B.form != FORM_JACOBI);
   // every slot of a leaf reads the leaf's whole old r while each writes only
   // its own rows of the new r, so old and new live in different buffers
   const T* rold = r_buf<T>(G, B, it - 1);
   T* rnew = r_buf<T>(G, B, it);
   // ---- one batch of loads ----
-  issue_restrict_dma<T>(G, B, bk, dyn);
+  if (restrict_r) issue_restrict_dma<T>(G, B, bk, dyn);
   const double pqv = init ? 0.0 : load_partials(B.pq_part, bk.s, G.nblk_sys);
   int state = ST_RUNNING;
   double rzv = 0.0;
@@ -621,7 +640,7 @@ __device__ __forceinline__ void phase_B(const Geom& G, const Bufs& B, int b, int
     }
   }
   __syncthreads();
-  restrict_leaf(G, B, bk, dyn, sm);
+  if (restrict_r) restrict_leaf(G, B, bk, dyn, sm);
   const double rr = wg_sum<T>(loc, sm.dred);
   if (tid == 0) {
     B.rr_part[bk.item] = rr;
@@ -634,14 +653,38 @@ __device__ __forceinline__ void phase_B(const Geom& G, const Bufs& B, int b, int
   }
 }
 
+// stage 0: convergence test, z = M r, partial r.z (direct and Jacobi forms);
+// squared form: stage 1 = test and w = H r, stage 2 = z = H w and r.z.
 template <typename T>
-__device__ __forceinline__ void phase_C(const Geom& G, const Bufs& B, int b, int it, Smem<T>& sm, float* dyn) {
+__device__ __forceinline__ void phase_C(const Geom& G, const Bufs& B, int b, int it, Smem<T>& sm, float* dyn,
+                                        int stage = 0) {
   const Blk bk = decode(G, b);
   const int tid = threadIdx.x;
   SysState* st = B.st + bk.s;
   const bool lead = (tid == 0 && bk.lb == 0);
+  const bool jacobi = (B.form == FORM_JACOBI);
+  if (stage == 2) {
+    issue_prolong_dma<T>(G, B, bk, dyn, sm);
+    if (tid == 0) sm.flag = load_state(st);
+    T rv = 0;
+    if (tid < G.RB) {
+      rv = r_buf<T>(G, B, it)[bk.grow0 + tid];
+      sm.r[tid] = reinterpret_cast<const T*>(B.w)[bk.grow0 + tid];   // the vector H is applied to
+    }
+    lds_dma_wait();
+    if (sm.flag != ST_RUNNING) return;
+    const T zv = prolong_rows(G, B, bk, dyn, sm);
+    double loc = 0.0;
+    if (tid < G.RB) {
+      reinterpret_cast<T*>(B.z)[bk.grow0 + tid] = zv;
+      loc = (double)rv * (double)zv;
+    }
+    const double rz = wg_sum<T>(loc, sm.dred);
+    if (tid == 0) B.rz_part[bk.item] = rz;
+    return;
+  }
   // ---- one batch of loads ----
-  issue_prolong_dma<T>(G, B, bk, dyn, sm);
+  if (!jacobi) issue_prolong_dma<T>(G, B, bk, dyn, sm);
   const double rrv = load_partials(B.rr_part, bk.s, G.nblk_sys);
   int state = ST_RUNNING;
   double bnorm = 0.0;
@@ -680,7 +723,22 @@ __device__ __forceinline__ void phase_C(const Geom& G, const Bufs& B, int b, int
       return;
     }
   }
+  if (jacobi) {
+    double loc = 0.0;
+    if (tid < G.RB) {
+      const T zv = (T)((double)sm.r[tid] * B.dinv[bk.grow0 + tid]);
+      reinterpret_cast<T*>(B.z)[bk.grow0 + tid] = zv;
+      loc = (double)sm.r[tid] * (double)zv;
+    }
+    const double rz = wg_sum<T>(loc, sm.dred);
+    if (tid == 0) B.rz_part[bk.item] = rz;
+    return;
+  }
   const T zv = prolong_rows(G, B, bk, dyn, sm);
+  if (stage == 1) {                       // squared form: w = H r, no partial yet
+    if (tid < G.RB) reinterpret_cast<T*>(B.w)[bk.grow0 + tid] = zv;
+    return;
+  }
   double loc = 0.0;
   if (tid < G.RB) {
     reinterpret_cast<T*>(B.z)[bk.grow0 + tid] = zv;

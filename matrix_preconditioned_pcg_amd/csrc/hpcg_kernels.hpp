@@ -94,19 +94,19 @@ __global__ __launch_bounds__(NT) void k_phase_A(Geom G, Bufs B, int off) {
 
 // absolute >= 0 selects a fixed iteration (0 = initial restriction of b).
 template <typename T>
-__global__ __launch_bounds__(NT) void k_phase_B(Geom G, Bufs B, int off, int absolute) {
+__global__ __launch_bounds__(NT) void k_phase_B(Geom G, Bufs B, int off, int absolute, int stage) {
   __shared__ Smem<T> sm;
   extern __shared__ float4 dyn4[];
   const int it = absolute >= 0 ? absolute : *B.itbase + off;
-  phase_B(G, B, blockIdx.x, it, sm, reinterpret_cast<float*>(dyn4));
+  phase_B(G, B, blockIdx.x, it, sm, reinterpret_cast<float*>(dyn4), stage);
 }
 
 template <typename T>
-__global__ __launch_bounds__(NT) void k_phase_C(Geom G, Bufs B, int off, int absolute) {
+__global__ __launch_bounds__(NT) void k_phase_C(Geom G, Bufs B, int off, int absolute, int stage) {
   __shared__ Smem<T> sm;
   extern __shared__ float4 dyn4[];
   const int it = absolute >= 0 ? absolute : *B.itbase + off;
-  phase_C(G, B, blockIdx.x, it, sm, reinterpret_cast<float*>(dyn4));
+  phase_C(G, B, blockIdx.x, it, sm, reinterpret_cast<float*>(dyn4), stage);
 }
 
 // End of a replay: advance the iteration base and publish (replay count, all
@@ -291,6 +291,25 @@ __global__ void k_add_scaled(double* __restrict__ x, const double* __restrict__ 
                              int n, int N) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < N) x[i] = fma(scale[i / n], d[i], x[i]);
+}
+
+// dinv_i = 1 / A_ii (0 for a row without a stored diagonal).
+__global__ void k_diag_inv(const int* __restrict__ row_ptr, const int* __restrict__ col,
+                           const float* __restrict__ val, double* __restrict__ dinv, int nrows, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nrows) return;
+  double d = 0.0;
+  for (int e = row_ptr[i]; e < row_ptr[i + 1]; ++e)
+    if (col[e] == i) d = (double)val[e];
+  (void)n;
+  dinv[i] = d != 0.0 ? 1.0 / d : 0.0;
+}
+
+// y = diag(A)^-1 r (fp32 in and out).
+__global__ void k_jacobi_apply(const float* __restrict__ r, const double* __restrict__ dinv, float* __restrict__ y,
+                               int nrows) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nrows) y[i] = (float)((double)r[i] * dinv[i]);
 }
 
 __global__ void k_copy_x(const double* __restrict__ src, double* __restrict__ dst, int n) {

@@ -45,6 +45,14 @@ HPCG_OPT_PRECISION = 4
 HPCG_OPT_LEAF_SPLIT = 8
 HPCG_OPT_APPLY_PATH = 16
 
+HPCG_OPT_FORM = 32
+
+HPCG_OPT_FALLBACK = 64
+
+HPCG_FORM_DIRECT = 0
+HPCG_FORM_SQUARED = 1
+HPCG_FORM_JACOBI = 2
+
 HPCG_APPLY_AUTO = 0
 HPCG_APPLY_STREAMING = 1
 HPCG_APPLY_FUSED = 2
@@ -101,6 +109,8 @@ def lib() -> ctypes.CDLL:
         "hpcg_set_option": (i32, [vp, i32, i32]),
         "hpcg_last_engine": (i32, [vp]),
         "hpcg_last_apply_path": (i32, [vp]),
+        "hpcg_last_fallback": (i32, [vp]),
+        "hpcg_estimate_spectrum": (i32, [vp, i32, P(dbl), P(dbl)]),
         "hpcg_last_launch_info": (i32, [vp, P(i32), P(i32)]),
         "hpcg_status_string": (ctypes.c_char_p, [i32]),
         "hpcg_last_error": (ctypes.c_char_p, [vp]),
@@ -281,6 +291,17 @@ def hpcg_last_engine(h) -> int:
     return int(lib().hpcg_last_engine(h))
 
 
+def hpcg_last_fallback(h) -> int:
+    return int(lib().hpcg_last_fallback(h))
+
+
+def hpcg_estimate_spectrum(h, steps: int = 40) -> tuple:
+    """(lambda_min, lambda_max) Lanczos estimates for H, the factor operator."""
+    lo, hi = ctypes.c_double(), ctypes.c_double()
+    _check(lib().hpcg_estimate_spectrum(h, int(steps), ctypes.byref(lo), ctypes.byref(hi)), h)
+    return lo.value, hi.value
+
+
 def hpcg_last_apply_path(h) -> int:
     return int(lib().hpcg_last_apply_path(h))
 
@@ -424,6 +445,13 @@ class Solver:
         st, iters, outer, rel = hpcg_solve_refined(self.handle, self.part, b, x, tol, maxit, inner_tol, max_outer)
         sys_st = hpcg_last_solve_status(self.handle, self.batch)
         return SolveResult(x.reshape(self.batch, self.n), iters, rel, st, sys_st), outer
+
+    def estimate_spectrum(self, steps: int = 40) -> tuple:
+        return hpcg_estimate_spectrum(self.handle, steps)
+
+    @property
+    def last_fallback(self) -> int:
+        return hpcg_last_fallback(self.handle)
 
     @property
     def last_engine(self) -> int:

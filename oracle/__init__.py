@@ -13,6 +13,7 @@ Modules
   sparse   CSR matrix-vector product and the true residual
   pcg      preconditioned conjugate gradients
   bridge   the pages' bridge-and-core off-diagonal format and its apply
+  forms    M = H H, M = diag(A)^-1, the lambda_min(H) monitor, Jacobi fallback
 
 Every function in this package is pinned by a CPU test against something other
 than itself (printed values, closed forms, library routines, brute force).
@@ -37,4 +38,11 @@ from .bridge import (  # noqa: F401
     pack_bridge,
     weyl_lower_bound_bridge,
     core_count,
+)
+from .forms import (  # noqa: F401
+    apply_M_squared,
+    apply_jacobi,
+    diag_of,
+    h_extreme_eigenvalues,
+    pcg_with_fallback,
 )

@@ -1,0 +1,232 @@
+"""GPU parity of the other preconditioner forms through the C ABI: M = H H
+(two structured applies per product), M = diag(A)^-1 (Jacobi), the Lanczos
+monitor of lambda_min(H), and the Jacobi fallback after a breakdown.
+
+References are the oracle's squared and Jacobi applies, its PCG with the same
+preconditioner, its dense eigenvalues of H, and its fallback loop.  Bars: 1e-5
+relative per apply (elementwise against |H| (|H| |r|)), iteration counts within
+2, true residual within 1.05 tol, the Lanczos extremes inside the exact
+spectrum up to the fp32 apply's rounding and within 1e-3 of it after 120 steps.
+Factors are the seeded random ones and the SVD-fitted ones (A^{-1/2} for the
+squared form, A^{-1} for the direct form)."""
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from workloads import make_config  # noqa: E402
+from workloads.fitted import fitted_batch  # noqa: E402
+
+from matrix_preconditioned_pcg_amd import hpcg  # noqa: E402
+
+TOL = 1e-5
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _solver(b, factors=True):
+    s = hpcg.Solver(b.n, b.row_ptr, b.col, b.val, batch=b.batch, levels=b.levels)
+    if factors:
+        s.set_factors(b.U, b.W, b.g)
+    return s
+
+
+@pytest.mark.parametrize("name,batch", [("N1k", None), ("N8k", None), ("tet4k", None), ("batch64x2k", 4)])
+def test_squared_apply_parity(name, batch):
+    b = make_config(name, batch=batch)
+    _log(f"squared apply {name}")
+    s = _solver(b)
+    s.set_option(hpcg.HPCG_OPT_FORM, hpcg.HPCG_FORM_SQUARED)
+    r = np.random.default_rng(31).standard_normal((b.batch, b.n)).astype(np.float32)
+    y = s.apply_M(r.reshape(-1)).cpu().numpy().astype(np.float64).reshape(b.batch, b.n)
+    for i in range(b.batch):
+        sy = b.system(i)
+        ref = oracle.apply_M_squared(sy.U, sy.W, sy.g, r[i])
+        aU, aW, ag = np.abs(sy.U), np.abs(sy.W), np.abs(sy.g)
+        mag = oracle.apply_M_squared(aU, aW, ag, np.abs(r[i]))
+        assert np.linalg.norm(y[i] - ref) <= TOL * np.linalg.norm(ref)
+        assert not (np.abs(y[i] - ref) > TOL * mag + 1e-30).any()
+    s.close()
+
+
+@pytest.mark.parametrize("name,batch", [("N8k", None), ("batch64x2k", 4)])
+def test_jacobi_apply_parity(name, batch):
+    b = make_config(name, batch=batch)
+    _log(f"jacobi apply {name}")
+    s = _solver(b, factors=False)
+    s.set_option(hpcg.HPCG_OPT_FORM, hpcg.HPCG_FORM_JACOBI)
+    r = np.random.default_rng(32).standard_normal((b.batch, b.n)).astype(np.float32)
+    y = s.apply_M(r.reshape(-1)).cpu().numpy().astype(np.float64).reshape(b.batch, b.n)
+    for i in range(b.batch):
+        sy = b.system(i)
+        ref = oracle.apply_jacobi(oracle.diag_of(sy.row_ptr, sy.col, sy.val), r[i])
+        np.testing.assert_allclose(y[i], ref, rtol=2e-7, atol=0)
+    s.close()
+
+
+def _oracle_precond(sy, form):
+    if form == hpcg.HPCG_FORM_SQUARED:
+        return lambda v: oracle.apply_M_squared(sy.U, sy.W, sy.g, v)
+    if form == hpcg.HPCG_FORM_JACOBI:
+        d = oracle.diag_of(sy.row_ptr, sy.col, sy.val)
+        return lambda v: oracle.apply_jacobi(d, v)
+    return (sy.U, sy.W, sy.g)
+
+
+def _check_solve(b, s, form, engine=hpcg.HPCG_ENGINE_AUTO, prec=None, systems=None):
+    s.set_option(hpcg.HPCG_OPT_FORM, form)
+    s.set_option(hpcg.HPCG_OPT_ENGINE, engine)
+    if prec is not None:
+        s.set_option(hpcg.HPCG_OPT_PRECISION, prec)
+    res = s.solve(b.b.reshape(-1), tol=b.tol, maxit=b.maxit)
+    assert res.status == hpcg.HPCG_OK, (res.status, hpcg.hpcg_last_error(s.handle))
+    for i in (range(b.batch) if systems is None else systems):
+        sy = b.system(i)
+        ref = oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b, _oracle_precond(sy, form), b.tol, b.maxit)
+        assert ref.status == "converged"
+        assert abs(res.iterations[i] - ref.iterations) <= 2, (i, res.iterations[i], ref.iterations)
+        tr = oracle.true_relres(sy.row_ptr, sy.col, sy.val, sy.b, res.x[i].cpu().numpy())
+        assert res.relres[i] <= b.tol and tr <= 1.05 * b.tol, (i, res.relres[i], tr)
+    return res
+
+
+@pytest.mark.parametrize("prec", [hpcg.HPCG_PREC_VEC64, hpcg.HPCG_PREC_VEC32])
+@pytest.mark.parametrize("form", [hpcg.HPCG_FORM_SQUARED, hpcg.HPCG_FORM_JACOBI])
+@pytest.mark.parametrize("name,batch", [("N1k", None), ("N8k", None), ("batch64x2k", 3)])
+def test_form_solve_parity(name, batch, form, prec):
+    b = make_config(name, batch=batch)
+    _log(f"form solve {name} form={form} prec={prec}")
+    s = _solver(b, factors=form != hpcg.HPCG_FORM_JACOBI)
+    _check_solve(b, s, form, prec=prec)
+    assert s.last_engine == hpcg.HPCG_ENGINE_GRAPH
+    s.close()
+
+
+@pytest.mark.parametrize("name", ["N1k", "tet4k"])
+def test_fitted_factors_solve(name):
+    b = make_config(name)
+    _log(f"fitted factors {name}")
+    for power, form in ((-0.5, hpcg.HPCG_FORM_SQUARED), (-1.0, hpcg.HPCG_FORM_DIRECT)):
+        f = fitted_batch(b, power)
+        s = _solver(f)
+        res = _check_solve(f, s, form)
+        assert res.iterations[0] <= 20, res.iterations
+        s.close()
+
+
+def test_switching_forms_between_solves():
+    # the graph engine keeps one recorded graph; a change of form must re-record it
+    b = make_config("N1k")
+    _log("form switching N1k")
+    s = _solver(b)
+    for form in (hpcg.HPCG_FORM_DIRECT, hpcg.HPCG_FORM_SQUARED, hpcg.HPCG_FORM_JACOBI, hpcg.HPCG_FORM_DIRECT):
+        _check_solve(b, s, form, engine=hpcg.HPCG_ENGINE_GRAPH)
+    s.close()
+
+
+@pytest.mark.parametrize("name", ["N1k", "N8k"])
+def test_spectrum_monitor(name):
+    b = make_config(name)
+    _log(f"spectrum monitor {name}")
+    s = _solver(b)
+    s.set_option(hpcg.HPCG_OPT_FORM, hpcg.HPCG_FORM_SQUARED)    # the monitor looks at H regardless
+    lo, hi = s.estimate_spectrum(120)
+    sy = b.system(0)
+    if b.n <= 2048:
+        elo, ehi = oracle.h_extreme_eigenvalues(sy.U, sy.W, sy.g)
+        slack = 1e-5 * ehi
+        assert elo - slack <= lo <= elo + 1e-3 * abs(elo), (lo, elo)
+        assert ehi - 1e-4 * ehi <= hi <= ehi + slack, (hi, ehi)
+    else:
+        # no dense H: the Weyl certificate bounds lambda_min from below, and
+        # lambda_max is at least the largest Rayleigh quotient on unit vectors
+        assert lo >= oracle.weyl_lower_bound(sy.U, sy.W, sy.g) - 1e-5 * hi
+        e = np.zeros(b.n)
+        e[0] = 1.0
+        assert hi >= oracle.apply_M(sy.U, sy.W, sy.g, e)[0] * (1 - 1e-5)
+    s.close()
+
+
+def _indefinite(b):
+    g = b.g.copy()
+    g[:, ::2] = -2.0                      # H indefinite, still nonsingular
+    return g
+
+
+def test_monitor_sees_indefinite_H():
+    b = make_config("N1k")
+    _log("monitor on indefinite H")
+    g = _indefinite(b)
+    s = hpcg.Solver(b.n, b.row_ptr, b.col, b.val, levels=b.levels)
+    s.set_factors(b.U, b.W, g)
+    lo, hi = s.estimate_spectrum(60)
+    elo, ehi = oracle.h_extreme_eigenvalues(b.U[0], b.W[0], g[0])
+    assert elo < 0 and lo < 0 and lo >= elo - 1e-5 * ehi
+    # the squared form of the same H is SPD and converges
+    s.set_option(hpcg.HPCG_OPT_FORM, hpcg.HPCG_FORM_SQUARED)
+    res = s.solve(b.b.reshape(-1), tol=b.tol, maxit=b.maxit)
+    sy = b.system(0)
+    ref = oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b, lambda v: oracle.apply_M_squared(sy.U, sy.W, g[0], v),
+                     b.tol, b.maxit)
+    assert res.status == hpcg.HPCG_OK and ref.status == "converged"
+    assert abs(res.iterations[0] - ref.iterations) <= 2, (res.iterations, ref.iterations)
+    s.close()
+
+
+@pytest.mark.parametrize("engine", [hpcg.HPCG_ENGINE_AUTO, hpcg.HPCG_ENGINE_GRAPH, hpcg.HPCG_ENGINE_PERSISTENT])
+def test_jacobi_fallback(engine):
+    b = make_config("N1k")
+    _log(f"fallback engine={engine}")
+    sy = b.system(0)
+    U = np.zeros_like(b.U)
+    W = np.zeros_like(b.W)
+    g = -np.abs(b.g) - 1.0                # H = diag(g) < 0: breakdown at once
+    s = hpcg.Solver(b.n, b.row_ptr, b.col, b.val, levels=b.levels)
+    s.set_factors(U, W, g)
+    s.set_option(hpcg.HPCG_OPT_ENGINE, engine)
+    res = s.solve(b.b.reshape(-1), tol=b.tol, maxit=b.maxit)
+    assert res.status == hpcg.HPCG_ERR_BREAKDOWN and res.system_status == [hpcg.HPCG_SYS_BREAKDOWN]
+    assert s.last_fallback == 0
+    s.set_option(hpcg.HPCG_OPT_FALLBACK, 1)
+    res = s.solve(b.b.reshape(-1), tol=b.tol, maxit=b.maxit)
+    assert res.status == hpcg.HPCG_OK and s.last_fallback == 1
+    ref, fell = oracle.pcg_with_fallback(sy.row_ptr, sy.col, sy.val, sy.b, (U[0], W[0], g[0]), b.tol, b.maxit)
+    assert fell and ref.status == "converged"
+    assert abs(res.iterations[0] - ref.iterations) <= 2, (res.iterations, ref.iterations)
+    tr = oracle.true_relres(sy.row_ptr, sy.col, sy.val, sy.b, res.x[0].cpu().numpy())
+    assert tr <= 1.05 * b.tol
+    # a healthy preconditioner does not fall back
+    s.set_factors(b.U, b.W, b.g)
+    res = s.solve(b.b.reshape(-1), tol=b.tol, maxit=b.maxit)
+    assert res.status == hpcg.HPCG_OK and s.last_fallback == 0
+    s.close()
+
+
+def test_form_argument_errors():
+    b = make_config("N1k")
+    s = _solver(b, factors=False)
+    with pytest.raises(hpcg.HPCGError):
+        s.set_option(hpcg.HPCG_OPT_FORM, 3)
+    with pytest.raises(hpcg.HPCGError):
+        s.set_option(hpcg.HPCG_OPT_FALLBACK, 2)
+    with pytest.raises(hpcg.HPCGError):
+        s.apply_M(np.ones(b.n, np.float32))                 # direct form without factors
+    with pytest.raises(hpcg.HPCGError):
+        s.estimate_spectrum(40)                             # monitor without factors
+    s.set_factors(b.U, b.W, b.g)
+    for steps in (1, 201):
+        with pytest.raises(hpcg.HPCGError):
+            s.estimate_spectrum(steps)
+    s.set_option(hpcg.HPCG_OPT_FORM, hpcg.HPCG_FORM_SQUARED)
+    s.set_option(hpcg.HPCG_OPT_ENGINE, hpcg.HPCG_ENGINE_PERSISTENT)
+    with pytest.raises(hpcg.HPCGError):
+        s.solve(b.b.reshape(-1), tol=b.tol, maxit=b.maxit)
+    with pytest.raises(hpcg.HPCGError):
+        s.apply_M_block(np.zeros((b.n, 16), np.float32), 16)
+    s.close()
