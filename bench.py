@@ -55,7 +55,7 @@ def spmv_bytes(n: int, nnz: int, B: int = 1) -> int:
 
 
 # sources of the single-vector apply and SpMV kernels and of their launch code
-APPLY_SPMV_SOURCES = ("hpcg_device.hpp", "hpcg_kernels.hpp", "hpcg.hip")
+APPLY_SPMV_SOURCES = ("hpcg_device.hpp", "hpcg_kernels.hpp", "hpcg_resident.hpp", "hpcg.hip")
 
 
 def kernel_source_digest() -> str:
@@ -175,7 +175,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-others", action="store_true", help="skip ms/solve of the other workloads")
     ap.add_argument("--no-block", action="store_true", help="skip the block (probe) apply timing")
-    ap.add_argument("--no-fused", action="store_true", help="skip the single-launch (cooperative) apply timing")
+    ap.add_argument("--no-fused", action="store_true", help="skip the forced single-launch apply timing")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run three 256 MiB device-to-device copies (calibrates HBM byte counters)")
     args = ap.parse_args(argv)
@@ -213,12 +213,16 @@ def main(argv=None):
             apply()
         ab = apply_bytes(batch.n, batch.K, batch.levels, batch.batch)
         sb = spmv_bytes(batch.n, batch.nnz, batch.batch)
-        fused_us = None
-        if not args.no_fused and batch.batch * batch.K <= 256:
-            # the single-launch apply (reads every factor byte once) for comparison
-            solver.set_option(hpcg.HPCG_OPT_APPLY_PATH, hpcg.HPCG_APPLY_FUSED)
+        fused_us = streaming_us = None
+        if not args.no_fused:
+            # both apply paths forced, for comparison with what AUTO picks
+            solver.set_option(hpcg.HPCG_OPT_APPLY_PATH, hpcg.HPCG_APPLY_STREAMING)
             with torch.cuda.stream(stream):
-                fused_us = time_graph(apply, args.reps, stream, torch)
+                streaming_us = time_graph(apply, args.reps, stream, torch)
+            if batch.batch * batch.K <= 256:
+                solver.set_option(hpcg.HPCG_OPT_APPLY_PATH, hpcg.HPCG_APPLY_FUSED)
+                with torch.cuda.stream(stream):
+                    fused_us = time_graph(apply, args.reps, stream, torch)
             solver.set_option(hpcg.HPCG_OPT_APPLY_PATH, hpcg.HPCG_APPLY_AUTO)
         with torch.cuda.stream(stream):
             apply()
@@ -229,7 +233,8 @@ def main(argv=None):
                    "spmv_us": time_graph(spmv, args.reps, stream, torch),
                    "pair_us": time_graph(pair, args.reps, stream, torch)}
             out["apply_us_eager"], _ = time_calls(apply, args.reps, stream, torch)
-        out.update(apply_path=path, apply_fused_us=fused_us, apply_bytes=ab, spmv_bytes=sb,
+        out.update(apply_path=path, apply_fused_us=fused_us, apply_streaming_us=streaming_us,
+                   apply_bytes=ab, spmv_bytes=sb,
                    apply_gbs=ab / out["apply_us"] / 1e3, spmv_gbs=sb / out["spmv_us"] / 1e3,
                    pair_gbs=(ab + sb) / out["pair_us"] / 1e3)
         out["pair_frac"] = out["pair_gbs"] / HBM_PEAK_GBS
@@ -389,6 +394,8 @@ def main(argv=None):
         "apply_spmv_us": round(main_out["pair_us"], 3),
         "apply_us_eager": round(main_out["apply_us_eager"], 3),
         "apply_fused_us": None if main_out["apply_fused_us"] is None else round(main_out["apply_fused_us"], 3),
+        "apply_streaming_us": (None if main_out["apply_streaming_us"] is None
+                               else round(main_out["apply_streaming_us"], 3)),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),
@@ -396,7 +403,7 @@ def main(argv=None):
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_record(args.config),
-            "kernel": ("M-apply (k_apply_fused: one cooperative launch)" if main_out["apply_path"] == "fused"
+            "kernel": ("M-apply (k_apply_fused: one launch, factors read once)" if main_out["apply_path"] == "fused"
                        else "M-apply (k_apply_restrict + k_apply_prolong)")
                       + " + CSR SpMV (k_spmv), pairs graph-replayed back to back on the library stream",
             "algorithmic_bytes": ab + sb,

@@ -100,7 +100,7 @@ typedef enum {
                                    of the batch gets a CU, else graph            */
     HPCG_ENGINE_GRAPH = 1,      /* per-phase kernels, unrolled iterations replayed
                                    as one hipGraph, host polls a pinned flag      */
-    HPCG_ENGINE_PERSISTENT = 2  /* one cooperative launch runs the whole solve with
+    HPCG_ENGINE_PERSISTENT = 2  /* one launch runs the whole solve with
                                    device-wide barriers between phases: one
                                    512-thread workgroup per leaf with the factors
                                    in VGPRs when B*K <= #CUs (two barriers per
@@ -145,13 +145,14 @@ typedef enum {
 
 /* How hpcg_apply_M runs (hpcg_set_option(HPCG_OPT_APPLY_PATH, ...)).
  * STREAMING: two launches (restriction, then prolongation), any batch size;
- * the prolongation reads the level slabs a second time.  FUSED: one
- * cooperative launch in which the workgroup of each leaf keeps U_k and its
- * slabs in registers from the restriction to the prolongation, across one
- * device-wide barrier, so every factor byte is read once; needs one compute
- * unit per leaf of the batch (HPCG_ERR_SHAPE otherwise).  A cooperative launch
- * costs far more than it saves for a single apply on this hardware (about 25 us
- * against 10 us at n = 8192), so AUTO (default) means STREAMING. */
+ * the prolongation reads the level slabs a second time.  FUSED: one launch in
+ * which the 512-thread workgroup of each leaf keeps U_k and its slabs in
+ * registers from the restriction to the prolongation, across one device-wide
+ * barrier, so every factor byte is read once; needs every workgroup of the
+ * batch resident at once, one per compute unit (HPCG_ERR_SHAPE otherwise).
+ * The barrier's wait is bounded (about a second): should other work hold the
+ * compute units that long, the apply gives up and its output is undefined.
+ * AUTO (default): FUSED where it fits, else STREAMING. */
 typedef enum {
     HPCG_APPLY_AUTO = 0,
     HPCG_APPLY_STREAMING = 1,

@@ -152,7 +152,6 @@ struct hpcg_ctx {
   int prec = HPCG_PREC_VEC64;
   int last_engine = 0;
   int num_cu = 0;
-  int coop = 0;
   size_t max_lds = 0;
   hipGraph_t graph = nullptr;
   hipGraphExec_t gexec = nullptr;
@@ -351,7 +350,7 @@ hpcg_status run_resident(hpcg_ctx* h, bool& ran) {
   const Geom G = h->G;
   const Bufs B = h->B;
   const int items = G.B * G.K;
-  if (!h->coop || items > h->num_cu || B.form != FORM_DIRECT) return HPCG_OK;
+  if (items > h->num_cu || B.form != FORM_DIRECT) return HPCG_OK;
   const void* fn = resident_kernel<T>(G.levels);
   if (!fn) return HPCG_OK;
   const size_t dyn = ((size_t)h->max_leaf_nnz * 8 + (LEAF + 1) * 4 + 15) / 16 * 16 +
@@ -367,21 +366,21 @@ hpcg_status run_resident(hpcg_ctx* h, bool& ran) {
   Bufs Ba = B;
   int mln = h->max_leaf_nnz;
   void* args[] = {&Ga, &Ba, &mln};
-  HIP_OR_FAIL(h, hipLaunchCooperativeKernel(fn, dim3(items), dim3(NTR), args, (unsigned)dyn, h->stream));
+  HIP_OR_FAIL(h, hipLaunchKernel(fn, dim3(items), dim3(NTR), args, (unsigned)dyn, h->stream));
   h->last_grid = items;
   h->last_lds = (int)dyn;
   ran = true;
   return HPCG_OK;
 }
 
-// One cooperative launch for the whole solve; the grid is as many workgroups
-// as can be co-resident (at most one per (leaf, slot) item).
+// One launch for the whole solve; the grid is as many workgroups as can be
+// co-resident (at most one per (leaf, slot) item), per the occupancy query.
 template <typename T>
 hpcg_status run_persistent(hpcg_ctx* h, bool& ran) {
   ran = false;
   const Geom G = h->G;
   const Bufs B = h->B;
-  if (!h->coop || B.form != FORM_DIRECT) return HPCG_OK;
+  if (B.form != FORM_DIRECT) return HPCG_OK;
   const size_t dyn = std::max(restrict_lds_bytes(G), prolong_lds_bytes<T>(G));
   const void* fn = reinterpret_cast<const void*>(&k_persistent<T>);
   hpcg_status s = allow_lds(h, fn, dyn);
@@ -395,7 +394,7 @@ hpcg_status run_persistent(hpcg_ctx* h, bool& ran) {
   Geom Ga = G;
   Bufs Ba = B;
   void* args[] = {&Ga, &Ba};
-  HIP_OR_FAIL(h, hipLaunchCooperativeKernel(fn, dim3(grid), dim3(NT), args, (unsigned)dyn, h->stream));
+  HIP_OR_FAIL(h, hipLaunchKernel(fn, dim3(grid), dim3(NT), args, (unsigned)dyn, h->stream));
   h->last_grid = grid;
   h->last_lds = (int)dyn;
   ran = true;
@@ -457,9 +456,6 @@ hpcg_status hpcg_create(const hpcg_partition* part, const int32_t* d_row_ptr, co
   int max_lds = 0;
   CREATE_HIP(hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev));
   h->max_lds = max_lds > 0 ? (size_t)max_lds : 65536;
-  int coop = 0;
-  CREATE_HIP(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev));
-  h->coop = coop;
   CREATE_HIP(hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking));
   CREATE_HIP(hipHostMalloc(reinterpret_cast<void**>(&h->h_flag), 256, hipHostMallocMapped));
   CREATE_HIP(hipHostGetDevicePointer(reinterpret_cast<void**>(&h->d_flag), h->h_flag, 0));
@@ -573,13 +569,17 @@ const void* fused_apply_kernel(int levels) {
   }
 }
 
-// Single cooperative launch of the apply when every leaf gets its own CU;
-// ran = false when it does not fit (the caller then uses the two launches).
+// Single launch of the apply when every leaf gets its own CU (one 512-thread
+// workgroup per leaf, the occupancy query confirming that all of them fit at
+// once); ran = false when it does not fit (the caller then uses the two
+// launches).  An ordinary launch: the one device-wide barrier inside waits for
+// workgroups that the hardware dispatches as soon as resources free up, and
+// its wait is bounded.
 hpcg_status run_fused_apply(hpcg_ctx* h, const float* d_r, float* d_y, bool& ran) {
   ran = false;
   const Geom G = h->G;
   const int items = G.B * G.K;
-  if (!h->coop || items > h->num_cu) return HPCG_OK;
+  if (items > h->num_cu) return HPCG_OK;
   const void* fn = fused_apply_kernel(G.levels);
   if (!fn) return HPCG_OK;
   const size_t dyn = (size_t)std::max(G.K - 1, 1) * RANK * sizeof(float);
@@ -594,7 +594,7 @@ hpcg_status run_fused_apply(hpcg_ctx* h, const float* d_r, float* d_y, bool& ran
   const float* ra = d_r;
   float* ya = d_y;
   void* args[] = {&Ga, &Ba, &ra, &ya};
-  HIP_OR_FAIL(h, hipLaunchCooperativeKernel(fn, dim3(items), dim3(NTR), args, (unsigned)dyn, h->stream));
+  HIP_OR_FAIL(h, hipLaunchKernel(fn, dim3(items), dim3(NTR), args, (unsigned)dyn, h->stream));
   ran = true;
   return HPCG_OK;
 }
@@ -644,7 +644,7 @@ hpcg_status hpcg_apply_M(hpcg_handle h, const float* d_r, float* d_y) {
 namespace {
 // y = H r with the H-matrix factors (the apply paths of hpcg_apply_M).
 hpcg_status apply_H(hpcg_ctx* h, const float* d_r, float* d_y) {
-  if (h->apply_path == HPCG_APPLY_FUSED) {
+  if (h->apply_path != HPCG_APPLY_STREAMING) {
     bool ran = false;
     hpcg_status s = run_fused_apply(h, d_r, d_y, ran);
     if (s != HPCG_OK) return s;
@@ -652,7 +652,8 @@ hpcg_status apply_H(hpcg_ctx* h, const float* d_r, float* d_y) {
       h->last_apply_path = HPCG_APPLY_FUSED;
       return HPCG_OK;
     }
-    return fail(h, HPCG_ERR_SHAPE, "fused apply: the batch has more leaves than co-resident workgroups");
+    if (h->apply_path == HPCG_APPLY_FUSED)
+      return fail(h, HPCG_ERR_SHAPE, "fused apply: the batch has more leaves than co-resident workgroups");
   }
   h->last_apply_path = HPCG_APPLY_STREAMING;
   const Geom& G = h->Gapply;

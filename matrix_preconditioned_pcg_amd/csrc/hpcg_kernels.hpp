@@ -3,8 +3,9 @@
 // Two solve engines share the phase functions of hpcg_device.hpp:
 //  * graph engine: one kernel per phase, G unrolled iterations captured in a
 //    hipGraph and replayed; the host reads a pinned flag between replays.
-//  * persistent engine: a single cooperative launch runs the whole solve; phases
-//    are separated by a device-wide barrier.
+//  * persistent engine: a single launch runs the whole solve; phases are
+//    separated by a device-wide barrier.  The grid never exceeds what the
+//    occupancy query says can be resident at once, and every wait is bounded.
 // Standalone kernels serve hpcg_apply_M (restriction, then prolongation) and
 // hpcg_spmv.
 #pragma once

@@ -157,7 +157,7 @@ def test_apply_parity(cfg, name):
 @pytest.mark.parametrize("path", [hpcg.HPCG_APPLY_STREAMING, hpcg.HPCG_APPLY_FUSED])
 @pytest.mark.parametrize("name", ["N1k", "N8k", "N16k", "tet4k"])
 def test_apply_paths(cfg, name, path):
-    # the two-launch and the single cooperative launch apply give the same M r
+    # the two-launch and the single-launch apply give the same M r
     batch = cfg(name)
     _log(f"apply path {path} {name}")
     s = _solver(batch)
@@ -179,10 +179,11 @@ def test_apply_auto_path_and_fused_refusal(cfg):
     with pytest.raises(hpcg.HPCGError):
         s.apply_M(r.reshape(-1))
     s.close()
+    # where every leaf gets a compute unit, AUTO takes the single launch
     small = cfg("N8k")
     s = _solver(small)
     s.apply_M(np.ones(small.n, np.float32))
-    assert hpcg.hpcg_last_apply_path(s.handle) == hpcg.HPCG_APPLY_STREAMING
+    assert hpcg.hpcg_last_apply_path(s.handle) == hpcg.HPCG_APPLY_FUSED
     s.close()
 
 
