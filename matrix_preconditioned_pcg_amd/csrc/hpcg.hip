@@ -30,6 +30,7 @@ struct Layout {
   size_t row_ptr, col, val, U, W, g, b, r, z, q, p0, p1, x, tleaf, pleaf, pq, rr, rz, st, ctl;
   size_t fr, fd, frhs, fsc;   // outer refinement: residual, correction, scaled rhs, per-system scalars
   size_t w, dinv, ftmp;       // squared form: H r; Jacobi: 1 / A_ii; apply scratch
+  size_t llw, lle;            // single-pass apply: flagged restriction words, per-leaf epochs
   size_t total;
 };
 
@@ -38,7 +39,7 @@ constexpr size_t kMaxLds = 160 * 1024;
 
 // control words, each on its own 256-byte line
 constexpr size_t kCtlBarrier = 0, kCtlAbort = 256, kCtlItbase = 512, kCtlReplays = 768, kCtlFlag = 1024,
-                 kCtlApplyCtr = 1280, kCtlApplyGen = 1536, kCtlBytes = 1792;
+                 kCtlBytes = 1280;
 
 constexpr int kMaxSplit = 8;   // workgroups per leaf in the streaming kernels
 
@@ -129,6 +130,8 @@ Layout make_layout(const Geom& G, int64_t nnz) {
   L.w = take(N * 8);
   L.dinv = take(N * 8);
   L.ftmp = take(N * 4);
+  L.llw = take((size_t)G.B * G.levels * G.K * RANK * 8 + 16);
+  L.lle = take((size_t)G.B * G.K * 4);
   L.total = off;
   return L;
 }
@@ -489,16 +492,17 @@ hpcg_status hpcg_create(const hpcg_partition* part, const int32_t* d_row_ptr, co
   B.itbase = reinterpret_cast<int*>(w + lay.ctl + kCtlItbase);
   B.replays = reinterpret_cast<int*>(w + lay.ctl + kCtlReplays);
   B.bflag = reinterpret_cast<unsigned*>(w + lay.ctl + kCtlFlag);
-  B.actr = reinterpret_cast<unsigned*>(w + lay.ctl + kCtlApplyCtr);
+  B.llw = reinterpret_cast<unsigned long long*>(w + lay.llw);
+  B.lle = reinterpret_cast<unsigned*>(w + lay.lle);
   B.w = w + lay.w;
   B.dinv = reinterpret_cast<const double*>(w + lay.dinv);
   B.form = FORM_DIRECT;
-  B.agen = reinterpret_cast<unsigned*>(w + lay.ctl + kCtlApplyGen);
   B.tol = 1e-6;
   B.maxit = 1000;
 
   const size_t N = (size_t)G.B * G.n;
   CREATE_HIP(hipMemsetAsync(w + lay.ctl, 0, kCtlBytes, h->stream));
+  CREATE_HIP(hipMemsetAsync(w + lay.llw, 0, lay.lle + (size_t)G.B * G.K * 4 - lay.llw, h->stream));
   CREATE_HIP(hipMemcpyAsync(w + lay.row_ptr, d_row_ptr, (N + 1) * 4, hipMemcpyDeviceToDevice, h->stream));
   if (nnz_total > 0) {
     CREATE_HIP(hipMemcpyAsync(w + lay.col, d_col, (size_t)nnz_total * 4, hipMemcpyDeviceToDevice, h->stream));

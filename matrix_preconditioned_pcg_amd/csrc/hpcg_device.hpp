@@ -105,8 +105,8 @@ struct Bufs {
   SysState* st;        // [B]
   unsigned* barrier;   // device-wide barrier arrival counter
   unsigned* bflag;     // resident engine: number of the last completed barrier
-  unsigned* actr;      // fused apply: arrivals at its barrier (returns to 0 after each)
-  unsigned* agen;      // fused apply: barrier generation
+  unsigned long long* llw;  // fused apply: [B][levels][K][RANK] W_l[k]^T r as (value, epoch) words
+  unsigned* lle;       // fused apply: [B*K] calls completed per leaf (the epoch)
   int* abort_flag;     // set when a barrier wait exceeds its bound
   int* itbase;         // graph engine: absolute iteration of the replay's first step
   int* replays;        // graph engine: replays finished

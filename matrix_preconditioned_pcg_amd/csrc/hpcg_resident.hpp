@@ -253,7 +253,7 @@ __device__ __forceinline__ void r_restrict(const Geom& G, int s, int k, const Re
 #pragma unroll
       for (int w = 1; w < NWR; ++w) a += sm.redW[w][tid];
       const int l = tid / RANK, c = tid - l * RANK;
-      st_c(pout + (((size_t)s * G.levels + l) * G.K + k) * RANK + c, a);
+      if (pout) st_c(pout + (((size_t)s * G.levels + l) * G.K + k) * RANK + c, a);
       own[tid] = a;
     }
   }
@@ -275,72 +275,84 @@ __device__ __forceinline__ void r_stage_partners(const Geom& G, const T* src, in
   }
 }
 
-// z = M r_new on the leaf's rows into sm.z.  Needs sm.t (= U_k^T r_new), sm.r
-// (= r_new) and the staged partner restrictions of r (stR) and q (stQ):
-// P_l = sum(stR) - alpha sum(stQ).  With stQ == nullptr, P_l = sum(stR).
+// Strip aggregation (eq. (3)) from the staged partner restrictions of r
+// (stR, level l at stage row 2^l - 1) and of q (stQ): sm.P[l] = sum(stR) -
+// alpha sum(stQ), or sum(stR) with stQ == nullptr.  16 groups of threads per
+// column, then across waves; two barriers.
 template <typename T, int LEV>
-__device__ __forceinline__ void r_prolong(const Resident<T, LEV>& F, RSmem<T>& sm, const T* stR, const T* stQ,
-                                          double alpha, float gate) {
+__device__ __forceinline__ void prolong_strips(RSmem<T>& sm, const T* stR, const T* stQ, double alpha) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if constexpr (LEV > 0) {
-    // strip aggregation (eq. (3)) from the staged partner restrictions (level l
-    // at stage row 2^l - 1): 16 groups of threads per column, then across waves
-    const int c = tid & 31, g = tid >> 5;
+  const int c = tid & 31, g = tid >> 5;
 #pragma unroll
-    for (int l = 0; l < LEV; ++l) {
-      const T* vr = stR + (size_t)((1 << l) - 1) * RANK + c;
-      T a = 0, b = 0;
+  for (int l = 0; l < LEV; ++l) {
+    const T* vr = stR + (size_t)((1 << l) - 1) * RANK + c;
+    T a = 0, b = 0;
 #pragma unroll
-      for (int m = 0; m < ((1 << l) + 15) / 16; ++m) {
-        const int i = g + 16 * m;
-        if (i < (1 << l)) {
-          a += vr[i * RANK];
-          if (stQ) b += stQ[(size_t)((1 << l) - 1) * RANK + c + i * RANK];
-        }
-      }
-      a += lane_x32(a);
-      b += lane_x32(b);
-      if (lane < 32) {
-        sm.redW[wave][l * RANK + c] = a;
-        sm.redW[wave][(MAX_LEVELS + l) * RANK + c] = b;
+    for (int m = 0; m < ((1 << l) + 15) / 16; ++m) {
+      const int i = g + 16 * m;
+      if (i < (1 << l)) {
+        a += vr[i * RANK];
+        if (stQ) b += stQ[(size_t)((1 << l) - 1) * RANK + c + i * RANK];
       }
     }
-    __syncthreads();
-    if (tid < LEV * RANK) {
-      T a = sm.redW[0][tid], b = sm.redW[0][MAX_LEVELS * RANK + tid];
-#pragma unroll
-      for (int w = 1; w < NWR; ++w) { a += sm.redW[w][tid]; b += sm.redW[w][MAX_LEVELS * RANK + tid]; }
-      sm.P[tid] = stQ ? (T)((double)a - alpha * (double)b) : a;
+    a += lane_x32(a);
+    if (stQ) b += lane_x32(b);
+    if (lane < 32) {
+      sm.redW[wave][l * RANK + c] = a;
+      if (stQ) sm.redW[wave][(MAX_LEVELS + l) * RANK + c] = b;
     }
-    __syncthreads();
   }
-  if constexpr (LEV == 0) __syncthreads();   // sm.t and sm.r of the caller
-  // diagonal stage: rows rg + 16m (m < 8), dots over 32 column slots; the eight
-  // rows of a lane are folded with a transpose-reduce (7 + 2 shuffles)
-  {
-    const int cs = tid & 31, rg = tid >> 5;
-    const Vec4<T> t4 = lds4(&sm.t[4 * cs]);
-    T v[8];
+  __syncthreads();
+  if (tid < LEV * RANK) {
+    T a = sm.redW[0][tid];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) v[m] = dot4(F.u[m], t4);
-    const bool b4 = (cs & 16) != 0, b3 = (cs & 8) != 0, b2 = (cs & 4) != 0;
-    T a[4];
+    for (int w = 1; w < NWR; ++w) a += sm.redW[w][tid];
+    if (stQ) {
+      T b = sm.redW[0][MAX_LEVELS * RANK + tid];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {           // xor 16: keep the upper four rows if b4
-      const T keep = b4 ? v[4 + i] : v[i], send = b4 ? v[i] : v[4 + i];
-      a[i] = keep + lane_x16(send);
+      for (int w = 1; w < NWR; ++w) b += sm.redW[w][MAX_LEVELS * RANK + tid];
+      a = (T)((double)a - alpha * (double)b);
     }
-    T bb[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {           // xor 8
-      const T keep = b3 ? a[2 + i] : a[i], send = b3 ? a[i] : a[2 + i];
-      bb[i] = keep + lane_x8(send);
-    }
-    T kk = b2 ? bb[1] : bb[0];              // bit 2 (lane j pairs with 7 - j)
-    kk += lane_m4(b2 ? bb[0] : bb[1]);
-    kk = group4_sum(kk);
-    if ((cs & 3) == 0) sm.yleaf[rg + 16 * ((b4 ? 4 : 0) + (b3 ? 2 : 0) + (b2 ? 1 : 0))] = kk;
+    sm.P[tid] = a;
   }
+  __syncthreads();
+}
+
+// Diagonal stage U_k sm.t into sm.yleaf: rows rg + 16m (m < 8), dots over 32
+// column slots; the eight rows of a lane are folded with a transpose-reduce
+// (7 + 2 shuffles).  No barrier.
+template <typename T, int LEV>
+__device__ __forceinline__ void prolong_diag(const Resident<T, LEV>& F, RSmem<T>& sm) {
+  const int tid = threadIdx.x;
+  const int cs = tid & 31, rg = tid >> 5;
+  const Vec4<T> t4 = lds4(&sm.t[4 * cs]);
+  T v[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) v[m] = dot4(F.u[m], t4);
+  const bool b4 = (cs & 16) != 0, b3 = (cs & 8) != 0, b2 = (cs & 4) != 0;
+  T a[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {           // xor 16: keep the upper four rows if b4
+    const T keep = b4 ? v[4 + i] : v[i], send = b4 ? v[i] : v[4 + i];
+    a[i] = keep + lane_x16(send);
+  }
+  T bb[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {           // xor 8
+    const T keep = b3 ? a[2 + i] : a[i], send = b3 ? a[i] : a[2 + i];
+    bb[i] = keep + lane_x8(send);
+  }
+  T kk = b2 ? bb[1] : bb[0];              // bit 2 (lane j pairs with 7 - j)
+  kk += lane_m4(b2 ? bb[0] : bb[1]);
+  kk = group4_sum(kk);
+  if ((cs & 3) == 0) sm.yleaf[rg + 16 * ((b4 ? 4 : 0) + (b3 ? 2 : 0) + (b2 ? 1 : 0))] = kk;
+}
+
+// Off-diagonal prolongation sum_l W_l[k] sm.P[l] into sm.yoff (eq. (5)).
+// No barrier.
+template <typename T, int LEV>
+__device__ __forceinline__ void prolong_offdiag(const Resident<T, LEV>& F, RSmem<T>& sm) {
+  const int tid = threadIdx.x;
   if constexpr (LEV > 0) {
     const int cs = tid & 7, row = tid >> 3;
     T o0 = 0, o1 = 0;
@@ -356,6 +368,19 @@ __device__ __forceinline__ void r_prolong(const Resident<T, LEV>& F, RSmem<T>& s
   } else {
     if (tid < LEAF) sm.yoff[tid] = 0;
   }
+}
+
+// z = M r_new on the leaf's rows into sm.z.  Needs sm.t (= U_k^T r_new), sm.r
+// (= r_new) and the staged partner restrictions of r (stR) and q (stQ):
+// P_l = sum(stR) - alpha sum(stQ).  With stQ == nullptr, P_l = sum(stR).
+template <typename T, int LEV>
+__device__ __forceinline__ void r_prolong(const Resident<T, LEV>& F, RSmem<T>& sm, const T* stR, const T* stQ,
+                                          double alpha, float gate) {
+  const int tid = threadIdx.x;
+  if constexpr (LEV > 0) prolong_strips<T, LEV>(sm, stR, stQ, alpha);
+  if constexpr (LEV == 0) __syncthreads();   // sm.t and sm.r of the caller
+  prolong_diag<T, LEV>(F, sm);
+  prolong_offdiag<T, LEV>(F, sm);
   __syncthreads();
   if (tid < LEAF) sm.z[tid] = sm.yleaf[tid] + sm.yoff[tid] + (T)gate * sm.r[tid];
   __syncthreads();
@@ -382,12 +407,72 @@ __device__ __forceinline__ void load_factors(const Geom& G, const Bufs& B, int s
 
 // Single-launch apply y = M r (fp32 in and out) for batches whose leaves all
 // get a compute unit: the workgroup of leaf k loads U_k and its slabs into
-// registers once, restricts (eq. (2)), meets the others at one device-wide
-// barrier, and prolongs (eqs. (3)-(5)) and adds the diagonal stage and the gate
-// with the same registers, so every factor byte crosses HBM once per apply.
-// The barrier is self-resetting (the arrival counter wraps to zero, the last
-// arrival advances a generation word), so the launch can be replayed from a
-// captured graph.
+// registers once, restricts (eq. (2)), gathers the partner halves'
+// restrictions (eq. (3)), and prolongs (eqs. (4)-(5)) and adds the diagonal
+// stage and the gate with the same registers, so every factor byte crosses HBM
+// once per apply.
+//
+// No device-wide barrier: each restriction value travels with the number of
+// the call that produced it, packed into one 8-byte word (value in the low
+// half, epoch in the high half) that is stored and loaded as a whole with
+// agent-scope atomics, so a reader that sees the epoch it expects also sees
+// that call's value.  The epoch of a leaf counts the calls that leaf has
+// completed (every call runs every leaf once, so all leaves agree at a call's
+// start); the words hold the previous call's epoch until overwritten.  A
+// reader therefore polls exactly the words it needs, and a workgroup waits for
+// its partners only, for about one memory round trip after the last of them
+// has written.  The polls are bounded: past the bound the abort flag is raised
+// and the output is undefined (only if other work holds the device's compute
+// units for about a second).
+template <int LEV>
+__device__ __forceinline__ void gather_partners_ll(const Geom& G, const Bufs& B, int s, int k, unsigned want,
+                                                   float* stage) {
+  if constexpr (LEV > 0) {
+    // word w = row * RANK + c, row = 2^l - 1 + i: column c of the i-th leaf of
+    // level l's partner half, staged at the same position
+    constexpr int NWORDS = RANK * ((1 << LEV) - 1);
+    constexpr int WPT = (NWORDS + NTR - 1) / NTR;
+    const int tid = threadIdx.x;
+    const unsigned long long* src[WPT];
+    unsigned long long v[WPT];
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+      const int w = tid + j * NTR;
+      src[j] = nullptr;
+      if (w < NWORDS) {
+        const int row = w / RANK, c = w - row * RANK;
+        const int l = 31 - __clz(row + 1);
+        const int kp = (((k >> l) ^ 1) << l) + (row + 1 - (1 << l));
+        src[j] = B.llw + (((size_t)s * G.levels + l) * G.K + kp) * RANK + c;
+        v[j] = ld_c(src[j]);
+      }
+    }
+    // re-poll every word still short of its epoch together, so that a late
+    // partner costs one round trip, not one per word
+    unsigned pending = 0;
+#pragma unroll
+    for (int j = 0; j < WPT; ++j)
+      if (src[j] && (unsigned)(v[j] >> 32) != want) pending |= 1u << j;
+    unsigned polls = 0;
+    while (pending) {
+      __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+      for (int j = 0; j < WPT; ++j)
+        if (pending & (1u << j)) v[j] = ld_c(src[j]);
+#pragma unroll
+      for (int j = 0; j < WPT; ++j)
+        if ((pending & (1u << j)) && (unsigned)(v[j] >> 32) == want) pending &= ~(1u << j);
+      if (++polls > (1u << 20)) {
+        st_c(B.abort_flag, 1);
+        break;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < WPT; ++j)
+      if (src[j]) stage[tid + j * NTR] = __uint_as_float((unsigned)v[j]);
+  }
+}
+
 template <int LEV>
 __global__ __launch_bounds__(NTR) void k_apply_fused(Geom G, Bufs B, const float* __restrict__ rin,
                                                      float* __restrict__ yout) {
@@ -398,37 +483,31 @@ __global__ __launch_bounds__(NTR) void k_apply_fused(Geom G, Bufs B, const float
   const int item = blockIdx.x;
   const int s = item / G.K, k = item - s * G.K;
   const int leaf0 = s * G.n + k * LEAF;
-  __shared__ unsigned gen0;
-  if (tid == 0) gen0 = ld_c(B.agen);
+  if (tid == 0) sm.flag[0] = (int)ld_c(B.lle + item);
   Resident<float, LEV> F;
   load_factors(G, B, s, k, F);
   const float gate = (tid < LEAF) ? B.g[leaf0 + tid] : 0.f;
   if (tid < LEAF) sm.r[tid] = rin[leaf0 + tid];
   __syncthreads();
-  float* pR = reinterpret_cast<float*>(B.pleaf);
-  r_restrict<float, LEV>(G, s, k, F, sm.r, sm.t, pR, sm.ownR, sm);
-  // device-wide barrier
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned old = __builtin_amdgcn_atomic_inc32(B.actr, gridDim.x - 1, __ATOMIC_RELAXED, "agent");
-    if (old == gridDim.x - 1) st_c(B.agen, gen0 + 1);
-    unsigned polls = 0;
-    while (ld_c(B.agen) == gen0) {
-      __builtin_amdgcn_s_sleep(1);
-      if (++polls > (1u << 26)) {
-        st_c(B.abort_flag, 1);
-        break;
-      }
+  const unsigned want = (unsigned)sm.flag[0] + 1u;
+  r_restrict<float, LEV>(G, s, k, F, sm.r, sm.t, (float*)nullptr, sm.ownR, sm);
+  if constexpr (LEV > 0) {
+    if (tid < LEV * RANK) {
+      const int l = tid / RANK, c = tid - l * RANK;
+      st_c(B.llw + (((size_t)s * G.levels + l) * G.K + k) * RANK + c,
+           ((unsigned long long)want << 32) | __float_as_uint(sm.ownR[tid]));
     }
   }
+  // the diagonal stage needs nothing from other leaves: it runs while the
+  // partners' words are in flight
+  prolong_diag<float, LEV>(F, sm);
+  gather_partners_ll<LEV>(G, B, s, k, want, stR);
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  if constexpr (LEV > 0) r_stage_partners<float, LEV>(G, pR, s, k, stR);
-  lds_dma_wait();
-  r_prolong<float, LEV>(F, sm, stR, (const float*)nullptr, 0.0, gate);
-  if (tid < LEAF) yout[leaf0 + tid] = sm.z[tid];
+  if constexpr (LEV > 0) prolong_strips<float, LEV>(sm, stR, (const float*)nullptr, 0.0);
+  prolong_offdiag<float, LEV>(F, sm);
+  __syncthreads();
+  if (tid < LEAF) yout[leaf0 + tid] = sm.yleaf[tid] + sm.yoff[tid] + gate * sm.r[tid];
+  if (tid == 0) st_c(B.lle + item, want);
 }
 
 template <typename T, int LEV>
