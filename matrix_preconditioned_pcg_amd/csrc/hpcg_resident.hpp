@@ -170,35 +170,32 @@ struct Resident {
   float4 w[LEV > 0 ? LEV : 1][2];
 };
 
-// Restriction of the LDS vector v: U_k^T v into tout (LDS, complete) and
-// W_l[k]^T v into pout (global, [levels][K][RANK] of system s) and own (LDS).
-// With part_dst, the workgroup sum of `loc` is stored there as well (sharing
-// the restriction's barriers).
+// Per-wave partials of U_k^T v into sm.red[wave] (thread = 4-column slot cs
+// of 32, row group rg of 16; the two row groups of a wave are added with xor
+// 32).  No barrier.
 template <typename T, int LEV>
-__device__ __forceinline__ void r_restrict(const Geom& G, int s, int k, const Resident<T, LEV>& F,
-                                           const T* v, T* tout, T* pout, T* own, RSmem<T>& sm,
-                                           double loc = 0.0, double* part_dst = nullptr) {
+__device__ __forceinline__ void restrict_u_partials(const Resident<T, LEV>& F, const T* v, RSmem<T>& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (part_dst) {
-    loc = wave_sum(loc);
-    if (lane == 0) sm.dred[wave] = loc;
-  }
-  {
-    const int cs = tid & 31, rg = tid >> 5;
-    Vec4<T> acc{0, 0, 0, 0};
+  const int cs = tid & 31, rg = tid >> 5;
+  Vec4<T> acc{0, 0, 0, 0};
 #pragma unroll
-    for (int m = 0; m < 8; ++m) axpy4(acc, F.u[m], v[rg + 16 * m]);
-    acc.x += lane_x32(acc.x); acc.y += lane_x32(acc.y);
-    acc.z += lane_x32(acc.z); acc.w += lane_x32(acc.w);
-    if (lane < 32) {
-      T* d = &sm.red[wave][4 * cs];
-      d[0] = acc.x; d[1] = acc.y; d[2] = acc.z; d[3] = acc.w;
-    }
+  for (int m = 0; m < 8; ++m) axpy4(acc, F.u[m], v[rg + 16 * m]);
+  acc.x += lane_x32(acc.x); acc.y += lane_x32(acc.y);
+  acc.z += lane_x32(acc.z); acc.w += lane_x32(acc.w);
+  if (lane < 32) {
+    T* d = &sm.red[wave][4 * cs];
+    d[0] = acc.x; d[1] = acc.y; d[2] = acc.z; d[3] = acc.w;
   }
+}
+
+// Per-wave partials of W_l[k]^T v for every level into sm.redW[wave].
+// Thread = (4-column slot cs of 8, rows row and row + 64); the eight rows of
+// a wave (lane bits 3..5) are folded per pair of levels with a
+// transpose-reduce: 8 values -> 1 per lane in 4 + 2 + 1 shuffles.  No barrier.
+template <typename T, int LEV>
+__device__ __forceinline__ void restrict_w_partials(const Resident<T, LEV>& F, const T* v, RSmem<T>& sm) {
   if constexpr (LEV > 0) {
-    // thread = (4-column slot cs of 8, rows row and row + 64); the eight rows of
-    // a wave (lane bits 3..5) are folded per pair of levels with a
-    // transpose-reduce: 8 values -> 1 per lane in 4 + 2 + 1 shuffles
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cs = tid & 7, row = tid >> 3;
     const T r0 = v[row], r1 = v[row + 64];
     const bool b5 = (lane & 32) != 0, b4 = (lane & 16) != 0, b3 = (lane & 8) != 0;
@@ -234,6 +231,23 @@ __device__ __forceinline__ void r_restrict(const Geom& G, int s, int k, const Re
       if (l < LEV) sm.redW[wave][l * RANK + 4 * cs + (which & 3)] = kk;
     }
   }
+}
+
+// Restriction of the LDS vector v: U_k^T v into tout (LDS, complete) and
+// W_l[k]^T v into pout (global, [levels][K][RANK] of system s; skipped when
+// null) and own (LDS).  With part_dst, the workgroup sum of `loc` is stored
+// there as well (sharing the restriction's barriers).
+template <typename T, int LEV>
+__device__ __forceinline__ void r_restrict(const Geom& G, int s, int k, const Resident<T, LEV>& F,
+                                           const T* v, T* tout, T* pout, T* own, RSmem<T>& sm,
+                                           double loc = 0.0, double* part_dst = nullptr) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (part_dst) {
+    loc = wave_sum(loc);
+    if (lane == 0) sm.dred[wave] = loc;
+  }
+  restrict_u_partials<T, LEV>(F, v, sm);
+  restrict_w_partials<T, LEV>(F, v, sm);
   __syncthreads();
   if (part_dst && tid == 0) {
     double p = sm.dred[0];
@@ -392,8 +406,8 @@ __device__ __forceinline__ void load_factors(const Geom& G, const Bufs& B, int s
   const int tid = threadIdx.x;
   const int cs = tid & 31, rg = tid >> 5;
   const float* Uk = B.U + ((size_t)s * G.K + k) * LEAF * LEAF;
-#pragma unroll
-  for (int m = 0; m < 8; ++m) F.u[m] = *reinterpret_cast<const float4*>(Uk + (rg + 16 * m) * LEAF + 4 * cs);
+  // slabs first: the single-pass apply publishes their restriction before it
+  // needs U_k
   if constexpr (LEV > 0) {
     const int c8 = tid & 7, row = tid >> 3;
 #pragma unroll
@@ -403,6 +417,8 @@ __device__ __forceinline__ void load_factors(const Geom& G, const Bufs& B, int s
       F.w[l][1] = *reinterpret_cast<const float4*>(Wl + (row + 64) * RANK + 4 * c8);
     }
   }
+#pragma unroll
+  for (int m = 0; m < 8; ++m) F.u[m] = *reinterpret_cast<const float4*>(Uk + (rg + 16 * m) * LEAF + 4 * cs);
 }
 
 // Single-launch apply y = M r (fp32 in and out) for batches whose leaves all
@@ -483,21 +499,40 @@ __global__ __launch_bounds__(NTR) void k_apply_fused(Geom G, Bufs B, const float
   const int item = blockIdx.x;
   const int s = item / G.K, k = item - s * G.K;
   const int leaf0 = s * G.n + k * LEAF;
-  if (tid == 0) sm.flag[0] = (int)ld_c(B.lle + item);
+  // r, the gate and the epoch are issued before the factors: the loads
+  // return in order, so storing r to LDS then waits for r alone
+  float rv = 0.f, gate = 0.f;
+  if (tid < LEAF) {
+    rv = rin[leaf0 + tid];
+    gate = B.g[leaf0 + tid];
+  }
+  const unsigned want = ld_c(B.lle + item) + 1u;
   Resident<float, LEV> F;
   load_factors(G, B, s, k, F);
-  const float gate = (tid < LEAF) ? B.g[leaf0 + tid] : 0.f;
-  if (tid < LEAF) sm.r[tid] = rin[leaf0 + tid];
+  if (tid < LEAF) sm.r[tid] = rv;
   __syncthreads();
-  const unsigned want = (unsigned)sm.flag[0] + 1u;
-  r_restrict<float, LEV>(G, s, k, F, sm.r, sm.t, (float*)nullptr, sm.ownR, sm);
+  // the slabs' restriction (what the partners need) first, then U_k^T r
   if constexpr (LEV > 0) {
+    restrict_w_partials<float, LEV>(F, sm.r, sm);
+    __syncthreads();
     if (tid < LEV * RANK) {
+      float a = sm.redW[0][tid];
+#pragma unroll
+      for (int w = 1; w < NWR; ++w) a += sm.redW[w][tid];
       const int l = tid / RANK, c = tid - l * RANK;
       st_c(B.llw + (((size_t)s * G.levels + l) * G.K + k) * RANK + c,
-           ((unsigned long long)want << 32) | __float_as_uint(sm.ownR[tid]));
+           ((unsigned long long)want << 32) | __float_as_uint(a));
     }
   }
+  restrict_u_partials<float, LEV>(F, sm.r, sm);
+  __syncthreads();
+  if (tid < LEAF) {
+    float a = sm.red[0][tid];
+#pragma unroll
+    for (int w = 1; w < NWR; ++w) a += sm.red[w][tid];
+    sm.t[tid] = a;
+  }
+  __syncthreads();
   // the diagonal stage needs nothing from other leaves: it runs while the
   // partners' words are in flight
   prolong_diag<float, LEV>(F, sm);
