@@ -359,6 +359,41 @@ def main(argv=None):
                  "refined_vec32_ms_per_solve": round(ms_r, 4), "refined_inner_iterations": res_r.iterations[0],
                  "refined_outer_steps": outer[0], "refined_true_relres": res_r.relres[0]}
         solver.close()
+    forms = None
+    if not args.no_variants:
+        # the other preconditioner forms on the workload (graph engine), and
+        # factors fitted to A^{-1/2} (squared form) / A^{-1} (direct form)
+        from workloads.fitted import fitted_batch
+        log("bench: preconditioner forms")
+        forms = {}
+        bf = make_config(args.config)
+        bvec = torch.as_tensor(bf.b.reshape(-1)).cuda()
+        for label, form in (("squared", hpcg.HPCG_FORM_SQUARED), ("jacobi", hpcg.HPCG_FORM_JACOBI)):
+            solver = hpcg.Solver(bf.n, bf.row_ptr, bf.col, bf.val, batch=bf.batch, levels=bf.levels, stream=stream)
+            if form != hpcg.HPCG_FORM_JACOBI:
+                solver.set_factors(bf.U, bf.W, bf.g)
+            solver.set_option(hpcg.HPCG_OPT_FORM, form)
+            ms, its, _r = time_solves(solver, bvec, bf.tol, bf.maxit, max(3, args.steps // 2), 1, torch)
+            forms[label] = {"workload": args.config, "ms_per_solve": round(ms, 4), "iterations": its[0],
+                            "engine": solver.last_engine}
+            solver.close()
+        for name in ("N1k", "tet4k"):
+            base_b = make_config(name)
+            bvec = torch.as_tensor(base_b.b.reshape(-1)).cuda()
+            for power, form, label in ((-0.5, hpcg.HPCG_FORM_SQUARED, "fit_inv_sqrt_squared"),
+                                       (-1.0, hpcg.HPCG_FORM_DIRECT, "fit_inv_direct")):
+                log(f"bench: fitted factors {name} {label}")
+                fb = fitted_batch(base_b, power)
+                solver = hpcg.Solver(fb.n, fb.row_ptr, fb.col, fb.val, batch=fb.batch, levels=fb.levels,
+                                     stream=stream)
+                solver.set_factors(fb.U, fb.W, fb.g)
+                solver.set_option(hpcg.HPCG_OPT_FORM, form)
+                ms, its, _r = time_solves(solver, bvec, fb.tol, fb.maxit, max(3, args.steps // 2), 1, torch)
+                lo, hi = solver.estimate_spectrum(60)
+                forms[f"{label}_{name}"] = {"ms_per_solve": round(ms, 4), "iterations": its[0],
+                                            "engine": solver.last_engine,
+                                            "lambda_min_H": round(lo, 6), "lambda_max_H": round(hi, 6)}
+                solver.close()
     block = []
     if not args.no_block:
         for name in ("N8k", "N16k"):
@@ -416,6 +451,7 @@ def main(argv=None):
         "block_apply": block,
         "bridge_format": bridge,
         "tight_tolerance": tight,
+        "preconditioner_forms": forms,
     }
     print(json.dumps(line), flush=True)
     return 0
