@@ -55,7 +55,7 @@ def spmv_bytes(n: int, nnz: int, B: int = 1) -> int:
 
 
 # sources of the single-vector apply and SpMV kernels and of their launch code
-APPLY_SPMV_SOURCES = ("hpcg_device.hpp", "hpcg_kernels.hpp", "hpcg_resident.hpp", "hpcg.hip")
+APPLY_SPMV_SOURCES = ("hpcg_device.hpp", "hpcg_leaf.hpp", "hpcg_apply.hpp")
 
 
 def kernel_source_digest() -> str:

@@ -18,7 +18,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "hpcg.hip")
-DEPS = [os.path.join(HERE, "csrc", f) for f in ("hpcg.hip", "hpcg_device.hpp", "hpcg_kernels.hpp")]
+DEPS = [os.path.join(HERE, "csrc", f) for f in ("hpcg.hip", "hpcg_device.hpp", "hpcg_kernels.hpp", "hpcg_leaf.hpp",
+                                                 "hpcg_apply.hpp", "hpcg_resident.hpp", "hpcg_block.hpp")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIB_DIR, "libhpcg.so")

@@ -15,6 +15,7 @@
 #include <string>
 #include <vector>
 
+#include "hpcg_apply.hpp"
 #include "hpcg_resident.hpp"
 #include "hpcg_block.hpp"
 

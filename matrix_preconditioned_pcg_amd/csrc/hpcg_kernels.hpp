@@ -6,8 +6,8 @@
 //  * persistent engine: a single launch runs the whole solve; phases are
 //    separated by a device-wide barrier.  The grid never exceeds what the
 //    occupancy query says can be resident at once, and every wait is bounded.
-// Standalone kernels serve hpcg_apply_M (restriction, then prolongation) and
-// hpcg_spmv.
+// Standalone kernels serve the two-launch hpcg_apply_M (restriction, then
+// prolongation).
 #pragma once
 #include "hpcg_device.hpp"
 
@@ -194,25 +194,6 @@ __global__ __launch_bounds__(NT) void k_apply_prolong(Geom G, Bufs B, const floa
   if (threadIdx.x < G.RB) yout[bk.grow0 + threadIdx.x] = y;
 }
 
-// y = A x; SPMV_TPR consecutive lanes share a row and stride over its entries.
-constexpr int SPMV_TPR = 4;
-constexpr int SPMV_ROWS = NT / SPMV_TPR;
-
-__global__ __launch_bounds__(NT) void k_spmv(const int* __restrict__ row_ptr, const int* __restrict__ col,
-                                             const float* __restrict__ val, const float* __restrict__ x,
-                                             float* __restrict__ y, int nrows) {
-  const int tid = threadIdx.x;
-  const int row = blockIdx.x * SPMV_ROWS + tid / SPMV_TPR;
-  const int lr = tid & (SPMV_TPR - 1);
-  float acc = 0.f;
-  if (row < nrows) {
-    const int e1 = row_ptr[row + 1];
-    for (int e = row_ptr[row] + lr; e < e1; e += SPMV_TPR) acc = fmaf(val[e], x[col[e]], acc);
-  }
-#pragma unroll
-  for (int o = 1; o < SPMV_TPR; o <<= 1) acc += __shfl_xor(acc, o);
-  if (row < nrows && lr == 0) y[row] = acc;
-}
 
 // Bridge format -> per-level slabs: for tile m of level l, a row-half leaf k
 // gets W_l[k] = U~_k B_m and a column-half leaf gets W_l[k] = V~_k, which gives

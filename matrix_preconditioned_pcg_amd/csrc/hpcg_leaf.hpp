@@ -1,0 +1,230 @@
+// Leaf-resident building blocks for gfx950: one workgroup of NTR = 512
+// threads (8 wave64 wavefronts) per leaf, U_k and the leaf's level slabs held
+// in VGPRs, and the restriction / prolongation steps of the H-matrix apply on
+// them.  Shared by the single-pass apply and the register-resident solve.
+#pragma once
+#include "hpcg_device.hpp"
+
+namespace hpcg {
+
+constexpr int NTR = 512;
+constexpr int NWR = NTR / 64;
+
+template <typename T>
+struct alignas(16) RSmem {
+  T r[LEAF];
+  T q[LEAF];
+  T z[LEAF];
+  T p[LEAF];                         // p of the current iteration (own rows)
+  T tr[LEAF];                        // U_k^T r
+  T tq[LEAF];                        // U_k^T q
+  T t[LEAF];                         // U_k^T r_new = tr - alpha tq
+  T P[MAX_LEVELS * RANK];            // partner-half sums
+  T ownR[MAX_LEVELS * RANK];         // this leaf's W_l[k]^T r
+  T ownQ[MAX_LEVELS * RANK];         // this leaf's W_l[k]^T q
+  T yleaf[LEAF];
+  T yoff[LEAF];
+  T red[NWR][LEAF];                  // cross-wave reductions of t
+  T redW[NWR][2 * MAX_LEVELS * RANK];  // cross-wave reductions (restriction, strip sums)
+  double dred[NWR];
+  double dred2[NWR];
+  double dsc[4];
+  int flag[4];
+};
+
+// Agent-scope (XCD-coherent) load and store of one value.
+template <typename T>
+__device__ __forceinline__ T ld_c(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ void st_c(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename T, int LEV>
+struct Resident {
+  float4 u[8];
+  float4 w[LEV > 0 ? LEV : 1][2];
+};
+
+// Per-wave partials of U_k^T v into sm.red[wave] (thread = 4-column slot cs
+// of 32, row group rg of 16; the two row groups of a wave are added with xor
+// 32).  No barrier.
+template <typename T, int LEV>
+__device__ __forceinline__ void restrict_u_partials(const Resident<T, LEV>& F, const T* v, RSmem<T>& sm) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cs = tid & 31, rg = tid >> 5;
+  Vec4<T> acc{0, 0, 0, 0};
+#pragma unroll
+  for (int m = 0; m < 8; ++m) axpy4(acc, F.u[m], v[rg + 16 * m]);
+  acc.x += lane_x32(acc.x); acc.y += lane_x32(acc.y);
+  acc.z += lane_x32(acc.z); acc.w += lane_x32(acc.w);
+  if (lane < 32) {
+    T* d = &sm.red[wave][4 * cs];
+    d[0] = acc.x; d[1] = acc.y; d[2] = acc.z; d[3] = acc.w;
+  }
+}
+
+// Per-wave partials of W_l[k]^T v for every level into sm.redW[wave].
+// Thread = (4-column slot cs of 8, rows row and row + 64); the eight rows of
+// a wave (lane bits 3..5) are folded per pair of levels with a
+// transpose-reduce: 8 values -> 1 per lane in 4 + 2 + 1 shuffles.  No barrier.
+template <typename T, int LEV>
+__device__ __forceinline__ void restrict_w_partials(const Resident<T, LEV>& F, const T* v, RSmem<T>& sm) {
+  if constexpr (LEV > 0) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int cs = tid & 7, row = tid >> 3;
+    const T r0 = v[row], r1 = v[row + 64];
+    const bool b5 = (lane & 32) != 0, b4 = (lane & 16) != 0, b3 = (lane & 8) != 0;
+    const int which = (b5 ? 4 : 0) + (b4 ? 2 : 0) + (b3 ? 1 : 0);   // value index a lane ends with
+#pragma unroll
+    for (int l0 = 0; l0 < LEV; l0 += 2) {
+      T x[8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        Vec4<T> acc{0, 0, 0, 0};
+        if (l0 + h < LEV) {
+          axpy4(acc, F.w[l0 + h < LEV ? l0 + h : 0][0], r0);
+          axpy4(acc, F.w[l0 + h < LEV ? l0 + h : 0][1], r1);
+        }
+        x[4 * h + 0] = acc.x; x[4 * h + 1] = acc.y; x[4 * h + 2] = acc.z; x[4 * h + 3] = acc.w;
+      }
+      T a[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const T keep = b5 ? x[4 + i] : x[i], send = b5 ? x[i] : x[4 + i];
+        a[i] = keep + lane_x32(send);
+      }
+      T bb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const T keep = b4 ? a[2 + i] : a[i], send = b4 ? a[i] : a[2 + i];
+        bb[i] = keep + lane_x16(send);
+      }
+      T kk = b3 ? bb[1] : bb[0];
+      kk += lane_x8(b3 ? bb[0] : bb[1]);
+      // value index `which` = 4h + component: level l0 + which/4, column 4cs + which%4
+      const int l = l0 + (which >> 2);
+      if (l < LEV) sm.redW[wave][l * RANK + 4 * cs + (which & 3)] = kk;
+    }
+  }
+}
+
+// U_k and the leaf's level slabs into the register layout of Resident.
+template <typename T, int LEV>
+__device__ __forceinline__ void load_factors(const Geom& G, const Bufs& B, int s, int k, Resident<T, LEV>& F) {
+  const int tid = threadIdx.x;
+  const int cs = tid & 31, rg = tid >> 5;
+  const float* Uk = B.U + ((size_t)s * G.K + k) * LEAF * LEAF;
+  // slabs first: the single-pass apply publishes their restriction before it
+  // needs U_k
+  if constexpr (LEV > 0) {
+    const int c8 = tid & 7, row = tid >> 3;
+#pragma unroll
+    for (int l = 0; l < LEV; ++l) {
+      const float* Wl = B.W + (((size_t)s * G.levels + l) * G.K + k) * LEAF * RANK;
+      F.w[l][0] = *reinterpret_cast<const float4*>(Wl + row * RANK + 4 * c8);
+      F.w[l][1] = *reinterpret_cast<const float4*>(Wl + (row + 64) * RANK + 4 * c8);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < 8; ++m) F.u[m] = *reinterpret_cast<const float4*>(Uk + (rg + 16 * m) * LEAF + 4 * cs);
+}
+
+// Strip aggregation (eq. (3)) from the staged partner restrictions of r
+// (stR, level l at stage row 2^l - 1) and of q (stQ): sm.P[l] = sum(stR) -
+// alpha sum(stQ), or sum(stR) with stQ == nullptr.  16 groups of threads per
+// column, then across waves; two barriers.
+template <typename T, int LEV>
+__device__ __forceinline__ void prolong_strips(RSmem<T>& sm, const T* stR, const T* stQ, double alpha) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = tid & 31, g = tid >> 5;
+#pragma unroll
+  for (int l = 0; l < LEV; ++l) {
+    const T* vr = stR + (size_t)((1 << l) - 1) * RANK + c;
+    T a = 0, b = 0;
+#pragma unroll
+    for (int m = 0; m < ((1 << l) + 15) / 16; ++m) {
+      const int i = g + 16 * m;
+      if (i < (1 << l)) {
+        a += vr[i * RANK];
+        if (stQ) b += stQ[(size_t)((1 << l) - 1) * RANK + c + i * RANK];
+      }
+    }
+    a += lane_x32(a);
+    if (stQ) b += lane_x32(b);
+    if (lane < 32) {
+      sm.redW[wave][l * RANK + c] = a;
+      if (stQ) sm.redW[wave][(MAX_LEVELS + l) * RANK + c] = b;
+    }
+  }
+  __syncthreads();
+  if (tid < LEV * RANK) {
+    T a = sm.redW[0][tid];
+#pragma unroll
+    for (int w = 1; w < NWR; ++w) a += sm.redW[w][tid];
+    if (stQ) {
+      T b = sm.redW[0][MAX_LEVELS * RANK + tid];
+#pragma unroll
+      for (int w = 1; w < NWR; ++w) b += sm.redW[w][MAX_LEVELS * RANK + tid];
+      a = (T)((double)a - alpha * (double)b);
+    }
+    sm.P[tid] = a;
+  }
+  __syncthreads();
+}
+
+// Diagonal stage U_k sm.t into sm.yleaf: rows rg + 16m (m < 8), dots over 32
+// column slots; the eight rows of a lane are folded with a transpose-reduce
+// (7 + 2 shuffles).  No barrier.
+template <typename T, int LEV>
+__device__ __forceinline__ void prolong_diag(const Resident<T, LEV>& F, RSmem<T>& sm) {
+  const int tid = threadIdx.x;
+  const int cs = tid & 31, rg = tid >> 5;
+  const Vec4<T> t4 = lds4(&sm.t[4 * cs]);
+  T v[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) v[m] = dot4(F.u[m], t4);
+  const bool b4 = (cs & 16) != 0, b3 = (cs & 8) != 0, b2 = (cs & 4) != 0;
+  T a[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {           // xor 16: keep the upper four rows if b4
+    const T keep = b4 ? v[4 + i] : v[i], send = b4 ? v[i] : v[4 + i];
+    a[i] = keep + lane_x16(send);
+  }
+  T bb[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {           // xor 8
+    const T keep = b3 ? a[2 + i] : a[i], send = b3 ? a[i] : a[2 + i];
+    bb[i] = keep + lane_x8(send);
+  }
+  T kk = b2 ? bb[1] : bb[0];              // bit 2 (lane j pairs with 7 - j)
+  kk += lane_m4(b2 ? bb[0] : bb[1]);
+  kk = group4_sum(kk);
+  if ((cs & 3) == 0) sm.yleaf[rg + 16 * ((b4 ? 4 : 0) + (b3 ? 2 : 0) + (b2 ? 1 : 0))] = kk;
+}
+
+// Off-diagonal prolongation sum_l W_l[k] sm.P[l] into sm.yoff (eq. (5)).
+// No barrier.
+template <typename T, int LEV>
+__device__ __forceinline__ void prolong_offdiag(const Resident<T, LEV>& F, RSmem<T>& sm) {
+  const int tid = threadIdx.x;
+  if constexpr (LEV > 0) {
+    const int cs = tid & 7, row = tid >> 3;
+    T o0 = 0, o1 = 0;
+#pragma unroll
+    for (int l = 0; l < LEV; ++l) {
+      const Vec4<T> p4 = lds4(&sm.P[l * RANK + 4 * cs]);
+      o0 += dot4(F.w[l][0], p4);
+      o1 += dot4(F.w[l][1], p4);
+    }
+    o0 = group8_sum(o0);
+    o1 = group8_sum(o1);
+    if (cs == 0) { sm.yoff[row] = o0; sm.yoff[row + 64] = o1; }
+  } else {
+    if (tid < LEAF) sm.yoff[tid] = 0;
+  }
+}
+
+}  // namespace hpcg

@@ -34,43 +34,9 @@
 // the barrier number on a line of its own that the others poll.
 #pragma once
 #include "hpcg_kernels.hpp"
+#include "hpcg_leaf.hpp"
 
 namespace hpcg {
-
-constexpr int NTR = 512;
-constexpr int NWR = NTR / 64;
-
-template <typename T>
-struct alignas(16) RSmem {
-  T r[LEAF];
-  T q[LEAF];
-  T z[LEAF];
-  T p[LEAF];                         // p of the current iteration (own rows)
-  T tr[LEAF];                        // U_k^T r
-  T tq[LEAF];                        // U_k^T q
-  T t[LEAF];                         // U_k^T r_new = tr - alpha tq
-  T P[MAX_LEVELS * RANK];            // partner-half sums
-  T ownR[MAX_LEVELS * RANK];         // this leaf's W_l[k]^T r
-  T ownQ[MAX_LEVELS * RANK];         // this leaf's W_l[k]^T q
-  T yleaf[LEAF];
-  T yoff[LEAF];
-  T red[NWR][LEAF];                  // cross-wave reductions of t
-  T redW[NWR][2 * MAX_LEVELS * RANK];  // cross-wave reductions (restriction, strip sums)
-  double dred[NWR];
-  double dred2[NWR];
-  double dsc[4];
-  int flag[4];
-};
-
-// Agent-scope (XCD-coherent) load and store of one value.
-template <typename T>
-__device__ __forceinline__ T ld_c(const T* p) {
-  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <typename T>
-__device__ __forceinline__ void st_c(T* p, T v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // Device-wide barrier over agent-coherent data (see the header).  `epoch`
 // counts this workgroup's barriers; the flag holds the last completed one.
@@ -164,75 +130,6 @@ __device__ __forceinline__ double sum_partials_r(const double* part, int s, int 
 template <typename T>
 constexpr int kRefresh = sizeof(T) == 8 ? 8 : 1;
 
-template <typename T, int LEV>
-struct Resident {
-  float4 u[8];
-  float4 w[LEV > 0 ? LEV : 1][2];
-};
-
-// Per-wave partials of U_k^T v into sm.red[wave] (thread = 4-column slot cs
-// of 32, row group rg of 16; the two row groups of a wave are added with xor
-// 32).  No barrier.
-template <typename T, int LEV>
-__device__ __forceinline__ void restrict_u_partials(const Resident<T, LEV>& F, const T* v, RSmem<T>& sm) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int cs = tid & 31, rg = tid >> 5;
-  Vec4<T> acc{0, 0, 0, 0};
-#pragma unroll
-  for (int m = 0; m < 8; ++m) axpy4(acc, F.u[m], v[rg + 16 * m]);
-  acc.x += lane_x32(acc.x); acc.y += lane_x32(acc.y);
-  acc.z += lane_x32(acc.z); acc.w += lane_x32(acc.w);
-  if (lane < 32) {
-    T* d = &sm.red[wave][4 * cs];
-    d[0] = acc.x; d[1] = acc.y; d[2] = acc.z; d[3] = acc.w;
-  }
-}
-
-// Per-wave partials of W_l[k]^T v for every level into sm.redW[wave].
-// Thread = (4-column slot cs of 8, rows row and row + 64); the eight rows of
-// a wave (lane bits 3..5) are folded per pair of levels with a
-// transpose-reduce: 8 values -> 1 per lane in 4 + 2 + 1 shuffles.  No barrier.
-template <typename T, int LEV>
-__device__ __forceinline__ void restrict_w_partials(const Resident<T, LEV>& F, const T* v, RSmem<T>& sm) {
-  if constexpr (LEV > 0) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int cs = tid & 7, row = tid >> 3;
-    const T r0 = v[row], r1 = v[row + 64];
-    const bool b5 = (lane & 32) != 0, b4 = (lane & 16) != 0, b3 = (lane & 8) != 0;
-    const int which = (b5 ? 4 : 0) + (b4 ? 2 : 0) + (b3 ? 1 : 0);   // value index a lane ends with
-#pragma unroll
-    for (int l0 = 0; l0 < LEV; l0 += 2) {
-      T x[8];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        Vec4<T> acc{0, 0, 0, 0};
-        if (l0 + h < LEV) {
-          axpy4(acc, F.w[l0 + h < LEV ? l0 + h : 0][0], r0);
-          axpy4(acc, F.w[l0 + h < LEV ? l0 + h : 0][1], r1);
-        }
-        x[4 * h + 0] = acc.x; x[4 * h + 1] = acc.y; x[4 * h + 2] = acc.z; x[4 * h + 3] = acc.w;
-      }
-      T a[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const T keep = b5 ? x[4 + i] : x[i], send = b5 ? x[i] : x[4 + i];
-        a[i] = keep + lane_x32(send);
-      }
-      T bb[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const T keep = b4 ? a[2 + i] : a[i], send = b4 ? a[i] : a[2 + i];
-        bb[i] = keep + lane_x16(send);
-      }
-      T kk = b3 ? bb[1] : bb[0];
-      kk += lane_x8(b3 ? bb[0] : bb[1]);
-      // value index `which` = 4h + component: level l0 + which/4, column 4cs + which%4
-      const int l = l0 + (which >> 2);
-      if (l < LEV) sm.redW[wave][l * RANK + 4 * cs + (which & 3)] = kk;
-    }
-  }
-}
-
 // Restriction of the LDS vector v: U_k^T v into tout (LDS, complete) and
 // W_l[k]^T v into pout (global, [levels][K][RANK] of system s; skipped when
 // null) and own (LDS).  With part_dst, the workgroup sum of `loc` is stored
@@ -289,101 +186,6 @@ __device__ __forceinline__ void r_stage_partners(const Geom& G, const T* src, in
   }
 }
 
-// Strip aggregation (eq. (3)) from the staged partner restrictions of r
-// (stR, level l at stage row 2^l - 1) and of q (stQ): sm.P[l] = sum(stR) -
-// alpha sum(stQ), or sum(stR) with stQ == nullptr.  16 groups of threads per
-// column, then across waves; two barriers.
-template <typename T, int LEV>
-__device__ __forceinline__ void prolong_strips(RSmem<T>& sm, const T* stR, const T* stQ, double alpha) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = tid & 31, g = tid >> 5;
-#pragma unroll
-  for (int l = 0; l < LEV; ++l) {
-    const T* vr = stR + (size_t)((1 << l) - 1) * RANK + c;
-    T a = 0, b = 0;
-#pragma unroll
-    for (int m = 0; m < ((1 << l) + 15) / 16; ++m) {
-      const int i = g + 16 * m;
-      if (i < (1 << l)) {
-        a += vr[i * RANK];
-        if (stQ) b += stQ[(size_t)((1 << l) - 1) * RANK + c + i * RANK];
-      }
-    }
-    a += lane_x32(a);
-    if (stQ) b += lane_x32(b);
-    if (lane < 32) {
-      sm.redW[wave][l * RANK + c] = a;
-      if (stQ) sm.redW[wave][(MAX_LEVELS + l) * RANK + c] = b;
-    }
-  }
-  __syncthreads();
-  if (tid < LEV * RANK) {
-    T a = sm.redW[0][tid];
-#pragma unroll
-    for (int w = 1; w < NWR; ++w) a += sm.redW[w][tid];
-    if (stQ) {
-      T b = sm.redW[0][MAX_LEVELS * RANK + tid];
-#pragma unroll
-      for (int w = 1; w < NWR; ++w) b += sm.redW[w][MAX_LEVELS * RANK + tid];
-      a = (T)((double)a - alpha * (double)b);
-    }
-    sm.P[tid] = a;
-  }
-  __syncthreads();
-}
-
-// Diagonal stage U_k sm.t into sm.yleaf: rows rg + 16m (m < 8), dots over 32
-// column slots; the eight rows of a lane are folded with a transpose-reduce
-// (7 + 2 shuffles).  No barrier.
-template <typename T, int LEV>
-__device__ __forceinline__ void prolong_diag(const Resident<T, LEV>& F, RSmem<T>& sm) {
-  const int tid = threadIdx.x;
-  const int cs = tid & 31, rg = tid >> 5;
-  const Vec4<T> t4 = lds4(&sm.t[4 * cs]);
-  T v[8];
-#pragma unroll
-  for (int m = 0; m < 8; ++m) v[m] = dot4(F.u[m], t4);
-  const bool b4 = (cs & 16) != 0, b3 = (cs & 8) != 0, b2 = (cs & 4) != 0;
-  T a[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {           // xor 16: keep the upper four rows if b4
-    const T keep = b4 ? v[4 + i] : v[i], send = b4 ? v[i] : v[4 + i];
-    a[i] = keep + lane_x16(send);
-  }
-  T bb[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {           // xor 8
-    const T keep = b3 ? a[2 + i] : a[i], send = b3 ? a[i] : a[2 + i];
-    bb[i] = keep + lane_x8(send);
-  }
-  T kk = b2 ? bb[1] : bb[0];              // bit 2 (lane j pairs with 7 - j)
-  kk += lane_m4(b2 ? bb[0] : bb[1]);
-  kk = group4_sum(kk);
-  if ((cs & 3) == 0) sm.yleaf[rg + 16 * ((b4 ? 4 : 0) + (b3 ? 2 : 0) + (b2 ? 1 : 0))] = kk;
-}
-
-// Off-diagonal prolongation sum_l W_l[k] sm.P[l] into sm.yoff (eq. (5)).
-// No barrier.
-template <typename T, int LEV>
-__device__ __forceinline__ void prolong_offdiag(const Resident<T, LEV>& F, RSmem<T>& sm) {
-  const int tid = threadIdx.x;
-  if constexpr (LEV > 0) {
-    const int cs = tid & 7, row = tid >> 3;
-    T o0 = 0, o1 = 0;
-#pragma unroll
-    for (int l = 0; l < LEV; ++l) {
-      const Vec4<T> p4 = lds4(&sm.P[l * RANK + 4 * cs]);
-      o0 += dot4(F.w[l][0], p4);
-      o1 += dot4(F.w[l][1], p4);
-    }
-    o0 = group8_sum(o0);
-    o1 = group8_sum(o1);
-    if (cs == 0) { sm.yoff[row] = o0; sm.yoff[row + 64] = o1; }
-  } else {
-    if (tid < LEAF) sm.yoff[tid] = 0;
-  }
-}
-
 // z = M r_new on the leaf's rows into sm.z.  Needs sm.t (= U_k^T r_new), sm.r
 // (= r_new) and the staged partner restrictions of r (stR) and q (stQ):
 // P_l = sum(stR) - alpha sum(stQ).  With stQ == nullptr, P_l = sum(stR).
@@ -398,151 +200,6 @@ __device__ __forceinline__ void r_prolong(const Resident<T, LEV>& F, RSmem<T>& s
   __syncthreads();
   if (tid < LEAF) sm.z[tid] = sm.yleaf[tid] + sm.yoff[tid] + (T)gate * sm.r[tid];
   __syncthreads();
-}
-
-// U_k and the leaf's level slabs into the register layout of Resident.
-template <typename T, int LEV>
-__device__ __forceinline__ void load_factors(const Geom& G, const Bufs& B, int s, int k, Resident<T, LEV>& F) {
-  const int tid = threadIdx.x;
-  const int cs = tid & 31, rg = tid >> 5;
-  const float* Uk = B.U + ((size_t)s * G.K + k) * LEAF * LEAF;
-  // slabs first: the single-pass apply publishes their restriction before it
-  // needs U_k
-  if constexpr (LEV > 0) {
-    const int c8 = tid & 7, row = tid >> 3;
-#pragma unroll
-    for (int l = 0; l < LEV; ++l) {
-      const float* Wl = B.W + (((size_t)s * G.levels + l) * G.K + k) * LEAF * RANK;
-      F.w[l][0] = *reinterpret_cast<const float4*>(Wl + row * RANK + 4 * c8);
-      F.w[l][1] = *reinterpret_cast<const float4*>(Wl + (row + 64) * RANK + 4 * c8);
-    }
-  }
-#pragma unroll
-  for (int m = 0; m < 8; ++m) F.u[m] = *reinterpret_cast<const float4*>(Uk + (rg + 16 * m) * LEAF + 4 * cs);
-}
-
-// Single-launch apply y = M r (fp32 in and out) for batches whose leaves all
-// get a compute unit: the workgroup of leaf k loads U_k and its slabs into
-// registers once, restricts (eq. (2)), gathers the partner halves'
-// restrictions (eq. (3)), and prolongs (eqs. (4)-(5)) and adds the diagonal
-// stage and the gate with the same registers, so every factor byte crosses HBM
-// once per apply.
-//
-// No device-wide barrier: each restriction value travels with the number of
-// the call that produced it, packed into one 8-byte word (value in the low
-// half, epoch in the high half) that is stored and loaded as a whole with
-// agent-scope atomics, so a reader that sees the epoch it expects also sees
-// that call's value.  The epoch of a leaf counts the calls that leaf has
-// completed (every call runs every leaf once, so all leaves agree at a call's
-// start); the words hold the previous call's epoch until overwritten.  A
-// reader therefore polls exactly the words it needs, and a workgroup waits for
-// its partners only, for about one memory round trip after the last of them
-// has written.  The polls are bounded: past the bound the abort flag is raised
-// and the output is undefined (only if other work holds the device's compute
-// units for about a second).
-template <int LEV>
-__device__ __forceinline__ void gather_partners_ll(const Geom& G, const Bufs& B, int s, int k, unsigned want,
-                                                   float* stage) {
-  if constexpr (LEV > 0) {
-    // word w = row * RANK + c, row = 2^l - 1 + i: column c of the i-th leaf of
-    // level l's partner half, staged at the same position
-    constexpr int NWORDS = RANK * ((1 << LEV) - 1);
-    constexpr int WPT = (NWORDS + NTR - 1) / NTR;
-    const int tid = threadIdx.x;
-    const unsigned long long* src[WPT];
-    unsigned long long v[WPT];
-#pragma unroll
-    for (int j = 0; j < WPT; ++j) {
-      const int w = tid + j * NTR;
-      src[j] = nullptr;
-      if (w < NWORDS) {
-        const int row = w / RANK, c = w - row * RANK;
-        const int l = 31 - __clz(row + 1);
-        const int kp = (((k >> l) ^ 1) << l) + (row + 1 - (1 << l));
-        src[j] = B.llw + (((size_t)s * G.levels + l) * G.K + kp) * RANK + c;
-        v[j] = ld_c(src[j]);
-      }
-    }
-    // re-poll every word still short of its epoch together, so that a late
-    // partner costs one round trip, not one per word
-    unsigned pending = 0;
-#pragma unroll
-    for (int j = 0; j < WPT; ++j)
-      if (src[j] && (unsigned)(v[j] >> 32) != want) pending |= 1u << j;
-    unsigned polls = 0;
-    while (pending) {
-      __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-      for (int j = 0; j < WPT; ++j)
-        if (pending & (1u << j)) v[j] = ld_c(src[j]);
-#pragma unroll
-      for (int j = 0; j < WPT; ++j)
-        if ((pending & (1u << j)) && (unsigned)(v[j] >> 32) == want) pending &= ~(1u << j);
-      if (++polls > (1u << 20)) {
-        st_c(B.abort_flag, 1);
-        break;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < WPT; ++j)
-      if (src[j]) stage[tid + j * NTR] = __uint_as_float((unsigned)v[j]);
-  }
-}
-
-template <int LEV>
-__global__ __launch_bounds__(NTR) void k_apply_fused(Geom G, Bufs B, const float* __restrict__ rin,
-                                                     float* __restrict__ yout) {
-  __shared__ RSmem<float> sm;
-  extern __shared__ int4 fdyn4[];
-  float* stR = reinterpret_cast<float*>(fdyn4);
-  const int tid = threadIdx.x;
-  const int item = blockIdx.x;
-  const int s = item / G.K, k = item - s * G.K;
-  const int leaf0 = s * G.n + k * LEAF;
-  // r, the gate and the epoch are issued before the factors: the loads
-  // return in order, so storing r to LDS then waits for r alone
-  float rv = 0.f, gate = 0.f;
-  if (tid < LEAF) {
-    rv = rin[leaf0 + tid];
-    gate = B.g[leaf0 + tid];
-  }
-  const unsigned want = ld_c(B.lle + item) + 1u;
-  Resident<float, LEV> F;
-  load_factors(G, B, s, k, F);
-  if (tid < LEAF) sm.r[tid] = rv;
-  __syncthreads();
-  // the slabs' restriction (what the partners need) first, then U_k^T r
-  if constexpr (LEV > 0) {
-    restrict_w_partials<float, LEV>(F, sm.r, sm);
-    __syncthreads();
-    if (tid < LEV * RANK) {
-      float a = sm.redW[0][tid];
-#pragma unroll
-      for (int w = 1; w < NWR; ++w) a += sm.redW[w][tid];
-      const int l = tid / RANK, c = tid - l * RANK;
-      st_c(B.llw + (((size_t)s * G.levels + l) * G.K + k) * RANK + c,
-           ((unsigned long long)want << 32) | __float_as_uint(a));
-    }
-  }
-  restrict_u_partials<float, LEV>(F, sm.r, sm);
-  __syncthreads();
-  if (tid < LEAF) {
-    float a = sm.red[0][tid];
-#pragma unroll
-    for (int w = 1; w < NWR; ++w) a += sm.red[w][tid];
-    sm.t[tid] = a;
-  }
-  __syncthreads();
-  // the diagonal stage needs nothing from other leaves: it runs while the
-  // partners' words are in flight
-  prolong_diag<float, LEV>(F, sm);
-  gather_partners_ll<LEV>(G, B, s, k, want, stR);
-  __syncthreads();
-  if constexpr (LEV > 0) prolong_strips<float, LEV>(sm, stR, (const float*)nullptr, 0.0);
-  prolong_offdiag<float, LEV>(F, sm);
-  __syncthreads();
-  if (tid < LEAF) yout[leaf0 + tid] = sm.yleaf[tid] + sm.yoff[tid] + gate * sm.r[tid];
-  if (tid == 0) st_c(B.lle + item, want);
 }
 
 template <typename T, int LEV>
