@@ -259,9 +259,24 @@ def main(argv=None):
             t_spmv = time_graph(lambda: hpcg.hpcg_spmv_block(solver.handle, solver.part, R, X, nrhs),
                                 max(20, args.reps // 10), stream, torch)
         fl = block_apply_flops(batch.n, batch.levels, nrhs, batch.batch)
+        # block PCG on the same block (every column its own solve)
+        Bm = torch.randn(batch.batch * batch.n * nrhs, device="cuda", dtype=torch.float32)
+        torch.cuda.synchronize()
+        solver.solve_block(Bm, nrhs, tol=batch.tol, maxit=batch.maxit)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        reps = 3
+        for _ in range(reps):
+            _X, its_b, _rel, st_b = solver.solve_block(Bm, nrhs, tol=batch.tol, maxit=batch.maxit)
+        torch.cuda.synchronize()
+        ms_block = (time.perf_counter() - t0) * 1e3 / reps
         solver.close()
         tf = fl / t_apply / 1e6
+        solve = {"ms_per_block_solve": round(ms_block, 3), "status": st_b,
+                 "iterations": {"min": min(its_b), "max": max(its_b)},
+                 "column_solves_per_s": round(nrhs * batch.batch / ms_block * 1e3, 1)}
         return {"workload": name, "nrhs": nrhs, "probe_columns": kz, "apply_us": round(t_apply, 3),
+                "block_solve": solve,
                 "tflops": round(tf, 2), "peak_tflops": FP32_MFMA_PEAK_TFLOPS,
                 "frac": round(tf / FP32_MFMA_PEAK_TFLOPS, 4), "flops": fl, "dtype": "f32 (mfma 16x16x4)",
                 "spmv_block_us": round(t_spmv, 3)}

@@ -298,6 +298,30 @@ hpcg_status hpcg_solve_refined(hpcg_handle h, const float* d_b, double* d_x, dou
                                double* h_relres);
 
 
+/* Block PCG: for every system s and column j of a block of right-hand sides,
+ * an independent preconditioned CG on A_s x = b_{s,j} (x_0 = 0, stop when
+ * ||r|| <= tol ||b||, the rules of hpcg_solve), run in lockstep so that each
+ * application of M is one block apply on the matrix cores and each product
+ * with A one block SpMV: the multi-vector form of "Hierarchical Transformer
+ * Preconditioning for Interactive Physics Simulation", section 5, stages
+ * (i)-(ii).  Columns share nothing but the launches; each keeps its own step
+ * sizes, test and count, and a finished column stays as it was while the
+ * others continue.
+ *  d_B      fp32 [batch*n][nrhs], node-major (the block apply's layout), 16-byte aligned
+ *  d_X      fp64 [batch*n][nrhs] out, node-major, 16-byte aligned
+ *  nrhs     multiple of 16 in [16, 1024]
+ *  d_work   device scratch of hpcg_block_solve_workspace_bytes(h, nrhs) bytes
+ *  h_iters  [batch*nrhs] iterations per (system, column), system-major (may be NULL)
+ *  h_relres [batch*nrhs] final recursive ||r|| / ||b|| (may be NULL)
+ * Arithmetic: R, Z, P, Q fp32 (the block apply's), x and all scalars fp64.
+ * Direct form only (HPCG_ERR_STATE otherwise).  Returns HPCG_ERR_BREAKDOWN or
+ * HPCG_ERR_NOT_CONVERGED when some column ends so (x and counts still
+ * written).  Records the iterations in a hipGraph, kept for repeated calls
+ * with the same buffers; synchronizes with the host once per replay. */
+size_t hpcg_block_solve_workspace_bytes(hpcg_handle h, int32_t nrhs);
+hpcg_status hpcg_solve_block(hpcg_handle h, const float* d_B, double* d_X, int32_t nrhs, double tol, int32_t maxit,
+                             void* d_work, size_t work_bytes, int32_t* h_iters, double* h_relres);
+
 /* Per-system hpcg_system_status values of the last hpcg_solve, int32 [batch]. */
 hpcg_status hpcg_last_solve_status(hpcg_handle h, int32_t* h_status);
 

@@ -18,6 +18,7 @@
 #include "hpcg_apply.hpp"
 #include "hpcg_resident.hpp"
 #include "hpcg_block.hpp"
+#include "hpcg_bsolve.hpp"
 
 using namespace hpcg;
 
@@ -175,8 +176,14 @@ struct hpcg_ctx {
   int last_grid = 0;
   int last_lds = 0;
   int max_leaf_nnz = 0;
-  int* h_flag = nullptr;   // pinned, device-mapped
+  int* h_flag = nullptr;   // pinned, device-mapped (word 0: graph engine, word 16: block solve)
   int* d_flag = nullptr;
+  // block solve: the recorded iterations and what they were recorded for
+  hipGraph_t bs_graph = nullptr;
+  hipGraphExec_t bs_gexec = nullptr;
+  const void* bs_key[2] = {nullptr, nullptr};
+  int bs_nrhs = 0, bs_unroll = 0, bs_maxit = -1;
+  double bs_tol = -1.0;
   SysState* h_st = nullptr;
   int* h_ctl = nullptr;    // pinned copy of the abort flag
   std::vector<int32_t> last_status;
@@ -701,6 +708,43 @@ size_t block_half_bytes(const hpcg_ctx* h, int32_t nrhs) {
   return align_up((size_t)h->G.B * h->G.levels * h->G.K * RANK * nrhs * 4);
 }
 
+// The three launches of Y = M R for a block (scratch Q and H of
+// block_half_bytes each; unused without tile levels).
+hpcg_status launch_block_apply(hpcg_ctx* h, int32_t nrhs, const float* d_R, float* d_Y, float* Q, float* H,
+                               hipStream_t stream) {
+  const BlockGeom bg = block_geom(h, nrhs);
+  const int grid = h->G.B * h->G.K * bg.tiles;
+  switch (h->G.levels) {
+#define HPCG_BLOCK_RESTRICT(LV)                                                                          \
+    case LV:                                                                                             \
+      hipLaunchKernelGGL(k_block_restrict<LV>, dim3(grid), dim3(BNT), 0, stream, bg, h->B.U, h->B.W,     \
+                         h->B.g, d_R, d_Y, Q);                                                           \
+      break;
+    HPCG_BLOCK_RESTRICT(0) HPCG_BLOCK_RESTRICT(1) HPCG_BLOCK_RESTRICT(2) HPCG_BLOCK_RESTRICT(3)
+    HPCG_BLOCK_RESTRICT(4) HPCG_BLOCK_RESTRICT(5) HPCG_BLOCK_RESTRICT(6) HPCG_BLOCK_RESTRICT(7)
+    HPCG_BLOCK_RESTRICT(8)
+#undef HPCG_BLOCK_RESTRICT
+    default: return fail(h, HPCG_ERR_SHAPE, "levels out of range");
+  }
+  if (h->G.levels > 0) {
+    size_t sys_total = 0;
+    for (int l = 0; l < h->G.levels; ++l) sys_total += (size_t)(h->G.K >> l) * RANK * nrhs;
+    const size_t total = sys_total * h->G.B;
+    hipLaunchKernelGGL(k_block_halfsum, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, bg, Q, H);
+    switch (h->G.levels) {
+#define HPCG_BLOCK_PROLONG(LV)                                                                          \
+      case LV:                                                                                          \
+        hipLaunchKernelGGL(k_block_prolong<LV>, dim3(grid), dim3(BNT), 0, stream, bg, h->B.W, H, d_Y);  \
+        break;
+      HPCG_BLOCK_PROLONG(1) HPCG_BLOCK_PROLONG(2) HPCG_BLOCK_PROLONG(3) HPCG_BLOCK_PROLONG(4)
+      HPCG_BLOCK_PROLONG(5) HPCG_BLOCK_PROLONG(6) HPCG_BLOCK_PROLONG(7) HPCG_BLOCK_PROLONG(8)
+#undef HPCG_BLOCK_PROLONG
+      default: return fail(h, HPCG_ERR_SHAPE, "levels out of range");
+    }
+  }
+  return HPCG_OK;
+}
+
 }  // namespace
 
 size_t hpcg_block_workspace_bytes(hpcg_handle h, int32_t nrhs) {
@@ -723,39 +767,10 @@ hpcg_status hpcg_apply_M_block(hpcg_handle h, const float* d_R, float* d_Y, int3
     if (!d_work) return fail(h, HPCG_ERR_INVALID_ARG, "d_work is NULL");
     if (work_bytes < hpcg_block_workspace_bytes(h, nrhs)) return fail(h, HPCG_ERR_WORKSPACE, "block workspace too small");
   }
-  const BlockGeom bg = block_geom(h, nrhs);
   char* wk = reinterpret_cast<char*>(align_up(reinterpret_cast<uintptr_t>(d_work)));
-  float* Q = reinterpret_cast<float*>(wk);
-  float* H = reinterpret_cast<float*>(wk + half);
-  const int grid = h->G.B * h->G.K * bg.tiles;
-  switch (h->G.levels) {
-#define HPCG_BLOCK_RESTRICT(LV)                                                                          \
-    case LV:                                                                                             \
-      hipLaunchKernelGGL(k_block_restrict<LV>, dim3(grid), dim3(BNT), 0, h->stream, bg, h->B.U, h->B.W, \
-                         h->B.g, d_R, d_Y, Q);                                                           \
-      break;
-    HPCG_BLOCK_RESTRICT(0) HPCG_BLOCK_RESTRICT(1) HPCG_BLOCK_RESTRICT(2) HPCG_BLOCK_RESTRICT(3)
-    HPCG_BLOCK_RESTRICT(4) HPCG_BLOCK_RESTRICT(5) HPCG_BLOCK_RESTRICT(6) HPCG_BLOCK_RESTRICT(7)
-    HPCG_BLOCK_RESTRICT(8)
-#undef HPCG_BLOCK_RESTRICT
-    default: return fail(h, HPCG_ERR_SHAPE, "levels out of range");
-  }
-  if (h->G.levels > 0) {
-    size_t sys_total = 0;
-    for (int l = 0; l < h->G.levels; ++l) sys_total += (size_t)(h->G.K >> l) * RANK * nrhs;
-    const size_t total = sys_total * h->G.B;
-    hipLaunchKernelGGL(k_block_halfsum, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, h->stream, bg, Q, H);
-    switch (h->G.levels) {
-#define HPCG_BLOCK_PROLONG(LV)                                                                          \
-      case LV:                                                                                          \
-        hipLaunchKernelGGL(k_block_prolong<LV>, dim3(grid), dim3(BNT), 0, h->stream, bg, h->B.W, H, d_Y); \
-        break;
-      HPCG_BLOCK_PROLONG(1) HPCG_BLOCK_PROLONG(2) HPCG_BLOCK_PROLONG(3) HPCG_BLOCK_PROLONG(4)
-      HPCG_BLOCK_PROLONG(5) HPCG_BLOCK_PROLONG(6) HPCG_BLOCK_PROLONG(7) HPCG_BLOCK_PROLONG(8)
-#undef HPCG_BLOCK_PROLONG
-      default: return fail(h, HPCG_ERR_SHAPE, "levels out of range");
-    }
-  }
+  hpcg_status s = launch_block_apply(h, nrhs, d_R, d_Y, reinterpret_cast<float*>(wk),
+                                     reinterpret_cast<float*>(wk + half), h->stream);
+  if (s != HPCG_OK) return s;
   return check_launch(h, "hpcg_apply_M_block launch");
 }
 
@@ -770,6 +785,179 @@ hpcg_status hpcg_spmv_block(hpcg_handle h, const float* d_X, float* d_Y, int32_t
   hipLaunchKernelGGL(k_spmv_block, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, h->stream, h->B.row_ptr,
                      h->B.col, h->B.val, d_X, d_Y, h->G.B * h->G.n, nrhs);
   return check_launch(h, "hpcg_spmv_block launch");
+}
+
+namespace {
+
+// Sub-buffers of the block solve's caller-provided work buffer.
+struct BlockSolveLayout {
+  size_t R, Z, P, Q, scratchQ, scratchH, part, cs, ctr, total;
+};
+
+BlockSolveLayout block_solve_layout(const hpcg_ctx* h, int32_t nrhs) {
+  BlockSolveLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+  const size_t vec = (size_t)h->G.B * h->G.n * nrhs * 4;
+  L.R = take(vec);
+  L.Z = take(vec);
+  L.P = take(vec);
+  L.Q = take(vec);
+  const size_t half = h->G.levels > 0 ? block_half_bytes(h, nrhs) : 0;
+  L.scratchQ = take(half);
+  L.scratchH = take(half);
+  L.part = take((size_t)h->G.B * h->G.K * nrhs * 8);
+  L.cs = take((size_t)h->G.B * nrhs * sizeof(ColState));
+  L.ctr = take(256);
+  L.total = off;
+  return L;
+}
+
+// One block-PCG iteration (nine steps; see hpcg_bsolve.hpp) on `stream`.
+hpcg_status block_iteration(hpcg_ctx* h, int32_t nrhs, char* wk, const BlockSolveLayout& L, double* d_X,
+                            double tol, int32_t maxit, hipStream_t stream) {
+  const Geom& G = h->G;
+  float* R = reinterpret_cast<float*>(wk + L.R);
+  float* Z = reinterpret_cast<float*>(wk + L.Z);
+  float* P = reinterpret_cast<float*>(wk + L.P);
+  float* Q = reinterpret_cast<float*>(wk + L.Q);
+  double* part = reinterpret_cast<double*>(wk + L.part);
+  ColState* cs = reinterpret_cast<ColState*>(wk + L.cs);
+  const dim3 rows_grid((unsigned)(G.B * G.K), (unsigned)((nrhs + BS_COLS - 1) / BS_COLS));
+  const int ncol = G.B * nrhs;
+  const dim3 sc_grid((unsigned)((ncol + 255) / 256));
+  const size_t threads = (size_t)G.B * G.n * (nrhs / 4);
+  hipLaunchKernelGGL(k_spmv_block, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, h->B.row_ptr,
+                     h->B.col, h->B.val, P, Q, G.B * G.n, nrhs);
+  hipLaunchKernelGGL(k_bs_dot, rows_grid, dim3(BS_NT), 0, stream, P, Q, part, nrhs);
+  hipLaunchKernelGGL(k_bs_scalars<BS_PQ>, sc_grid, dim3(256), 0, stream, cs, part, G.B, nrhs, G.K, tol, maxit);
+  hipLaunchKernelGGL(k_bs_update, rows_grid, dim3(BS_NT), 0, stream, cs, P, Q, R, d_X, part, nrhs, G.K);
+  hipLaunchKernelGGL(k_bs_scalars<BS_RR>, sc_grid, dim3(256), 0, stream, cs, part, G.B, nrhs, G.K, tol, maxit);
+  hpcg_status s = launch_block_apply(h, nrhs, R, Z, reinterpret_cast<float*>(wk + L.scratchQ),
+                                     reinterpret_cast<float*>(wk + L.scratchH), stream);
+  if (s != HPCG_OK) return s;
+  hipLaunchKernelGGL(k_bs_dot, rows_grid, dim3(BS_NT), 0, stream, R, Z, part, nrhs);
+  hipLaunchKernelGGL(k_bs_scalars<BS_RZ>, sc_grid, dim3(256), 0, stream, cs, part, G.B, nrhs, G.K, tol, maxit);
+  hipLaunchKernelGGL(k_bs_direction, rows_grid, dim3(BS_NT), 0, stream, cs, Z, P, nrhs, G.K);
+  return HPCG_OK;
+}
+
+}  // namespace
+
+size_t hpcg_block_solve_workspace_bytes(hpcg_handle h, int32_t nrhs) {
+  if (!h || !block_nrhs_ok(nrhs)) return 0;
+  return block_solve_layout(h, nrhs).total + kAlign;
+}
+
+hpcg_status hpcg_solve_block(hpcg_handle h, const float* d_B, double* d_X, int32_t nrhs, double tol, int32_t maxit,
+                             void* d_work, size_t work_bytes, int32_t* h_iters, double* h_relres) {
+  if (!h) return fail(nullptr, HPCG_ERR_INVALID_ARG, "handle is NULL");
+  if (!d_B || !d_X || !d_work) return fail(h, HPCG_ERR_INVALID_ARG, "block or work pointer is NULL");
+  if (!block_nrhs_ok(nrhs)) return fail(h, HPCG_ERR_SHAPE, "nrhs must be a multiple of 16 in [16, 1024]");
+  if ((reinterpret_cast<uintptr_t>(d_B) | reinterpret_cast<uintptr_t>(d_X)) % 16)
+    return fail(h, HPCG_ERR_INVALID_ARG, "d_B and d_X must be 16-byte aligned");
+  if (!(tol > 0.0) || !(tol < 1.0)) return fail(h, HPCG_ERR_INVALID_ARG, "tol must lie in (0, 1)");
+  if (maxit < 1) return fail(h, HPCG_ERR_INVALID_ARG, "maxit must be >= 1");
+  if (!h->factors_set) return fail(h, HPCG_ERR_STATE, "hpcg_set_factors has not been called");
+  if (h->B.form != FORM_DIRECT) return fail(h, HPCG_ERR_STATE, "the block solve runs the direct form (M = H) only");
+  if (work_bytes < hpcg_block_solve_workspace_bytes(h, nrhs)) return fail(h, HPCG_ERR_WORKSPACE, "block work buffer too small");
+  const Geom& G = h->G;
+  const BlockSolveLayout L = block_solve_layout(h, nrhs);
+  char* wk = reinterpret_cast<char*>(align_up(reinterpret_cast<uintptr_t>(d_work)));
+  float* R = reinterpret_cast<float*>(wk + L.R);
+  float* Z = reinterpret_cast<float*>(wk + L.Z);
+  float* P = reinterpret_cast<float*>(wk + L.P);
+  double* part = reinterpret_cast<double*>(wk + L.part);
+  ColState* cs = reinterpret_cast<ColState*>(wk + L.cs);
+  int* ctr = reinterpret_cast<int*>(wk + L.ctr);
+  int* hflag = h->h_flag + 16;
+  int* dflag = h->d_flag + 16;
+  const dim3 rows_grid((unsigned)(G.B * G.K), (unsigned)((nrhs + BS_COLS - 1) / BS_COLS));
+  const int ncol = G.B * nrhs;
+  const dim3 sc_grid((unsigned)((ncol + 255) / 256));
+
+  // the recorded iterations depend on the buffers, nrhs, tol, maxit and the unroll
+  if (!h->bs_gexec || h->bs_key[0] != d_X || h->bs_key[1] != wk || h->bs_nrhs != nrhs || h->bs_tol != tol ||
+      h->bs_maxit != maxit || h->bs_unroll != h->unroll) {
+    if (h->bs_gexec) (void)hipGraphExecDestroy(h->bs_gexec);
+    if (h->bs_graph) (void)hipGraphDestroy(h->bs_graph);
+    h->bs_gexec = nullptr;
+    h->bs_graph = nullptr;
+    HIP_OR_FAIL(h, hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal));
+    hpcg_status s = HPCG_OK;
+    for (int j = 0; j < h->unroll && s == HPCG_OK; ++j) s = block_iteration(h, nrhs, wk, L, d_X, tol, maxit, h->cap_stream);
+    if (s == HPCG_OK)
+      hipLaunchKernelGGL(k_bs_progress, dim3(1), dim3(256), 0, h->cap_stream, cs, ncol, ctr, dflag);
+    hipGraph_t g = nullptr;
+    const hipError_t e = hipStreamEndCapture(h->cap_stream, &g);
+    if (s != HPCG_OK) { if (g) (void)hipGraphDestroy(g); return s; }
+    if (e != hipSuccess) return hip_fail(h, e, "hipStreamEndCapture (block solve)");
+    h->bs_graph = g;
+    const hipError_t e2 = hipGraphInstantiate(&h->bs_gexec, h->bs_graph, nullptr, nullptr, 0);
+    if (e2 != hipSuccess) return hip_fail(h, e2, "hipGraphInstantiate (block solve)");
+    h->bs_key[0] = d_X;
+    h->bs_key[1] = wk;
+    h->bs_nrhs = nrhs;
+    h->bs_tol = tol;
+    h->bs_maxit = maxit;
+    h->bs_unroll = h->unroll;
+  }
+
+  // R = B, X = 0, ||B_j||, Z = M R, rz, P = Z
+  __atomic_store_n(hflag, 0, __ATOMIC_RELEASE);
+  hipLaunchKernelGGL(k_bs_reset, dim3(1), dim3(64), 0, h->stream, ctr, dflag);
+  hipLaunchKernelGGL(k_bs_init, rows_grid, dim3(BS_NT), 0, h->stream, d_B, R, d_X, part, nrhs);
+  hipLaunchKernelGGL(k_bs_scalars<BS_INIT>, sc_grid, dim3(256), 0, h->stream, cs, part, G.B, nrhs, G.K, tol, maxit);
+  hpcg_status s = launch_block_apply(h, nrhs, R, Z, reinterpret_cast<float*>(wk + L.scratchQ),
+                                     reinterpret_cast<float*>(wk + L.scratchH), h->stream);
+  if (s != HPCG_OK) return s;
+  hipLaunchKernelGGL(k_bs_dot, rows_grid, dim3(BS_NT), 0, h->stream, R, Z, part, nrhs);
+  hipLaunchKernelGGL(k_bs_scalars<BS_RZ0>, sc_grid, dim3(256), 0, h->stream, cs, part, G.B, nrhs, G.K, tol, maxit);
+  hipLaunchKernelGGL(k_bs_direction, rows_grid, dim3(BS_NT), 0, h->stream, cs, Z, P, nrhs, G.K);
+  s = check_launch(h, "block solve setup launch");
+  if (s != HPCG_OK) return s;
+
+  // replays, two in flight, until no column is running (or maxit is spent)
+  const int max_replays = (maxit + h->unroll - 1) / h->unroll;
+  int launched = 0, seen = 0;
+  bool done = false;
+  while (!done) {
+    while (launched < max_replays && launched - seen < 2) {
+      HIP_OR_FAIL(h, hipGraphLaunch(h->bs_gexec, h->stream));
+      ++launched;
+    }
+    unsigned spins = 0;
+    for (;;) {
+      const int f = __atomic_load_n(hflag, __ATOMIC_ACQUIRE);
+      if ((f >> 1) > seen) {
+        seen = f >> 1;
+        done = (f & 1) != 0 || seen >= max_replays;
+        break;
+      }
+      if ((++spins & 1023u) == 0) {
+        const hipError_t q = hipStreamQuery(h->stream);
+        if (q == hipSuccess) {
+          const int f2 = __atomic_load_n(hflag, __ATOMIC_ACQUIRE);
+          if ((f2 >> 1) <= seen) return fail(h, HPCG_ERR_HIP, "block solve: stream drained without progress flag");
+        } else if (q != hipErrorNotReady) {
+          return hip_fail(h, q, "hipStreamQuery");
+        }
+      }
+    }
+  }
+  std::vector<ColState> host((size_t)ncol);
+  HIP_OR_FAIL(h, hipMemcpyAsync(host.data(), cs, host.size() * sizeof(ColState), hipMemcpyDeviceToHost, h->stream));
+  HIP_OR_FAIL(h, hipStreamSynchronize(h->stream));
+  bool any_break = false, any_nc = false;
+  for (int i = 0; i < ncol; ++i) {
+    if (h_iters) h_iters[i] = host[i].iters;
+    if (h_relres) h_relres[i] = host[i].relres;
+    if (host[i].status == ST_BREAKDOWN) any_break = true;
+    else if (host[i].status != ST_CONVERGED) any_nc = true;
+  }
+  if (any_break) return fail(h, HPCG_ERR_BREAKDOWN, "breakdown in some column: p.Ap or r.Mr not positive and finite");
+  if (any_nc) return fail(h, HPCG_ERR_NOT_CONVERGED, "maxit reached before the tolerance in some column");
+  return HPCG_OK;
 }
 
 namespace {
@@ -1113,6 +1301,8 @@ const char* hpcg_last_error(hpcg_handle h) {
 void hpcg_destroy(hpcg_handle h) {
   if (!h) return;
   destroy_graph(h);
+  if (h->bs_gexec) (void)hipGraphExecDestroy(h->bs_gexec);
+  if (h->bs_graph) (void)hipGraphDestroy(h->bs_graph);
   if (h->cap_stream) (void)hipStreamDestroy(h->cap_stream);
   if (h->h_flag) (void)hipHostFree(h->h_flag);
   if (h->h_st) (void)hipHostFree(h->h_st);

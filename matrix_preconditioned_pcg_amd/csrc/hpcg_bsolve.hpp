@@ -1,0 +1,217 @@
+// Block PCG: one independent preconditioned CG per (system, column) of a
+// node-major block of right-hand sides, run in lockstep so that every apply of
+// M is a block apply on the matrix cores (hpcg_block.hpp) and every A product
+// a block SpMV.  The columns share nothing but the launches: each has its own
+// step sizes, its own convergence test and its own iteration count, exactly as
+// if it were solved alone ("Hierarchical Transformer Preconditioning for
+// Interactive Physics Simulation", project page, Background, the
+// preconditioned CG the solve runs; the multi-vector apply of section 5,
+// stages (i)-(ii)).
+//
+// Per iteration, for every running column j:
+//   Q = A P;  pq_j = P_j . Q_j;  alpha_j = rz_j / pq_j;
+//   X_j += alpha_j P_j;  R_j -= alpha_j Q_j;  stop when ||R_j|| / ||B_j|| <= tol;
+//   Z = M R;  rz'_j = R_j . Z_j;  beta_j = rz'_j / rz_j;  P_j = Z_j + beta_j P_j.
+// R, Z, P, Q are fp32 (the block apply's arithmetic), X and every scalar fp64.
+// A finished column gets alpha = beta = 0 from then on, so its X and R stay
+// as they were while the others continue.
+//
+// Dot products: a workgroup owns 128 rows (one leaf) and 64 columns; a thread
+// owns one column and sums rows rg, rg + 4, ... in fp64, the four row groups
+// are added in a fixed order, and the per-leaf partials of a system are added
+// in leaf order by one thread per (system, column): every sum has one fixed
+// order, so a solve is bitwise reproducible.
+#pragma once
+#include "hpcg_device.hpp"
+
+namespace hpcg {
+
+constexpr int BS_ROWS = LEAF;   // rows per workgroup
+constexpr int BS_COLS = 64;     // columns per workgroup
+constexpr int BS_NT = 256;      // threads per workgroup
+
+struct ColState {
+  double bnorm;    // ||B_j||
+  double rz;       // R_j . Z_j of the last completed iteration
+  double alpha;
+  double beta;
+  double relres;   // ||R_j|| / ||B_j|| after the last update
+  int status;      // ST_*
+  int iters;
+  int pad[2];
+};
+
+enum : int { BS_INIT = 0, BS_RZ0 = 1, BS_PQ = 2, BS_RR = 3, BS_RZ = 4 };
+
+// Workgroup (leaf rb, column tile) -> thread's column c, row group rg.
+__device__ __forceinline__ double bs_rowgroup_reduce(double acc, double* red) {
+  const int tid = threadIdx.x, c = tid & (BS_COLS - 1), rg = tid / BS_COLS;
+  red[rg * BS_COLS + c] = acc;
+  __syncthreads();
+  double s = 0.0;
+  if (rg == 0) s = ((red[c] + red[BS_COLS + c]) + red[2 * BS_COLS + c]) + red[3 * BS_COLS + c];
+  return s;
+}
+
+// part[rb][c] = sum over the rows of leaf rb of X[row][c] * Y[row][c].
+__global__ __launch_bounds__(BS_NT) void k_bs_dot(const float* __restrict__ X, const float* __restrict__ Y,
+                                                  double* __restrict__ part, int nrhs) {
+  __shared__ double red[BS_NT];
+  const int tid = threadIdx.x, rg = tid / BS_COLS;
+  const int c = blockIdx.y * BS_COLS + (tid & (BS_COLS - 1));
+  const size_t rb = blockIdx.x;
+  double acc = 0.0;
+  if (c < nrhs) {
+    for (int r = rg; r < BS_ROWS; r += BS_NT / BS_COLS) {
+      const size_t i = (rb * BS_ROWS + r) * nrhs + c;
+      acc = fma((double)X[i], (double)Y[i], acc);
+    }
+  }
+  const double s = bs_rowgroup_reduce(acc, red);
+  if (rg == 0 && c < nrhs) part[rb * nrhs + c] = s;
+}
+
+// R = B, X = 0, part = per-leaf partials of B . B.
+__global__ __launch_bounds__(BS_NT) void k_bs_init(const float* __restrict__ Bm, float* __restrict__ R,
+                                                   double* __restrict__ X, double* __restrict__ part, int nrhs) {
+  __shared__ double red[BS_NT];
+  const int tid = threadIdx.x, rg = tid / BS_COLS;
+  const int c = blockIdx.y * BS_COLS + (tid & (BS_COLS - 1));
+  const size_t rb = blockIdx.x;
+  double acc = 0.0;
+  if (c < nrhs) {
+    for (int r = rg; r < BS_ROWS; r += BS_NT / BS_COLS) {
+      const size_t i = (rb * BS_ROWS + r) * nrhs + c;
+      const float b = Bm[i];
+      R[i] = b;
+      X[i] = 0.0;
+      acc = fma((double)b, (double)b, acc);
+    }
+  }
+  const double s = bs_rowgroup_reduce(acc, red);
+  if (rg == 0 && c < nrhs) part[rb * nrhs + c] = s;
+}
+
+// X += alpha P, R -= alpha Q (alpha per column of the row's system), part =
+// per-leaf partials of the new R . R.  A finished column (alpha = 0) is left
+// untouched, whatever its P and Q hold.
+__global__ __launch_bounds__(BS_NT) void k_bs_update(const ColState* __restrict__ cs, const float* __restrict__ P,
+                                                     const float* __restrict__ Q, float* __restrict__ R,
+                                                     double* __restrict__ X, double* __restrict__ part, int nrhs,
+                                                     int leaves_per_system) {
+  __shared__ double red[BS_NT];
+  const int tid = threadIdx.x, rg = tid / BS_COLS;
+  const int c = blockIdx.y * BS_COLS + (tid & (BS_COLS - 1));
+  const size_t rb = blockIdx.x;
+  const int s = (int)(rb / leaves_per_system);
+  double acc = 0.0;
+  if (c < nrhs) {
+    const double alpha = cs[(size_t)s * nrhs + c].alpha;
+    for (int r = rg; r < BS_ROWS; r += BS_NT / BS_COLS) {
+      const size_t i = (rb * BS_ROWS + r) * nrhs + c;
+      float rn = R[i];
+      if (alpha != 0.0) {
+        X[i] = fma(alpha, (double)P[i], X[i]);
+        rn = (float)((double)rn - alpha * (double)Q[i]);
+        R[i] = rn;
+      }
+      acc = fma((double)rn, (double)rn, acc);
+    }
+  }
+  const double sum = bs_rowgroup_reduce(acc, red);
+  if (rg == 0 && c < nrhs) part[rb * nrhs + c] = sum;
+}
+
+// P = Z + beta P (beta per column of the row's system).  beta = 0 (the first
+// step, and every step of a finished column) takes P = Z without reading P,
+// which holds no value before the first step.
+__global__ __launch_bounds__(BS_NT) void k_bs_direction(const ColState* __restrict__ cs, const float* __restrict__ Z,
+                                                        float* __restrict__ P, int nrhs, int leaves_per_system) {
+  const int tid = threadIdx.x, rg = tid / BS_COLS;
+  const int c = blockIdx.y * BS_COLS + (tid & (BS_COLS - 1));
+  const size_t rb = blockIdx.x;
+  const int s = (int)(rb / leaves_per_system);
+  if (c >= nrhs) return;
+  const double beta = cs[(size_t)s * nrhs + c].beta;
+  for (int r = rg; r < BS_ROWS; r += BS_NT / BS_COLS) {
+    const size_t i = (rb * BS_ROWS + r) * nrhs + c;
+    P[i] = beta == 0.0 ? Z[i] : (float)((double)Z[i] + beta * (double)P[i]);
+  }
+}
+
+// One thread per (system, column): add the system's per-leaf partials in leaf
+// order and take the step the mode names.
+template <int MODE>
+__global__ void k_bs_scalars(ColState* __restrict__ cs, const double* __restrict__ part, int systems, int nrhs,
+                             int leaves_per_system, double tol, int maxit) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= systems * nrhs) return;
+  const int s = idx / nrhs, c = idx - s * nrhs;
+  double sum = 0.0;
+  for (int k = 0; k < leaves_per_system; ++k) sum += part[((size_t)s * leaves_per_system + k) * nrhs + c];
+  ColState st = cs[idx];
+  if constexpr (MODE == BS_INIT) {
+    st.bnorm = sqrt(sum);
+    st.rz = st.alpha = st.beta = 0.0;
+    st.iters = 0;
+    st.status = sum == 0.0 ? ST_CONVERGED : ST_RUNNING;
+    st.relres = sum == 0.0 ? 0.0 : 1.0;
+  } else if constexpr (MODE == BS_RZ0) {
+    st.beta = 0.0;
+    if (st.status == ST_RUNNING) {
+      if (!(sum > 0.0) || !isfinite(sum)) st.status = ST_BREAKDOWN;
+      else st.rz = sum;
+    }
+  } else if constexpr (MODE == BS_PQ) {
+    st.alpha = 0.0;
+    if (st.status == ST_RUNNING) {
+      st.iters += 1;
+      if (!(sum > 0.0) || !isfinite(sum)) st.status = ST_BREAKDOWN;
+      else st.alpha = st.rz / sum;
+    }
+  } else if constexpr (MODE == BS_RR) {
+    if (st.status == ST_RUNNING) {
+      st.relres = sqrt(sum) / st.bnorm;
+      if (st.relres <= tol) st.status = ST_CONVERGED;
+      else if (st.iters >= maxit) st.status = ST_NOT_CONVERGED;
+    }
+  } else {   // BS_RZ
+    st.beta = 0.0;
+    if (st.status == ST_RUNNING) {
+      if (!(sum > 0.0) || !isfinite(sum)) {
+        st.status = ST_BREAKDOWN;
+      } else {
+        st.beta = sum / st.rz;
+        st.rz = sum;
+      }
+    }
+  }
+  cs[idx] = st;
+}
+
+// Progress word for the host: bit 0 = no column is running, bits 1.. = replays
+// completed (counted in *ctr on the device).
+__global__ __launch_bounds__(256) void k_bs_progress(const ColState* __restrict__ cs, int total, int* ctr,
+                                                     int* host_flag) {
+  __shared__ int any;
+  if (threadIdx.x == 0) any = 0;
+  __syncthreads();
+  int mine = 0;
+  for (int i = threadIdx.x; i < total; i += blockDim.x) mine |= (cs[i].status == ST_RUNNING);
+  if (mine) any = 1;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int r = *ctr + 1;
+    *ctr = r;
+    __hip_atomic_store(host_flag, (r << 1) | (any ? 0 : 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+}
+
+__global__ void k_bs_reset(int* ctr, int* host_flag) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    *ctr = 0;
+    __hip_atomic_store(host_flag, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+}
+
+}  // namespace hpcg

@@ -110,6 +110,8 @@ def lib() -> ctypes.CDLL:
         "hpcg_last_engine": (i32, [vp]),
         "hpcg_last_apply_path": (i32, [vp]),
         "hpcg_last_fallback": (i32, [vp]),
+        "hpcg_block_solve_workspace_bytes": (sz, [vp, i32]),
+        "hpcg_solve_block": (i32, [vp, vp, vp, i32, dbl, i32, vp, sz, P(i32), P(dbl)]),
         "hpcg_estimate_spectrum": (i32, [vp, i32, P(dbl), P(dbl)]),
         "hpcg_last_launch_info": (i32, [vp, P(i32), P(i32)]),
         "hpcg_status_string": (ctypes.c_char_p, [i32]),
@@ -291,6 +293,25 @@ def hpcg_last_engine(h) -> int:
     return int(lib().hpcg_last_engine(h))
 
 
+def hpcg_block_solve_workspace_bytes(h, nrhs: int) -> int:
+    return int(lib().hpcg_block_solve_workspace_bytes(h, int(nrhs)))
+
+
+def hpcg_solve_block(h, part: hpcg_partition, B, X, nrhs: int, tol: float, maxit: int, work):
+    """Returns (status, iters[batch*nrhs], relres[batch*nrhs]); raises on
+    argument/HIP errors, not on HPCG_ERR_NOT_CONVERGED or HPCG_ERR_BREAKDOWN."""
+    N = part.n * part.batch
+    cnt = part.batch * nrhs
+    iters = (ctypes.c_int32 * cnt)()
+    rel = (ctypes.c_double * cnt)()
+    st = lib().hpcg_solve_block(h, _ptr(B, torch.float32, N * nrhs, "B"), _ptr(X, torch.float64, N * nrhs, "X"),
+                                int(nrhs), float(tol), int(maxit), _ptr(work, torch.uint8, work.numel(), "work"),
+                                int(work.numel()), iters, rel)
+    if st not in (HPCG_OK, HPCG_ERR_NOT_CONVERGED, HPCG_ERR_BREAKDOWN):
+        _check(st, h)
+    return st, list(iters), list(rel)
+
+
 def hpcg_last_fallback(h) -> int:
     return int(lib().hpcg_last_fallback(h))
 
@@ -435,6 +456,22 @@ class Solver:
         st, iters, rel = hpcg_solve(self.handle, self.part, b, x, tol, maxit)
         sys_st = hpcg_last_solve_status(self.handle, self.batch)
         return SolveResult(x.reshape(self.batch, self.n), iters, rel, st, sys_st)
+
+    def solve_block(self, B, nrhs: int, tol: float = 1e-6, maxit: int = 1000, X=None):
+        """Block PCG on a node-major block [batch*n, nrhs]; returns
+        (X fp64 [batch*n, nrhs], iterations, relres, status), the lists
+        system-major over (system, column)."""
+        B = self._block(B, nrhs)
+        X = torch.empty(B.numel(), dtype=torch.float64, device=self.device) if X is None else X
+        nbytes = hpcg_block_solve_workspace_bytes(self.handle, nrhs)
+        if nbytes == 0:
+            raise HPCGError(HPCG_ERR_SHAPE, "nrhs must be a multiple of 16 in [16, 1024]")
+        work = getattr(self, "_bswork", None)
+        if work is None or work.numel() < nbytes:
+            work = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+            self._bswork = work
+        st, iters, rel = hpcg_solve_block(self.handle, self.part, B, X, nrhs, tol, maxit, work)
+        return X.reshape(-1, nrhs), iters, rel, st
 
     def solve_refined(self, b, tol: float = 1e-10, maxit: int = 5000, inner_tol: float = 1e-5,
                       max_outer: int = 10, x=None):

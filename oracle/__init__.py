@@ -30,7 +30,7 @@ from .hmatrix import (  # noqa: F401
     weyl_lower_bound,
 )
 from .sparse import spmv, spmv_batch, spmv_block, true_relres, dense_A  # noqa: F401
-from .pcg import pcg, pcg_batch, pcg_refined, PCGResult  # noqa: F401
+from .pcg import pcg, pcg_batch, pcg_block, pcg_refined, PCGResult  # noqa: F401
 from .bridge import (  # noqa: F401
     apply_M_bridge,
     dense_M_bridge_entry,

@@ -124,6 +124,14 @@ def pcg_refined(row_ptr, col, val, b, precond, tol: float, maxit: int, inner_tol
         x = x + rn * inner.x
 
 
+def pcg_block(row_ptr, col, val, Bm, precond, tol: float, maxit: int) -> list:
+    """PCG on every column of a node-major block Bm [n, nrhs]: one independent
+    solve per column (own step sizes, test and count), the block form of the
+    loop above.  Returns one PCGResult per column."""
+    Bm = np.asarray(Bm, dtype=np.float64)
+    return [pcg(row_ptr, col, val, Bm[:, j], precond, tol, maxit) for j in range(Bm.shape[1])]
+
+
 def pcg_batch(batch, tol: float | None = None, maxit: int | None = None,
               systems=None) -> list:
     """Independent PCG per system of a workloads.Batch (or the listed systems)."""

@@ -1,0 +1,140 @@
+"""GPU parity of the block PCG (hpcg_solve_block) through the C ABI.
+
+Reference: the oracle's PCG on each column (oracle.pcg_block), fp64, with the
+same fp32 A, factors and right-hand sides.  The block solve's vectors are fp32
+(the block apply's arithmetic) with fp64 x and scalars, so the bar is that of
+the fp32-vector solve on the grid systems: iteration count within 2 of the
+oracle per (system, column), reported recursive residual <= tol, true residual
+<= 1.05 tol from the returned fp64 x."""
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from workloads import make_config  # noqa: E402
+
+from matrix_preconditioned_pcg_amd import hpcg  # noqa: E402
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _solver(b):
+    s = hpcg.Solver(b.n, b.row_ptr, b.col, b.val, batch=b.batch, levels=b.levels)
+    s.set_factors(b.U, b.W, b.g)
+    return s
+
+
+def _check(b, X, iters, rel, Bm, cols, systems=(0,)):
+    nrhs = Bm.shape[-1]
+    for s in systems:
+        sy = b.system(s)
+        Xs = X[s * b.n:(s + 1) * b.n]
+        for j in cols:
+            ref = oracle.pcg(sy.row_ptr, sy.col, sy.val, Bm[s, :, j], (sy.U, sy.W, sy.g), b.tol, b.maxit)
+            i = s * nrhs + j
+            assert ref.status == "converged"
+            assert abs(iters[i] - ref.iterations) <= 2, (s, j, iters[i], ref.iterations)
+            assert rel[i] <= b.tol, (s, j, rel[i])
+            tr = oracle.true_relres(sy.row_ptr, sy.col, sy.val, Bm[s, :, j], Xs[:, j])
+            assert tr <= 1.05 * b.tol, (s, j, tr)
+
+
+@pytest.mark.parametrize("name,nrhs,cols", [("N1k", 16, range(16)), ("N1k", 48, (0, 17, 47)),
+                                            ("N8k", 32, (0, 11, 31)), ("N16k", 16, (0, 15))])
+def test_block_solve_parity(name, nrhs, cols):
+    b = make_config(name)
+    _log(f"block solve {name} nrhs={nrhs}")
+    s = _solver(b)
+    Bm = np.random.default_rng(nrhs).standard_normal((1, b.n, nrhs)).astype(np.float32)
+    X, iters, rel, st = s.solve_block(Bm.reshape(-1), nrhs, tol=b.tol, maxit=b.maxit)
+    assert st == hpcg.HPCG_OK, hpcg.hpcg_last_error(s.handle)
+    _check(b, X.cpu().numpy(), iters, rel, Bm.astype(np.float64), cols)
+    s.close()
+
+
+def test_block_solve_batch():
+    b = make_config("batch64x2k", batch=3)
+    _log("block solve batch of 3")
+    s = _solver(b)
+    Bm = np.random.default_rng(7).standard_normal((3, b.n, 16)).astype(np.float32)
+    X, iters, rel, st = s.solve_block(Bm.reshape(-1), 16, tol=b.tol, maxit=b.maxit)
+    assert st == hpcg.HPCG_OK, hpcg.hpcg_last_error(s.handle)
+    _check(b, X.cpu().numpy(), iters, rel, Bm.astype(np.float64), (0, 9, 15), systems=(0, 1, 2))
+    s.close()
+
+
+def test_block_solve_columns_agree_with_single_solves():
+    # the workload's right-hand side in every column: every column ends with the
+    # same count and x, which match the fp32-vector single solve within the bar
+    b = make_config("N8k")
+    _log("block solve vs single solve N8k")
+    s = _solver(b)
+    Bm = np.repeat(b.b.reshape(b.n, 1), 16, axis=1).astype(np.float32)
+    X, iters, rel, st = s.solve_block(Bm.reshape(-1), 16, tol=b.tol, maxit=b.maxit)
+    assert st == hpcg.HPCG_OK
+    X = X.cpu().numpy()
+    assert len(set(iters)) == 1
+    for j in range(1, 16):
+        np.testing.assert_allclose(X[:, j], X[:, 0], rtol=0, atol=1e-12 * np.abs(X[:, 0]).max())
+    s.set_option(hpcg.HPCG_OPT_PRECISION, hpcg.HPCG_PREC_VEC32)
+    res = s.solve(b.b.reshape(-1), tol=b.tol, maxit=b.maxit)
+    assert abs(res.iterations[0] - iters[0]) <= 2
+    x1 = res.x[0].cpu().numpy()
+    assert np.linalg.norm(X[:, 0] - x1) <= 1e-4 * np.linalg.norm(x1)
+    s.close()
+
+
+def test_block_solve_edge_cases_and_reuse():
+    b = make_config("N1k")
+    _log("block solve edge cases")
+    s = _solver(b)
+    # the work buffer starts as NaN bit patterns: nothing may read a value the
+    # solve has not written (regression: the first direction once took Z + 0 P)
+    s._bswork = torch.full((hpcg.hpcg_block_solve_workspace_bytes(s.handle, 16),), 0xFF, dtype=torch.uint8,
+                           device="cuda")
+    rng = np.random.default_rng(3)
+    Bm = rng.standard_normal((b.n, 16)).astype(np.float32)
+    Bm[:, 5] = 0.0                                   # a zero column stops at once
+    X, iters, rel, st = s.solve_block(Bm.reshape(-1), 16, tol=b.tol, maxit=b.maxit)
+    assert st == hpcg.HPCG_OK
+    assert iters[5] == 0 and rel[5] == 0.0 and not X[:, 5].any()
+    # the same call again (recorded graph reused) gives the same bits
+    X2, iters2, rel2, st2 = s.solve_block(Bm.reshape(-1), 16, tol=b.tol, maxit=b.maxit)
+    assert st2 == hpcg.HPCG_OK and iters2 == iters and torch.equal(X, X2)
+    # a budget too small: every non-zero column stops at maxit, not converged
+    X3, iters3, rel3, st3 = s.solve_block(Bm.reshape(-1), 16, tol=b.tol, maxit=10)
+    assert st3 == hpcg.HPCG_ERR_NOT_CONVERGED
+    assert all(it == 10 for j, it in enumerate(iters3) if j != 5) and iters3[5] == 0
+    ref = oracle.pcg(b.system(0).row_ptr, b.system(0).col, b.system(0).val, Bm[:, 0].astype(np.float64),
+                     (b.U[0], b.W[0], b.g[0]), b.tol, 10)
+    assert rel3[0] == pytest.approx(ref.relres, rel=1e-4)
+    # and back to the full budget
+    X4, iters4, _r, st4 = s.solve_block(Bm.reshape(-1), 16, tol=b.tol, maxit=b.maxit)
+    assert st4 == hpcg.HPCG_OK and iters4 == iters and torch.equal(X, X4)
+    s.close()
+
+
+def test_block_solve_argument_errors():
+    b = make_config("N1k")
+    s = _solver(b)
+    assert hpcg.hpcg_block_solve_workspace_bytes(s.handle, 8) == 0
+    assert hpcg.hpcg_block_solve_workspace_bytes(s.handle, 16) > 4 * b.n * 16 * 4
+    with pytest.raises(hpcg.HPCGError):
+        s.solve_block(np.zeros(b.n * 24, np.float32), 24)
+    Bt = torch.zeros(b.n * 16, device="cuda")
+    Xt = torch.zeros(b.n * 16, dtype=torch.float64, device="cuda")
+    small = torch.empty(64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(hpcg.HPCGError):
+        hpcg.hpcg_solve_block(s.handle, s.part, Bt, Xt, 16, 1e-6, 100, small)
+    with pytest.raises(hpcg.HPCGError):
+        s.solve_block(np.ones(b.n * 16, np.float32), 16, tol=0.0)
+    s.set_option(hpcg.HPCG_OPT_FORM, hpcg.HPCG_FORM_SQUARED)
+    with pytest.raises(hpcg.HPCGError):
+        s.solve_block(np.ones(b.n * 16, np.float32), 16)
+    s.close()

@@ -185,3 +185,27 @@ def test_refinement_reaches_tight_tolerance():
     A = oracle.dense_A(sy.row_ptr, sy.col, sy.val)
     xs = np.linalg.solve(A, sy.b.astype(np.float64))
     assert np.linalg.norm(x - xs) <= 1e-6 * np.linalg.norm(xs)
+
+
+def test_block_pcg_columns_are_independent_solves():
+    # block PCG = one solve per column: equal columns give equal results, a zero
+    # column stops at once, a permutation of the columns permutes the results,
+    # and a scaled column gives the scaled solution with the same count
+    from workloads.generate import random_system
+    sy = random_system(256, seed=31, levels=1).system(0)
+    rng = np.random.default_rng(5)
+    b0, b1 = rng.standard_normal(256), rng.standard_normal(256)
+    Bm = np.stack([b0, np.zeros(256), b1, b0, 4.0 * b1], axis=1)
+    res = oracle.pcg_block(sy.row_ptr, sy.col, sy.val, Bm, (sy.U, sy.W, sy.g), 1e-8, 300)
+    assert [r.status for r in res] == ["converged"] * 5
+    assert res[1].iterations == 0 and not res[1].x.any()
+    assert res[0].iterations == res[3].iterations and np.array_equal(res[0].x, res[3].x)
+    assert res[4].iterations == res[2].iterations
+    np.testing.assert_allclose(res[4].x, 4.0 * res[2].x, rtol=1e-12, atol=1e-14)
+    perm = oracle.pcg_block(sy.row_ptr, sy.col, sy.val, Bm[:, ::-1], (sy.U, sy.W, sy.g), 1e-8, 300)
+    for a, b in zip(res, perm[::-1]):
+        assert a.iterations == b.iterations and np.array_equal(a.x, b.x)
+    # each column solves its own system
+    A = oracle.dense_A(sy.row_ptr, sy.col, sy.val)
+    for j in (0, 2):
+        np.testing.assert_allclose(A @ res[j].x, Bm[:, j], atol=1e-7 * np.linalg.norm(Bm[:, j]))
