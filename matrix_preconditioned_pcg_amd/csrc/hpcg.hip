@@ -806,7 +806,7 @@ BlockSolveLayout block_solve_layout(const hpcg_ctx* h, int32_t nrhs) {
   const size_t half = h->G.levels > 0 ? block_half_bytes(h, nrhs) : 0;
   L.scratchQ = take(half);
   L.scratchH = take(half);
-  L.part = take((size_t)h->G.B * h->G.K * nrhs * 8);
+  L.part = take((size_t)h->G.B * (h->G.n / BS_ROWS) * nrhs * 8);
   L.cs = take((size_t)h->G.B * nrhs * sizeof(ColState));
   L.ctr = take(256);
   L.total = off;
@@ -823,22 +823,23 @@ hpcg_status block_iteration(hpcg_ctx* h, int32_t nrhs, char* wk, const BlockSolv
   float* Q = reinterpret_cast<float*>(wk + L.Q);
   double* part = reinterpret_cast<double*>(wk + L.part);
   ColState* cs = reinterpret_cast<ColState*>(wk + L.cs);
-  const dim3 rows_grid((unsigned)(G.B * G.K), (unsigned)((nrhs + BS_COLS - 1) / BS_COLS));
+  const int rblocks = G.n / BS_ROWS;   // row blocks per system
+  const dim3 rows_grid((unsigned)(G.B * rblocks), (unsigned)((nrhs + BS_COLS - 1) / BS_COLS));
   const int ncol = G.B * nrhs;
-  const dim3 sc_grid((unsigned)((ncol + 255) / 256));
+  const dim3 sc_grid((unsigned)((ncol + BS_SC_COLS - 1) / BS_SC_COLS));
   const size_t threads = (size_t)G.B * G.n * (nrhs / 4);
   hipLaunchKernelGGL(k_spmv_block, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, h->B.row_ptr,
                      h->B.col, h->B.val, P, Q, G.B * G.n, nrhs);
   hipLaunchKernelGGL(k_bs_dot, rows_grid, dim3(BS_NT), 0, stream, P, Q, part, nrhs);
-  hipLaunchKernelGGL(k_bs_scalars<BS_PQ>, sc_grid, dim3(256), 0, stream, cs, part, G.B, nrhs, G.K, tol, maxit);
-  hipLaunchKernelGGL(k_bs_update, rows_grid, dim3(BS_NT), 0, stream, cs, P, Q, R, d_X, part, nrhs, G.K);
-  hipLaunchKernelGGL(k_bs_scalars<BS_RR>, sc_grid, dim3(256), 0, stream, cs, part, G.B, nrhs, G.K, tol, maxit);
+  hipLaunchKernelGGL(k_bs_scalars<BS_PQ>, sc_grid, dim3(64 * BS_SC_COLS), 0, stream, cs, part, G.B, nrhs, rblocks, tol, maxit);
+  hipLaunchKernelGGL(k_bs_update, rows_grid, dim3(BS_NT), 0, stream, cs, P, Q, R, d_X, part, nrhs, rblocks);
+  hipLaunchKernelGGL(k_bs_scalars<BS_RR>, sc_grid, dim3(64 * BS_SC_COLS), 0, stream, cs, part, G.B, nrhs, rblocks, tol, maxit);
   hpcg_status s = launch_block_apply(h, nrhs, R, Z, reinterpret_cast<float*>(wk + L.scratchQ),
                                      reinterpret_cast<float*>(wk + L.scratchH), stream);
   if (s != HPCG_OK) return s;
   hipLaunchKernelGGL(k_bs_dot, rows_grid, dim3(BS_NT), 0, stream, R, Z, part, nrhs);
-  hipLaunchKernelGGL(k_bs_scalars<BS_RZ>, sc_grid, dim3(256), 0, stream, cs, part, G.B, nrhs, G.K, tol, maxit);
-  hipLaunchKernelGGL(k_bs_direction, rows_grid, dim3(BS_NT), 0, stream, cs, Z, P, nrhs, G.K);
+  hipLaunchKernelGGL(k_bs_scalars<BS_RZ>, sc_grid, dim3(64 * BS_SC_COLS), 0, stream, cs, part, G.B, nrhs, rblocks, tol, maxit);
+  hipLaunchKernelGGL(k_bs_direction, rows_grid, dim3(BS_NT), 0, stream, cs, Z, P, nrhs, rblocks);
   return HPCG_OK;
 }
 
@@ -872,9 +873,10 @@ hpcg_status hpcg_solve_block(hpcg_handle h, const float* d_B, double* d_X, int32
   int* ctr = reinterpret_cast<int*>(wk + L.ctr);
   int* hflag = h->h_flag + 16;
   int* dflag = h->d_flag + 16;
-  const dim3 rows_grid((unsigned)(G.B * G.K), (unsigned)((nrhs + BS_COLS - 1) / BS_COLS));
+  const int rblocks = G.n / BS_ROWS;   // row blocks per system
+  const dim3 rows_grid((unsigned)(G.B * rblocks), (unsigned)((nrhs + BS_COLS - 1) / BS_COLS));
   const int ncol = G.B * nrhs;
-  const dim3 sc_grid((unsigned)((ncol + 255) / 256));
+  const dim3 sc_grid((unsigned)((ncol + BS_SC_COLS - 1) / BS_SC_COLS));
 
   // the recorded iterations depend on the buffers, nrhs, tol, maxit and the unroll
   if (!h->bs_gexec || h->bs_key[0] != d_X || h->bs_key[1] != wk || h->bs_nrhs != nrhs || h->bs_tol != tol ||
@@ -907,13 +909,13 @@ hpcg_status hpcg_solve_block(hpcg_handle h, const float* d_B, double* d_X, int32
   __atomic_store_n(hflag, 0, __ATOMIC_RELEASE);
   hipLaunchKernelGGL(k_bs_reset, dim3(1), dim3(64), 0, h->stream, ctr, dflag);
   hipLaunchKernelGGL(k_bs_init, rows_grid, dim3(BS_NT), 0, h->stream, d_B, R, d_X, part, nrhs);
-  hipLaunchKernelGGL(k_bs_scalars<BS_INIT>, sc_grid, dim3(256), 0, h->stream, cs, part, G.B, nrhs, G.K, tol, maxit);
+  hipLaunchKernelGGL(k_bs_scalars<BS_INIT>, sc_grid, dim3(64 * BS_SC_COLS), 0, h->stream, cs, part, G.B, nrhs, rblocks, tol, maxit);
   hpcg_status s = launch_block_apply(h, nrhs, R, Z, reinterpret_cast<float*>(wk + L.scratchQ),
                                      reinterpret_cast<float*>(wk + L.scratchH), h->stream);
   if (s != HPCG_OK) return s;
   hipLaunchKernelGGL(k_bs_dot, rows_grid, dim3(BS_NT), 0, h->stream, R, Z, part, nrhs);
-  hipLaunchKernelGGL(k_bs_scalars<BS_RZ0>, sc_grid, dim3(256), 0, h->stream, cs, part, G.B, nrhs, G.K, tol, maxit);
-  hipLaunchKernelGGL(k_bs_direction, rows_grid, dim3(BS_NT), 0, h->stream, cs, Z, P, nrhs, G.K);
+  hipLaunchKernelGGL(k_bs_scalars<BS_RZ0>, sc_grid, dim3(64 * BS_SC_COLS), 0, h->stream, cs, part, G.B, nrhs, rblocks, tol, maxit);
+  hipLaunchKernelGGL(k_bs_direction, rows_grid, dim3(BS_NT), 0, h->stream, cs, Z, P, nrhs, rblocks);
   s = check_launch(h, "block solve setup launch");
   if (s != HPCG_OK) return s;
 

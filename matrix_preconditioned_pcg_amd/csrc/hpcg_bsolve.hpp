@@ -16,17 +16,17 @@
 // A finished column gets alpha = beta = 0 from then on, so its X and R stay
 // as they were while the others continue.
 //
-// Dot products: a workgroup owns 128 rows (one leaf) and 64 columns; a thread
-// owns one column and sums rows rg, rg + 4, ... in fp64, the four row groups
-// are added in a fixed order, and the per-leaf partials of a system are added
-// in leaf order by one thread per (system, column): every sum has one fixed
-// order, so a solve is bitwise reproducible.
+// Dot products: a workgroup owns 32 rows and 64 columns; a thread owns one
+// column and sums rows rg, rg + 4, ... in fp64, the four row groups are added
+// in a fixed order, and the per-block partials of a system are added by one
+// wave per (system, column) in a fixed order (lane-strided, then a fixed
+// butterfly): every sum has one order, so a solve is bitwise reproducible.
 #pragma once
 #include "hpcg_device.hpp"
 
 namespace hpcg {
 
-constexpr int BS_ROWS = LEAF;   // rows per workgroup
+constexpr int BS_ROWS = 32;     // rows per workgroup (n is a multiple of 128)
 constexpr int BS_COLS = 64;     // columns per workgroup
 constexpr int BS_NT = 256;      // threads per workgroup
 
@@ -62,6 +62,7 @@ __global__ __launch_bounds__(BS_NT) void k_bs_dot(const float* __restrict__ X, c
   const size_t rb = blockIdx.x;
   double acc = 0.0;
   if (c < nrhs) {
+#pragma unroll
     for (int r = rg; r < BS_ROWS; r += BS_NT / BS_COLS) {
       const size_t i = (rb * BS_ROWS + r) * nrhs + c;
       acc = fma((double)X[i], (double)Y[i], acc);
@@ -80,6 +81,7 @@ __global__ __launch_bounds__(BS_NT) void k_bs_init(const float* __restrict__ Bm,
   const size_t rb = blockIdx.x;
   double acc = 0.0;
   if (c < nrhs) {
+#pragma unroll
     for (int r = rg; r < BS_ROWS; r += BS_NT / BS_COLS) {
       const size_t i = (rb * BS_ROWS + r) * nrhs + c;
       const float b = Bm[i];
@@ -98,15 +100,16 @@ __global__ __launch_bounds__(BS_NT) void k_bs_init(const float* __restrict__ Bm,
 __global__ __launch_bounds__(BS_NT) void k_bs_update(const ColState* __restrict__ cs, const float* __restrict__ P,
                                                      const float* __restrict__ Q, float* __restrict__ R,
                                                      double* __restrict__ X, double* __restrict__ part, int nrhs,
-                                                     int leaves_per_system) {
+                                                     int blocks_per_system) {
   __shared__ double red[BS_NT];
   const int tid = threadIdx.x, rg = tid / BS_COLS;
   const int c = blockIdx.y * BS_COLS + (tid & (BS_COLS - 1));
   const size_t rb = blockIdx.x;
-  const int s = (int)(rb / leaves_per_system);
+  const int s = (int)(rb / blocks_per_system);
   double acc = 0.0;
   if (c < nrhs) {
     const double alpha = cs[(size_t)s * nrhs + c].alpha;
+#pragma unroll
     for (int r = rg; r < BS_ROWS; r += BS_NT / BS_COLS) {
       const size_t i = (rb * BS_ROWS + r) * nrhs + c;
       float rn = R[i];
@@ -126,29 +129,37 @@ __global__ __launch_bounds__(BS_NT) void k_bs_update(const ColState* __restrict_
 // step, and every step of a finished column) takes P = Z without reading P,
 // which holds no value before the first step.
 __global__ __launch_bounds__(BS_NT) void k_bs_direction(const ColState* __restrict__ cs, const float* __restrict__ Z,
-                                                        float* __restrict__ P, int nrhs, int leaves_per_system) {
+                                                        float* __restrict__ P, int nrhs, int blocks_per_system) {
   const int tid = threadIdx.x, rg = tid / BS_COLS;
   const int c = blockIdx.y * BS_COLS + (tid & (BS_COLS - 1));
   const size_t rb = blockIdx.x;
-  const int s = (int)(rb / leaves_per_system);
+  const int s = (int)(rb / blocks_per_system);
   if (c >= nrhs) return;
   const double beta = cs[(size_t)s * nrhs + c].beta;
+#pragma unroll
   for (int r = rg; r < BS_ROWS; r += BS_NT / BS_COLS) {
     const size_t i = (rb * BS_ROWS + r) * nrhs + c;
     P[i] = beta == 0.0 ? Z[i] : (float)((double)Z[i] + beta * (double)P[i]);
   }
 }
 
-// One thread per (system, column): add the system's per-leaf partials in leaf
-// order and take the step the mode names.
+// One wave per (system, column): lane l adds the system's per-block partials
+// l, l + 64, ... and the lanes are combined by the fixed butterfly of
+// wave_sum (one order, every call); lane 0 takes the step the mode names.
+constexpr int BS_SC_COLS = 4;   // columns (waves) per workgroup
 template <int MODE>
-__global__ void k_bs_scalars(ColState* __restrict__ cs, const double* __restrict__ part, int systems, int nrhs,
-                             int leaves_per_system, double tol, int maxit) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= systems * nrhs) return;
+__global__ __launch_bounds__(64 * BS_SC_COLS) void k_bs_scalars(ColState* __restrict__ cs,
+                                                                const double* __restrict__ part, int systems,
+                                                                int nrhs, int blocks_per_system, double tol,
+                                                                int maxit) {
+  const int idx = blockIdx.x * BS_SC_COLS + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (idx >= systems * nrhs) return;     // whole waves leave together
   const int s = idx / nrhs, c = idx - s * nrhs;
-  double sum = 0.0;
-  for (int k = 0; k < leaves_per_system; ++k) sum += part[((size_t)s * leaves_per_system + k) * nrhs + c];
+  double v = 0.0;
+  for (int k = lane; k < blocks_per_system; k += 64) v += part[((size_t)s * blocks_per_system + k) * nrhs + c];
+  const double sum = wave_sum(v);
+  if (lane != 0) return;
   ColState st = cs[idx];
   if constexpr (MODE == BS_INIT) {
     st.bnorm = sqrt(sum);
