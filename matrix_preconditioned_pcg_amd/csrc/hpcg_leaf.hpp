@@ -24,6 +24,8 @@ struct alignas(16) RSmem {
   T ownQ[MAX_LEVELS * RANK];         // this leaf's W_l[k]^T q
   T yleaf[LEAF];
   T yoff[LEAF];
+  T yr[LEAF];                        // U_k U_k^T r (resident solve)
+  T yq[LEAF];                        // U_k U_k^T q (resident solve)
   T red[NWR][LEAF];                  // cross-wave reductions of t
   T redW[NWR][2 * MAX_LEVELS * RANK];  // cross-wave reductions (restriction, strip sums)
   double dred[NWR];
@@ -175,14 +177,14 @@ __device__ __forceinline__ void prolong_strips(RSmem<T>& sm, const T* stR, const
   __syncthreads();
 }
 
-// Diagonal stage U_k sm.t into sm.yleaf: rows rg + 16m (m < 8), dots over 32
+// Diagonal stage y = U_k t (t, y in LDS): rows rg + 16m (m < 8), dots over 32
 // column slots; the eight rows of a lane are folded with a transpose-reduce
 // (7 + 2 shuffles).  No barrier.
 template <typename T, int LEV>
-__device__ __forceinline__ void prolong_diag(const Resident<T, LEV>& F, RSmem<T>& sm) {
+__device__ __forceinline__ void diag_times(const Resident<T, LEV>& F, const T* t, T* y) {
   const int tid = threadIdx.x;
   const int cs = tid & 31, rg = tid >> 5;
-  const Vec4<T> t4 = lds4(&sm.t[4 * cs]);
+  const Vec4<T> t4 = lds4(&t[4 * cs]);
   T v[8];
 #pragma unroll
   for (int m = 0; m < 8; ++m) v[m] = dot4(F.u[m], t4);
@@ -202,7 +204,13 @@ __device__ __forceinline__ void prolong_diag(const Resident<T, LEV>& F, RSmem<T>
   T kk = b2 ? bb[1] : bb[0];              // bit 2 (lane j pairs with 7 - j)
   kk += lane_m4(b2 ? bb[0] : bb[1]);
   kk = group4_sum(kk);
-  if ((cs & 3) == 0) sm.yleaf[rg + 16 * ((b4 ? 4 : 0) + (b3 ? 2 : 0) + (b2 ? 1 : 0))] = kk;
+  if ((cs & 3) == 0) y[rg + 16 * ((b4 ? 4 : 0) + (b3 ? 2 : 0) + (b2 ? 1 : 0))] = kk;
+}
+
+// Diagonal stage U_k sm.t into sm.yleaf.  No barrier.
+template <typename T, int LEV>
+__device__ __forceinline__ void prolong_diag(const Resident<T, LEV>& F, RSmem<T>& sm) {
+  diag_times<T, LEV>(F, sm.t, sm.yleaf);
 }
 
 // Off-diagonal prolongation sum_l W_l[k] sm.P[l] into sm.yoff (eq. (5)).

@@ -143,13 +143,13 @@ constexpr int kRefresh = sizeof(T) == 8 ? 8 : 1;
 template <typename T, int LEV>
 __device__ __forceinline__ void r_restrict(const Geom& G, int s, int k, const Resident<T, LEV>& F,
                                            const T* v, T* tout, T* pout, T* own, RSmem<T>& sm,
-                                           double loc = 0.0, double* part_dst = nullptr) {
+                                           double loc = 0.0, double* part_dst = nullptr, bool with_u = true) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (part_dst) {
     loc = wave_sum(loc);
     if (lane == 0) sm.dred[wave] = loc;
   }
-  restrict_u_partials<T, LEV>(F, v, sm);
+  if (with_u) restrict_u_partials<T, LEV>(F, v, sm);
   restrict_w_partials<T, LEV>(F, v, sm);
   __syncthreads();
   if (part_dst && tid == 0) {
@@ -158,7 +158,7 @@ __device__ __forceinline__ void r_restrict(const Geom& G, int s, int k, const Re
     for (int w = 1; w < NWR; ++w) p += sm.dred[w];
     st_c(part_dst, p);
   }
-  if (tid < LEAF) {
+  if (with_u && tid < LEAF) {
     T a = sm.red[0][tid];
 #pragma unroll
     for (int w = 1; w < NWR; ++w) a += sm.red[w][tid];
@@ -190,6 +190,38 @@ __device__ __forceinline__ void r_stage_partners(const Geom& G, const T* src, in
     dma_to_lds_n<NWR, CPOL_AGENT>(stage + (size_t)((1 << l) - 1) * RANK, (1 << l) * CPV,
                       [&](int c) { return reinterpret_cast<const char*>(from) + 16 * c; });
   }
+}
+
+// y = U_k (U_k^T v) with tmp for U_k^T v (all LDS).  y is complete after the
+// caller's next barrier.
+template <typename T, int LEV>
+__device__ __forceinline__ void leaf_apply(const Resident<T, LEV>& F, const T* v, T* tmp, T* y, RSmem<T>& sm) {
+  const int tid = threadIdx.x;
+  restrict_u_partials<T, LEV>(F, v, sm);
+  __syncthreads();
+  if (tid < LEAF) {
+    T a = sm.red[0][tid];
+#pragma unroll
+    for (int w = 1; w < NWR; ++w) a += sm.red[w][tid];
+    tmp[tid] = a;
+  }
+  __syncthreads();
+  diag_times<T, LEV>(F, tmp, y);
+}
+
+// z = M r_new on the leaf's rows into sm.z, with the leaf stage already in
+// hand: U_k U_k^T r_new = sm.yr - alpha sm.yq.  Needs sm.r (= r_new) and the
+// staged partner restrictions of r (stR) and q (stQ).
+template <typename T, int LEV>
+__device__ __forceinline__ void r_prolong_split(const Resident<T, LEV>& F, RSmem<T>& sm, const T* stR, const T* stQ,
+                                                double alpha, float gate) {
+  const int tid = threadIdx.x;
+  if constexpr (LEV > 0) prolong_strips<T, LEV>(sm, stR, stQ, alpha);
+  prolong_offdiag<T, LEV>(F, sm);
+  __syncthreads();
+  if (tid < LEAF)
+    sm.z[tid] = (T)((double)sm.yr[tid] - alpha * (double)sm.yq[tid]) + sm.yoff[tid] + (T)gate * sm.r[tid];
+  __syncthreads();
 }
 
 // z = M r_new on the leaf's rows into sm.z.  Needs sm.t (= U_k^T r_new), sm.r
@@ -254,6 +286,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
   }
   __syncthreads();
   r_restrict<T, LEV>(G, s, k, F, sm.r, sm.tr, pR[0], sm.ownR, sm);
+  diag_times<T, LEV>(F, sm.tr, sm.yr);       // U_k U_k^T r0 (read in the first phase BC)
   double part = wg_sum_r(loc, sm);
   if (tid == 0) {
     st_c(B.rr_part + item, part);
@@ -367,11 +400,15 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
           loc = (double)pn * (double)acc;
         }
         __syncthreads();
-        // the restriction of q also sums and stores the partial p.q
-        r_restrict<T, LEV>(G, s, k, F, sm.q, sm.tq, pQ, sm.ownQ, sm, loc, B.pq_part + item);
+        // the slab restriction of q (what the partners read) also sums and
+        // stores the partial p.q
+        r_restrict<T, LEV>(G, s, k, F, sm.q, sm.tq, pQ, sm.ownQ, sm, loc, B.pq_part + item, false);
       }
     }
-    if (cgrid_barrier(B, target, epoch)) return;
+    cgrid_arrive(B, target, epoch);
+    // U_k U_k^T q is this workgroup's alone: it overlaps the wait
+    if (!done) leaf_apply<T, LEV>(F, sm.q, sm.tq, sm.yq, sm);
+    if (cgrid_wait(B, target, epoch)) return;
     // ---------------- phase BC (it) ----------------
     {
       if (lead && pend_status != ST_RUNNING) {
@@ -397,10 +434,9 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
             sm.r[tid] = rn;
             x += alpha * (double)sm.p[tid];
             loc_rr = (double)rn * (double)rn;
-            sm.t[tid] = (T)((double)sm.tr[tid] - alpha * (double)sm.tq[tid]);
           }
-          // (r_prolong synchronizes before it reads sm.r and sm.t)
-          r_prolong<T, LEV>(F, sm, stR, stQ, alpha, gate);
+          // (r_prolong_split synchronizes before it reads sm.r)
+          r_prolong_split<T, LEV>(F, sm, stR, stQ, alpha, gate);
           double loc_rz = 0.0;
           if (tid < LEAF) {
             st_c(zg + leaf0 + tid, sm.z[tid]);
@@ -427,8 +463,9 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
       rbuf ^= 1;
       if (it % kRefresh<T> == 0) {
         r_restrict<T, LEV>(G, s, k, F, sm.r, sm.tr, pR[rbuf], sm.ownR, sm);
+        diag_times<T, LEV>(F, sm.tr, sm.yr);
       } else {
-        if (tid < LEAF) sm.tr[tid] = sm.t[tid];
+        if (tid < LEAF) sm.yr[tid] = (T)((double)sm.yr[tid] - next_alpha * (double)sm.yq[tid]);
         if (tid < LEV * RANK) {
           const T v = (T)((double)sm.ownR[tid] - next_alpha * (double)sm.ownQ[tid]);
           sm.ownR[tid] = v;
