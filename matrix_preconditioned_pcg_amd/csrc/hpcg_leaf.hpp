@@ -136,10 +136,13 @@ __device__ __forceinline__ void load_factors(const Geom& G, const Bufs& B, int s
 
 // Strip aggregation (eq. (3)) from the staged partner restrictions of r
 // (stR, level l at stage row 2^l - 1) and of q (stQ): sm.P[l] = sum(stR) -
-// alpha sum(stQ), or sum(stR) with stQ == nullptr.  16 groups of threads per
-// column, then across waves; two barriers.
+// alpha sum(stQ), or sum(stR) with stQ == nullptr.  With r_from_prev the
+// partner sums of r are not staged: sm.P still holds them (the previous
+// P, by linearity) and becomes sm.P - alpha sum(stQ).  16 groups of threads
+// per column, then across waves; two barriers.
 template <typename T, int LEV>
-__device__ __forceinline__ void prolong_strips(RSmem<T>& sm, const T* stR, const T* stQ, double alpha) {
+__device__ __forceinline__ void prolong_strips(RSmem<T>& sm, const T* stR, const T* stQ, double alpha,
+                                               bool r_from_prev = false) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = tid & 31, g = tid >> 5;
 #pragma unroll
@@ -150,22 +153,27 @@ __device__ __forceinline__ void prolong_strips(RSmem<T>& sm, const T* stR, const
     for (int m = 0; m < ((1 << l) + 15) / 16; ++m) {
       const int i = g + 16 * m;
       if (i < (1 << l)) {
-        a += vr[i * RANK];
+        if (!r_from_prev) a += vr[i * RANK];
         if (stQ) b += stQ[(size_t)((1 << l) - 1) * RANK + c + i * RANK];
       }
     }
-    a += lane_x32(a);
+    if (!r_from_prev) a += lane_x32(a);
     if (stQ) b += lane_x32(b);
     if (lane < 32) {
-      sm.redW[wave][l * RANK + c] = a;
+      if (!r_from_prev) sm.redW[wave][l * RANK + c] = a;
       if (stQ) sm.redW[wave][(MAX_LEVELS + l) * RANK + c] = b;
     }
   }
   __syncthreads();
   if (tid < LEV * RANK) {
-    T a = sm.redW[0][tid];
+    T a;
+    if (r_from_prev) {
+      a = sm.P[tid];
+    } else {
+      a = sm.redW[0][tid];
 #pragma unroll
-    for (int w = 1; w < NWR; ++w) a += sm.redW[w][tid];
+      for (int w = 1; w < NWR; ++w) a += sm.redW[w][tid];
+    }
     if (stQ) {
       T b = sm.redW[0][MAX_LEVELS * RANK + tid];
 #pragma unroll

@@ -211,12 +211,13 @@ __device__ __forceinline__ void leaf_apply(const Resident<T, LEV>& F, const T* v
 
 // z = M r_new on the leaf's rows into sm.z, with the leaf stage already in
 // hand: U_k U_k^T r_new = sm.yr - alpha sm.yq.  Needs sm.r (= r_new) and the
-// staged partner restrictions of r (stR) and q (stQ).
+// staged partner restrictions of q (stQ) and of r (stR; with r_from_prev
+// their sums are the previous sm.P instead).
 template <typename T, int LEV>
 __device__ __forceinline__ void r_prolong_split(const Resident<T, LEV>& F, RSmem<T>& sm, const T* stR, const T* stQ,
-                                                double alpha, float gate) {
+                                                double alpha, float gate, bool r_from_prev) {
   const int tid = threadIdx.x;
-  if constexpr (LEV > 0) prolong_strips<T, LEV>(sm, stR, stQ, alpha);
+  if constexpr (LEV > 0) prolong_strips<T, LEV>(sm, stR, stQ, alpha, r_from_prev);
   prolong_offdiag<T, LEV>(F, sm);
   __syncthreads();
   if (tid < LEAF)
@@ -416,9 +417,12 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
         set_state(st, pend_status, pend_iters);
         pend_status = ST_RUNNING;   // written once
       }
+      // The partner sums of W^T r are staged only after an exact refresh (and
+      // for the initial r); otherwise they are the previous P (linearity).
+      const bool r_from_prev = (it - 1) % kRefresh<T> != 0;
       if (!done) {
         if constexpr (LEV > 0) {
-          r_stage_partners<T, LEV>(G, pR[rbuf], s, k, stR);
+          if (!r_from_prev) r_stage_partners<T, LEV>(G, pR[rbuf], s, k, stR);
           r_stage_partners<T, LEV>(G, pQ, s, k, stQ);
         }
         const double pq = sum_partials_r(B.pq_part, s, G.K);
@@ -436,7 +440,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
             loc_rr = (double)rn * (double)rn;
           }
           // (r_prolong_split synchronizes before it reads sm.r)
-          r_prolong_split<T, LEV>(F, sm, stR, stQ, alpha, gate);
+          r_prolong_split<T, LEV>(F, sm, stR, stQ, alpha, gate, r_from_prev);
           double loc_rz = 0.0;
           if (tid < LEAF) {
             st_c(zg + leaf0 + tid, sm.z[tid]);
@@ -460,19 +464,14 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
       // exact every kRefresh iterations, else by the same linear update the
       // partners used above (its rounding drift is bounded by the refreshes)
       restrict_next = false;
-      rbuf ^= 1;
       if (it % kRefresh<T> == 0) {
+        // exact W^T r for the partners' next phase BC (into the other buffer:
+        // slow partners may still be staging the previous one) and U U^T r
+        rbuf ^= 1;
         r_restrict<T, LEV>(G, s, k, F, sm.r, sm.tr, pR[rbuf], sm.ownR, sm);
         diag_times<T, LEV>(F, sm.tr, sm.yr);
       } else {
         if (tid < LEAF) sm.yr[tid] = (T)((double)sm.yr[tid] - next_alpha * (double)sm.yq[tid]);
-        if (tid < LEV * RANK) {
-          const T v = (T)((double)sm.ownR[tid] - next_alpha * (double)sm.ownQ[tid]);
-          sm.ownR[tid] = v;
-          const int l = tid / RANK, c = tid - l * RANK;
-          st_c(pR[rbuf] + (((size_t)s * G.levels + l) * G.K + k) * RANK + c, v);
-        }
-        __syncthreads();
       }
     }
     if (cgrid_wait(B, target, epoch)) return;
