@@ -337,17 +337,14 @@ hpcg_status run_graph(hpcg_ctx* h) {
 }
 
 template <typename T>
-const void* resident_kernel(int levels) {
-  switch (levels) {
-    case 0: return reinterpret_cast<const void*>(&k_resident<T, 0>);
-    case 1: return reinterpret_cast<const void*>(&k_resident<T, 1>);
-    case 2: return reinterpret_cast<const void*>(&k_resident<T, 2>);
-    case 3: return reinterpret_cast<const void*>(&k_resident<T, 3>);
-    case 4: return reinterpret_cast<const void*>(&k_resident<T, 4>);
-    case 5: return reinterpret_cast<const void*>(&k_resident<T, 5>);
-    case 6: return reinterpret_cast<const void*>(&k_resident<T, 6>);
-    case 7: return reinterpret_cast<const void*>(&k_resident<T, 7>);
-    case 8: return reinterpret_cast<const void*>(&k_resident<T, 8>);
+const void* resident_kernel(int levels, bool sq) {
+  switch (levels * 2 + (sq ? 1 : 0)) {
+#define HPCG_RESIDENT(LV)                                                          \
+    case 2 * LV: return reinterpret_cast<const void*>(&k_resident<T, LV, false>); \
+    case 2 * LV + 1: return reinterpret_cast<const void*>(&k_resident<T, LV, true>);
+    HPCG_RESIDENT(0) HPCG_RESIDENT(1) HPCG_RESIDENT(2) HPCG_RESIDENT(3) HPCG_RESIDENT(4)
+    HPCG_RESIDENT(5) HPCG_RESIDENT(6) HPCG_RESIDENT(7) HPCG_RESIDENT(8)
+#undef HPCG_RESIDENT
     default: return nullptr;
   }
 }
@@ -361,8 +358,8 @@ hpcg_status run_resident(hpcg_ctx* h, bool& ran) {
   const Geom G = h->G;
   const Bufs B = h->B;
   const int items = G.B * G.K;
-  if (items > h->num_cu || B.form != FORM_DIRECT) return HPCG_OK;
-  const void* fn = resident_kernel<T>(G.levels);
+  if (items > h->num_cu || B.form == FORM_JACOBI) return HPCG_OK;
+  const void* fn = resident_kernel<T>(G.levels, B.form == FORM_SQUARED);
   if (!fn) return HPCG_OK;
   const size_t dyn = ((size_t)h->max_leaf_nnz * 8 + (LEAF + 1) * 4 + 15) / 16 * 16 +
                      2 * (size_t)std::max(G.K - 1, 1) * RANK * sizeof(T);
@@ -990,7 +987,7 @@ hpcg_status solve_core(hpcg_ctx* h, const float* d_b, double* d_x, double tol, i
     if (s != HPCG_OK) return s;
     if (!ran && h->engine_opt == HPCG_ENGINE_PERSISTENT)
       return fail(h, HPCG_ERR_SHAPE, h->B.form != FORM_DIRECT
-                                         ? "persistent engines run the direct form only"
+                                         ? "persistent engines run the direct (and, register-resident, the squared) form only"
                                          : "persistent engine: device does not support a co-resident grid for this partition");
     if (ran) h->last_engine = HPCG_ENGINE_PERSISTENT;
   }

@@ -241,7 +241,7 @@ __device__ __forceinline__ void r_prolong(const Resident<T, LEV>& F, RSmem<T>& s
   __syncthreads();
 }
 
-template <typename T, int LEV>
+template <typename T, int LEV, bool SQ>
 __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_nnz) {
   __shared__ RSmem<T> sm;
   extern __shared__ int4 rdyn4[];
@@ -257,11 +257,11 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
   const int leaf0 = s * G.n + k * LEAF;
   SysState* st = B.st + s;
   const bool lead = (tid == 0 && k == 0);
-  unsigned target = 0, epoch = 0;
   // restriction buffers: W^T r in two halves of pleaf (ping-pong), W^T q in tleaf
   const size_t half = (size_t)G.B * G.levels * G.K * RANK;
   T* pR[2] = {reinterpret_cast<T*>(B.pleaf), reinterpret_cast<T*>(B.pleaf) + half};
   T* pQ = reinterpret_cast<T*>(B.tleaf);
+  T* pW = pQ + half;                   // squared form: W^T w of w = H r
   int rbuf = 0;
 
   // ---- factors into registers, CSR rows into LDS ----
@@ -277,6 +277,40 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
   const float gate = (tid < LEAF) ? B.g[leaf0 + tid] : 0.f;
   double x = 0.0;                      // x of row tid (tid < LEAF)
   T* zg = reinterpret_cast<T*>(B.z);
+  unsigned target = 0, epoch = 0;
+
+  // Squared form M = H H: with w = H r in sm.z, z = H w into sm.z.  The
+  // slabs' restriction of w is new data, so it costs one more device-wide
+  // exchange; U_k U_k^T w overlaps its wait.  Every workgroup calls this (it
+  // holds a barrier); inactive ones only pass the barrier.  sm.P (the partner
+  // sums of W^T r, carried to the next iteration) is kept aside meanwhile.
+  auto squared = [&](bool active) -> bool {
+    if constexpr (!SQ) return true;
+    if (active) {
+      if (tid < LEAF) sm.t[tid] = sm.z[tid];
+      __syncthreads();
+      r_restrict<T, LEV>(G, s, k, F, sm.t, sm.tq, pW, sm.ownQ, sm, 0.0, nullptr, false);
+    }
+    cgrid_arrive(B, target, epoch);
+    if (active) leaf_apply<T, LEV>(F, sm.t, sm.tq, sm.yleaf, sm);
+    if (cgrid_wait(B, target, epoch)) return false;
+    if (active) {
+      if constexpr (LEV > 0) {
+        r_stage_partners<T, LEV>(G, pW, s, k, stR);
+        if (tid < LEV * RANK) sm.ownR[tid] = sm.P[tid];
+      }
+      lds_dma_wait();
+      if constexpr (LEV > 0) prolong_strips<T, LEV>(sm, stR, (const T*)nullptr, 0.0, false);
+      prolong_offdiag<T, LEV>(F, sm);
+      __syncthreads();
+      if (tid < LEAF) sm.z[tid] = sm.yleaf[tid] + sm.yoff[tid] + (T)gate * sm.t[tid];
+      if constexpr (LEV > 0) {
+        if (tid < LEV * RANK) sm.P[tid] = sm.ownR[tid];
+      }
+      __syncthreads();
+    }
+    return true;
+  };
 
   // ---- r = b, its restriction (t_r, W^T r), ||b||^2 ----
   double loc = 0.0;
@@ -316,6 +350,11 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
       if (tid < LEAF) sm.t[tid] = sm.tr[tid];
       __syncthreads();
       r_prolong<T, LEV>(F, sm, stR, (const T*)nullptr, 0.0, gate);
+    }
+    if constexpr (SQ) {
+      if (!squared(!done)) return;
+    }
+    if (!done) {
       loc = 0.0;
       if (tid < LEAF) {
         st_c(zg + leaf0 + tid, sm.z[tid]);
@@ -334,6 +373,21 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
   double pend_rel = 0.0;
   bool restrict_next = false;
   double next_alpha = 0.0;
+  // the end of phase BC: z for the neighbours' SpMV, the partials r.r and r.z
+  auto finish_bc = [&](double alpha, double loc_rr) {
+    double loc_rz = 0.0;
+    if (tid < LEAF) {
+      st_c(zg + leaf0 + tid, sm.z[tid]);
+      loc_rz = (double)sm.r[tid] * (double)sm.z[tid];
+    }
+    wg_sum2_r(loc_rr, loc_rz, sm);
+    if (tid == 0) {
+      st_c(B.rr_part + item, loc_rr);
+      st_c(B.rz_part + item, loc_rz);
+    }
+    next_alpha = alpha;
+    restrict_next = true;
+  };
   for (int it = 1; it <= B.maxit + 2; ++it) {
     // ---------------- phase A (it) ----------------
     {
@@ -420,6 +474,8 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
       // The partner sums of W^T r are staged only after an exact refresh (and
       // for the initial r); otherwise they are the previous P (linearity).
       const bool r_from_prev = (it - 1) % kRefresh<T> != 0;
+      bool stepped = false;
+      double alpha = 0.0, loc_rr = 0.0;
       if (!done) {
         if constexpr (LEV > 0) {
           if (!r_from_prev) r_stage_partners<T, LEV>(G, pR[rbuf], s, k, stR);
@@ -431,8 +487,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
           done = true;
           if (lead) set_state(st, ST_BREAKDOWN, it);
         } else {
-          const double alpha = rz_old / pq;
-          double loc_rr = 0.0;
+          alpha = rz_old / pq;
           if (tid < LEAF) {
             const T rn = (T)((double)sm.r[tid] - alpha * (double)sm.q[tid]);
             sm.r[tid] = rn;
@@ -441,19 +496,13 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
           }
           // (r_prolong_split synchronizes before it reads sm.r)
           r_prolong_split<T, LEV>(F, sm, stR, stQ, alpha, gate, r_from_prev);
-          double loc_rz = 0.0;
-          if (tid < LEAF) {
-            st_c(zg + leaf0 + tid, sm.z[tid]);
-            loc_rz = (double)sm.r[tid] * (double)sm.z[tid];
-          }
-          wg_sum2_r(loc_rr, loc_rz, sm);
-          if (tid == 0) {
-            st_c(B.rr_part + item, loc_rr);
-            st_c(B.rz_part + item, loc_rz);
-          }
-          next_alpha = alpha;
-          restrict_next = true;
+          stepped = true;
+          if constexpr (!SQ) finish_bc(alpha, loc_rr);
         }
+      }
+      if constexpr (SQ) {
+        if (!squared(stepped)) return;
+        if (stepped) finish_bc(alpha, loc_rr);
       }
     }
     // Everything the next phase A reads (z, the partials, the statuses) is

@@ -104,7 +104,29 @@ def test_form_solve_parity(name, batch, form, prec):
     _log(f"form solve {name} form={form} prec={prec}")
     s = _solver(b, factors=form != hpcg.HPCG_FORM_JACOBI)
     _check_solve(b, s, form, prec=prec)
+    # the squared form runs on the register-resident engine where it fits,
+    # Jacobi on the graph engine
+    assert s.last_engine == (hpcg.HPCG_ENGINE_PERSISTENT if form == hpcg.HPCG_FORM_SQUARED
+                             else hpcg.HPCG_ENGINE_GRAPH)
+    s.close()
+
+
+@pytest.mark.parametrize("name,batch", [("N8k", None), ("tet4k", None), ("batch64x2k", 3)])
+def test_squared_solve_graph_engine(name, batch):
+    b = make_config(name, batch=batch)
+    _log(f"squared solve on the graph engine {name}")
+    s = _solver(b)
+    _check_solve(b, s, hpcg.HPCG_FORM_SQUARED, engine=hpcg.HPCG_ENGINE_GRAPH)
     assert s.last_engine == hpcg.HPCG_ENGINE_GRAPH
+    s.close()
+
+
+def test_squared_solve_resident_tet4k():
+    b = make_config("tet4k")
+    _log("squared solve resident tet4k")
+    s = _solver(b)
+    _check_solve(b, s, hpcg.HPCG_FORM_SQUARED, engine=hpcg.HPCG_ENGINE_PERSISTENT)
+    assert s.last_engine == hpcg.HPCG_ENGINE_PERSISTENT
     s.close()
 
 
@@ -223,10 +245,11 @@ def test_form_argument_errors():
     for steps in (1, 201):
         with pytest.raises(hpcg.HPCGError):
             s.estimate_spectrum(steps)
-    s.set_option(hpcg.HPCG_OPT_FORM, hpcg.HPCG_FORM_SQUARED)
+    s.set_option(hpcg.HPCG_OPT_FORM, hpcg.HPCG_FORM_JACOBI)
     s.set_option(hpcg.HPCG_OPT_ENGINE, hpcg.HPCG_ENGINE_PERSISTENT)
     with pytest.raises(hpcg.HPCGError):
         s.solve(b.b.reshape(-1), tol=b.tol, maxit=b.maxit)
+    s.set_option(hpcg.HPCG_OPT_FORM, hpcg.HPCG_FORM_SQUARED)
     with pytest.raises(hpcg.HPCGError):
         s.apply_M_block(np.zeros((b.n, 16), np.float32), 16)
     s.close()
