@@ -32,7 +32,8 @@ struct Layout {
   size_t row_ptr, col, val, U, W, g, b, r, z, q, p0, p1, x, tleaf, pleaf, pq, rr, rz, st, ctl;
   size_t fr, fd, frhs, fsc;   // outer refinement: residual, correction, scaled rhs, per-system scalars
   size_t w, dinv, ftmp;       // squared form: H r; Jacobi: 1 / A_ii; apply scratch
-  size_t llw, lle;            // single-pass apply: flagged restriction words, per-leaf epochs
+  size_t llw, lle, lly;       // single-pass apply: flagged restriction words, per-leaf epochs,
+                              // flagged diagonal-stage words of the split variant
   size_t total;
 };
 
@@ -134,6 +135,7 @@ Layout make_layout(const Geom& G, int64_t nnz) {
   L.ftmp = take(N * 4);
   L.llw = take((size_t)G.B * G.levels * G.K * RANK * 8 + 16);
   L.lle = take((size_t)G.B * G.K * 4);
+  L.lly = take((size_t)G.B * G.K * LEAF * 8);
   L.total = off;
   return L;
 }
@@ -171,6 +173,8 @@ struct hpcg_ctx {
   Geom Gapply{};           // geometry of the standalone apply kernels
   int last_apply_path = 0;
   int fused_per_cu = -1;
+  int split_per_cu = -1;
+  int split_apply = 1;     // single-pass apply with two workgroups per leaf where it fits
   double graph_tol = -1.0;
   int graph_maxit = -1;
   int last_grid = 0;
@@ -499,6 +503,7 @@ hpcg_status hpcg_create(const hpcg_partition* part, const int32_t* d_row_ptr, co
   B.bflag = reinterpret_cast<unsigned*>(w + lay.ctl + kCtlFlag);
   B.llw = reinterpret_cast<unsigned long long*>(w + lay.llw);
   B.lle = reinterpret_cast<unsigned*>(w + lay.lle);
+  B.lly = reinterpret_cast<unsigned long long*>(w + lay.lly);
   B.w = w + lay.w;
   B.dinv = reinterpret_cast<const double*>(w + lay.dinv);
   B.form = FORM_DIRECT;
@@ -507,7 +512,7 @@ hpcg_status hpcg_create(const hpcg_partition* part, const int32_t* d_row_ptr, co
 
   const size_t N = (size_t)G.B * G.n;
   CREATE_HIP(hipMemsetAsync(w + lay.ctl, 0, kCtlBytes, h->stream));
-  CREATE_HIP(hipMemsetAsync(w + lay.llw, 0, lay.lle + (size_t)G.B * G.K * 4 - lay.llw, h->stream));
+  CREATE_HIP(hipMemsetAsync(w + lay.llw, 0, lay.lly + (size_t)G.B * G.K * LEAF * 8 - lay.llw, h->stream));
   CREATE_HIP(hipMemcpyAsync(w + lay.row_ptr, d_row_ptr, (N + 1) * 4, hipMemcpyDeviceToDevice, h->stream));
   if (nnz_total > 0) {
     CREATE_HIP(hipMemcpyAsync(w + lay.col, d_col, (size_t)nnz_total * 4, hipMemcpyDeviceToDevice, h->stream));
@@ -584,25 +589,56 @@ const void* fused_apply_kernel(int levels) {
 // launches).  An ordinary launch: the one device-wide barrier inside waits for
 // workgroups that the hardware dispatches as soon as resources free up, and
 // its wait is bounded.
+const void* split_apply_kernel(int levels) {
+  switch (levels) {
+    case 1: return reinterpret_cast<const void*>(&k_apply_split<1>);
+    case 2: return reinterpret_cast<const void*>(&k_apply_split<2>);
+    case 3: return reinterpret_cast<const void*>(&k_apply_split<3>);
+    case 4: return reinterpret_cast<const void*>(&k_apply_split<4>);
+    case 5: return reinterpret_cast<const void*>(&k_apply_split<5>);
+    case 6: return reinterpret_cast<const void*>(&k_apply_split<6>);
+    case 7: return reinterpret_cast<const void*>(&k_apply_split<7>);
+    case 8: return reinterpret_cast<const void*>(&k_apply_split<8>);
+    default: return nullptr;
+  }
+}
+
 hpcg_status run_fused_apply(hpcg_ctx* h, const float* d_r, float* d_y, bool& ran) {
   ran = false;
   const Geom G = h->G;
   const int items = G.B * G.K;
   if (items > h->num_cu) return HPCG_OK;
+  Geom Ga = G;
+  Bufs Ba = h->B;
+  const float* ra = d_r;
+  float* ya = d_y;
+  void* args[] = {&Ga, &Ba, &ra, &ya};
+  const size_t dyn = (size_t)std::max(G.K - 1, 1) * RANK * sizeof(float);
+  // two workgroups per leaf (diagonal / off-diagonal roles) while the batch
+  // has at most a quarter as many leaves as the device has compute units and
+  // every workgroup can be resident at once.  Measured: n = 1,024 / 4,096 /
+  // 8,192 gain 9 / 4 / 3%; at 128 leaves (half the CUs already busy) the
+  // split gains nothing warm and loses 4% with the factors in HBM.
+  const bool split = h->split_apply && 4 * (int64_t)items <= h->num_cu;
+  if (const void* fs = split ? split_apply_kernel(G.levels) : nullptr) {
+    hpcg_status s = allow_lds(h, fs, dyn);
+    if (s != HPCG_OK) return s;
+    if (h->split_per_cu < 0)
+      HIP_OR_FAIL(h, hipOccupancyMaxActiveBlocksPerMultiprocessor(&h->split_per_cu, fs, NTR, dyn));
+    if (dyn + sizeof(RSmem<float>) <= kMaxLds && (int64_t)h->split_per_cu * h->num_cu >= 2 * (int64_t)items) {
+      HIP_OR_FAIL(h, hipLaunchKernel(fs, dim3(2 * items), dim3(NTR), args, (unsigned)dyn, h->stream));
+      ran = true;
+      return HPCG_OK;
+    }
+  }
   const void* fn = fused_apply_kernel(G.levels);
   if (!fn) return HPCG_OK;
-  const size_t dyn = (size_t)std::max(G.K - 1, 1) * RANK * sizeof(float);
   if (dyn + sizeof(RSmem<float>) > kMaxLds) return HPCG_OK;
   hpcg_status s = allow_lds(h, fn, dyn);
   if (s != HPCG_OK) return s;
   if (h->fused_per_cu < 0)
     HIP_OR_FAIL(h, hipOccupancyMaxActiveBlocksPerMultiprocessor(&h->fused_per_cu, fn, NTR, dyn));
   if ((int64_t)h->fused_per_cu * h->num_cu < items) return HPCG_OK;
-  Geom Ga = G;
-  Bufs Ba = h->B;
-  const float* ra = d_r;
-  float* ya = d_y;
-  void* args[] = {&Ga, &Ba, &ra, &ya};
   HIP_OR_FAIL(h, hipLaunchKernel(fn, dim3(items), dim3(NTR), args, (unsigned)dyn, h->stream));
   ran = true;
   return HPCG_OK;

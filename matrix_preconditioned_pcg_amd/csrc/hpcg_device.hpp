@@ -107,6 +107,7 @@ struct Bufs {
   unsigned* bflag;     // resident engine: number of the last completed barrier
   unsigned long long* llw;  // fused apply: [B][levels][K][RANK] W_l[k]^T r as (value, epoch) words
   unsigned* lle;       // fused apply: [B*K] calls completed per leaf (the epoch)
+  unsigned long long* lly;  // split apply: [B*K][LEAF] U_k U_k^T r as (value, epoch) words
   int* abort_flag;     // set when a barrier wait exceeds its bound
   int* itbase;         // graph engine: absolute iteration of the replay's first step
   int* replays;        // graph engine: replays finished

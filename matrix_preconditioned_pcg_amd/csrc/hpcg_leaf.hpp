@@ -113,15 +113,11 @@ __device__ __forceinline__ void restrict_w_partials(const Resident<T, LEV>& F, c
   }
 }
 
-// U_k and the leaf's level slabs into the register layout of Resident.
+// The leaf's level slabs into the register layout of Resident.
 template <typename T, int LEV>
-__device__ __forceinline__ void load_factors(const Geom& G, const Bufs& B, int s, int k, Resident<T, LEV>& F) {
-  const int tid = threadIdx.x;
-  const int cs = tid & 31, rg = tid >> 5;
-  const float* Uk = B.U + ((size_t)s * G.K + k) * LEAF * LEAF;
-  // slabs first: the single-pass apply publishes their restriction before it
-  // needs U_k
+__device__ __forceinline__ void load_slabs(const Geom& G, const Bufs& B, int s, int k, Resident<T, LEV>& F) {
   if constexpr (LEV > 0) {
+    const int tid = threadIdx.x;
     const int c8 = tid & 7, row = tid >> 3;
 #pragma unroll
     for (int l = 0; l < LEV; ++l) {
@@ -130,8 +126,25 @@ __device__ __forceinline__ void load_factors(const Geom& G, const Bufs& B, int s
       F.w[l][1] = *reinterpret_cast<const float4*>(Wl + (row + 64) * RANK + 4 * c8);
     }
   }
+}
+
+// U_k into the register layout of Resident.
+template <typename T, int LEV>
+__device__ __forceinline__ void load_leaf(const Geom& G, const Bufs& B, int s, int k, Resident<T, LEV>& F) {
+  const int tid = threadIdx.x;
+  const int cs = tid & 31, rg = tid >> 5;
+  const float* Uk = B.U + ((size_t)s * G.K + k) * LEAF * LEAF;
 #pragma unroll
   for (int m = 0; m < 8; ++m) F.u[m] = *reinterpret_cast<const float4*>(Uk + (rg + 16 * m) * LEAF + 4 * cs);
+}
+
+// U_k and the leaf's level slabs into the register layout of Resident (slabs
+// first: the single-pass apply publishes their restriction before it needs
+// U_k).
+template <typename T, int LEV>
+__device__ __forceinline__ void load_factors(const Geom& G, const Bufs& B, int s, int k, Resident<T, LEV>& F) {
+  load_slabs(G, B, s, k, F);
+  load_leaf(G, B, s, k, F);
 }
 
 // Strip aggregation (eq. (3)) from the staged partner restrictions of r

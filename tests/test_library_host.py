@@ -61,7 +61,7 @@ def test_workspace_bytes_covers_the_buffers(hp):
     vectors = 16384 * (2 * 4 + 7 * 8)            # g, b fp32; r (two), z, q, p0, p1, x fp64
     # per leaf: diagonal shares of up to 8 slots and two copies of W_l[k]^T r_k, fp64
     restrictions = 128 * (8 * 128 + 2 * 7 * 32) * 8
-    flagged = 128 * 7 * 32 * 8                   # single-pass apply: (value, epoch) words
+    flagged = 128 * 7 * 32 * 8 + 128 * 128 * 8   # single-pass apply: (value, epoch) words
     need = factors + csr + vectors + restrictions + flagged
     assert need <= nbytes <= need + (1 << 20)
     assert hp.hpcg_workspace_bytes(hp.partition(2048, batch=64), 851968) > 64 * hp.hpcg_workspace_bytes(
