@@ -254,6 +254,33 @@ def test_apply_spmv_small_and_ragged(n, levels, batch):
     s.close()
 
 
+@pytest.mark.parametrize("form", [hpcg.HPCG_FORM_DIRECT, hpcg.HPCG_FORM_SQUARED])
+@pytest.mark.parametrize("engine", [hpcg.HPCG_ENGINE_PERSISTENT, hpcg.HPCG_ENGINE_GRAPH])
+@pytest.mark.parametrize("n,levels,batch", [(128, 0, 1), (256, 1, 2), (1024, 3, 1), (2048, 2, 3), (4096, 0, 1)])
+def test_solve_small_and_ragged(n, levels, batch, engine, form):
+    # single-leaf systems, partial hierarchies (fewer levels than log2 K) and
+    # small batches through every resident-engine instantiation they reach
+    _log(f"solve small n={n} levels={levels} batch={batch} engine={engine} form={form}")
+    systems = [random_system(n, seed=300 + s, levels=levels).system(0) for s in range(batch)]
+    b = build_batch(systems, name=f"small{n}_{levels}_{batch}")
+    s = _solver(b)
+    s.set_option(hpcg.HPCG_OPT_ENGINE, engine)
+    s.set_option(hpcg.HPCG_OPT_FORM, form)
+    res = s.solve(b.b.reshape(-1), tol=b.tol, maxit=b.maxit)
+    assert res.status == hpcg.HPCG_OK, hpcg.hpcg_last_error(s.handle)
+    assert s.last_engine == engine
+    for i in range(batch):
+        sy = b.system(i)
+        pre = ((lambda v, sy=sy: oracle.apply_M(sy.U, sy.W, sy.g, oracle.apply_M(sy.U, sy.W, sy.g, v)))
+               if form == hpcg.HPCG_FORM_SQUARED else (sy.U, sy.W, sy.g))
+        ref = oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b, pre, b.tol, b.maxit)
+        assert ref.status == "converged"
+        assert abs(res.iterations[i] - ref.iterations) <= 2, (i, res.iterations[i], ref.iterations)
+        tr = oracle.true_relres(sy.row_ptr, sy.col, sy.val, sy.b, res.x[i].cpu().numpy())
+        assert res.relres[i] <= b.tol and tr <= 1.05 * b.tol, (i, res.relres[i], tr)
+    s.close()
+
+
 def _check_solve(batch, res, refs):
     for i, ref in enumerate(refs):
         sy = batch.system(i)
