@@ -824,7 +824,7 @@ namespace {
 
 // Sub-buffers of the block solve's caller-provided work buffer.
 struct BlockSolveLayout {
-  size_t R, Z, P, Q, scratchQ, scratchH, part, cs, ctr, total;
+  size_t R, Z, P, Q, scratchQ, scratchH, part, part2, cs, ctr, total;
 };
 
 BlockSolveLayout block_solve_layout(const hpcg_ctx* h, int32_t nrhs) {
@@ -840,13 +840,14 @@ BlockSolveLayout block_solve_layout(const hpcg_ctx* h, int32_t nrhs) {
   L.scratchQ = take(half);
   L.scratchH = take(half);
   L.part = take((size_t)h->G.B * (h->G.n / BS_ROWS) * nrhs * 8);
+  L.part2 = take((size_t)h->G.B * (h->G.n / BS_ROWS) * nrhs * 8);
   L.cs = take((size_t)h->G.B * nrhs * sizeof(ColState));
   L.ctr = take(256);
   L.total = off;
   return L;
 }
 
-// One block-PCG iteration (nine steps; see hpcg_bsolve.hpp) on `stream`.
+// One block-PCG iteration (eight launches, the steps of hpcg_bsolve.hpp) on `stream`.
 hpcg_status block_iteration(hpcg_ctx* h, int32_t nrhs, char* wk, const BlockSolveLayout& L, double* d_X,
                             double tol, int32_t maxit, hipStream_t stream) {
   const Geom& G = h->G;
@@ -855,6 +856,7 @@ hpcg_status block_iteration(hpcg_ctx* h, int32_t nrhs, char* wk, const BlockSolv
   float* P = reinterpret_cast<float*>(wk + L.P);
   float* Q = reinterpret_cast<float*>(wk + L.Q);
   double* part = reinterpret_cast<double*>(wk + L.part);
+  double* part2 = reinterpret_cast<double*>(wk + L.part2);
   ColState* cs = reinterpret_cast<ColState*>(wk + L.cs);
   const int rblocks = G.n / BS_ROWS;   // row blocks per system
   const dim3 rows_grid((unsigned)(G.B * rblocks), (unsigned)((nrhs + BS_COLS - 1) / BS_COLS));
@@ -864,14 +866,15 @@ hpcg_status block_iteration(hpcg_ctx* h, int32_t nrhs, char* wk, const BlockSolv
   hipLaunchKernelGGL(k_spmv_block, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, h->B.row_ptr,
                      h->B.col, h->B.val, P, Q, G.B * G.n, nrhs);
   hipLaunchKernelGGL(k_bs_dot, rows_grid, dim3(BS_NT), 0, stream, P, Q, part, nrhs);
-  hipLaunchKernelGGL(k_bs_scalars<BS_PQ>, sc_grid, dim3(64 * BS_SC_COLS), 0, stream, cs, part, G.B, nrhs, rblocks, tol, maxit);
-  hipLaunchKernelGGL(k_bs_update, rows_grid, dim3(BS_NT), 0, stream, cs, P, Q, R, d_X, part, nrhs, rblocks);
-  hipLaunchKernelGGL(k_bs_scalars<BS_RR>, sc_grid, dim3(64 * BS_SC_COLS), 0, stream, cs, part, G.B, nrhs, rblocks, tol, maxit);
+  hipLaunchKernelGGL(k_bs_scalars<BS_PQ>, sc_grid, dim3(64 * BS_SC_COLS), 0, stream, cs, part, G.B, nrhs, rblocks, tol, maxit,
+                     (const double*)nullptr);
+  hipLaunchKernelGGL(k_bs_update, rows_grid, dim3(BS_NT), 0, stream, cs, P, Q, R, d_X, part2, nrhs, rblocks);
   hpcg_status s = launch_block_apply(h, nrhs, R, Z, reinterpret_cast<float*>(wk + L.scratchQ),
                                      reinterpret_cast<float*>(wk + L.scratchH), stream);
   if (s != HPCG_OK) return s;
   hipLaunchKernelGGL(k_bs_dot, rows_grid, dim3(BS_NT), 0, stream, R, Z, part, nrhs);
-  hipLaunchKernelGGL(k_bs_scalars<BS_RZ>, sc_grid, dim3(64 * BS_SC_COLS), 0, stream, cs, part, G.B, nrhs, rblocks, tol, maxit);
+  hipLaunchKernelGGL(k_bs_scalars<BS_RRZ>, sc_grid, dim3(64 * BS_SC_COLS), 0, stream, cs, part, G.B, nrhs, rblocks, tol, maxit,
+                     (const double*)part2);
   hipLaunchKernelGGL(k_bs_direction, rows_grid, dim3(BS_NT), 0, stream, cs, Z, P, nrhs, rblocks);
   return HPCG_OK;
 }
@@ -942,12 +945,14 @@ hpcg_status hpcg_solve_block(hpcg_handle h, const float* d_B, double* d_X, int32
   __atomic_store_n(hflag, 0, __ATOMIC_RELEASE);
   hipLaunchKernelGGL(k_bs_reset, dim3(1), dim3(64), 0, h->stream, ctr, dflag);
   hipLaunchKernelGGL(k_bs_init, rows_grid, dim3(BS_NT), 0, h->stream, d_B, R, d_X, part, nrhs);
-  hipLaunchKernelGGL(k_bs_scalars<BS_INIT>, sc_grid, dim3(64 * BS_SC_COLS), 0, h->stream, cs, part, G.B, nrhs, rblocks, tol, maxit);
+  hipLaunchKernelGGL(k_bs_scalars<BS_INIT>, sc_grid, dim3(64 * BS_SC_COLS), 0, h->stream, cs, part, G.B, nrhs, rblocks, tol, maxit,
+                     (const double*)nullptr);
   hpcg_status s = launch_block_apply(h, nrhs, R, Z, reinterpret_cast<float*>(wk + L.scratchQ),
                                      reinterpret_cast<float*>(wk + L.scratchH), h->stream);
   if (s != HPCG_OK) return s;
   hipLaunchKernelGGL(k_bs_dot, rows_grid, dim3(BS_NT), 0, h->stream, R, Z, part, nrhs);
-  hipLaunchKernelGGL(k_bs_scalars<BS_RZ0>, sc_grid, dim3(64 * BS_SC_COLS), 0, h->stream, cs, part, G.B, nrhs, rblocks, tol, maxit);
+  hipLaunchKernelGGL(k_bs_scalars<BS_RZ0>, sc_grid, dim3(64 * BS_SC_COLS), 0, h->stream, cs, part, G.B, nrhs, rblocks, tol, maxit,
+                     (const double*)nullptr);
   hipLaunchKernelGGL(k_bs_direction, rows_grid, dim3(BS_NT), 0, h->stream, cs, Z, P, nrhs, rblocks);
   s = check_launch(h, "block solve setup launch");
   if (s != HPCG_OK) return s;

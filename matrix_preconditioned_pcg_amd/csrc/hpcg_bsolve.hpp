@@ -10,8 +10,12 @@
 //
 // Per iteration, for every running column j:
 //   Q = A P;  pq_j = P_j . Q_j;  alpha_j = rz_j / pq_j;
-//   X_j += alpha_j P_j;  R_j -= alpha_j Q_j;  stop when ||R_j|| / ||B_j|| <= tol;
-//   Z = M R;  rz'_j = R_j . Z_j;  beta_j = rz'_j / rz_j;  P_j = Z_j + beta_j P_j.
+//   X_j += alpha_j P_j;  R_j -= alpha_j Q_j;  Z = M R;  rz'_j = R_j . Z_j;
+//   stop when ||R_j|| / ||B_j|| <= tol, else beta_j = rz'_j / rz_j;
+//   P_j = Z_j + beta_j P_j.
+// The test is taken with beta, after Z = M R: a column that has just
+// converged costs one unused column of the block apply, and its count and x
+// are those of the textbook loop, with one launch fewer per iteration.
 // R, Z, P, Q are fp32 (the block apply's arithmetic), X and every scalar fp64.
 // A finished column gets alpha = beta = 0 from then on, so its X and R stay
 // as they were while the others continue.
@@ -41,7 +45,7 @@ struct ColState {
   int pad[2];
 };
 
-enum : int { BS_INIT = 0, BS_RZ0 = 1, BS_PQ = 2, BS_RR = 3, BS_RZ = 4 };
+enum : int { BS_INIT = 0, BS_RZ0 = 1, BS_PQ = 2, BS_RRZ = 3 };
 
 // Workgroup (leaf rb, column tile) -> thread's column c, row group rg.
 __device__ __forceinline__ double bs_rowgroup_reduce(double acc, double* red) {
@@ -147,18 +151,25 @@ __global__ __launch_bounds__(BS_NT) void k_bs_direction(const ColState* __restri
 // l, l + 64, ... and the lanes are combined by the fixed butterfly of
 // wave_sum (one order, every call); lane 0 takes the step the mode names.
 constexpr int BS_SC_COLS = 4;   // columns (waves) per workgroup
+// RRZ takes the convergence test on part2 (r.r) and then beta on part (r.z).
 template <int MODE>
 __global__ __launch_bounds__(64 * BS_SC_COLS) void k_bs_scalars(ColState* __restrict__ cs,
                                                                 const double* __restrict__ part, int systems,
                                                                 int nrhs, int blocks_per_system, double tol,
-                                                                int maxit) {
+                                                                int maxit, const double* __restrict__ part2) {
   const int idx = blockIdx.x * BS_SC_COLS + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (idx >= systems * nrhs) return;     // whole waves leave together
   const int s = idx / nrhs, c = idx - s * nrhs;
-  double v = 0.0;
-  for (int k = lane; k < blocks_per_system; k += 64) v += part[((size_t)s * blocks_per_system + k) * nrhs + c];
+  double v = 0.0, v2 = 0.0;
+  for (int k = lane; k < blocks_per_system; k += 64) {
+    const size_t o = ((size_t)s * blocks_per_system + k) * nrhs + c;
+    v += part[o];
+    if constexpr (MODE == BS_RRZ) v2 += part2[o];
+  }
   const double sum = wave_sum(v);
+  double sum2 = 0.0;
+  if constexpr (MODE == BS_RRZ) sum2 = wave_sum(v2);
   if (lane != 0) return;
   ColState st = cs[idx];
   if constexpr (MODE == BS_INIT) {
@@ -180,13 +191,12 @@ __global__ __launch_bounds__(64 * BS_SC_COLS) void k_bs_scalars(ColState* __rest
       if (!(sum > 0.0) || !isfinite(sum)) st.status = ST_BREAKDOWN;
       else st.alpha = st.rz / sum;
     }
-  } else if constexpr (MODE == BS_RR) {
+  } else {   // BS_RRZ
     if (st.status == ST_RUNNING) {
-      st.relres = sqrt(sum) / st.bnorm;
+      st.relres = sqrt(sum2) / st.bnorm;
       if (st.relres <= tol) st.status = ST_CONVERGED;
       else if (st.iters >= maxit) st.status = ST_NOT_CONVERGED;
     }
-  } else {   // BS_RZ
     st.beta = 0.0;
     if (st.status == ST_RUNNING) {
       if (!(sum > 0.0) || !isfinite(sum)) {
