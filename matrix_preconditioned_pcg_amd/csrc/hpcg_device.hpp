@@ -194,13 +194,27 @@ __device__ __forceinline__ void dma_to_lds(void* dst, int nchunks, AddrFn addr) 
   }
 }
 
+// threadIdx.x, with FRESH behind an empty asm.  The persistent solves call
+// the steps that take it every iteration; the compiler otherwise hoists every
+// address those steps derive from the thread index out of the solve loop,
+// where the addresses hold registers for the whole solve.  Where that does not
+// fit in the register file they spill to scratch, and each reload in the loop
+// waits for every outstanding memory operation; recomputing an address costs a
+// couple of integer operations.  Where it fits, the hoisted form is faster.
+template <bool FRESH>
+__device__ __forceinline__ int tid_of() {
+  int t = threadIdx.x;
+  if constexpr (FRESH) asm volatile("" : "+v"(t));
+  return t;
+}
+
 // dma_to_lds for a workgroup of NW waves.  CPOL is the load's cache policy:
 // 0 = default, CPOL_AGENT = agent-scope coherent (sc1: never served from a
 // stale copy in another XCD's L2).
 constexpr int CPOL_AGENT = 16;
-template <int NW, int CPOL = 0, typename AddrFn>
+template <int NW, int CPOL = 0, bool FRESH = false, typename AddrFn>
 __device__ __forceinline__ void dma_to_lds_n(void* dst, int nchunks, AddrFn addr) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = tid_of<FRESH>(), lane = tid & 63, wave = tid >> 6;
   for (int q = wave; q * 64 < nchunks; q += NW) {
     const int c = q * 64 + lane;
     lds_vptr l = (lds_vptr)((__attribute__((address_space(3))) char*)dst + q * 1024);

@@ -44,6 +44,15 @@ __device__ __forceinline__ void st_c(T* p, T v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Register budget of the leaf steps (see tid_of): with fp64 vectors and six
+// or more levels the hoisted addresses no longer fit beside the resident
+// factors, so the steps recompute them; from seven levels the partner staging
+// does too.  (Measured per level: below these the hoisted form is faster.)
+template <typename T, int LEV>
+constexpr bool kFresh = sizeof(T) == 8 && LEV >= 6;
+template <typename T, int LEV>
+constexpr bool kFreshDma = sizeof(T) == 8 && LEV >= 7;
+
 template <typename T, int LEV>
 struct Resident {
   float4 u[8];
@@ -55,7 +64,7 @@ struct Resident {
 // 32).  No barrier.
 template <typename T, int LEV>
 __device__ __forceinline__ void restrict_u_partials(const Resident<T, LEV>& F, const T* v, RSmem<T>& sm) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = tid_of<kFresh<T, LEV>>(), lane = tid & 63, wave = tid >> 6;
   const int cs = tid & 31, rg = tid >> 5;
   Vec4<T> acc{0, 0, 0, 0};
 #pragma unroll
@@ -75,7 +84,7 @@ __device__ __forceinline__ void restrict_u_partials(const Resident<T, LEV>& F, c
 template <typename T, int LEV>
 __device__ __forceinline__ void restrict_w_partials(const Resident<T, LEV>& F, const T* v, RSmem<T>& sm) {
   if constexpr (LEV > 0) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = tid_of<kFresh<T, LEV>>(), lane = tid & 63, wave = tid >> 6;
     const int cs = tid & 7, row = tid >> 3;
     const T r0 = v[row], r1 = v[row + 64];
     const bool b5 = (lane & 32) != 0, b4 = (lane & 16) != 0, b3 = (lane & 8) != 0;
@@ -156,7 +165,7 @@ __device__ __forceinline__ void load_factors(const Geom& G, const Bufs& B, int s
 template <typename T, int LEV>
 __device__ __forceinline__ void prolong_strips(RSmem<T>& sm, const T* stR, const T* stQ, double alpha,
                                                bool r_from_prev = false) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = tid_of<kFresh<T, LEV>>(), lane = tid & 63, wave = tid >> 6;
   const int c = tid & 31, g = tid >> 5;
 #pragma unroll
   for (int l = 0; l < LEV; ++l) {
@@ -203,7 +212,7 @@ __device__ __forceinline__ void prolong_strips(RSmem<T>& sm, const T* stR, const
 // (7 + 2 shuffles).  No barrier.
 template <typename T, int LEV>
 __device__ __forceinline__ void diag_times(const Resident<T, LEV>& F, const T* t, T* y) {
-  const int tid = threadIdx.x;
+  const int tid = tid_of<kFresh<T, LEV>>();
   const int cs = tid & 31, rg = tid >> 5;
   const Vec4<T> t4 = lds4(&t[4 * cs]);
   T v[8];
@@ -238,7 +247,7 @@ __device__ __forceinline__ void prolong_diag(const Resident<T, LEV>& F, RSmem<T>
 // No barrier.
 template <typename T, int LEV>
 __device__ __forceinline__ void prolong_offdiag(const Resident<T, LEV>& F, RSmem<T>& sm) {
-  const int tid = threadIdx.x;
+  const int tid = tid_of<kFresh<T, LEV>>();
   if constexpr (LEV > 0) {
     const int cs = tid & 7, row = tid >> 3;
     T o0 = 0, o1 = 0;

@@ -87,10 +87,10 @@ __device__ __forceinline__ bool cgrid_barrier(const Bufs& B, unsigned& target, u
 }
 
 // Sum over the workgroup in a fixed order.
-template <typename T>
+template <bool FRESH, typename T>
 __device__ __forceinline__ double wg_sum_r(double v, RSmem<T>& sm) {
   v = wave_sum(v);
-  const int tid = threadIdx.x;
+  const int tid = tid_of<FRESH>();
   if ((tid & 63) == 0) sm.dred[tid >> 6] = v;
   __syncthreads();
   double s = sm.dred[0];
@@ -101,11 +101,11 @@ __device__ __forceinline__ double wg_sum_r(double v, RSmem<T>& sm) {
 }
 
 // Two workgroup sums with one pair of barriers.
-template <typename T>
+template <bool FRESH, typename T>
 __device__ __forceinline__ void wg_sum2_r(double& a, double& b, RSmem<T>& sm) {
   a = wave_sum(a);
   b = wave_sum(b);
-  const int tid = threadIdx.x;
+  const int tid = tid_of<FRESH>();
   if ((tid & 63) == 0) {
     sm.dred[tid >> 6] = a;
     sm.dred2[tid >> 6] = b;
@@ -144,7 +144,7 @@ template <typename T, int LEV>
 __device__ __forceinline__ void r_restrict(const Geom& G, int s, int k, const Resident<T, LEV>& F,
                                            const T* v, T* tout, T* pout, T* own, RSmem<T>& sm,
                                            double loc = 0.0, double* part_dst = nullptr, bool with_u = true) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = tid_of<kFresh<T, LEV>>(), lane = tid & 63, wave = tid >> 6;
   if (part_dst) {
     loc = wave_sum(loc);
     if (lane == 0) sm.dred[wave] = loc;
@@ -187,7 +187,7 @@ __device__ __forceinline__ void r_stage_partners(const Geom& G, const T* src, in
   for (int l = 0; l < LEV; ++l) {
     const int kp0 = ((k >> l) ^ 1) << l;
     const T* from = src + (((size_t)s * G.levels + l) * G.K + kp0) * RANK;
-    dma_to_lds_n<NWR, CPOL_AGENT>(stage + (size_t)((1 << l) - 1) * RANK, (1 << l) * CPV,
+    dma_to_lds_n<NWR, CPOL_AGENT, kFreshDma<T, LEV>>(stage + (size_t)((1 << l) - 1) * RANK, (1 << l) * CPV,
                       [&](int c) { return reinterpret_cast<const char*>(from) + 16 * c; });
   }
 }
@@ -196,7 +196,7 @@ __device__ __forceinline__ void r_stage_partners(const Geom& G, const T* src, in
 // caller's next barrier.
 template <typename T, int LEV>
 __device__ __forceinline__ void leaf_apply(const Resident<T, LEV>& F, const T* v, T* tmp, T* y, RSmem<T>& sm) {
-  const int tid = threadIdx.x;
+  const int tid = tid_of<kFresh<T, LEV>>();
   restrict_u_partials<T, LEV>(F, v, sm);
   __syncthreads();
   if (tid < LEAF) {
@@ -216,7 +216,7 @@ __device__ __forceinline__ void leaf_apply(const Resident<T, LEV>& F, const T* v
 template <typename T, int LEV>
 __device__ __forceinline__ void r_prolong_split(const Resident<T, LEV>& F, RSmem<T>& sm, const T* stR, const T* stQ,
                                                 double alpha, float gate, bool r_from_prev) {
-  const int tid = threadIdx.x;
+  const int tid = tid_of<kFresh<T, LEV>>();
   if constexpr (LEV > 0) prolong_strips<T, LEV>(sm, stR, stQ, alpha, r_from_prev);
   prolong_offdiag<T, LEV>(F, sm);
   __syncthreads();
@@ -231,7 +231,7 @@ __device__ __forceinline__ void r_prolong_split(const Resident<T, LEV>& F, RSmem
 template <typename T, int LEV>
 __device__ __forceinline__ void r_prolong(const Resident<T, LEV>& F, RSmem<T>& sm, const T* stR, const T* stQ,
                                           double alpha, float gate) {
-  const int tid = threadIdx.x;
+  const int tid = tid_of<kFresh<T, LEV>>();
   if constexpr (LEV > 0) prolong_strips<T, LEV>(sm, stR, stQ, alpha);
   if constexpr (LEV == 0) __syncthreads();   // sm.t and sm.r of the caller
   prolong_diag<T, LEV>(F, sm);
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
   __syncthreads();
   r_restrict<T, LEV>(G, s, k, F, sm.r, sm.tr, pR[0], sm.ownR, sm);
   diag_times<T, LEV>(F, sm.tr, sm.yr);       // U_k U_k^T r0 (read in the first phase BC)
-  double part = wg_sum_r(loc, sm);
+  double part = wg_sum_r<kFresh<T, LEV>>(loc, sm);
   if (tid == 0) {
     st_c(B.rr_part + item, part);
     if (k == 0) {
@@ -360,7 +360,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
         st_c(zg + leaf0 + tid, sm.z[tid]);
         loc = (double)sm.r[tid] * (double)sm.z[tid];
       }
-      part = wg_sum_r(loc, sm);
+      part = wg_sum_r<kFresh<T, LEV>>(loc, sm);
       if (tid == 0) st_c(B.rz_part + item, part);
     }
   }
@@ -380,7 +380,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
       st_c(zg + leaf0 + tid, sm.z[tid]);
       loc_rz = (double)sm.r[tid] * (double)sm.z[tid];
     }
-    wg_sum2_r(loc_rr, loc_rz, sm);
+    wg_sum2_r<kFresh<T, LEV>>(loc_rr, loc_rz, sm);
     if (tid == 0) {
       st_c(B.rr_part + item, loc_rr);
       st_c(B.rz_part + item, loc_rz);
