@@ -304,6 +304,31 @@ __device__ __forceinline__ T lane_x32(T v) {
   });
 }
 
+// Folding steps of a transpose-reduce: one swap moves a's partner into the
+// lanes that keep a and b's partner into the lanes that keep b, so lanes with
+// bit 5 (bit 4) clear end with a + a(lane ^ 32) (a + a(lane ^ 16)) and the
+// others with b + b(partner), with no per-lane selects.  Each sum adds the same
+// two values as the select-and-exchange form.
+template <typename T, typename Swap>
+__device__ __forceinline__ T fold_pair(T a, T b, Swap swap) {
+  if constexpr (sizeof(T) == 4) {
+    const auto p = swap(__float_as_uint(a), __float_as_uint(b));
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  } else {
+    const auto lo = swap((unsigned)__double2loint(a), (unsigned)__double2loint(b));
+    const auto hi = swap((unsigned)__double2hiint(a), (unsigned)__double2hiint(b));
+    return __hiloint2double((int)hi[0], (int)lo[0]) + __hiloint2double((int)hi[1], (int)lo[1]);
+  }
+}
+template <typename T>
+__device__ __forceinline__ T fold_x32(T a, T b) {
+  return fold_pair(a, b, [](unsigned x, unsigned y) { return __builtin_amdgcn_permlane32_swap(x, y, false, false); });
+}
+template <typename T>
+__device__ __forceinline__ T fold_x16(T a, T b) {
+  return fold_pair(a, b, [](unsigned x, unsigned y) { return __builtin_amdgcn_permlane16_swap(x, y, false, false); });
+}
+
 // Sum over groups of 4 / 8 consecutive lanes (every lane of the group gets it).
 template <typename T>
 __device__ __forceinline__ T group4_sum(T v) { v += lane_x1(v); return v + lane_x2(v); }

@@ -69,12 +69,11 @@ __device__ __forceinline__ void restrict_u_partials(const Resident<T, LEV>& F, c
   Vec4<T> acc{0, 0, 0, 0};
 #pragma unroll
   for (int m = 0; m < 8; ++m) axpy4(acc, F.u[m], v[rg + 16 * m]);
-  acc.x += lane_x32(acc.x); acc.y += lane_x32(acc.y);
-  acc.z += lane_x32(acc.z); acc.w += lane_x32(acc.w);
-  if (lane < 32) {
-    T* d = &sm.red[wave][4 * cs];
-    d[0] = acc.x; d[1] = acc.y; d[2] = acc.z; d[3] = acc.w;
-  }
+  // lanes < 32 finish components x and z, lanes >= 32 components y and w
+  const T f0 = fold_x32(acc.x, acc.y), f1 = fold_x32(acc.z, acc.w);
+  T* d = &sm.red[wave][4 * cs + (lane >> 5)];
+  d[0] = f0;
+  d[2] = f1;
 }
 
 // Per-wave partials of W_l[k]^T v for every level into sm.redW[wave].
@@ -103,16 +102,10 @@ __device__ __forceinline__ void restrict_w_partials(const Resident<T, LEV>& F, c
       }
       T a[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const T keep = b5 ? x[4 + i] : x[i], send = b5 ? x[i] : x[4 + i];
-        a[i] = keep + lane_x32(send);
-      }
+      for (int i = 0; i < 4; ++i) a[i] = fold_x32(x[i], x[4 + i]);
       T bb[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const T keep = b4 ? a[2 + i] : a[i], send = b4 ? a[i] : a[2 + i];
-        bb[i] = keep + lane_x16(send);
-      }
+      for (int i = 0; i < 2; ++i) bb[i] = fold_x16(a[i], a[2 + i]);
       T kk = b3 ? bb[1] : bb[0];
       kk += lane_x8(b3 ? bb[0] : bb[1]);
       // value index `which` = 4h + component: level l0 + which/4, column 4cs + which%4
@@ -167,24 +160,41 @@ __device__ __forceinline__ void prolong_strips(RSmem<T>& sm, const T* stR, const
                                                bool r_from_prev = false) {
   const int tid = tid_of<kFresh<T, LEV>>(), lane = tid & 63, wave = tid >> 6;
   const int c = tid & 31, g = tid >> 5;
+  const bool hi = (lane & 32) != 0;
+  constexpr int NL = LEV > 0 ? LEV : 1;
+  T a[NL], b[NL];
 #pragma unroll
   for (int l = 0; l < LEV; ++l) {
     const T* vr = stR + (size_t)((1 << l) - 1) * RANK + c;
-    T a = 0, b = 0;
+    a[l] = 0;
+    b[l] = 0;
 #pragma unroll
     for (int m = 0; m < ((1 << l) + 15) / 16; ++m) {
       const int i = g + 16 * m;
       if (i < (1 << l)) {
-        if (!r_from_prev) a += vr[i * RANK];
-        if (stQ) b += stQ[(size_t)((1 << l) - 1) * RANK + c + i * RANK];
+        if (!r_from_prev) a[l] += vr[i * RANK];
+        if (stQ) b[l] += stQ[(size_t)((1 << l) - 1) * RANK + c + i * RANK];
       }
     }
-    if (!r_from_prev) a += lane_x32(a);
-    if (stQ) b += lane_x32(b);
-    if (lane < 32) {
-      if (!r_from_prev) sm.redW[wave][l * RANK + c] = a;
-      if (stQ) sm.redW[wave][(MAX_LEVELS + l) * RANK + c] = b;
+  }
+  // the two 32-lane halves of the wave are folded pairwise (fold_x32)
+  T* dR = &sm.redW[wave][c];
+  T* dQ = &sm.redW[wave][MAX_LEVELS * RANK + c];
+  auto fold_levels = [&](const T* v, T* d) {
+#pragma unroll
+    for (int l = 0; l + 1 < LEV; l += 2) d[(hi ? l + 1 : l) * RANK] = fold_x32(v[l], v[l + 1]);
+    if constexpr (LEV % 2 == 1) {
+      const T f = v[LEV - 1] + lane_x32(v[LEV - 1]);
+      if (!hi) d[(LEV - 1) * RANK] = f;
     }
+  };
+  if (!r_from_prev && stQ) {
+#pragma unroll
+    for (int l = 0; l < LEV; ++l) (hi ? dQ : dR)[l * RANK] = fold_x32(a[l], b[l]);
+  } else if (stQ) {
+    fold_levels(b, dQ);
+  } else if (!r_from_prev) {
+    fold_levels(a, dR);
   }
   __syncthreads();
   if (tid < LEV * RANK) {
@@ -221,10 +231,7 @@ __device__ __forceinline__ void diag_times(const Resident<T, LEV>& F, const T* t
   const bool b4 = (cs & 16) != 0, b3 = (cs & 8) != 0, b2 = (cs & 4) != 0;
   T a[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {           // xor 16: keep the upper four rows if b4
-    const T keep = b4 ? v[4 + i] : v[i], send = b4 ? v[i] : v[4 + i];
-    a[i] = keep + lane_x16(send);
-  }
+  for (int i = 0; i < 4; ++i) a[i] = fold_x16(v[i], v[4 + i]);   // xor 16: the upper four rows if b4
   T bb[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {           // xor 8
