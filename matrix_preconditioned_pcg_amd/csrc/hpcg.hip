@@ -30,6 +30,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
   size_t row_ptr, col, val, U, W, g, b, r, z, q, p0, p1, x, tleaf, pleaf, pq, rr, rz, st, ctl;
+  size_t wgflag;              // resident engine: per-workgroup barrier lines
   size_t fr, fd, frhs, fsc;   // outer refinement: residual, correction, scaled rhs, per-system scalars
   size_t w, dinv, ftmp;       // squared form: H r; Jacobi: 1 / A_ii; apply scratch
   size_t llw, lle, lly;       // single-pass apply: flagged restriction words, per-leaf epochs,
@@ -41,8 +42,7 @@ struct Layout {
 constexpr size_t kMaxLds = 160 * 1024;
 
 // control words, each on its own 256-byte line
-constexpr size_t kCtlBarrier = 0, kCtlAbort = 256, kCtlItbase = 512, kCtlReplays = 768, kCtlFlag = 1024,
-                 kCtlBytes = 1280;
+constexpr size_t kCtlBarrier = 0, kCtlAbort = 256, kCtlItbase = 512, kCtlReplays = 768, kCtlBytes = 1024;
 
 constexpr int kMaxSplit = 8;   // workgroups per leaf in the streaming kernels
 
@@ -126,6 +126,7 @@ Layout make_layout(const Geom& G, int64_t nnz) {
   L.rz = take(items * 8);
   L.st = take((size_t)G.B * sizeof(SysState));
   L.ctl = take(kCtlBytes);
+  L.wgflag = take((size_t)G.B * G.K * kFlagStride * 4);
   L.fr = take(N * 8);
   L.fd = take(N * 8);
   L.frhs = take(N * 4);
@@ -295,7 +296,7 @@ hpcg_status run_graph(hpcg_ctx* h) {
     if (s != HPCG_OK) return s;
   }
   __atomic_store_n(h->h_flag, 0, __ATOMIC_RELEASE);
-  hipLaunchKernelGGL(k_reset, dim3(1), dim3(64), 0, h->stream, B, 1, h->d_flag);
+  hipLaunchKernelGGL(k_reset, dim3(1), dim3(64), 0, h->stream, B, 1, h->d_flag, G.B * G.K);
   hipLaunchKernelGGL(k_phase_B<T>, dim3(G.nblk), dim3(NT), restrict_lds_bytes(G), h->stream, G, B, 0, 0, 0);
   if (B.form == FORM_SQUARED) {
     hipLaunchKernelGGL(k_phase_C<T>, dim3(G.nblk), dim3(NT), prolong_lds_bytes<T>(G), h->stream, G, B, 0, 0, 1);
@@ -373,7 +374,7 @@ hpcg_status run_resident(hpcg_ctx* h, bool& ran) {
   int per_cu = 0;
   HIP_OR_FAIL(h, hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NTR, dyn));
   if ((int64_t)per_cu * h->num_cu < items) return HPCG_OK;
-  hipLaunchKernelGGL(k_reset, dim3(1), dim3(64), 0, h->stream, B, 0, (int*)nullptr);
+  hipLaunchKernelGGL(k_reset, dim3(1), dim3(64), 0, h->stream, B, 0, (int*)nullptr, G.B * G.K);
   Geom Ga = G;
   Bufs Ba = B;
   int mln = h->max_leaf_nnz;
@@ -402,7 +403,7 @@ hpcg_status run_persistent(hpcg_ctx* h, bool& ran) {
   const int64_t cap = (int64_t)per_cu * h->num_cu;
   if (cap <= 0) return HPCG_OK;
   const int grid = (int)std::min<int64_t>(cap, G.nblk);
-  hipLaunchKernelGGL(k_reset, dim3(1), dim3(64), 0, h->stream, B, 0, (int*)nullptr);
+  hipLaunchKernelGGL(k_reset, dim3(1), dim3(64), 0, h->stream, B, 0, (int*)nullptr, G.B * G.K);
   Geom Ga = G;
   Bufs Ba = B;
   void* args[] = {&Ga, &Ba};
@@ -500,7 +501,7 @@ hpcg_status hpcg_create(const hpcg_partition* part, const int32_t* d_row_ptr, co
   B.abort_flag = reinterpret_cast<int*>(w + lay.ctl + kCtlAbort);
   B.itbase = reinterpret_cast<int*>(w + lay.ctl + kCtlItbase);
   B.replays = reinterpret_cast<int*>(w + lay.ctl + kCtlReplays);
-  B.bflag = reinterpret_cast<unsigned*>(w + lay.ctl + kCtlFlag);
+  B.wgflag = reinterpret_cast<unsigned*>(w + lay.wgflag);
   B.llw = reinterpret_cast<unsigned long long*>(w + lay.llw);
   B.lle = reinterpret_cast<unsigned*>(w + lay.lle);
   B.lly = reinterpret_cast<unsigned long long*>(w + lay.lly);

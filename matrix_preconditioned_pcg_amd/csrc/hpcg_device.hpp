@@ -104,7 +104,7 @@ struct Bufs {
   double* rz_part;
   SysState* st;        // [B]
   unsigned* barrier;   // device-wide barrier arrival counter
-  unsigned* bflag;     // resident engine: number of the last completed barrier
+  unsigned* wgflag;    // resident engine: per-workgroup barrier counts, one 128-byte line each
   unsigned long long* llw;  // fused apply: [B][levels][K][RANK] W_l[k]^T r as (value, epoch) words
   unsigned* lle;       // fused apply: [B*K] calls completed per leaf (the epoch)
   unsigned long long* lly;  // split apply: [B*K][LEAF] U_k U_k^T r as (value, epoch) words

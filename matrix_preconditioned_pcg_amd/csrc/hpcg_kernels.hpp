@@ -123,12 +123,13 @@ __global__ void k_advance(Geom G, Bufs B, int unroll, int* host_flag) {
   __hip_atomic_store(host_flag, (rep << 1) | done, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-// Reset the control words before a solve (a kernel, not a memset, so that it
-// can also sit inside captured work).
-__global__ void k_reset(Bufs B, int itbase, int* host_flag) {
+// Reset the control words and the nflags per-workgroup barrier lines before a
+// solve (a kernel, not a memset, so that it can also sit inside captured work).
+constexpr int kFlagStride = 32;   // unsigned words per barrier line (128 bytes)
+__global__ void k_reset(Bufs B, int itbase, int* host_flag, int nflags) {
+  for (int i = threadIdx.x; i < nflags; i += blockDim.x) B.wgflag[(size_t)i * kFlagStride] = 0u;
   if (threadIdx.x != 0 || blockIdx.x != 0) return;
   *B.barrier = 0u;
-  *B.bflag = 0u;
   *B.abort_flag = 0;
   *B.itbase = itbase;
   *B.replays = 0;

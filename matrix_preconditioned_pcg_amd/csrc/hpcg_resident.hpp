@@ -11,79 +11,83 @@
 //     the per-leaf restrictions W_l[k]^T r_k and W_l[k]^T q_k, and the scalar
 //     partials.
 //
-// Two device-wide barriers per iteration.  The restriction is linear, so
-// W^T r_new = W^T r - alpha W^T q: phase A, which owns the whole leaf's q,
-// restricts q right after the SpMV, and the next phase forms the partner-half
-// sums of (W^T r - alpha W^T q) and applies M to r_new without another
-// barrier.  W^T r is recomputed exactly from r_new every iteration (into the
-// other of two buffers), so the recurrence never accumulates rounding drift.
+// Two barriers per iteration, each among the workgroups of one system.  The
+// restriction is linear, so W^T r_new = W^T r - alpha W^T q: phase A, which
+// owns the whole leaf's q, restricts q right after the SpMV, and the next
+// phase forms the partner-half sums of (W^T r - alpha W^T q) and applies M to
+// r_new without another barrier.  Every kRefresh iterations W^T r is
+// recomputed exactly from r_new (into the other of two buffers) and its
+// partner sums are staged afresh; in between they are carried forward by the
+// same linear update, so rounding drift never accumulates past a refresh.
 //   A(it):  convergence test on ||r_{it-1}||; beta; p = z + beta p;
-//           q = A p; t_q = U_k^T q, W_l[k]^T q; partial p.q
+//           q = A p; W_l[k]^T q; partial p.q; then, during the barrier,
+//           U_k U_k^T q
 //   BC(it): alpha; x += alpha p; r -= alpha q; partial r.r;
-//           z = U_k (t_r - alpha t_q) + sum_l W_l[k] P_l + g r with
+//           z = U_k U_k^T r_new + sum_l W_l[k] P_l + g r_new with
 //           P_l = partner-half sum of (W^T r - alpha W^T q);  partial r.z;
-//           t_r = U_k^T r, W_l[k]^T r for the next iteration
+//           then, during the barrier, U_k U_k^T r_new (and at a refresh
+//           W_l[k]^T r_new)
 // Per iteration the factors are never reloaded.
 //
 // Coherence without cache maintenance.  Every value one workgroup writes for
-// another (z and p, the restrictions, the scalar partials, the statuses) is
-// stored and loaded with agent-scope accesses (sc1: written through to, and
-// read from, the point where all XCDs agree), so the device-wide barrier needs
-// no L2 write-back or invalidation: arriving waits until this workgroup's
-// stores are acknowledged, then bumps the counter; the last arrival publishes
-// the barrier number on a line of its own that the others poll.
+// another (z and p, the restrictions, the scalar partials, the statuses, the
+// barrier lines) is stored and loaded with agent-scope accesses (sc1: written
+// through to, and read from, the point where all XCDs agree), so the barrier
+// needs no L2 write-back or invalidation: arriving waits until this
+// workgroup's stores are acknowledged, then stores its barrier count on its
+// own line, which the system's other workgroups poll.
 #pragma once
 #include "hpcg_kernels.hpp"
 #include "hpcg_leaf.hpp"
 
 namespace hpcg {
 
-// Device-wide barrier over agent-coherent data (see the header).  `epoch`
-// counts this workgroup's barriers; the flag holds the last completed one.
-// Small grids (kPollCounterMax workgroups or fewer) poll the arrival counter
-// itself, which saves the flag store's hop (N1k: 1.06 -> 0.98 ms per solve);
-// larger grids poll the flag line, because polls of the line that every
-// arrival increments slow the increments down (128 workgroups: 3.9 -> 4.4 ms).
-constexpr unsigned kPollCounterMax = 16;
-__device__ __forceinline__ void cgrid_arrive(const Bufs& B, unsigned& target, unsigned& epoch) {
+// Per-system barrier over agent-coherent data (see the header).  `epoch`
+// counts this workgroup's barriers.  Arriving waits until this workgroup's
+// stores are acknowledged, then stores the count on the workgroup's own
+// 128-byte line; waiting polls the lines of the system's K workgroups (one
+// wave, a line per lane) until all of them hold it.  No read-modify-write is
+// on the path, so a barrier costs one store and one load after the last
+// arrival, and the systems of a batch synchronize independently.
+__device__ __forceinline__ void cgrid_arrive(const Bufs& B, unsigned& epoch) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  target += gridDim.x;
   ++epoch;
-  if (threadIdx.x == 0) {
-    const unsigned old = __hip_atomic_fetch_add(B.barrier, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (gridDim.x > kPollCounterMax && old + 1 == target) st_c(B.bflag, epoch);
-  }
+  if (threadIdx.x == 0) st_c(B.wgflag + (size_t)blockIdx.x * kFlagStride, epoch);
 }
 
-__device__ __forceinline__ bool cgrid_wait(const Bufs& B, unsigned target, unsigned epoch) {
+__device__ __forceinline__ bool cgrid_wait(const Bufs& B, int s, int K, unsigned epoch) {
   __shared__ int aborted_c;
-  if (threadIdx.x == 0) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const unsigned* f = B.wgflag + (size_t)s * K * kFlagStride;
     unsigned polls = 0;
     int ab = 0;
-    const bool counter = gridDim.x <= kPollCounterMax;
-    while (counter ? ld_c(B.barrier) < target : ld_c(B.bflag) < epoch) {
+    for (;;) {
+      int ready = 1;
+      for (int j = lane; j < K; j += 64) ready &= (ld_c(f + (size_t)j * kFlagStride) >= epoch) ? 1 : 0;
+      if (__all(ready)) break;
       __builtin_amdgcn_s_sleep(1);
       if (((++polls) & 1023u) == 0) {
         if (ld_c(B.abort_flag)) { ab = 1; break; }
         if (polls > (1u << 26)) {
-          st_c(B.abort_flag, 1);
+          if (lane == 0) st_c(B.abort_flag, 1);
           ab = 1;
           break;
         }
       }
     }
-    aborted_c = ab;
+    if (lane == 0) aborted_c = ab;
   }
   __syncthreads();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   return aborted_c != 0;
 }
 
-__device__ __forceinline__ bool cgrid_barrier(const Bufs& B, unsigned& target, unsigned& epoch) {
-  cgrid_arrive(B, target, epoch);
-  return cgrid_wait(B, target, epoch);
+__device__ __forceinline__ bool cgrid_barrier(const Bufs& B, int s, int K, unsigned& epoch) {
+  cgrid_arrive(B, epoch);
+  return cgrid_wait(B, s, K, epoch);
 }
 
 // Sum over the workgroup in a fixed order.
@@ -277,7 +281,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
   const float gate = (tid < LEAF) ? B.g[leaf0 + tid] : 0.f;
   double x = 0.0;                      // x of row tid (tid < LEAF)
   T* zg = reinterpret_cast<T*>(B.z);
-  unsigned target = 0, epoch = 0;
+  unsigned epoch = 0;
 
   // Squared form M = H H: with w = H r in sm.z, z = H w into sm.z.  The
   // slabs' restriction of w is new data, so it costs one more device-wide
@@ -291,9 +295,9 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
       __syncthreads();
       r_restrict<T, LEV>(G, s, k, F, sm.t, sm.tq, pW, sm.ownQ, sm, 0.0, nullptr, false);
     }
-    cgrid_arrive(B, target, epoch);
+    cgrid_arrive(B, epoch);
     if (active) leaf_apply<T, LEV>(F, sm.t, sm.tq, sm.yleaf, sm);
-    if (cgrid_wait(B, target, epoch)) return false;
+    if (cgrid_wait(B, s, G.K, epoch)) return false;
     if (active) {
       if constexpr (LEV > 0) {
         r_stage_partners<T, LEV>(G, pW, s, k, stR);
@@ -332,7 +336,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
       set_state(st, ST_RUNNING, 0);
     }
   }
-  if (cgrid_barrier(B, target, epoch)) return;
+  if (cgrid_barrier(B, s, G.K, epoch)) return;
 
   // ---- z0 = M r0 ----
   bool done = false;                   // this system has finished (decided locally)
@@ -364,11 +368,12 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
       if (tid == 0) st_c(B.rz_part + item, part);
     }
   }
-  if (cgrid_barrier(B, target, epoch)) return;
+  if (cgrid_barrier(B, s, G.K, epoch)) return;
 
-  // Statuses are written by each system's lead only in the second phase of an
-  // iteration and read by everyone only in the first, so every workgroup sees
-  // the same values and leaves the loop together.
+  // A system's status is written by its lead only in the second phase of an
+  // iteration and read by the system's workgroups only in the first, so they
+  // all see the same value and leave the loop together (a finished system's
+  // workgroups leave while other systems of the batch continue).
   int pend_status = ST_RUNNING, pend_iters = 0;
   double pend_rel = 0.0;
   bool restrict_next = false;
@@ -413,9 +418,8 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
           if (!first) pc[u] = ld_c(pold + c);
         }
       }
-      int running = 0;
-      for (int q = tid; q < G.B; q += NTR)
-        running |= (__hip_atomic_load(&B.st[q].status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ST_RUNNING);
+      const int running =
+          __hip_atomic_load(&st->status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ST_RUNNING;
       const double rr = sum_partials_r(B.rr_part, s, G.K);
       const double rz = sum_partials_r(B.rz_part, s, G.K);
       if (!__syncthreads_or(running)) break;
@@ -460,10 +464,10 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
         r_restrict<T, LEV>(G, s, k, F, sm.q, sm.tq, pQ, sm.ownQ, sm, loc, B.pq_part + item, false);
       }
     }
-    cgrid_arrive(B, target, epoch);
+    cgrid_arrive(B, epoch);
     // U_k U_k^T q is this workgroup's alone: it overlaps the wait
     if (!done) leaf_apply<T, LEV>(F, sm.q, sm.tq, sm.yq, sm);
-    if (cgrid_wait(B, target, epoch)) return;
+    if (cgrid_wait(B, s, G.K, epoch)) return;
     // ---------------- phase BC (it) ----------------
     {
       if (lead && pend_status != ST_RUNNING) {
@@ -508,7 +512,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
     // Everything the next phase A reads (z, the partials, the statuses) is
     // written: arrive now.  The restriction of the new r is read by the
     // partners only after the following barrier, so it overlaps the wait.
-    cgrid_arrive(B, target, epoch);
+    cgrid_arrive(B, epoch);
     if (restrict_next) {
       // exact every kRefresh iterations, else by the same linear update the
       // partners used above (its rounding drift is bounded by the refreshes)
@@ -523,7 +527,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
         if (tid < LEAF) sm.yr[tid] = (T)((double)sm.yr[tid] - next_alpha * (double)sm.yq[tid]);
       }
     }
-    if (cgrid_wait(B, target, epoch)) return;
+    if (cgrid_wait(B, s, G.K, epoch)) return;
   }
   // ---- the solution of the leaf's rows ----
   if (tid < LEAF) B.x[leaf0 + tid] = x;

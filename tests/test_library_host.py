@@ -62,7 +62,8 @@ def test_workspace_bytes_covers_the_buffers(hp):
     # per leaf: diagonal shares of up to 8 slots and two copies of W_l[k]^T r_k, fp64
     restrictions = 128 * (8 * 128 + 2 * 7 * 32) * 8
     flagged = 128 * 7 * 32 * 8 + 128 * 128 * 8   # single-pass apply: (value, epoch) words
-    need = factors + csr + vectors + restrictions + flagged
+    barrier_lines = 128 * 128                     # resident solve: one 128-byte line per leaf
+    need = factors + csr + vectors + restrictions + flagged + barrier_lines
     assert need <= nbytes <= need + (1 << 20)
     assert hp.hpcg_workspace_bytes(hp.partition(2048, batch=64), 851968) > 64 * hp.hpcg_workspace_bytes(
         hp.partition(2048), 13312) * 0.9
