@@ -97,15 +97,17 @@ typedef struct {
 /* Solve engines (hpcg_set_option(HPCG_OPT_ENGINE, ...)). */
 typedef enum {
     HPCG_ENGINE_AUTO = 0,       /* persistent (register-resident) when every leaf
-                                   of the batch gets a CU, else graph            */
+                                   of a system gets a CU, else graph             */
     HPCG_ENGINE_GRAPH = 1,      /* per-phase kernels, unrolled iterations replayed
                                    as one hipGraph, host polls a pinned flag      */
-    HPCG_ENGINE_PERSISTENT = 2  /* one launch runs the whole solve with
-                                   device-wide barriers between phases: one
-                                   512-thread workgroup per leaf with the factors
-                                   in VGPRs when B*K <= #CUs (two barriers per
-                                   iteration), else workgroups streaming the
-                                   factors (three barriers per iteration)        */
+    HPCG_ENGINE_PERSISTENT = 2  /* one launch runs the whole solve with barriers
+                                   between phases: one 512-thread workgroup per
+                                   leaf with the factors in VGPRs when K <= #CUs
+                                   (two barriers per iteration among a system's
+                                   workgroups; a batch with more leaves than CUs
+                                   runs in groups of whole systems, one launch
+                                   each), else workgroups streaming the factors
+                                   (three device-wide barriers per iteration)    */
 } hpcg_engine;
 
 typedef enum {
@@ -122,7 +124,10 @@ typedef enum {
                                    graph and streaming engines: 0 = automatic
                                    (default), else 1, 2, 4 or 8; a split whose LDS
                                    need exceeds a compute unit is raised to the
-                                   next that fits                                 */
+                                   next that fits.  A nonzero split also keeps
+                                   solves off the register-resident engine (one
+                                   workgroup per leaf): AUTO then runs the graph
+                                   engine, PERSISTENT the streaming one          */
 } hpcg_option;
 
 /* Which preconditioner the apply and the solve use (hpcg_set_option(

@@ -355,15 +355,19 @@ const void* resident_kernel(int levels, bool sq) {
 }
 
 // Register-resident persistent solve: one 512-thread workgroup per leaf, all
-// co-resident (one per CU).  Declines (ran = false) when the batch has more
-// leaves than the device has CUs.
+// of a launch co-resident (one per CU).  A batch with more leaves than that is
+// solved in groups of whole systems, one launch per group in stream order
+// (systems are independent, so a group needs nothing from another).  Declines
+// (ran = false) when one system alone has more leaves than the device has
+// CUs.
 template <typename T>
 hpcg_status run_resident(hpcg_ctx* h, bool& ran) {
   ran = false;
   const Geom G = h->G;
   const Bufs B = h->B;
-  const int items = G.B * G.K;
-  if (items > h->num_cu || B.form == FORM_JACOBI) return HPCG_OK;
+  // an explicit leaf split asks for the streaming engines (one workgroup per
+  // slot of a leaf); the resident engine always gives a leaf one workgroup
+  if (G.K > h->num_cu || B.form == FORM_JACOBI || h->split > 0) return HPCG_OK;
   const void* fn = resident_kernel<T>(G.levels, B.form == FORM_SQUARED);
   if (!fn) return HPCG_OK;
   const size_t dyn = ((size_t)h->max_leaf_nnz * 8 + (LEAF + 1) * 4 + 15) / 16 * 16 +
@@ -373,14 +377,20 @@ hpcg_status run_resident(hpcg_ctx* h, bool& ran) {
   if (s != HPCG_OK) return s;
   int per_cu = 0;
   HIP_OR_FAIL(h, hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NTR, dyn));
-  if ((int64_t)per_cu * h->num_cu < items) return HPCG_OK;
+  const int64_t cap = (int64_t)per_cu * h->num_cu;   // co-resident workgroups
+  if (cap < G.K) return HPCG_OK;
+  const int group = (int)std::min<int64_t>(G.B, cap / G.K);   // systems per launch
   hipLaunchKernelGGL(k_reset, dim3(1), dim3(64), 0, h->stream, B, 0, (int*)nullptr, G.B * G.K);
   Geom Ga = G;
   Bufs Ba = B;
   int mln = h->max_leaf_nnz;
-  void* args[] = {&Ga, &Ba, &mln};
-  HIP_OR_FAIL(h, hipLaunchKernel(fn, dim3(items), dim3(NTR), args, (unsigned)dyn, h->stream));
-  h->last_grid = items;
+  for (int s0 = 0; s0 < G.B; s0 += group) {
+    int first = s0;
+    void* args[] = {&Ga, &Ba, &mln, &first};
+    const int nsys = std::min(group, G.B - s0);
+    HIP_OR_FAIL(h, hipLaunchKernel(fn, dim3((unsigned)(nsys * G.K)), dim3(NTR), args, (unsigned)dyn, h->stream));
+  }
+  h->last_grid = group * G.K;
   h->last_lds = (int)dyn;
   ran = true;
   return HPCG_OK;
@@ -1014,13 +1024,15 @@ hpcg_status solve_core(hpcg_ctx* h, const float* d_b, double* d_x, double tol, i
   hpcg_status s = HPCG_OK;
   bool ran = false;
   const bool f32 = (h->prec == HPCG_PREC_VEC32);
-  // AUTO runs the register-resident persistent engine when every leaf of the
-  // batch gets its own CU (B*K <= #CUs): the factors then never leave VGPRs
-  // and an iteration costs two device-wide barriers.  Larger batches run the
-  // graph engine: a kernel boundary inside a graph (about 2 us) is cheaper
-  // than an agent-scope barrier over a full grid of streaming workgroups
-  // (about 10 us at 256 workgroups, dominated by the per-workgroup L2
-  // writeback and invalidate of the release/acquire fences).
+  // AUTO runs the register-resident persistent engine when every leaf of a
+  // system gets its own CU (K <= #CUs; a larger batch runs in groups of whole
+  // systems, one launch each): the factors then never leave VGPRs and an
+  // iteration costs two barriers among the system's workgroups.  Otherwise
+  // (and for the Jacobi form) the graph engine runs: a kernel boundary inside
+  // a graph (about 2 us) is cheaper than an agent-scope barrier over a full
+  // grid of streaming workgroups (about 10 us at 256 workgroups, dominated by
+  // the per-workgroup L2 writeback and invalidate of the release/acquire
+  // fences).
   if (h->engine_opt == HPCG_ENGINE_PERSISTENT || h->engine_opt == HPCG_ENGINE_AUTO) {
     s = f32 ? run_resident<float>(h, ran) : run_resident<double>(h, ran);
     if (s != HPCG_OK) return s;

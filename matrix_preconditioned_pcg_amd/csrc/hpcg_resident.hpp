@@ -49,12 +49,12 @@ namespace hpcg {
 // wave, a line per lane) until all of them hold it.  No read-modify-write is
 // on the path, so a barrier costs one store and one load after the last
 // arrival, and the systems of a batch synchronize independently.
-__device__ __forceinline__ void cgrid_arrive(const Bufs& B, unsigned& epoch) {
+__device__ __forceinline__ void cgrid_arrive(const Bufs& B, int item, unsigned& epoch) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   ++epoch;
-  if (threadIdx.x == 0) st_c(B.wgflag + (size_t)blockIdx.x * kFlagStride, epoch);
+  if (threadIdx.x == 0) st_c(B.wgflag + (size_t)item * kFlagStride, epoch);
 }
 
 __device__ __forceinline__ bool cgrid_wait(const Bufs& B, int s, int K, unsigned epoch) {
@@ -85,8 +85,8 @@ __device__ __forceinline__ bool cgrid_wait(const Bufs& B, int s, int K, unsigned
   return aborted_c != 0;
 }
 
-__device__ __forceinline__ bool cgrid_barrier(const Bufs& B, int s, int K, unsigned& epoch) {
-  cgrid_arrive(B, epoch);
+__device__ __forceinline__ bool cgrid_barrier(const Bufs& B, int item, int s, int K, unsigned& epoch) {
+  cgrid_arrive(B, item, epoch);
   return cgrid_wait(B, s, K, epoch);
 }
 
@@ -245,8 +245,10 @@ __device__ __forceinline__ void r_prolong(const Resident<T, LEV>& F, RSmem<T>& s
   __syncthreads();
 }
 
+// The grid covers systems s0 .. s0 + gridDim.x / K - 1 (a batch with more
+// leaves than CUs is solved in groups of whole systems, one launch each).
 template <typename T, int LEV, bool SQ>
-__global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_nnz) {
+__global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_nnz, int s0) {
   __shared__ RSmem<T> sm;
   extern __shared__ int4 rdyn4[];
   int* colL = reinterpret_cast<int*>(rdyn4);
@@ -256,7 +258,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
   T* stR = reinterpret_cast<T*>(rdyn4 + (2 * max_leaf_nnz + LEAF + 1 + 3) / 4);
   T* stQ = stR + (size_t)stage_rows * RANK;
   const int tid = threadIdx.x;
-  const int item = blockIdx.x;
+  const int item = s0 * G.K + blockIdx.x;
   const int s = item / G.K, k = item - s * G.K;
   const int leaf0 = s * G.n + k * LEAF;
   SysState* st = B.st + s;
@@ -295,7 +297,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
       __syncthreads();
       r_restrict<T, LEV>(G, s, k, F, sm.t, sm.tq, pW, sm.ownQ, sm, 0.0, nullptr, false);
     }
-    cgrid_arrive(B, epoch);
+    cgrid_arrive(B, item, epoch);
     if (active) leaf_apply<T, LEV>(F, sm.t, sm.tq, sm.yleaf, sm);
     if (cgrid_wait(B, s, G.K, epoch)) return false;
     if (active) {
@@ -336,7 +338,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
       set_state(st, ST_RUNNING, 0);
     }
   }
-  if (cgrid_barrier(B, s, G.K, epoch)) return;
+  if (cgrid_barrier(B, item, s, G.K, epoch)) return;
 
   // ---- z0 = M r0 ----
   bool done = false;                   // this system has finished (decided locally)
@@ -368,7 +370,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
       if (tid == 0) st_c(B.rz_part + item, part);
     }
   }
-  if (cgrid_barrier(B, s, G.K, epoch)) return;
+  if (cgrid_barrier(B, item, s, G.K, epoch)) return;
 
   // A system's status is written by its lead only in the second phase of an
   // iteration and read by the system's workgroups only in the first, so they
@@ -464,7 +466,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
         r_restrict<T, LEV>(G, s, k, F, sm.q, sm.tq, pQ, sm.ownQ, sm, loc, B.pq_part + item, false);
       }
     }
-    cgrid_arrive(B, epoch);
+    cgrid_arrive(B, item, epoch);
     // U_k U_k^T q is this workgroup's alone: it overlaps the wait
     if (!done) leaf_apply<T, LEV>(F, sm.q, sm.tq, sm.yq, sm);
     if (cgrid_wait(B, s, G.K, epoch)) return;
@@ -512,7 +514,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
     // Everything the next phase A reads (z, the partials, the statuses) is
     // written: arrive now.  The restriction of the new r is read by the
     // partners only after the following barrier, so it overlaps the wait.
-    cgrid_arrive(B, epoch);
+    cgrid_arrive(B, item, epoch);
     if (restrict_next) {
       // exact every kRefresh iterations, else by the same linear update the
       // partners used above (its rounding drift is bounded by the refreshes)

@@ -376,6 +376,26 @@ def test_launch_info(cfg):
     s.close()
 
 
+def test_resident_groups_of_systems(cfg):
+    # 64 systems of 16 leaves: more leaves than CUs, so AUTO runs the resident
+    # engine in launches of 16 whole systems; every group matches the graph
+    # engine's run of the same batch to the iteration tolerance
+    batch = cfg("batch64x2k")
+    _log("resident groups batch64")
+    s = _solver(batch)
+    res = s.solve(batch.b.reshape(-1), tol=batch.tol, maxit=batch.maxit)
+    assert s.last_engine == hpcg.HPCG_ENGINE_PERSISTENT
+    grid, _ = hpcg.hpcg_last_launch_info(s.handle)
+    assert grid == 256
+    s.set_option(hpcg.HPCG_OPT_ENGINE, hpcg.HPCG_ENGINE_GRAPH)
+    ref = s.solve(batch.b.reshape(-1), tol=batch.tol, maxit=batch.maxit)
+    assert res.status == ref.status == hpcg.HPCG_OK
+    for i in range(batch.batch):
+        assert abs(res.iterations[i] - ref.iterations[i]) <= ITER_TOL, (i, res.iterations[i], ref.iterations[i])
+        assert res.relres[i] <= batch.tol
+    s.close()
+
+
 def test_engines_agree(cfg, oracle_solves):
     # each engine is deterministic; the graph engine and the persistent engine
     # reduce in different orders, so they agree to the iteration tolerance
