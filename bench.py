@@ -162,6 +162,17 @@ def cpu_baseline(batch, budget_s=12.0):
                       f"{batch.n} unknowns)"}
 
 
+def single_pass_kernel(batch):
+    """Which single-pass apply kernel AUTO launches: two workgroups per leaf
+    (diagonal / off-diagonal roles) when the batch has at most a quarter as
+    many leaves as the device has CUs, else one per leaf."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if 4 * batch.batch * batch.K <= cus:
+        return f"M-apply (k_apply_split<{batch.levels}>: one launch, two workgroups per leaf, factors read once)"
+    return f"M-apply (k_apply_fused<{batch.levels}>: one launch, one workgroup per leaf, factors read once)"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -489,7 +500,7 @@ def main(argv=None):
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_record(args.config),
-            "kernel": ("M-apply (k_apply_fused: one launch, factors read once)" if main_out["apply_path"] == "fused"
+            "kernel": (single_pass_kernel(batch) if main_out["apply_path"] == "fused"
                        else "M-apply (k_apply_restrict + k_apply_prolong)")
                       + " + CSR SpMV (k_spmv), pairs graph-replayed back to back on the library stream",
             "algorithmic_bytes": ab + sb,
