@@ -189,6 +189,9 @@ def main(argv=None):
     ap.add_argument("--no-fused", action="store_true", help="skip the forced single-launch apply timing")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run three 256 MiB device-to-device copies (calibrates HBM byte counters)")
+    ap.add_argument("--solve-only", action="store_true",
+                    help="time only the solves of --config (nothing else runs: a kernel trace of this run "
+                         "holds exactly warmup + steps solves)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this solver path is built and measured on a single "
@@ -351,6 +354,13 @@ def main(argv=None):
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.solve_only:
+        batch, o = run_config(args.config, args.steps, args.warmup, False)
+        print(json.dumps({"config": args.config, "ms_per_solve": round(o["ms_per_solve"], 4),
+                          "solves": args.steps + args.warmup, "iterations": o["iterations"]
+                          if len(o["iterations"]) <= 4 else {"min": min(o["iterations"]), "max": max(o["iterations"])},
+                          "engine": o["engine"]}))
+        return 0
     batch, main_out = run_config(args.config, args.steps, args.warmup, True)
     ab, sb = main_out["apply_bytes"], main_out["spmv_bytes"]
     achieved = main_out["pair_gbs"]
