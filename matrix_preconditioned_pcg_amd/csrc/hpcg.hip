@@ -31,6 +31,8 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   size_t row_ptr, col, val, U, W, g, b, r, z, q, p0, p1, x, tleaf, pleaf, pq, rr, rz, st, ctl;
   size_t wgflag;              // resident engine: per-workgroup barrier lines
+  size_t lcol, hoff, hcol;    // resident engine: leaf-local CSR columns and halo lists
+  size_t zll, pll;            // resident engine: flagged z words and flagged partials
   size_t fr, fd, frhs, fsc;   // outer refinement: residual, correction, scaled rhs, per-system scalars
   size_t w, dinv, ftmp;       // squared form: H r; Jacobi: 1 / A_ii; apply scratch
   size_t llw, lle, lly;       // single-pass apply: flagged restriction words, per-leaf epochs,
@@ -127,6 +129,11 @@ Layout make_layout(const Geom& G, int64_t nnz) {
   L.st = take((size_t)G.B * sizeof(SysState));
   L.ctl = take(kCtlBytes);
   L.wgflag = take((size_t)G.B * G.K * kFlagStride * 4);
+  L.lcol = take((size_t)nnz * 4);
+  L.hoff = take(((size_t)G.B * G.K + 1) * 4);
+  L.hcol = take((size_t)nnz * 4);           // a leaf has at most as many halo columns as entries
+  L.zll = take(N * 16);
+  L.pll = take((size_t)G.B * G.K * 32);
   L.fr = take(N * 8);
   L.fd = take(N * 8);
   L.frhs = take(N * 4);
@@ -181,6 +188,8 @@ struct hpcg_ctx {
   int last_grid = 0;
   int last_lds = 0;
   int max_leaf_nnz = 0;
+  int max_halo = 0;        // most halo columns of a leaf (resident engine)
+  unsigned ep_next = 1;    // resident engine: epoch base of the next solve
   int* h_flag = nullptr;   // pinned, device-mapped (word 0: graph engine, word 16: block solve)
   int* d_flag = nullptr;
   // block solve: the recorded iterations and what they were recorded for
@@ -370,8 +379,11 @@ hpcg_status run_resident(hpcg_ctx* h, bool& ran) {
   if (G.K > h->num_cu || B.form == FORM_JACOBI || h->split > 0) return HPCG_OK;
   const void* fn = resident_kernel<T>(G.levels, B.form == FORM_SQUARED);
   if (!fn) return HPCG_OK;
+  // CSR rows, the partner stages of W^T r and W^T q, the halo's z and p and
+  // its column list
   const size_t dyn = ((size_t)h->max_leaf_nnz * 8 + (LEAF + 1) * 4 + 15) / 16 * 16 +
-                     2 * (size_t)std::max(G.K - 1, 1) * RANK * sizeof(T);
+                     2 * (size_t)std::max(G.K - 1, 1) * RANK * sizeof(T) +
+                     (size_t)h->max_halo * (2 * sizeof(T) + 4);
   if (dyn + sizeof(RSmem<T>) > kMaxLds) return HPCG_OK;
   hpcg_status s = allow_lds(h, fn, dyn);
   if (s != HPCG_OK) return s;
@@ -381,12 +393,23 @@ hpcg_status run_resident(hpcg_ctx* h, bool& ran) {
   if (cap < G.K) return HPCG_OK;
   const int group = (int)std::min<int64_t>(G.B, cap / G.K);   // systems per launch
   hipLaunchKernelGGL(k_reset, dim3(1), dim3(64), 0, h->stream, B, 0, (int*)nullptr, G.B * G.K);
+  // This solve's flagged words carry epochs ep_base + i, i = 0 .. maxit + 1:
+  // never one that an earlier solve left in the buffers.  Near the end of the
+  // 32-bit range the words are cleared and the count restarts.
+  const uint64_t span = (uint64_t)B.maxit + 4;
+  if ((uint64_t)h->ep_next + span >= 0xFFFFFFF0ull) {
+    HIP_OR_FAIL(h, hipMemsetAsync(h->ws + h->lay.zll, 0,
+                                  h->lay.pll + (size_t)G.B * G.K * 32 - h->lay.zll, h->stream));
+    h->ep_next = 1;
+  }
   Geom Ga = G;
   Bufs Ba = B;
-  int mln = h->max_leaf_nnz;
+  Ba.ep_base = h->ep_next;
+  h->ep_next += (unsigned)span;
+  int mln = h->max_leaf_nnz, mh = h->max_halo;
   for (int s0 = 0; s0 < G.B; s0 += group) {
     int first = s0;
-    void* args[] = {&Ga, &Ba, &mln, &first};
+    void* args[] = {&Ga, &Ba, &mln, &mh, &first};
     const int nsys = std::min(group, G.B - s0);
     HIP_OR_FAIL(h, hipLaunchKernel(fn, dim3((unsigned)(nsys * G.K)), dim3(NTR), args, (unsigned)dyn, h->stream));
   }
@@ -512,6 +535,12 @@ hpcg_status hpcg_create(const hpcg_partition* part, const int32_t* d_row_ptr, co
   B.itbase = reinterpret_cast<int*>(w + lay.ctl + kCtlItbase);
   B.replays = reinterpret_cast<int*>(w + lay.ctl + kCtlReplays);
   B.wgflag = reinterpret_cast<unsigned*>(w + lay.wgflag);
+  B.lcol = reinterpret_cast<const int*>(w + lay.lcol);
+  B.hoff = reinterpret_cast<const int*>(w + lay.hoff);
+  B.hcol = reinterpret_cast<const int*>(w + lay.hcol);
+  B.zll = reinterpret_cast<unsigned long long*>(w + lay.zll);
+  B.pll = reinterpret_cast<unsigned long long*>(w + lay.pll);
+  B.ep_base = 1u;
   B.llw = reinterpret_cast<unsigned long long*>(w + lay.llw);
   B.lle = reinterpret_cast<unsigned*>(w + lay.lle);
   B.lly = reinterpret_cast<unsigned long long*>(w + lay.lly);
@@ -546,9 +575,40 @@ hpcg_status hpcg_create(const hpcg_partition* part, const int32_t* d_row_ptr, co
   hipLaunchKernelGGL(k_diag_inv, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, h->stream, h->B.row_ptr, h->B.col,
                      h->B.val, reinterpret_cast<double*>(h->ws + h->lay.dinv), (int)N, G.n);
   CREATE_HIP(hipGetLastError());
-#undef CREATE_HIP
   for (size_t i0 = 0; i0 < N; i0 += LEAF)
     h->max_leaf_nnz = std::max(h->max_leaf_nnz, rp[i0 + LEAF] - rp[i0]);
+  {
+    // Resident engine: every CSR column as a leaf-local index (own rows 0 ..
+    // LEAF-1, other columns LEAF + their slot in the leaf's halo, the sorted
+    // distinct columns outside the leaf that its rows reference).
+    std::vector<int32_t> lcol((size_t)nnz_total), hoff((size_t)G.B * G.K + 1, 0), hcol;
+    std::vector<int32_t> halo;
+    for (size_t item = 0; item < (size_t)G.B * G.K; ++item) {
+      const int32_t lo = (int32_t)(item * LEAF), hi = lo + LEAF;
+      halo.clear();
+      for (int32_t e = rp[lo]; e < rp[hi]; ++e)
+        if (cols[e] < lo || cols[e] >= hi) halo.push_back(cols[e]);
+      std::sort(halo.begin(), halo.end());
+      halo.erase(std::unique(halo.begin(), halo.end()), halo.end());
+      hoff[item] = (int32_t)hcol.size();
+      hcol.insert(hcol.end(), halo.begin(), halo.end());
+      h->max_halo = std::max(h->max_halo, (int)halo.size());
+      for (int32_t e = rp[lo]; e < rp[hi]; ++e) {
+        const int32_t c = cols[e];
+        lcol[e] = (c >= lo && c < hi) ? c - lo
+                                      : LEAF + (int32_t)(std::lower_bound(halo.begin(), halo.end(), c) - halo.begin());
+      }
+    }
+    hoff.back() = (int32_t)hcol.size();
+    CREATE_HIP(hipMemcpyAsync(w + lay.hoff, hoff.data(), hoff.size() * 4, hipMemcpyHostToDevice, h->stream));
+    if (nnz_total > 0)
+      CREATE_HIP(hipMemcpyAsync(w + lay.lcol, lcol.data(), lcol.size() * 4, hipMemcpyHostToDevice, h->stream));
+    if (!hcol.empty())
+      CREATE_HIP(hipMemcpyAsync(w + lay.hcol, hcol.data(), hcol.size() * 4, hipMemcpyHostToDevice, h->stream));
+    CREATE_HIP(hipMemsetAsync(w + lay.zll, 0, lay.pll + (size_t)G.B * G.K * 32 - lay.zll, h->stream));
+    CREATE_HIP(hipStreamSynchronize(h->stream));   // the host vectors go out of scope
+  }
+#undef CREATE_HIP
   h->last_status.assign(G.B, HPCG_SYS_RUNNING);
   *out = h;
   return HPCG_OK;

@@ -113,6 +113,13 @@ struct Bufs {
   int* replays;        // graph engine: replays finished
   void* w;             // [B*n] H r in the squared form
   const double* dinv;  // [B*n] 1 / A_ii
+  const int* lcol;     // resident engine: [nnz] column as a leaf-local index: own rows
+                       // 0 .. LEAF-1, else LEAF + the column's slot in the leaf's halo
+  const int* hoff;     // resident engine: [B*K + 1] first halo slot of each leaf
+  const int* hcol;     // resident engine: [halo slots] global column of each slot
+  unsigned long long* zll;  // resident engine: [B*n][2] z as (word, epoch) pairs
+  unsigned long long* pll;  // resident engine: [B*K][4] r.r and r.z partials as (word, epoch) pairs
+  unsigned ep_base;    // resident engine: epoch of this solve's z0 (z of step i has ep_base + i)
   int form;            // FORM_*
   double tol;
   int maxit;

@@ -245,77 +245,173 @@ __device__ __forceinline__ void r_prolong(const Resident<T, LEV>& F, RSmem<T>& s
   __syncthreads();
 }
 
+// Flagged words: a 32-bit word of the value in the low half, the epoch in the
+// high half, stored and loaded whole (8-byte agent-scope atomics), so a reader
+// that sees the epoch it waits for holds that step's word.  An fp64 value is
+// two such words.
+__device__ __forceinline__ unsigned long long ll_word(unsigned v, unsigned e) {
+  return ((unsigned long long)e << 32) | v;
+}
+__device__ __forceinline__ bool ll_ready(unsigned long long w, unsigned e) { return (unsigned)(w >> 32) == e; }
+
+template <typename T>
+__device__ __forceinline__ void ll_put(unsigned long long* p, T v, unsigned e) {
+  if constexpr (sizeof(T) == 4) {
+    st_c(p, ll_word(__float_as_uint(v), e));
+  } else {
+    st_c(p, ll_word((unsigned)__double2loint(v), e));
+    st_c(p + 1, ll_word((unsigned)__double2hiint(v), e));
+  }
+}
+
+// Bound on the polls of one flagged word (each ~1 us): a writer that never
+// comes (an aborted workgroup) ends the wait with the abort flag.
+constexpr unsigned kLLPollMax = 1u << 22;
+
+// z of global row c (two words apart per row) once it carries epoch e.
+template <typename T>
+__device__ __forceinline__ T ll_get_z(const Bufs& B, int c, unsigned e, int& bad) {
+  const unsigned long long* p = B.zll + 2 * (size_t)c;
+  for (unsigned polls = 0;; ++polls) {
+    if constexpr (sizeof(T) == 4) {
+      const unsigned long long w = ld_c(p);
+      if (ll_ready(w, e)) return __uint_as_float((unsigned)w);
+    } else {
+      const unsigned long long w0 = ld_c(p), w1 = ld_c(p + 1);
+      if (ll_ready(w0, e) && ll_ready(w1, e)) return __hiloint2double((int)(unsigned)w1, (int)(unsigned)w0);
+    }
+    if (polls > kLLPollMax || ((polls & 1023u) == 1023u && ld_c(B.abort_flag))) {
+      st_c(B.abort_flag, 1);
+      bad = 1;
+      return T(0);
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// The system's K flagged r.r and r.z partials of epoch e, summed by one wave in
+// the fixed order of sum_partials_r (lane-strided, then the butterfly).
+__device__ __forceinline__ void ll_get_partials(const Bufs& B, int s, int K, unsigned e, double& rr, double& rz,
+                                                int& bad) {
+  const int lane = threadIdx.x & 63;
+  double a = 0.0, b = 0.0;
+  for (int j = lane; j < K; j += 64) {
+    const unsigned long long* p = B.pll + ((size_t)s * K + j) * 4;
+    for (unsigned polls = 0;; ++polls) {
+      const unsigned long long w0 = ld_c(p), w1 = ld_c(p + 1), w2 = ld_c(p + 2), w3 = ld_c(p + 3);
+      if (ll_ready(w0, e) && ll_ready(w1, e) && ll_ready(w2, e) && ll_ready(w3, e)) {
+        a += __hiloint2double((int)(unsigned)w1, (int)(unsigned)w0);
+        b += __hiloint2double((int)(unsigned)w3, (int)(unsigned)w2);
+        break;
+      }
+      if (polls > kLLPollMax || ((polls & 1023u) == 1023u && ld_c(B.abort_flag))) {
+        st_c(B.abort_flag, 1);
+        bad = 1;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  rr = wave_sum(a);
+  rz = wave_sum(b);
+}
+
 // The grid covers systems s0 .. s0 + gridDim.x / K - 1 (a batch with more
 // leaves than CUs is solved in groups of whole systems, one launch each).
+//
+// The end of an iteration has no barrier: the next phase A needs only the
+// neighbours' new z and the partials r.r and r.z, and those travel as flagged
+// words that the readers poll directly.  Every workgroup of a system computes
+// the same sums in the same order, so they all take the same convergence
+// decision and leave the loop at the same step.  What a workgroup may still
+// read while a faster one runs ahead into the next phase A (W^T q and the p.q
+// partials of phase BC) is double-buffered by the step's parity.
 template <typename T, int LEV, bool SQ>
-__global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_nnz, int s0) {
+__global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_nnz, int max_halo, int s0) {
   __shared__ RSmem<T> sm;
   extern __shared__ int4 rdyn4[];
-  int* colL = reinterpret_cast<int*>(rdyn4);
+  int* colL = reinterpret_cast<int*>(rdyn4);              // leaf-local columns (own, then halo)
   float* valL = reinterpret_cast<float*>(colL + max_leaf_nnz);
   int* rpL = reinterpret_cast<int*>(valL + max_leaf_nnz);
   const int stage_rows = G.K > 1 ? G.K - 1 : 1;
   T* stR = reinterpret_cast<T*>(rdyn4 + (2 * max_leaf_nnz + LEAF + 1 + 3) / 4);
   T* stQ = stR + (size_t)stage_rows * RANK;
+  T* hz = stQ + (size_t)stage_rows * RANK;                // halo z of the previous step
+  T* hp = hz + max_halo;                                  // halo p of the previous step
+  int* hcolL = reinterpret_cast<int*>(hp + max_halo);     // halo global columns
   const int tid = threadIdx.x;
   const int item = s0 * G.K + blockIdx.x;
   const int s = item / G.K, k = item - s * G.K;
   const int leaf0 = s * G.n + k * LEAF;
   SysState* st = B.st + s;
   const bool lead = (tid == 0 && k == 0);
-  // restriction buffers: W^T r in two halves of pleaf (ping-pong), W^T q in tleaf
+  // restriction buffers: W^T r in two halves of pleaf (ping-pong at refreshes),
+  // W^T q in two quarters of tleaf (by step parity), W^T w in a third
   const size_t half = (size_t)G.B * G.levels * G.K * RANK;
   T* pR[2] = {reinterpret_cast<T*>(B.pleaf), reinterpret_cast<T*>(B.pleaf) + half};
-  T* pQ = reinterpret_cast<T*>(B.tleaf);
-  T* pW = pQ + half;                   // squared form: W^T w of w = H r
+  T* pQ[2] = {reinterpret_cast<T*>(B.tleaf), reinterpret_cast<T*>(B.tleaf) + half};
+  T* pW = reinterpret_cast<T*>(B.tleaf) + 2 * half;   // squared form: W^T w of w = H r
+  const size_t BK = (size_t)G.B * G.K;                  // p.q partials: two halves of pq_part
   int rbuf = 0;
 
-  // ---- factors into registers, CSR rows into LDS ----
+  // ---- factors into registers, CSR rows and the halo list into LDS ----
   Resident<T, LEV> F;
   load_factors(G, B, s, k, F);
   const int e_begin = B.row_ptr[leaf0];
   if (tid <= LEAF) rpL[tid] = B.row_ptr[leaf0 + tid] - e_begin;
   const int leaf_nnz = B.row_ptr[leaf0 + LEAF] - e_begin;
   for (int e = tid; e < leaf_nnz; e += NTR) {
-    colL[e] = B.col[e_begin + e];
+    colL[e] = B.lcol[e_begin + e];
     valL[e] = B.val[e_begin + e];
   }
+  const int h0 = B.hoff[item], nh = B.hoff[item + 1] - h0;
+  for (int h = tid; h < nh; h += NTR) hcolL[h] = B.hcol[h0 + h];
   const float gate = (tid < LEAF) ? B.g[leaf0 + tid] : 0.f;
   double x = 0.0;                      // x of row tid (tid < LEAF)
-  T* zg = reinterpret_cast<T*>(B.z);
-  unsigned epoch = 0;
+  unsigned epoch = 0;                  // barriers passed
 
   // Squared form M = H H: with w = H r in sm.z, z = H w into sm.z.  The
-  // slabs' restriction of w is new data, so it costs one more device-wide
-  // exchange; U_k U_k^T w overlaps its wait.  Every workgroup calls this (it
-  // holds a barrier); inactive ones only pass the barrier.  sm.P (the partner
+  // slabs' restriction of w is new data, so it costs one more exchange among
+  // the system's workgroups; U_k U_k^T w overlaps its wait.  sm.P (the partner
   // sums of W^T r, carried to the next iteration) is kept aside meanwhile.
-  auto squared = [&](bool active) -> bool {
+  auto squared = [&]() -> bool {
     if constexpr (!SQ) return true;
-    if (active) {
-      if (tid < LEAF) sm.t[tid] = sm.z[tid];
-      __syncthreads();
-      r_restrict<T, LEV>(G, s, k, F, sm.t, sm.tq, pW, sm.ownQ, sm, 0.0, nullptr, false);
-    }
+    if (tid < LEAF) sm.t[tid] = sm.z[tid];
+    __syncthreads();
+    r_restrict<T, LEV>(G, s, k, F, sm.t, sm.tq, pW, sm.ownQ, sm, 0.0, nullptr, false);
     cgrid_arrive(B, item, epoch);
-    if (active) leaf_apply<T, LEV>(F, sm.t, sm.tq, sm.yleaf, sm);
+    leaf_apply<T, LEV>(F, sm.t, sm.tq, sm.yleaf, sm);
     if (cgrid_wait(B, s, G.K, epoch)) return false;
-    if (active) {
-      if constexpr (LEV > 0) {
-        r_stage_partners<T, LEV>(G, pW, s, k, stR);
-        if (tid < LEV * RANK) sm.ownR[tid] = sm.P[tid];
-      }
-      lds_dma_wait();
-      if constexpr (LEV > 0) prolong_strips<T, LEV>(sm, stR, (const T*)nullptr, 0.0, false);
-      prolong_offdiag<T, LEV>(F, sm);
-      __syncthreads();
-      if (tid < LEAF) sm.z[tid] = sm.yleaf[tid] + sm.yoff[tid] + (T)gate * sm.t[tid];
-      if constexpr (LEV > 0) {
-        if (tid < LEV * RANK) sm.P[tid] = sm.ownR[tid];
-      }
-      __syncthreads();
+    if constexpr (LEV > 0) {
+      r_stage_partners<T, LEV>(G, pW, s, k, stR);
+      if (tid < LEV * RANK) sm.ownR[tid] = sm.P[tid];
     }
+    lds_dma_wait();
+    if constexpr (LEV > 0) prolong_strips<T, LEV>(sm, stR, (const T*)nullptr, 0.0, false);
+    prolong_offdiag<T, LEV>(F, sm);
+    __syncthreads();
+    if (tid < LEAF) sm.z[tid] = sm.yleaf[tid] + sm.yoff[tid] + (T)gate * sm.t[tid];
+    if constexpr (LEV > 0) {
+      if (tid < LEV * RANK) sm.P[tid] = sm.ownR[tid];
+    }
+    __syncthreads();
     return true;
+  };
+
+  // z (sm.z) and the partials r.r (given) and r.z of step i as flagged words
+  // of epoch ep_base + i: everything the next phase A reads from this leaf.
+  auto publish = [&](double loc_rr, int i) {
+    const unsigned e = B.ep_base + (unsigned)i;
+    double loc_rz = 0.0;
+    if (tid < LEAF) {
+      ll_put<T>(B.zll + 2 * (size_t)(leaf0 + tid), sm.z[tid], e);
+      loc_rz = (double)sm.r[tid] * (double)sm.z[tid];
+    }
+    wg_sum2_r<kFresh<T, LEV>>(loc_rr, loc_rz, sm);
+    if (tid == 0) {
+      ll_put<double>(B.pll + (size_t)item * 4, loc_rr, e);
+      ll_put<double>(B.pll + (size_t)item * 4 + 2, loc_rz, e);
+    }
   };
 
   // ---- r = b, its restriction (t_r, W^T r), ||b||^2 ----
@@ -328,9 +424,9 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
   __syncthreads();
   r_restrict<T, LEV>(G, s, k, F, sm.r, sm.tr, pR[0], sm.ownR, sm);
   diag_times<T, LEV>(F, sm.tr, sm.yr);       // U_k U_k^T r0 (read in the first phase BC)
-  double part = wg_sum_r<kFresh<T, LEV>>(loc, sm);
+  const double part_bb = wg_sum_r<kFresh<T, LEV>>(loc, sm);
   if (tid == 0) {
-    st_c(B.rr_part + item, part);
+    st_c(B.rr_part + item, part_bb);
     if (k == 0) {
       st->relres = 1.0;
       st->brk = 0;
@@ -340,196 +436,146 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
   }
   if (cgrid_barrier(B, item, s, G.K, epoch)) return;
 
-  // ---- z0 = M r0 ----
-  bool done = false;                   // this system has finished (decided locally)
+  // ---- z0 = M r0, published with r.z0 (no barrier: phase A polls for them) ----
   double bnorm = 1.0, rz_old = 1.0;
   {
     if constexpr (LEV > 0) r_stage_partners<T, LEV>(G, pR[0], s, k, stR);
     const double rr = sum_partials_r(B.rr_part, s, G.K);
     lds_dma_wait();
     bnorm = sqrt(rr);
-    if (rr == 0.0) {
-      done = true;
+    if (rr == 0.0) {                   // b = 0: x = 0 at step 0 (every workgroup sees rr = 0)
       if (lead) { st->bnorm = 0.0; st->relres = 0.0; set_state(st, ST_CONVERGED, 0); }
-    } else {
-      if (lead) st->bnorm = bnorm;
-      if (tid < LEAF) sm.t[tid] = sm.tr[tid];
-      __syncthreads();
-      r_prolong<T, LEV>(F, sm, stR, (const T*)nullptr, 0.0, gate);
+      if (tid < LEAF) B.x[leaf0 + tid] = 0.0;
+      return;
     }
+    if (lead) st->bnorm = bnorm;
+    if (tid < LEAF) sm.t[tid] = sm.tr[tid];
+    __syncthreads();
+    r_prolong<T, LEV>(F, sm, stR, (const T*)nullptr, 0.0, gate);
     if constexpr (SQ) {
-      if (!squared(!done)) return;
+      if (!squared()) return;
     }
-    if (!done) {
-      loc = 0.0;
-      if (tid < LEAF) {
-        st_c(zg + leaf0 + tid, sm.z[tid]);
-        loc = (double)sm.r[tid] * (double)sm.z[tid];
-      }
-      part = wg_sum_r<kFresh<T, LEV>>(loc, sm);
-      if (tid == 0) st_c(B.rz_part + item, part);
-    }
+    publish(loc, 0);
   }
-  if (cgrid_barrier(B, item, s, G.K, epoch)) return;
 
-  // A system's status is written by its lead only in the second phase of an
-  // iteration and read by the system's workgroups only in the first, so they
-  // all see the same value and leave the loop together (a finished system's
-  // workgroups leave while other systems of the batch continue).
-  int pend_status = ST_RUNNING, pend_iters = 0;
   double pend_rel = 0.0;
-  bool restrict_next = false;
-  double next_alpha = 0.0;
-  // the end of phase BC: z for the neighbours' SpMV, the partials r.r and r.z
-  auto finish_bc = [&](double alpha, double loc_rr) {
-    double loc_rz = 0.0;
-    if (tid < LEAF) {
-      st_c(zg + leaf0 + tid, sm.z[tid]);
-      loc_rz = (double)sm.r[tid] * (double)sm.z[tid];
-    }
-    wg_sum2_r<kFresh<T, LEV>>(loc_rr, loc_rz, sm);
-    if (tid == 0) {
-      st_c(B.rr_part + item, loc_rr);
-      st_c(B.rz_part + item, loc_rz);
-    }
-    next_alpha = alpha;
-    restrict_next = true;
-  };
   for (int it = 1; it <= B.maxit + 2; ++it) {
+    const unsigned ez = B.ep_base + (unsigned)(it - 1);   // epoch of z and the partials of step it-1
     // ---------------- phase A (it) ----------------
     {
-      // the SpMV's first gathers go out together with the scalar loads
       const T* pold = reinterpret_cast<const T*>((it & 1) ? B.p0 : B.p1);
       T* pnew = reinterpret_cast<T*>((it & 1) ? B.p1 : B.p0);
       const bool first = (it == 1);
+      // the halo's z (flagged words) and p (plain: written before the last
+      // barrier) into LDS; wave 0 also collects the partials r.r and r.z
+      int bad = 0;
+      for (int h = tid; h < nh; h += NTR) {
+        const int c = hcolL[h];
+        const T pv = first ? T(0) : ld_c(pold + c);
+        hz[h] = ll_get_z<T>(B, c, ez, bad);
+        hp[h] = pv;
+      }
+      if (tid < 64) {
+        double rr, rz;
+        ll_get_partials(B, s, G.K, ez, rr, rz, bad);
+        if (tid == 0) {
+          sm.dsc[1] = rr;
+          sm.dsc[2] = rz;
+        }
+      }
+      if (__syncthreads_or(bad)) return;   // a bounded poll ran out: the abort flag is set
+      const double rr = sm.dsc[1], rz = sm.dsc[2];
+      int fin = ST_RUNNING, fin_it = 0;
+      if (it >= 2) {
+        const double rel = sqrt(rr) / bnorm;
+        pend_rel = rel;
+        if (rel <= B.tol) { fin = ST_CONVERGED; fin_it = it - 1; }
+        else if (it - 1 >= B.maxit) { fin = ST_NOT_CONVERGED; fin_it = B.maxit; }
+      }
+      if (fin == ST_RUNNING && (!(rz > 0.0) || !isfinite(rz))) { fin = ST_BREAKDOWN; fin_it = it - 1; }
+      if (fin != ST_RUNNING) {
+        if (lead) {
+          st->relres = pend_rel;
+          set_state(st, fin, fin_it);
+        }
+        break;
+      }
+      const double beta = first ? 0.0 : rz / rz_old;
+      rz_old = rz;
+      // SpMV: 4 threads per row, CSR rows from LDS, own columns from sm.z / sm.p,
+      // halo columns from hz / hp; p = z + beta p formed on the fly
       const int row = tid >> 2, lr = tid & 3;
       const int e0 = rpL[row], e1 = rpL[row + 1];
-      constexpr int PF = 2;
-      T zc[PF], pc[PF];
-      float vv[PF];
-#pragma unroll
-      for (int u = 0; u < PF; ++u) {
-        const int e = e0 + lr + 4 * u;
-        zc[u] = 0;
-        pc[u] = 0;
-        vv[u] = 0.f;
-        if (e < e1) {
-          const int c = colL[e];
-          vv[u] = valL[e];
-          zc[u] = ld_c(zg + c);
-          if (!first) pc[u] = ld_c(pold + c);
-        }
+      T acc = 0;
+      for (int e = e0 + lr; e < e1; e += 4) {
+        const int c = colL[e];
+        T v;
+        if (c < LEAF) v = first ? sm.z[c] : pdir<T>(sm.z[c], sm.p[c], beta);
+        else v = first ? hz[c - LEAF] : pdir<T>(hz[c - LEAF], hp[c - LEAF], beta);
+        acc = fma((T)valL[e], v, acc);
       }
-      const int running =
-          __hip_atomic_load(&st->status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ST_RUNNING;
-      const double rr = sum_partials_r(B.rr_part, s, G.K);
-      const double rz = sum_partials_r(B.rz_part, s, G.K);
-      if (!__syncthreads_or(running)) break;
-      if (!done && it >= 2) {
-        const double rel = sqrt(rr) / bnorm;
-        if (rel <= B.tol) {
-          done = true; pend_status = ST_CONVERGED; pend_iters = it - 1; pend_rel = rel;
-        } else if (it - 1 >= B.maxit) {
-          done = true; pend_status = ST_NOT_CONVERGED; pend_iters = B.maxit; pend_rel = rel;
-        } else {
-          pend_rel = rel;
-        }
+      acc = group4_sum(acc);
+      T pn = 0;
+      loc = 0.0;
+      if (lr == 0) {
+        pn = first ? sm.z[row] : pdir<T>(sm.z[row], sm.p[row], beta);
+        sm.q[row] = acc;
+        st_c(pnew + leaf0 + row, pn);
+        loc = (double)pn * (double)acc;
       }
-      if (!done && (!(rz > 0.0) || !isfinite(rz))) {
-        done = true; pend_status = ST_BREAKDOWN; pend_iters = it - 1;
-      }
-      if (!done) {
-        const double beta = first ? 0.0 : rz / rz_old;
-        rz_old = rz;
-        sm.dsc[0] = rz;
-        // SpMV: 4 threads per row, CSR rows from LDS, z and p gathered globally
-        T acc = 0;
-#pragma unroll
-        for (int u = 0; u < PF; ++u) acc = fma((T)vv[u], first ? zc[u] : pdir<T>(zc[u], pc[u], beta), acc);
-        for (int e = e0 + lr + 4 * PF; e < e1; e += 4) {
-          const int c = colL[e];
-          const T v = first ? ld_c(zg + c) : pdir<T>(ld_c(zg + c), ld_c(pold + c), beta);
-          acc = fma((T)valL[e], v, acc);
-        }
-        acc = group4_sum(acc);
-        loc = 0.0;
-        if (lr == 0) {
-          const T pn = first ? sm.z[row] : pdir<T>(sm.z[row], sm.p[row], beta);
-          sm.p[row] = pn;
-          sm.q[row] = acc;
-          st_c(pnew + leaf0 + row, pn);
-          loc = (double)pn * (double)acc;
-        }
-        __syncthreads();
-        // the slab restriction of q (what the partners read) also sums and
-        // stores the partial p.q
-        r_restrict<T, LEV>(G, s, k, F, sm.q, sm.tq, pQ, sm.ownQ, sm, loc, B.pq_part + item, false);
-      }
+      __syncthreads();                  // every SpMV read of sm.p is done
+      if (lr == 0) sm.p[row] = pn;
+      // the slab restriction of q (what the partners read) also sums and
+      // stores the partial p.q
+      r_restrict<T, LEV>(G, s, k, F, sm.q, sm.tq, pQ[it & 1], sm.ownQ, sm, loc, B.pq_part + (it & 1) * BK + item,
+                         false);
     }
     cgrid_arrive(B, item, epoch);
     // U_k U_k^T q is this workgroup's alone: it overlaps the wait
-    if (!done) leaf_apply<T, LEV>(F, sm.q, sm.tq, sm.yq, sm);
+    leaf_apply<T, LEV>(F, sm.q, sm.tq, sm.yq, sm);
     if (cgrid_wait(B, s, G.K, epoch)) return;
     // ---------------- phase BC (it) ----------------
+    double alpha = 0.0;
     {
-      if (lead && pend_status != ST_RUNNING) {
-        st->relres = pend_rel;
-        set_state(st, pend_status, pend_iters);
-        pend_status = ST_RUNNING;   // written once
-      }
       // The partner sums of W^T r are staged only after an exact refresh (and
       // for the initial r); otherwise they are the previous P (linearity).
       const bool r_from_prev = (it - 1) % kRefresh<T> != 0;
-      bool stepped = false;
-      double alpha = 0.0, loc_rr = 0.0;
-      if (!done) {
-        if constexpr (LEV > 0) {
-          if (!r_from_prev) r_stage_partners<T, LEV>(G, pR[rbuf], s, k, stR);
-          r_stage_partners<T, LEV>(G, pQ, s, k, stQ);
-        }
-        const double pq = sum_partials_r(B.pq_part, s, G.K);
-        lds_dma_wait();
-        if (!(pq > 0.0) || !isfinite(pq)) {
-          done = true;
-          if (lead) set_state(st, ST_BREAKDOWN, it);
-        } else {
-          alpha = rz_old / pq;
-          if (tid < LEAF) {
-            const T rn = (T)((double)sm.r[tid] - alpha * (double)sm.q[tid]);
-            sm.r[tid] = rn;
-            x += alpha * (double)sm.p[tid];
-            loc_rr = (double)rn * (double)rn;
-          }
-          // (r_prolong_split synchronizes before it reads sm.r)
-          r_prolong_split<T, LEV>(F, sm, stR, stQ, alpha, gate, r_from_prev);
-          stepped = true;
-          if constexpr (!SQ) finish_bc(alpha, loc_rr);
-        }
+      if constexpr (LEV > 0) {
+        if (!r_from_prev) r_stage_partners<T, LEV>(G, pR[rbuf], s, k, stR);
+        r_stage_partners<T, LEV>(G, pQ[it & 1], s, k, stQ);
       }
+      const double pq = sum_partials_r(B.pq_part + (it & 1) * BK, s, G.K);
+      lds_dma_wait();
+      if (!(pq > 0.0) || !isfinite(pq)) {   // every workgroup of the system sees the same pq
+        if (lead) set_state(st, ST_BREAKDOWN, it);
+        break;
+      }
+      alpha = rz_old / pq;
+      double loc_rr = 0.0;
+      if (tid < LEAF) {
+        const T rn = (T)((double)sm.r[tid] - alpha * (double)sm.q[tid]);
+        sm.r[tid] = rn;
+        x += alpha * (double)sm.p[tid];
+        loc_rr = (double)rn * (double)rn;
+      }
+      // (r_prolong_split synchronizes before it reads sm.r)
+      r_prolong_split<T, LEV>(F, sm, stR, stQ, alpha, gate, r_from_prev);
       if constexpr (SQ) {
-        if (!squared(stepped)) return;
-        if (stepped) finish_bc(alpha, loc_rr);
+        if (!squared()) return;
       }
+      publish(loc_rr, it);
     }
-    // Everything the next phase A reads (z, the partials, the statuses) is
-    // written: arrive now.  The restriction of the new r is read by the
-    // partners only after the following barrier, so it overlaps the wait.
-    cgrid_arrive(B, item, epoch);
-    if (restrict_next) {
-      // exact every kRefresh iterations, else by the same linear update the
-      // partners used above (its rounding drift is bounded by the refreshes)
-      restrict_next = false;
-      if (it % kRefresh<T> == 0) {
-        // exact W^T r for the partners' next phase BC (into the other buffer:
-        // slow partners may still be staging the previous one) and U U^T r
-        rbuf ^= 1;
-        r_restrict<T, LEV>(G, s, k, F, sm.r, sm.tr, pR[rbuf], sm.ownR, sm);
-        diag_times<T, LEV>(F, sm.tr, sm.yr);
-      } else {
-        if (tid < LEAF) sm.yr[tid] = (T)((double)sm.yr[tid] - next_alpha * (double)sm.yq[tid]);
-      }
+    // exact restriction every kRefresh steps, else the same linear update the
+    // partners use (its rounding drift is bounded by the refreshes)
+    if (it % kRefresh<T> == 0) {
+      // exact W^T r for the partners' next phase BC (into the other buffer:
+      // slow partners may still be staging the previous one) and U U^T r
+      rbuf ^= 1;
+      r_restrict<T, LEV>(G, s, k, F, sm.r, sm.tr, pR[rbuf], sm.ownR, sm);
+      diag_times<T, LEV>(F, sm.tr, sm.yr);
+    } else {
+      if (tid < LEAF) sm.yr[tid] = (T)((double)sm.yr[tid] - alpha * (double)sm.yq[tid]);
     }
-    if (cgrid_wait(B, s, G.K, epoch)) return;
   }
   // ---- the solution of the leaf's rows ----
   if (tid < LEAF) B.x[leaf0 + tid] = x;

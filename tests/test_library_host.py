@@ -63,7 +63,10 @@ def test_workspace_bytes_covers_the_buffers(hp):
     restrictions = 128 * (8 * 128 + 2 * 7 * 32) * 8
     flagged = 128 * 7 * 32 * 8 + 128 * 128 * 8   # single-pass apply: (value, epoch) words
     barrier_lines = 128 * 128                     # resident solve: one 128-byte line per leaf
-    need = factors + csr + vectors + restrictions + flagged + barrier_lines
+    # resident solve: leaf-local CSR columns, halo lists (at most one slot per
+    # entry), z as two flagged words per row, four flagged partials per leaf
+    resident = 2 * nnz * 4 + 129 * 4 + 16384 * 16 + 128 * 32
+    need = factors + csr + vectors + restrictions + flagged + barrier_lines + resident
     assert need <= nbytes <= need + (1 << 20)
     assert hp.hpcg_workspace_bytes(hp.partition(2048, batch=64), 851968) > 64 * hp.hpcg_workspace_bytes(
         hp.partition(2048), 13312) * 0.9
