@@ -33,6 +33,7 @@ struct Layout {
   size_t wgflag;              // resident engine: per-workgroup barrier lines
   size_t lcol, hoff, hcol;    // resident engine: leaf-local CSR columns and halo lists
   size_t zll, pll;            // resident engine: flagged z words and flagged partials
+  size_t qll, pqll;           // resident engine: flagged W^T q words and p.q partials
   size_t fr, fd, frhs, fsc;   // outer refinement: residual, correction, scaled rhs, per-system scalars
   size_t w, dinv, ftmp;       // squared form: H r; Jacobi: 1 / A_ii; apply scratch
   size_t llw, lle, lly;       // single-pass apply: flagged restriction words, per-leaf epochs,
@@ -134,6 +135,8 @@ Layout make_layout(const Geom& G, int64_t nnz) {
   L.hcol = take((size_t)nnz * 4);           // a leaf has at most as many halo columns as entries
   L.zll = take(N * 16);
   L.pll = take((size_t)G.B * G.K * 32);
+  L.qll = take(2 * (size_t)G.B * G.levels * G.K * RANK * 8 + 16);
+  L.pqll = take(2 * (size_t)G.B * G.K * 16);
   L.fr = take(N * 8);
   L.fd = take(N * 8);
   L.frhs = take(N * 4);
@@ -399,9 +402,12 @@ hpcg_status run_resident(hpcg_ctx* h, bool& ran) {
   const uint64_t span = (uint64_t)B.maxit + 4;
   if ((uint64_t)h->ep_next + span >= 0xFFFFFFF0ull) {
     HIP_OR_FAIL(h, hipMemsetAsync(h->ws + h->lay.zll, 0,
-                                  h->lay.pll + (size_t)G.B * G.K * 32 - h->lay.zll, h->stream));
+                                  h->lay.pqll + 2 * (size_t)G.B * G.K * 16 - h->lay.zll, h->stream));
     h->ep_next = 1;
   }
+  // the fp64 W^T q words carry only an 8-bit step tag: cleared every solve
+  if (G.levels > 0)
+    HIP_OR_FAIL(h, hipMemsetAsync(h->ws + h->lay.qll, 0, 2 * (size_t)G.B * G.levels * G.K * RANK * 8, h->stream));
   Geom Ga = G;
   Bufs Ba = B;
   Ba.ep_base = h->ep_next;
@@ -540,6 +546,8 @@ hpcg_status hpcg_create(const hpcg_partition* part, const int32_t* d_row_ptr, co
   B.hcol = reinterpret_cast<const int*>(w + lay.hcol);
   B.zll = reinterpret_cast<unsigned long long*>(w + lay.zll);
   B.pll = reinterpret_cast<unsigned long long*>(w + lay.pll);
+  B.qll = reinterpret_cast<unsigned long long*>(w + lay.qll);
+  B.pqll = reinterpret_cast<unsigned long long*>(w + lay.pqll);
   B.ep_base = 1u;
   B.llw = reinterpret_cast<unsigned long long*>(w + lay.llw);
   B.lle = reinterpret_cast<unsigned*>(w + lay.lle);
@@ -605,7 +613,7 @@ hpcg_status hpcg_create(const hpcg_partition* part, const int32_t* d_row_ptr, co
       CREATE_HIP(hipMemcpyAsync(w + lay.lcol, lcol.data(), lcol.size() * 4, hipMemcpyHostToDevice, h->stream));
     if (!hcol.empty())
       CREATE_HIP(hipMemcpyAsync(w + lay.hcol, hcol.data(), hcol.size() * 4, hipMemcpyHostToDevice, h->stream));
-    CREATE_HIP(hipMemsetAsync(w + lay.zll, 0, lay.pll + (size_t)G.B * G.K * 32 - lay.zll, h->stream));
+    CREATE_HIP(hipMemsetAsync(w + lay.zll, 0, lay.pqll + 2 * (size_t)G.B * G.K * 16 - lay.zll, h->stream));
     CREATE_HIP(hipStreamSynchronize(h->stream));   // the host vectors go out of scope
   }
 #undef CREATE_HIP

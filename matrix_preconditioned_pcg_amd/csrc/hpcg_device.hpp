@@ -119,6 +119,8 @@ struct Bufs {
   const int* hcol;     // resident engine: [halo slots] global column of each slot
   unsigned long long* zll;  // resident engine: [B*n][2] z as (word, epoch) pairs
   unsigned long long* pll;  // resident engine: [B*K][4] r.r and r.z partials as (word, epoch) pairs
+  unsigned long long* qll;  // resident engine: [2][B][levels][K][RANK] W^T q words by step parity
+  unsigned long long* pqll; // resident engine: [2][B*K][2] p.q partials as (word, epoch) pairs by step parity
   unsigned ep_base;    // resident engine: epoch of this solve's z0 (z of step i has ep_base + i)
   int form;            // FORM_*
   double tol;

@@ -316,16 +316,148 @@ __device__ __forceinline__ void ll_get_partials(const Bufs& B, int s, int K, uns
   rz = wave_sum(b);
 }
 
+// A restriction value of W^T q as one flagged word.  fp32: the value's bits
+// and the 32-bit epoch.  fp64: the value with its eight lowest mantissa bits
+// replaced by an 8-bit step tag (1 .. 255, never 0 = cleared); the 44 bits
+// left keep it within 2^-44 relative, far inside the fp32 factors' rounding.
+// The tag is unambiguous because the words are cleared at every solve and a
+// buffer (one per step parity) is rewritten only two steps later.
+template <typename T>
+__device__ __forceinline__ unsigned long long q_word(T v, unsigned tag, unsigned e) {
+  if constexpr (sizeof(T) == 4) return ll_word(__float_as_uint(v), e);
+  else return ((unsigned long long)__double_as_longlong(v) & ~0xFFull) | tag;
+}
+template <typename T>
+__device__ __forceinline__ bool q_ready(unsigned long long w, unsigned tag, unsigned e) {
+  if constexpr (sizeof(T) == 4) return ll_ready(w, e);
+  else return (unsigned)(w & 0xFFull) == tag;
+}
+template <typename T>
+__device__ __forceinline__ T q_value(unsigned long long w) {
+  if constexpr (sizeof(T) == 4) return __uint_as_float((unsigned)w);
+  else return __longlong_as_double((long long)(w & ~0xFFull));
+}
+__device__ __forceinline__ unsigned q_tag(int it) { return 1u + (unsigned)(it % 255); }
+
+// Restriction of q for the partners, published as flagged words: W_l[k]^T q
+// of step it into qll (parity par) and the workgroup's partial p.q (`loc`
+// summed over the threads) into pqll.
+template <typename T, int LEV>
+__device__ __forceinline__ void r_restrict_q_ll(const Geom& G, const Bufs& B, int s, int k, int item,
+                                                const Resident<T, LEV>& F, RSmem<T>& sm, double loc, int par,
+                                                unsigned tag, unsigned e) {
+  const int tid = tid_of<kFresh<T, LEV>>(), lane = tid & 63, wave = tid >> 6;
+  loc = wave_sum(loc);
+  if (lane == 0) sm.dred[wave] = loc;
+  restrict_w_partials<T, LEV>(F, sm.q, sm);
+  __syncthreads();
+  if (tid == 0) {
+    double p = sm.dred[0];
+#pragma unroll
+    for (int w = 1; w < NWR; ++w) p += sm.dred[w];
+    ll_put<double>(B.pqll + ((size_t)par * G.B * G.K + item) * 2, p, e);
+  }
+  if constexpr (LEV > 0) {
+    if (tid < LEV * RANK) {
+      T a = sm.redW[0][tid];
+#pragma unroll
+      for (int w = 1; w < NWR; ++w) a += sm.redW[w][tid];
+      const int l = tid / RANK, c = tid - l * RANK;
+      const size_t half = (size_t)G.B * G.levels * G.K * RANK;
+      st_c(B.qll + par * half + (((size_t)s * G.levels + l) * G.K + k) * RANK + c, q_word<T>(a, tag, e));
+    }
+  }
+  __syncthreads();
+}
+
+// The partner halves' W^T q of step it (every level; level l at stage row
+// 2^l - 1, its i-th leaf at row 2^l - 1 + i) polled from their flagged words
+// into `stage` by the first NST threads (the last wave polls the p.q partials
+// meanwhile).  Every word is loaded at once and the late ones re-polled
+// together, so a late partner costs one round trip, not one per word.
+constexpr int NST = NTR - 64;
+template <typename T, int LEV>
+__device__ __forceinline__ void ll_stage_q(const Geom& G, const Bufs& B, int s, int k, int par, unsigned tag,
+                                           unsigned e, T* stage, int& bad) {
+  if constexpr (LEV > 0) {
+    constexpr int NWORDS = RANK * ((1 << LEV) - 1);
+    constexpr int WPT = (NWORDS + NST - 1) / NST;
+    static_assert(WPT <= 32, "poll mask");
+    const int tid = tid_of<kFresh<T, LEV>>();
+    const unsigned long long* base =
+        B.qll + (size_t)par * G.B * G.levels * G.K * RANK + (size_t)s * G.levels * G.K * RANK;
+    int off[WPT];
+    unsigned long long v[WPT];
+    unsigned pending = 0;
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+      const int w = tid + j * NST;
+      off[j] = 0;
+      if (w < NWORDS) {
+        const int row = w / RANK, c = w - row * RANK;
+        const int l = 31 - __clz(row + 1);
+        const int kp = (((k >> l) ^ 1) << l) + (row + 1 - (1 << l));
+        off[j] = (l * G.K + kp) * RANK + c;
+        v[j] = ld_c(base + off[j]);
+        pending |= 1u << j;
+      }
+    }
+    for (unsigned polls = 0;; ++polls) {
+#pragma unroll
+      for (int j = 0; j < WPT; ++j)
+        if ((pending & (1u << j)) && q_ready<T>(v[j], tag, e)) {
+          stage[tid + j * NST] = q_value<T>(v[j]);
+          pending &= ~(1u << j);
+        }
+      if (!pending) break;
+      if (polls > kLLPollMax || ((polls & 1023u) == 1023u && ld_c(B.abort_flag))) {
+        st_c(B.abort_flag, 1);
+        bad = 1;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+      for (int j = 0; j < WPT; ++j)
+        if (pending & (1u << j)) v[j] = ld_c(base + off[j]);
+    }
+  }
+}
+
+// The system's K flagged p.q partials of epoch e (parity par), summed by one
+// wave in the fixed order of sum_partials_r.
+__device__ __forceinline__ double ll_get_pq(const Bufs& B, int s, int K, size_t BK, int par, unsigned e, int& bad) {
+  const int lane = threadIdx.x & 63;
+  double a = 0.0;
+  for (int j = lane; j < K; j += 64) {
+    const unsigned long long* p = B.pqll + ((size_t)par * BK + (size_t)s * K + j) * 2;
+    for (unsigned polls = 0;; ++polls) {
+      const unsigned long long w0 = ld_c(p), w1 = ld_c(p + 1);
+      if (ll_ready(w0, e) && ll_ready(w1, e)) {
+        a += __hiloint2double((int)(unsigned)w1, (int)(unsigned)w0);
+        break;
+      }
+      if (polls > kLLPollMax || ((polls & 1023u) == 1023u && ld_c(B.abort_flag))) {
+        st_c(B.abort_flag, 1);
+        bad = 1;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  return wave_sum(a);
+}
+
 // The grid covers systems s0 .. s0 + gridDim.x / K - 1 (a batch with more
 // leaves than CUs is solved in groups of whole systems, one launch each).
 //
-// The end of an iteration has no barrier: the next phase A needs only the
-// neighbours' new z and the partials r.r and r.z, and those travel as flagged
-// words that the readers poll directly.  Every workgroup of a system computes
-// the same sums in the same order, so they all take the same convergence
-// decision and leave the loop at the same step.  What a workgroup may still
-// read while a faster one runs ahead into the next phase A (W^T q and the p.q
-// partials of phase BC) is double-buffered by the step's parity.
+// An iteration has no barrier.  Phase A needs only the neighbours' new z and
+// the partials r.r and r.z, phase BC only the partners' W^T q and the partials
+// p.q (and, after a refresh, W^T r): all of it travels as flagged words that
+// the readers poll directly.  A workgroup can run at most one phase ahead of
+// the slowest of its system (each phase needs every workgroup's partial of the
+// previous one), so the phase A outputs are double-buffered by step parity.
+// Every workgroup of a system computes the same sums in the same order, so
+// they all take the same convergence decision and leave the loop together.
 template <typename T, int LEV, bool SQ>
 __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_nnz, int max_halo, int s0) {
   __shared__ RSmem<T> sm;
@@ -345,13 +477,12 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
   const int leaf0 = s * G.n + k * LEAF;
   SysState* st = B.st + s;
   const bool lead = (tid == 0 && k == 0);
-  // restriction buffers: W^T r in two halves of pleaf (ping-pong at refreshes),
-  // W^T q in two quarters of tleaf (by step parity), W^T w in a third
+  // W^T r in two halves of pleaf (ping-pong at refreshes); W^T q and the p.q
+  // partials are flagged words (qll, pqll) by step parity
   const size_t half = (size_t)G.B * G.levels * G.K * RANK;
   T* pR[2] = {reinterpret_cast<T*>(B.pleaf), reinterpret_cast<T*>(B.pleaf) + half};
-  T* pQ[2] = {reinterpret_cast<T*>(B.tleaf), reinterpret_cast<T*>(B.tleaf) + half};
-  T* pW = reinterpret_cast<T*>(B.tleaf) + 2 * half;   // squared form: W^T w of w = H r
-  const size_t BK = (size_t)G.B * G.K;                  // p.q partials: two halves of pq_part
+  T* pW = reinterpret_cast<T*>(B.tleaf);   // squared form: W^T w of w = H r
+  const size_t BK = (size_t)G.B * G.K;
   int rbuf = 0;
 
   // ---- factors into registers, CSR rows and the halo list into LDS ----
@@ -402,6 +533,9 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
   // of epoch ep_base + i: everything the next phase A reads from this leaf.
   auto publish = [&](double loc_rr, int i) {
     const unsigned e = B.ep_base + (unsigned)i;
+    // this workgroup's earlier stores (p of phase A, W^T r of a refresh) are
+    // acknowledged first: whoever sees these words sees those values too
+    __builtin_amdgcn_s_waitcnt(0);
     double loc_rz = 0.0;
     if (tid < LEAF) {
       ll_put<T>(B.zll + 2 * (size_t)(leaf0 + tid), sm.z[tid], e);
@@ -525,15 +659,13 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
       }
       __syncthreads();                  // every SpMV read of sm.p is done
       if (lr == 0) sm.p[row] = pn;
-      // the slab restriction of q (what the partners read) also sums and
-      // stores the partial p.q
-      r_restrict<T, LEV>(G, s, k, F, sm.q, sm.tq, pQ[it & 1], sm.ownQ, sm, loc, B.pq_part + (it & 1) * BK + item,
-                         false);
+      // the slab restriction of q and the partial p.q, published as flagged
+      // words (what the partners read)
+      r_restrict_q_ll<T, LEV>(G, B, s, k, item, F, sm, loc, it & 1, q_tag(it), B.ep_base + (unsigned)it);
     }
-    cgrid_arrive(B, item, epoch);
-    // U_k U_k^T q is this workgroup's alone: it overlaps the wait
+    // U_k U_k^T q is this workgroup's alone: it overlaps the partners' words
+    // in flight
     leaf_apply<T, LEV>(F, sm.q, sm.tq, sm.yq, sm);
-    if (cgrid_wait(B, s, G.K, epoch)) return;
     // ---------------- phase BC (it) ----------------
     double alpha = 0.0;
     {
@@ -542,10 +674,17 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
       const bool r_from_prev = (it - 1) % kRefresh<T> != 0;
       if constexpr (LEV > 0) {
         if (!r_from_prev) r_stage_partners<T, LEV>(G, pR[rbuf], s, k, stR);
-        r_stage_partners<T, LEV>(G, pQ[it & 1], s, k, stQ);
       }
-      const double pq = sum_partials_r(B.pq_part + (it & 1) * BK, s, G.K);
-      lds_dma_wait();
+      int bad = 0;
+      if (tid < NST) {
+        ll_stage_q<T, LEV>(G, B, s, k, it & 1, q_tag(it), B.ep_base + (unsigned)it, stQ, bad);
+      } else {
+        const double pqs = ll_get_pq(B, s, G.K, BK, it & 1, B.ep_base + (unsigned)it, bad);
+        if (tid == NST) sm.dsc[3] = pqs;
+      }
+      __builtin_amdgcn_s_waitcnt(0);    // the W^T r stage has landed
+      if (__syncthreads_or(bad)) return;
+      const double pq = sm.dsc[3];
       if (!(pq > 0.0) || !isfinite(pq)) {   // every workgroup of the system sees the same pq
         if (lead) set_state(st, ST_BREAKDOWN, it);
         break;
@@ -563,18 +702,20 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
       if constexpr (SQ) {
         if (!squared()) return;
       }
+      // exact restriction every kRefresh steps, before z is published (the
+      // partners' next phase BC reads it once they hold this step's words);
+      // else the same linear update the partners use (its rounding drift is
+      // bounded by the refreshes)
+      const bool refresh = (it % kRefresh<T> == 0);
+      if (refresh) {
+        // exact W^T r (into the other buffer: slow partners may still be
+        // staging the previous one) and U U^T r
+        rbuf ^= 1;
+        r_restrict<T, LEV>(G, s, k, F, sm.r, sm.tr, pR[rbuf], sm.ownR, sm);
+        diag_times<T, LEV>(F, sm.tr, sm.yr);
+      }
       publish(loc_rr, it);
-    }
-    // exact restriction every kRefresh steps, else the same linear update the
-    // partners use (its rounding drift is bounded by the refreshes)
-    if (it % kRefresh<T> == 0) {
-      // exact W^T r for the partners' next phase BC (into the other buffer:
-      // slow partners may still be staging the previous one) and U U^T r
-      rbuf ^= 1;
-      r_restrict<T, LEV>(G, s, k, F, sm.r, sm.tr, pR[rbuf], sm.ownR, sm);
-      diag_times<T, LEV>(F, sm.tr, sm.yr);
-    } else {
-      if (tid < LEAF) sm.yr[tid] = (T)((double)sm.yr[tid] - alpha * (double)sm.yq[tid]);
+      if (!refresh && tid < LEAF) sm.yr[tid] = (T)((double)sm.yr[tid] - alpha * (double)sm.yq[tid]);
     }
   }
   // ---- the solution of the leaf's rows ----

@@ -66,6 +66,8 @@ def test_workspace_bytes_covers_the_buffers(hp):
     # resident solve: leaf-local CSR columns, halo lists (at most one slot per
     # entry), z as two flagged words per row, four flagged partials per leaf
     resident = 2 * nnz * 4 + 129 * 4 + 16384 * 16 + 128 * 32
+    # resident solve: W^T q and p.q as flagged words, two step parities
+    resident += 2 * 7 * 128 * 32 * 8 + 2 * 128 * 16
     need = factors + csr + vectors + restrictions + flagged + barrier_lines + resident
     assert need <= nbytes <= need + (1 << 20)
     assert hp.hpcg_workspace_bytes(hp.partition(2048, batch=64), 851968) > 64 * hp.hpcg_workspace_bytes(
