@@ -268,24 +268,27 @@ __device__ __forceinline__ void ll_put(unsigned long long* p, T v, unsigned e) {
 // comes (an aborted workgroup) ends the wait with the abort flag.
 constexpr unsigned kLLPollMax = 1u << 22;
 
-// z of global row c (two words apart per row) once it carries epoch e.
+// z of global row c (two words apart per row) once it carries epoch e.  The
+// polls are pipelined two deep: the next load is in flight while the previous
+// one is checked, so a word that lands is seen about half a round trip later.
 template <typename T>
 __device__ __forceinline__ T ll_get_z(const Bufs& B, int c, unsigned e, int& bad) {
   const unsigned long long* p = B.zll + 2 * (size_t)c;
+  unsigned long long a0 = ld_c(p), a1 = (sizeof(T) == 8) ? ld_c(p + 1) : 0ull;
   for (unsigned polls = 0;; ++polls) {
+    const unsigned long long b0 = ld_c(p), b1 = (sizeof(T) == 8) ? ld_c(p + 1) : 0ull;
     if constexpr (sizeof(T) == 4) {
-      const unsigned long long w = ld_c(p);
-      if (ll_ready(w, e)) return __uint_as_float((unsigned)w);
+      if (ll_ready(a0, e)) return __uint_as_float((unsigned)a0);
     } else {
-      const unsigned long long w0 = ld_c(p), w1 = ld_c(p + 1);
-      if (ll_ready(w0, e) && ll_ready(w1, e)) return __hiloint2double((int)(unsigned)w1, (int)(unsigned)w0);
+      if (ll_ready(a0, e) && ll_ready(a1, e)) return __hiloint2double((int)(unsigned)a1, (int)(unsigned)a0);
     }
     if (polls > kLLPollMax || ((polls & 1023u) == 1023u && ld_c(B.abort_flag))) {
       st_c(B.abort_flag, 1);
       bad = 1;
       return T(0);
     }
-    __builtin_amdgcn_s_sleep(1);
+    a0 = b0;
+    a1 = b1;
   }
 }
 
@@ -297,8 +300,10 @@ __device__ __forceinline__ void ll_get_partials(const Bufs& B, int s, int K, uns
   double a = 0.0, b = 0.0;
   for (int j = lane; j < K; j += 64) {
     const unsigned long long* p = B.pll + ((size_t)s * K + j) * 4;
+    // pipelined two deep, as in ll_get_z
+    unsigned long long w0 = ld_c(p), w1 = ld_c(p + 1), w2 = ld_c(p + 2), w3 = ld_c(p + 3);
     for (unsigned polls = 0;; ++polls) {
-      const unsigned long long w0 = ld_c(p), w1 = ld_c(p + 1), w2 = ld_c(p + 2), w3 = ld_c(p + 3);
+      const unsigned long long n0 = ld_c(p), n1 = ld_c(p + 1), n2 = ld_c(p + 2), n3 = ld_c(p + 3);
       if (ll_ready(w0, e) && ll_ready(w1, e) && ll_ready(w2, e) && ll_ready(w3, e)) {
         a += __hiloint2double((int)(unsigned)w1, (int)(unsigned)w0);
         b += __hiloint2double((int)(unsigned)w3, (int)(unsigned)w2);
@@ -309,7 +314,7 @@ __device__ __forceinline__ void ll_get_partials(const Bufs& B, int s, int K, uns
         bad = 1;
         break;
       }
-      __builtin_amdgcn_s_sleep(1);
+      w0 = n0; w1 = n1; w2 = n2; w3 = n3;
     }
   }
   rr = wave_sum(a);
@@ -430,8 +435,10 @@ __device__ __forceinline__ double ll_get_pq(const Bufs& B, int s, int K, size_t 
   double a = 0.0;
   for (int j = lane; j < K; j += 64) {
     const unsigned long long* p = B.pqll + ((size_t)par * BK + (size_t)s * K + j) * 2;
+    // pipelined two deep, as in ll_get_z
+    unsigned long long w0 = ld_c(p), w1 = ld_c(p + 1);
     for (unsigned polls = 0;; ++polls) {
-      const unsigned long long w0 = ld_c(p), w1 = ld_c(p + 1);
+      const unsigned long long n0 = ld_c(p), n1 = ld_c(p + 1);
       if (ll_ready(w0, e) && ll_ready(w1, e)) {
         a += __hiloint2double((int)(unsigned)w1, (int)(unsigned)w0);
         break;
@@ -441,7 +448,8 @@ __device__ __forceinline__ double ll_get_pq(const Bufs& B, int s, int K, size_t 
         bad = 1;
         break;
       }
-      __builtin_amdgcn_s_sleep(1);
+      w0 = n0;
+      w1 = n1;
     }
   }
   return wave_sum(a);
