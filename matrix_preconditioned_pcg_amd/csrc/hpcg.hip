@@ -382,11 +382,11 @@ hpcg_status run_resident(hpcg_ctx* h, bool& ran) {
   if (G.K > h->num_cu || B.form == FORM_JACOBI || h->split > 0) return HPCG_OK;
   const void* fn = resident_kernel<T>(G.levels, B.form == FORM_SQUARED);
   if (!fn) return HPCG_OK;
-  // CSR rows, the partner stages of W^T r and W^T q, the halo's z and p and
-  // its column list
+  // CSR rows, the partner stages of W^T r and W^T q, z and p by leaf-local
+  // column (own rows, then the halo), the halo's column list
   const size_t dyn = ((size_t)h->max_leaf_nnz * 8 + (LEAF + 1) * 4 + 15) / 16 * 16 +
                      2 * (size_t)std::max(G.K - 1, 1) * RANK * sizeof(T) +
-                     (size_t)h->max_halo * (2 * sizeof(T) + 4);
+                     2 * ((size_t)LEAF + h->max_halo) * sizeof(T) + (size_t)h->max_halo * 4;
   if (dyn + sizeof(RSmem<T>) > kMaxLds) return HPCG_OK;
   hpcg_status s = allow_lds(h, fn, dyn);
   if (s != HPCG_OK) return s;

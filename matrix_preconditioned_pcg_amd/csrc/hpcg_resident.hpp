@@ -476,9 +476,10 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
   const int stage_rows = G.K > 1 ? G.K - 1 : 1;
   T* stR = reinterpret_cast<T*>(rdyn4 + (2 * max_leaf_nnz + LEAF + 1 + 3) / 4);
   T* stQ = stR + (size_t)stage_rows * RANK;
-  T* hz = stQ + (size_t)stage_rows * RANK;                // halo z of the previous step
-  T* hp = hz + max_halo;                                  // halo p of the previous step
-  int* hcolL = reinterpret_cast<int*>(hp + max_halo);     // halo global columns
+  // z and p of the previous step by leaf-local column: own rows, then the halo
+  T* zc = stQ + (size_t)stage_rows * RANK;
+  T* pc = zc + LEAF + max_halo;
+  int* hcolL = reinterpret_cast<int*>(pc + LEAF + max_halo);   // halo global columns
   const int tid = threadIdx.x;
   const int item = s0 * G.K + blockIdx.x;
   const int s = item / G.K, k = item - s * G.K;
@@ -614,8 +615,12 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
       for (int h = tid; h < nh; h += NTR) {
         const int c = hcolL[h];
         const T pv = first ? T(0) : ld_c(pold + c);
-        hz[h] = ll_get_z<T>(B, c, ez, bad);
-        hp[h] = pv;
+        zc[LEAF + h] = ll_get_z<T>(B, c, ez, bad);
+        pc[LEAF + h] = pv;
+      }
+      if (tid < LEAF) {
+        zc[tid] = sm.z[tid];
+        pc[tid] = sm.p[tid];
       }
       if (tid < 64) {
         double rr, rz;
@@ -651,10 +656,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
       T acc = 0;
       for (int e = e0 + lr; e < e1; e += 4) {
         const int c = colL[e];
-        T v;
-        if (c < LEAF) v = first ? sm.z[c] : pdir<T>(sm.z[c], sm.p[c], beta);
-        else v = first ? hz[c - LEAF] : pdir<T>(hz[c - LEAF], hp[c - LEAF], beta);
-        acc = fma((T)valL[e], v, acc);
+        acc = fma((T)valL[e], first ? zc[c] : pdir<T>(zc[c], pc[c], beta), acc);
       }
       acc = group4_sum(acc);
       T pn = 0;
