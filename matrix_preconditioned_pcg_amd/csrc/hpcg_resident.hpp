@@ -11,31 +11,33 @@
 //     the per-leaf restrictions W_l[k]^T r_k and W_l[k]^T q_k, and the scalar
 //     partials.
 //
-// Two barriers per iteration, each among the workgroups of one system.  The
+// No barrier inside an iteration.  Each value one workgroup needs from another
+// travels as a flagged word (the value's bits and the step it belongs to,
+// stored and loaded whole) that the reader polls directly, so a value costs
+// one trip through the coherence point instead of a barrier plus a load.  The
 // restriction is linear, so W^T r_new = W^T r - alpha W^T q: phase A, which
-// owns the whole leaf's q, restricts q right after the SpMV, and the next
-// phase forms the partner-half sums of (W^T r - alpha W^T q) and applies M to
-// r_new without another barrier.  Every kRefresh iterations W^T r is
-// recomputed exactly from r_new (into the other of two buffers) and its
-// partner sums are staged afresh; in between they are carried forward by the
-// same linear update, so rounding drift never accumulates past a refresh.
-//   A(it):  convergence test on ||r_{it-1}||; beta; p = z + beta p;
-//           q = A p; W_l[k]^T q; partial p.q; then, during the barrier,
-//           U_k U_k^T q
-//   BC(it): alpha; x += alpha p; r -= alpha q; partial r.r;
-//           z = U_k U_k^T r_new + sum_l W_l[k] P_l + g r_new with
-//           P_l = partner-half sum of (W^T r - alpha W^T q);  partial r.z;
-//           then, during the barrier, U_k U_k^T r_new (and at a refresh
-//           W_l[k]^T r_new)
+// owns the whole leaf's q, restricts q right after the SpMV, and phase BC forms
+// the partner-half sums of (W^T r - alpha W^T q) and applies M to r_new.
+// Every kRefresh iterations W^T r is recomputed exactly from r_new (into the
+// other of two buffers) and its partner sums are staged afresh; in between
+// they are carried forward by the same linear update.
+//   A(it):  poll the halo's z and the system's r.r, r.z partials of step it-1;
+//           convergence test on ||r_{it-1}||; beta; p = z + beta p;
+//           q = A p (CSR rows, z and p in LDS); publish W_l[k]^T q and the
+//           partial p.q; then U_k U_k^T q while those words travel
+//   BC(it): poll the partners' W^T q and the p.q partials; alpha;
+//           x += alpha p; r -= alpha q; z = U_k U_k^T r_new + sum_l W_l[k] P_l
+//           + g r_new with P_l = partner-half sum of (W^T r - alpha W^T q);
+//           at a refresh W^T r_new and U_k U_k^T r_new; publish z and the
+//           partials r.r and r.z
 // Per iteration the factors are never reloaded.
 //
 // Coherence without cache maintenance.  Every value one workgroup writes for
-// another (z and p, the restrictions, the scalar partials, the statuses, the
-// barrier lines) is stored and loaded with agent-scope accesses (sc1: written
-// through to, and read from, the point where all XCDs agree), so the barrier
-// needs no L2 write-back or invalidation: arriving waits until this
-// workgroup's stores are acknowledged, then stores its barrier count on its
-// own line, which the system's other workgroups poll.
+// another is stored and loaded with agent-scope accesses (sc1: written through
+// to, and read from, the point where all XCDs agree), so no L2 write-back or
+// invalidation is needed; a value written plainly (p, a refreshed W^T r) is
+// acknowledged before the flagged words that announce it are stored.  The
+// per-system barrier below remains for the set-up and the squared form.
 #pragma once
 #include "hpcg_kernels.hpp"
 #include "hpcg_leaf.hpp"
