@@ -569,6 +569,26 @@ def test_deterministic(cfg):
     s.close()
 
 
+def test_flagged_word_epochs_wrap(cfg):
+    # the resident engine's flagged words carry a per-solve epoch base that
+    # advances by maxit + 4 per solve; with maxit near 2^30 it wraps the
+    # 32-bit range within four solves (the words are then cleared and the
+    # count restarts).  Every solve before, at and after the wrap, and solves
+    # with a small budget in between, must match the first one bit for bit.
+    batch = cfg("N1k")
+    _log("flagged-word epoch wrap N1k")
+    s = _solver(batch)
+    ref = s.solve(batch.b.reshape(-1), tol=batch.tol, maxit=batch.maxit)
+    assert s.last_engine == hpcg.HPCG_ENGINE_PERSISTENT
+    for i in range(6):
+        res = s.solve(batch.b.reshape(-1), tol=batch.tol, maxit=(1 << 30) - 7)
+        assert res.status == hpcg.HPCG_OK and res.iterations == ref.iterations, (i, res.iterations)
+        assert torch.equal(res.x, ref.x), i
+        short = s.solve(batch.b.reshape(-1), tol=batch.tol, maxit=7)
+        assert short.status == hpcg.HPCG_ERR_NOT_CONVERGED and short.iterations == [7]
+    s.close()
+
+
 def test_set_values_refreshes_matrix(cfg):
     batch = cfg("N1k")
     _log("set_values")
