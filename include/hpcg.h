@@ -139,11 +139,11 @@ typedef enum {
  *           section 2, "SPD by construction"); two applications of H per
  *           iteration;
  *  JACOBI   M = diag(A)^-1, the fallback those pages name; needs no factors.
- * SQUARED solves run on the register-resident engine where it fits (one more
- * device-wide exchange per iteration, for the restriction of w = H r), else
- * on the graph engine; JACOBI solves run on the graph engine (the persistent
- * engines return HPCG_ERR_SHAPE for it).  The block apply and the block solve
- * run DIRECT only (HPCG_ERR_STATE otherwise). */
+ * SQUARED and JACOBI solves run on the register-resident engine where it fits
+ * (SQUARED with one more exchange per iteration, for the restriction of
+ * w = H r), else on the graph engine (the streaming persistent engine returns
+ * HPCG_ERR_SHAPE for them).  The block apply and the block solve run DIRECT
+ * only (HPCG_ERR_STATE otherwise). */
 typedef enum {
     HPCG_FORM_DIRECT = 0,
     HPCG_FORM_SQUARED = 1,

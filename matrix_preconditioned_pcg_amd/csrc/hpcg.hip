@@ -354,11 +354,13 @@ hpcg_status run_graph(hpcg_ctx* h) {
 }
 
 template <typename T>
-const void* resident_kernel(int levels, bool sq) {
+const void* resident_kernel(int levels, int form) {
+  if (form == FORM_JACOBI) return reinterpret_cast<const void*>(&k_resident<T, 0, FM_JACOBI>);
+  const bool sq = (form == FORM_SQUARED);
   switch (levels * 2 + (sq ? 1 : 0)) {
-#define HPCG_RESIDENT(LV)                                                          \
-    case 2 * LV: return reinterpret_cast<const void*>(&k_resident<T, LV, false>); \
-    case 2 * LV + 1: return reinterpret_cast<const void*>(&k_resident<T, LV, true>);
+#define HPCG_RESIDENT(LV)                                                              \
+    case 2 * LV: return reinterpret_cast<const void*>(&k_resident<T, LV, FM_DIRECT>); \
+    case 2 * LV + 1: return reinterpret_cast<const void*>(&k_resident<T, LV, FM_SQUARED>);
     HPCG_RESIDENT(0) HPCG_RESIDENT(1) HPCG_RESIDENT(2) HPCG_RESIDENT(3) HPCG_RESIDENT(4)
     HPCG_RESIDENT(5) HPCG_RESIDENT(6) HPCG_RESIDENT(7) HPCG_RESIDENT(8)
 #undef HPCG_RESIDENT
@@ -379,8 +381,8 @@ hpcg_status run_resident(hpcg_ctx* h, bool& ran) {
   const Bufs B = h->B;
   // an explicit leaf split asks for the streaming engines (one workgroup per
   // slot of a leaf); the resident engine always gives a leaf one workgroup
-  if (G.K > h->num_cu || B.form == FORM_JACOBI || h->split > 0) return HPCG_OK;
-  const void* fn = resident_kernel<T>(G.levels, B.form == FORM_SQUARED);
+  if (G.K > h->num_cu || h->split > 0) return HPCG_OK;
+  const void* fn = resident_kernel<T>(G.levels, B.form);
   if (!fn) return HPCG_OK;
   // CSR rows, the partner stages of W^T r and W^T q, z and p by leaf-local
   // column (own rows, then the halo), the halo's column list
@@ -1109,7 +1111,7 @@ hpcg_status solve_core(hpcg_ctx* h, const float* d_b, double* d_x, double tol, i
     if (s != HPCG_OK) return s;
     if (!ran && h->engine_opt == HPCG_ENGINE_PERSISTENT)
       return fail(h, HPCG_ERR_SHAPE, h->B.form != FORM_DIRECT
-                                         ? "persistent engines run the direct (and, register-resident, the squared) form only"
+                                         ? "the streaming persistent engine runs the direct form only"
                                          : "persistent engine: device does not support a co-resident grid for this partition");
     if (ran) h->last_engine = HPCG_ENGINE_PERSISTENT;
   }
@@ -1152,7 +1154,7 @@ hpcg_status hpcg_solve(hpcg_handle h, const float* d_b, double* d_x, double tol,
     for (int i = 0; i < h->G.B; ++i) broke |= (h->h_st[i].status == ST_BREAKDOWN);
     if (broke) {
       // the preconditioner is not SPD for some system: solve again with Jacobi
-      // (the persistent engines run the direct form only)
+      // (the streaming persistent engine runs the direct form only)
       const int form = h->B.form, engine = h->engine_opt;
       h->B.form = FORM_JACOBI;
       if (engine == HPCG_ENGINE_PERSISTENT) h->engine_opt = HPCG_ENGINE_AUTO;

@@ -468,8 +468,14 @@ __device__ __forceinline__ double ll_get_pq(const Bufs& B, int s, int K, size_t 
 // previous one), so the phase A outputs are double-buffered by step parity.
 // Every workgroup of a system computes the same sums in the same order, so
 // they all take the same convergence decision and leave the loop together.
-template <typename T, int LEV, bool SQ>
+// FM selects the preconditioner form: FM_DIRECT (M = H), FM_SQUARED (M = H H)
+// or FM_JACOBI (M = diag(A)^-1: no factors, no restrictions, only the SpMV
+// halo and the partials cross workgroups; instantiated with LEV = 0).
+constexpr int FM_DIRECT = 0, FM_SQUARED = 1, FM_JACOBI = 2;
+template <typename T, int LEV, int FM>
 __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_nnz, int max_halo, int s0) {
+  constexpr bool SQ = (FM == FM_SQUARED), JAC = (FM == FM_JACOBI);
+  static_assert(!JAC || LEV == 0, "the Jacobi form has no levels");
   __shared__ RSmem<T> sm;
   extern __shared__ int4 rdyn4[];
   int* colL = reinterpret_cast<int*>(rdyn4);              // leaf-local columns (own, then halo)
@@ -498,7 +504,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
 
   // ---- factors into registers, CSR rows and the halo list into LDS ----
   Resident<T, LEV> F;
-  load_factors(G, B, s, k, F);
+  if constexpr (!JAC) load_factors(G, B, s, k, F);
   const int e_begin = B.row_ptr[leaf0];
   if (tid <= LEAF) rpL[tid] = B.row_ptr[leaf0 + tid] - e_begin;
   const int leaf_nnz = B.row_ptr[leaf0 + LEAF] - e_begin;
@@ -508,7 +514,8 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
   }
   const int h0 = B.hoff[item], nh = B.hoff[item + 1] - h0;
   for (int h = tid; h < nh; h += NTR) hcolL[h] = B.hcol[h0 + h];
-  const float gate = (tid < LEAF) ? B.g[leaf0 + tid] : 0.f;
+  const float gate = (!JAC && tid < LEAF) ? B.g[leaf0 + tid] : 0.f;
+  const double dinv = (JAC && tid < LEAF) ? B.dinv[leaf0 + tid] : 0.0;   // Jacobi: 1 / A_ii
   double x = 0.0;                      // x of row tid (tid < LEAF)
   unsigned epoch = 0;                  // barriers passed
 
@@ -567,8 +574,10 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
     loc = (double)bv * (double)bv;
   }
   __syncthreads();
-  r_restrict<T, LEV>(G, s, k, F, sm.r, sm.tr, pR[0], sm.ownR, sm);
-  diag_times<T, LEV>(F, sm.tr, sm.yr);       // U_k U_k^T r0 (read in the first phase BC)
+  if constexpr (!JAC) {
+    r_restrict<T, LEV>(G, s, k, F, sm.r, sm.tr, pR[0], sm.ownR, sm);
+    diag_times<T, LEV>(F, sm.tr, sm.yr);     // U_k U_k^T r0 (read in the first phase BC)
+  }
   const double part_bb = wg_sum_r<kFresh<T, LEV>>(loc, sm);
   if (tid == 0) {
     st_c(B.rr_part + item, part_bb);
@@ -594,9 +603,13 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
       return;
     }
     if (lead) st->bnorm = bnorm;
-    if (tid < LEAF) sm.t[tid] = sm.tr[tid];
-    __syncthreads();
-    r_prolong<T, LEV>(F, sm, stR, (const T*)nullptr, 0.0, gate);
+    if constexpr (JAC) {
+      if (tid < LEAF) sm.z[tid] = (T)(dinv * (double)sm.r[tid]);
+    } else {
+      if (tid < LEAF) sm.t[tid] = sm.tr[tid];
+      __syncthreads();
+      r_prolong<T, LEV>(F, sm, stR, (const T*)nullptr, 0.0, gate);
+    }
     if constexpr (SQ) {
       if (!squared()) return;
     }
@@ -677,7 +690,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
     }
     // U_k U_k^T q is this workgroup's alone: it overlaps the partners' words
     // in flight
-    leaf_apply<T, LEV>(F, sm.q, sm.tq, sm.yq, sm);
+    if constexpr (!JAC) leaf_apply<T, LEV>(F, sm.q, sm.tq, sm.yq, sm);
     // ---------------- phase BC (it) ----------------
     double alpha = 0.0;
     {
@@ -709,8 +722,12 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
         x += alpha * (double)sm.p[tid];
         loc_rr = (double)rn * (double)rn;
       }
-      // (r_prolong_split synchronizes before it reads sm.r)
-      r_prolong_split<T, LEV>(F, sm, stR, stQ, alpha, gate, r_from_prev);
+      if constexpr (JAC) {
+        if (tid < LEAF) sm.z[tid] = (T)(dinv * (double)sm.r[tid]);
+      } else {
+        // (r_prolong_split synchronizes before it reads sm.r)
+        r_prolong_split<T, LEV>(F, sm, stR, stQ, alpha, gate, r_from_prev);
+      }
       if constexpr (SQ) {
         if (!squared()) return;
       }
@@ -718,7 +735,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
       // partners' next phase BC reads it once they hold this step's words);
       // else the same linear update the partners use (its rounding drift is
       // bounded by the refreshes)
-      const bool refresh = (it % kRefresh<T> == 0);
+      const bool refresh = !JAC && (it % kRefresh<T> == 0);
       if (refresh) {
         // exact W^T r (into the other buffer: slow partners may still be
         // staging the previous one) and U U^T r
@@ -727,7 +744,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
         diag_times<T, LEV>(F, sm.tr, sm.yr);
       }
       publish(loc_rr, it);
-      if (!refresh && tid < LEAF) sm.yr[tid] = (T)((double)sm.yr[tid] - alpha * (double)sm.yq[tid]);
+      if (!JAC && !refresh && tid < LEAF) sm.yr[tid] = (T)((double)sm.yr[tid] - alpha * (double)sm.yq[tid]);
     }
   }
   // ---- the solution of the leaf's rows ----

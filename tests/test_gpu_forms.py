@@ -104,10 +104,18 @@ def test_form_solve_parity(name, batch, form, prec):
     _log(f"form solve {name} form={form} prec={prec}")
     s = _solver(b, factors=form != hpcg.HPCG_FORM_JACOBI)
     _check_solve(b, s, form, prec=prec)
-    # the squared form runs on the register-resident engine where it fits,
-    # Jacobi on the graph engine
-    assert s.last_engine == (hpcg.HPCG_ENGINE_PERSISTENT if form == hpcg.HPCG_FORM_SQUARED
-                             else hpcg.HPCG_ENGINE_GRAPH)
+    # both forms run on the register-resident engine where it fits
+    assert s.last_engine == hpcg.HPCG_ENGINE_PERSISTENT
+    s.close()
+
+
+@pytest.mark.parametrize("name,batch", [("N8k", None), ("tet4k", None), ("batch64x2k", 3)])
+def test_jacobi_solve_graph_engine(name, batch):
+    b = make_config(name, batch=batch)
+    _log(f"jacobi solve on the graph engine {name}")
+    s = _solver(b, factors=False)
+    _check_solve(b, s, hpcg.HPCG_FORM_JACOBI, engine=hpcg.HPCG_ENGINE_GRAPH)
+    assert s.last_engine == hpcg.HPCG_ENGINE_GRAPH
     s.close()
 
 
@@ -247,8 +255,12 @@ def test_form_argument_errors():
             s.estimate_spectrum(steps)
     s.set_option(hpcg.HPCG_OPT_FORM, hpcg.HPCG_FORM_JACOBI)
     s.set_option(hpcg.HPCG_OPT_ENGINE, hpcg.HPCG_ENGINE_PERSISTENT)
+    res = s.solve(b.b.reshape(-1), tol=b.tol, maxit=b.maxit)       # register-resident Jacobi
+    assert res.status == hpcg.HPCG_OK and s.last_engine == hpcg.HPCG_ENGINE_PERSISTENT
+    s.set_option(hpcg.HPCG_OPT_LEAF_SPLIT, 2)      # streaming persistent engine: direct form only
     with pytest.raises(hpcg.HPCGError):
         s.solve(b.b.reshape(-1), tol=b.tol, maxit=b.maxit)
+    s.set_option(hpcg.HPCG_OPT_LEAF_SPLIT, 0)
     s.set_option(hpcg.HPCG_OPT_FORM, hpcg.HPCG_FORM_SQUARED)
     with pytest.raises(hpcg.HPCGError):
         s.apply_M_block(np.zeros((b.n, 16), np.float32), 16)
