@@ -120,6 +120,13 @@ typedef enum {
                                    down (M not SPD) solves the whole batch again
                                    from x = 0 with M = diag(A)^-1 and reports
                                    that solve; 0 (default): report the breakdown */
+    HPCG_OPT_POLL_LIMIT = 128,  /* register-resident engine: polls of one flagged
+                                   word before the solve gives up (abort flag,
+                                   hpcg_solve returns HPCG_ERR_HIP), 1 .. 2^30;
+                                   0 restores the default (2^22, seconds).  A
+                                   diagnostic bound: small values make a healthy
+                                   solve abort, which is how its error path is
+                                   tested                                         */
     HPCG_OPT_LEAF_SPLIT = 8     /* workgroups per leaf in the apply kernels and the
                                    graph and streaming engines: 0 = automatic
                                    (default), else 1, 2, 4 or 8; a split whose LDS

@@ -45,6 +45,7 @@ struct Layout {
 constexpr size_t kMaxLds = 160 * 1024;
 
 // control words, each on its own 256-byte line
+constexpr unsigned kPollLimitDefault = 1u << 22;   // polls of one flagged word (resident engine)
 constexpr size_t kCtlBarrier = 0, kCtlAbort = 256, kCtlItbase = 512, kCtlReplays = 768, kCtlBytes = 1024;
 
 constexpr int kMaxSplit = 8;   // workgroups per leaf in the streaming kernels
@@ -551,6 +552,7 @@ hpcg_status hpcg_create(const hpcg_partition* part, const int32_t* d_row_ptr, co
   B.qll = reinterpret_cast<unsigned long long*>(w + lay.qll);
   B.pqll = reinterpret_cast<unsigned long long*>(w + lay.pqll);
   B.ep_base = 1u;
+  B.poll_limit = kPollLimitDefault;
   B.llw = reinterpret_cast<unsigned long long*>(w + lay.llw);
   B.lle = reinterpret_cast<unsigned*>(w + lay.lle);
   B.lly = reinterpret_cast<unsigned long long*>(w + lay.lly);
@@ -1126,7 +1128,9 @@ hpcg_status solve_core(hpcg_ctx* h, const float* d_b, double* d_x, double tol, i
   HIP_OR_FAIL(h, hipMemcpyAsync(h->h_st, h->B.st, (size_t)G.B * sizeof(SysState), hipMemcpyDeviceToHost, h->stream));
   HIP_OR_FAIL(h, hipMemcpyAsync(h->h_ctl, h->B.abort_flag, sizeof(int), hipMemcpyDeviceToHost, h->stream));
   HIP_OR_FAIL(h, hipStreamSynchronize(h->stream));
-  if (*h->h_ctl) return fail(h, HPCG_ERR_HIP, "device-wide barrier timed out (workgroups not co-resident)");
+  if (*h->h_ctl)
+    return fail(h, HPCG_ERR_HIP, "a bounded wait of the persistent solve ran out (workgroups not co-resident, "
+                                 "or HPCG_OPT_POLL_LIMIT below the exchange latency)");
   return HPCG_OK;
 }
 
@@ -1360,6 +1364,10 @@ hpcg_status hpcg_set_option(hpcg_handle h, int32_t option, int32_t value) {
     case HPCG_OPT_PRECISION:
       if (value != HPCG_PREC_VEC64 && value != HPCG_PREC_VEC32) return fail(h, HPCG_ERR_INVALID_ARG, "bad precision");
       h->prec = value;
+      return HPCG_OK;
+    case HPCG_OPT_POLL_LIMIT:
+      if (value < 0 || value > (1 << 30)) return fail(h, HPCG_ERR_INVALID_ARG, "poll limit must be 0 .. 2^30");
+      h->B.poll_limit = value == 0 ? kPollLimitDefault : (unsigned)value;
       return HPCG_OK;
     case HPCG_OPT_FALLBACK:
       if (value != 0 && value != 1) return fail(h, HPCG_ERR_INVALID_ARG, "fallback must be 0 or 1");

@@ -122,6 +122,7 @@ struct Bufs {
   unsigned long long* qll;  // resident engine: [2][B][levels][K][RANK] W^T q words by step parity
   unsigned long long* pqll; // resident engine: [2][B*K][2] p.q partials as (word, epoch) pairs by step parity
   unsigned ep_base;    // resident engine: epoch of this solve's z0 (z of step i has ep_base + i)
+  unsigned poll_limit; // resident engine: polls of one flagged word before the solve aborts
   int form;            // FORM_*
   double tol;
   int maxit;

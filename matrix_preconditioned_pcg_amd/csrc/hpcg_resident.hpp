@@ -266,9 +266,9 @@ __device__ __forceinline__ void ll_put(unsigned long long* p, T v, unsigned e) {
   }
 }
 
-// Bound on the polls of one flagged word (each ~1 us): a writer that never
-// comes (an aborted workgroup) ends the wait with the abort flag.
-constexpr unsigned kLLPollMax = 1u << 22;
+// Polls of one flagged word are bounded by B.poll_limit (default 2^22, each
+// well under a microsecond): a writer that never comes (an aborted workgroup)
+// ends the wait with the abort flag.
 
 // z of global row c (two words apart per row) once it carries epoch e.  The
 // polls are pipelined two deep: the next load is in flight while the previous
@@ -284,7 +284,7 @@ __device__ __forceinline__ T ll_get_z(const Bufs& B, int c, unsigned e, int& bad
     } else {
       if (ll_ready(a0, e) && ll_ready(a1, e)) return __hiloint2double((int)(unsigned)a1, (int)(unsigned)a0);
     }
-    if (polls > kLLPollMax || ((polls & 1023u) == 1023u && ld_c(B.abort_flag))) {
+    if (polls > B.poll_limit || ((polls & 1023u) == 1023u && ld_c(B.abort_flag))) {
       st_c(B.abort_flag, 1);
       bad = 1;
       return T(0);
@@ -311,7 +311,7 @@ __device__ __forceinline__ void ll_get_partials(const Bufs& B, int s, int K, uns
         b += __hiloint2double((int)(unsigned)w3, (int)(unsigned)w2);
         break;
       }
-      if (polls > kLLPollMax || ((polls & 1023u) == 1023u && ld_c(B.abort_flag))) {
+      if (polls > B.poll_limit || ((polls & 1023u) == 1023u && ld_c(B.abort_flag))) {
         st_c(B.abort_flag, 1);
         bad = 1;
         break;
@@ -417,7 +417,7 @@ __device__ __forceinline__ void ll_stage_q(const Geom& G, const Bufs& B, int s, 
           pending &= ~(1u << j);
         }
       if (!pending) break;
-      if (polls > kLLPollMax || ((polls & 1023u) == 1023u && ld_c(B.abort_flag))) {
+      if (polls > B.poll_limit || ((polls & 1023u) == 1023u && ld_c(B.abort_flag))) {
         st_c(B.abort_flag, 1);
         bad = 1;
         break;
@@ -445,7 +445,7 @@ __device__ __forceinline__ double ll_get_pq(const Bufs& B, int s, int K, size_t 
         a += __hiloint2double((int)(unsigned)w1, (int)(unsigned)w0);
         break;
       }
-      if (polls > kLLPollMax || ((polls & 1023u) == 1023u && ld_c(B.abort_flag))) {
+      if (polls > B.poll_limit || ((polls & 1023u) == 1023u && ld_c(B.abort_flag))) {
         st_c(B.abort_flag, 1);
         bad = 1;
         break;

@@ -48,6 +48,7 @@ HPCG_OPT_APPLY_PATH = 16
 HPCG_OPT_FORM = 32
 
 HPCG_OPT_FALLBACK = 64
+HPCG_OPT_POLL_LIMIT = 128
 
 HPCG_FORM_DIRECT = 0
 HPCG_FORM_SQUARED = 1

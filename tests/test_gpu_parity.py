@@ -589,6 +589,36 @@ def test_flagged_word_epochs_wrap(cfg):
     s.close()
 
 
+@pytest.mark.parametrize("prec", [hpcg.HPCG_PREC_VEC64, hpcg.HPCG_PREC_VEC32])
+def test_resident_poll_limit(cfg, prec):
+    # With a bound of two re-polls per flagged word a resident solve either
+    # still finishes with the same result (every word came in time) or gives
+    # up through the abort flag, which hpcg_solve reports; it never hangs and
+    # never returns anything else.  With the default bound restored the next
+    # solve is healthy and bit-identical to one before.
+    batch = cfg("N8k")
+    _log(f"poll limit N8k prec={prec}")
+    s = _solver(batch)
+    s.set_option(hpcg.HPCG_OPT_PRECISION, prec)
+    ref = s.solve(batch.b.reshape(-1), tol=batch.tol, maxit=batch.maxit)
+    s.set_option(hpcg.HPCG_OPT_POLL_LIMIT, 1)
+    for _ in range(3):
+        try:
+            tight = s.solve(batch.b.reshape(-1), tol=batch.tol, maxit=batch.maxit)
+        except hpcg.HPCGError as err:
+            assert err.status == hpcg.HPCG_ERR_HIP and "bounded wait" in str(err), err
+        else:
+            assert tight.iterations == ref.iterations and torch.equal(tight.x, ref.x)
+    s.set_option(hpcg.HPCG_OPT_POLL_LIMIT, 0)
+    res = s.solve(batch.b.reshape(-1), tol=batch.tol, maxit=batch.maxit)
+    assert res.status == hpcg.HPCG_OK and res.iterations == ref.iterations
+    assert torch.equal(res.x, ref.x)
+    for bad in (-1, (1 << 30) + 1):
+        with pytest.raises(hpcg.HPCGError):
+            s.set_option(hpcg.HPCG_OPT_POLL_LIMIT, bad)
+    s.close()
+
+
 def test_set_values_refreshes_matrix(cfg):
     batch = cfg("N1k")
     _log("set_values")
