@@ -233,7 +233,7 @@ def main(argv=None):
             solver.set_option(hpcg.HPCG_OPT_APPLY_PATH, hpcg.HPCG_APPLY_STREAMING)
             with torch.cuda.stream(stream):
                 streaming_us = time_graph(apply, args.reps, stream, torch)
-            if batch.batch * batch.K <= 256:
+            if batch.K <= 256:
                 solver.set_option(hpcg.HPCG_OPT_APPLY_PATH, hpcg.HPCG_APPLY_FUSED)
                 with torch.cuda.stream(stream):
                     fused_us = time_graph(apply, args.reps, stream, torch)

@@ -161,11 +161,14 @@ typedef enum {
  * STREAMING: two launches (restriction, then prolongation), any batch size;
  * the prolongation reads the level slabs a second time.  FUSED: one launch in
  * which the 512-thread workgroup of each leaf keeps U_k and its slabs in
- * registers from the restriction to the prolongation, across one device-wide
- * barrier, so every factor byte is read once; needs every workgroup of the
- * batch resident at once, one per compute unit (HPCG_ERR_SHAPE otherwise).
- * The barrier's wait is bounded (about a second): should other work hold the
- * compute units that long, the apply gives up and its output is undefined.
+ * registers from the restriction to the prolongation and takes its partners'
+ * restrictions from flagged words, so every factor byte is read once; the
+ * workgroups of one system must be resident at once, one per compute unit
+ * (HPCG_ERR_SHAPE when a system has more leaves than that).  A batch with
+ * more leaves than the device has compute units runs as several such
+ * launches, each over as many whole systems as fit.  The wait for a partner's
+ * words is bounded (about a second): should other work hold the compute
+ * units that long, the apply gives up and its output is undefined.
  * AUTO (default): FUSED where it fits, else STREAMING. */
 typedef enum {
     HPCG_APPLY_AUTO = 0,

@@ -690,7 +690,7 @@ hpcg_status run_fused_apply(hpcg_ctx* h, const float* d_r, float* d_y, bool& ran
   ran = false;
   const Geom G = h->G;
   const int items = G.B * G.K;
-  if (items > h->num_cu) return HPCG_OK;
+  if (G.K > h->num_cu) return HPCG_OK;
   Geom Ga = G;
   Bufs Ba = h->B;
   const float* ra = d_r;
@@ -721,8 +721,18 @@ hpcg_status run_fused_apply(hpcg_ctx* h, const float* d_r, float* d_y, bool& ran
   if (s != HPCG_OK) return s;
   if (h->fused_per_cu < 0)
     HIP_OR_FAIL(h, hipOccupancyMaxActiveBlocksPerMultiprocessor(&h->fused_per_cu, fn, NTR, dyn));
-  if ((int64_t)h->fused_per_cu * h->num_cu < items) return HPCG_OK;
-  HIP_OR_FAIL(h, hipLaunchKernel(fn, dim3(items), dim3(NTR), args, (unsigned)dyn, h->stream));
+  // a leaf waits only for leaves of its own system: a batch larger than the
+  // co-resident workgroups runs as launches over as many whole systems as fit
+  const int64_t cap = (int64_t)h->fused_per_cu * h->num_cu;
+  const int per_launch = (int)std::min<int64_t>(G.B, cap / G.K);
+  if (per_launch < 1) return HPCG_OK;
+  int item0 = 0;
+  void* fargs[] = {&Ga, &Ba, &ra, &ya, &item0};
+  for (int s0 = 0; s0 < G.B; s0 += per_launch) {
+    item0 = s0 * G.K;
+    const int nsys = std::min(per_launch, G.B - s0);
+    HIP_OR_FAIL(h, hipLaunchKernel(fn, dim3(nsys * G.K), dim3(NTR), fargs, (unsigned)dyn, h->stream));
+  }
   ran = true;
   return HPCG_OK;
 }
@@ -781,7 +791,7 @@ hpcg_status apply_H(hpcg_ctx* h, const float* d_r, float* d_y) {
       return HPCG_OK;
     }
     if (h->apply_path == HPCG_APPLY_FUSED)
-      return fail(h, HPCG_ERR_SHAPE, "fused apply: the batch has more leaves than co-resident workgroups");
+      return fail(h, HPCG_ERR_SHAPE, "fused apply: a system has more leaves than co-resident workgroups");
   }
   h->last_apply_path = HPCG_APPLY_STREAMING;
   const Geom& G = h->Gapply;

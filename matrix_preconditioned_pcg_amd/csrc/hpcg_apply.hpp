@@ -26,8 +26,11 @@ __global__ __launch_bounds__(NT) void k_spmv(const int* __restrict__ row_ptr, co
   if (row < nrows && lr == 0) y[row] = acc;
 }
 
-// Single-launch apply y = M r (fp32 in and out) for batches whose leaves all
-// get a compute unit: the workgroup of leaf k loads U_k and its slabs into
+// Single-launch apply y = M r (fp32 in and out) over whole systems whose leaves
+// all get a compute unit (a larger batch runs as several launches, each over
+// as many whole systems as fit, item0 being the first leaf of the launch,
+// since a leaf waits only for leaves of its own system): the workgroup of
+// leaf k loads U_k and its slabs into
 // registers once, restricts (eq. (2)), gathers the partner halves'
 // restrictions (eq. (3)), and prolongs (eqs. (4)-(5)) and adds the diagonal
 // stage and the gate with the same registers, so every factor byte crosses HBM
@@ -96,12 +99,12 @@ __device__ __forceinline__ void gather_partners_ll(const Geom& G, const Bufs& B,
 
 template <int LEV>
 __global__ __launch_bounds__(NTR) void k_apply_fused(Geom G, Bufs B, const float* __restrict__ rin,
-                                                     float* __restrict__ yout) {
+                                                     float* __restrict__ yout, int item0) {
   __shared__ RSmem<float> sm;
   extern __shared__ int4 fdyn4[];
   float* stR = reinterpret_cast<float*>(fdyn4);
   const int tid = threadIdx.x;
-  const int item = blockIdx.x;
+  const int item = item0 + (int)blockIdx.x;
   const int s = item / G.K, k = item - s * G.K;
   const int leaf0 = s * G.n + k * LEAF;
   // r, the gate and the epoch are issued before the factors: the loads

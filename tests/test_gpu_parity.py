@@ -155,7 +155,7 @@ def test_apply_parity(cfg, name):
 
 
 @pytest.mark.parametrize("path", [hpcg.HPCG_APPLY_STREAMING, hpcg.HPCG_APPLY_FUSED])
-@pytest.mark.parametrize("name", ["N1k", "N8k", "N16k", "tet4k"])
+@pytest.mark.parametrize("name", ["N1k", "N8k", "N16k", "tet4k", "batch64x2k"])
 def test_apply_paths(cfg, name, path):
     # the two-launch and the single-launch apply give the same M r
     batch = cfg(name)
@@ -170,10 +170,21 @@ def test_apply_paths(cfg, name, path):
 
 
 def test_apply_auto_path_and_fused_refusal(cfg):
-    big = cfg("batch64x2k")        # 1024 leaves: more than one compute unit each
+    # 1024 leaves, more than the compute units: AUTO takes the single-pass
+    # apply in launches of whole systems
+    big = cfg("batch64x2k")
     s = _solver(big)
     r = np.random.default_rng(15).standard_normal((big.batch, big.n)).astype(np.float32)
     _check_apply(big, s, r)
+    assert hpcg.hpcg_last_apply_path(s.handle) == hpcg.HPCG_APPLY_FUSED
+    s.close()
+    # one system with more leaves than compute units: FUSED refuses, AUTO streams
+    wide = random_system(512 * 128, seed=7, levels=0)
+    assert wide.K > torch.cuda.get_device_properties(0).multi_processor_count
+    _log("apply auto path, 512 leaves in one system")
+    s = _solver(wide)
+    r = np.random.default_rng(17).standard_normal((1, wide.n)).astype(np.float32)
+    _check_apply(wide, s, r)
     assert hpcg.hpcg_last_apply_path(s.handle) == hpcg.HPCG_APPLY_STREAMING
     s.set_option(hpcg.HPCG_OPT_APPLY_PATH, hpcg.HPCG_APPLY_FUSED)
     with pytest.raises(hpcg.HPCGError):
@@ -187,18 +198,20 @@ def test_apply_auto_path_and_fused_refusal(cfg):
     s.close()
 
 
-def test_fused_apply_graph_replays(cfg):
-    # the fused apply's barrier resets itself: captured calls replay correctly,
-    # with eager work and synchronizations between the replays
-    batch = cfg("N8k")
-    _log("fused apply graph replays")
+@pytest.mark.parametrize("name", ["N8k", "batch64x2k"])
+def test_fused_apply_graph_replays(cfg, name):
+    # the fused apply's flagged words need no reset: captured calls (one launch,
+    # or several over groups of whole systems) replay correctly, with eager
+    # work and synchronizations between the replays
+    batch = cfg(name)
+    _log(f"fused apply graph replays {name}")
     stream = torch.cuda.Stream()
     s = hpcg.Solver(batch.n, batch.row_ptr, batch.col, batch.val, batch=batch.batch, levels=batch.levels,
                     stream=stream)
     s.set_factors(batch.U, batch.W, batch.g)
     s.set_option(hpcg.HPCG_OPT_APPLY_PATH, hpcg.HPCG_APPLY_FUSED)
     rng = np.random.default_rng(16)
-    rs = [torch.as_tensor(rng.standard_normal(batch.n).astype(np.float32)).cuda() for _ in range(3)]
+    rs = [torch.as_tensor(rng.standard_normal(batch.batch * batch.n).astype(np.float32)).cuda() for _ in range(3)]
     ys = [torch.empty_like(rs[0]) for _ in range(3)]
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
