@@ -100,14 +100,17 @@ typedef enum {
                                    of a system gets a CU, else graph             */
     HPCG_ENGINE_GRAPH = 1,      /* per-phase kernels, unrolled iterations replayed
                                    as one hipGraph, host polls a pinned flag      */
-    HPCG_ENGINE_PERSISTENT = 2  /* one launch runs the whole solve with barriers
-                                   between phases: one 512-thread workgroup per
-                                   leaf with the factors in VGPRs when K <= #CUs
-                                   (two barriers per iteration among a system's
-                                   workgroups; a batch with more leaves than CUs
-                                   runs in groups of whole systems, one launch
-                                   each), else workgroups streaming the factors
-                                   (three device-wide barriers per iteration)    */
+    HPCG_ENGINE_PERSISTENT = 2  /* one launch runs the whole solve: one 512-thread
+                                   workgroup per leaf with the factors in VGPRs
+                                   when K <= #CUs (the values that cross
+                                   workgroups travel as flagged words, two
+                                   exchanges per iteration and no barrier; the
+                                   SQUARED form adds one barrier among a
+                                   system's workgroups; a batch with more leaves
+                                   than CUs runs in groups of whole systems, one
+                                   launch each), else workgroups streaming the
+                                   factors (three device-wide barriers per
+                                   iteration)                                     */
 } hpcg_engine;
 
 typedef enum {
