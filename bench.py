@@ -380,6 +380,11 @@ def main(argv=None):
                             "apply_spmv_us": round(o["pair_us"], 3),
                             "apply_spmv_gbs": round(o["pair_gbs"], 1),
                             "apply_spmv_frac": round(o["pair_frac"], 4)}
+            if o["apply_bytes"] + o["spmv_bytes"] >= 64 << 20:
+                # a workload whose pair moves more than a quarter of the Infinity
+                # Cache: also timed with the factors cycled through HBM
+                log(f"bench: {name} cold (factors from HBM) apply + SpMV")
+                others[name]["cold"] = measure_cold(_b)
     variants = {}
     if not args.no_variants:
         for label, eng, prec in (("persistent_vec64", 2, 0), ("persistent_vec32", 2, 1),
