@@ -819,6 +819,17 @@ namespace {
 
 bool block_nrhs_ok(int32_t nrhs) { return nrhs >= BNC && nrhs <= 1024 && nrhs % BNC == 0; }
 
+// 16-column tiles per workgroup of the block apply (1, 2 or 4): doubled while
+// they divide nrhs and the grid would still hold more workgroups than the
+// device has compute units, so that each factor operand a workgroup loads
+// feeds more products without leaving compute units idle.
+int block_nct(const hpcg_ctx* h, int32_t nrhs) {
+  const int64_t leaves = (int64_t)h->G.B * h->G.K;
+  int nct = 1;
+  while (nct < 4 && nrhs % (2 * nct * BNC) == 0 && leaves * (nrhs / (nct * BNC)) > h->num_cu) nct *= 2;
+  return nct;
+}
+
 BlockGeom block_geom(const hpcg_ctx* h, int32_t nrhs) {
   BlockGeom bg;
   bg.n = h->G.n;
@@ -826,7 +837,7 @@ BlockGeom block_geom(const hpcg_ctx* h, int32_t nrhs) {
   bg.levels = h->G.levels;
   bg.B = h->G.B;
   bg.nrhs = nrhs;
-  bg.tiles = nrhs / BNC;
+  bg.tiles = nrhs / (BNC * block_nct(h, nrhs));
   return bg;
 }
 
@@ -839,12 +850,20 @@ size_t block_half_bytes(const hpcg_ctx* h, int32_t nrhs) {
 hpcg_status launch_block_apply(hpcg_ctx* h, int32_t nrhs, const float* d_R, float* d_Y, float* Q, float* H,
                                hipStream_t stream) {
   const BlockGeom bg = block_geom(h, nrhs);
+  const int nct = block_nct(h, nrhs);
   const int grid = h->G.B * h->G.K * bg.tiles;
   switch (h->G.levels) {
 #define HPCG_BLOCK_RESTRICT(LV)                                                                          \
     case LV:                                                                                             \
-      hipLaunchKernelGGL(k_block_restrict<LV>, dim3(grid), dim3(BNT), 0, stream, bg, h->B.U, h->B.W,     \
-                         h->B.g, d_R, d_Y, Q);                                                           \
+      if (nct == 4)                                                                                      \
+        hipLaunchKernelGGL((k_block_restrict<LV, 4>), dim3(grid), dim3(BNT), 0, stream, bg, h->B.U, h->B.W, \
+                           h->B.g, d_R, d_Y, Q);                                                         \
+      else if (nct == 2)                                                                                 \
+        hipLaunchKernelGGL((k_block_restrict<LV, 2>), dim3(grid), dim3(BNT), 0, stream, bg, h->B.U, h->B.W, \
+                           h->B.g, d_R, d_Y, Q);                                                         \
+      else                                                                                               \
+        hipLaunchKernelGGL((k_block_restrict<LV, 1>), dim3(grid), dim3(BNT), 0, stream, bg, h->B.U, h->B.W, \
+                           h->B.g, d_R, d_Y, Q);                                                         \
       break;
     HPCG_BLOCK_RESTRICT(0) HPCG_BLOCK_RESTRICT(1) HPCG_BLOCK_RESTRICT(2) HPCG_BLOCK_RESTRICT(3)
     HPCG_BLOCK_RESTRICT(4) HPCG_BLOCK_RESTRICT(5) HPCG_BLOCK_RESTRICT(6) HPCG_BLOCK_RESTRICT(7)
@@ -860,7 +879,12 @@ hpcg_status launch_block_apply(hpcg_ctx* h, int32_t nrhs, const float* d_R, floa
     switch (h->G.levels) {
 #define HPCG_BLOCK_PROLONG(LV)                                                                          \
       case LV:                                                                                          \
-        hipLaunchKernelGGL(k_block_prolong<LV>, dim3(grid), dim3(BNT), 0, stream, bg, h->B.W, H, d_Y);  \
+        if (nct == 4)                                                                                   \
+          hipLaunchKernelGGL((k_block_prolong<LV, 4>), dim3(grid), dim3(BNT), 0, stream, bg, h->B.W, H, d_Y); \
+        else if (nct == 2)                                                                              \
+          hipLaunchKernelGGL((k_block_prolong<LV, 2>), dim3(grid), dim3(BNT), 0, stream, bg, h->B.W, H, d_Y); \
+        else                                                                                            \
+          hipLaunchKernelGGL((k_block_prolong<LV, 1>), dim3(grid), dim3(BNT), 0, stream, bg, h->B.W, H, d_Y); \
         break;
       HPCG_BLOCK_PROLONG(1) HPCG_BLOCK_PROLONG(2) HPCG_BLOCK_PROLONG(3) HPCG_BLOCK_PROLONG(4)
       HPCG_BLOCK_PROLONG(5) HPCG_BLOCK_PROLONG(6) HPCG_BLOCK_PROLONG(7) HPCG_BLOCK_PROLONG(8)

@@ -11,7 +11,9 @@
 // section 5, stages (i)-(ii), eqs. (2)-(5).
 //
 // Layout: R, Y, X are node-major, [B*n][nrhs] fp32 (the nrhs values of a node are
-// contiguous).  A workgroup (4 wave64) owns one leaf and one 16-column tile.
+// contiguous).  A workgroup (4 wave64) owns one leaf and NCT 16-column tiles
+// (two where nrhs is a multiple of 32, so that each factor operand it loads
+// feeds twice the products).
 // Products use v_mfma_f32_16x16x4_f32 (fp32 in, fp32 accumulate).  Lane l of a
 // wave supplies A[l % 16][l / 16] and B[l / 16][l % 16] and receives
 // D[4 (l / 16) + v][l % 16], v = 0..3.  Where an operand is read along the
@@ -44,7 +46,7 @@ __device__ __forceinline__ mf4 mfma4(float a, float b, mf4 c) {
 struct BlockGeom {
   int n, K, levels, B;   // as Geom
   int nrhs;              // columns of R / Y (multiple of BNC)
-  int tiles;             // nrhs / BNC
+  int tiles;             // column tiles of a leaf: nrhs / (BNC NCT), NCT the kernels' tiles per workgroup
 };
 
 // Workgroup -> (system, leaf, column tile).  Workgroups are dispatched to the
@@ -72,25 +74,30 @@ __device__ __forceinline__ size_t q_index(const BlockGeom& G, int s, int l, int 
 
 // (1) leaf stage, gate and restriction.  All global operand loads of a stage
 // are issued before its products, and the next level's before this level's.
-template <int LEV>
+// A workgroup owns NCT 16-column tiles (BW = 16 NCT columns): every U_k and
+// W_l[k] operand it loads feeds the MFMAs of all NCT tiles.
+template <int LEV, int NCT>
 __global__ __launch_bounds__(BNT) void k_block_restrict(BlockGeom G, const float* __restrict__ U,
                                                         const float* __restrict__ W, const float* __restrict__ g,
                                                         const float* __restrict__ R, float* __restrict__ Y,
                                                         float* __restrict__ Q) {
-  __shared__ __attribute__((aligned(16))) float Rs[LEAF * BNC];          // R_k tile, [row][16]
-  __shared__ __attribute__((aligned(16))) float Ts[BNC * TS_STRIDE];     // T^T, [col][row]
+  constexpr int BW = BNC * NCT;
+  __shared__ __attribute__((aligned(16))) float Rs[LEAF * BW];          // R_k tile, [row][BW]
+  __shared__ __attribute__((aligned(16))) float Ts[BW * TS_STRIDE];     // T^T, [col][row]
   const BItem it = bitem(G);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int q = lane >> 4, r = lane & 15;
-  const int c0 = it.ct * BNC;
+  const int c0 = it.ct * BW;
   const float* Uk = U + ((size_t)it.s * G.K + it.k) * LEAF * LEAF;
   // restriction work of this wave: rank tile (w & 1) of levels (w >> 1), +2, ...
   const int mt = w & 1;
   auto wlev = [&](int l) {
     return W + (((size_t)it.s * LEV + l) * G.K + it.k) * LEAF * RANK + 16 * mt + r;
   };
-  // R tile: 128 rows x 64 bytes, straight into LDS
-  dma_to_lds(Rs, LEAF * BNC / 4, [&](int c) { return R + (size_t)(it.leaf0 + (c >> 2)) * G.nrhs + c0 + 4 * (c & 3); });
+  // R tile: 128 rows x 4 BW bytes, straight into LDS
+  dma_to_lds(Rs, LEAF * BW / 4, [&](int c) {
+    return R + (size_t)(it.leaf0 + c / (BW / 4)) * G.nrhs + c0 + 4 * (c % (BW / 4));
+  });
   // GEMM 1 A operands: U[4s + q][32w + r] and U[4s + q][32w + 16 + r], s = 0..31
   float ua[32], ub[32], wa[32];
 #pragma unroll
@@ -105,17 +112,25 @@ __global__ __launch_bounds__(BNT) void k_block_restrict(BlockGeom G, const float
     for (int s = 0; s < 32; ++s) wa[s] = Wl[(size_t)(4 * s + q) * RANK];
   }
   lds_dma_wait();
-  // T = U_k^T R_k: this wave's rows [32w, 32w + 32) of T
-  mf4 ta = {0, 0, 0, 0}, tb = {0, 0, 0, 0};
+  // T = U_k^T R_k: this wave's rows [32w, 32w + 32) of T, for every tile
+  mf4 ta[NCT], tb[NCT];
+#pragma unroll
+  for (int j = 0; j < NCT; ++j) ta[j] = tb[j] = mf4{0, 0, 0, 0};
 #pragma unroll
   for (int s = 0; s < 32; ++s) {
-    const float bv = Rs[(4 * s + q) * BNC + r];
-    ta = mfma4(ua[s], bv, ta);
-    tb = mfma4(ub[s], bv, tb);
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) {
+      const float bv = Rs[(4 * s + q) * BW + 16 * j + r];
+      ta[j] = mfma4(ua[s], bv, ta[j]);
+      tb[j] = mfma4(ub[s], bv, tb[j]);
+    }
   }
-  // T^T into LDS: lane holds T[32w + 4q + v][r] (and + 16)
-  *reinterpret_cast<mf4*>(&Ts[r * TS_STRIDE + 32 * w + 4 * q]) = ta;
-  *reinterpret_cast<mf4*>(&Ts[r * TS_STRIDE + 32 * w + 16 + 4 * q]) = tb;
+  // T^T into LDS: lane holds T[32w + 4q + v][16j + r] (and + 16)
+#pragma unroll
+  for (int j = 0; j < NCT; ++j) {
+    *reinterpret_cast<mf4*>(&Ts[(16 * j + r) * TS_STRIDE + 32 * w + 4 * q]) = ta[j];
+    *reinterpret_cast<mf4*>(&Ts[(16 * j + r) * TS_STRIDE + 32 * w + 16 + 4 * q]) = tb[j];
+  }
   // restriction Q_l = W_l[k]^T R_k, two accumulation chains (even / odd k
   // steps) summed at the end
 #pragma unroll
@@ -127,16 +142,19 @@ __global__ __launch_bounds__(BNT) void k_block_restrict(BlockGeom G, const float
 #pragma unroll
       for (int s = 0; s < 32; ++s) wn[s] = Wn[(size_t)(4 * s + q) * RANK];
     }
-    mf4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
-#pragma unroll
-    for (int s = 0; s < 32; s += 2) {
-      a0 = mfma4(wa[s], Rs[(4 * s + q) * BNC + r], a0);
-      a1 = mfma4(wa[s + 1], Rs[(4 * s + 4 + q) * BNC + r], a1);
-    }
-    const mf4 acc = a0 + a1;
     float* Qo = Q + q_index(G, it.s, l, it.k, 16 * mt + 4 * q) + c0 + r;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) Qo[(size_t)v * G.nrhs] = acc[v];
+    for (int j = 0; j < NCT; ++j) {
+      mf4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
+#pragma unroll
+      for (int s = 0; s < 32; s += 2) {
+        a0 = mfma4(wa[s], Rs[(4 * s + q) * BW + 16 * j + r], a0);
+        a1 = mfma4(wa[s + 1], Rs[(4 * s + 4 + q) * BW + 16 * j + r], a1);
+      }
+      const mf4 acc = a0 + a1;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) Qo[(size_t)v * G.nrhs + 16 * j] = acc[v];
+    }
     if (l + 2 < LEV) {
 #pragma unroll
       for (int s = 0; s < 32; ++s) wa[s] = wn[s];
@@ -152,22 +170,26 @@ __global__ __launch_bounds__(BNT) void k_block_restrict(BlockGeom G, const float
     bu[ch] = *reinterpret_cast<const mf4*>(Ub + 16 * ch);
   }
   __syncthreads();
-  // Y = U_k T + g R: this wave's rows [32w, 32w + 32)
-  mf4 ya = {0, 0, 0, 0}, yb = {0, 0, 0, 0};
+  // Y = U_k T + g R: this wave's rows [32w, 32w + 32), tile by tile
 #pragma unroll
-  for (int ch = 0; ch < LEAF / 16; ++ch) {
-    const mf4 bt = *reinterpret_cast<const mf4*>(&Ts[r * TS_STRIDE + 16 * ch + 4 * q]);
+  for (int j = 0; j < NCT; ++j) {
+    mf4 ya = {0, 0, 0, 0}, yb = {0, 0, 0, 0};
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      ya = mfma4(au[ch][t], bt[t], ya);
-      yb = mfma4(bu[ch][t], bt[t], yb);
+    for (int ch = 0; ch < LEAF / 16; ++ch) {
+      const mf4 bt = *reinterpret_cast<const mf4*>(&Ts[(16 * j + r) * TS_STRIDE + 16 * ch + 4 * q]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        ya = mfma4(au[ch][t], bt[t], ya);
+        yb = mfma4(bu[ch][t], bt[t], yb);
+      }
     }
-  }
+    const int cj = c0 + 16 * j + r;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int ia = 32 * w + 4 * q + v, ib = ia + 16;
-    Y[(size_t)(it.leaf0 + ia) * G.nrhs + c0 + r] = ya[v] + g[it.leaf0 + ia] * Rs[ia * BNC + r];
-    Y[(size_t)(it.leaf0 + ib) * G.nrhs + c0 + r] = yb[v] + g[it.leaf0 + ib] * Rs[ib * BNC + r];
+    for (int v = 0; v < 4; ++v) {
+      const int ia = 32 * w + 4 * q + v, ib = ia + 16;
+      Y[(size_t)(it.leaf0 + ia) * G.nrhs + cj] = ya[v] + g[it.leaf0 + ia] * Rs[ia * BW + 16 * j + r];
+      Y[(size_t)(it.leaf0 + ib) * G.nrhs + cj] = yb[v] + g[it.leaf0 + ib] * Rs[ib * BW + 16 * j + r];
+    }
   }
 }
 
@@ -210,15 +232,16 @@ __global__ void k_block_halfsum(BlockGeom G, const float* __restrict__ Q, float*
 }
 
 // (3) prolongation: Y_k += sum_l W_l[k] H_l[(k >> l) ^ 1].  Every level's slab
-// rows are loaded in one batch up front.
-template <int LEV>
+// rows are loaded in one batch up front and feed the MFMAs of all NCT tiles.
+template <int LEV, int NCT>
 __global__ __launch_bounds__(BNT) void k_block_prolong(BlockGeom G, const float* __restrict__ W,
                                                        const float* __restrict__ H, float* __restrict__ Y) {
-  __shared__ __attribute__((aligned(16))) float Ps[(LEV > 0 ? LEV : 1) * BNC * PS_STRIDE];   // [l][col][rank]
+  constexpr int BW = BNC * NCT;
+  __shared__ __attribute__((aligned(16))) float Ps[(LEV > 0 ? LEV : 1) * BW * PS_STRIDE];   // [l][col][rank]
   const BItem it = bitem(G);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int q = lane >> 4, r = lane & 15;
-  const int c0 = it.ct * BNC;
+  const int c0 = it.ct * BW;
   mf4 aw[LEV > 0 ? LEV : 1][2], bw[LEV > 0 ? LEV : 1][2];
 #pragma unroll
   for (int l = 0; l < LEV; ++l) {
@@ -230,46 +253,55 @@ __global__ __launch_bounds__(BNT) void k_block_prolong(BlockGeom G, const float*
     }
   }
   // accumulators start from the leaf stage's Y
-  mf4 ya, yb;
+  mf4 ya[NCT], yb[NCT];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    ya[v] = Y[(size_t)(it.leaf0 + 32 * w + 4 * q + v) * G.nrhs + c0 + r];
-    yb[v] = Y[(size_t)(it.leaf0 + 32 * w + 16 + 4 * q + v) * G.nrhs + c0 + r];
+  for (int j = 0; j < NCT; ++j) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      ya[j][v] = Y[(size_t)(it.leaf0 + 32 * w + 4 * q + v) * G.nrhs + c0 + 16 * j + r];
+      yb[j][v] = Y[(size_t)(it.leaf0 + 32 * w + 16 + 4 * q + v) * G.nrhs + c0 + 16 * j + r];
+    }
   }
   // partner half sums, transposed into LDS: all loads first, then the stores
-  constexpr int PER = (LEV > 0 ? LEV : 1) * RANK * BNC / BNT;   // elements per thread
+  constexpr int PER = (LEV > 0 ? LEV : 1) * RANK * BW / BNT;   // elements per thread
   float hv[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int e = tid + u * BNT;
-    const int l = e / (RANK * BNC), rem = e - l * RANK * BNC;
-    const int row = rem / BNC, col = rem - row * BNC;
+    const int l = e / (RANK * BW), rem = e - l * RANK * BW;
+    const int row = rem / BW, col = rem - row * BW;
     hv[u] = H[q_index(G, it.s, l, (it.k >> l) ^ 1, row) + c0 + col];
   }
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int e = tid + u * BNT;
-    const int l = e / (RANK * BNC), rem = e - l * RANK * BNC;
-    const int row = rem / BNC, col = rem - row * BNC;
-    Ps[(l * BNC + col) * PS_STRIDE + row] = hv[u];
+    const int l = e / (RANK * BW), rem = e - l * RANK * BW;
+    const int row = rem / BW, col = rem - row * BW;
+    Ps[(l * BW + col) * PS_STRIDE + row] = hv[u];
   }
   __syncthreads();
 #pragma unroll
   for (int l = 0; l < LEV; ++l) {
 #pragma unroll
     for (int ch = 0; ch < RANK / 16; ++ch) {
-      const mf4 bp = *reinterpret_cast<const mf4*>(&Ps[(l * BNC + r) * PS_STRIDE + 16 * ch + 4 * q]);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        ya = mfma4(aw[l][ch][t], bp[t], ya);
-        yb = mfma4(bw[l][ch][t], bp[t], yb);
+      for (int j = 0; j < NCT; ++j) {
+        const mf4 bp = *reinterpret_cast<const mf4*>(&Ps[(l * BW + 16 * j + r) * PS_STRIDE + 16 * ch + 4 * q]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          ya[j] = mfma4(aw[l][ch][t], bp[t], ya[j]);
+          yb[j] = mfma4(bw[l][ch][t], bp[t], yb[j]);
+        }
       }
     }
   }
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    Y[(size_t)(it.leaf0 + 32 * w + 4 * q + v) * G.nrhs + c0 + r] = ya[v];
-    Y[(size_t)(it.leaf0 + 32 * w + 16 + 4 * q + v) * G.nrhs + c0 + r] = yb[v];
+  for (int j = 0; j < NCT; ++j) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      Y[(size_t)(it.leaf0 + 32 * w + 4 * q + v) * G.nrhs + c0 + 16 * j + r] = ya[j][v];
+      Y[(size_t)(it.leaf0 + 32 * w + 16 + 4 * q + v) * G.nrhs + c0 + 16 * j + r] = yb[j][v];
+    }
   }
 }
 

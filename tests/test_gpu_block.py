@@ -45,8 +45,10 @@ def _check_block_apply(batch, s, R):
     return Y
 
 
-@pytest.mark.parametrize("name,nrhs", [("N1k", 16), ("N1k", 64), ("N8k", 64), ("N16k", 128), ("tet4k", 48),
-                                       ("batch64x2k", 16)])
+# 16-column tiles per workgroup on a 256-CU device: one for most cases, two for
+# N8k x 96 and the 8-system batch x 64, four for N16k x 128
+@pytest.mark.parametrize("name,nrhs", [("N1k", 16), ("N1k", 64), ("N8k", 64), ("N8k", 96), ("N16k", 128),
+                                       ("tet4k", 48), ("batch64x2k", 16), ("batch64x2k", 64)])
 def test_block_apply_parity(name, nrhs):
     batch = make_config(name, batch=8 if name == "batch64x2k" else None)
     _log(f"block apply {name} nrhs={nrhs}")

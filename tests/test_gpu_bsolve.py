@@ -46,7 +46,8 @@ def _check(b, X, iters, rel, Bm, cols, systems=(0,)):
 
 
 @pytest.mark.parametrize("name,nrhs,cols", [("N1k", 16, range(16)), ("N1k", 48, (0, 17, 47)),
-                                            ("N8k", 32, (0, 11, 31)), ("N16k", 16, (0, 15))])
+                                            ("N8k", 32, (0, 11, 31)), ("N16k", 16, (0, 15)),
+                                            ("N8k", 96, (0, 50, 95)), ("N16k", 128, (0, 64, 127))])
 def test_block_solve_parity(name, nrhs, cols):
     b = make_config(name)
     _log(f"block solve {name} nrhs={nrhs}")
