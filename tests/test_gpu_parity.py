@@ -409,6 +409,27 @@ def test_resident_groups_of_systems(cfg):
     s.close()
 
 
+def test_ragged_groups_of_systems():
+    # 17 systems of 16 leaves (272 leaves, more than the CUs): one launch of 16
+    # whole systems, then one of a single system, for the single-pass apply and
+    # for the resident solve; every system against the oracle
+    batch = make_config("batch64x2k", batch=17)
+    _log("ragged groups batch17")
+    s = _solver(batch)
+    r = np.random.default_rng(18).standard_normal((batch.batch, batch.n)).astype(np.float32)
+    _check_apply(batch, s, r)
+    assert hpcg.hpcg_last_apply_path(s.handle) == hpcg.HPCG_APPLY_FUSED
+    res = s.solve(batch.b.reshape(-1), tol=batch.tol, maxit=batch.maxit)
+    assert res.status == hpcg.HPCG_OK, hpcg.hpcg_last_error(s.handle)
+    assert s.last_engine == hpcg.HPCG_ENGINE_PERSISTENT
+    for i in range(batch.batch):
+        sy = batch.system(i)
+        ref = oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b, (sy.U, sy.W, sy.g), batch.tol, batch.maxit)
+        assert abs(res.iterations[i] - ref.iterations) <= ITER_TOL, (i, res.iterations[i], ref.iterations)
+        assert res.relres[i] <= batch.tol
+    s.close()
+
+
 def test_engines_agree(cfg, oracle_solves):
     # each engine is deterministic; the graph engine and the persistent engine
     # reduce in different orders, so they agree to the iteration tolerance
