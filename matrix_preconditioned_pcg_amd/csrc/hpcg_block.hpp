@@ -315,14 +315,30 @@ __global__ __launch_bounds__(256) void k_spmv_block(const int* __restrict__ row_
   if (row >= nrows) return;
   const int c4 = (int)(idx - (size_t)row * groups) * 4;
   mf4 acc = {0, 0, 0, 0};
-  const int e1 = row_ptr[row + 1];
-  for (int e = row_ptr[row]; e < e1; ++e) {
-    const float a = val[e];
-    const mf4 x = *reinterpret_cast<const mf4*>(X + (size_t)col[e] * nrhs + c4);
-    acc.x = fmaf(a, x.x, acc.x);
-    acc.y = fmaf(a, x.y, acc.y);
-    acc.z = fmaf(a, x.z, acc.z);
-    acc.w = fmaf(a, x.w, acc.w);
+  const int e0 = row_ptr[row], e1 = row_ptr[row + 1];
+  // four entries per round: their indices, then their X rows, are all in
+  // flight together; the entries past the row's end are skipped
+  for (int e = e0; e < e1; e += 4) {
+    int c[4];
+    float a[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool in = e + u < e1;
+      c[u] = in ? col[e + u] : row;
+      a[u] = in ? val[e + u] : 0.f;
+    }
+    mf4 x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const mf4*>(X + (size_t)c[u] * nrhs + c4);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (e + u < e1) {
+        acc.x = fmaf(a[u], x[u].x, acc.x);
+        acc.y = fmaf(a[u], x[u].y, acc.y);
+        acc.z = fmaf(a[u], x[u].z, acc.z);
+        acc.w = fmaf(a[u], x[u].w, acc.w);
+      }
+    }
   }
   *reinterpret_cast<mf4*>(Y + (size_t)row * nrhs + c4) = acc;
 }
