@@ -19,7 +19,23 @@ __global__ __launch_bounds__(NT) void k_spmv(const int* __restrict__ row_ptr, co
   float acc = 0.f;
   if (row < nrows) {
     const int e1 = row_ptr[row + 1];
-    for (int e = row_ptr[row] + lr; e < e1; e += SPMV_TPR) acc = fmaf(val[e], x[col[e]], acc);
+    // two of this thread's entries per round, both column indices and then
+    // both x values in flight together; the sum keeps the entry order
+    for (int e = row_ptr[row] + lr; e < e1; e += 2 * SPMV_TPR) {
+      const int eb = e + SPMV_TPR;
+      const bool hb = eb < e1;
+      const int ca = col[e];
+      const float va = val[e];
+      int cb = ca;
+      float vb = 0.f;
+      if (hb) {
+        cb = col[eb];
+        vb = val[eb];
+      }
+      const float xa = x[ca], xb = x[cb];
+      acc = fmaf(va, xa, acc);
+      if (hb) acc = fmaf(vb, xb, acc);
+    }
   }
 #pragma unroll
   for (int o = 1; o < SPMV_TPR; o <<= 1) acc += __shfl_xor(acc, o);
