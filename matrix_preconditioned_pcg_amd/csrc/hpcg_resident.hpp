@@ -137,10 +137,13 @@ __device__ __forceinline__ double sum_partials_r(const double* part, int s, int 
 }
 
 // Iterations between exact restrictions of r (the others use the linear
-// update).  fp64 drift over 8 updates stays near 1e-15 of |r|; fp32 vectors
-// refresh every iteration.
+// update).  In fp64 each update adds at most the 2^-44 rounding of the
+// exchanged W^T q words, relative to alpha W^T q; over 16 updates, in which
+// ||r|| falls by far less than 2^20 on these systems, that stays far below
+// the fp32 factors' rounding relative to the current r.  fp32 vectors refresh
+// every iteration.
 template <typename T>
-constexpr int kRefresh = sizeof(T) == 8 ? 8 : 1;
+constexpr int kRefresh = sizeof(T) == 8 ? 16 : 1;
 
 // Restriction of the LDS vector v: U_k^T v into tout (LDS, complete) and
 // W_l[k]^T v into pout (global, [levels][K][RANK] of system s; skipped when
