@@ -141,9 +141,10 @@ __device__ __forceinline__ double sum_partials_r(const double* part, int s, int 
 // exchanged W^T q words, relative to alpha W^T q; over 16 updates, in which
 // ||r|| falls by far less than 2^20 on these systems, that stays far below
 // the fp32 factors' rounding relative to the current r.  fp32 vectors refresh
-// every iteration.
+// every second iteration: one update adds a rounding of the size fp32 vectors
+// already carry.
 template <typename T>
-constexpr int kRefresh = sizeof(T) == 8 ? 16 : 1;
+constexpr int kRefresh = sizeof(T) == 8 ? 16 : 2;
 
 // Restriction of the LDS vector v: U_k^T v into tout (LDS, complete) and
 // W_l[k]^T v into pout (global, [levels][K][RANK] of system s; skipped when
