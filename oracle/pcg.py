@@ -45,10 +45,23 @@ class PCGResult:
     history: list = field(default_factory=list)   # ||r_k|| / ||b|| for k = 1 ..
 
 
-def pcg(row_ptr, col, val, b, precond, tol: float, maxit: int, dtype=np.float64) -> PCGResult:
+def pcg(row_ptr, col, val, b, precond, tol: float, maxit: int, dtype=np.float64, store=None) -> PCGResult:
     """Solve A x = b.  precond is either a callable r -> M r or a tuple (U, W, g)
     of preconditioner factors applied with the structured apply.  Vectors and
-    scalars are carried in `dtype` (fp64 unless asked otherwise)."""
+    scalars are carried in `dtype` (fp64 unless asked otherwise).
+
+    store (e.g. np.float32): the solve vectors r, z, p and q are rounded to
+    this type each time one is formed, while every product, dot product,
+    scalar and x stay in `dtype`: the vector storage of the pages' precision
+    split read as fp32 vectors ("Hierarchical Transformer Preconditioning for
+    Interactive Physics Simulation", Supplementary section 7, "Mixed precision
+    split": float32 apply path, float64 scalar accumulators)."""
+    if store is None:
+        def keep(v):
+            return v
+    else:
+        def keep(v):
+            return np.asarray(v, dtype=store).astype(dtype)
     if callable(precond):
         apply = precond
     else:
@@ -70,30 +83,30 @@ def pcg(row_ptr, col, val, b, precond, tol: float, maxit: int, dtype=np.float64)
     def out(it, status, rel):
         return PCGResult(x, it, status, float(rel), true_relres(row_ptr, col, val, b, x, dtype), history)
 
-    z = np.asarray(apply(r), dtype=dtype)
+    z = keep(np.asarray(apply(r), dtype=dtype))
     p = z.copy()
     rz = dtype(r @ z)
     history = []
     if not (np.isfinite(rz) and rz > 0.0):
         return PCGResult(x, 0, "breakdown", 1.0, 1.0, history)
     for it in range(1, maxit + 1):
-        q = spmv(row_ptr, col, val, p, dtype)
+        q = keep(spmv(row_ptr, col, val, p, dtype))
         pq = dtype(p @ q)
         if not (np.isfinite(pq) and pq > 0.0):
             return out(it, "breakdown", norm(r) / bnorm)
         alpha = rz / pq
         x += alpha * p
-        r -= alpha * q
+        r = keep(r - alpha * q)
         rel = norm(r) / bnorm
         history.append(float(rel))
         if rel <= tol:
             return out(it, "converged", rel)
-        z = np.asarray(apply(r), dtype=dtype)
+        z = keep(np.asarray(apply(r), dtype=dtype))
         rz_new = dtype(r @ z)
         if not (np.isfinite(rz_new) and rz_new > 0.0):
             return out(it, "breakdown", rel)
         beta = rz_new / rz
-        p = z + beta * p
+        p = keep(z + beta * p)
         rz = rz_new
     return out(maxit, "not_converged", norm(r) / bnorm)
 

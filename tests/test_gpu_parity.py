@@ -9,9 +9,8 @@ scalars and x (fp32 vectors are an option, checked separately).  Bars:
   * Truncated PCG (a fixed number of steps, before rounding differences have
     grown): x and the residual agree with the fp64 oracle's to 1e-9 relative.
   * PCG to the tolerance: same outcome, iteration count within 2 of the
-    oracle's (on the tetrahedral system, within 2 of the band that rounding
-    alone produces), recursive residual <= tol and true residual
-    ||b - A x||/||b|| <= 1.05 tol, both engines.
+    oracle's on every configuration, recursive residual <= tol and true
+    residual ||b - A x||/||b|| <= 1.05 tol, both engines.
 The workloads are the five benchmark systems at full size plus small edge
 cases (one leaf, two leaves, levels below the maximum, odd batch sizes).
 """
@@ -61,7 +60,8 @@ def oracle_solves():
 
 
 def rounding_band(sy, tol, maxit, eps=1e-15, runs=4, seed=0):
-    """Range of CG iteration counts that rounding alone produces on one system.
+    """Range of CG iteration counts that rounding alone produces on one system
+    (a diagnostic printed when a count misses the bar; never the bar itself).
 
     Low end: the oracle run in extended precision (64-bit significand), the
     near-exact count.  High end: the fp64 oracle with every apply of M
@@ -69,7 +69,7 @@ def rounding_band(sy, tol, maxit, eps=1e-15, runs=4, seed=0):
     few runs.  On the tetrahedral system the first differences of 1e-16 grow by
     about four orders of magnitude every ten steps, so the count of a fp64 run
     depends on its summation order (extended 499, fp64 517, perturbed fp64
-    515-523); a GPU run with its own order is held to this band widened by 2.
+    515-523).
     """
     ext = oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b, (sy.U, sy.W, sy.g), tol, maxit,
                      dtype=np.longdouble).iterations
@@ -83,19 +83,13 @@ def rounding_band(sy, tol, maxit, eps=1e-15, runs=4, seed=0):
     return min([ext] + counts), max([ext] + counts)
 
 
-_BANDS = {}
-
-
-def _iter_band(batch, i, ref):
-    """Allowed iteration range: oracle +-2; on the tetrahedral system the
-    rounding band (rounding_band) widened by 2 on each side."""
-    lo, hi = ref.iterations, ref.iterations
-    if batch.meta.get("n_tets"):
-        key = (batch.name, i)
-        if key not in _BANDS:
-            _BANDS[key] = rounding_band(batch.system(i), batch.tol, batch.maxit)
-        lo, hi = min(lo, _BANDS[key][0]), max(hi, _BANDS[key][1])
-    return lo - ITER_TOL, hi + ITER_TOL
+def _check_count(batch, i, got, ref):
+    """The iteration bar: the oracle's count +-2 on every configuration."""
+    if abs(got - ref.iterations) <= ITER_TOL:
+        return
+    band = rounding_band(batch.system(i), batch.tol, batch.maxit)
+    raise AssertionError(f"system {i}: {got} iterations, oracle {ref.iterations} (+-{ITER_TOL}); "
+                         f"rounding band of the oracle {band}")
 
 
 def _solver(batch, levels=None):
@@ -299,8 +293,9 @@ def _check_solve(batch, res, refs):
         sy = batch.system(i)
         assert res.system_status[i] == hpcg.HPCG_SYS_CONVERGED, (i, res.system_status[i])
         assert ref.status == "converged"
-        lo, hi = _iter_band(batch, i, ref)
-        assert lo <= res.iterations[i] <= hi, (i, res.iterations[i], ref.iterations, lo, hi)
+        if batch.batch == 1:
+            _log(f"  {res.iterations[i]} iterations (oracle {ref.iterations})")
+        _check_count(batch, i, res.iterations[i], ref)
         assert res.relres[i] <= batch.tol
         x = res.x[i].cpu().numpy()
         tr = oracle.true_relres(sy.row_ptr, sy.col, sy.val, sy.b, x)
@@ -349,12 +344,14 @@ def test_truncated_solve_parity(cfg, name, engine):
     s.close()
 
 
-# fp32 vectors (the pages' split) hold the oracle's count on the grid systems;
-# on the tetrahedral system fp32 rounding of the SpMV or apply alone delays CG by
-# about a quarter (an fp32-rounding emulation of the loop takes 638-652 steps
-# against the fp64 oracle's 517) and leaves the true residual up to about 1.2x
-# the recursive one, so there convergence is required with the count inside
-# [oracle, 1.35 oracle] and the true residual within 2 tol.
+# fp32 vectors (the pages' split) hold the oracle's count on the grid systems.
+# On the tetrahedral system CG is so sensitive to rounding that fp32 storage of
+# the vectors alone costs about a quarter more steps: the oracle run with r, z,
+# p and q rounded to fp32 (store=np.float32, everything else fp64) needs ~640
+# against 517 in fp64, and this mode, whose apply and SpMV also accumulate in
+# fp32, ~670.  There the bar is documented as looser: convergence, a count
+# between the fp64 oracle's and 1.1 times the fp32-storage oracle's, and a
+# true residual within 2 tol.
 @pytest.mark.parametrize("name", NAMES)
 def test_solve_vec32_mode(cfg, oracle_solves, name):
     batch = cfg(name)
@@ -368,8 +365,11 @@ def test_solve_vec32_mode(cfg, oracle_solves, name):
         sy = batch.system(i)
         tr = oracle.true_relres(sy.row_ptr, sy.col, sy.val, sy.b, res.x[i].cpu().numpy())
         if batch.meta.get("n_tets"):
-            # fp32 vectors also open a gap between the recursive and the true residual
-            assert ref.iterations <= res.iterations[i] <= 1.35 * ref.iterations
+            ref32 = oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b, (sy.U, sy.W, sy.g), batch.tol, batch.maxit,
+                               store=np.float32)
+            _log(f"  tet4k fp32 vectors: {res.iterations[i]} iterations (oracle fp64 {ref.iterations}, "
+                 f"fp32 storage {ref32.iterations}), true relres {tr:.3e}")
+            assert ref.iterations <= res.iterations[i] <= 1.1 * ref32.iterations
             assert tr <= 2.0 * batch.tol, (i, tr)
         else:
             assert abs(res.iterations[i] - ref.iterations) <= ITER_TOL, (i, res.iterations[i], ref.iterations)
@@ -650,6 +650,55 @@ def test_resident_poll_limit(cfg, prec):
     for bad in (-1, (1 << 30) + 1):
         with pytest.raises(hpcg.HPCGError):
             s.set_option(hpcg.HPCG_OPT_POLL_LIMIT, bad)
+    s.close()
+
+
+@pytest.mark.parametrize("name", ["N1k", "N8k", "N16k"])
+def test_fused_apply_poll_limit(cfg, name):
+    # The single-pass apply with a bound of one re-poll per partner word: each
+    # call either gets every word in time (y bit-identical to a healthy call,
+    # status OK) or gives up, which hpcg_apply_status reports (and then
+    # clears), or which the next hpcg_solve reports.  Every kernel still exits
+    # normally; with the default bound restored the next apply is healthy and
+    # bit-identical, and so is the next solve.
+    batch = cfg(name)
+    _log(f"apply poll limit {name}")
+    s = _solver(batch)
+    r = np.random.default_rng(41).standard_normal(batch.batch * batch.n).astype(np.float32)
+    ref = s.apply_M(r).clone()
+    assert s.apply_status() == hpcg.HPCG_OK
+    assert hpcg.hpcg_last_apply_path(s.handle) == hpcg.HPCG_APPLY_FUSED
+    sref = s.solve(batch.b.reshape(-1), tol=batch.tol, maxit=batch.maxit)
+    s.set_option(hpcg.HPCG_OPT_APPLY_POLL_LIMIT, 1)
+    gave_up = 0
+    for _ in range(3):
+        y = s.apply_M(r)
+        st = s.apply_status()
+        if st == hpcg.HPCG_OK:
+            assert torch.equal(y, ref)
+        else:
+            assert st == hpcg.HPCG_ERR_HIP and "bounded partner wait" in hpcg.hpcg_last_error(s.handle)
+            gave_up += 1
+            assert s.apply_status() == hpcg.HPCG_OK        # the record was cleared
+    # a timed-out apply left unchecked is reported by the next solve
+    s.apply_M(r)
+    try:
+        res = s.solve(batch.b.reshape(-1), tol=batch.tol, maxit=batch.maxit)
+    except hpcg.HPCGError as err:
+        assert err.status == hpcg.HPCG_ERR_HIP and "single-pass" in str(err), err
+        gave_up += 1
+    else:
+        assert res.status == hpcg.HPCG_OK and torch.equal(res.x, sref.x)
+    _log(f"  {gave_up} of 4 tight applies gave up")
+    s.set_option(hpcg.HPCG_OPT_APPLY_POLL_LIMIT, 0)
+    assert s.apply_status() == hpcg.HPCG_OK
+    assert torch.equal(s.apply_M(r), ref)
+    assert s.apply_status() == hpcg.HPCG_OK
+    res = s.solve(batch.b.reshape(-1), tol=batch.tol, maxit=batch.maxit)
+    assert res.status == hpcg.HPCG_OK and res.iterations == sref.iterations and torch.equal(res.x, sref.x)
+    for bad in (-1, (1 << 30) + 1):
+        with pytest.raises(hpcg.HPCGError):
+            s.set_option(hpcg.HPCG_OPT_APPLY_POLL_LIMIT, bad)
     s.close()
 
 

@@ -134,3 +134,24 @@ def test_block_apply_is_dense_product(K, L, R, levels):
     R_blk = np.random.default_rng(5).standard_normal((K * L, 7))
     np.testing.assert_allclose(oracle.apply_M_block(U, W, g, R_blk), oracle.dense_M(U, W, g) @ R_blk,
                                rtol=1e-12, atol=1e-12 * np.abs(R_blk).max())
+
+
+def test_batch_apply_is_per_system_dense_product():
+    # three systems with their own factors, gates and inputs: every row of the
+    # batched apply must be that system's own entrywise M times its own r (an
+    # axis mix-up between systems, leaves or levels lands on another system's
+    # factors and fails)
+    K, L, R, levels, B = 4, 6, 2, 2, 3
+    fac = [_factors(K, L, R, levels, seed=70 + s) for s in range(B)]
+    U = np.stack([f[0] for f in fac])
+    W = np.stack([f[1] for f in fac])
+    g = np.stack([f[2] for f in fac])
+    r = np.random.default_rng(9).standard_normal((B, K * L))
+    y = oracle.apply_M_batch(U, W, g, r)
+    assert y.shape == (B, K * L)
+    N = K * L
+    for s in range(B):
+        M = np.array([[oracle.dense_M_entry(U[s], W[s], g[s], i, j) for j in range(N)] for i in range(N)])
+        np.testing.assert_allclose(y[s], M @ r[s], rtol=1e-12, atol=1e-12 * np.abs(M).sum())
+    # the systems really differ, so a swap would have been seen
+    assert np.abs(y[0] - y[1]).max() > 1e-3

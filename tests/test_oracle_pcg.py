@@ -123,13 +123,22 @@ def test_edge_cases():
 
 
 def test_batch_equals_per_system():
-    b = make_config("batch64x2k", batch=2)
+    # pcg_batch against scipy's independent PCG loop on each system's diagonal
+    # block, cut by hand from the batch's global (block-diagonal) CSR, with M
+    # applied from that system's own factors: a system or axis mix-up fails
+    b = make_config("batch64x2k", batch=3)
     res = oracle.pcg_batch(b)
-    for s in range(2):
-        sy = b.system(s)
-        r = oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b, (sy.U, sy.W, sy.g), b.tol, b.maxit)
-        assert r.iterations == res[s].iterations
-        np.testing.assert_array_equal(r.x, res[s].x)
+    A = scipy.sparse.csr_matrix((b.val.astype(np.float64), b.col, b.row_ptr), shape=(b.batch * b.n,) * 2)
+    for s in range(b.batch):
+        As = A[s * b.n:(s + 1) * b.n, s * b.n:(s + 1) * b.n]
+        assert A[s * b.n:(s + 1) * b.n].nnz == As.nnz          # block-diagonal batch
+        Mop = spla.LinearOperator((b.n, b.n), matvec=lambda v, s=s: oracle.apply_M(b.U[s], b.W[s], b.g[s], v))
+        rhs = b.b[s].astype(np.float64)
+        xs, its, info = _scipy_cg(As, rhs, b.tol, b.maxit, M=Mop)
+        assert info == 0 and res[s].status == "converged"
+        assert res[s].iterations == its, (s, res[s].iterations, its)
+        np.testing.assert_allclose(res[s].x, xs, rtol=1e-9, atol=1e-9 * np.abs(xs).max())
+    assert len({r.iterations for r in res}) > 1 or not np.allclose(res[0].x, res[1].x)
 
 
 def test_extended_precision_run():
@@ -209,3 +218,34 @@ def test_block_pcg_columns_are_independent_solves():
     A = oracle.dense_A(sy.row_ptr, sy.col, sy.val)
     for j in (0, 2):
         np.testing.assert_allclose(A @ res[j].x, Bm[:, j], atol=1e-7 * np.linalg.norm(Bm[:, j]))
+
+
+def test_fp32_vector_storage_option():
+    # store=np.float32 keeps r, z, p and q as fp32 values (the pages' fp32
+    # vectors) with fp64 products, scalars and x.  store=np.float64 changes
+    # nothing; an exact inverse still stops after one step (at a tolerance
+    # above the fp32 rounding of z times the condition number); a
+    # well-conditioned grid system keeps the fp64 count within 2; on the
+    # tetrahedral system the
+    # fp32 storage alone costs about a quarter more iterations (the reason the
+    # fp32-vector mode is not held to the fp64 count there).
+    sy = make_config("N1k").system(0)
+    pre = (sy.U, sy.W, sy.g)
+    d = oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b, pre, 1e-6, 1000)
+    same = oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b, pre, 1e-6, 1000, store=np.float64)
+    assert same.iterations == d.iterations and np.array_equal(same.x, d.x)
+    f = oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b, pre, 1e-6, 1000, store=np.float32)
+    assert f.status == "converged" and abs(f.iterations - d.iterations) <= 2
+    assert not np.array_equal(f.x, d.x)
+    np.testing.assert_allclose(f.x, d.x, rtol=0, atol=1e-4 * np.abs(d.x).max())
+    assert f.true_relres <= 1.1e-6
+    b = random_system(256, seed=4, leaf=32, rank=4)
+    s2 = b.system(0)
+    Ainv = np.linalg.inv(oracle.dense_A(s2.row_ptr, s2.col, s2.val))
+    one = oracle.pcg(s2.row_ptr, s2.col, s2.val, s2.b, lambda v: Ainv @ v, 1e-4, 10, store=np.float32)
+    assert one.iterations == 1
+    t = make_config("tet4k").system(0)
+    pre = (t.U, t.W, t.g)
+    d = oracle.pcg(t.row_ptr, t.col, t.val, t.b, pre, 1e-6, 2000)
+    f = oracle.pcg(t.row_ptr, t.col, t.val, t.b, pre, 1e-6, 2000, store=np.float32)
+    assert f.status == "converged" and f.iterations >= 1.15 * d.iterations, (f.iterations, d.iterations)
