@@ -7,9 +7,10 @@
 //     two rows of W_l[k] as float4 (rows tid/8 and tid/8 + 64, columns
 //     4(tid % 8)..);
 //   * its rows of r, q, z and p and its CSR rows live in LDS, x in registers;
-//   * only what other leaves need crosses workgroups: z and p (the SpMV halo),
-//     the per-leaf restrictions W_l[k]^T r_k and W_l[k]^T q_k, and the scalar
-//     partials.
+//   * only what other leaves need crosses workgroups: z (the SpMV halo; the
+//     halo's p = z + beta p is formed locally, beta being the same in every
+//     workgroup), the per-leaf restrictions W_l[k]^T r_k and W_l[k]^T q_k, and
+//     the scalar partials.
 //
 // No barrier inside an iteration.  Each value one workgroup needs from another
 // travels as a flagged word (the value's bits and the step it belongs to,
@@ -35,9 +36,11 @@
 // Coherence without cache maintenance.  Every value one workgroup writes for
 // another is stored and loaded with agent-scope accesses (sc1: written through
 // to, and read from, the point where all XCDs agree), so no L2 write-back or
-// invalidation is needed; a value written plainly (p, a refreshed W^T r) is
-// acknowledged before the flagged words that announce it are stored.  The
-// per-system barrier below remains for the set-up and the squared form.
+// invalidation is needed; a value written plainly (a refreshed W^T r) is
+// acknowledged by every thread that wrote it, and a workgroup barrier passed,
+// before the flagged partial words that announce it are stored (readers load
+// it only after seeing those words).  The per-system barrier below remains for
+// the set-up and the squared form.
 #pragma once
 #include "hpcg_kernels.hpp"
 #include "hpcg_leaf.hpp"
@@ -555,8 +558,9 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
   // of epoch ep_base + i: everything the next phase A reads from this leaf.
   auto publish = [&](double loc_rr, int i) {
     const unsigned e = B.ep_base + (unsigned)i;
-    // this workgroup's earlier stores (p of phase A, W^T r of a refresh) are
-    // acknowledged first: whoever sees these words sees those values too
+    // this workgroup's earlier stores (W^T r of a refresh) are acknowledged
+    // first, by every thread, and the barrier inside wg_sum2_r separates that
+    // from the partial words below: whoever sees those words sees W^T r too
     __builtin_amdgcn_s_waitcnt(0);
     double loc_rz = 0.0;
     if (tid < LEAF) {
@@ -625,18 +629,14 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
     const unsigned ez = B.ep_base + (unsigned)(it - 1);   // epoch of z and the partials of step it-1
     // ---------------- phase A (it) ----------------
     {
-      const T* pold = reinterpret_cast<const T*>((it & 1) ? B.p0 : B.p1);
-      T* pnew = reinterpret_cast<T*>((it & 1) ? B.p1 : B.p0);
       const bool first = (it == 1);
-      // the halo's z (flagged words) and p (plain: written before the last
-      // barrier) into LDS; wave 0 also collects the partials r.r and r.z
+      // the halo's z (flagged words) into LDS; wave 0 also collects the
+      // partials r.r and r.z.  The halo's p is not read from its owners: every
+      // workgroup of a system computes the same beta, so the copy of the
+      // halo's p that this workgroup keeps in pc (updated below with the
+      // owners' own formula) equals theirs bit for bit
       int bad = 0;
-      for (int h = tid; h < nh; h += NTR) {
-        const int c = hcolL[h];
-        const T pv = first ? T(0) : ld_c(pold + c);
-        zc[LEAF + h] = ll_get_z<T>(B, c, ez, bad);
-        pc[LEAF + h] = pv;
-      }
+      for (int h = tid; h < nh; h += NTR) zc[LEAF + h] = ll_get_z<T>(B, hcolL[h], ez, bad);
       if (tid < LEAF) {
         zc[tid] = sm.z[tid];
         pc[tid] = sm.p[tid];
@@ -683,11 +683,12 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
       if (lr == 0) {
         pn = first ? sm.z[row] : pdir<T>(sm.z[row], sm.p[row], beta);
         sm.q[row] = acc;
-        st_c(pnew + leaf0 + row, pn);
         loc = (double)pn * (double)acc;
       }
-      __syncthreads();                  // every SpMV read of sm.p is done
+      __syncthreads();                  // every SpMV read of sm.p and pc is done
       if (lr == 0) sm.p[row] = pn;
+      for (int h = tid; h < nh; h += NTR)
+        pc[LEAF + h] = first ? zc[LEAF + h] : pdir<T>(zc[LEAF + h], pc[LEAF + h], beta);
       // the slab restriction of q and the partial p.q, published as flagged
       // words (what the partners read)
       r_restrict_q_ll<T, LEV>(G, B, s, k, item, F, sm, loc, it & 1, q_tag(it), B.ep_base + (unsigned)it);
