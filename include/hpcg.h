@@ -130,6 +130,14 @@ typedef enum {
                                    diagnostic bound: small values make a healthy
                                    solve abort, which is how its error path is
                                    tested                                         */
+    HPCG_OPT_APPLY_POLL_LIMIT = 256, /* single-pass hpcg_apply_M: poll rounds of the
+                                   partners' flagged words before a workgroup
+                                   gives up, 1 .. 2^30; 0 restores the default
+                                   (2^20, about a second).  A run-out leaves that
+                                   apply's y undefined and is reported by
+                                   hpcg_apply_status (or the next hpcg_solve or
+                                   hpcg_estimate_spectrum); a diagnostic bound,
+                                   like HPCG_OPT_POLL_LIMIT                       */
     HPCG_OPT_LEAF_SPLIT = 8     /* workgroups per leaf in the apply kernels and the
                                    graph and streaming engines: 0 = automatic
                                    (default), else 1, 2, 4 or 8; a split whose LDS
@@ -170,8 +178,9 @@ typedef enum {
  * (HPCG_ERR_SHAPE when a system has more leaves than that).  A batch with
  * more leaves than the device has compute units runs as several such
  * launches, each over as many whole systems as fit.  The wait for a partner's
- * words is bounded (about a second): should other work hold the compute
- * units that long, the apply gives up and its output is undefined.
+ * words is bounded (HPCG_OPT_APPLY_POLL_LIMIT, about a second by default):
+ * should other work hold the compute units that long, the apply gives up, its
+ * output is undefined, and hpcg_apply_status reports it.
  * AUTO (default): FUSED where it fits, else STREAMING. */
 typedef enum {
     HPCG_APPLY_AUTO = 0,
@@ -183,15 +192,40 @@ typedef enum {
  * Factors and matrix values are fp32 and scalars and x are fp64 in both modes. */
 typedef enum {
     HPCG_PREC_VEC64 = 0,        /* r, z, p, q and every accumulation in fp64 (default) */
-    HPCG_PREC_VEC32 = 1         /* the pages' split: fp32 vectors and apply arithmetic */
+    HPCG_PREC_VEC32 = 1         /* fp32 vectors and apply arithmetic, the plain
+                                   reading of the pages' split ("Hierarchical
+                                   Transformer Preconditioning for Interactive
+                                   Physics Simulation", Supplementary sections 1
+                                   and 7, "Mixed precision split": float32
+                                   weights and apply path, float64 scalar
+                                   accumulators; the vectors' type is not
+                                   named).  On the grid systems it takes the
+                                   fp64 count +-2.  On the tetrahedral system
+                                   (P1 stiffness, 100:1 conductivity) CG is so
+                                   sensitive to rounding that storing any one of
+                                   r, z, p or q in fp32 costs about a quarter
+                                   more iterations: the fp64 oracle with only
+                                   that rounding added needs 630-641 steps
+                                   against 517, and this mode takes ~671, with a
+                                   true residual up to ~1.3 tol.  Use VEC64
+                                   where the fp64 count matters.               */
 } hpcg_precision;
 
 /* Bytes of device workspace hpcg_create needs for this partition and a CSR of
  * nnz_total stored entries (all systems together).  Returns 0 when the
- * partition is invalid.  The workspace must be 256-byte aligned. */
+ * partition is invalid.  The workspace must be 256-byte aligned.  The sizes
+ * follow the pages' apply-path layout ("Hierarchical Transformer
+ * Preconditioning for Interactive Physics Simulation", Supplementary section 2,
+ * "Apply-path tensor layout", and Table 3: K leaf blocks of L x L, K - 1
+ * tiles) with the per-level slabs of this library. */
 size_t hpcg_workspace_bytes(const hpcg_partition* part, int64_t nnz_total);
 
-/* Create a solver for one sparsity pattern and value set of A.
+/* Create a solver for one sparsity pattern and value set of A: the sparse SPD
+ * matrix that the simulator hands over in CSR ("Hierarchical Transformer
+ * Preconditioning for Interactive Physics Simulation", Supplementary section 1:
+ * the GPU SpMV uses the generator's CSR, and the SpMV of section 5 stage (iii)
+ * is the only sparse operation of the loop), with the leaf partition of
+ * Supplementary section 2 (L = 128, K = n / L, weak admissibility).
  *  part        partition and batch size (validated: HPCG_ERR_SHAPE).
  *  d_row_ptr   int32 [batch*n + 1], d_row_ptr[0] == 0, nondecreasing,
  *              d_row_ptr[batch*n] == nnz_total.
@@ -209,12 +243,19 @@ hpcg_status hpcg_create(const hpcg_partition* part, const int32_t* d_row_ptr,
                         void* d_workspace, size_t ws_bytes, void* stream,
                         hpcg_handle* out);
 
-/* Replace the matrix values (same pattern) without rebuilding the handle.
- * d_val float32 [nnz_total], copied in stream order. */
+/* Replace the matrix values (same pattern) without rebuilding the handle, as a
+ * simulator does from frame to frame ("Hierarchical Transformer
+ * Preconditioning for Interactive Physics Simulation", section 1: A changes
+ * every frame while the partition is reused).  d_val float32 [nnz_total], copied in stream
+ * order. */
 hpcg_status hpcg_set_values(hpcg_handle h, const float* d_val);
 
-/* Load the preconditioner factors (the stand-in for the pages' network output),
- * copied into the workspace in stream order:
+/* Load the preconditioner factors (the stand-in for the pages' network output:
+ * leaf factors U_k with blocks F_k = U_k U_k^T, "A Neural Hierarchical-Matrix
+ * Preconditioner for Real-Time GPU Solves", section 2 "Preconditioner";
+ * rank-32 off-diagonal tiles and the diagonal gate of "Hierarchical
+ * Transformer Preconditioning for Interactive Physics Simulation", section 4.4
+ * "Decoder"), copied into the workspace in stream order:
  *  d_leafU  float32 [batch][K][L][L]            U_k, row-major, row = node in leaf
  *  d_tileW  float32 [batch][levels][K][L][R]    slab of leaf k at level l: a slab
  *           of U_{l,j} when (k >> l) is even, of V_{l,j} when it is odd
@@ -243,11 +284,32 @@ hpcg_status hpcg_set_factors(hpcg_handle h, const float* d_leafU, const float* d
 hpcg_status hpcg_set_factors_bridge(hpcg_handle h, const float* d_leafF, const float* d_bridgeU,
                                     const float* d_bridgeV, const float* d_cores, const float* d_gate);
 
-/* y = M r for every system of the batch (asynchronous, stream-ordered).
- * d_r, d_y float32 [batch*n], must not alias. */
+/* y = M r for every system of the batch (asynchronous, stream-ordered): the
+ * preconditioner application of "Hierarchical Transformer Preconditioning for
+ * Interactive Physics Simulation", section 5 "Preconditioner Application",
+ * stage (i) (the diagonal leaf blocks as one batched product over leaves) and
+ * stage (ii) (restriction, strip aggregation, coupling and prolongation of
+ * eqs. (2)-(5)), plus the diagonal gate; M is never assembled.  The form option may make it H H or
+ * diag(A)^-1 instead.
+ *  d_r, d_y float32 [batch*n], must not alias.
+ * Returns an error only for bad arguments or a failed launch.  A single-pass
+ * apply whose bounded partner wait runs out (see hpcg_apply_path) still
+ * returns HPCG_OK here, since the call does not wait for the device: its y is
+ * undefined and hpcg_apply_status reports it. */
 hpcg_status hpcg_apply_M(hpcg_handle h, const float* d_r, float* d_y);
 
-/* y = A x for every system of the batch (asynchronous, stream-ordered).
+/* Synchronize the handle's stream and report whether any single-pass
+ * hpcg_apply_M since the last report gave up a bounded wait (HPCG_ERR_HIP,
+ * with text in hpcg_last_error; the record is then cleared) or not
+ * (HPCG_OK).  hpcg_solve and hpcg_estimate_spectrum make the same check at
+ * their final synchronization. */
+hpcg_status hpcg_apply_status(hpcg_handle h);
+
+/* y = A x for every system of the batch (asynchronous, stream-ordered): the
+ * CSR SpMV of "Hierarchical Transformer Preconditioning for Interactive
+ * Physics Simulation", section 5, stage (iii), the loop's only sparse
+ * operation.  fp32 values and vectors,
+ * entries of a row summed in stored order.
  * d_x, d_y float32 [batch*n], must not alias. */
 hpcg_status hpcg_spmv(hpcg_handle h, const float* d_x, float* d_y);
 
@@ -278,9 +340,15 @@ hpcg_status hpcg_apply_M_block(hpcg_handle h, const float* d_R, float* d_Y, int3
                                void* d_work, size_t work_bytes);
 hpcg_status hpcg_spmv_block(hpcg_handle h, const float* d_X, float* d_Y, int32_t nrhs);
 
-/* Solve A x = b for every system with x_0 = 0, stopping a system when its
- * recursively updated residual satisfies ||r_k||_2 <= tol * ||b||_2 (the pages'
- * ||r_k|| / ||r_0|| with r_0 = b), or after maxit iterations.
+/* Solve A x = b for every system with preconditioned conjugate gradients
+ * ("Hierarchical Transformer Preconditioning for Interactive Physics
+ * Simulation", project page, Introduction and Background, eq. (1); section 5
+ * "Single-graph capture": the whole iteration, apply, SpMV, vector updates
+ * and dot reductions, runs on the device without host dispatch), x_0 = 0,
+ * stopping a system when its
+ * recursively updated residual satisfies ||r_k||_2 <= tol * ||b||_2 (the
+ * pages' ||r_k|| / ||r_0|| with r_0 = b: Supplementary section 1,
+ * "Convergence criterion"), or after maxit iterations.
  *  d_b      float32 [batch*n]
  *  d_x      float64 [batch*n]  solution (written also when not converged)
  *  tol      > 0;  maxit >= 1
@@ -291,7 +359,9 @@ hpcg_status hpcg_spmv_block(hpcg_handle h, const float* d_X, float* d_Y, int32_t
  * HPCG_OPT_PRECISION.
  * Returns HPCG_OK when every system converged, HPCG_ERR_BREAKDOWN when any
  * system broke down, else HPCG_ERR_NOT_CONVERGED when any system ran out of
- * iterations.  Synchronizes the handle's stream before returning. */
+ * iterations; HPCG_ERR_HIP when a bounded wait of the solve ran out, or when an
+ * earlier single-pass hpcg_apply_M had (see hpcg_apply_status).  Synchronizes
+ * the handle's stream before returning. */
 hpcg_status hpcg_solve(hpcg_handle h, const float* d_b, double* d_x, double tol,
                        int32_t maxit, int32_t* h_iters, double* h_relres);
 
@@ -333,7 +403,9 @@ hpcg_status hpcg_solve_refined(hpcg_handle h, const float* d_b, double* d_x, dou
  *  d_work   device scratch of hpcg_block_solve_workspace_bytes(h, nrhs) bytes
  *  h_iters  [batch*nrhs] iterations per (system, column), system-major (may be NULL)
  *  h_relres [batch*nrhs] final recursive ||r|| / ||b|| (may be NULL)
- * Arithmetic: R, Z, P, Q fp32 (the block apply's), x and all scalars fp64.
+ * Arithmetic: R, Z, P, Q fp32 (the block apply's), x and all scalars fp64:
+ * the pages' split, so on the tetrahedral system the columns need about a
+ * quarter more iterations than fp64 PCG, as HPCG_PREC_VEC32 does.
  * Direct form only (HPCG_ERR_STATE otherwise).  Returns HPCG_ERR_BREAKDOWN or
  * HPCG_ERR_NOT_CONVERGED when some column ends so (x and counts still
  * written).  Records the iterations in a hipGraph, kept for repeated calls

@@ -46,7 +46,10 @@ constexpr size_t kMaxLds = 160 * 1024;
 
 // control words, each on its own 256-byte line
 constexpr unsigned kPollLimitDefault = 1u << 22;   // polls of one flagged word (resident engine)
-constexpr size_t kCtlBarrier = 0, kCtlAbort = 256, kCtlItbase = 512, kCtlReplays = 768, kCtlBytes = 1024;
+constexpr unsigned kApplyPollDefault = 1u << 20;   // poll rounds of the single-pass apply (about a second)
+// the apply's abort word sits beside the solve's (one 8-byte read covers both)
+constexpr size_t kCtlBarrier = 0, kCtlAbort = 256, kCtlApplyAbort = 260, kCtlItbase = 512, kCtlReplays = 768,
+                 kCtlBytes = 1024;
 
 constexpr int kMaxSplit = 8;   // workgroups per leaf in the streaming kernels
 
@@ -203,7 +206,7 @@ struct hpcg_ctx {
   int bs_nrhs = 0, bs_unroll = 0, bs_maxit = -1;
   double bs_tol = -1.0;
   SysState* h_st = nullptr;
-  int* h_ctl = nullptr;    // pinned copy of the abort flag
+  int* h_ctl = nullptr;    // pinned copy of the abort words (solve, apply)
   std::vector<int32_t> last_status;
   std::string err;
 };
@@ -233,6 +236,16 @@ hpcg_status check_launch(hpcg_ctx* h, const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(h, e, what);
   return HPCG_OK;
+}
+
+// The host has seen the single-pass apply's abort word set (after a
+// synchronization): clear it and report the undefined output.
+hpcg_status apply_timed_out(hpcg_ctx* h) {
+  HIP_OR_FAIL(h, hipMemsetAsync(h->B.apply_abort, 0, sizeof(int), h->stream));
+  HIP_OR_FAIL(h, hipStreamSynchronize(h->stream));
+  return fail(h, HPCG_ERR_HIP, "a bounded partner wait of an earlier single-pass hpcg_apply_M ran out (other work "
+                               "held the compute units, or HPCG_OPT_APPLY_POLL_LIMIT below the exchange latency): "
+                               "that apply's output is undefined");
 }
 
 // Raise a kernel's dynamic-LDS limit when it needs more than the default.
@@ -541,6 +554,7 @@ hpcg_status hpcg_create(const hpcg_partition* part, const int32_t* d_row_ptr, co
   B.st = reinterpret_cast<SysState*>(w + lay.st);
   B.barrier = reinterpret_cast<unsigned*>(w + lay.ctl + kCtlBarrier);
   B.abort_flag = reinterpret_cast<int*>(w + lay.ctl + kCtlAbort);
+  B.apply_abort = reinterpret_cast<int*>(w + lay.ctl + kCtlApplyAbort);
   B.itbase = reinterpret_cast<int*>(w + lay.ctl + kCtlItbase);
   B.replays = reinterpret_cast<int*>(w + lay.ctl + kCtlReplays);
   B.wgflag = reinterpret_cast<unsigned*>(w + lay.wgflag);
@@ -553,6 +567,7 @@ hpcg_status hpcg_create(const hpcg_partition* part, const int32_t* d_row_ptr, co
   B.pqll = reinterpret_cast<unsigned long long*>(w + lay.pqll);
   B.ep_base = 1u;
   B.poll_limit = kPollLimitDefault;
+  B.apply_poll_limit = kApplyPollDefault;
   B.llw = reinterpret_cast<unsigned long long*>(w + lay.llw);
   B.lle = reinterpret_cast<unsigned*>(w + lay.lle);
   B.lly = reinterpret_cast<unsigned long long*>(w + lay.lly);
@@ -804,6 +819,14 @@ hpcg_status apply_H(hpcg_ctx* h, const float* d_r, float* d_y) {
   return check_launch(h, "hpcg_apply_M launch");
 }
 }  // namespace
+
+hpcg_status hpcg_apply_status(hpcg_handle h) {
+  if (!h) return fail(nullptr, HPCG_ERR_INVALID_ARG, "handle is NULL");
+  HIP_OR_FAIL(h, hipMemcpyAsync(h->h_ctl + 1, h->B.apply_abort, sizeof(int), hipMemcpyDeviceToHost, h->stream));
+  HIP_OR_FAIL(h, hipStreamSynchronize(h->stream));
+  if (h->h_ctl[1]) return apply_timed_out(h);
+  return HPCG_OK;
+}
 
 hpcg_status hpcg_spmv(hpcg_handle h, const float* d_x, float* d_y) {
   if (!h) return fail(nullptr, HPCG_ERR_INVALID_ARG, "handle is NULL");
@@ -1160,11 +1183,12 @@ hpcg_status solve_core(hpcg_ctx* h, const float* d_b, double* d_x, double tol, i
   s = check_launch(h, "copy-out launch");
   if (s != HPCG_OK) return s;
   HIP_OR_FAIL(h, hipMemcpyAsync(h->h_st, h->B.st, (size_t)G.B * sizeof(SysState), hipMemcpyDeviceToHost, h->stream));
-  HIP_OR_FAIL(h, hipMemcpyAsync(h->h_ctl, h->B.abort_flag, sizeof(int), hipMemcpyDeviceToHost, h->stream));
+  HIP_OR_FAIL(h, hipMemcpyAsync(h->h_ctl, h->B.abort_flag, 2 * sizeof(int), hipMemcpyDeviceToHost, h->stream));
   HIP_OR_FAIL(h, hipStreamSynchronize(h->stream));
-  if (*h->h_ctl)
+  if (h->h_ctl[0])
     return fail(h, HPCG_ERR_HIP, "a bounded wait of the persistent solve ran out (workgroups not co-resident, "
                                  "or HPCG_OPT_POLL_LIMIT below the exchange latency)");
+  if (h->h_ctl[1]) return apply_timed_out(h);
   return HPCG_OK;
 }
 
@@ -1371,6 +1395,10 @@ hpcg_status hpcg_estimate_spectrum(hpcg_handle h, int32_t steps, double* h_lmin,
     beta.push_back(bn);
     for (size_t i = 0; i < N; ++i) v[i] = w[i] / bn;
   }
+  {
+    hpcg_status s = hpcg_apply_status(h);   // every apply above waited within its bound
+    if (s != HPCG_OK) return s;
+  }
   beta.resize(alpha.size() > 0 ? alpha.size() - 1 : 0);
   if (h_lmin) *h_lmin = tridiag_eig(alpha, beta, 0);
   if (h_lmax) *h_lmax = tridiag_eig(alpha, beta, (int)alpha.size() - 1);
@@ -1402,6 +1430,10 @@ hpcg_status hpcg_set_option(hpcg_handle h, int32_t option, int32_t value) {
     case HPCG_OPT_POLL_LIMIT:
       if (value < 0 || value > (1 << 30)) return fail(h, HPCG_ERR_INVALID_ARG, "poll limit must be 0 .. 2^30");
       h->B.poll_limit = value == 0 ? kPollLimitDefault : (unsigned)value;
+      return HPCG_OK;
+    case HPCG_OPT_APPLY_POLL_LIMIT:
+      if (value < 0 || value > (1 << 30)) return fail(h, HPCG_ERR_INVALID_ARG, "apply poll limit must be 0 .. 2^30");
+      h->B.apply_poll_limit = value == 0 ? kApplyPollDefault : (unsigned)value;
       return HPCG_OK;
     case HPCG_OPT_FALLBACK:
       if (value != 0 && value != 1) return fail(h, HPCG_ERR_INVALID_ARG, "fallback must be 0 or 1");

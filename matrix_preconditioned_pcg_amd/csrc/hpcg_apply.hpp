@@ -61,9 +61,11 @@ __global__ __launch_bounds__(NT) void k_spmv(const int* __restrict__ row_ptr, co
 // start); the words hold the previous call's epoch until overwritten.  A
 // reader therefore polls exactly the words it needs, and a workgroup waits for
 // its partners only, for about one memory round trip after the last of them
-// has written.  The polls are bounded: past the bound the abort flag is raised
-// and the output is undefined (only if other work holds the device's compute
-// units for about a second).
+// has written.  The polls are bounded (B.apply_poll_limit, about a second by
+// default): past the bound the workgroup raises the apply's own abort word,
+// which stays set until the host reads it, and finishes with whatever words
+// it has, so the output is undefined but every workgroup exits and every
+// leaf's epoch still advances by one (the next call is consistent).
 template <int LEV>
 __device__ __forceinline__ void gather_partners_ll(const Geom& G, const Bufs& B, int s, int k, unsigned want,
                                                    float* stage) {
@@ -102,8 +104,8 @@ __device__ __forceinline__ void gather_partners_ll(const Geom& G, const Bufs& B,
 #pragma unroll
       for (int j = 0; j < WPT; ++j)
         if ((pending & (1u << j)) && (unsigned)(v[j] >> 32) == want) pending &= ~(1u << j);
-      if (++polls > (1u << 20)) {
-        st_c(B.abort_flag, 1);
+      if (pending && ++polls > B.apply_poll_limit) {
+        st_c(B.apply_abort, 1);
         break;
       }
     }
@@ -209,8 +211,8 @@ __device__ __forceinline__ void gather_partners_diag_ll(const Geom& G, const Buf
 #pragma unroll
     for (int j = 0; j < WPT; ++j)
       if ((pending & (1u << j)) && (unsigned)(v[j] >> 32) == want) pending &= ~(1u << j);
-    if (++polls > (1u << 20)) {
-      st_c(B.abort_flag, 1);
+    if (pending && ++polls > B.apply_poll_limit) {
+      st_c(B.apply_abort, 1);
       break;
     }
   }

@@ -109,6 +109,8 @@ struct Bufs {
   unsigned* lle;       // fused apply: [B*K] calls completed per leaf (the epoch)
   unsigned long long* lly;  // split apply: [B*K][LEAF] U_k U_k^T r as (value, epoch) words
   int* abort_flag;     // set when a barrier wait exceeds its bound
+  int* apply_abort;    // single-pass apply: set when a partner poll exceeds apply_poll_limit;
+                       // cleared only by the host once it has read it
   int* itbase;         // graph engine: absolute iteration of the replay's first step
   int* replays;        // graph engine: replays finished
   void* w;             // [B*n] H r in the squared form
@@ -123,6 +125,7 @@ struct Bufs {
   unsigned long long* pqll; // resident engine: [2][B*K][2] p.q partials as (word, epoch) pairs by step parity
   unsigned ep_base;    // resident engine: epoch of this solve's z0 (z of step i has ep_base + i)
   unsigned poll_limit; // resident engine: polls of one flagged word before the solve aborts
+  unsigned apply_poll_limit;  // single-pass apply: poll rounds before a workgroup gives up
   int form;            // FORM_*
   double tol;
   int maxit;

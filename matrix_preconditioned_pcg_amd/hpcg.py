@@ -49,6 +49,7 @@ HPCG_OPT_FORM = 32
 
 HPCG_OPT_FALLBACK = 64
 HPCG_OPT_POLL_LIMIT = 128
+HPCG_OPT_APPLY_POLL_LIMIT = 256
 
 HPCG_FORM_DIRECT = 0
 HPCG_FORM_SQUARED = 1
@@ -100,6 +101,7 @@ def lib() -> ctypes.CDLL:
         "hpcg_set_factors": (i32, [vp, vp, vp, vp]),
         "hpcg_set_factors_bridge": (i32, [vp, vp, vp, vp, vp, vp]),
         "hpcg_apply_M": (i32, [vp, vp, vp]),
+        "hpcg_apply_status": (i32, [vp]),
         "hpcg_spmv": (i32, [vp, vp, vp]),
         "hpcg_block_workspace_bytes": (sz, [vp, i32]),
         "hpcg_apply_M_block": (i32, [vp, vp, vp, i32, vp, sz]),
@@ -227,6 +229,12 @@ def hpcg_set_factors_bridge(h, part: hpcg_partition, F, Ub, Vb, Bc, g):
 def hpcg_apply_M(h, part: hpcg_partition, r, y):
     N = part.n * part.batch
     _check(lib().hpcg_apply_M(h, _ptr(r, torch.float32, N, "r"), _ptr(y, torch.float32, N, "y")), h)
+
+
+def hpcg_apply_status(h) -> int:
+    """Synchronizes; returns the status code (HPCG_ERR_HIP when an earlier
+    single-pass apply gave up a bounded wait), without raising."""
+    return int(lib().hpcg_apply_status(h))
 
 
 def hpcg_spmv(h, part: hpcg_partition, x, y):
@@ -417,6 +425,11 @@ class Solver:
         y = torch.empty_like(r) if y is None else y
         hpcg_apply_M(self.handle, self.part, r, y)
         return y
+
+    def apply_status(self) -> int:
+        """HPCG_OK, or HPCG_ERR_HIP if a single-pass apply since the last call
+        gave up its bounded wait (synchronizes the stream)."""
+        return hpcg_apply_status(self.handle)
 
     def spmv(self, x, y=None):
         x = self._vec(x)
