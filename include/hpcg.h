@@ -340,6 +340,20 @@ hpcg_status hpcg_apply_M_block(hpcg_handle h, const float* d_R, float* d_Y, int3
                                void* d_work, size_t work_bytes);
 hpcg_status hpcg_spmv_block(hpcg_handle h, const float* d_X, float* d_Y, int32_t nrhs);
 
+/* hpcg_apply_M_block without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same kernels and result as
+ * hpcg_apply_M_block; the per-leaf restrictions and their half sums live in a
+ * fixed scratch of 32 MiB that the library holds on every GPU it runs on until
+ * the process ends (its address is looked up at hpcg_create).  Limit: 2 *
+ * batch * levels * K * 32 * nrhs * 4 bytes must fit in it (e.g. n = 16,384
+ * with nrhs <= 128, or n = 8,192 with nrhs <= 256); larger calls return
+ * HPCG_ERR_WORKSPACE.  Allocates nothing and launches only kernels.  Every
+ * call on a GPU shares that GPU's scratch and leaves it as it was written:
+ * calls that overlap in time on one GPU (other streams, other handles, other
+ * threads) race and must be ordered by the caller. */
+hpcg_status hpcg_apply_M_block_noalloc(hpcg_handle h, const float* d_R, float* d_Y, int32_t nrhs);
+
 /* Solve A x = b for every system with preconditioned conjugate gradients
  * ("Hierarchical Transformer Preconditioning for Interactive Physics
  * Simulation", project page, Introduction and Background, eq. (1); section 5

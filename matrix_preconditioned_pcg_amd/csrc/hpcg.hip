@@ -159,6 +159,14 @@ thread_local std::string g_create_error;
 
 }  // namespace
 
+// Scratch of the allocation-free block apply: the per-leaf restrictions Q and
+// their half sums H of one call (each block_half_bytes).  One copy per GPU,
+// held until the process ends; every call on that GPU shares it.  Host code
+// never uses the array's name as an address: the device address of each GPU's
+// copy comes from hipGetSymbolAddress at set-up (scratch_address).
+constexpr size_t kNoAllocScratchBytes = 32u << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
 struct hpcg_ctx {
   hpcg_partition part{};
   int64_t nnz = 0;
@@ -207,6 +215,7 @@ struct hpcg_ctx {
   double bs_tol = -1.0;
   SysState* h_st = nullptr;
   int* h_ctl = nullptr;    // pinned copy of the abort words (solve, apply)
+  char* d_scratch = nullptr;   // this device's copy of `scratch`
   std::vector<int32_t> last_status;
   std::string err;
 };
@@ -236,6 +245,25 @@ hpcg_status check_launch(hpcg_ctx* h, const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(h, e, what);
   return HPCG_OK;
+}
+
+// Device address of this device's copy of `scratch`, looked up once per
+// device (with that device current) and kept.
+hipError_t scratch_address(int dev, char** out) {
+  static std::mutex mu;
+  static std::vector<std::pair<int, char*>> known;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto& k : known)
+    if (k.first == dev) {
+      *out = k.second;
+      return hipSuccess;
+    }
+  void* ptr = nullptr;
+  hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  known.emplace_back(dev, reinterpret_cast<char*>(ptr));
+  *out = reinterpret_cast<char*>(ptr);
+  return hipSuccess;
 }
 
 // The host has seen the single-pass apply's abort word set (after a
@@ -521,6 +549,7 @@ hpcg_status hpcg_create(const hpcg_partition* part, const int32_t* d_row_ptr, co
   hipDeviceProp_t prop;
   CREATE_HIP(hipGetDeviceProperties(&prop, dev));
   h->num_cu = prop.multiProcessorCount;
+  CREATE_HIP(scratch_address(dev, &h->d_scratch));
   int max_lds = 0;
   CREATE_HIP(hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev));
   h->max_lds = max_lds > 0 ? (size_t)max_lds : 65536;
@@ -945,6 +974,27 @@ hpcg_status hpcg_apply_M_block(hpcg_handle h, const float* d_R, float* d_Y, int3
                                      reinterpret_cast<float*>(wk + half), h->stream);
   if (s != HPCG_OK) return s;
   return check_launch(h, "hpcg_apply_M_block launch");
+}
+
+hpcg_status hpcg_apply_M_block_noalloc(hpcg_handle h, const float* d_R, float* d_Y, int32_t nrhs) {
+  if (!h) return fail(nullptr, HPCG_ERR_INVALID_ARG, "handle is NULL");
+  if (!d_R || !d_Y) return fail(h, HPCG_ERR_INVALID_ARG, "block pointer is NULL");
+  if (d_R == d_Y) return fail(h, HPCG_ERR_INVALID_ARG, "d_R and d_Y must not alias");
+  if (!block_nrhs_ok(nrhs)) return fail(h, HPCG_ERR_SHAPE, "nrhs must be a multiple of 16 in [16, 1024]");
+  if ((reinterpret_cast<uintptr_t>(d_R) | reinterpret_cast<uintptr_t>(d_Y)) % 16)
+    return fail(h, HPCG_ERR_INVALID_ARG, "d_R and d_Y must be 16-byte aligned");
+  if (!h->factors_set) return fail(h, HPCG_ERR_STATE, "hpcg_set_factors has not been called");
+  if (h->B.form != FORM_DIRECT) return fail(h, HPCG_ERR_STATE, "the block apply runs the direct form (M = H) only");
+  const size_t half = block_half_bytes(h, nrhs);
+  if (h->G.levels > 0 && 2 * half > kNoAllocScratchBytes)
+    return fail(h, HPCG_ERR_WORKSPACE,
+                "allocation-free block apply: batch * levels * K * 32 * nrhs * 4 bytes, twice, exceed its fixed "
+                "32 MiB scratch; use hpcg_apply_M_block with a caller workspace");
+  if (!h->d_scratch) return fail(h, HPCG_ERR_STATE, "scratch address unknown");
+  hpcg_status s = launch_block_apply(h, nrhs, d_R, d_Y, reinterpret_cast<float*>(h->d_scratch),
+                                     reinterpret_cast<float*>(h->d_scratch + half), h->stream);
+  if (s != HPCG_OK) return s;
+  return check_launch(h, "hpcg_apply_M_block_noalloc launch");
 }
 
 hpcg_status hpcg_spmv_block(hpcg_handle h, const float* d_X, float* d_Y, int32_t nrhs) {

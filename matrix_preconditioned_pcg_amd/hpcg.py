@@ -106,6 +106,7 @@ def lib() -> ctypes.CDLL:
         "hpcg_block_workspace_bytes": (sz, [vp, i32]),
         "hpcg_apply_M_block": (i32, [vp, vp, vp, i32, vp, sz]),
         "hpcg_spmv_block": (i32, [vp, vp, vp, i32]),
+        "hpcg_apply_M_block_noalloc": (i32, [vp, vp, vp, i32]),
         "hpcg_solve": (i32, [vp, vp, vp, dbl, i32, P(i32), P(dbl)]),
         "hpcg_last_solve_status": (i32, [vp, P(i32)]),
         "hpcg_solve_refined": (i32, [vp, vp, vp, dbl, i32, dbl, i32, P(i32), P(i32), P(dbl)]),
@@ -254,6 +255,13 @@ def hpcg_apply_M_block(h, part: hpcg_partition, R, Y, nrhs: int, work=None):
     wp, wb = (None, 0) if work is None else (work.data_ptr(), work.numel())
     _check(lib().hpcg_apply_M_block(h, _ptr(R, torch.float32, N * nrhs, "R"), _ptr(Y, torch.float32, N * nrhs, "Y"),
                                     int(nrhs), wp, wb), h)
+
+
+def hpcg_apply_M_block_noalloc(h, part: hpcg_partition, R, Y, nrhs: int):
+    """hpcg_apply_M_block with the library's fixed scratch instead of a caller workspace."""
+    N = part.n * part.batch
+    _check(lib().hpcg_apply_M_block_noalloc(h, _ptr(R, torch.float32, N * nrhs, "R"),
+                                            _ptr(Y, torch.float32, N * nrhs, "Y"), int(nrhs)), h)
 
 
 def hpcg_spmv_block(h, part: hpcg_partition, X, Y, nrhs: int):
