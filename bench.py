@@ -9,11 +9,16 @@ workload is the N = 8,192 system (3D 7-point variable-coefficient Poisson on a
 16 x 16 x 32 Morton-ordered grid, K = 64 leaves, 6 tile levels).
 
 Printed: one JSON line on stdout.  `value` is ms per solve (lower is better).
-`roofline` covers the M-apply + SpMV pair: `reps` pairs are captured into one
-graph on the library's stream and replayed between HIP events on that stream;
-achieved = algorithmic bytes (each factor, matrix entry and vector read or
-written once per call) / GPU time per pair, against MI355X's 8 TB/s HBM peak.
-`cpu_baseline` times the fp64 numpy oracle on a bounded sample on host cores.
+`roofline` covers the dominant kernel of the metric's apply + SpMV pair, the
+single-pass M-apply: `reps` calls are captured into one graph on the library's
+stream and replayed between HIP events on that stream; achieved = algorithmic
+bytes (each factor, gate and vector entry read or written once per call) / GPU
+time per call, against MI355X's 8 TB/s HBM peak.  Measured warm (the same
+factors call after call, served from the Infinity Cache) and cold (factors of
+enough copies cycled that they come from HBM), each beside the read ceiling of
+one launch over the same bytes from the same place (hpcg_read_probe).  The
+pair itself is in `roofline.apply_spmv`.  `cpu_baseline` times the plain C
+fp64 oracle on host cores (1 thread and all threads).
 """
 
 from __future__ import annotations
@@ -39,6 +44,15 @@ def apply_bytes(n: int, K: int, levels: int, B: int = 1) -> int:
     """Algorithmic bytes of one M-apply: leaf factors, level slabs, gate, r in, y out."""
     L, R = 128, 32
     return B * 4 * (n * L + n * R * levels + n) + B * 8 * n
+
+
+def bridge_apply_bytes(n: int, K: int, levels: int, B: int = 1) -> int:
+    """Algorithmic bytes of one M-apply in the pages' bridge format: leaf
+    factors, the two bridges per leaf, one R x R core per tile, gate, r in, y
+    out (the factor part is the packed width of Supplementary Table 3)."""
+    L, R = 128, 32
+    cores = sum(K >> (l + 1) for l in range(levels))
+    return B * 4 * (n * L + (2 * n * R if levels else 0) + cores * R * R + n) + B * 8 * n
 
 
 def block_apply_flops(n: int, levels: int, nrhs: int, B: int = 1) -> int:
@@ -141,25 +155,52 @@ def time_graph(fn, reps, stream, torch, replays=5):
     return float(np.median(out))
 
 
-def cpu_baseline(batch, budget_s=12.0):
-    import oracle
+def cpu_model() -> str:
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(batch, budget_s=25.0):
+    """The plain C fp64 oracle (oracle/c/pcg_oracle.c) solving the workload on
+    host cores: median of up to 5 timed solves after one warm-up, at one
+    thread and at every thread OpenMP gets (the box's share of cores); the
+    number of solves shrinks so that the whole leg stays near budget_s."""
+    from oracle import c_oracle
     sy = batch.system(0)
-    t0 = time.perf_counter()
-    solves = 0
-    while True:
-        oracle.pcg(sy.row_ptr, sy.col, sy.val, sy.b, (sy.U, sy.W, sy.g), batch.tol, batch.maxit)
-        solves += 1
-        if time.perf_counter() - t0 > budget_s or solves >= 20:
-            break
-    ms = (time.perf_counter() - t0) * 1e3 / solves
-    return {"value": round(ms, 3), "unit": "ms/solve", "cores": int(threads), "kind": "oracle",
-            "sample": f"{solves} complete fp64 solves of the {batch.name} system (numpy oracle, "
-                      f"{batch.n} unknowns)"}
+    args = (sy.row_ptr, sy.col, sy.val, sy.b, sy.U, sy.W, sy.g, batch.tol, batch.maxit)
+    all_threads = c_oracle.max_threads()
+    per_iter_bytes = apply_bytes(batch.n, batch.K, batch.levels) + spmv_bytes(batch.n, len(sy.col))
+    out = {}
+    for label, threads in (("one_thread", 1), ("all_threads", all_threads)):
+        c_oracle.set_threads(threads)
+        t0 = time.perf_counter()
+        _x, it, st, _rel = c_oracle.pcg(*args)          # warm-up
+        first = time.perf_counter() - t0
+        reps = int(max(1, min(5, (budget_s / 2 - first) // max(first, 1e-3))))
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            _x, it, st, _rel = c_oracle.pcg(*args)
+            ts.append(time.perf_counter() - t0)
+        ms = float(np.median(ts)) * 1e3
+        out[label] = {"threads": threads, "ms_per_solve": round(ms, 2), "solves_timed": reps, "iterations": it,
+                      "status": st, "iterations_per_s": round(it / ms * 1e3, 1),
+                      "apply_spmv_gbs": round(it * per_iter_bytes / ms / 1e6, 2)}
+    c_oracle.set_threads(all_threads)
+    best = out["all_threads"]
+    return {"value": best["ms_per_solve"], "unit": "ms/solve", "cores": best["threads"], "kind": "oracle",
+            "sample": f"median of {best['solves_timed']} complete fp64 solves of the {batch.name} system "
+                      f"({batch.n} unknowns, {best['iterations']} iterations) by the plain C oracle after one "
+                      f"warm-up, at {best['threads']} OpenMP threads; one-thread figure beside it",
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+            "iterations_per_s": best["iterations_per_s"], "one_thread": out["one_thread"],
+            "all_threads": out["all_threads"]}
 
 
 def single_pass_kernel(batch):
@@ -255,9 +296,10 @@ def main(argv=None):
         return out
 
     def measure_cold(batch, target_bytes=640 << 20):
-        """Apply + SpMV pairs cycling over enough independent copies of the
-        system (own workspace, own factor copy) that together they exceed the
-        256 MB Infinity Cache: every pair then fetches its factors from HBM."""
+        """Apply + SpMV pairs, and applies alone, cycling over enough
+        independent copies of the system (own workspace, own factor copy) that
+        together they exceed the 256 MB Infinity Cache: every call then
+        fetches its factors from HBM."""
         ab = apply_bytes(batch.n, batch.K, batch.levels, batch.batch)
         sb = spmv_bytes(batch.n, batch.nnz, batch.batch)
         copies = max(2, int(np.ceil(target_bytes / (ab + sb))))
@@ -279,12 +321,52 @@ def main(argv=None):
             r, y, q = vecs[i]
             hpcg.hpcg_spmv(solvers[i].handle, solvers[i].part, r, q)
             hpcg.hpcg_apply_M(solvers[i].handle, solvers[i].part, r, y)
+
+        def apply_only():
+            i = state["i"] % copies
+            state["i"] += 1
+            r, y, _q = vecs[i]
+            hpcg.hpcg_apply_M(solvers[i].handle, solvers[i].part, r, y)
         with torch.cuda.stream(stream):
             us = time_graph(pair, 2 * copies, stream, torch)
+            us_apply = time_graph(apply_only, 2 * copies, stream, torch)
         for sv in solvers:
             sv.close()
         return {"copies": copies, "bytes_cycled": int(copies * (ab + sb)), "apply_spmv_us": round(us, 3),
-                "achieved": round((ab + sb) / us / 1e3, 1), "frac": round((ab + sb) / us / 1e3 / HBM_PEAK_GBS, 4)}
+                "achieved": round((ab + sb) / us / 1e3, 1), "frac": round((ab + sb) / us / 1e3 / HBM_PEAK_GBS, 4),
+                "apply_us": round(us_apply, 3), "apply_gbs": round(ab / us_apply / 1e3, 1),
+                "apply_frac": round(ab / us_apply / 1e3 / HBM_PEAK_GBS, 4)}
+
+    def measure_read_ceiling(nbytes, target_bytes=640 << 20):
+        """The fastest one-launch read of nbytes (hpcg_read_probe, best of a
+        few grid sizes): warm = the same bytes launch after launch (Infinity
+        Cache), cold = launches cycling over buffers that together exceed it
+        (HBM)."""
+        nbytes = (nbytes + 15) // 16 * 16
+        copies = max(2, int(np.ceil(target_bytes / nbytes)))
+        bufs = [torch.ones(nbytes // 4, device="cuda", dtype=torch.float32) for _ in range(copies)]
+        best = {"warm_us": None, "cold_us": None}
+        grids = (256, 512, 1024, 2048)
+        sinks = {g: torch.empty(g, device="cuda", dtype=torch.float32) for g in grids}
+        state = {"i": 0}
+        with torch.cuda.stream(stream):
+            for g in grids:
+                warm = time_graph(lambda: hpcg.hpcg_read_probe(bufs[0], nbytes, sinks[g], g, stream),
+                                  args.reps, stream, torch)
+
+                def cyc():
+                    i = state["i"] % copies
+                    state["i"] += 1
+                    hpcg.hpcg_read_probe(bufs[i], nbytes, sinks[g], g, stream)
+                cold = time_graph(cyc, 2 * copies, stream, torch)
+                if best["warm_us"] is None or warm < best["warm_us"]:
+                    best.update(warm_us=warm, warm_grid=g)
+                if best["cold_us"] is None or cold < best["cold_us"]:
+                    best.update(cold_us=cold, cold_grid=g)
+        del bufs
+        return {"bytes": nbytes, "warm_us": round(best["warm_us"], 3), "warm_gbs": round(nbytes / best["warm_us"] / 1e3, 1),
+                "warm_grid": best["warm_grid"], "cold_us": round(best["cold_us"], 3),
+                "cold_gbs": round(nbytes / best["cold_us"] / 1e3, 1), "cold_grid": best["cold_grid"]}
 
     def measure_block(name):
         """Block apply M R on the matrix cores with the pages' probe width
@@ -379,12 +461,22 @@ def main(argv=None):
                             "apply_us": round(o["apply_us"], 3), "spmv_us": round(o["spmv_us"], 3),
                             "apply_spmv_us": round(o["pair_us"], 3),
                             "apply_spmv_gbs": round(o["pair_gbs"], 1),
-                            "apply_spmv_frac": round(o["pair_frac"], 4)}
-            if o["apply_bytes"] + o["spmv_bytes"] >= 64 << 20:
-                # a workload whose pair moves more than a quarter of the Infinity
-                # Cache: also timed with the factors cycled through HBM
-                log(f"bench: {name} cold (factors from HBM) apply + SpMV")
+                            "apply_spmv_frac": round(o["pair_frac"], 4),
+                            "apply_gbs": round(o["apply_gbs"], 1),
+                            "apply_frac": round(o["apply_gbs"] / HBM_PEAK_GBS, 4),
+                            "spmv_gbs": round(o["spmv_gbs"], 1),
+                            "spmv_frac": round(o["spmv_gbs"] / HBM_PEAK_GBS, 4),
+                            "residency": "warm (Infinity Cache); peak 8 TB/s HBM"}
+            if o["apply_bytes"] + o["spmv_bytes"] >= 8 << 20:
+                # also timed with the factors cycled through HBM, and both
+                # residencies beside the read ceiling of the apply's bytes
+                log(f"bench: {name} cold (factors from HBM) apply + SpMV, read ceilings")
                 others[name]["cold"] = measure_cold(_b)
+                ceil = measure_read_ceiling(o["apply_bytes"])
+                others[name]["read_ceiling"] = ceil
+                others[name]["apply_frac_of_warm_ceiling"] = round(o["apply_gbs"] / ceil["warm_gbs"], 4)
+                others[name]["apply_frac_of_cold_ceiling"] = round(others[name]["cold"]["apply_gbs"]
+                                                                   / ceil["cold_gbs"], 4)
     variants = {}
     if not args.no_variants:
         for label, eng, prec in (("persistent_vec64", 2, 0), ("persistent_vec32", 2, 1),
@@ -394,22 +486,36 @@ def main(argv=None):
             variants[label] = {"ms_per_solve": round(o["ms_per_solve"], 4), "iterations": o["iterations"][0]}
     bridge = None
     if not args.no_variants:
-        # the pages' own factor format: bridges + cores, expanded on the device
+        # the pages' own factor format: bridges + cores, applied natively (and
+        # expanded on the device into slabs for the solve)
         from workloads.generate import bridge_factors_for
-        log("bench: bridge-format factors")
-        bb = make_config(args.config)
-        Ub, Vb, Bc = bridge_factors_for(bb)
-        solver = hpcg.Solver(bb.n, bb.row_ptr, bb.col, bb.val, batch=bb.batch, levels=bb.levels, stream=stream)
-        dev = [torch.as_tensor(a).cuda() for a in (bb.U, Ub, Vb, Bc, bb.g)]
-        torch.cuda.synchronize()
-        with torch.cuda.stream(stream):
-            t_exp = time_graph(lambda: hpcg.hpcg_set_factors_bridge(solver.handle, solver.part, *dev), 20,
-                               stream, torch)
-        bvec = torch.as_tensor(bb.b.reshape(-1)).cuda()
-        ms, its, _res = time_solves(solver, bvec, bb.tol, bb.maxit, max(3, args.steps // 2), 1, torch)
-        bridge = {"expand_us": round(t_exp, 3), "ms_per_solve": round(ms, 4), "iterations": its[0],
-                  "factor_bytes": int(sum(a.numel() * 4 for a in dev))}
-        solver.close()
+        bridge = {}
+        for name in dict.fromkeys((args.config, "N16k")):
+            log(f"bench: bridge-format factors {name}")
+            bb = make_config(name)
+            Ub, Vb, Bc = bridge_factors_for(bb)
+            solver = hpcg.Solver(bb.n, bb.row_ptr, bb.col, bb.val, batch=bb.batch, levels=bb.levels, stream=stream)
+            dev = [torch.as_tensor(a).cuda() for a in (bb.U, Ub, Vb, Bc, bb.g)]
+            torch.cuda.synchronize()
+            with torch.cuda.stream(stream):
+                t_set = time_graph(lambda: hpcg.hpcg_set_factors_bridge(solver.handle, solver.part, *dev), 20,
+                                   stream, torch)
+            r = torch.randn(bb.batch * bb.n, device="cuda", dtype=torch.float32)
+            y = torch.empty_like(r)
+            with torch.cuda.stream(stream):
+                t_apply = time_graph(lambda: hpcg.hpcg_apply_M(solver.handle, solver.part, r, y), args.reps,
+                                     stream, torch)
+            path = hpcg.hpcg_last_apply_path(solver.handle)
+            bvec = torch.as_tensor(bb.b.reshape(-1)).cuda()
+            ms, its, _res = time_solves(solver, bvec, bb.tol, bb.maxit, max(3, args.steps // 2), 1, torch)
+            nb = bridge_apply_bytes(bb.n, bb.K, bb.levels, bb.batch)
+            bridge[name] = {"set_factors_us": round(t_set, 3), "factor_bytes": int(sum(a.numel() * 4 for a in dev)),
+                            "apply_path": "bridge" if path == hpcg.HPCG_APPLY_BRIDGE else str(path),
+                            "apply_us": round(t_apply, 3), "apply_bytes": nb,
+                            "apply_gbs": round(nb / t_apply / 1e3, 1),
+                            "apply_frac": round(nb / t_apply / 1e3 / HBM_PEAK_GBS, 4),
+                            "ms_per_solve": round(ms, 4), "iterations": its[0]}
+            solver.close()
     tight = None
     if not args.no_variants:
         # rtol 1e-10: fp64 vectors directly, and the outer refinement around
@@ -472,10 +578,9 @@ def main(argv=None):
         for name in ("N8k", "N16k"):
             log(f"bench: block apply {name}")
             block.append(measure_block(name))
-    cold = None
-    if not args.no_variants:
-        log("bench: cold (factors from HBM) apply + SpMV")
-        cold = measure_cold(batch)
+    log("bench: cold (factors from HBM) apply + SpMV, read ceilings")
+    cold = measure_cold(batch)
+    ceiling = measure_read_ceiling(ab)
     cpu = None if args.no_cpu else cpu_baseline(batch)
     iters = main_out["iterations"][0]
     line = {
@@ -510,20 +615,36 @@ def main(argv=None):
                                else round(main_out["apply_streaming_us"], 3)),
         "roofline": {
             "bound": "hbm",
-            "achieved": round(achieved, 1),
+            "achieved": round(main_out["apply_gbs"], 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "frac": round(main_out["apply_gbs"] / HBM_PEAK_GBS, 4),
             "traffic": traffic_record(args.config),
             "kernel": (single_pass_kernel(batch) if main_out["apply_path"] == "fused"
                        else "M-apply (k_apply_restrict + k_apply_prolong)")
-                      + " + CSR SpMV (k_spmv), pairs graph-replayed back to back on the library stream",
-            "algorithmic_bytes": ab + sb,
-            "apply_gbs": round(main_out["apply_gbs"], 1),
-            "spmv_gbs": round(main_out["spmv_gbs"], 1),
-            "residency": "warm: the same system's factors replayed back to back stay in the 256 MB "
-                         "Infinity Cache; see cold",
-            "cold": cold,
+                      + ", calls graph-replayed back to back on the library stream",
+            "bytes_per_launch": ab,
+            "us_per_launch": round(main_out["apply_us"], 3),
+            "residency": "warm: the same factors call after call, read from the 256 MB Infinity Cache "
+                         "(frac is still quoted against the 8 TB/s HBM peak); `cold` has them from HBM",
+            "warm_read_ceiling_gbs": ceiling["warm_gbs"],
+            "frac_of_warm_read_ceiling": round(main_out["apply_gbs"] / ceiling["warm_gbs"], 4),
+            "cold": {"apply_us": cold["apply_us"], "achieved": cold["apply_gbs"], "frac": cold["apply_frac"],
+                     "cold_read_ceiling_gbs": ceiling["cold_gbs"],
+                     "frac_of_cold_read_ceiling": round(cold["apply_gbs"] / ceiling["cold_gbs"], 4),
+                     "copies_cycled": cold["copies"]},
+            "read_ceiling": ceiling,
+            "apply_spmv": {
+                "kernels": "the apply above + CSR SpMV (k_spmv), pairs graph-replayed back to back",
+                "bytes": ab + sb, "us": round(main_out["pair_us"], 3), "achieved": round(achieved, 1),
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "spmv_us": round(main_out["spmv_us"], 3), "spmv_gbs": round(main_out["spmv_gbs"], 1),
+                "spmv_frac": round(main_out["spmv_gbs"] / HBM_PEAK_GBS, 4),
+                "cold": {k: cold[k] for k in ("apply_spmv_us", "achieved", "frac", "bytes_cycled")}},
+            "solve": {
+                "kernel": "the whole solve (persistent kernel): iterations x the pair's algorithmic bytes "
+                          "per ms of solve, i.e. what an apply + SpMV per iteration would have to stream",
+                "effective_gbs": round(iters * (ab + sb) / (main_out["ms_per_solve"] * 1e-3) / 1e9, 1)},
         },
         "cpu_baseline": cpu,
         "by_config": others,

@@ -181,11 +181,20 @@ typedef enum {
  * words is bounded (HPCG_OPT_APPLY_POLL_LIMIT, about a second by default):
  * should other work hold the compute units that long, the apply gives up, its
  * output is undefined, and hpcg_apply_status reports it.
- * AUTO (default): FUSED where it fits, else STREAMING. */
+ * BRIDGE: the single pass in the pages' own format, reading the per-leaf
+ * bridges U~_k, V~_k and the per-tile cores B_m as given to
+ * hpcg_set_factors_bridge (O(N) factor bytes: 13.2 MB at n = 16,384 against
+ * the slabs' 23.3 MB), with the coarse coupling t = B_m s in each leaf's
+ * workgroup ("Hierarchical Transformer Preconditioning for Interactive Physics
+ * Simulation", section 5, eqs. (2)-(5)); HPCG_ERR_STATE after
+ * hpcg_set_factors, or where a system has more leaves than compute units.
+ * AUTO (default): BRIDGE where the factors came in that format and it fits,
+ * else FUSED where it fits, else STREAMING. */
 typedef enum {
     HPCG_APPLY_AUTO = 0,
     HPCG_APPLY_STREAMING = 1,
-    HPCG_APPLY_FUSED = 2
+    HPCG_APPLY_FUSED = 2,
+    HPCG_APPLY_BRIDGE = 3
 } hpcg_apply_path;
 
 /* Arithmetic of the solve's vectors (hpcg_set_option(HPCG_OPT_PRECISION, ...)).
@@ -278,9 +287,11 @@ hpcg_status hpcg_set_factors(hpcg_handle h, const float* d_leafU, const float* d
  *             tiles in level order, j ascending within a level
  *  d_gate     float32 [batch][n]
  * (the three off-diagonal pointers may be NULL when levels == 0).  The library
- * expands the format on the device into its per-level slabs (W_l[k] = U~_k B_m
- * for the row half of a tile, V~_k for the column half; fp32 products), after
- * which every call behaves as with hpcg_set_factors.  Stream-ordered. */
+ * keeps the format as given for hpcg_apply_M (HPCG_APPLY_BRIDGE, the default
+ * path after this call) and also expands it on the device into its per-level
+ * slabs (W_l[k] = U~_k B_m for the row half of a tile, V~_k for the column
+ * half; fp32 products), which the solve engines, the other apply paths and the
+ * block calls use.  Stream-ordered. */
 hpcg_status hpcg_set_factors_bridge(hpcg_handle h, const float* d_leafF, const float* d_bridgeU,
                                     const float* d_bridgeV, const float* d_cores, const float* d_gate);
 
@@ -427,6 +438,24 @@ hpcg_status hpcg_solve_refined(hpcg_handle h, const float* d_b, double* d_x, dou
 size_t hpcg_block_solve_workspace_bytes(hpcg_handle h, int32_t nrhs);
 hpcg_status hpcg_solve_block(hpcg_handle h, const float* d_B, double* d_X, int32_t nrhs, double tol, int32_t maxit,
                              void* d_work, size_t work_bytes, int32_t* h_iters, double* h_relres);
+
+/* Measurement aid (no part of the solve): read `bytes` from d_src with one
+ * launch of `workgroups` workgroups, as fast as plain 16-byte loads go, and
+ * write one float per workgroup to d_sink [workgroups].  Timing it over the
+ * apply's bytes gives the read ceiling that the apply's bandwidth is quoted
+ * against (from the Infinity Cache when the same bytes are read back to back,
+ * from HBM when the buffers cycled exceed it).  bytes a positive multiple of
+ * 16, d_src 16-byte aligned; asynchronous on `stream` (a hipStream_t or
+ * NULL).  Errors are reported through hpcg_last_error(NULL). */
+hpcg_status hpcg_read_probe(const void* d_src, size_t bytes, float* d_sink, int32_t workgroups, void* stream);
+
+/* Measurement aid: the in-kernel timeline of a library built with HPCG_TRACE
+ * (python -m matrix_preconditioned_pcg_amd.timeline builds and reads it).
+ * Kernels record the 100 MHz real-time counter at fixed points of their work
+ * (slot s of workgroup w at index w * 16 + s, 4,096 workgroups); this copies
+ * the first `count` entries to h_out and, if clear != 0, zeroes the table.
+ * Synchronous.  The ordinary build returns HPCG_ERR_STATE. */
+hpcg_status hpcg_trace_read(uint64_t* h_out, size_t count, int32_t clear);
 
 /* Per-system hpcg_system_status values of the last hpcg_solve, int32 [batch]. */
 hpcg_status hpcg_last_solve_status(hpcg_handle h, int32_t* h_status);

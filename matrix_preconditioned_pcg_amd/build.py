@@ -19,10 +19,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "hpcg.hip")
 DEPS = [os.path.join(HERE, "csrc", f) for f in ("hpcg.hip", "hpcg_device.hpp", "hpcg_kernels.hpp", "hpcg_leaf.hpp",
-                                                 "hpcg_apply.hpp", "hpcg_resident.hpp", "hpcg_block.hpp")]
+                                                 "hpcg_apply.hpp", "hpcg_bridge.hpp", "hpcg_resident.hpp", "hpcg_block.hpp",
+                                                 "hpcg_bsolve.hpp")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIB_DIR, "libhpcg.so")
+TRACE_LIB = os.path.join(LIB_DIR, "libhpcg_trace.so")   # the same sources with HPCG_TRACE (timeline)
 ARCH = "gfx950"
 
 
@@ -33,18 +35,20 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
 
 
-def command(out: str) -> list:
+def command(out: str, trace: bool = False) -> list:
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-Wno-unused-command-line-argument",
+            "-Wno-unused-command-line-argument"] + (["-DHPCG_TRACE"] if trace else []) + [
             "-I", INCLUDE, "-o", out, SRC]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile libhpcg.so (always recompiles) and return its path."""
+def build(verbose: bool = False, trace: bool = False) -> str:
+    """Compile libhpcg.so (or, with trace, the timeline build libhpcg_trace.so;
+    always recompiles) and return its path."""
     os.makedirs(LIB_DIR, exist_ok=True)
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = command(tmp)
+    target = TRACE_LIB if trace else LIB
+    tmp = target + f".tmp{os.getpid()}"
+    cmd = command(tmp, trace)
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
@@ -52,9 +56,9 @@ def build(verbose: bool = False) -> str:
         if os.path.exists(tmp):
             os.remove(tmp)
         raise RuntimeError("hipcc failed:\n" + proc.stdout + proc.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, target)
+    return target
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, trace="--trace" in sys.argv))

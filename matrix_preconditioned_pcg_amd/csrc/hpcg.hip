@@ -16,6 +16,7 @@
 #include <vector>
 
 #include "hpcg_apply.hpp"
+#include "hpcg_bridge.hpp"
 #include "hpcg_resident.hpp"
 #include "hpcg_block.hpp"
 #include "hpcg_bsolve.hpp"
@@ -36,6 +37,7 @@ struct Layout {
   size_t qll, pqll;           // resident engine: flagged W^T q words and p.q partials
   size_t fr, fd, frhs, fsc;   // outer refinement: residual, correction, scaled rhs, per-system scalars
   size_t w, dinv, ftmp;       // squared form: H r; Jacobi: 1 / A_ii; apply scratch
+  size_t Ub, Vb, Bc;          // bridge-format factors as given (native bridge apply)
   size_t llw, lle, lly;       // single-pass apply: flagged restriction words, per-leaf epochs,
                               // flagged diagonal-stage words of the split variant
   size_t total;
@@ -103,6 +105,13 @@ bool make_geom(const hpcg_partition* p, Geom& G, std::string& why, int split) {
   return true;
 }
 
+// Tiles (cores) per system: K/2 + K/4 + ... over the levels present.
+int tile_count(const Geom& G) {
+  int c = 0;
+  for (int l = 0; l < G.levels; ++l) c += G.K >> (l + 1);
+  return c;
+}
+
 Layout make_layout(const Geom& G, int64_t nnz) {
   Layout L{};
   size_t off = 0;
@@ -151,6 +160,11 @@ Layout make_layout(const Geom& G, int64_t nnz) {
   L.llw = take((size_t)G.B * G.levels * G.K * RANK * 8 + 16);
   L.lle = take((size_t)G.B * G.K * 4);
   L.lly = take((size_t)G.B * G.K * LEAF * 8);
+  if (G.levels > 0) {
+    L.Ub = take((size_t)G.B * G.K * LEAF * RANK * 4);
+    L.Vb = take((size_t)G.B * G.K * LEAF * RANK * 4);
+    L.Bc = take((size_t)G.B * tile_count(G) * RANK * RANK * 4);
+  }
   L.total = off;
   return L;
 }
@@ -177,6 +191,7 @@ struct hpcg_ctx {
   hipStream_t cap_stream = nullptr;
   char* ws = nullptr;
   bool factors_set = false;
+  bool bridge_set = false;   // the factors came in the bridge format (native bridge apply possible)
   int engine_opt = HPCG_ENGINE_AUTO;
   int unroll = 8;
   int prec = HPCG_PREC_VEC64;
@@ -197,6 +212,8 @@ struct hpcg_ctx {
   int last_apply_path = 0;
   int fused_per_cu = -1;
   int split_per_cu = -1;
+  int bridge_per_cu = -1;
+  int bridge_split_per_cu = -1;
   int split_apply = 1;     // single-pass apply with two workgroups per leaf where it fits
   double graph_tol = -1.0;
   int graph_maxit = -1;
@@ -600,6 +617,10 @@ hpcg_status hpcg_create(const hpcg_partition* part, const int32_t* d_row_ptr, co
   B.llw = reinterpret_cast<unsigned long long*>(w + lay.llw);
   B.lle = reinterpret_cast<unsigned*>(w + lay.lle);
   B.lly = reinterpret_cast<unsigned long long*>(w + lay.lly);
+  B.Ub = reinterpret_cast<const float*>(w + lay.Ub);
+  B.Vb = reinterpret_cast<const float*>(w + lay.Vb);
+  B.Bc = reinterpret_cast<const float*>(w + lay.Bc);
+  B.ncores = tile_count(G);
   B.w = w + lay.w;
   B.dinv = reinterpret_cast<const double*>(w + lay.dinv);
   B.form = FORM_DIRECT;
@@ -692,6 +713,7 @@ hpcg_status hpcg_set_factors(hpcg_handle h, const float* d_leafU, const float* d
                                   hipMemcpyDeviceToDevice, h->stream));
   HIP_OR_FAIL(h, hipMemcpyAsync(h->ws + h->lay.g, d_gate, (size_t)G.B * G.n * 4, hipMemcpyDeviceToDevice, h->stream));
   h->factors_set = true;
+  h->bridge_set = false;
   return HPCG_OK;
 }
 
@@ -728,6 +750,56 @@ const void* split_apply_kernel(int levels) {
     case 8: return reinterpret_cast<const void*>(&k_apply_split<8>);
     default: return nullptr;
   }
+}
+
+#define HPCG_BRIDGE_KERNEL(LV)                                                                          \
+  case LV:                                                                                              \
+    return split ? reinterpret_cast<const void*>(&k_apply_bridge<LV, true>)                            \
+                 : reinterpret_cast<const void*>(&k_apply_bridge<LV, false>);
+const void* bridge_apply_kernel(int levels, bool split) {
+  switch (levels) {
+    HPCG_BRIDGE_KERNEL(1) HPCG_BRIDGE_KERNEL(2) HPCG_BRIDGE_KERNEL(3) HPCG_BRIDGE_KERNEL(4)
+    HPCG_BRIDGE_KERNEL(5) HPCG_BRIDGE_KERNEL(6) HPCG_BRIDGE_KERNEL(7) HPCG_BRIDGE_KERNEL(8)
+    default: return nullptr;
+  }
+}
+#undef HPCG_BRIDGE_KERNEL
+
+// The native bridge-format apply (factors from hpcg_set_factors_bridge): one
+// launch per group of whole systems whose leaves all get a compute unit, two
+// workgroups per leaf while a quarter of the CUs hold the batch's leaves (as
+// the slab apply).  ran = false when it does not fit.
+hpcg_status run_bridge_apply(hpcg_ctx* h, const float* d_r, float* d_y, bool& ran) {
+  ran = false;
+  const Geom G = h->G;
+  const int items = G.B * G.K;
+  if (G.levels < 1 || !h->bridge_set || G.K > h->num_cu) return HPCG_OK;
+  const size_t dyn = ((size_t)std::max(G.K - 1, 1) * RANK + (size_t)G.levels * RANK * CSTRIDE) * sizeof(float);
+  if (dyn + sizeof(RSmem<float>) > kMaxLds) return HPCG_OK;
+  const bool split = h->split_apply && 4 * (int64_t)items <= h->num_cu;
+  const void* fn = bridge_apply_kernel(G.levels, split);
+  if (!fn) return HPCG_OK;
+  hpcg_status s = allow_lds(h, fn, dyn);
+  if (s != HPCG_OK) return s;
+  int& per_cu = split ? h->bridge_split_per_cu : h->bridge_per_cu;
+  if (per_cu < 0) HIP_OR_FAIL(h, hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NTR, dyn));
+  const int wg_per_leaf = split ? 2 : 1;
+  const int64_t cap = (int64_t)per_cu * h->num_cu / wg_per_leaf;
+  const int per_launch = (int)std::min<int64_t>(G.B, cap / G.K);
+  if (per_launch < 1) return HPCG_OK;
+  Geom Ga = G;
+  Bufs Ba = h->B;
+  const float* ra = d_r;
+  float* ya = d_y;
+  int item0 = 0;
+  void* args[] = {&Ga, &Ba, &ra, &ya, &item0};
+  for (int s0 = 0; s0 < G.B; s0 += per_launch) {
+    item0 = s0 * G.K;
+    const int nsys = std::min(per_launch, G.B - s0);
+    HIP_OR_FAIL(h, hipLaunchKernel(fn, dim3(wg_per_leaf * nsys * G.K), dim3(NTR), args, (unsigned)dyn, h->stream));
+  }
+  ran = true;
+  return HPCG_OK;
 }
 
 hpcg_status run_fused_apply(hpcg_ctx* h, const float* d_r, float* d_y, bool& ran) {
@@ -793,9 +865,18 @@ hpcg_status hpcg_set_factors_bridge(hpcg_handle h, const float* d_leafF, const f
     hipLaunchKernelGGL(k_expand_bridge, dim3(G.B * G.levels * G.K), dim3(NT), 0, h->stream, G, d_bridgeU, d_bridgeV,
                        d_cores, reinterpret_cast<float*>(h->ws + h->lay.W));
   HIP_OR_FAIL(h, hipMemcpyAsync(h->ws + h->lay.g, d_gate, (size_t)G.B * G.n * 4, hipMemcpyDeviceToDevice, h->stream));
+  if (G.levels > 0) {
+    // the format as given, for the native bridge apply
+    const size_t bridge = (size_t)G.B * G.K * LEAF * RANK * 4;
+    HIP_OR_FAIL(h, hipMemcpyAsync(h->ws + h->lay.Ub, d_bridgeU, bridge, hipMemcpyDeviceToDevice, h->stream));
+    HIP_OR_FAIL(h, hipMemcpyAsync(h->ws + h->lay.Vb, d_bridgeV, bridge, hipMemcpyDeviceToDevice, h->stream));
+    HIP_OR_FAIL(h, hipMemcpyAsync(h->ws + h->lay.Bc, d_cores, (size_t)G.B * h->B.ncores * RANK * RANK * 4,
+                                  hipMemcpyDeviceToDevice, h->stream));
+  }
   hpcg_status s = check_launch(h, "bridge expansion launch");
   if (s != HPCG_OK) return s;
   h->factors_set = true;
+  h->bridge_set = G.levels > 0;
   return HPCG_OK;
 }
 
@@ -826,6 +907,18 @@ hpcg_status hpcg_apply_M(hpcg_handle h, const float* d_r, float* d_y) {
 namespace {
 // y = H r with the H-matrix factors (the apply paths of hpcg_apply_M).
 hpcg_status apply_H(hpcg_ctx* h, const float* d_r, float* d_y) {
+  if (h->apply_path == HPCG_APPLY_BRIDGE || (h->apply_path == HPCG_APPLY_AUTO && h->bridge_set)) {
+    bool ran = false;
+    hpcg_status s = run_bridge_apply(h, d_r, d_y, ran);
+    if (s != HPCG_OK) return s;
+    if (ran) {
+      h->last_apply_path = HPCG_APPLY_BRIDGE;
+      return HPCG_OK;
+    }
+    if (h->apply_path == HPCG_APPLY_BRIDGE)
+      return fail(h, HPCG_ERR_STATE, h->bridge_set ? "bridge apply: a system has more leaves than compute units"
+                                                   : "bridge apply: factors were not set with hpcg_set_factors_bridge");
+  }
   if (h->apply_path != HPCG_APPLY_STREAMING) {
     bool ran = false;
     hpcg_status s = run_fused_apply(h, d_r, d_y, ran);
@@ -848,6 +941,44 @@ hpcg_status apply_H(hpcg_ctx* h, const float* d_r, float* d_y) {
   return check_launch(h, "hpcg_apply_M launch");
 }
 }  // namespace
+
+hpcg_status hpcg_read_probe(const void* d_src, size_t bytes, float* d_sink, int32_t workgroups, void* stream) {
+  if (!d_src || !d_sink) return fail(nullptr, HPCG_ERR_INVALID_ARG, "read probe: pointer is NULL");
+  if (bytes == 0 || bytes % 16 || reinterpret_cast<uintptr_t>(d_src) % 16)
+    return fail(nullptr, HPCG_ERR_INVALID_ARG, "read probe: bytes and d_src must be positive multiples of 16");
+  if (workgroups < 1 || workgroups > (1 << 20)) return fail(nullptr, HPCG_ERR_INVALID_ARG, "read probe: bad grid");
+  hipLaunchKernelGGL(k_read_probe, dim3((unsigned)workgroups), dim3(PROBE_NT), 0,
+                     reinterpret_cast<hipStream_t>(stream), reinterpret_cast<const float4*>(d_src), bytes / 16,
+                     d_sink);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(nullptr, e, "read probe launch");
+  return HPCG_OK;
+}
+
+hpcg_status hpcg_trace_read(uint64_t* h_out, size_t count, int32_t clear) {
+#ifdef HPCG_TRACE
+  const size_t total = (size_t)kTraceItems * kTraceSlots;
+  if (count > total) return fail(nullptr, HPCG_ERR_INVALID_ARG, "trace: count exceeds the table");
+  if (count > 0) {
+    if (!h_out) return fail(nullptr, HPCG_ERR_INVALID_ARG, "trace: h_out is NULL");
+    hipError_t e = hipMemcpyFromSymbol(h_out, HIP_SYMBOL(trace_table), count * sizeof(uint64_t), 0,
+                                       hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(nullptr, e, "trace: hipMemcpyFromSymbol");
+  }
+  if (clear) {
+    std::vector<uint64_t> zero(total, 0);
+    hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(trace_table), zero.data(), total * sizeof(uint64_t), 0,
+                                     hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(nullptr, e, "trace: hipMemcpyToSymbol");
+  }
+  return HPCG_OK;
+#else
+  (void)h_out;
+  (void)count;
+  (void)clear;
+  return fail(nullptr, HPCG_ERR_STATE, "this build has no timeline (compile with HPCG_TRACE)");
+#endif
+}
 
 hpcg_status hpcg_apply_status(hpcg_handle h) {
   if (!h) return fail(nullptr, HPCG_ERR_INVALID_ARG, "handle is NULL");
@@ -1494,7 +1625,7 @@ hpcg_status hpcg_set_option(hpcg_handle h, int32_t option, int32_t value) {
       h->B.form = value;
       return HPCG_OK;
     case HPCG_OPT_APPLY_PATH:
-      if (value < HPCG_APPLY_AUTO || value > HPCG_APPLY_FUSED) return fail(h, HPCG_ERR_INVALID_ARG, "bad apply path");
+      if (value < HPCG_APPLY_AUTO || value > HPCG_APPLY_BRIDGE) return fail(h, HPCG_ERR_INVALID_ARG, "bad apply path");
       h->apply_path = value;
       return HPCG_OK;
     case HPCG_OPT_LEAF_SPLIT: {

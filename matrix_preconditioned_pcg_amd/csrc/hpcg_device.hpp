@@ -50,6 +50,22 @@ constexpr int NT = 256;
 constexpr int NWAVE = NT / 64;
 constexpr int MAX_LEVELS = 8;      // K <= 256 leaves per system
 
+// In-kernel timeline, compiled in only with HPCG_TRACE (a separate build of
+// the library): stamp(wg, slot) records thread 0's reading of the constant
+// 100 MHz real-time counter into trace_table[wg][slot]; hpcg_trace_read copies
+// the table to the host.  In the ordinary build stamp() is empty.
+constexpr int kTraceSlots = 16;
+constexpr int kTraceItems = 4096;
+#ifdef HPCG_TRACE
+__device__ unsigned long long trace_table[kTraceItems * kTraceSlots];
+__device__ __forceinline__ void stamp(int wg, int slot) {
+  if (threadIdx.x == 0 && wg < kTraceItems)
+    trace_table[wg * kTraceSlots + slot] = __builtin_amdgcn_s_memrealtime();
+}
+#else
+__device__ __forceinline__ void stamp(int, int) {}
+#endif
+
 enum : int { ST_RUNNING = 0, ST_CONVERGED = 1, ST_NOT_CONVERGED = 2, ST_BREAKDOWN = 3 };
 
 // Preconditioner forms: M = H (the H-matrix itself), M = H H, M = diag(A)^-1.
@@ -108,6 +124,10 @@ struct Bufs {
   unsigned long long* llw;  // fused apply: [B][levels][K][RANK] W_l[k]^T r as (value, epoch) words
   unsigned* lle;       // fused apply: [B*K] calls completed per leaf (the epoch)
   unsigned long long* lly;  // split apply: [B*K][LEAF] U_k U_k^T r as (value, epoch) words
+  const float* Ub;     // bridge format: [B][K][LEAF][RANK] U~_k
+  const float* Vb;     // bridge format: [B][K][LEAF][RANK] V~_k
+  const float* Bc;     // bridge format: [B][ncores][RANK][RANK] B_m, level-major, j ascending
+  int ncores;          // tiles (cores) per system
   int* abort_flag;     // set when a barrier wait exceeds its bound
   int* apply_abort;    // single-pass apply: set when a partner poll exceeds apply_poll_limit;
                        // cleared only by the host once it has read it

@@ -300,4 +300,36 @@ __global__ void k_copy_x(const double* __restrict__ src, double* __restrict__ ds
   if (i < n) dst[i] = src[i];
 }
 
+// Measurement aid: stream `n4` float4 from src as fast as one launch can
+// (workgroup b reads the contiguous chunk b of gridDim.x, eight independent
+// 16-byte loads in flight per thread), and write one sum per workgroup so the
+// loads are not removed.  The read ceiling that the apply's bandwidth is set
+// against.
+constexpr int PROBE_NT = 256;
+__global__ __launch_bounds__(PROBE_NT) void k_read_probe(const float4* __restrict__ src, size_t n4,
+                                                        float* __restrict__ sink) {
+  __shared__ float red[PROBE_NT / 64];
+  const size_t chunk = (n4 + gridDim.x - 1) / gridDim.x;
+  const size_t beg = (size_t)blockIdx.x * chunk;
+  const size_t end = beg + chunk < n4 ? beg + chunk : n4;
+  float acc = 0.f;
+  size_t i = beg + threadIdx.x;
+  for (; i + 7 * PROBE_NT < end; i += 8 * PROBE_NT) {
+    float4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = src[i + j * PROBE_NT];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc += (v[j].x + v[j].y) + (v[j].z + v[j].w);
+  }
+  for (; i < end; i += PROBE_NT) {
+    const float4 v = src[i];
+    acc += (v.x + v.y) + (v.z + v.w);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
 }  // namespace hpcg

@@ -154,8 +154,13 @@ __device__ __forceinline__ void load_factors(const Geom& G, const Bufs& B, int s
 // alpha sum(stQ), or sum(stR) with stQ == nullptr.  With r_from_prev the
 // partner sums of r are not staged: sm.P still holds them (the previous
 // P, by linearity) and becomes sm.P - alpha sum(stQ).  16 groups of threads
-// per column, then across waves; two barriers.
-template <typename T, int LEV>
+// per column, then across waves; two barriers.  BATCH issues every read
+// unconditionally (levels with fewer than 16 partner leaves read leaf 0 in
+// the idle groups and add zero instead), so that all of them are in flight
+// before the first wait: measured faster in the single-pass apply (N16k 7.08
+// -> 6.92 us) and slower in the resident solve (N8k 1.91 -> 1.96 ms), which
+// keeps the branches.
+template <typename T, int LEV, bool BATCH = false>
 __device__ __forceinline__ void prolong_strips(RSmem<T>& sm, const T* stR, const T* stQ, double alpha,
                                                bool r_from_prev = false) {
   const int tid = tid_of<kFresh<T, LEV>>(), lane = tid & 63, wave = tid >> 6;
@@ -171,7 +176,18 @@ __device__ __forceinline__ void prolong_strips(RSmem<T>& sm, const T* stR, const
 #pragma unroll
     for (int m = 0; m < ((1 << l) + 15) / 16; ++m) {
       const int i = g + 16 * m;
-      if (i < (1 << l)) {
+      if constexpr (BATCH) {
+        const bool ok = (1 << l) >= 16 || i < (1 << l);
+        const int ic = ok ? i : 0;
+        if (!r_from_prev) {
+          const T v = vr[ic * RANK];
+          a[l] += ok ? v : T(0);
+        }
+        if (stQ) {
+          const T v = stQ[(size_t)((1 << l) - 1) * RANK + c + ic * RANK];
+          b[l] += ok ? v : T(0);
+        }
+      } else if (i < (1 << l)) {
         if (!r_from_prev) a[l] += vr[i * RANK];
         if (stQ) b[l] += stQ[(size_t)((1 << l) - 1) * RANK + c + i * RANK];
       }

@@ -58,6 +58,7 @@ HPCG_FORM_JACOBI = 2
 HPCG_APPLY_AUTO = 0
 HPCG_APPLY_STREAMING = 1
 HPCG_APPLY_FUSED = 2
+HPCG_APPLY_BRIDGE = 3
 
 HPCG_PREC_VEC64 = 0
 HPCG_PREC_VEC32 = 1
@@ -81,17 +82,20 @@ _lib = None
 
 
 def library_path() -> str:
-    return LIB
+    """The library this process loads: libhpcg.so, or the file named by the
+    HPCG_LIBRARY environment variable (e.g. the timeline build)."""
+    return os.environ.get("HPCG_LIBRARY") or LIB
 
 
 def lib() -> ctypes.CDLL:
-    """Load libhpcg.so (once).  Raises if it has not been built."""
+    """Load the library (once).  Raises if it has not been built."""
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB):
-        raise RuntimeError(f"{LIB} is missing: build it with `python -m matrix_preconditioned_pcg_amd.build`")
-    L = ctypes.CDLL(LIB)
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m matrix_preconditioned_pcg_amd.build`")
+    L = ctypes.CDLL(path)
     P = ctypes.POINTER
     vp, i32, i64, dbl, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double, ctypes.c_size_t
     sig = {
@@ -102,6 +106,8 @@ def lib() -> ctypes.CDLL:
         "hpcg_set_factors_bridge": (i32, [vp, vp, vp, vp, vp, vp]),
         "hpcg_apply_M": (i32, [vp, vp, vp]),
         "hpcg_apply_status": (i32, [vp]),
+        "hpcg_read_probe": (i32, [vp, sz, vp, i32, vp]),
+        "hpcg_trace_read": (i32, [vp, sz, i32]),
         "hpcg_spmv": (i32, [vp, vp, vp]),
         "hpcg_block_workspace_bytes": (sz, [vp, i32]),
         "hpcg_apply_M_block": (i32, [vp, vp, vp, i32, vp, sz]),
@@ -236,6 +242,22 @@ def hpcg_apply_status(h) -> int:
     """Synchronizes; returns the status code (HPCG_ERR_HIP when an earlier
     single-pass apply gave up a bounded wait), without raising."""
     return int(lib().hpcg_apply_status(h))
+
+
+def hpcg_read_probe(src, nbytes: int, sink, workgroups: int, stream=None):
+    """Measurement aid: one launch reading nbytes of the device tensor src
+    (sink: float32 device tensor of `workgroups` elements)."""
+    if src.device.type != "cuda" or nbytes > src.numel() * src.element_size():
+        raise ValueError("src must be a device tensor of at least nbytes bytes")
+    _check(lib().hpcg_read_probe(src.data_ptr(), int(nbytes), _ptr(sink, torch.float32, int(workgroups), "sink"),
+                                 int(workgroups), _stream(stream)), None)
+
+
+def hpcg_trace_read(count: int, clear: bool = True):
+    """The first `count` timeline entries (uint64) of a HPCG_TRACE build, as a list."""
+    out = (ctypes.c_uint64 * max(int(count), 1))()
+    _check(lib().hpcg_trace_read(out, int(count), int(bool(clear))), None)
+    return list(out)[:count]
 
 
 def hpcg_spmv(h, part: hpcg_partition, x, y):

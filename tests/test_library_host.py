@@ -68,7 +68,9 @@ def test_workspace_bytes_covers_the_buffers(hp):
     resident = 2 * nnz * 4 + 129 * 4 + 16384 * 16 + 128 * 32
     # resident solve: W^T q and p.q as flagged words, two step parities
     resident += 2 * 7 * 128 * 32 * 8 + 2 * 128 * 16
-    need = factors + csr + vectors + restrictions + flagged + barrier_lines + resident
+    # the bridge format as given (native bridge apply): U~, V~ and K - 1 cores
+    bridge = 2 * 128 * 128 * 32 * 4 + 127 * 32 * 32 * 4
+    need = factors + csr + vectors + restrictions + flagged + barrier_lines + resident + bridge
     assert need <= nbytes <= need + (1 << 20)
     assert hp.hpcg_workspace_bytes(hp.partition(2048, batch=64), 851968) > 64 * hp.hpcg_workspace_bytes(
         hp.partition(2048), 13312) * 0.9
@@ -100,6 +102,12 @@ def test_null_handle_calls(hp):
     assert L.hpcg_spmv(None, None, None) == hp.HPCG_ERR_INVALID_ARG
     assert L.hpcg_solve(None, None, None, 1e-6, 10, None, None) == hp.HPCG_ERR_INVALID_ARG
     assert L.hpcg_last_engine(None) == 0
+    assert L.hpcg_apply_status(None) == hp.HPCG_ERR_INVALID_ARG
+    assert L.hpcg_apply_M_block_noalloc(None, None, None, 16) == hp.HPCG_ERR_INVALID_ARG
+    # the read probe validates before it launches (no device touched)
+    assert L.hpcg_read_probe(None, 16, None, 1, None) == hp.HPCG_ERR_INVALID_ARG
+    assert L.hpcg_read_probe(16, 24, 16, 1, None) == hp.HPCG_ERR_INVALID_ARG
+    assert L.hpcg_read_probe(16, 32, 16, 0, None) == hp.HPCG_ERR_INVALID_ARG
     L.hpcg_destroy(None)
     for code in range(8):
         assert hp.hpcg_status_string(code) not in ("", "unknown status")
