@@ -85,17 +85,18 @@ def kernel_source_digest() -> str:
 
 
 def traffic_record(config: str):
-    """HBM bytes per apply+SpMV pair from the committed rocprofv3 counter
-    summary (FETCH_SIZE and WRITE_SIZE, scaled by a copy kernel's reading), or
-    None when there is none for this workload or the kernels changed since."""
-    path = os.path.join(ROOT, "profiles", f"apply_spmv_traffic_{config}.json")
+    """HBM bytes per launch of the single-pass apply from the committed
+    rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, scaled by a copy
+    kernel's reading), or None when there is none for this workload or the
+    kernels changed since."""
+    path = os.path.join(ROOT, "profiles", f"apply_traffic_{config}.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         rec = json.load(fh)
     if rec.get("kernel_source_digest") != kernel_source_digest():
         return None
-    return rec.get("bytes_per_pair")
+    return rec.get("apply_bytes_per_launch")
 
 
 def log(msg):
@@ -228,6 +229,8 @@ def main(argv=None):
     ap.add_argument("--no-others", action="store_true", help="skip ms/solve of the other workloads")
     ap.add_argument("--no-block", action="store_true", help="skip the block (probe) apply timing")
     ap.add_argument("--no-fused", action="store_true", help="skip the forced single-launch apply timing")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the runs with the factors cycled through HBM and the read ceilings (profiling runs)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run three 256 MiB device-to-device copies (calibrates HBM byte counters)")
     ap.add_argument("--solve-only", action="store_true",
@@ -368,6 +371,15 @@ def main(argv=None):
                 "warm_grid": best["warm_grid"], "cold_us": round(best["cold_us"], 3),
                 "cold_gbs": round(nbytes / best["cold_us"] / 1e3, 1), "cold_grid": best["cold_grid"]}
 
+    def measure_launch_floor():
+        """Per-call time of the smallest kernel (one workgroup reading 16
+        bytes) replayed back to back in a graph: the floor any launch starts
+        from."""
+        buf = torch.ones(4, device="cuda", dtype=torch.float32)
+        sink = torch.empty(1, device="cuda", dtype=torch.float32)
+        with torch.cuda.stream(stream):
+            return round(time_graph(lambda: hpcg.hpcg_read_probe(buf, 16, sink, 1, stream), args.reps, stream, torch), 3)
+
     def measure_block(name):
         """Block apply M R on the matrix cores with the pages' probe width
         K_z = max(64, ceil(sqrt(N))) rounded up to 16."""
@@ -467,7 +479,7 @@ def main(argv=None):
                             "spmv_gbs": round(o["spmv_gbs"], 1),
                             "spmv_frac": round(o["spmv_gbs"] / HBM_PEAK_GBS, 4),
                             "residency": "warm (Infinity Cache); peak 8 TB/s HBM"}
-            if o["apply_bytes"] + o["spmv_bytes"] >= 8 << 20:
+            if o["apply_bytes"] + o["spmv_bytes"] >= 8 << 20 and not args.no_cold:
                 # also timed with the factors cycled through HBM, and both
                 # residencies beside the read ceiling of the apply's bytes
                 log(f"bench: {name} cold (factors from HBM) apply + SpMV, read ceilings")
@@ -578,9 +590,16 @@ def main(argv=None):
         for name in ("N8k", "N16k"):
             log(f"bench: block apply {name}")
             block.append(measure_block(name))
-    log("bench: cold (factors from HBM) apply + SpMV, read ceilings")
-    cold = measure_cold(batch)
-    ceiling = measure_read_ceiling(ab)
+    if args.no_cold:
+        cold = {k: None for k in ("apply_us", "apply_gbs", "apply_frac", "copies", "apply_spmv_us", "achieved",
+                                  "frac", "bytes_cycled")}
+        ceiling = {"warm_gbs": None, "cold_gbs": None}
+        floor_us = None
+    else:
+        log("bench: cold (factors from HBM) apply + SpMV, read ceilings")
+        cold = measure_cold(batch)
+        ceiling = measure_read_ceiling(ab)
+        floor_us = measure_launch_floor()
     cpu = None if args.no_cpu else cpu_baseline(batch)
     iters = main_out["iterations"][0]
     line = {
@@ -628,10 +647,13 @@ def main(argv=None):
             "residency": "warm: the same factors call after call, read from the 256 MB Infinity Cache "
                          "(frac is still quoted against the 8 TB/s HBM peak); `cold` has them from HBM",
             "warm_read_ceiling_gbs": ceiling["warm_gbs"],
-            "frac_of_warm_read_ceiling": round(main_out["apply_gbs"] / ceiling["warm_gbs"], 4),
+            "frac_of_warm_read_ceiling": (round(main_out["apply_gbs"] / ceiling["warm_gbs"], 4)
+                                          if ceiling["warm_gbs"] else None),
+            "launch_floor_us": floor_us,
             "cold": {"apply_us": cold["apply_us"], "achieved": cold["apply_gbs"], "frac": cold["apply_frac"],
                      "cold_read_ceiling_gbs": ceiling["cold_gbs"],
-                     "frac_of_cold_read_ceiling": round(cold["apply_gbs"] / ceiling["cold_gbs"], 4),
+                     "frac_of_cold_read_ceiling": (round(cold["apply_gbs"] / ceiling["cold_gbs"], 4)
+                                                   if ceiling["cold_gbs"] else None),
                      "copies_cycled": cold["copies"]},
             "read_ceiling": ceiling,
             "apply_spmv": {

@@ -625,8 +625,14 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
   }
 
   double pend_rel = 0.0;
+  // timeline build: stamps of one iteration (empty otherwise)
+  constexpr int kTraceIt = 65;   // an iteration without the exact refresh
+  auto stamp_it = [&](int it, int slot) {
+    if (it == kTraceIt) stamp(blockIdx.x, slot);
+  };
   for (int it = 1; it <= B.maxit + 2; ++it) {
     const unsigned ez = B.ep_base + (unsigned)(it - 1);   // epoch of z and the partials of step it-1
+    stamp_it(it, 0);
     // ---------------- phase A (it) ----------------
     {
       const bool first = (it == 1);
@@ -650,6 +656,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
         }
       }
       if (__syncthreads_or(bad)) return;   // a bounded poll ran out: the abort flag is set
+      stamp_it(it, 1);
       const double rr = sm.dsc[1], rz = sm.dsc[2];
       int fin = ST_RUNNING, fin_it = 0;
       if (it >= 2) {
@@ -686,16 +693,19 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
         loc = (double)pn * (double)acc;
       }
       __syncthreads();                  // every SpMV read of sm.p and pc is done
+      stamp_it(it, 2);
       if (lr == 0) sm.p[row] = pn;
       for (int h = tid; h < nh; h += NTR)
         pc[LEAF + h] = first ? zc[LEAF + h] : pdir<T>(zc[LEAF + h], pc[LEAF + h], beta);
       // the slab restriction of q and the partial p.q, published as flagged
       // words (what the partners read)
       r_restrict_q_ll<T, LEV>(G, B, s, k, item, F, sm, loc, it & 1, q_tag(it), B.ep_base + (unsigned)it);
+      stamp_it(it, 3);
     }
     // U_k U_k^T q is this workgroup's alone: it overlaps the partners' words
     // in flight
     if constexpr (!JAC) leaf_apply<T, LEV>(F, sm.q, sm.tq, sm.yq, sm);
+    stamp_it(it, 4);
     // ---------------- phase BC (it) ----------------
     double alpha = 0.0;
     {
@@ -714,6 +724,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
       }
       __builtin_amdgcn_s_waitcnt(0);    // the W^T r stage has landed
       if (__syncthreads_or(bad)) return;
+      stamp_it(it, 5);
       const double pq = sm.dsc[3];
       if (!(pq > 0.0) || !isfinite(pq)) {   // every workgroup of the system sees the same pq
         if (lead) set_state(st, ST_BREAKDOWN, it);
@@ -733,6 +744,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
         // (r_prolong_split synchronizes before it reads sm.r)
         r_prolong_split<T, LEV>(F, sm, stR, stQ, alpha, gate, r_from_prev);
       }
+      stamp_it(it, 6);
       if constexpr (SQ) {
         if (!squared()) return;
       }
@@ -748,7 +760,9 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
         r_restrict<T, LEV>(G, s, k, F, sm.r, sm.tr, pR[rbuf], sm.ownR, sm);
         diag_times<T, LEV>(F, sm.tr, sm.yr);
       }
+      stamp_it(it, 7);
       publish(loc_rr, it);
+      stamp_it(it, 8);
       if (!JAC && !refresh && tid < LEAF) sm.yr[tid] = (T)((double)sm.yr[tid] - alpha * (double)sm.yq[tid]);
     }
   }

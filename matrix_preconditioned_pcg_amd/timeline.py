@@ -36,6 +36,10 @@ SPLIT_DIAG = {0: "start", 1: "r in LDS", 2: "U_k U_k^T r published"}
 SPLIT_OFF = {0: "start", 1: "r in LDS", 2: "restriction published",
              5: "partner + diagonal words gathered", 6: "prolongation done", 7: "y stored and acknowledged"}
 SPMV = {0: "start", 7: "y stored and acknowledged"}
+RESIDENT = {0: "iteration start", 1: "halo z and r.r, r.z partials polled", 2: "SpMV done",
+            3: "restriction of q and p.q published", 4: "U_k U_k^T q done",
+            5: "partners' W^T q and p.q polled", 6: "alpha, r, x and z = M r done", 7: "exact refresh (when due)",
+            8: "z and partials published"}
 
 
 def table(title, stamps, names, t0):
@@ -53,6 +57,7 @@ def main(argv=None):
     ap.add_argument("--calls", type=int, default=200)
     ap.add_argument("--build", action="store_true")
     ap.add_argument("--bridge", action="store_true", help="factors in the bridge format (native bridge apply)")
+    ap.add_argument("--solve", action="store_true", help="also one resident solve: its 65th iteration")
     args = ap.parse_args(argv)
     from matrix_preconditioned_pcg_amd import build as build_mod
     if args.build or not os.path.exists(build_mod.TRACE_LIB):
@@ -128,6 +133,25 @@ def main(argv=None):
     out.append(table("CSR SpMV (k_spmv)", sp, SPMV, t0))
     out += ["", f"SpMV: first workgroup start to last acknowledged store "
                 f"{(int(sp[:, 7].astype(np.int64).max()) - t0) * TICK_US:.2f} us."]
+    if args.solve:
+        b = torch.as_tensor(batch.b.reshape(-1)).cuda()
+        with torch.cuda.stream(stream):
+            solver.solve(b)
+            torch.cuda.synchronize()
+            hpcg.hpcg_trace_read(0, clear=True)
+            res = solver.solve(b)
+            torch.cuda.synchronize()
+        if hpcg.hpcg_last_engine(solver.handle) == hpcg.HPCG_ENGINE_PERSISTENT and min(res.iterations) > 65:
+            nwg = min(items, ncu)
+            rs = np.array(hpcg.hpcg_trace_read(nwg * SLOTS), dtype=np.uint64).reshape(nwg, SLOTS)
+            t0 = int(rs[:, 0].astype(np.int64).min())
+            out += ["", table(f"resident solve, iteration 65 of {res.iterations[0]} (first launch)", rs,
+                              RESIDENT, t0)]
+            d = np.diff(rs[:, [0, 1, 2, 3, 4, 5, 6, 7, 8]].astype(np.int64), axis=1) * TICK_US
+            names = list(RESIDENT.values())
+            out += ["", "Per workgroup, median time between consecutive stamps (us):", "",
+                    "| from | to | median |", "|---|---|---|"]
+            out += [f"| {names[i]} | {names[i + 1]} | {np.median(d[:, i]):.2f} |" for i in range(d.shape[1])]
     solver.close()
     print("\n".join(out))
     return 0
