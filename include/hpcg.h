@@ -430,7 +430,9 @@ hpcg_status hpcg_solve_refined(hpcg_handle h, const float* d_b, double* d_x, dou
  *  h_relres [batch*nrhs] final recursive ||r|| / ||b|| (may be NULL)
  * Arithmetic: R, Z, P, Q fp32 (the block apply's), x and all scalars fp64:
  * the pages' split, so on the tetrahedral system the columns need about a
- * quarter more iterations than fp64 PCG, as HPCG_PREC_VEC32 does.
+ * quarter more iterations than fp64 PCG, as HPCG_PREC_VEC32 does.  Each row
+ * of A P is summed in fp64 and rounded to fp32 once, so that the true
+ * residual ||b - A x|| stays with the recursive one.
  * Direct form only (HPCG_ERR_STATE otherwise).  Returns HPCG_ERR_BREAKDOWN or
  * HPCG_ERR_NOT_CONVERGED when some column ends so (x and counts still
  * written).  Records the iterations in a hipGraph, kept for repeated calls

@@ -1030,28 +1030,37 @@ size_t block_half_bytes(const hpcg_ctx* h, int32_t nrhs) {
 
 // The three launches of Y = M R for a block (scratch Q and H of
 // block_half_bytes each; unused without tile levels).
+// The block solve passes upd (the leaf stage takes its residual update) and,
+// with tile levels, dot (the prolongation leaves its r.z partials); the plain
+// block apply passes neither.
 hpcg_status launch_block_apply(hpcg_ctx* h, int32_t nrhs, const float* d_R, float* d_Y, float* Q, float* H,
-                               hipStream_t stream) {
+                               hipStream_t stream, const BlockUpd* upd = nullptr, const BlockDot* dot = nullptr) {
   const BlockGeom bg = block_geom(h, nrhs);
   const int nct = block_nct(h, nrhs);
   const int grid = h->G.B * h->G.K * bg.tiles;
+  const BlockUpd up = upd ? *upd : BlockUpd{};
+  const BlockDot dt = dot ? *dot : BlockDot{};
+#define HPCG_BLOCK_RESTRICT_N(LV, N)                                                                     \
+  do {                                                                                                   \
+    if (upd)                                                                                             \
+      hipLaunchKernelGGL((k_block_restrict<LV, N, true>), dim3(grid), dim3(BNT), 0, stream, bg, h->B.U,   \
+                         h->B.W, h->B.g, d_R, d_Y, Q, up);                                               \
+    else                                                                                                 \
+      hipLaunchKernelGGL((k_block_restrict<LV, N, false>), dim3(grid), dim3(BNT), 0, stream, bg, h->B.U,  \
+                         h->B.W, h->B.g, d_R, d_Y, Q, up);                                               \
+  } while (0)
   switch (h->G.levels) {
 #define HPCG_BLOCK_RESTRICT(LV)                                                                          \
     case LV:                                                                                             \
-      if (nct == 4)                                                                                      \
-        hipLaunchKernelGGL((k_block_restrict<LV, 4>), dim3(grid), dim3(BNT), 0, stream, bg, h->B.U, h->B.W, \
-                           h->B.g, d_R, d_Y, Q);                                                         \
-      else if (nct == 2)                                                                                 \
-        hipLaunchKernelGGL((k_block_restrict<LV, 2>), dim3(grid), dim3(BNT), 0, stream, bg, h->B.U, h->B.W, \
-                           h->B.g, d_R, d_Y, Q);                                                         \
-      else                                                                                               \
-        hipLaunchKernelGGL((k_block_restrict<LV, 1>), dim3(grid), dim3(BNT), 0, stream, bg, h->B.U, h->B.W, \
-                           h->B.g, d_R, d_Y, Q);                                                         \
+      if (nct == 4) HPCG_BLOCK_RESTRICT_N(LV, 4);                                                        \
+      else if (nct == 2) HPCG_BLOCK_RESTRICT_N(LV, 2);                                                   \
+      else HPCG_BLOCK_RESTRICT_N(LV, 1);                                                                 \
       break;
     HPCG_BLOCK_RESTRICT(0) HPCG_BLOCK_RESTRICT(1) HPCG_BLOCK_RESTRICT(2) HPCG_BLOCK_RESTRICT(3)
     HPCG_BLOCK_RESTRICT(4) HPCG_BLOCK_RESTRICT(5) HPCG_BLOCK_RESTRICT(6) HPCG_BLOCK_RESTRICT(7)
     HPCG_BLOCK_RESTRICT(8)
 #undef HPCG_BLOCK_RESTRICT
+#undef HPCG_BLOCK_RESTRICT_N
     default: return fail(h, HPCG_ERR_SHAPE, "levels out of range");
   }
   if (h->G.levels > 0) {
@@ -1059,19 +1068,26 @@ hpcg_status launch_block_apply(hpcg_ctx* h, int32_t nrhs, const float* d_R, floa
     for (int l = 0; l < h->G.levels; ++l) sys_total += (size_t)(h->G.K >> l) * RANK * nrhs;
     const size_t total = sys_total * h->G.B;
     hipLaunchKernelGGL(k_block_halfsum, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, bg, Q, H);
+#define HPCG_BLOCK_PROLONG_N(LV, N)                                                                     \
+  do {                                                                                                  \
+    if (dot)                                                                                            \
+      hipLaunchKernelGGL((k_block_prolong<LV, N, true>), dim3(grid), dim3(BNT), 0, stream, bg, h->B.W, H, \
+                         d_Y, dt);                                                                      \
+    else                                                                                                \
+      hipLaunchKernelGGL((k_block_prolong<LV, N, false>), dim3(grid), dim3(BNT), 0, stream, bg, h->B.W, H, \
+                         d_Y, dt);                                                                      \
+  } while (0)
     switch (h->G.levels) {
 #define HPCG_BLOCK_PROLONG(LV)                                                                          \
       case LV:                                                                                          \
-        if (nct == 4)                                                                                   \
-          hipLaunchKernelGGL((k_block_prolong<LV, 4>), dim3(grid), dim3(BNT), 0, stream, bg, h->B.W, H, d_Y); \
-        else if (nct == 2)                                                                              \
-          hipLaunchKernelGGL((k_block_prolong<LV, 2>), dim3(grid), dim3(BNT), 0, stream, bg, h->B.W, H, d_Y); \
-        else                                                                                            \
-          hipLaunchKernelGGL((k_block_prolong<LV, 1>), dim3(grid), dim3(BNT), 0, stream, bg, h->B.W, H, d_Y); \
+        if (nct == 4) HPCG_BLOCK_PROLONG_N(LV, 4);                                                      \
+        else if (nct == 2) HPCG_BLOCK_PROLONG_N(LV, 2);                                                 \
+        else HPCG_BLOCK_PROLONG_N(LV, 1);                                                               \
         break;
       HPCG_BLOCK_PROLONG(1) HPCG_BLOCK_PROLONG(2) HPCG_BLOCK_PROLONG(3) HPCG_BLOCK_PROLONG(4)
       HPCG_BLOCK_PROLONG(5) HPCG_BLOCK_PROLONG(6) HPCG_BLOCK_PROLONG(7) HPCG_BLOCK_PROLONG(8)
 #undef HPCG_BLOCK_PROLONG
+#undef HPCG_BLOCK_PROLONG_N
       default: return fail(h, HPCG_ERR_SHAPE, "levels out of range");
     }
   }
@@ -1168,7 +1184,7 @@ BlockSolveLayout block_solve_layout(const hpcg_ctx* h, int32_t nrhs) {
   return L;
 }
 
-// One block-PCG iteration (eight launches, the steps of hpcg_bsolve.hpp) on `stream`.
+// One block-PCG iteration (the steps of hpcg_bsolve.hpp) on `stream`.
 hpcg_status block_iteration(hpcg_ctx* h, int32_t nrhs, char* wk, const BlockSolveLayout& L, double* d_X,
                             double tol, int32_t maxit, hipStream_t stream) {
   const Geom& G = h->G;
@@ -1183,20 +1199,26 @@ hpcg_status block_iteration(hpcg_ctx* h, int32_t nrhs, char* wk, const BlockSolv
   const dim3 rows_grid((unsigned)(G.B * rblocks), (unsigned)((nrhs + BS_COLS - 1) / BS_COLS));
   const int ncol = G.B * nrhs;
   const dim3 sc_grid((unsigned)((ncol + BS_SC_COLS - 1) / BS_SC_COLS));
-  const size_t threads = (size_t)G.B * G.n * (nrhs / 4);
-  hipLaunchKernelGGL(k_spmv_block, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, h->B.row_ptr,
-                     h->B.col, h->B.val, P, Q, G.B * G.n, nrhs);
-  hipLaunchKernelGGL(k_bs_dot, rows_grid, dim3(BS_NT), 0, stream, P, Q, part, nrhs);
+  hipLaunchKernelGGL(k_bs_spmv_dot, rows_grid, dim3(BS_NT), 0, stream, h->B.row_ptr, h->B.col, h->B.val, P, Q,
+                     part, nrhs);
   hipLaunchKernelGGL(k_bs_scalars<BS_PQ>, sc_grid, dim3(64 * BS_SC_COLS), 0, stream, cs, part, G.B, nrhs, rblocks, tol, maxit,
-                     (const double*)nullptr);
-  hipLaunchKernelGGL(k_bs_update, rows_grid, dim3(BS_NT), 0, stream, cs, P, Q, R, d_X, part2, nrhs, rblocks);
+                     (const double*)nullptr, 0);
+  // R -= alpha Q and the r.r partials in the leaf stage; the r.z partials in
+  // the prolongation (per leaf), or, without tile levels, by a pass of their own
+  static_assert(sizeof(ColState) % sizeof(double) == 0, "ColState holds whole doubles");
+  const BlockUpd upd{&cs[0].alpha, (int)(sizeof(ColState) / sizeof(double)), Q, R, part2};
+  const BlockDot dot{R, part};
   hpcg_status s = launch_block_apply(h, nrhs, R, Z, reinterpret_cast<float*>(wk + L.scratchQ),
-                                     reinterpret_cast<float*>(wk + L.scratchH), stream);
+                                     reinterpret_cast<float*>(wk + L.scratchH), stream, &upd, &dot);
   if (s != HPCG_OK) return s;
-  hipLaunchKernelGGL(k_bs_dot, rows_grid, dim3(BS_NT), 0, stream, R, Z, part, nrhs);
-  hipLaunchKernelGGL(k_bs_scalars<BS_RRZ>, sc_grid, dim3(64 * BS_SC_COLS), 0, stream, cs, part, G.B, nrhs, rblocks, tol, maxit,
-                     (const double*)part2);
-  hipLaunchKernelGGL(k_bs_direction, rows_grid, dim3(BS_NT), 0, stream, cs, Z, P, nrhs, rblocks);
+  int rz_blocks = G.K;
+  if (G.levels == 0) {
+    hipLaunchKernelGGL(k_bs_dot, rows_grid, dim3(BS_NT), 0, stream, R, Z, part, nrhs);
+    rz_blocks = rblocks;
+  }
+  hipLaunchKernelGGL(k_bs_scalars<BS_RRZ>, sc_grid, dim3(64 * BS_SC_COLS), 0, stream, cs, part, G.B, nrhs, rz_blocks,
+                     tol, maxit, (const double*)part2, G.K);
+  hipLaunchKernelGGL(k_bs_direction, rows_grid, dim3(BS_NT), 0, stream, cs, Z, P, d_X, nrhs, rblocks);
   return HPCG_OK;
 }
 
@@ -1267,14 +1289,14 @@ hpcg_status hpcg_solve_block(hpcg_handle h, const float* d_B, double* d_X, int32
   hipLaunchKernelGGL(k_bs_reset, dim3(1), dim3(64), 0, h->stream, ctr, dflag);
   hipLaunchKernelGGL(k_bs_init, rows_grid, dim3(BS_NT), 0, h->stream, d_B, R, d_X, part, nrhs);
   hipLaunchKernelGGL(k_bs_scalars<BS_INIT>, sc_grid, dim3(64 * BS_SC_COLS), 0, h->stream, cs, part, G.B, nrhs, rblocks, tol, maxit,
-                     (const double*)nullptr);
+                     (const double*)nullptr, 0);
   hpcg_status s = launch_block_apply(h, nrhs, R, Z, reinterpret_cast<float*>(wk + L.scratchQ),
                                      reinterpret_cast<float*>(wk + L.scratchH), h->stream);
   if (s != HPCG_OK) return s;
   hipLaunchKernelGGL(k_bs_dot, rows_grid, dim3(BS_NT), 0, h->stream, R, Z, part, nrhs);
   hipLaunchKernelGGL(k_bs_scalars<BS_RZ0>, sc_grid, dim3(64 * BS_SC_COLS), 0, h->stream, cs, part, G.B, nrhs, rblocks, tol, maxit,
-                     (const double*)nullptr);
-  hipLaunchKernelGGL(k_bs_direction, rows_grid, dim3(BS_NT), 0, h->stream, cs, Z, P, nrhs, rblocks);
+                     (const double*)nullptr, 0);
+  hipLaunchKernelGGL(k_bs_direction, rows_grid, dim3(BS_NT), 0, h->stream, cs, Z, P, d_X, nrhs, rblocks);
   s = check_launch(h, "block solve setup launch");
   if (s != HPCG_OK) return s;
 

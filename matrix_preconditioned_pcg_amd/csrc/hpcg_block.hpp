@@ -26,7 +26,9 @@
 // per-leaf restrictions Q_l[k] = W_l[k]^T R_k; (2) per (level, half, element):
 // the half sums of Q_l over every tile half (eq. (3)), in a fixed order; (3) per
 // (leaf, tile): Y += sum_l W_l[k] P_l with P_l the partner half's sum (eqs.
-// (4)-(5), identity core).
+// (4)-(5), identity core).  The block solve has (1) take its residual update
+// and (3) its r.z partials (BlockUpd, BlockDot), so that neither needs a pass
+// of its own over the block.
 #pragma once
 #include "hpcg_device.hpp"
 
@@ -72,18 +74,42 @@ __device__ __forceinline__ size_t q_index(const BlockGeom& G, int s, int l, int 
   return ((((size_t)s * G.levels + l) * G.K + k) * RANK + row) * G.nrhs;
 }
 
+// The block solve's residual update, taken by the leaf stage as it loads R
+// (UPD): R <- R - alpha_c (A P) column by column, in fp64 and rounded to fp32
+// once, a column whose alpha is 0 keeping its R; the new R is written back and
+// the apply runs on it, and the workgroup leaves its (system, leaf, column)
+// partials of the new R . R.
+struct BlockUpd {
+  const double* alpha;   // alpha of (system s, column c) at alpha[(s nrhs + c) stride]
+  int stride;
+  const float* AP;       // A P, node-major like R
+  float* R;              // where the new R goes (the buffer R is read from)
+  double* rr;            // [B][K][nrhs] partials of the new R . R
+};
+
+// The block solve's r.z partials, taken by the prolongation as it stores Z
+// (DOT): per (system, leaf, column), the fp64 sum of R Z over the leaf's rows.
+struct BlockDot {
+  const float* R;
+  double* rz;            // [B][K][nrhs]
+};
+
 // (1) leaf stage, gate and restriction.  All global operand loads of a stage
 // are issued before its products, and the next level's before this level's.
 // A workgroup owns NCT 16-column tiles (BW = 16 NCT columns): every U_k and
-// W_l[k] operand it loads feeds the MFMAs of all NCT tiles.
-template <int LEV, int NCT>
+// W_l[k] operand it loads feeds the MFMAs of all NCT tiles.  R is only read
+// through the DMA into LDS, before any write of the UPD update.
+template <int LEV, int NCT, bool UPD = false>
 __global__ __launch_bounds__(BNT) void k_block_restrict(BlockGeom G, const float* __restrict__ U,
                                                         const float* __restrict__ W, const float* __restrict__ g,
-                                                        const float* __restrict__ R, float* __restrict__ Y,
-                                                        float* __restrict__ Q) {
+                                                        const float* R, float* __restrict__ Y,
+                                                        float* __restrict__ Q, BlockUpd up) {
   constexpr int BW = BNC * NCT;
+  constexpr int C4 = BW / 4;                 // 16-byte chunks per tile row
+  constexpr int CH = LEAF * C4 / BNT;        // chunks of the tile per thread
   __shared__ __attribute__((aligned(16))) float Rs[LEAF * BW];          // R_k tile, [row][BW]
   __shared__ __attribute__((aligned(16))) float Ts[BW * TS_STRIDE];     // T^T, [col][row]
+  __shared__ double red[UPD ? NWAVE * BW : 1];
   const BItem it = bitem(G);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int q = lane >> 4, r = lane & 15;
@@ -111,7 +137,36 @@ __global__ __launch_bounds__(BNT) void k_block_restrict(BlockGeom G, const float
 #pragma unroll
     for (int s = 0; s < 32; ++s) wa[s] = Wl[(size_t)(4 * s + q) * RANK];
   }
+  // UPD: the thread's chunks c = tid + BNT i of the tile, all in its four
+  // columns cc..cc+3 (BNT is a multiple of C4)
+  const int cc = c0 + 4 * (tid % C4);
+  double al[4] = {0.0, 0.0, 0.0, 0.0}, rr4[4] = {0.0, 0.0, 0.0, 0.0};
+  mf4 ap[UPD ? CH : 1];
+  if constexpr (UPD) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) al[v] = up.alpha[((size_t)it.s * G.nrhs + cc + v) * up.stride];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int row = (tid + BNT * i) / C4;
+      ap[i] = *reinterpret_cast<const mf4*>(up.AP + (size_t)(it.leaf0 + row) * G.nrhs + cc);
+    }
+  }
   lds_dma_wait();
+  if constexpr (UPD) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = tid + BNT * i, row = c / C4;
+      mf4 v = *reinterpret_cast<const mf4*>(&Rs[4 * c]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (al[t] != 0.0) v[t] = (float)((double)v[t] - al[t] * (double)ap[i][t]);
+        rr4[t] = fma((double)v[t], (double)v[t], rr4[t]);
+      }
+      *reinterpret_cast<mf4*>(&Rs[4 * c]) = v;
+      *reinterpret_cast<mf4*>(up.R + (size_t)(it.leaf0 + row) * G.nrhs + cc) = v;
+    }
+    __syncthreads();
+  }
   // T = U_k^T R_k: this wave's rows [32w, 32w + 32) of T, for every tile
   mf4 ta[NCT], tb[NCT];
 #pragma unroll
@@ -191,6 +246,23 @@ __global__ __launch_bounds__(BNT) void k_block_restrict(BlockGeom G, const float
       Y[(size_t)(it.leaf0 + ib) * G.nrhs + cj] = yb[v] + g[it.leaf0 + ib] * Rs[ib * BW + 16 * j + r];
     }
   }
+  if constexpr (UPD) {
+    // R.R partials: lanes of a wave with the same columns differ in lane bits
+    // >= log2(C4) (fixed butterfly), then the four waves in order
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int o = C4; o < 64; o <<= 1) rr4[t] += __shfl_xor(rr4[t], o);
+    }
+    if (lane < C4) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) red[w * BW + 4 * lane + t] = rr4[t];
+    }
+    __syncthreads();
+    if (tid < BW)
+      up.rr[((size_t)it.s * G.K + it.k) * G.nrhs + c0 + tid] =
+          ((red[tid] + red[BW + tid]) + red[2 * BW + tid]) + red[3 * BW + tid];
+  }
 }
 
 // (2) half sums: H_l[h] = sum of Q_l[k] over the 2^l leaves k of half h, summed
@@ -233,11 +305,13 @@ __global__ void k_block_halfsum(BlockGeom G, const float* __restrict__ Q, float*
 
 // (3) prolongation: Y_k += sum_l W_l[k] H_l[(k >> l) ^ 1].  Every level's slab
 // rows are loaded in one batch up front and feed the MFMAs of all NCT tiles.
-template <int LEV, int NCT>
+template <int LEV, int NCT, bool DOT = false>
 __global__ __launch_bounds__(BNT) void k_block_prolong(BlockGeom G, const float* __restrict__ W,
-                                                       const float* __restrict__ H, float* __restrict__ Y) {
+                                                       const float* __restrict__ H, float* __restrict__ Y,
+                                                       BlockDot dt) {
   constexpr int BW = BNC * NCT;
   __shared__ __attribute__((aligned(16))) float Ps[(LEV > 0 ? LEV : 1) * BW * PS_STRIDE];   // [l][col][rank]
+  __shared__ double red[DOT ? NWAVE * BW : 1];
   const BItem it = bitem(G);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int q = lane >> 4, r = lane & 15;
@@ -260,6 +334,18 @@ __global__ __launch_bounds__(BNT) void k_block_prolong(BlockGeom G, const float*
     for (int v = 0; v < 4; ++v) {
       ya[j][v] = Y[(size_t)(it.leaf0 + 32 * w + 4 * q + v) * G.nrhs + c0 + 16 * j + r];
       yb[j][v] = Y[(size_t)(it.leaf0 + 32 * w + 16 + 4 * q + v) * G.nrhs + c0 + 16 * j + r];
+    }
+  }
+  // DOT: R at the lane's accumulator elements
+  float rv[DOT ? NCT : 1][8];
+  if constexpr (DOT) {
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        rv[j][v] = dt.R[(size_t)(it.leaf0 + 32 * w + 4 * q + v) * G.nrhs + c0 + 16 * j + r];
+        rv[j][4 + v] = dt.R[(size_t)(it.leaf0 + 32 * w + 16 + 4 * q + v) * G.nrhs + c0 + 16 * j + r];
+      }
     }
   }
   // partner half sums, transposed into LDS: all loads first, then the stores
@@ -302,6 +388,25 @@ __global__ __launch_bounds__(BNT) void k_block_prolong(BlockGeom G, const float*
       Y[(size_t)(it.leaf0 + 32 * w + 4 * q + v) * G.nrhs + c0 + 16 * j + r] = ya[j][v];
       Y[(size_t)(it.leaf0 + 32 * w + 16 + 4 * q + v) * G.nrhs + c0 + 16 * j + r] = yb[j][v];
     }
+  }
+  if constexpr (DOT) {
+    // R.Z partials: the lane's eight rows, then the four lane groups q (fixed
+    // butterfly), then the four waves in order
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) {
+      double d = 0.0;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) d = fma((double)rv[j][v], (double)ya[j][v], d);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) d = fma((double)rv[j][4 + v], (double)yb[j][v], d);
+      d += __shfl_xor(d, 16);
+      d += __shfl_xor(d, 32);
+      if (q == 0) red[w * BW + 16 * j + r] = d;
+    }
+    __syncthreads();
+    if (tid < BW)
+      dt.rz[((size_t)it.s * G.K + it.k) * G.nrhs + c0 + tid] =
+          ((red[tid] + red[BW + tid]) + red[2 * BW + tid]) + red[3 * BW + tid];
   }
 }
 

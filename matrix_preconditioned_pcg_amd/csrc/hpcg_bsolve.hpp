@@ -16,15 +16,21 @@
 // The test is taken with beta, after Z = M R: a column that has just
 // converged costs one unused column of the block apply, and its count and x
 // are those of the textbook loop, with one launch fewer per iteration.
+// Six launches per iteration (eight with the block apply's three): the SpMV
+// leaves the p.q partials; the apply's leaf stage takes R -= alpha Q and
+// leaves the r.r partials, its prolongation the r.z partials; X += alpha P
+// waits for the direction step, which reads P anyway.
 // R, Z, P, Q are fp32 (the block apply's arithmetic), X and every scalar fp64.
 // A finished column gets alpha = beta = 0 from then on, so its X and R stay
 // as they were while the others continue.
 //
-// Dot products: a workgroup owns 32 rows and 64 columns; a thread owns one
-// column and sums rows rg, rg + 4, ... in fp64, the four row groups are added
-// in a fixed order, and the per-block partials of a system are added by one
-// wave per (system, column) in a fixed order (lane-strided, then a fixed
-// butterfly): every sum has one order, so a solve is bitwise reproducible.
+// Dot products: every product is taken in fp64 and every partial is a sum in
+// a fixed order: p.q per 32-row block (the SpMV's workgroups, which own 32 rows
+// and 64 columns), r.r and r.z per leaf (the block apply's workgroups), and
+// the setup's b.b and r.z per 32-row block (k_bs_init, k_bs_dot).  The
+// partials of a system are added by one wave per (system, column) in a fixed
+// order (lane-strided, then a fixed butterfly): every sum has one order, so a
+// solve is bitwise reproducible.
 #pragma once
 #include "hpcg_device.hpp"
 
@@ -98,52 +104,115 @@ __global__ __launch_bounds__(BS_NT) void k_bs_init(const float* __restrict__ Bm,
   if (rg == 0 && c < nrhs) part[rb * nrhs + c] = s;
 }
 
-// X += alpha P, R -= alpha Q (alpha per column of the row's system), part =
-// per-leaf partials of the new R . R.  A finished column (alpha = 0) is left
-// untouched, whatever its P and Q hold.
-__global__ __launch_bounds__(BS_NT) void k_bs_update(const ColState* __restrict__ cs, const float* __restrict__ P,
-                                                     const float* __restrict__ Q, float* __restrict__ R,
-                                                     double* __restrict__ X, double* __restrict__ part, int nrhs,
-                                                     int blocks_per_system) {
-  __shared__ double red[BS_NT];
-  const int tid = threadIdx.x, rg = tid / BS_COLS;
-  const int c = blockIdx.y * BS_COLS + (tid & (BS_COLS - 1));
+// Q = A P and the block's partials of P . Q (the layout of k_bs_dot).  Thread
+// (rr, g) takes rows rr and rr + 16 of the 32-row block and columns 4g..4g+3 of
+// the 64-column tile; the two rows' entries are taken four at a time, their
+// indices and then their P rows all in flight together.  A row's sum is taken
+// in fp64 and rounded to fp32 once: R -= alpha Q moves R away from B - A X by
+// alpha (A P - Q) every step, and a sum of the stencil's cancelling terms
+// rounded at every step moved it by several times tol on long, stiff grids.
+// The partial of a column adds the thread's two rows (with the stored, rounded
+// Q), the four row groups of a wave (fixed butterfly) and the four waves in
+// order.
+__global__ __launch_bounds__(BS_NT) void k_bs_spmv_dot(const int* __restrict__ row_ptr, const int* __restrict__ col,
+                                                       const float* __restrict__ val, const float* __restrict__ P,
+                                                       float* __restrict__ Q, double* __restrict__ part, int nrhs) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  __shared__ double red[(BS_NT / 64) * BS_COLS];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = tid & 15, rr = tid >> 4;
+  const int c4 = blockIdx.y * BS_COLS + 4 * g;
   const size_t rb = blockIdx.x;
-  const int s = (int)(rb / blocks_per_system);
-  double acc = 0.0;
-  if (c < nrhs) {
-    const double alpha = cs[(size_t)s * nrhs + c].alpha;
+  double d[4] = {0.0, 0.0, 0.0, 0.0};
+  if (c4 < nrhs) {
+    int row[2], e0[2], e1[2];
 #pragma unroll
-    for (int r = rg; r < BS_ROWS; r += BS_NT / BS_COLS) {
-      const size_t i = (rb * BS_ROWS + r) * nrhs + c;
-      float rn = R[i];
-      if (alpha != 0.0) {
-        X[i] = fma(alpha, (double)P[i], X[i]);
-        rn = (float)((double)rn - alpha * (double)Q[i]);
-        R[i] = rn;
+    for (int h = 0; h < 2; ++h) {
+      row[h] = (int)(rb * BS_ROWS) + rr + 16 * h;
+      e0[h] = row_ptr[row[h]];
+      e1[h] = row_ptr[row[h] + 1];
+    }
+    f4 pv[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) pv[h] = *reinterpret_cast<const f4*>(P + (size_t)row[h] * nrhs + c4);
+    double acc[2][4] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
+    const int len = max(e1[0] - e0[0], e1[1] - e0[1]);
+    for (int o = 0; o < len; o += 4) {
+      int c[2][4];
+      float a[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const bool in = e0[h] + o + u < e1[h];
+          c[h][u] = in ? col[e0[h] + o + u] : row[h];
+          a[h][u] = in ? val[e0[h] + o + u] : 0.f;
+        }
       }
-      acc = fma((double)rn, (double)rn, acc);
+      f4 x[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x[h][u] = *reinterpret_cast<const f4*>(P + (size_t)c[h][u] * nrhs + c4);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (e0[h] + o + u < e1[h]) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[h][t] = fma((double)a[h][u], (double)x[h][u][t], acc[h][t]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const f4 qv = {(float)acc[h][0], (float)acc[h][1], (float)acc[h][2], (float)acc[h][3]};
+      *reinterpret_cast<f4*>(Q + (size_t)row[h] * nrhs + c4) = qv;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) d[t] = fma((double)pv[h][t], (double)qv[t], d[t]);
     }
   }
-  const double sum = bs_rowgroup_reduce(acc, red);
-  if (rg == 0 && c < nrhs) part[rb * nrhs + c] = sum;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    d[t] += __shfl_xor(d[t], 16);
+    d[t] += __shfl_xor(d[t], 32);
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) red[w * BS_COLS + 4 * lane + t] = d[t];
+  }
+  __syncthreads();
+  const int c = blockIdx.y * BS_COLS + tid;
+  if (tid < BS_COLS && c < nrhs)
+    part[rb * nrhs + c] = ((red[tid] + red[BS_COLS + tid]) + red[2 * BS_COLS + tid]) + red[3 * BS_COLS + tid];
 }
 
-// P = Z + beta P (beta per column of the row's system).  beta = 0 (the first
-// step, and every step of a finished column) takes P = Z without reading P,
-// which holds no value before the first step.
+// X += alpha P, then P = Z + beta P (alpha and beta per column of the row's
+// system).  alpha = 0 (the setup, and every step of a finished column) leaves X
+// as it is; beta = 0 (the first step, and every step of a finished column)
+// takes P = Z without reading P, which holds no value before the first step.
 __global__ __launch_bounds__(BS_NT) void k_bs_direction(const ColState* __restrict__ cs, const float* __restrict__ Z,
-                                                        float* __restrict__ P, int nrhs, int blocks_per_system) {
+                                                        float* __restrict__ P, double* __restrict__ X, int nrhs,
+                                                        int blocks_per_system) {
   const int tid = threadIdx.x, rg = tid / BS_COLS;
   const int c = blockIdx.y * BS_COLS + (tid & (BS_COLS - 1));
   const size_t rb = blockIdx.x;
   const int s = (int)(rb / blocks_per_system);
   if (c >= nrhs) return;
+  const double alpha = cs[(size_t)s * nrhs + c].alpha;
   const double beta = cs[(size_t)s * nrhs + c].beta;
 #pragma unroll
   for (int r = rg; r < BS_ROWS; r += BS_NT / BS_COLS) {
     const size_t i = (rb * BS_ROWS + r) * nrhs + c;
-    P[i] = beta == 0.0 ? Z[i] : (float)((double)Z[i] + beta * (double)P[i]);
+    if (alpha != 0.0) {
+      const float p = P[i];
+      X[i] = fma(alpha, (double)p, X[i]);
+      P[i] = beta == 0.0 ? Z[i] : (float)((double)Z[i] + beta * (double)p);
+    } else {
+      P[i] = beta == 0.0 ? Z[i] : (float)((double)Z[i] + beta * (double)P[i]);
+    }
   }
 }
 
@@ -152,20 +221,22 @@ __global__ __launch_bounds__(BS_NT) void k_bs_direction(const ColState* __restri
 // wave_sum (one order, every call); lane 0 takes the step the mode names.
 constexpr int BS_SC_COLS = 4;   // columns (waves) per workgroup
 // RRZ takes the convergence test on part2 (r.r) and then beta on part (r.z).
+// part holds blocks_per_system partials per (system, column), part2 (RRZ only)
+// blocks2 of them.
 template <int MODE>
 __global__ __launch_bounds__(64 * BS_SC_COLS) void k_bs_scalars(ColState* __restrict__ cs,
                                                                 const double* __restrict__ part, int systems,
                                                                 int nrhs, int blocks_per_system, double tol,
-                                                                int maxit, const double* __restrict__ part2) {
+                                                                int maxit, const double* __restrict__ part2,
+                                                                int blocks2) {
   const int idx = blockIdx.x * BS_SC_COLS + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (idx >= systems * nrhs) return;     // whole waves leave together
   const int s = idx / nrhs, c = idx - s * nrhs;
   double v = 0.0, v2 = 0.0;
-  for (int k = lane; k < blocks_per_system; k += 64) {
-    const size_t o = ((size_t)s * blocks_per_system + k) * nrhs + c;
-    v += part[o];
-    if constexpr (MODE == BS_RRZ) v2 += part2[o];
+  for (int k = lane; k < blocks_per_system; k += 64) v += part[((size_t)s * blocks_per_system + k) * nrhs + c];
+  if constexpr (MODE == BS_RRZ) {
+    for (int k = lane; k < blocks2; k += 64) v2 += part2[((size_t)s * blocks2 + k) * nrhs + c];
   }
   const double sum = wave_sum(v);
   double sum2 = 0.0;

@@ -17,6 +17,7 @@ torch = pytest.importorskip("torch")
 
 import oracle  # noqa: E402
 from workloads import make_config  # noqa: E402
+from workloads.generate import build_batch, random_system  # noqa: E402
 
 from matrix_preconditioned_pcg_amd import hpcg  # noqa: E402
 
@@ -57,6 +58,21 @@ def test_block_solve_parity(name, nrhs, cols):
     X, iters, rel, st = s.solve_block(Bm.reshape(-1), nrhs, tol=b.tol, maxit=b.maxit)
     assert st == hpcg.HPCG_OK, hpcg.hpcg_last_error(s.handle)
     _check(b, X.cpu().numpy(), iters, rel, Bm.astype(np.float64), cols)
+    s.close()
+
+
+@pytest.mark.parametrize("n,levels,batch", [(128, 0, 1), (256, 1, 2), (2048, 2, 3), (4096, 0, 1)])
+def test_block_solve_small_and_ragged(n, levels, batch):
+    # single-leaf systems and hierarchies without tile levels (the r.z partials
+    # then come from a pass of their own), partial hierarchies, small batches
+    _log(f"block solve small n={n} levels={levels} batch={batch}")
+    systems = [random_system(n, seed=600 + i, levels=levels).system(0) for i in range(batch)]
+    b = build_batch(systems, name=f"bsmall{n}_{levels}_{batch}")
+    s = _solver(b)
+    Bm = np.random.default_rng(n + levels).standard_normal((batch, n, 16)).astype(np.float32)
+    X, iters, rel, st = s.solve_block(Bm.reshape(-1), 16, tol=b.tol, maxit=b.maxit)
+    assert st == hpcg.HPCG_OK, hpcg.hpcg_last_error(s.handle)
+    _check(b, X.cpu().numpy(), iters, rel, Bm.astype(np.float64), (0, 7, 15), systems=range(batch))
     s.close()
 
 
