@@ -138,6 +138,14 @@ typedef enum {
                                    hpcg_apply_status (or the next hpcg_solve or
                                    hpcg_estimate_spectrum); a diagnostic bound,
                                    like HPCG_OPT_POLL_LIMIT                       */
+    HPCG_OPT_BLOCK_SPLIT = 512, /* block apply and block solve, where there are
+                                   tile levels and a workgroup takes at most two
+                                   16-column tiles: 0 = automatic (default: two
+                                   workgroups per (leaf, column tile) while fewer
+                                   such items than compute units), 1 = one
+                                   workgroup takes the leaf stage and the
+                                   restriction, 2 = each in a workgroup of its
+                                   own.  Same results either way               */
     HPCG_OPT_LEAF_SPLIT = 8     /* workgroups per leaf in the apply kernels and the
                                    graph and streaming engines: 0 = automatic
                                    (default), else 1, 2, 4 or 8; a split whose LDS

@@ -207,6 +207,7 @@ struct hpcg_ctx {
   int fallback = 0;
   int last_fallback = 0;
   int split = 0;
+  int block_split = 0;   // HPCG_OPT_BLOCK_SPLIT: 0 automatic, 1 one workgroup per item, 2 two
   int apply_path = HPCG_APPLY_AUTO;
   Geom Gapply{};           // geometry of the standalone apply kernels
   int last_apply_path = 0;
@@ -228,7 +229,7 @@ struct hpcg_ctx {
   hipGraph_t bs_graph = nullptr;
   hipGraphExec_t bs_gexec = nullptr;
   const void* bs_key[2] = {nullptr, nullptr};
-  int bs_nrhs = 0, bs_unroll = 0, bs_maxit = -1;
+  int bs_nrhs = 0, bs_unroll = 0, bs_maxit = -1, bs_split = -1;
   double bs_tol = -1.0;
   SysState* h_st = nullptr;
   int* h_ctl = nullptr;    // pinned copy of the abort words (solve, apply)
@@ -1024,6 +1025,17 @@ BlockGeom block_geom(const hpcg_ctx* h, int32_t nrhs) {
   return bg;
 }
 
+// Leaf stage and restriction in workgroups of their own: with tile levels and
+// at most two column tiles per workgroup (four would not fit two workgroups'
+// registers on a compute unit), when asked, or (automatic) while the items
+// leave compute units idle.
+bool block_split(const hpcg_ctx* h, int32_t nrhs) {
+  if (h->G.levels == 0 || h->block_split == 1 || block_nct(h, nrhs) > 2) return false;
+  if (h->block_split == 2) return true;
+  const BlockGeom bg = block_geom(h, nrhs);
+  return (int64_t)h->G.B * h->G.K * bg.tiles < h->num_cu;
+}
+
 size_t block_half_bytes(const hpcg_ctx* h, int32_t nrhs) {
   return align_up((size_t)h->G.B * h->G.levels * h->G.K * RANK * nrhs * 4);
 }
@@ -1040,14 +1052,21 @@ hpcg_status launch_block_apply(hpcg_ctx* h, int32_t nrhs, const float* d_R, floa
   const int grid = h->G.B * h->G.K * bg.tiles;
   const BlockUpd up = upd ? *upd : BlockUpd{};
   const BlockDot dt = dot ? *dot : BlockDot{};
+  const bool sp = block_split(h, nrhs);
+  // (block_split() holds only where a split instantiation exists: LV > 0, N < 4)
+#define HPCG_BLOCK_RESTRICT_UPD(LV, N, UP)                                                               \
+  do {                                                                                                   \
+    if (sp && LV > 0 && N < 4)                                                                           \
+      hipLaunchKernelGGL((k_block_restrict<LV, N, UP, (LV > 0 && N < 4)>), dim3(2 * grid), dim3(BNT), 0, \
+                         stream, bg, h->B.U, h->B.W, h->B.g, d_R, d_Y, Q, up);                           \
+    else                                                                                                 \
+      hipLaunchKernelGGL((k_block_restrict<LV, N, UP, false>), dim3(grid), dim3(BNT), 0, stream, bg,      \
+                         h->B.U, h->B.W, h->B.g, d_R, d_Y, Q, up);                                       \
+  } while (0)
 #define HPCG_BLOCK_RESTRICT_N(LV, N)                                                                     \
   do {                                                                                                   \
-    if (upd)                                                                                             \
-      hipLaunchKernelGGL((k_block_restrict<LV, N, true>), dim3(grid), dim3(BNT), 0, stream, bg, h->B.U,   \
-                         h->B.W, h->B.g, d_R, d_Y, Q, up);                                               \
-    else                                                                                                 \
-      hipLaunchKernelGGL((k_block_restrict<LV, N, false>), dim3(grid), dim3(BNT), 0, stream, bg, h->B.U,  \
-                         h->B.W, h->B.g, d_R, d_Y, Q, up);                                               \
+    if (upd) HPCG_BLOCK_RESTRICT_UPD(LV, N, true);                                                       \
+    else HPCG_BLOCK_RESTRICT_UPD(LV, N, false);                                                          \
   } while (0)
   switch (h->G.levels) {
 #define HPCG_BLOCK_RESTRICT(LV)                                                                          \
@@ -1061,6 +1080,7 @@ hpcg_status launch_block_apply(hpcg_ctx* h, int32_t nrhs, const float* d_R, floa
     HPCG_BLOCK_RESTRICT(8)
 #undef HPCG_BLOCK_RESTRICT
 #undef HPCG_BLOCK_RESTRICT_N
+#undef HPCG_BLOCK_RESTRICT_UPD
     default: return fail(h, HPCG_ERR_SHAPE, "levels out of range");
   }
   if (h->G.levels > 0) {
@@ -1257,9 +1277,10 @@ hpcg_status hpcg_solve_block(hpcg_handle h, const float* d_B, double* d_X, int32
   const int ncol = G.B * nrhs;
   const dim3 sc_grid((unsigned)((ncol + BS_SC_COLS - 1) / BS_SC_COLS));
 
-  // the recorded iterations depend on the buffers, nrhs, tol, maxit and the unroll
+  // the recorded iterations depend on the buffers, nrhs, tol, maxit, the unroll
+  // and the block split
   if (!h->bs_gexec || h->bs_key[0] != d_X || h->bs_key[1] != wk || h->bs_nrhs != nrhs || h->bs_tol != tol ||
-      h->bs_maxit != maxit || h->bs_unroll != h->unroll) {
+      h->bs_maxit != maxit || h->bs_unroll != h->unroll || h->bs_split != h->block_split) {
     if (h->bs_gexec) (void)hipGraphExecDestroy(h->bs_gexec);
     if (h->bs_graph) (void)hipGraphDestroy(h->bs_graph);
     h->bs_gexec = nullptr;
@@ -1282,6 +1303,7 @@ hpcg_status hpcg_solve_block(hpcg_handle h, const float* d_B, double* d_X, int32
     h->bs_tol = tol;
     h->bs_maxit = maxit;
     h->bs_unroll = h->unroll;
+    h->bs_split = h->block_split;
   }
 
   // R = B, X = 0, ||B_j||, Z = M R, rz, P = Z
@@ -1649,6 +1671,10 @@ hpcg_status hpcg_set_option(hpcg_handle h, int32_t option, int32_t value) {
     case HPCG_OPT_APPLY_PATH:
       if (value < HPCG_APPLY_AUTO || value > HPCG_APPLY_BRIDGE) return fail(h, HPCG_ERR_INVALID_ARG, "bad apply path");
       h->apply_path = value;
+      return HPCG_OK;
+    case HPCG_OPT_BLOCK_SPLIT:
+      if (value < 0 || value > 2) return fail(h, HPCG_ERR_INVALID_ARG, "block split must be 0 (automatic), 1 or 2");
+      h->block_split = value;
       return HPCG_OK;
     case HPCG_OPT_LEAF_SPLIT: {
       if (value != 0 && value != 1 && value != 2 && value != 4 && value != 8)

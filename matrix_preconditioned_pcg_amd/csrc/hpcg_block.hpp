@@ -69,6 +69,23 @@ __device__ __forceinline__ BItem bitem(const BlockGeom& G) {
   return o;
 }
 
+// The same dealing over two workgroups per item (SPLIT): role 0 and role 1 of
+// an item are consecutive in the dealt order, so they run on one XCD.
+__device__ __forceinline__ BItem bitem2(const BlockGeom& G, int& role) {
+  BItem o;
+  const int nblk = 2 * G.B * G.K * G.tiles;
+  const int b = (nblk % NXCD) ? (int)blockIdx.x
+                              : (int)(blockIdx.x % NXCD) * (nblk / NXCD) + (int)(blockIdx.x / NXCD);
+  role = b & 1;
+  const int item = b >> 1;
+  o.ct = item % G.tiles;
+  const int lk = item / G.tiles;
+  o.s = lk / G.K;
+  o.k = lk - o.s * G.K;
+  o.leaf0 = o.s * G.n + o.k * LEAF;
+  return o;
+}
+
 // Q layout: [B][levels][K][RANK][nrhs].
 __device__ __forceinline__ size_t q_index(const BlockGeom& G, int s, int l, int k, int row) {
   return ((((size_t)s * G.levels + l) * G.K + k) * RANK + row) * G.nrhs;
@@ -98,45 +115,90 @@ struct BlockDot {
 // are issued before its products, and the next level's before this level's.
 // A workgroup owns NCT 16-column tiles (BW = 16 NCT columns): every U_k and
 // W_l[k] operand it loads feeds the MFMAs of all NCT tiles.  R is only read
-// through the DMA into LDS, before any write of the UPD update.
-template <int LEV, int NCT, bool UPD = false>
-__global__ __launch_bounds__(BNT) void k_block_restrict(BlockGeom G, const float* __restrict__ U,
+// through the DMA into LDS, before any write of the UPD update.  SPLIT runs
+// the leaf stage (role 0) and the restriction (role 1) of an item in two
+// workgroups, each with its own copy of the R tile (both take the UPD update,
+// the same arithmetic; role 0 writes it back and leaves the partials).  With
+// SPLIT, role 1 loads the operands of all its levels at once; in one
+// workgroup the levels' operands are double-buffered (a level's loads are
+// issued a level ahead).  At most 256 VGPRs (two waves per SIMD), so that two
+// workgroups share a compute unit.
+template <int LEV, int NCT, bool UPD = false, bool SPLIT = false>
+__global__ __launch_bounds__(BNT, 2) void k_block_restrict(BlockGeom G, const float* __restrict__ U,
                                                         const float* __restrict__ W, const float* __restrict__ g,
                                                         const float* R, float* __restrict__ Y,
                                                         float* __restrict__ Q, BlockUpd up) {
   constexpr int BW = BNC * NCT;
   constexpr int C4 = BW / 4;                 // 16-byte chunks per tile row
   constexpr int CH = LEAF * C4 / BNT;        // chunks of the tile per thread
+  constexpr int WL = (LEV + 1) / 2;          // levels of a wave, at most
   __shared__ __attribute__((aligned(16))) float Rs[LEAF * BW];          // R_k tile, [row][BW]
   __shared__ __attribute__((aligned(16))) float Ts[BW * TS_STRIDE];     // T^T, [col][row]
   __shared__ double red[UPD ? NWAVE * BW : 1];
-  const BItem it = bitem(G);
+  int role = 0;
+  const BItem it = SPLIT ? bitem2(G, role) : bitem(G);
+  const bool leaf_role = !SPLIT || role == 0;      // leaf stage, gate, write-back
+  const int wgi = (int)blockIdx.x;
+  stamp(wgi, 0);
+  stamp_value(wgi, 7, (unsigned long long)(SPLIT ? role : 2));
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int q = lane >> 4, r = lane & 15;
   const int c0 = it.ct * BW;
   const float* Uk = U + ((size_t)it.s * G.K + it.k) * LEAF * LEAF;
-  // restriction work of this wave: rank tile (w & 1) of levels (w >> 1), +2, ...
-  const int mt = w & 1;
+  // restriction work of this wave: rank tile (w & 1) of levels par, par + 2, ...
+  const int mt = w & 1, par = w >> 1;
   auto wlev = [&](int l) {
     return W + (((size_t)it.s * LEV + l) * G.K + it.k) * LEAF * RANK + 16 * mt + r;
+  };
+  auto load_level = [&](float (&dst)[32], int l) {
+    const float* Wl = wlev(l);
+#pragma unroll
+    for (int s = 0; s < 32; ++s) dst[s] = Wl[(size_t)(4 * s + q) * RANK];
+  };
+  // GEMM 2 operands: rows 32w + r and 32w + 16 + r of U_k
+  mf4 au[LEAF / 16], bu[LEAF / 16];
+  auto load_gemm2 = [&]() {
+    asm volatile("" ::: "memory");   // issued where called, not hoisted over GEMM 1
+    const float* Ua = Uk + (size_t)(32 * w + r) * LEAF + 4 * q;
+    const float* Ub = Ua + 16 * LEAF;
+#pragma unroll
+    for (int ch = 0; ch < LEAF / 16; ++ch) {
+      au[ch] = *reinterpret_cast<const mf4*>(Ua + 16 * ch);
+      bu[ch] = *reinterpret_cast<const mf4*>(Ub + 16 * ch);
+    }
+  };
+  // GEMM 1 A operands: U[4s + q][32w + r] and U[4s + q][32w + 16 + r], s = 0..31,
+  // and the gate at the lane's rows of Y
+  float ua[32], ub[32], gv[8];
+  auto load_leaf = [&]() {
+#pragma unroll
+    for (int s = 0; s < 32; ++s) {
+      const float* row = Uk + (size_t)(4 * s + q) * LEAF + 32 * w + r;
+      ua[s] = row[0];
+      ub[s] = row[16];
+    }
+  };
+  auto load_gate = [&]() {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      gv[v] = g[it.leaf0 + 32 * w + 4 * q + v];
+      gv[4 + v] = g[it.leaf0 + 32 * w + 16 + 4 * q + v];
+    }
+  };
+  float wv[SPLIT ? WL : 2][32];
+  auto load_restr = [&]() {
+    if constexpr (SPLIT) {
+#pragma unroll
+      for (int i = 0; i < WL; ++i)
+        if (par + 2 * i < LEV) load_level(wv[i], par + 2 * i);
+    } else {
+      if (par < LEV) load_level(wv[0], par);
+    }
   };
   // R tile: 128 rows x 4 BW bytes, straight into LDS
   dma_to_lds(Rs, LEAF * BW / 4, [&](int c) {
     return R + (size_t)(it.leaf0 + c / (BW / 4)) * G.nrhs + c0 + 4 * (c % (BW / 4));
   });
-  // GEMM 1 A operands: U[4s + q][32w + r] and U[4s + q][32w + 16 + r], s = 0..31
-  float ua[32], ub[32], wa[32];
-#pragma unroll
-  for (int s = 0; s < 32; ++s) {
-    const float* row = Uk + (size_t)(4 * s + q) * LEAF + 32 * w + r;
-    ua[s] = row[0];
-    ub[s] = row[16];
-  }
-  if (LEV > (w >> 1)) {
-    const float* Wl = wlev(w >> 1);
-#pragma unroll
-    for (int s = 0; s < 32; ++s) wa[s] = Wl[(size_t)(4 * s + q) * RANK];
-  }
   // UPD: the thread's chunks c = tid + BNT i of the tile, all in its four
   // columns cc..cc+3 (BNT is a multiple of C4)
   const int cc = c0 + 4 * (tid % C4);
@@ -151,114 +213,181 @@ __global__ __launch_bounds__(BNT) void k_block_restrict(BlockGeom G, const float
       ap[i] = *reinterpret_cast<const mf4*>(up.AP + (size_t)(it.leaf0 + row) * G.nrhs + cc);
     }
   }
-  lds_dma_wait();
-  if constexpr (UPD) {
+  // every load so far has landed; the UPD update of the R tile
+  auto wait_update = [&]() {
+    lds_dma_wait();
+    stamp(wgi, 1);
+    if constexpr (UPD) {
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = tid + BNT * i, row = c / C4;
-      mf4 v = *reinterpret_cast<const mf4*>(&Rs[4 * c]);
+      for (int i = 0; i < CH; ++i) {
+        const int c = tid + BNT * i, row = c / C4;
+        mf4 v = *reinterpret_cast<const mf4*>(&Rs[4 * c]);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        if (al[t] != 0.0) v[t] = (float)((double)v[t] - al[t] * (double)ap[i][t]);
-        rr4[t] = fma((double)v[t], (double)v[t], rr4[t]);
+        for (int t = 0; t < 4; ++t) {
+          if (al[t] != 0.0) v[t] = (float)((double)v[t] - al[t] * (double)ap[i][t]);
+          rr4[t] = fma((double)v[t], (double)v[t], rr4[t]);
+        }
+        *reinterpret_cast<mf4*>(&Rs[4 * c]) = v;
+        if (leaf_role) *reinterpret_cast<mf4*>(up.R + (size_t)(it.leaf0 + row) * G.nrhs + cc) = v;
       }
-      *reinterpret_cast<mf4*>(&Rs[4 * c]) = v;
-      *reinterpret_cast<mf4*>(up.R + (size_t)(it.leaf0 + row) * G.nrhs + cc) = v;
+      if (leaf_role) {
+        // R.R partials of the wave: lanes with the same columns differ in lane
+        // bits >= log2(C4) (fixed butterfly); summed over the waves at the end
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+#pragma unroll
+          for (int o = C4; o < 64; o <<= 1) rr4[t] += __shfl_xor(rr4[t], o);
+        }
+        if (lane < C4) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) red[w * BW + 4 * lane + t] = rr4[t];
+        }
+      }
+      __syncthreads();
     }
-    __syncthreads();
-  }
-  // T = U_k^T R_k: this wave's rows [32w, 32w + 32) of T, for every tile
-  mf4 ta[NCT], tb[NCT];
+    stamp(wgi, 2);
+  };
+  // T = U_k^T R_k: this wave's rows [32w, 32w + 32) of T, for every tile,
+  // then T^T into LDS (lane holds T[32w + 4q + v][16j + r] and + 16)
+  auto gemm1 = [&]() {
+    mf4 ta[NCT], tb[NCT];
 #pragma unroll
-  for (int j = 0; j < NCT; ++j) ta[j] = tb[j] = mf4{0, 0, 0, 0};
+    for (int j = 0; j < NCT; ++j) ta[j] = tb[j] = mf4{0, 0, 0, 0};
+    // B operands eight k-steps at a time, read ahead of their products
 #pragma unroll
-  for (int s = 0; s < 32; ++s) {
+    for (int s0 = 0; s0 < 32; s0 += 8) {
+      float bv[8][NCT];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+#pragma unroll
+        for (int j = 0; j < NCT; ++j) bv[u][j] = Rs[(4 * (s0 + u) + q) * BW + 16 * j + r];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+#pragma unroll
+        for (int j = 0; j < NCT; ++j) {
+          ta[j] = mfma4(ua[s0 + u], bv[u][j], ta[j]);
+          tb[j] = mfma4(ub[s0 + u], bv[u][j], tb[j]);
+        }
+      }
+    }
 #pragma unroll
     for (int j = 0; j < NCT; ++j) {
-      const float bv = Rs[(4 * s + q) * BW + 16 * j + r];
-      ta[j] = mfma4(ua[s], bv, ta[j]);
-      tb[j] = mfma4(ub[s], bv, tb[j]);
+      *reinterpret_cast<mf4*>(&Ts[(16 * j + r) * TS_STRIDE + 32 * w + 4 * q]) = ta[j];
+      *reinterpret_cast<mf4*>(&Ts[(16 * j + r) * TS_STRIDE + 32 * w + 16 + 4 * q]) = tb[j];
     }
-  }
-  // T^T into LDS: lane holds T[32w + 4q + v][16j + r] (and + 16)
-#pragma unroll
-  for (int j = 0; j < NCT; ++j) {
-    *reinterpret_cast<mf4*>(&Ts[(16 * j + r) * TS_STRIDE + 32 * w + 4 * q]) = ta[j];
-    *reinterpret_cast<mf4*>(&Ts[(16 * j + r) * TS_STRIDE + 32 * w + 16 + 4 * q]) = tb[j];
-  }
+    stamp(wgi, 3);
+  };
   // restriction Q_l = W_l[k]^T R_k, two accumulation chains (even / odd k
-  // steps) summed at the end
+  // steps) summed at the end.  SPLIT: every level's operands are in registers,
+  // so the tiles are the outer loop and a tile's R operands are read once.
+  auto restriction = [&]() {
+    if constexpr (SPLIT) {
 #pragma unroll
-  for (int l = 0; l < LEV; ++l) {
-    if ((l & 1) != (w >> 1)) continue;
-    float wn[32];
-    if (l + 2 < LEV) {
-      const float* Wn = wlev(l + 2);
+      for (int j = 0; j < NCT; ++j) {
+        float rv[32];
 #pragma unroll
-      for (int s = 0; s < 32; ++s) wn[s] = Wn[(size_t)(4 * s + q) * RANK];
-    }
-    float* Qo = Q + q_index(G, it.s, l, it.k, 16 * mt + 4 * q) + c0 + r;
+        for (int s = 0; s < 32; ++s) rv[s] = Rs[(4 * s + q) * BW + 16 * j + r];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < NCT; ++j) {
-      mf4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
+        for (int i = 0; i < WL; ++i) {
+          const int l = par + 2 * i;
+          if (l >= LEV) break;
+          mf4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
 #pragma unroll
-      for (int s = 0; s < 32; s += 2) {
-        a0 = mfma4(wa[s], Rs[(4 * s + q) * BW + 16 * j + r], a0);
-        a1 = mfma4(wa[s + 1], Rs[(4 * s + 4 + q) * BW + 16 * j + r], a1);
+          for (int s = 0; s < 32; s += 2) {
+            a0 = mfma4(wv[i][s], rv[s], a0);
+            a1 = mfma4(wv[i][s + 1], rv[s + 1], a1);
+          }
+          const mf4 acc = a0 + a1;
+          float* Qo = Q + q_index(G, it.s, l, it.k, 16 * mt + 4 * q) + c0 + r;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) Qo[(size_t)v * G.nrhs + 16 * j] = acc[v];
+        }
       }
-      const mf4 acc = a0 + a1;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) Qo[(size_t)v * G.nrhs + 16 * j] = acc[v];
+      stamp(wgi, 4);
+      return;
     }
-    if (l + 2 < LEV) {
 #pragma unroll
-      for (int s = 0; s < 32; ++s) wa[s] = wn[s];
+    for (int i = 0; i < WL; ++i) {
+      const int l = par + 2 * i;
+      if (l >= LEV) break;
+      // the level two ahead, issued here and not hoisted (that would hold
+      // every level's operands at once)
+      asm volatile("" ::: "memory");
+      if (l + 2 < LEV) load_level(wv[(i + 1) & 1], l + 2);
+      const float(&wa)[32] = wv[i & 1];
+      float* Qo = Q + q_index(G, it.s, l, it.k, 16 * mt + 4 * q) + c0 + r;
+#pragma unroll
+      for (int j = 0; j < NCT; ++j) {
+        float rv[32];
+#pragma unroll
+        for (int s = 0; s < 32; ++s) rv[s] = Rs[(4 * s + q) * BW + 16 * j + r];
+        __builtin_amdgcn_sched_barrier(0);
+        mf4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
+#pragma unroll
+        for (int s = 0; s < 32; s += 2) {
+          a0 = mfma4(wa[s], rv[s], a0);
+          a1 = mfma4(wa[s + 1], rv[s + 1], a1);
+        }
+        const mf4 acc = a0 + a1;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) Qo[(size_t)v * G.nrhs + 16 * j] = acc[v];
+      }
     }
+    stamp(wgi, 4);
+  };
+  if (SPLIT && role == 1) {        // the restriction alone: its operands of every level at once
+    load_restr();
+    wait_update();
+    restriction();
+    return;
   }
-  // GEMM 2 operands: rows 32w + r and 32w + 16 + r of U_k (L2-resident by now)
-  const float* Ua = Uk + (size_t)(32 * w + r) * LEAF + 4 * q;
-  const float* Ub = Ua + 16 * LEAF;
-  mf4 au[LEAF / 16], bu[LEAF / 16];
-#pragma unroll
-  for (int ch = 0; ch < LEAF / 16; ++ch) {
-    au[ch] = *reinterpret_cast<const mf4*>(Ua + 16 * ch);
-    bu[ch] = *reinterpret_cast<const mf4*>(Ub + 16 * ch);
+  load_leaf();
+  if constexpr (SPLIT) {
+    load_gate();
+    wait_update();
+    gemm1();
+    load_gemm2();
+  } else {
+    load_restr();
+    wait_update();
+    gemm1();
+    restriction();
+    load_gemm2();                  // U_k is L2-resident by now
+    load_gate();
   }
   __syncthreads();
+  stamp(wgi, 5);
   // Y = U_k T + g R: this wave's rows [32w, 32w + 32), tile by tile
 #pragma unroll
   for (int j = 0; j < NCT; ++j) {
     mf4 ya = {0, 0, 0, 0}, yb = {0, 0, 0, 0};
+    mf4 bt[LEAF / 16];             // the tile's T operands, read ahead of the products
+#pragma unroll
+    for (int ch = 0; ch < LEAF / 16; ++ch)
+      bt[ch] = *reinterpret_cast<const mf4*>(&Ts[(16 * j + r) * TS_STRIDE + 16 * ch + 4 * q]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ch = 0; ch < LEAF / 16; ++ch) {
-      const mf4 bt = *reinterpret_cast<const mf4*>(&Ts[(16 * j + r) * TS_STRIDE + 16 * ch + 4 * q]);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        ya = mfma4(au[ch][t], bt[t], ya);
-        yb = mfma4(bu[ch][t], bt[t], yb);
+        ya = mfma4(au[ch][t], bt[ch][t], ya);
+        yb = mfma4(bu[ch][t], bt[ch][t], yb);
       }
     }
     const int cj = c0 + 16 * j + r;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int ia = 32 * w + 4 * q + v, ib = ia + 16;
-      Y[(size_t)(it.leaf0 + ia) * G.nrhs + cj] = ya[v] + g[it.leaf0 + ia] * Rs[ia * BW + 16 * j + r];
-      Y[(size_t)(it.leaf0 + ib) * G.nrhs + cj] = yb[v] + g[it.leaf0 + ib] * Rs[ib * BW + 16 * j + r];
+      Y[(size_t)(it.leaf0 + ia) * G.nrhs + cj] = ya[v] + gv[v] * Rs[ia * BW + 16 * j + r];
+      Y[(size_t)(it.leaf0 + ib) * G.nrhs + cj] = yb[v] + gv[4 + v] * Rs[ib * BW + 16 * j + r];
     }
   }
+  stamp(wgi, 6);
   if constexpr (UPD) {
-    // R.R partials: lanes of a wave with the same columns differ in lane bits
-    // >= log2(C4) (fixed butterfly), then the four waves in order
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int o = C4; o < 64; o <<= 1) rr4[t] += __shfl_xor(rr4[t], o);
-    }
-    if (lane < C4) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) red[w * BW + 4 * lane + t] = rr4[t];
-    }
-    __syncthreads();
+    // R.R partials: the four waves' sums (left in red by the update) in order
     if (tid < BW)
       up.rr[((size_t)it.s * G.K + it.k) * G.nrhs + c0 + tid] =
           ((red[tid] + red[BW + tid]) + red[2 * BW + tid]) + red[3 * BW + tid];
@@ -313,6 +442,7 @@ __global__ __launch_bounds__(BNT) void k_block_prolong(BlockGeom G, const float*
   __shared__ __attribute__((aligned(16))) float Ps[(LEV > 0 ? LEV : 1) * BW * PS_STRIDE];   // [l][col][rank]
   __shared__ double red[DOT ? NWAVE * BW : 1];
   const BItem it = bitem(G);
+  stamp((int)blockIdx.x, 8);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int q = lane >> 4, r = lane & 15;
   const int c0 = it.ct * BW;
@@ -366,6 +496,7 @@ __global__ __launch_bounds__(BNT) void k_block_prolong(BlockGeom G, const float*
     Ps[(l * BW + col) * PS_STRIDE + row] = hv[u];
   }
   __syncthreads();
+  stamp((int)blockIdx.x, 9);
 #pragma unroll
   for (int l = 0; l < LEV; ++l) {
 #pragma unroll
@@ -381,6 +512,7 @@ __global__ __launch_bounds__(BNT) void k_block_prolong(BlockGeom G, const float*
       }
     }
   }
+  stamp((int)blockIdx.x, 10);
 #pragma unroll
   for (int j = 0; j < NCT; ++j) {
 #pragma unroll
@@ -389,6 +521,7 @@ __global__ __launch_bounds__(BNT) void k_block_prolong(BlockGeom G, const float*
       Y[(size_t)(it.leaf0 + 32 * w + 16 + 4 * q + v) * G.nrhs + c0 + 16 * j + r] = yb[j][v];
     }
   }
+  stamp((int)blockIdx.x, 11);
   if constexpr (DOT) {
     // R.Z partials: the lane's eight rows, then the four lane groups q (fixed
     // butterfly), then the four waves in order

@@ -62,8 +62,13 @@ __device__ __forceinline__ void stamp(int wg, int slot) {
   if (threadIdx.x == 0 && wg < kTraceItems)
     trace_table[wg * kTraceSlots + slot] = __builtin_amdgcn_s_memrealtime();
 }
+// a plain value in place of a time (a workgroup's role, say)
+__device__ __forceinline__ void stamp_value(int wg, int slot, unsigned long long v) {
+  if (threadIdx.x == 0 && wg < kTraceItems) trace_table[wg * kTraceSlots + slot] = v;
+}
 #else
 __device__ __forceinline__ void stamp(int, int) {}
+__device__ __forceinline__ void stamp_value(int, int, unsigned long long) {}
 #endif
 
 enum : int { ST_RUNNING = 0, ST_CONVERGED = 1, ST_NOT_CONVERGED = 2, ST_BREAKDOWN = 3 };

@@ -43,6 +43,7 @@ HPCG_OPT_ENGINE = 1
 HPCG_OPT_GRAPH_UNROLL = 2
 HPCG_OPT_PRECISION = 4
 HPCG_OPT_LEAF_SPLIT = 8
+HPCG_OPT_BLOCK_SPLIT = 512
 HPCG_OPT_APPLY_PATH = 16
 
 HPCG_OPT_FORM = 32

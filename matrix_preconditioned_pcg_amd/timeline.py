@@ -1,6 +1,7 @@
 """In-kernel timeline of the single-pass apply and the SpMV (a measurement aid).
 
     python -m matrix_preconditioned_pcg_amd.timeline [--config N16k] [--build] [--calls 200]
+    python -m matrix_preconditioned_pcg_amd.timeline --config N8k --block 96
 
 Runs the HPCG_TRACE build of the library (libhpcg_trace.so, compiled first
 with --build or when missing): the kernels record thread 0's reading of the
@@ -36,6 +37,13 @@ SPLIT_DIAG = {0: "start", 1: "r in LDS", 2: "U_k U_k^T r published"}
 SPLIT_OFF = {0: "start", 1: "r in LDS", 2: "restriction published",
              5: "partner + diagonal words gathered", 6: "prolongation done", 7: "y stored and acknowledged"}
 SPMV = {0: "start", 7: "y stored and acknowledged"}
+BLOCK_LEAF = {0: "start", 1: "R tile and operands landed", 2: "residual update done (block solve)",
+              3: "T = U_k^T R in LDS", 5: "GEMM 2 operands in", 6: "Y stores issued"}
+BLOCK_RESTR = {0: "start", 1: "R tile and operands landed", 2: "residual update done (block solve)",
+               4: "restrictions stored"}
+BLOCK_BOTH = {0: "start", 1: "R tile and operands landed", 2: "residual update done (block solve)",
+              3: "T = U_k^T R in LDS", 4: "restrictions stored", 5: "GEMM 2 operands in", 6: "Y stores issued"}
+BLOCK_PROLONG = {8: "start", 9: "half sums in LDS", 10: "products done", 11: "Y stores issued"}
 RESIDENT = {0: "iteration start", 1: "halo z and r.r, r.z partials polled", 2: "SpMV done",
             3: "restriction of q and p.q published", 4: "U_k U_k^T q done",
             5: "partners' W^T q and p.q polled", 6: "alpha, r, x and z = M r done", 7: "exact refresh (when due)",
@@ -58,6 +66,9 @@ def main(argv=None):
     ap.add_argument("--build", action="store_true")
     ap.add_argument("--bridge", action="store_true", help="factors in the bridge format (native bridge apply)")
     ap.add_argument("--solve", action="store_true", help="also one resident solve: its 65th iteration")
+    ap.add_argument("--block", type=int, default=0, metavar="NRHS",
+                    help="instead: the block apply's leaf stage and prolongation on NRHS columns, in a "
+                         "replayed graph of block applies and in the last iteration of a block solve")
     args = ap.parse_args(argv)
     from matrix_preconditioned_pcg_amd import build as build_mod
     if args.build or not os.path.exists(build_mod.TRACE_LIB):
@@ -99,6 +110,9 @@ def main(argv=None):
         torch.cuda.synchronize()
         del g
 
+    if args.block:
+        solver.close()
+        return block_timeline(args, batch, stream, hpcg, torch)
     fmt = " --bridge" if args.bridge else ""
     out = [f"# In-kernel timeline, {args.config} (n = {batch.n}, K = {batch.K}, {batch.levels} levels, "
            f"batch {batch.batch}){', bridge-format factors' if args.bridge else ''}", "",
@@ -152,6 +166,76 @@ def main(argv=None):
             out += ["", "Per workgroup, median time between consecutive stamps (us):", "",
                     "| from | to | median |", "|---|---|---|"]
             out += [f"| {names[i]} | {names[i + 1]} | {np.median(d[:, i]):.2f} |" for i in range(d.shape[1])]
+    solver.close()
+    print("\n".join(out))
+    return 0
+
+
+def block_tables(st, items, title):
+    """Tables of the leaf-stage kernel (by role) and of the prolongation."""
+    role = st[:, 7].astype(np.int64)
+    split = bool(np.any(role[:2 * items] == 1))
+    nwg = 2 * items if split else items
+    wg = st[:nwg]
+    t0 = int(wg[:, 0].astype(np.int64).min())
+    out = []
+    if split:
+        r = role[:nwg]
+        out += [table(f"{title}: leaf stage (role 0 of two workgroups per item)", wg[r == 0], BLOCK_LEAF, t0), "",
+                table(f"{title}: restriction (role 1)", wg[r == 1], BLOCK_RESTR, t0), ""]
+        end = int(wg[r == 0][:, 6].astype(np.int64).max())
+    else:
+        out += [table(f"{title}: leaf stage and restriction (one workgroup per item)", wg, BLOCK_BOTH, t0), ""]
+        end = int(wg[:, 6].astype(np.int64).max())
+    out += [f"Leaf-stage kernel: first start to last Y store issued {(end - t0) * TICK_US:.2f} us.", ""]
+    pw = st[:items]
+    t1 = int(pw[:, 8].astype(np.int64).min())
+    out += [table(f"{title}: prolongation", pw, BLOCK_PROLONG, t1), "",
+            f"Prolongation: first start to last Y store issued "
+            f"{(int(pw[:, 11].astype(np.int64).max()) - t1) * TICK_US:.2f} us.", ""]
+    return out
+
+
+def block_timeline(args, batch, stream, hpcg, torch):
+    nrhs = args.block
+    solver = hpcg.Solver(batch.n, batch.row_ptr, batch.col, batch.val, batch=batch.batch, levels=batch.levels,
+                         stream=stream)
+    solver.set_factors(batch.U, batch.W, batch.g)
+    R = torch.randn(batch.batch * batch.n * nrhs, device="cuda", dtype=torch.float32)
+    Y = torch.empty_like(R)
+    work = torch.empty(hpcg.hpcg_block_workspace_bytes(solver.handle, nrhs), dtype=torch.uint8, device="cuda")
+    with torch.cuda.stream(stream):
+        fn = lambda: hpcg.hpcg_apply_M_block(solver.handle, solver.part, R, Y, nrhs, work)  # noqa: E731
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(max(1, args.calls // 10)):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        hpcg.hpcg_trace_read(0, clear=True)
+        g.replay()
+        torch.cuda.synchronize()
+        del g
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    # items = (system, leaf, column tile) workgroups of the kernels: read enough rows
+    st = np.array(hpcg.hpcg_trace_read(4096 * SLOTS), dtype=np.uint64).reshape(4096, SLOTS)
+    items = int(np.count_nonzero(st[:, 8]))
+    out = [f"# In-kernel timeline of the block apply, {args.config} (n = {batch.n}, K = {batch.K}, "
+           f"{batch.levels} levels, batch {batch.batch}), {nrhs} columns", "",
+           f"Command: `python -m matrix_preconditioned_pcg_amd.timeline --config {args.config} --block {nrhs} "
+           f"--build`", "", f"{items} (leaf, column tile) items on {ncu} compute units.", ""]
+    out += block_tables(st, items, "block apply")
+    Bm = torch.randn(batch.batch * batch.n * nrhs, device="cuda", dtype=torch.float32)
+    solver.solve_block(Bm, nrhs, tol=batch.tol, maxit=batch.maxit)
+    torch.cuda.synchronize()
+    hpcg.hpcg_trace_read(0, clear=True)
+    _x, its, _rel, _st = solver.solve_block(Bm, nrhs, tol=batch.tol, maxit=batch.maxit)
+    torch.cuda.synchronize()
+    st = np.array(hpcg.hpcg_trace_read(4096 * SLOTS), dtype=np.uint64).reshape(4096, SLOTS)
+    out += [f"Block solve ({min(its)}-{max(its)} iterations): the last iteration's kernels.", ""]
+    out += block_tables(st, items, "block solve")
     solver.close()
     print("\n".join(out))
     return 0

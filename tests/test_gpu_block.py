@@ -132,3 +132,33 @@ def test_block_argument_errors():
     with pytest.raises(hpcg.HPCGError):
         hpcg.hpcg_spmv_block(s.handle, s.part, R, R, 16)
     s.close()
+
+
+@pytest.mark.parametrize("name,nrhs", [("N1k", 32), ("N8k", 32), ("N8k", 96), ("N16k", 16)])
+def test_block_split_agrees(name, nrhs):
+    # the leaf stage and the restriction in one workgroup or in two (the
+    # automatic choice where these shapes leave compute units idle): the same
+    # products in the same order, so the same bits, in the block apply and in
+    # every step of the block solve (whose leaf stage also takes the residual
+    # update); and parity with the oracle on the split path
+    batch = make_config(name)
+    _log(f"block split {name} nrhs={nrhs}")
+    s = _solver(batch)
+    rng = np.random.default_rng(nrhs + 1)
+    R = rng.standard_normal((1, batch.n, nrhs)).astype(np.float32)
+    Bm = rng.standard_normal((1, batch.n, nrhs)).astype(np.float32)
+    out = {}
+    for sp in (1, 2):
+        s.set_option(hpcg.HPCG_OPT_BLOCK_SPLIT, sp)
+        Y = s.apply_M_block(R.reshape(-1), nrhs).clone()
+        X, iters, rel, st = s.solve_block(Bm.reshape(-1), nrhs, tol=batch.tol, maxit=batch.maxit)
+        assert st == hpcg.HPCG_OK, hpcg.hpcg_last_error(s.handle)
+        out[sp] = (Y, X.clone(), list(iters), list(rel))
+    torch.cuda.synchronize()
+    assert torch.equal(out[1][0], out[2][0])
+    assert torch.equal(out[1][1], out[2][1]) and out[1][2] == out[2][2] and out[1][3] == out[2][3]
+    s.set_option(hpcg.HPCG_OPT_BLOCK_SPLIT, 2)
+    _check_block_apply(batch, s, R)
+    with pytest.raises(hpcg.HPCGError):
+        s.set_option(hpcg.HPCG_OPT_BLOCK_SPLIT, 3)
+    s.close()
