@@ -56,11 +56,11 @@ def bridge_apply_bytes(n: int, K: int, levels: int, B: int = 1) -> int:
 
 
 def block_apply_flops(n: int, levels: int, nrhs: int, B: int = 1) -> int:
-    """Algorithmic flops of one block apply: per column the leaf stage (two
-    n x 128 products), restriction and prolongation (two n x 32 products per
-    level) and the gate."""
+    """Algorithmic flops of one block apply: per column the leaf stage (one
+    n x 128 product with the dense leaf blocks F_k = U_k U_k^T), restriction
+    and prolongation (two n x 32 products per level) and the gate."""
     L, R = 128, 32
-    return B * nrhs * (4 * n * L + 4 * n * R * levels + 2 * n)
+    return B * nrhs * (2 * n * L + 4 * n * R * levels + 2 * n)
 
 
 def spmv_bytes(n: int, nnz: int, B: int = 1) -> int:

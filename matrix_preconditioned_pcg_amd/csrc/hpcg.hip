@@ -30,7 +30,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t row_ptr, col, val, U, W, g, b, r, z, q, p0, p1, x, tleaf, pleaf, pq, rr, rz, st, ctl;
+  size_t row_ptr, col, val, U, F, W, g, b, r, z, q, p0, p1, x, tleaf, pleaf, pq, rr, rz, st, ctl;
   size_t wgflag;              // resident engine: per-workgroup barrier lines
   size_t lcol, hoff, hcol;    // resident engine: leaf-local CSR columns and halo lists
   size_t zll, pll;            // resident engine: flagged z words and flagged partials
@@ -121,6 +121,7 @@ Layout make_layout(const Geom& G, int64_t nnz) {
   L.col = take((size_t)nnz * 4);
   L.val = take((size_t)nnz * 4);
   L.U = take((size_t)G.B * G.K * LEAF * LEAF * 4);
+  L.F = take((size_t)G.B * G.K * LEAF * LEAF * 4);    // dense leaf blocks (block apply)
   L.W = take((size_t)G.B * G.levels * G.K * LEAF * RANK * 4);
   L.g = take(N * 4);
   L.b = take(N * 4);
@@ -584,6 +585,7 @@ hpcg_status hpcg_create(const hpcg_partition* part, const int32_t* d_row_ptr, co
   B.col = reinterpret_cast<const int*>(w + lay.col);
   B.val = reinterpret_cast<const float*>(w + lay.val);
   B.U = reinterpret_cast<const float*>(w + lay.U);
+  B.F = reinterpret_cast<const float*>(w + lay.F);
   B.W = reinterpret_cast<const float*>(w + lay.W);
   B.g = reinterpret_cast<const float*>(w + lay.g);
   B.b = reinterpret_cast<const float*>(w + lay.b);
@@ -713,6 +715,10 @@ hpcg_status hpcg_set_factors(hpcg_handle h, const float* d_leafU, const float* d
     HIP_OR_FAIL(h, hipMemcpyAsync(h->ws + h->lay.W, d_tileW, (size_t)G.B * G.levels * G.K * LEAF * RANK * 4,
                                   hipMemcpyDeviceToDevice, h->stream));
   HIP_OR_FAIL(h, hipMemcpyAsync(h->ws + h->lay.g, d_gate, (size_t)G.B * G.n * 4, hipMemcpyDeviceToDevice, h->stream));
+  hipLaunchKernelGGL(k_leaf_blocks, dim3(G.B * G.K), dim3(BNT), 0, h->stream, h->B.U,
+                     reinterpret_cast<float*>(h->ws + h->lay.F));
+  hpcg_status s = check_launch(h, "leaf block launch");
+  if (s != HPCG_OK) return s;
   h->factors_set = true;
   h->bridge_set = false;
   return HPCG_OK;
@@ -874,6 +880,8 @@ hpcg_status hpcg_set_factors_bridge(hpcg_handle h, const float* d_leafF, const f
     HIP_OR_FAIL(h, hipMemcpyAsync(h->ws + h->lay.Bc, d_cores, (size_t)G.B * h->B.ncores * RANK * RANK * 4,
                                   hipMemcpyDeviceToDevice, h->stream));
   }
+  hipLaunchKernelGGL(k_leaf_blocks, dim3(G.B * G.K), dim3(BNT), 0, h->stream, h->B.U,
+                     reinterpret_cast<float*>(h->ws + h->lay.F));
   hpcg_status s = check_launch(h, "bridge expansion launch");
   if (s != HPCG_OK) return s;
   h->factors_set = true;
@@ -1058,10 +1066,10 @@ hpcg_status launch_block_apply(hpcg_ctx* h, int32_t nrhs, const float* d_R, floa
   do {                                                                                                   \
     if (sp && LV > 0 && N < 4)                                                                           \
       hipLaunchKernelGGL((k_block_restrict<LV, N, UP, (LV > 0 && N < 4)>), dim3(2 * grid), dim3(BNT), 0, \
-                         stream, bg, h->B.U, h->B.W, h->B.g, d_R, d_Y, Q, up);                           \
+                         stream, bg, h->B.F, h->B.W, h->B.g, d_R, d_Y, Q, up);                           \
     else                                                                                                 \
       hipLaunchKernelGGL((k_block_restrict<LV, N, UP, false>), dim3(grid), dim3(BNT), 0, stream, bg,      \
-                         h->B.U, h->B.W, h->B.g, d_R, d_Y, Q, up);                                       \
+                         h->B.F, h->B.W, h->B.g, d_R, d_Y, Q, up);                                       \
   } while (0)
 #define HPCG_BLOCK_RESTRICT_N(LV, N)                                                                     \
   do {                                                                                                   \

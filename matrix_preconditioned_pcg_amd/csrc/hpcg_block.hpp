@@ -2,7 +2,8 @@
 // matrix cores.
 //
 // With a block of right-hand sides every stage of the apply is a real GEMM: the
-// leaf stage is U_k (U_k^T R_k) with R_k of 128 x nrhs, the restriction
+// leaf stage is F_k R_k with R_k of 128 x nrhs and F_k = U_k U_k^T the dense
+// leaf block (one product where U_k (U_k^T R_k) takes two), the restriction
 // W_l[k]^T R_k, the prolongation W_l[k] P_l.  This is the probe-block product
 // the pages' training objective needs (M A Z for a probe block Z of N x K_z,
 // project page "Cosine Hutchinson Probe Loss" and "Training Setup"; Supplementary
@@ -22,7 +23,8 @@
 // q = l / 16 contracts k0 + 4q + t in MFMA t); A and B use the same order, so
 // the sum is the same product.
 //
-// Three launches: (1) per (leaf, tile): T = U_k^T R_k, Y = U_k T + g R, and the
+// Three launches: (1) per (leaf, tile): Y = F_k R_k + g R with the dense leaf
+// block F_k = U_k U_k^T (formed once per set of factors, k_leaf_blocks), and the
 // per-leaf restrictions Q_l[k] = W_l[k]^T R_k; (2) per (level, half, element):
 // the half sums of Q_l over every tile half (eq. (3)), in a fixed order; (3) per
 // (leaf, tile): Y += sum_l W_l[k] P_l with P_l the partner half's sum (eqs.
@@ -36,7 +38,7 @@ namespace hpcg {
 
 constexpr int BNC = 16;          // right-hand-side columns per workgroup
 constexpr int BNT = 256;         // threads per workgroup
-constexpr int TS_STRIDE = 132;   // T^T rows in LDS (== 4 mod 64: conflict-free 16-byte reads)
+constexpr int TS_STRIDE = 132;   // R^T rows in LDS (== 4 mod 64: conflict-free 16-byte reads)
 constexpr int PS_STRIDE = 36;    // P^T rows in LDS (== 36 mod 64: conflict-free 16-byte reads)
 
 typedef float mf4 __attribute__((ext_vector_type(4)));
@@ -111,29 +113,59 @@ struct BlockDot {
   double* rz;            // [B][K][nrhs]
 };
 
-// (1) leaf stage, gate and restriction.  All global operand loads of a stage
-// are issued before its products, and the next level's before this level's.
-// A workgroup owns NCT 16-column tiles (BW = 16 NCT columns): every U_k and
-// W_l[k] operand it loads feeds the MFMAs of all NCT tiles.  R is only read
-// through the DMA into LDS, before any write of the UPD update.  SPLIT runs
-// the leaf stage (role 0) and the restriction (role 1) of an item in two
+// Dense leaf blocks F_k = U_k U_k^T, formed once per set of factors so that
+// the block apply's leaf stage is one product F_k R_k: every entry summed in
+// fp64 over the leaf's 128 columns in column order and rounded to fp32 once
+// (F_k is then exactly symmetric).  One workgroup per leaf; U_k is staged in
+// LDS with rows padded to 129 words, so the lanes' walks down a column hit
+// distinct banks.  Thread t owns row t % 128 of half t / 128 of the columns and
+// writes them as column entries (F_k is symmetric), coalesced across lanes.
+__global__ __launch_bounds__(BNT) void k_leaf_blocks(const float* __restrict__ U, float* __restrict__ F) {
+  constexpr int PAD = LEAF + 1;
+  __shared__ float Us[LEAF * PAD];
+  const size_t leaf = blockIdx.x;
+  const float* Uk = U + leaf * LEAF * LEAF;
+  for (int e = threadIdx.x; e < LEAF * LEAF; e += BNT) Us[(e / LEAF) * PAD + e % LEAF] = Uk[e];
+  __syncthreads();
+  const int i = threadIdx.x % LEAF, j0 = (threadIdx.x / LEAF) * (LEAF / 2);
+  double acc[LEAF / 2];
+#pragma unroll
+  for (int jj = 0; jj < LEAF / 2; ++jj) acc[jj] = 0.0;
+  for (int k = 0; k < LEAF; ++k) {
+    const double ui = Us[i * PAD + k];
+#pragma unroll
+    for (int jj = 0; jj < LEAF / 2; ++jj) acc[jj] = fma(ui, (double)Us[(j0 + jj) * PAD + k], acc[jj]);
+  }
+  float* Fk = F + leaf * LEAF * LEAF;
+#pragma unroll
+  for (int jj = 0; jj < LEAF / 2; ++jj) Fk[(size_t)(j0 + jj) * LEAF + i] = (float)acc[jj];
+}
+
+// (1) leaf stage, gate and restriction: Y = F_k R_k + g R (F_k = U_k U_k^T,
+// k_leaf_blocks) and Q_l = W_l[k]^T R_k.  All global operand loads of a stage
+// are issued before its products.  A workgroup owns NCT 16-column tiles (BW =
+// 16 NCT columns): every F_k and W_l[k] operand it loads feeds the MFMAs of all
+// NCT tiles.  R is only read through the DMA into LDS, before any write of the
+// UPD update; the leaf stage reads it through a transposed copy (Ts), where a
+// lane's four contraction steps of one MFMA group are one 16-byte read.  SPLIT
+// runs the leaf stage (role 0) and the restriction (role 1) of an item in two
 // workgroups, each with its own copy of the R tile (both take the UPD update,
 // the same arithmetic; role 0 writes it back and leaves the partials).  With
-// SPLIT, role 1 loads the operands of all its levels at once; in one
-// workgroup the levels' operands are double-buffered (a level's loads are
-// issued a level ahead).  At most 256 VGPRs (two waves per SIMD), so that two
-// workgroups share a compute unit.
+// SPLIT, role 1 loads the operands of all its levels at once; in one workgroup
+// the levels' operands are double-buffered (a level's loads are issued a level
+// ahead).  At most 256 VGPRs (two waves per SIMD), so that two workgroups share
+// a compute unit.
 template <int LEV, int NCT, bool UPD = false, bool SPLIT = false>
-__global__ __launch_bounds__(BNT, 2) void k_block_restrict(BlockGeom G, const float* __restrict__ U,
-                                                        const float* __restrict__ W, const float* __restrict__ g,
-                                                        const float* R, float* __restrict__ Y,
-                                                        float* __restrict__ Q, BlockUpd up) {
+__global__ __launch_bounds__(BNT, 2) void k_block_restrict(BlockGeom G, const float* __restrict__ F,
+                                                           const float* __restrict__ W, const float* __restrict__ g,
+                                                           const float* R, float* __restrict__ Y,
+                                                           float* __restrict__ Q, BlockUpd up) {
   constexpr int BW = BNC * NCT;
   constexpr int C4 = BW / 4;                 // 16-byte chunks per tile row
   constexpr int CH = LEAF * C4 / BNT;        // chunks of the tile per thread
   constexpr int WL = (LEV + 1) / 2;          // levels of a wave, at most
   __shared__ __attribute__((aligned(16))) float Rs[LEAF * BW];          // R_k tile, [row][BW]
-  __shared__ __attribute__((aligned(16))) float Ts[BW * TS_STRIDE];     // T^T, [col][row]
+  __shared__ __attribute__((aligned(16))) float Ts[BW * TS_STRIDE];     // R_k^T, [col][row]
   __shared__ double red[UPD ? NWAVE * BW : 1];
   int role = 0;
   const BItem it = SPLIT ? bitem2(G, role) : bitem(G);
@@ -144,7 +176,7 @@ __global__ __launch_bounds__(BNT, 2) void k_block_restrict(BlockGeom G, const fl
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int q = lane >> 4, r = lane & 15;
   const int c0 = it.ct * BW;
-  const float* Uk = U + ((size_t)it.s * G.K + it.k) * LEAF * LEAF;
+  const float* Fk = F + ((size_t)it.s * G.K + it.k) * LEAF * LEAF;
   // restriction work of this wave: rank tile (w & 1) of levels par, par + 2, ...
   const int mt = w & 1, par = w >> 1;
   auto wlev = [&](int l) {
@@ -155,30 +187,19 @@ __global__ __launch_bounds__(BNT, 2) void k_block_restrict(BlockGeom G, const fl
 #pragma unroll
     for (int s = 0; s < 32; ++s) dst[s] = Wl[(size_t)(4 * s + q) * RANK];
   };
-  // GEMM 2 operands: rows 32w + r and 32w + 16 + r of U_k
-  mf4 au[LEAF / 16], bu[LEAF / 16];
-  auto load_gemm2 = [&]() {
-    asm volatile("" ::: "memory");   // issued where called, not hoisted over GEMM 1
-    const float* Ua = Uk + (size_t)(32 * w + r) * LEAF + 4 * q;
-    const float* Ub = Ua + 16 * LEAF;
+  // leaf-stage A operands: rows 32w + r and 32w + 16 + r of F_k, columns
+  // 16 ch + 4 q .. + 3 (MFMA t of group ch contracts k = 16 ch + 4 q + t), and
+  // the gate at the lane's rows of Y
+  mf4 af[LEAF / 16], bf[LEAF / 16];
+  float gv[8];
+  auto load_leaf = [&]() {
+    const float* Fa = Fk + (size_t)(32 * w + r) * LEAF + 4 * q;
+    const float* Fb = Fa + 16 * LEAF;
 #pragma unroll
     for (int ch = 0; ch < LEAF / 16; ++ch) {
-      au[ch] = *reinterpret_cast<const mf4*>(Ua + 16 * ch);
-      bu[ch] = *reinterpret_cast<const mf4*>(Ub + 16 * ch);
+      af[ch] = *reinterpret_cast<const mf4*>(Fa + 16 * ch);
+      bf[ch] = *reinterpret_cast<const mf4*>(Fb + 16 * ch);
     }
-  };
-  // GEMM 1 A operands: U[4s + q][32w + r] and U[4s + q][32w + 16 + r], s = 0..31,
-  // and the gate at the lane's rows of Y
-  float ua[32], ub[32], gv[8];
-  auto load_leaf = [&]() {
-#pragma unroll
-    for (int s = 0; s < 32; ++s) {
-      const float* row = Uk + (size_t)(4 * s + q) * LEAF + 32 * w + r;
-      ua[s] = row[0];
-      ub[s] = row[16];
-    }
-  };
-  auto load_gate = [&]() {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       gv[v] = g[it.leaf0 + 32 * w + 4 * q + v];
@@ -213,24 +234,31 @@ __global__ __launch_bounds__(BNT, 2) void k_block_restrict(BlockGeom G, const fl
       ap[i] = *reinterpret_cast<const mf4*>(up.AP + (size_t)(it.leaf0 + row) * G.nrhs + cc);
     }
   }
-  // every load so far has landed; the UPD update of the R tile
-  auto wait_update = [&]() {
+  // every load so far has landed; the UPD update of the R tile and, for the
+  // leaf stage, the transposed copy
+  auto wait_update = [&](bool transpose) {
     lds_dma_wait();
     stamp(wgi, 1);
-    if constexpr (UPD) {
+    if (UPD || transpose) {
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
-        const int c = tid + BNT * i, row = c / C4;
+        const int c = tid + BNT * i, row = c / C4, col = 4 * (c % C4);
         mf4 v = *reinterpret_cast<const mf4*>(&Rs[4 * c]);
+        if constexpr (UPD) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          if (al[t] != 0.0) v[t] = (float)((double)v[t] - al[t] * (double)ap[i][t]);
-          rr4[t] = fma((double)v[t], (double)v[t], rr4[t]);
+          for (int t = 0; t < 4; ++t) {
+            if (al[t] != 0.0) v[t] = (float)((double)v[t] - al[t] * (double)ap[i][t]);
+            rr4[t] = fma((double)v[t], (double)v[t], rr4[t]);
+          }
+          *reinterpret_cast<mf4*>(&Rs[4 * c]) = v;
+          if (leaf_role) *reinterpret_cast<mf4*>(up.R + (size_t)(it.leaf0 + row) * G.nrhs + cc) = v;
         }
-        *reinterpret_cast<mf4*>(&Rs[4 * c]) = v;
-        if (leaf_role) *reinterpret_cast<mf4*>(up.R + (size_t)(it.leaf0 + row) * G.nrhs + cc) = v;
+        if (transpose) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) Ts[(col + t) * TS_STRIDE + row] = v[t];
+        }
       }
-      if (leaf_role) {
+      if (UPD && leaf_role) {
         // R.R partials of the wave: lanes with the same columns differ in lane
         // bits >= log2(C4) (fixed butterfly); summed over the waves at the end
 #pragma unroll
@@ -246,38 +274,6 @@ __global__ __launch_bounds__(BNT, 2) void k_block_restrict(BlockGeom G, const fl
       __syncthreads();
     }
     stamp(wgi, 2);
-  };
-  // T = U_k^T R_k: this wave's rows [32w, 32w + 32) of T, for every tile,
-  // then T^T into LDS (lane holds T[32w + 4q + v][16j + r] and + 16)
-  auto gemm1 = [&]() {
-    mf4 ta[NCT], tb[NCT];
-#pragma unroll
-    for (int j = 0; j < NCT; ++j) ta[j] = tb[j] = mf4{0, 0, 0, 0};
-    // B operands eight k-steps at a time, read ahead of their products
-#pragma unroll
-    for (int s0 = 0; s0 < 32; s0 += 8) {
-      float bv[8][NCT];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-#pragma unroll
-        for (int j = 0; j < NCT; ++j) bv[u][j] = Rs[(4 * (s0 + u) + q) * BW + 16 * j + r];
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-#pragma unroll
-        for (int j = 0; j < NCT; ++j) {
-          ta[j] = mfma4(ua[s0 + u], bv[u][j], ta[j]);
-          tb[j] = mfma4(ub[s0 + u], bv[u][j], tb[j]);
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < NCT; ++j) {
-      *reinterpret_cast<mf4*>(&Ts[(16 * j + r) * TS_STRIDE + 32 * w + 4 * q]) = ta[j];
-      *reinterpret_cast<mf4*>(&Ts[(16 * j + r) * TS_STRIDE + 32 * w + 16 + 4 * q]) = tb[j];
-    }
-    stamp(wgi, 3);
   };
   // restriction Q_l = W_l[k]^T R_k, two accumulation chains (even / odd k
   // steps) summed at the end.  SPLIT: every level's operands are in registers,
@@ -338,54 +334,45 @@ __global__ __launch_bounds__(BNT, 2) void k_block_restrict(BlockGeom G, const fl
     }
     stamp(wgi, 4);
   };
+  // Y = F_k R_k + g R: this wave's rows [32w, 32w + 32), tile by tile
+  auto leaf_stage = [&]() {
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) {
+      mf4 ya = {0, 0, 0, 0}, yb = {0, 0, 0, 0};
+      mf4 bt[LEAF / 16];           // the tile's R^T operands, read ahead of the products
+#pragma unroll
+      for (int ch = 0; ch < LEAF / 16; ++ch)
+        bt[ch] = *reinterpret_cast<const mf4*>(&Ts[(16 * j + r) * TS_STRIDE + 16 * ch + 4 * q]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ch = 0; ch < LEAF / 16; ++ch) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          ya = mfma4(af[ch][t], bt[ch][t], ya);
+          yb = mfma4(bf[ch][t], bt[ch][t], yb);
+        }
+      }
+      const int cj = c0 + 16 * j + r;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int ia = 32 * w + 4 * q + v, ib = ia + 16;
+        Y[(size_t)(it.leaf0 + ia) * G.nrhs + cj] = ya[v] + gv[v] * Rs[ia * BW + 16 * j + r];
+        Y[(size_t)(it.leaf0 + ib) * G.nrhs + cj] = yb[v] + gv[4 + v] * Rs[ib * BW + 16 * j + r];
+      }
+    }
+    stamp(wgi, 6);
+  };
   if (SPLIT && role == 1) {        // the restriction alone: its operands of every level at once
     load_restr();
-    wait_update();
+    wait_update(false);
     restriction();
     return;
   }
   load_leaf();
-  if constexpr (SPLIT) {
-    load_gate();
-    wait_update();
-    gemm1();
-    load_gemm2();
-  } else {
-    load_restr();
-    wait_update();
-    gemm1();
-    restriction();
-    load_gemm2();                  // U_k is L2-resident by now
-    load_gate();
-  }
-  __syncthreads();
-  stamp(wgi, 5);
-  // Y = U_k T + g R: this wave's rows [32w, 32w + 32), tile by tile
-#pragma unroll
-  for (int j = 0; j < NCT; ++j) {
-    mf4 ya = {0, 0, 0, 0}, yb = {0, 0, 0, 0};
-    mf4 bt[LEAF / 16];             // the tile's T operands, read ahead of the products
-#pragma unroll
-    for (int ch = 0; ch < LEAF / 16; ++ch)
-      bt[ch] = *reinterpret_cast<const mf4*>(&Ts[(16 * j + r) * TS_STRIDE + 16 * ch + 4 * q]);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ch = 0; ch < LEAF / 16; ++ch) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        ya = mfma4(au[ch][t], bt[ch][t], ya);
-        yb = mfma4(bu[ch][t], bt[ch][t], yb);
-      }
-    }
-    const int cj = c0 + 16 * j + r;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int ia = 32 * w + 4 * q + v, ib = ia + 16;
-      Y[(size_t)(it.leaf0 + ia) * G.nrhs + cj] = ya[v] + gv[v] * Rs[ia * BW + 16 * j + r];
-      Y[(size_t)(it.leaf0 + ib) * G.nrhs + cj] = yb[v] + gv[4 + v] * Rs[ib * BW + 16 * j + r];
-    }
-  }
-  stamp(wgi, 6);
+  if constexpr (!SPLIT) load_restr();
+  wait_update(true);
+  leaf_stage();
+  if constexpr (!SPLIT) restriction();
   if constexpr (UPD) {
     // R.R partials: the four waves' sums (left in red by the update) in order
     if (tid < BW)

@@ -37,12 +37,12 @@ SPLIT_DIAG = {0: "start", 1: "r in LDS", 2: "U_k U_k^T r published"}
 SPLIT_OFF = {0: "start", 1: "r in LDS", 2: "restriction published",
              5: "partner + diagonal words gathered", 6: "prolongation done", 7: "y stored and acknowledged"}
 SPMV = {0: "start", 7: "y stored and acknowledged"}
-BLOCK_LEAF = {0: "start", 1: "R tile and operands landed", 2: "residual update done (block solve)",
-              3: "T = U_k^T R in LDS", 5: "GEMM 2 operands in", 6: "Y stores issued"}
-BLOCK_RESTR = {0: "start", 1: "R tile and operands landed", 2: "residual update done (block solve)",
+BLOCK_LEAF = {0: "start", 1: "R tile and operands landed", 2: "R^T in LDS (and the block solve's update)",
+              6: "Y = F_k R + g R stores issued"}
+BLOCK_RESTR = {0: "start", 1: "R tile and operands landed", 2: "the block solve's update done",
                4: "restrictions stored"}
-BLOCK_BOTH = {0: "start", 1: "R tile and operands landed", 2: "residual update done (block solve)",
-              3: "T = U_k^T R in LDS", 4: "restrictions stored", 5: "GEMM 2 operands in", 6: "Y stores issued"}
+BLOCK_BOTH = {0: "start", 1: "R tile and operands landed", 2: "R^T in LDS (and the block solve's update)",
+              6: "Y = F_k R + g R stores issued", 4: "restrictions stored"}
 BLOCK_PROLONG = {8: "start", 9: "half sums in LDS", 10: "products done", 11: "Y stores issued"}
 RESIDENT = {0: "iteration start", 1: "halo z and r.r, r.z partials polled", 2: "SpMV done",
             3: "restriction of q and p.q published", 4: "U_k U_k^T q done",
@@ -183,11 +183,11 @@ def block_tables(st, items, title):
         r = role[:nwg]
         out += [table(f"{title}: leaf stage (role 0 of two workgroups per item)", wg[r == 0], BLOCK_LEAF, t0), "",
                 table(f"{title}: restriction (role 1)", wg[r == 1], BLOCK_RESTR, t0), ""]
-        end = int(wg[r == 0][:, 6].astype(np.int64).max())
+        end = max(int(wg[r == 0][:, 6].astype(np.int64).max()), int(wg[r == 1][:, 4].astype(np.int64).max()))
     else:
         out += [table(f"{title}: leaf stage and restriction (one workgroup per item)", wg, BLOCK_BOTH, t0), ""]
-        end = int(wg[:, 6].astype(np.int64).max())
-    out += [f"Leaf-stage kernel: first start to last Y store issued {(end - t0) * TICK_US:.2f} us.", ""]
+        end = int(wg[:, [4, 6]].astype(np.int64).max())
+    out += [f"Leaf-stage kernel: first start to its last store issued {(end - t0) * TICK_US:.2f} us.", ""]
     pw = st[:items]
     t1 = int(pw[:, 8].astype(np.int64).min())
     out += [table(f"{title}: prolongation", pw, BLOCK_PROLONG, t1), "",
