@@ -30,7 +30,9 @@ def test_n8k_pair_bytes_match_the_quoted_figure():
 @pytest.mark.parametrize("name,nrhs", [("N1k", 16), ("N8k", 96)])
 def test_block_apply_flops(name, nrhs):
     b = make_config(name)
-    per_column = 4 * b.U.size + 4 * b.W.size + 2 * b.g.size
+    # one product with the dense leaf blocks (F_k = U_k U_k^T, U's shape), two
+    # with every slab (restriction and prolongation), the gate
+    per_column = 2 * b.U.size + 4 * b.W.size + 2 * b.g.size
     assert bench.block_apply_flops(b.n, b.levels, nrhs, b.batch) == nrhs * per_column
 
 
