@@ -1094,8 +1094,8 @@ hpcg_status launch_block_apply(hpcg_ctx* h, int32_t nrhs, const float* d_R, floa
   if (h->G.levels > 0) {
     size_t sys_total = 0;
     for (int l = 0; l < h->G.levels; ++l) sys_total += (size_t)(h->G.K >> l) * RANK * nrhs;
-    const size_t total = sys_total * h->G.B;
-    hipLaunchKernelGGL(k_block_halfsum, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, bg, Q, H);
+    hipLaunchKernelGGL(k_block_halfsum, dim3((unsigned)((sys_total + 255) / 256), (unsigned)std::min(h->G.B, 65535)),
+                       dim3(256), 0, stream, bg, Q, H);
 #define HPCG_BLOCK_PROLONG_N(LV, N)                                                                     \
   do {                                                                                                  \
     if (dot)                                                                                            \

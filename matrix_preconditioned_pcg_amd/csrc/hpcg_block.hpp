@@ -383,40 +383,38 @@ __global__ __launch_bounds__(BNT, 2) void k_block_restrict(BlockGeom G, const fl
 
 // (2) half sums: H_l[h] = sum of Q_l[k] over the 2^l leaves k of half h, summed
 // in leaf order.  Same layout as Q (half index in place of the leaf index).
+// Grid: x over a system's (level, half, element) triples, y over the systems
+// (a stride of gridDim.y past 65535 systems); the index arithmetic is 32-bit
+// (a system's triples are far fewer than 2^31).
 __global__ void k_block_halfsum(BlockGeom G, const float* __restrict__ Q, float* __restrict__ H) {
-  const size_t per = (size_t)RANK * G.nrhs;       // elements per (level, leaf)
-  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  // enumerate (s, l, h, e) with h < K >> l: level l owns (K >> l) * per elements
-  size_t rem = idx;
+  constexpr int HB = 8;                            // loads in flight per batch
+  const unsigned per = (unsigned)RANK * (unsigned)G.nrhs;   // elements per (level, leaf)
+  unsigned rem = blockIdx.x * blockDim.x + threadIdx.x;
   int l = 0;
-  size_t level_elems = (size_t)G.K * per;         // l = 0
-  size_t sys_total = 0;
-  for (int ll = 0; ll < G.levels; ++ll) sys_total += (size_t)(G.K >> ll) * per;
-  const int s = (int)(rem / sys_total);
-  if (s >= G.B) return;
-  rem -= (size_t)s * sys_total;
+  unsigned level_elems = (unsigned)G.K * per;      // l = 0
   while (l < G.levels && rem >= level_elems) {
     rem -= level_elems;
     ++l;
-    level_elems = (size_t)(G.K >> l) * per;
+    level_elems = (unsigned)(G.K >> l) * per;
   }
   if (l >= G.levels) return;
-  const int h = (int)(rem / per);
-  const size_t e = rem - (size_t)h * per;
+  const unsigned h = rem / per, e = rem - h * per;
   const int span = 1 << l;
-  const float* src = Q + q_index(G, s, l, h * span, 0) + e;
-  // loads in batches of 8 in flight; the sum keeps leaf order
-  float a = 0.f;
-  int i = 0;
-  for (; i + 8 <= span; i += 8) {
-    float v[8];
+  for (int s = (int)blockIdx.y; s < G.B; s += (int)gridDim.y) {
+    const float* src = Q + q_index(G, s, l, (int)h * span, 0) + e;
+    // the sum keeps leaf order
+    float a = 0.f;
+    int i = 0;
+    for (; i + HB <= span; i += HB) {
+      float v[HB];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = src[(size_t)(i + u) * per];
+      for (int u = 0; u < HB; ++u) v[u] = src[(size_t)(i + u) * per];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) a += v[u];
+      for (int u = 0; u < HB; ++u) a += v[u];
+    }
+    for (; i < span; ++i) a += src[(size_t)i * per];
+    H[q_index(G, s, l, (int)h, 0) + e] = a;
   }
-  for (; i < span; ++i) a += src[(size_t)i * per];
-  H[q_index(G, s, l, h, 0) + e] = a;
 }
 
 // (3) prolongation: Y_k += sum_l W_l[k] H_l[(k >> l) ^ 1].  Every level's slab
@@ -433,16 +431,42 @@ __global__ __launch_bounds__(BNT) void k_block_prolong(BlockGeom G, const float*
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int q = lane >> 4, r = lane & 15;
   const int c0 = it.ct * BW;
+  // two stages of levels: the first stage's products run while the second
+  // stage's operands are still arriving; the products keep level order
+  constexpr int LA = (LEV + 1) / 2, LB = LEV - LA;
+  constexpr int PE = RANK * BW / BNT;        // half-sum elements per thread and level
   mf4 aw[LEV > 0 ? LEV : 1][2], bw[LEV > 0 ? LEV : 1][2];
+  auto load_w = [&](int l0, int l1) {
 #pragma unroll
-  for (int l = 0; l < LEV; ++l) {
-    const float* Wa = W + ((((size_t)it.s * LEV + l) * G.K + it.k) * LEAF + 32 * w + r) * RANK + 4 * q;
+    for (int l = l0; l < l1; ++l) {
+      const float* Wa = W + ((((size_t)it.s * LEV + l) * G.K + it.k) * LEAF + 32 * w + r) * RANK + 4 * q;
 #pragma unroll
-    for (int ch = 0; ch < 2; ++ch) {
-      aw[l][ch] = *reinterpret_cast<const mf4*>(Wa + 16 * ch);
-      bw[l][ch] = *reinterpret_cast<const mf4*>(Wa + 16 * RANK + 16 * ch);
+      for (int ch = 0; ch < 2; ++ch) {
+        aw[l][ch] = *reinterpret_cast<const mf4*>(Wa + 16 * ch);
+        bw[l][ch] = *reinterpret_cast<const mf4*>(Wa + 16 * RANK + 16 * ch);
+      }
     }
-  }
+  };
+  // partner half sums of levels [l0, l0 + NL): loads, then their transposed
+  // stores into LDS
+  auto load_h = [&](float* hv, int l0, int nl) {
+#pragma unroll
+    for (int u = 0; u < nl * PE; ++u) {
+      const int e = tid + u * BNT;
+      const int l = l0 + e / (RANK * BW), rem = e % (RANK * BW);
+      const int row = rem / BW, col = rem - row * BW;
+      hv[u] = H[q_index(G, it.s, l, (it.k >> l) ^ 1, row) + c0 + col];
+    }
+  };
+  auto store_h = [&](const float* hv, int l0, int nl) {
+#pragma unroll
+    for (int u = 0; u < nl * PE; ++u) {
+      const int e = tid + u * BNT;
+      const int l = l0 + e / (RANK * BW), rem = e % (RANK * BW);
+      const int row = rem / BW, col = rem - row * BW;
+      Ps[(l * BW + col) * PS_STRIDE + row] = hv[u];
+    }
+  };
   // accumulators start from the leaf stage's Y
   mf4 ya[NCT], yb[NCT];
 #pragma unroll
@@ -453,6 +477,28 @@ __global__ __launch_bounds__(BNT) void k_block_prolong(BlockGeom G, const float*
       yb[j][v] = Y[(size_t)(it.leaf0 + 32 * w + 16 + 4 * q + v) * G.nrhs + c0 + 16 * j + r];
     }
   }
+  auto products = [&](int l0, int l1) {
+#pragma unroll
+    for (int l = l0; l < l1; ++l) {
+#pragma unroll
+      for (int ch = 0; ch < RANK / 16; ++ch) {
+#pragma unroll
+        for (int j = 0; j < NCT; ++j) {
+          const mf4 bp = *reinterpret_cast<const mf4*>(&Ps[(l * BW + 16 * j + r) * PS_STRIDE + 16 * ch + 4 * q]);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            ya[j] = mfma4(aw[l][ch][t], bp[t], ya[j]);
+            yb[j] = mfma4(bw[l][ch][t], bp[t], yb[j]);
+          }
+        }
+      }
+    }
+  };
+  float ha[LA * PE], hb[LB > 0 ? LB * PE : 1];
+  load_w(0, LA);
+  load_h(ha, 0, LA);
+  load_w(LA, LEV);
+  if constexpr (LB > 0) load_h(hb, LA, LB);
   // DOT: R at the lane's accumulator elements
   float rv[DOT ? NCT : 1][8];
   if constexpr (DOT) {
@@ -465,39 +511,14 @@ __global__ __launch_bounds__(BNT) void k_block_prolong(BlockGeom G, const float*
       }
     }
   }
-  // partner half sums, transposed into LDS: all loads first, then the stores
-  constexpr int PER = (LEV > 0 ? LEV : 1) * RANK * BW / BNT;   // elements per thread
-  float hv[PER];
-#pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int e = tid + u * BNT;
-    const int l = e / (RANK * BW), rem = e - l * RANK * BW;
-    const int row = rem / BW, col = rem - row * BW;
-    hv[u] = H[q_index(G, it.s, l, (it.k >> l) ^ 1, row) + c0 + col];
-  }
-#pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int e = tid + u * BNT;
-    const int l = e / (RANK * BW), rem = e - l * RANK * BW;
-    const int row = rem / BW, col = rem - row * BW;
-    Ps[(l * BW + col) * PS_STRIDE + row] = hv[u];
-  }
+  store_h(ha, 0, LA);
   __syncthreads();
   stamp((int)blockIdx.x, 9);
-#pragma unroll
-  for (int l = 0; l < LEV; ++l) {
-#pragma unroll
-    for (int ch = 0; ch < RANK / 16; ++ch) {
-#pragma unroll
-      for (int j = 0; j < NCT; ++j) {
-        const mf4 bp = *reinterpret_cast<const mf4*>(&Ps[(l * BW + 16 * j + r) * PS_STRIDE + 16 * ch + 4 * q]);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          ya[j] = mfma4(aw[l][ch][t], bp[t], ya[j]);
-          yb[j] = mfma4(bw[l][ch][t], bp[t], yb[j]);
-        }
-      }
-    }
+  products(0, LA);
+  if constexpr (LB > 0) {
+    store_h(hb, LA, LB);
+    __syncthreads();
+    products(LA, LEV);
   }
   stamp((int)blockIdx.x, 10);
 #pragma unroll
