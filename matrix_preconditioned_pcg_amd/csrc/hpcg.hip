@@ -1227,7 +1227,7 @@ hpcg_status block_iteration(hpcg_ctx* h, int32_t nrhs, char* wk, const BlockSolv
   const dim3 rows_grid((unsigned)(G.B * rblocks), (unsigned)((nrhs + BS_COLS - 1) / BS_COLS));
   const int ncol = G.B * nrhs;
   const dim3 sc_grid((unsigned)((ncol + BS_SC_COLS - 1) / BS_SC_COLS));
-  hipLaunchKernelGGL(k_bs_spmv_dot, rows_grid, dim3(BS_NT), 0, stream, h->B.row_ptr, h->B.col, h->B.val, P, Q,
+  hipLaunchKernelGGL(k_bs_spmv_dot, rows_grid, dim3(BS_SPMV_NT), 0, stream, h->B.row_ptr, h->B.col, h->B.val, P, Q,
                      part, nrhs);
   hipLaunchKernelGGL(k_bs_scalars<BS_PQ>, sc_grid, dim3(64 * BS_SC_COLS), 0, stream, cs, part, G.B, nrhs, rblocks, tol, maxit,
                      (const double*)nullptr, 0);

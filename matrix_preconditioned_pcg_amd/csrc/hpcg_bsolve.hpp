@@ -104,75 +104,59 @@ __global__ __launch_bounds__(BS_NT) void k_bs_init(const float* __restrict__ Bm,
   if (rg == 0 && c < nrhs) part[rb * nrhs + c] = s;
 }
 
-// Q = A P and the block's partials of P . Q (the layout of k_bs_dot).  Thread
-// (rr, g) takes rows rr and rr + 16 of the 32-row block and columns 4g..4g+3 of
-// the 64-column tile; the two rows' entries are taken four at a time, their
-// indices and then their P rows all in flight together.  A row's sum is taken
-// in fp64 and rounded to fp32 once: R -= alpha Q moves R away from B - A X by
-// alpha (A P - Q) every step, and a sum of the stencil's cancelling terms
-// rounded at every step moved it by several times tol on long, stiff grids.
-// The partial of a column adds the thread's two rows (with the stored, rounded
-// Q), the four row groups of a wave (fixed butterfly) and the four waves in
-// order.
-__global__ __launch_bounds__(BS_NT) void k_bs_spmv_dot(const int* __restrict__ row_ptr, const int* __restrict__ col,
-                                                       const float* __restrict__ val, const float* __restrict__ P,
-                                                       float* __restrict__ Q, double* __restrict__ part, int nrhs) {
+// Q = A P and the block's partials of P . Q (the layout of k_bs_dot).  A
+// workgroup of 512 takes a 32-row block and a 64-column tile: thread (rr, g)
+// row rr and columns 4g..4g+3, the row's entries four at a time, their indices
+// and then their P rows all in flight together (two rows per thread, in 256,
+// were slower).  A row's sum is taken in fp64 and rounded to fp32 once:
+// R -= alpha Q moves R away from B - A X by alpha (A P - Q) every step, and a
+// sum of the stencil's cancelling terms rounded at every step moved it by
+// several times tol on long, stiff grids.  The partial of a column adds the
+// rows' products (with the stored, rounded Q) over the four row groups of a
+// wave (fixed butterfly) and then the eight waves in order.
+constexpr int BS_SPMV_NT = 512;
+__global__ __launch_bounds__(BS_SPMV_NT) void k_bs_spmv_dot(const int* __restrict__ row_ptr,
+                                                            const int* __restrict__ col,
+                                                            const float* __restrict__ val,
+                                                            const float* __restrict__ P, float* __restrict__ Q,
+                                                            double* __restrict__ part, int nrhs) {
   typedef float f4 __attribute__((ext_vector_type(4)));
-  __shared__ double red[(BS_NT / 64) * BS_COLS];
+  constexpr int NWV = BS_SPMV_NT / 64;
+  __shared__ double red[NWV * BS_COLS];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = tid & 15, rr = tid >> 4;
   const int c4 = blockIdx.y * BS_COLS + 4 * g;
   const size_t rb = blockIdx.x;
   double d[4] = {0.0, 0.0, 0.0, 0.0};
   if (c4 < nrhs) {
-    int row[2], e0[2], e1[2];
+    const int row = (int)(rb * BS_ROWS) + rr;
+    const int e0 = row_ptr[row], e1 = row_ptr[row + 1];
+    const f4 pv = *reinterpret_cast<const f4*>(P + (size_t)row * nrhs + c4);
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int e = e0; e < e1; e += 4) {
+      int c[4];
+      float a[4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      row[h] = (int)(rb * BS_ROWS) + rr + 16 * h;
-      e0[h] = row_ptr[row[h]];
-      e1[h] = row_ptr[row[h] + 1];
-    }
-    f4 pv[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) pv[h] = *reinterpret_cast<const f4*>(P + (size_t)row[h] * nrhs + c4);
-    double acc[2][4] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
-    const int len = max(e1[0] - e0[0], e1[1] - e0[1]);
-    for (int o = 0; o < len; o += 4) {
-      int c[2][4];
-      float a[2][4];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const bool in = e0[h] + o + u < e1[h];
-          c[h][u] = in ? col[e0[h] + o + u] : row[h];
-          a[h][u] = in ? val[e0[h] + o + u] : 0.f;
-        }
+      for (int u = 0; u < 4; ++u) {
+        const bool in = e + u < e1;
+        c[u] = in ? col[e + u] : row;
+        a[u] = in ? val[e + u] : 0.f;
       }
-      f4 x[2][4];
+      f4 x[4];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const f4*>(P + (size_t)c[u] * nrhs + c4);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) x[h][u] = *reinterpret_cast<const f4*>(P + (size_t)c[h][u] * nrhs + c4);
-      }
+      for (int u = 0; u < 4; ++u) {
+        if (e + u < e1) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (e0[h] + o + u < e1[h]) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) acc[h][t] = fma((double)a[h][u], (double)x[h][u][t], acc[h][t]);
-          }
+          for (int t = 0; t < 4; ++t) acc[t] = fma((double)a[u], (double)x[u][t], acc[t]);
         }
       }
     }
+    const f4 qv = {(float)acc[0], (float)acc[1], (float)acc[2], (float)acc[3]};
+    *reinterpret_cast<f4*>(Q + (size_t)row * nrhs + c4) = qv;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const f4 qv = {(float)acc[h][0], (float)acc[h][1], (float)acc[h][2], (float)acc[h][3]};
-      *reinterpret_cast<f4*>(Q + (size_t)row[h] * nrhs + c4) = qv;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) d[t] = fma((double)pv[h][t], (double)qv[t], d[t]);
-    }
+    for (int t = 0; t < 4; ++t) d[t] = (double)pv[t] * (double)qv[t];
   }
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -185,8 +169,12 @@ __global__ __launch_bounds__(BS_NT) void k_bs_spmv_dot(const int* __restrict__ r
   }
   __syncthreads();
   const int c = blockIdx.y * BS_COLS + tid;
-  if (tid < BS_COLS && c < nrhs)
-    part[rb * nrhs + c] = ((red[tid] + red[BS_COLS + tid]) + red[2 * BS_COLS + tid]) + red[3 * BS_COLS + tid];
+  if (tid < BS_COLS && c < nrhs) {
+    double sum = red[tid];
+#pragma unroll
+    for (int k = 1; k < NWV; ++k) sum += red[k * BS_COLS + tid];
+    part[rb * nrhs + c] = sum;
+  }
 }
 
 // X += alpha P, then P = Z + beta P (alpha and beta per column of the row's
