@@ -224,8 +224,8 @@ typedef enum {
                                    more iterations: the fp64 oracle with only
                                    that rounding added needs 630-641 steps
                                    against 517, and this mode takes ~671, with a
-                                   true residual up to ~1.3 tol.  Use VEC64
-                                   where the fp64 count matters.               */
+                                   true residual of ~1.03 tol.  Use VEC64 where
+                                   the fp64 count matters.                     */
 } hpcg_precision;
 
 /* Bytes of device workspace hpcg_create needs for this partition and a CSR of
@@ -234,7 +234,8 @@ typedef enum {
  * follow the pages' apply-path layout ("Hierarchical Transformer
  * Preconditioning for Interactive Physics Simulation", Supplementary section 2,
  * "Apply-path tensor layout", and Table 3: K leaf blocks of L x L, K - 1
- * tiles) with the per-level slabs of this library. */
+ * tiles) with the per-level slabs of this library, and, for the block apply,
+ * the dense leaf blocks U_k U_k^T (another L x L per leaf). */
 size_t hpcg_workspace_bytes(const hpcg_partition* part, int64_t nnz_total);
 
 /* Create a solver for one sparsity pattern and value set of A: the sparse SPD
