@@ -37,6 +37,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 FP32_MFMA_PEAK_TFLOPS = 157.3
+FP16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "PCG ms/solve and M-apply+SpMV HBM GB/s (fraction of peak) at N=8,192"
 
 
@@ -418,7 +419,9 @@ def main(argv=None):
         return {"workload": name, "nrhs": nrhs, "probe_columns": kz, "apply_us": round(t_apply, 3),
                 "block_solve": solve,
                 "tflops": round(tf, 2), "peak_tflops": FP32_MFMA_PEAK_TFLOPS,
-                "frac": round(tf / FP32_MFMA_PEAK_TFLOPS, 4), "flops": fl, "dtype": "f32 (mfma 16x16x4)",
+                "frac": round(tf / FP32_MFMA_PEAK_TFLOPS, 4), "flops": fl,
+                "dtype": "f32 products from fp16 pairs (mfma 16x16x32 f16, three per f32 product)",
+                "f16_mfma_frac": round(3 * tf / FP16_MFMA_PEAK_TFLOPS, 4),
                 "spmv_block_us": round(t_spmv, 3)}
 
     def run_config(name, steps, warmup, with_roofline, engine=None, prec=None):

@@ -339,7 +339,11 @@ hpcg_status hpcg_spmv(hpcg_handle h, const float* d_x, float* d_y);
  * Physics Simulation", project page, "Cosine Hutchinson Probe Loss" and
  * "Training Setup"; Supplementary section 3, "Probe vectors").  Every stage of
  * the apply (section 5, stages (i)-(ii), eqs. (2)-(5)) becomes a dense product
- * run on the matrix cores.
+ * run on the matrix cores: fp32 products formed from fp16 pairs (each fp32
+ * operand set scaled by a power of two and split into a high and a low fp16
+ * part; three fp16 products per fp32 product, accumulated in fp32; about 22
+ * bits per product), with the leaf stage one product with the dense leaf
+ * blocks U_k U_k^T, formed at hpcg_set_factors.
  *
  * Layout: node-major, float32 [batch*n][nrhs] (the nrhs values of one node are
  * contiguous), 16-byte aligned; nrhs a multiple of 16 in [16, 1024] (pad the

@@ -30,7 +30,8 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t row_ptr, col, val, U, F, W, g, b, r, z, q, p0, p1, x, tleaf, pleaf, pq, rr, rz, st, ctl;
+  size_t row_ptr, col, val, U, W, g, b, r, z, q, p0, p1, x, tleaf, pleaf, pq, rr, rz, st, ctl;
+  size_t Fh, Fl, Fe, Wh, Wl, Th, Tl, We;   // block apply: factors as fp16 pairs and their exponents
   size_t wgflag;              // resident engine: per-workgroup barrier lines
   size_t lcol, hoff, hcol;    // resident engine: leaf-local CSR columns and halo lists
   size_t zll, pll;            // resident engine: flagged z words and flagged partials
@@ -121,7 +122,18 @@ Layout make_layout(const Geom& G, int64_t nnz) {
   L.col = take((size_t)nnz * 4);
   L.val = take((size_t)nnz * 4);
   L.U = take((size_t)G.B * G.K * LEAF * LEAF * 4);
-  L.F = take((size_t)G.B * G.K * LEAF * LEAF * 4);    // dense leaf blocks (block apply)
+  // block apply: dense leaf blocks and slabs (also transposed) as fp16 pairs
+  L.Fh = take((size_t)G.B * G.K * LEAF * LEAF * 2);
+  L.Fl = take((size_t)G.B * G.K * LEAF * LEAF * 2);
+  L.Fe = take((size_t)G.B * G.K * 4);
+  {
+    const size_t slabs = (size_t)G.B * G.levels * G.K;
+    L.Wh = take(slabs * LEAF * RANK * 2);
+    L.Wl = take(slabs * LEAF * RANK * 2);
+    L.Th = take(slabs * LEAF * RANK * 2);
+    L.Tl = take(slabs * LEAF * RANK * 2);
+    L.We = take(slabs * 4);
+  }
   L.W = take((size_t)G.B * G.levels * G.K * LEAF * RANK * 4);
   L.g = take(N * 4);
   L.b = take(N * 4);
@@ -585,7 +597,6 @@ hpcg_status hpcg_create(const hpcg_partition* part, const int32_t* d_row_ptr, co
   B.col = reinterpret_cast<const int*>(w + lay.col);
   B.val = reinterpret_cast<const float*>(w + lay.val);
   B.U = reinterpret_cast<const float*>(w + lay.U);
-  B.F = reinterpret_cast<const float*>(w + lay.F);
   B.W = reinterpret_cast<const float*>(w + lay.W);
   B.g = reinterpret_cast<const float*>(w + lay.g);
   B.b = reinterpret_cast<const float*>(w + lay.b);
@@ -705,6 +716,32 @@ hpcg_status hpcg_set_values(hpcg_handle h, const float* d_val) {
   return check_launch(h, "diagonal launch");
 }
 
+namespace {
+// The block apply's operands as fp16 pairs, formed from U and the slabs in the
+// workspace (stream-ordered after their copies).
+BlockFactors16 block_factors16(const hpcg_ctx* h) {
+  const char* w = h->ws;
+  auto p = [&](size_t o) { return reinterpret_cast<const _Float16*>(w + o); };
+  BlockFactors16 f;
+  f.Fh = p(h->lay.Fh); f.Fl = p(h->lay.Fl); f.Fe = reinterpret_cast<const int*>(w + h->lay.Fe);
+  f.Wh = p(h->lay.Wh); f.Wl = p(h->lay.Wl); f.Th = p(h->lay.Th); f.Tl = p(h->lay.Tl);
+  f.We = reinterpret_cast<const int*>(w + h->lay.We);
+  return f;
+}
+void block_factor_pairs(hpcg_ctx* h) {
+  char* w = h->ws;
+  const Geom& G = h->G;
+  hipLaunchKernelGGL(k_leaf_blocks, dim3(G.B * G.K), dim3(BNT), 0, h->stream, h->B.U,
+                     reinterpret_cast<_Float16*>(w + h->lay.Fh), reinterpret_cast<_Float16*>(w + h->lay.Fl),
+                     reinterpret_cast<int*>(w + h->lay.Fe));
+  if (G.levels > 0)
+    hipLaunchKernelGGL(k_split_slabs, dim3(G.B * G.levels * G.K), dim3(BNT), 0, h->stream, h->B.W,
+                       reinterpret_cast<_Float16*>(w + h->lay.Wh), reinterpret_cast<_Float16*>(w + h->lay.Wl),
+                       reinterpret_cast<_Float16*>(w + h->lay.Th), reinterpret_cast<_Float16*>(w + h->lay.Tl),
+                       reinterpret_cast<int*>(w + h->lay.We));
+}
+}  // namespace
+
 hpcg_status hpcg_set_factors(hpcg_handle h, const float* d_leafU, const float* d_tileW, const float* d_gate) {
   if (!h) return fail(nullptr, HPCG_ERR_INVALID_ARG, "handle is NULL");
   const Geom& G = h->G;
@@ -715,8 +752,7 @@ hpcg_status hpcg_set_factors(hpcg_handle h, const float* d_leafU, const float* d
     HIP_OR_FAIL(h, hipMemcpyAsync(h->ws + h->lay.W, d_tileW, (size_t)G.B * G.levels * G.K * LEAF * RANK * 4,
                                   hipMemcpyDeviceToDevice, h->stream));
   HIP_OR_FAIL(h, hipMemcpyAsync(h->ws + h->lay.g, d_gate, (size_t)G.B * G.n * 4, hipMemcpyDeviceToDevice, h->stream));
-  hipLaunchKernelGGL(k_leaf_blocks, dim3(G.B * G.K), dim3(BNT), 0, h->stream, h->B.U,
-                     reinterpret_cast<float*>(h->ws + h->lay.F));
+  block_factor_pairs(h);
   hpcg_status s = check_launch(h, "leaf block launch");
   if (s != HPCG_OK) return s;
   h->factors_set = true;
@@ -880,8 +916,7 @@ hpcg_status hpcg_set_factors_bridge(hpcg_handle h, const float* d_leafF, const f
     HIP_OR_FAIL(h, hipMemcpyAsync(h->ws + h->lay.Bc, d_cores, (size_t)G.B * h->B.ncores * RANK * RANK * 4,
                                   hipMemcpyDeviceToDevice, h->stream));
   }
-  hipLaunchKernelGGL(k_leaf_blocks, dim3(G.B * G.K), dim3(BNT), 0, h->stream, h->B.U,
-                     reinterpret_cast<float*>(h->ws + h->lay.F));
+  block_factor_pairs(h);
   hpcg_status s = check_launch(h, "bridge expansion launch");
   if (s != HPCG_OK) return s;
   h->factors_set = true;
@@ -1061,15 +1096,16 @@ hpcg_status launch_block_apply(hpcg_ctx* h, int32_t nrhs, const float* d_R, floa
   const BlockUpd up = upd ? *upd : BlockUpd{};
   const BlockDot dt = dot ? *dot : BlockDot{};
   const bool sp = block_split(h, nrhs);
+  const BlockFactors16 f16 = block_factors16(h);
   // (block_split() holds only where a split instantiation exists: LV > 0, N < 4)
 #define HPCG_BLOCK_RESTRICT_UPD(LV, N, UP)                                                               \
   do {                                                                                                   \
     if (sp && LV > 0 && N < 4)                                                                           \
       hipLaunchKernelGGL((k_block_restrict<LV, N, UP, (LV > 0 && N < 4)>), dim3(2 * grid), dim3(BNT), 0, \
-                         stream, bg, h->B.F, h->B.W, h->B.g, d_R, d_Y, Q, up);                           \
+                         stream, bg, f16, h->B.g, d_R, d_Y, Q, up);                                      \
     else                                                                                                 \
       hipLaunchKernelGGL((k_block_restrict<LV, N, UP, false>), dim3(grid), dim3(BNT), 0, stream, bg,      \
-                         h->B.F, h->B.W, h->B.g, d_R, d_Y, Q, up);                                       \
+                         f16, h->B.g, d_R, d_Y, Q, up);                                                  \
   } while (0)
 #define HPCG_BLOCK_RESTRICT_N(LV, N)                                                                     \
   do {                                                                                                   \
@@ -1099,10 +1135,10 @@ hpcg_status launch_block_apply(hpcg_ctx* h, int32_t nrhs, const float* d_R, floa
 #define HPCG_BLOCK_PROLONG_N(LV, N)                                                                     \
   do {                                                                                                  \
     if (dot)                                                                                            \
-      hipLaunchKernelGGL((k_block_prolong<LV, N, true>), dim3(grid), dim3(BNT), 0, stream, bg, h->B.W, H, \
+      hipLaunchKernelGGL((k_block_prolong<LV, N, true>), dim3(grid), dim3(BNT), 0, stream, bg, f16, H,    \
                          d_Y, dt);                                                                      \
     else                                                                                                \
-      hipLaunchKernelGGL((k_block_prolong<LV, N, false>), dim3(grid), dim3(BNT), 0, stream, bg, h->B.W, H, \
+      hipLaunchKernelGGL((k_block_prolong<LV, N, false>), dim3(grid), dim3(BNT), 0, stream, bg, f16, H,   \
                          d_Y, dt);                                                                      \
   } while (0)
     switch (h->G.levels) {

@@ -13,15 +13,12 @@
 //
 // Layout: R, Y, X are node-major, [B*n][nrhs] fp32 (the nrhs values of a node are
 // contiguous).  A workgroup (4 wave64) owns one leaf and NCT 16-column tiles
-// (two where nrhs is a multiple of 32, so that each factor operand it loads
-// feeds twice the products).
-// Products use v_mfma_f32_16x16x4_f32 (fp32 in, fp32 accumulate).  Lane l of a
-// wave supplies A[l % 16][l / 16] and B[l / 16][l % 16] and receives
-// D[4 (l / 16) + v][l % 16], v = 0..3.  Where an operand is read along the
-// contraction index from memory that is contiguous in it, a lane reads four
-// consecutive k with one 16-byte load and feeds them to four MFMAs (lane group
-// q = l / 16 contracts k0 + 4q + t in MFMA t); A and B use the same order, so
-// the sum is the same product.
+// (up to four, so that each factor operand it loads feeds more products).
+// The products are fp32 products formed on the fp16 matrix cores from fp16
+// pairs (below): the operands of every product are held, or staged in LDS, in
+// the order of the contraction index, so that a lane's eight contraction steps
+// of an MFMA are one 16-byte read; A and B take the same order, so the sum is
+// the same product.
 //
 // Three launches: (1) per (leaf, tile): Y = F_k R_k + g R with the dense leaf
 // block F_k = U_k U_k^T (formed once per set of factors, k_leaf_blocks), and the
@@ -38,14 +35,49 @@ namespace hpcg {
 
 constexpr int BNC = 16;          // right-hand-side columns per workgroup
 constexpr int BNT = 256;         // threads per workgroup
-constexpr int TS_STRIDE = 132;   // R^T rows in LDS (== 4 mod 64: conflict-free 16-byte reads)
-constexpr int PS_STRIDE = 36;    // P^T rows in LDS (== 36 mod 64: conflict-free 16-byte reads)
 
 typedef float mf4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ mf4 mfma4(float a, float b, mf4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+// fp32 products from fp16 pairs.  A value x of a scaled set (one power of two
+// 2^e for the set, e from its largest magnitude so that it lands in
+// [2^13, 2^14)) is held as hi = fp16(x 2^e), lo = fp16(x 2^e - hi): 22 bits of
+// x.  A product a b is hi_a hi_b + hi_a lo_b + lo_a hi_b (each exact in the fp32
+// accumulator; the dropped lo_a lo_b and the pairs' own rounding are ~2^-22 of
+// |a b|), summed by v_mfma_f32_16x16x32_f16: lane l supplies A[l % 16][8 (l / 16)
+// + i] and B[8 (l / 16) + i][l % 16], i < 8, and receives D[4 (l / 16) + v][l % 16];
+// the result is unscaled by 2^-(e_a + e_b), exactly.
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ mf4 mfma16(h8 a, h8 b, mf4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
+// hi lo, hi lo products of one K = 32 step (three MFMAs)
+__device__ __forceinline__ mf4 mfma_pair(h8 ah, h8 al, h8 bh, h8 bl, mf4 c) {
+  c = mfma16(ah, bh, c);
+  c = mfma16(ah, bl, c);
+  return mfma16(al, bh, c);
+}
+// the scale exponent of a set whose largest magnitude is m
+__device__ __forceinline__ int pair_exponent(float m) {
+  if (!(m > 0.f) || !isfinite(m)) return 0;
+  int x;
+  (void)frexpf(m, &x);
+  return 14 - x;
+}
+__device__ __forceinline__ void to_pair(float v, int e, _Float16& hi, _Float16& lo) {
+  const float sv = ldexpf(v, e);
+  hi = (_Float16)sv;
+  lo = (_Float16)(sv - (float)hi);
+}
+
+// Factors of the block apply as fp16 pairs: the dense leaf blocks (exponent per
+// leaf), the slabs in their own layout for the prolongation and transposed
+// (rank-major) for the restriction (exponent per slab).
+struct BlockFactors16 {
+  const _Float16* Fh; const _Float16* Fl; const int* Fe;    // [B][K][LEAF][LEAF], [B][K]
+  const _Float16* Wh; const _Float16* Wl;                   // [B][levels][K][LEAF][RANK]
+  const _Float16* Th; const _Float16* Tl;                   // [B][levels][K][RANK][LEAF]
+  const int* We;                                            // [B][levels][K]
+};
 
 struct BlockGeom {
   int n, K, levels, B;   // as Geom
@@ -115,14 +147,17 @@ struct BlockDot {
 
 // Dense leaf blocks F_k = U_k U_k^T, formed once per set of factors so that
 // the block apply's leaf stage is one product F_k R_k: every entry summed in
-// fp64 over the leaf's 128 columns in column order and rounded to fp32 once
-// (F_k is then exactly symmetric).  One workgroup per leaf; U_k is staged in
-// LDS with rows padded to 129 words, so the lanes' walks down a column hit
-// distinct banks.  Thread t owns row t % 128 of half t / 128 of the columns and
-// writes them as column entries (F_k is symmetric), coalesced across lanes.
-__global__ __launch_bounds__(BNT) void k_leaf_blocks(const float* __restrict__ U, float* __restrict__ F) {
+// fp64 over the leaf's 128 columns in column order, then held as an fp16 pair
+// with one exponent for the leaf (F_k is exactly symmetric).  One workgroup per
+// leaf; U_k is staged in LDS with rows padded to 129 words, so the lanes' walks
+// down a column hit distinct banks.  Thread t owns row t % 128 of half t / 128
+// of the columns and writes them as column entries (F_k is symmetric),
+// coalesced across lanes.
+__global__ __launch_bounds__(BNT) void k_leaf_blocks(const float* __restrict__ U, _Float16* __restrict__ Fh,
+                                                     _Float16* __restrict__ Fl, int* __restrict__ Fe) {
   constexpr int PAD = LEAF + 1;
   __shared__ float Us[LEAF * PAD];
+  __shared__ float wmax[NWAVE];
   const size_t leaf = blockIdx.x;
   const float* Uk = U + leaf * LEAF * LEAF;
   for (int e = threadIdx.x; e < LEAF * LEAF; e += BNT) Us[(e / LEAF) * PAD + e % LEAF] = Uk[e];
@@ -136,36 +171,88 @@ __global__ __launch_bounds__(BNT) void k_leaf_blocks(const float* __restrict__ U
 #pragma unroll
     for (int jj = 0; jj < LEAF / 2; ++jj) acc[jj] = fma(ui, (double)Us[(j0 + jj) * PAD + k], acc[jj]);
   }
-  float* Fk = F + leaf * LEAF * LEAF;
+  float m = 0.f;
 #pragma unroll
-  for (int jj = 0; jj < LEAF / 2; ++jj) Fk[(size_t)(j0 + jj) * LEAF + i] = (float)acc[jj];
+  for (int jj = 0; jj < LEAF / 2; ++jj) m = fmaxf(m, fabsf((float)acc[jj]));
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = wmax[0];
+#pragma unroll
+  for (int w = 1; w < NWAVE; ++w) m = fmaxf(m, wmax[w]);
+  const int e = pair_exponent(m);
+  if (threadIdx.x == 0) Fe[leaf] = e;
+  const size_t base = leaf * LEAF * LEAF;
+#pragma unroll
+  for (int jj = 0; jj < LEAF / 2; ++jj) {
+    _Float16 hi, lo;
+    to_pair((float)acc[jj], e, hi, lo);
+    Fh[base + (size_t)(j0 + jj) * LEAF + i] = hi;
+    Fl[base + (size_t)(j0 + jj) * LEAF + i] = lo;
+  }
+}
+
+// Slabs as fp16 pairs (one exponent per slab), in the slab layout [row][rank]
+// and transposed [rank][row].  One workgroup per (system, level, leaf) slab.
+__global__ __launch_bounds__(BNT) void k_split_slabs(const float* __restrict__ W, _Float16* __restrict__ Wh,
+                                                     _Float16* __restrict__ Wl, _Float16* __restrict__ Th,
+                                                     _Float16* __restrict__ Tl, int* __restrict__ We) {
+  constexpr int N = LEAF * RANK, PER = N / BNT;
+  __shared__ float wmax[NWAVE];
+  const size_t base = (size_t)blockIdx.x * N;
+  float v[PER];
+  float m = 0.f;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    v[u] = W[base + threadIdx.x + u * BNT];
+    m = fmaxf(m, fabsf(v[u]));
+  }
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = wmax[0];
+#pragma unroll
+  for (int w = 1; w < NWAVE; ++w) m = fmaxf(m, wmax[w]);
+  const int e = pair_exponent(m);
+  if (threadIdx.x == 0) We[blockIdx.x] = e;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int idx = threadIdx.x + u * BNT, row = idx / RANK, c = idx - row * RANK;
+    _Float16 hi, lo;
+    to_pair(v[u], e, hi, lo);
+    Wh[base + idx] = hi;
+    Wl[base + idx] = lo;
+    Th[base + (size_t)c * LEAF + row] = hi;
+    Tl[base + (size_t)c * LEAF + row] = lo;
+  }
 }
 
 // (1) leaf stage, gate and restriction: Y = F_k R_k + g R (F_k = U_k U_k^T,
-// k_leaf_blocks) and Q_l = W_l[k]^T R_k.  All global operand loads of a stage
-// are issued before its products.  A workgroup owns NCT 16-column tiles (BW =
-// 16 NCT columns): every F_k and W_l[k] operand it loads feeds the MFMAs of all
-// NCT tiles.  R is only read through the DMA into LDS, before any write of the
-// UPD update; the leaf stage reads it through a transposed copy (Ts), where a
-// lane's four contraction steps of one MFMA group are one 16-byte read.  SPLIT
-// runs the leaf stage (role 0) and the restriction (role 1) of an item in two
-// workgroups, each with its own copy of the R tile (both take the UPD update,
-// the same arithmetic; role 0 writes it back and leaves the partials).  With
-// SPLIT, role 1 loads the operands of all its levels at once; in one workgroup
-// the levels' operands are double-buffered (a level's loads are issued a level
-// ahead).  At most 256 VGPRs (two waves per SIMD), so that two workgroups share
-// a compute unit.
+// k_leaf_blocks) and Q_l = W_l[k]^T R_k, both as fp16-pair products (above).
+// The R tile comes through a DMA into LDS (fp32, for the UPD update and the
+// gate) and is then held transposed as fp16 pairs with one exponent per column
+// (from the column's largest magnitude over the leaf's rows), where a lane's
+// eight contraction steps of one MFMA are one 16-byte read.  A workgroup owns
+// NCT 16-column tiles (BW = 16 NCT columns): every F_k and W_l[k] operand it
+// loads feeds the MFMAs of all NCT tiles.  SPLIT runs the leaf stage (role 0)
+// and the restriction (role 1) of an item in two workgroups, each with its own
+// copy of the R tile (both take the UPD update, the same arithmetic; role 0
+// writes it back and leaves the partials).  At most 256 VGPRs (two waves per
+// SIMD), so that two workgroups share a compute unit.
+constexpr int RT_STRIDE = 136;   // R^T pair rows in LDS, halfs (272 B: conflict-free 16-byte reads)
 template <int LEV, int NCT, bool UPD = false, bool SPLIT = false>
-__global__ __launch_bounds__(BNT, 2) void k_block_restrict(BlockGeom G, const float* __restrict__ F,
-                                                           const float* __restrict__ W, const float* __restrict__ g,
-                                                           const float* R, float* __restrict__ Y,
-                                                           float* __restrict__ Q, BlockUpd up) {
+__global__ __launch_bounds__(BNT, 2) void k_block_restrict(BlockGeom G, BlockFactors16 fw,
+                                                           const float* __restrict__ g, const float* R,
+                                                           float* __restrict__ Y, float* __restrict__ Q, BlockUpd up) {
   constexpr int BW = BNC * NCT;
   constexpr int C4 = BW / 4;                 // 16-byte chunks per tile row
   constexpr int CH = LEAF * C4 / BNT;        // chunks of the tile per thread
   constexpr int WL = (LEV + 1) / 2;          // levels of a wave, at most
-  __shared__ __attribute__((aligned(16))) float Rs[LEAF * BW];          // R_k tile, [row][BW]
-  __shared__ __attribute__((aligned(16))) float Ts[BW * TS_STRIDE];     // R_k^T, [col][row]
+  __shared__ __attribute__((aligned(16))) float Rs[LEAF * BW];              // R_k tile, [row][BW]
+  __shared__ __attribute__((aligned(16))) _Float16 Rth[BW * RT_STRIDE];     // R^T pairs, [col][row]
+  __shared__ __attribute__((aligned(16))) _Float16 Rtl[BW * RT_STRIDE];
+  __shared__ int eR[BW];                                                    // exponent per column
+  __shared__ float cmax[NWAVE * BW];
   __shared__ double red[UPD ? NWAVE * BW : 1];
   int role = 0;
   const BItem it = SPLIT ? bitem2(G, role) : bitem(G);
@@ -176,44 +263,54 @@ __global__ __launch_bounds__(BNT, 2) void k_block_restrict(BlockGeom G, const fl
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int q = lane >> 4, r = lane & 15;
   const int c0 = it.ct * BW;
-  const float* Fk = F + ((size_t)it.s * G.K + it.k) * LEAF * LEAF;
+  const size_t leaf = (size_t)it.s * G.K + it.k;
   // restriction work of this wave: rank tile (w & 1) of levels par, par + 2, ...
   const int mt = w & 1, par = w >> 1;
-  auto wlev = [&](int l) {
-    return W + (((size_t)it.s * LEV + l) * G.K + it.k) * LEAF * RANK + 16 * mt + r;
-  };
-  auto load_level = [&](float (&dst)[32], int l) {
-    const float* Wl = wlev(l);
-#pragma unroll
-    for (int s = 0; s < 32; ++s) dst[s] = Wl[(size_t)(4 * s + q) * RANK];
-  };
-  // leaf-stage A operands: rows 32w + r and 32w + 16 + r of F_k, columns
-  // 16 ch + 4 q .. + 3 (MFMA t of group ch contracts k = 16 ch + 4 q + t), and
-  // the gate at the lane's rows of Y
-  mf4 af[LEAF / 16], bf[LEAF / 16];
+  // leaf-stage A operands: rows 32w + r and 32w + 16 + r of F_k, step s covers
+  // columns 32 s + 8 q .. + 7
+  h8 fa_h[4], fa_l[4], fb_h[4], fb_l[4];
   float gv[8];
+  int eF = 0;
   auto load_leaf = [&]() {
-    const float* Fa = Fk + (size_t)(32 * w + r) * LEAF + 4 * q;
-    const float* Fb = Fa + 16 * LEAF;
+    const _Float16* Fa_h = fw.Fh + leaf * LEAF * LEAF + (size_t)(32 * w + r) * LEAF + 8 * q;
+    const _Float16* Fa_l = fw.Fl + leaf * LEAF * LEAF + (size_t)(32 * w + r) * LEAF + 8 * q;
 #pragma unroll
-    for (int ch = 0; ch < LEAF / 16; ++ch) {
-      af[ch] = *reinterpret_cast<const mf4*>(Fa + 16 * ch);
-      bf[ch] = *reinterpret_cast<const mf4*>(Fb + 16 * ch);
+    for (int st = 0; st < 4; ++st) {
+      fa_h[st] = *reinterpret_cast<const h8*>(Fa_h + 32 * st);
+      fa_l[st] = *reinterpret_cast<const h8*>(Fa_l + 32 * st);
+      fb_h[st] = *reinterpret_cast<const h8*>(Fa_h + 16 * LEAF + 32 * st);
+      fb_l[st] = *reinterpret_cast<const h8*>(Fa_l + 16 * LEAF + 32 * st);
     }
+    eF = fw.Fe[leaf];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       gv[v] = g[it.leaf0 + 32 * w + 4 * q + v];
       gv[4 + v] = g[it.leaf0 + 32 * w + 16 + 4 * q + v];
     }
   };
-  float wv[SPLIT ? WL : 2][32];
+  // restriction A operands of the wave's levels: row 16 mt + r of W_l[k]^T, step
+  // s covers rows 32 s + 8 q .. + 7 of the slab.  SPLIT: every level's at once;
+  // in one workgroup two levels' worth, a level's issued a level ahead.
+  constexpr int NB = SPLIT ? (WL > 0 ? WL : 1) : 2;
+  h8 wt_h[NB][4], wt_l[NB][4];
+  int eW[NB];
+  auto load_slot = [&](int b, int l) {
+    const size_t slab = ((size_t)it.s * LEV + l) * G.K + it.k;
+    const size_t o = slab * LEAF * RANK + (size_t)(16 * mt + r) * LEAF + 8 * q;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      wt_h[b][st] = *reinterpret_cast<const h8*>(fw.Th + o + 32 * st);
+      wt_l[b][st] = *reinterpret_cast<const h8*>(fw.Tl + o + 32 * st);
+    }
+    eW[b] = fw.We[slab];
+  };
   auto load_restr = [&]() {
     if constexpr (SPLIT) {
 #pragma unroll
       for (int i = 0; i < WL; ++i)
-        if (par + 2 * i < LEV) load_level(wv[i], par + 2 * i);
+        if (par + 2 * i < LEV) load_slot(i, par + 2 * i);
     } else {
-      if (par < LEV) load_level(wv[0], par);
+      if (par < LEV) load_slot(0, par);
     }
   };
   // R tile: 128 rows x 4 BW bytes, straight into LDS
@@ -234,102 +331,122 @@ __global__ __launch_bounds__(BNT, 2) void k_block_restrict(BlockGeom G, const fl
       ap[i] = *reinterpret_cast<const mf4*>(up.AP + (size_t)(it.leaf0 + row) * G.nrhs + cc);
     }
   }
-  // every load so far has landed; the UPD update of the R tile and, for the
-  // leaf stage, the transposed copy
-  auto wait_update = [&](bool transpose) {
+  // every load so far has landed; the UPD update of the R tile, the columns'
+  // exponents and the R^T pairs
+  auto wait_update = [&]() {
     lds_dma_wait();
     stamp(wgi, 1);
-    if (UPD || transpose) {
+    mf4 mx = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < CH; ++i) {
-        const int c = tid + BNT * i, row = c / C4, col = 4 * (c % C4);
-        mf4 v = *reinterpret_cast<const mf4*>(&Rs[4 * c]);
-        if constexpr (UPD) {
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            if (al[t] != 0.0) v[t] = (float)((double)v[t] - al[t] * (double)ap[i][t]);
-            rr4[t] = fma((double)v[t], (double)v[t], rr4[t]);
-          }
-          *reinterpret_cast<mf4*>(&Rs[4 * c]) = v;
-          if (leaf_role) *reinterpret_cast<mf4*>(up.R + (size_t)(it.leaf0 + row) * G.nrhs + cc) = v;
-        }
-        if (transpose) {
-#pragma unroll
-          for (int t = 0; t < 4; ++t) Ts[(col + t) * TS_STRIDE + row] = v[t];
-        }
-      }
-      if (UPD && leaf_role) {
-        // R.R partials of the wave: lanes with the same columns differ in lane
-        // bits >= log2(C4) (fixed butterfly); summed over the waves at the end
+    for (int i = 0; i < CH; ++i) {
+      const int c = tid + BNT * i, row = c / C4;
+      mf4 v = *reinterpret_cast<const mf4*>(&Rs[4 * c]);
+      if constexpr (UPD) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-#pragma unroll
-          for (int o = C4; o < 64; o <<= 1) rr4[t] += __shfl_xor(rr4[t], o);
+          if (al[t] != 0.0) v[t] = (float)((double)v[t] - al[t] * (double)ap[i][t]);
+          rr4[t] = fma((double)v[t], (double)v[t], rr4[t]);
         }
-        if (lane < C4) {
-#pragma unroll
-          for (int t = 0; t < 4; ++t) red[w * BW + 4 * lane + t] = rr4[t];
-        }
+        *reinterpret_cast<mf4*>(&Rs[4 * c]) = v;
+        if (leaf_role) *reinterpret_cast<mf4*>(up.R + (size_t)(it.leaf0 + row) * G.nrhs + cc) = v;
       }
-      __syncthreads();
+#pragma unroll
+      for (int t = 0; t < 4; ++t) mx[t] = fmaxf(mx[t], fabsf(v[t]));
     }
+    // column maxima: lanes with the same columns differ in lane bits >= log2(C4)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int o = C4; o < 64; o <<= 1) mx[t] = fmaxf(mx[t], __shfl_xor(mx[t], o));
+    }
+    if (lane < C4) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) cmax[w * BW + 4 * lane + t] = mx[t];
+    }
+    if (UPD && leaf_role) {
+      // R.R partials of the wave (fixed butterfly); summed over the waves at the end
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int o = C4; o < 64; o <<= 1) rr4[t] += __shfl_xor(rr4[t], o);
+      }
+      if (lane < C4) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) red[w * BW + 4 * lane + t] = rr4[t];
+      }
+    }
+    __syncthreads();
+    if (tid < BW) {
+      float m = cmax[tid];
+#pragma unroll
+      for (int ww = 1; ww < NWAVE; ++ww) m = fmaxf(m, cmax[ww * BW + tid]);
+      eR[tid] = pair_exponent(m);
+    }
+    __syncthreads();
+    int ec[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) ec[t] = eR[4 * (tid % C4) + t];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = tid + BNT * i, row = c / C4, col = 4 * (c % C4);
+      const mf4 v = *reinterpret_cast<const mf4*>(&Rs[4 * c]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        _Float16 hi, lo;
+        to_pair(v[t], ec[t], hi, lo);
+        Rth[(col + t) * RT_STRIDE + row] = hi;
+        Rtl[(col + t) * RT_STRIDE + row] = lo;
+      }
+    }
+    __syncthreads();
     stamp(wgi, 2);
   };
-  // restriction Q_l = W_l[k]^T R_k, two accumulation chains (even / odd k
-  // steps) summed at the end.  SPLIT: every level's operands are in registers,
-  // so the tiles are the outer loop and a tile's R operands are read once.
+  // the R^T pair operands of tile j: step s covers rows 32 s + 8 q .. + 7
+  auto load_b = [&](int j, h8 (&bh)[4], h8 (&bl)[4]) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      bh[st] = *reinterpret_cast<const h8*>(&Rth[(16 * j + r) * RT_STRIDE + 32 * st + 8 * q]);
+      bl[st] = *reinterpret_cast<const h8*>(&Rtl[(16 * j + r) * RT_STRIDE + 32 * st + 8 * q]);
+    }
+  };
+  // restriction Q_l = W_l[k]^T R_k.  SPLIT: tiles outer, the wave's levels
+  // inner (a tile's R operands are read once); in one workgroup levels outer,
+  // the next level's operands issued here and not hoisted.
+  auto restrict_one = [&](int b, int l, int j, const h8 (&bh)[4], const h8 (&bl)[4]) {
+    mf4 acc = {0, 0, 0, 0};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) acc = mfma_pair(wt_h[b][st], wt_l[b][st], bh[st], bl[st], acc);
+    const float sc = ldexpf(1.f, -(eW[b] + eR[16 * j + r]));
+    float* Qo = Q + q_index(G, it.s, l, it.k, 16 * mt + 4 * q) + c0 + r;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) Qo[(size_t)v * G.nrhs + 16 * j] = acc[v] * sc;
+  };
   auto restriction = [&]() {
     if constexpr (SPLIT) {
 #pragma unroll
       for (int j = 0; j < NCT; ++j) {
-        float rv[32];
-#pragma unroll
-        for (int s = 0; s < 32; ++s) rv[s] = Rs[(4 * s + q) * BW + 16 * j + r];
-        __builtin_amdgcn_sched_barrier(0);
+        h8 bh[4], bl[4];
+        load_b(j, bh, bl);
 #pragma unroll
         for (int i = 0; i < WL; ++i) {
           const int l = par + 2 * i;
           if (l >= LEV) break;
-          mf4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
-#pragma unroll
-          for (int s = 0; s < 32; s += 2) {
-            a0 = mfma4(wv[i][s], rv[s], a0);
-            a1 = mfma4(wv[i][s + 1], rv[s + 1], a1);
-          }
-          const mf4 acc = a0 + a1;
-          float* Qo = Q + q_index(G, it.s, l, it.k, 16 * mt + 4 * q) + c0 + r;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) Qo[(size_t)v * G.nrhs + 16 * j] = acc[v];
+          restrict_one(i, l, j, bh, bl);
         }
       }
-      stamp(wgi, 4);
-      return;
-    }
+    } else {
 #pragma unroll
-    for (int i = 0; i < WL; ++i) {
-      const int l = par + 2 * i;
-      if (l >= LEV) break;
-      // the level two ahead, issued here and not hoisted (that would hold
-      // every level's operands at once)
-      asm volatile("" ::: "memory");
-      if (l + 2 < LEV) load_level(wv[(i + 1) & 1], l + 2);
-      const float(&wa)[32] = wv[i & 1];
-      float* Qo = Q + q_index(G, it.s, l, it.k, 16 * mt + 4 * q) + c0 + r;
+      for (int i = 0; i < WL; ++i) {
+        const int l = par + 2 * i;
+        if (l >= LEV) break;
+        asm volatile("" ::: "memory");
+        if (l + 2 < LEV) load_slot((i + 1) & 1, l + 2);
 #pragma unroll
-      for (int j = 0; j < NCT; ++j) {
-        float rv[32];
-#pragma unroll
-        for (int s = 0; s < 32; ++s) rv[s] = Rs[(4 * s + q) * BW + 16 * j + r];
-        __builtin_amdgcn_sched_barrier(0);
-        mf4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
-#pragma unroll
-        for (int s = 0; s < 32; s += 2) {
-          a0 = mfma4(wa[s], rv[s], a0);
-          a1 = mfma4(wa[s + 1], rv[s + 1], a1);
+        for (int j = 0; j < NCT; ++j) {
+          h8 bh[4], bl[4];
+          load_b(j, bh, bl);
+          restrict_one(i & 1, l, j, bh, bl);
         }
-        const mf4 acc = a0 + a1;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) Qo[(size_t)v * G.nrhs + 16 * j] = acc[v];
       }
     }
     stamp(wgi, 4);
@@ -338,39 +455,34 @@ __global__ __launch_bounds__(BNT, 2) void k_block_restrict(BlockGeom G, const fl
   auto leaf_stage = [&]() {
 #pragma unroll
     for (int j = 0; j < NCT; ++j) {
+      h8 bh[4], bl[4];
+      load_b(j, bh, bl);
       mf4 ya = {0, 0, 0, 0}, yb = {0, 0, 0, 0};
-      mf4 bt[LEAF / 16];           // the tile's R^T operands, read ahead of the products
 #pragma unroll
-      for (int ch = 0; ch < LEAF / 16; ++ch)
-        bt[ch] = *reinterpret_cast<const mf4*>(&Ts[(16 * j + r) * TS_STRIDE + 16 * ch + 4 * q]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int ch = 0; ch < LEAF / 16; ++ch) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          ya = mfma4(af[ch][t], bt[ch][t], ya);
-          yb = mfma4(bf[ch][t], bt[ch][t], yb);
-        }
+      for (int st = 0; st < 4; ++st) {
+        ya = mfma_pair(fa_h[st], fa_l[st], bh[st], bl[st], ya);
+        yb = mfma_pair(fb_h[st], fb_l[st], bh[st], bl[st], yb);
       }
+      const float sc = ldexpf(1.f, -(eF + eR[16 * j + r]));
       const int cj = c0 + 16 * j + r;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int ia = 32 * w + 4 * q + v, ib = ia + 16;
-        Y[(size_t)(it.leaf0 + ia) * G.nrhs + cj] = ya[v] + gv[v] * Rs[ia * BW + 16 * j + r];
-        Y[(size_t)(it.leaf0 + ib) * G.nrhs + cj] = yb[v] + gv[4 + v] * Rs[ib * BW + 16 * j + r];
+        Y[(size_t)(it.leaf0 + ia) * G.nrhs + cj] = ya[v] * sc + gv[v] * Rs[ia * BW + 16 * j + r];
+        Y[(size_t)(it.leaf0 + ib) * G.nrhs + cj] = yb[v] * sc + gv[4 + v] * Rs[ib * BW + 16 * j + r];
       }
     }
     stamp(wgi, 6);
   };
-  if (SPLIT && role == 1) {        // the restriction alone: its operands of every level at once
+  if (SPLIT && role == 1) {        // the restriction alone
     load_restr();
-    wait_update(false);
+    wait_update();
     restriction();
     return;
   }
   load_leaf();
   if constexpr (!SPLIT) load_restr();
-  wait_update(true);
+  wait_update();
   leaf_stage();
   if constexpr (!SPLIT) restriction();
   if constexpr (UPD) {
@@ -417,38 +529,45 @@ __global__ void k_block_halfsum(BlockGeom G, const float* __restrict__ Q, float*
   }
 }
 
-// (3) prolongation: Y_k += sum_l W_l[k] H_l[(k >> l) ^ 1].  Every level's slab
-// rows are loaded in one batch up front and feed the MFMAs of all NCT tiles.
+// (3) prolongation: Y_k += sum_l W_l[k] H_l[(k >> l) ^ 1] as fp16-pair products
+// (the slab rows held as pairs with the slab's exponent, the partner half sums
+// as pairs with one exponent per (level, column), taken from the largest of the
+// column's 32 values).  The levels run in two stages: the first stage's
+// products while the second stage's operands are still arriving; the products
+// keep level order.
+constexpr int PH_STRIDE = 40;   // half-sum pair rows in LDS, halfs (80 B)
 template <int LEV, int NCT, bool DOT = false>
-__global__ __launch_bounds__(BNT) void k_block_prolong(BlockGeom G, const float* __restrict__ W,
+__global__ __launch_bounds__(BNT) void k_block_prolong(BlockGeom G, BlockFactors16 fw,
                                                        const float* __restrict__ H, float* __restrict__ Y,
                                                        BlockDot dt) {
   constexpr int BW = BNC * NCT;
-  __shared__ __attribute__((aligned(16))) float Ps[(LEV > 0 ? LEV : 1) * BW * PS_STRIDE];   // [l][col][rank]
+  constexpr int NL = LEV > 0 ? LEV : 1;
+  __shared__ __attribute__((aligned(16))) _Float16 Phh[NL * BW * PH_STRIDE];   // [l][col][rank]
+  __shared__ __attribute__((aligned(16))) _Float16 Phl[NL * BW * PH_STRIDE];
+  __shared__ int emax[NL * BW];                                                // largest |H| bits
   __shared__ double red[DOT ? NWAVE * BW : 1];
   const BItem it = bitem(G);
   stamp((int)blockIdx.x, 8);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int q = lane >> 4, r = lane & 15;
   const int c0 = it.ct * BW;
-  // two stages of levels: the first stage's products run while the second
-  // stage's operands are still arriving; the products keep level order
   constexpr int LA = (LEV + 1) / 2, LB = LEV - LA;
   constexpr int PE = RANK * BW / BNT;        // half-sum elements per thread and level
-  mf4 aw[LEV > 0 ? LEV : 1][2], bw[LEV > 0 ? LEV : 1][2];
+  // slab rows 32w + r (a) and 32w + 16 + r (b), rank 8q .. 8q + 7
+  h8 wa_h[NL], wa_l[NL], wb_h[NL], wb_l[NL];
+  int eW[NL];
   auto load_w = [&](int l0, int l1) {
 #pragma unroll
     for (int l = l0; l < l1; ++l) {
-      const float* Wa = W + ((((size_t)it.s * LEV + l) * G.K + it.k) * LEAF + 32 * w + r) * RANK + 4 * q;
-#pragma unroll
-      for (int ch = 0; ch < 2; ++ch) {
-        aw[l][ch] = *reinterpret_cast<const mf4*>(Wa + 16 * ch);
-        bw[l][ch] = *reinterpret_cast<const mf4*>(Wa + 16 * RANK + 16 * ch);
-      }
+      const size_t slab = ((size_t)it.s * LEV + l) * G.K + it.k;
+      const size_t o = slab * LEAF * RANK + (size_t)(32 * w + r) * RANK + 8 * q;
+      wa_h[l] = *reinterpret_cast<const h8*>(fw.Wh + o);
+      wa_l[l] = *reinterpret_cast<const h8*>(fw.Wl + o);
+      wb_h[l] = *reinterpret_cast<const h8*>(fw.Wh + o + 16 * RANK);
+      wb_l[l] = *reinterpret_cast<const h8*>(fw.Wl + o + 16 * RANK);
+      eW[l] = fw.We[slab];
     }
   };
-  // partner half sums of levels [l0, l0 + NL): loads, then their transposed
-  // stores into LDS
   auto load_h = [&](float* hv, int l0, int nl) {
 #pragma unroll
     for (int u = 0; u < nl * PE; ++u) {
@@ -458,15 +577,29 @@ __global__ __launch_bounds__(BNT) void k_block_prolong(BlockGeom G, const float*
       hv[u] = H[q_index(G, it.s, l, (it.k >> l) ^ 1, row) + c0 + col];
     }
   };
+  // the column maxima of levels [l0, l0 + nl) (as the bits of positive floats)
+  auto max_h = [&](const float* hv, int l0, int nl) {
+#pragma unroll
+    for (int u = 0; u < nl * PE; ++u) {
+      const int e = tid + u * BNT;
+      const int l = l0 + e / (RANK * BW), rem = e % (RANK * BW);
+      const int col = rem % BW;
+      atomicMax(&emax[l * BW + col], __float_as_int(fabsf(hv[u])));
+    }
+  };
   auto store_h = [&](const float* hv, int l0, int nl) {
 #pragma unroll
     for (int u = 0; u < nl * PE; ++u) {
       const int e = tid + u * BNT;
       const int l = l0 + e / (RANK * BW), rem = e % (RANK * BW);
       const int row = rem / BW, col = rem - row * BW;
-      Ps[(l * BW + col) * PS_STRIDE + row] = hv[u];
+      _Float16 hi, lo;
+      to_pair(hv[u], pair_exponent(__int_as_float(emax[l * BW + col])), hi, lo);
+      Phh[(l * BW + col) * PH_STRIDE + row] = hi;
+      Phl[(l * BW + col) * PH_STRIDE + row] = lo;
     }
   };
+  for (int e = tid; e < LEV * BW; e += BNT) emax[e] = 0;
   // accumulators start from the leaf stage's Y
   mf4 ya[NCT], yb[NCT];
 #pragma unroll
@@ -481,16 +614,16 @@ __global__ __launch_bounds__(BNT) void k_block_prolong(BlockGeom G, const float*
 #pragma unroll
     for (int l = l0; l < l1; ++l) {
 #pragma unroll
-      for (int ch = 0; ch < RANK / 16; ++ch) {
-#pragma unroll
-        for (int j = 0; j < NCT; ++j) {
-          const mf4 bp = *reinterpret_cast<const mf4*>(&Ps[(l * BW + 16 * j + r) * PS_STRIDE + 16 * ch + 4 * q]);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            ya[j] = mfma4(aw[l][ch][t], bp[t], ya[j]);
-            yb[j] = mfma4(bw[l][ch][t], bp[t], yb[j]);
-          }
-        }
+      for (int j = 0; j < NCT; ++j) {
+        const int col = 16 * j + r;
+        const h8 bh = *reinterpret_cast<const h8*>(&Phh[(l * BW + col) * PH_STRIDE + 8 * q]);
+        const h8 bl = *reinterpret_cast<const h8*>(&Phl[(l * BW + col) * PH_STRIDE + 8 * q]);
+        const mf4 z = {0, 0, 0, 0};
+        const mf4 pa = mfma_pair(wa_h[l], wa_l[l], bh, bl, z);
+        const mf4 pb = mfma_pair(wb_h[l], wb_l[l], bh, bl, z);
+        const float sc = ldexpf(1.f, -(eW[l] + pair_exponent(__int_as_float(emax[l * BW + col]))));
+        ya[j] += pa * sc;
+        yb[j] += pb * sc;
       }
     }
   };
@@ -511,11 +644,16 @@ __global__ __launch_bounds__(BNT) void k_block_prolong(BlockGeom G, const float*
       }
     }
   }
+  __syncthreads();                 // emax cleared
+  max_h(ha, 0, LA);
+  __syncthreads();
   store_h(ha, 0, LA);
   __syncthreads();
   stamp((int)blockIdx.x, 9);
   products(0, LA);
   if constexpr (LB > 0) {
+    max_h(hb, LA, LB);
+    __syncthreads();
     store_h(hb, LA, LB);
     __syncthreads();
     products(LA, LEV);

@@ -109,7 +109,6 @@ struct Bufs {
   const int* col;
   const float* val;
   const float* U;      // [B][K][LEAF][LEAF]
-  const float* F;      // [B][K][LEAF][LEAF] dense leaf blocks U_k U_k^T (block apply)
   const float* W;      // [B][levels][K][LEAF][RANK]
   const float* g;      // [B*n]
   const float* b;      // [B*n]

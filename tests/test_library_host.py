@@ -57,7 +57,9 @@ def test_workspace_bytes_covers_the_buffers(hp):
     nnz = 110592
     nbytes = hp.hpcg_workspace_bytes(part, nnz)
     factors = 128 * 128 * 128 * 4 + 7 * 128 * 128 * 32 * 4
-    factors += 128 * 128 * 128 * 4                # dense leaf blocks U_k U_k^T (block apply)
+    # block apply: dense leaf blocks U_k U_k^T and the slabs (also transposed) as
+    # fp16 pairs, one exponent per leaf and per slab
+    factors += 128 * 128 * 128 * 4 + 128 * 4 + 2 * 7 * 128 * 128 * 32 * 4 + 7 * 128 * 4
     csr = (16385 + 2 * nnz) * 4
     vectors = 16384 * (2 * 4 + 7 * 8)            # g, b fp32; r (two), z, q, p0, p1, x fp64
     # per leaf: diagonal shares of up to 8 slots and two copies of W_l[k]^T r_k, fp64
