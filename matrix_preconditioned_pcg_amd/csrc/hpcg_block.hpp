@@ -252,7 +252,7 @@ __global__ __launch_bounds__(BNT, 2) void k_block_restrict(BlockGeom G, BlockFac
   __shared__ __attribute__((aligned(16))) _Float16 Rth[BW * RT_STRIDE];     // R^T pairs, [col][row]
   __shared__ __attribute__((aligned(16))) _Float16 Rtl[BW * RT_STRIDE];
   __shared__ int eR[BW];                                                    // exponent per column
-  __shared__ float cmax[NWAVE * BW];
+  __shared__ float cmax[BNT];                                               // per (row group, column)
   __shared__ double red[UPD ? NWAVE * BW : 1];
   int role = 0;
   const BItem it = SPLIT ? bitem2(G, role) : bitem(G);
@@ -336,12 +336,11 @@ __global__ __launch_bounds__(BNT, 2) void k_block_restrict(BlockGeom G, BlockFac
   auto wait_update = [&]() {
     lds_dma_wait();
     stamp(wgi, 1);
-    mf4 mx = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (UPD) {
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = tid + BNT * i, row = c / C4;
-      mf4 v = *reinterpret_cast<const mf4*>(&Rs[4 * c]);
-      if constexpr (UPD) {
+      for (int i = 0; i < CH; ++i) {
+        const int c = tid + BNT * i, row = c / C4;
+        mf4 v = *reinterpret_cast<const mf4*>(&Rs[4 * c]);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           if (al[t] != 0.0) v[t] = (float)((double)v[t] - al[t] * (double)ap[i][t]);
@@ -350,53 +349,50 @@ __global__ __launch_bounds__(BNT, 2) void k_block_restrict(BlockGeom G, BlockFac
         *reinterpret_cast<mf4*>(&Rs[4 * c]) = v;
         if (leaf_role) *reinterpret_cast<mf4*>(up.R + (size_t)(it.leaf0 + row) * G.nrhs + cc) = v;
       }
+      if (leaf_role) {
+        // R.R partials of the wave (fixed butterfly); summed over the waves at the end
 #pragma unroll
-      for (int t = 0; t < 4; ++t) mx[t] = fmaxf(mx[t], fabsf(v[t]));
-    }
-    // column maxima: lanes with the same columns differ in lane bits >= log2(C4)
+        for (int t = 0; t < 4; ++t) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+          for (int o = C4; o < 64; o <<= 1) rr4[t] += __shfl_xor(rr4[t], o);
+        }
+        if (lane < C4) {
 #pragma unroll
-      for (int o = C4; o < 64; o <<= 1) mx[t] = fmaxf(mx[t], __shfl_xor(mx[t], o));
-    }
-    if (lane < C4) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) cmax[w * BW + 4 * lane + t] = mx[t];
-    }
-    if (UPD && leaf_role) {
-      // R.R partials of the wave (fixed butterfly); summed over the waves at the end
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-#pragma unroll
-        for (int o = C4; o < 64; o <<= 1) rr4[t] += __shfl_xor(rr4[t], o);
-      }
-      if (lane < C4) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) red[w * BW + 4 * lane + t] = rr4[t];
+          for (int t = 0; t < 4; ++t) red[w * BW + 4 * lane + t] = rr4[t];
+        }
       }
     }
+    __syncthreads();                 // the whole tile in LDS (and updated)
+    // the R^T pairs, a column pass: thread t takes column t % BW and the RPT
+    // rows of row group t / BW; the column's exponent from its largest
+    // magnitude over the row groups; eight pairs per 16-byte store
+    constexpr int RG = BNT / BW, RPT = LEAF / RG;
+    const int col = tid % BW, rg = tid / BW;
+    float v[RPT];
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      v[i] = Rs[(rg * RPT + i) * BW + col];
+      m = fmaxf(m, fabsf(v[i]));
+    }
+    cmax[rg * BW + col] = m;
     __syncthreads();
-    if (tid < BW) {
-      float m = cmax[tid];
 #pragma unroll
-      for (int ww = 1; ww < NWAVE; ++ww) m = fmaxf(m, cmax[ww * BW + tid]);
-      eR[tid] = pair_exponent(m);
-    }
-    __syncthreads();
-    int ec[4];
+    for (int g2 = 0; g2 < RG; ++g2) m = fmaxf(m, cmax[g2 * BW + col]);
+    const int e = pair_exponent(m);
+    if (rg == 0) eR[col] = e;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) ec[t] = eR[4 * (tid % C4) + t];
+    for (int c8 = 0; c8 < RPT / 8; ++c8) {
+      h8 hi, lo;
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = tid + BNT * i, row = c / C4, col = 4 * (c % C4);
-      const mf4 v = *reinterpret_cast<const mf4*>(&Rs[4 * c]);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        _Float16 hi, lo;
-        to_pair(v[t], ec[t], hi, lo);
-        Rth[(col + t) * RT_STRIDE + row] = hi;
-        Rtl[(col + t) * RT_STRIDE + row] = lo;
+      for (int i = 0; i < 8; ++i) {
+        _Float16 a, b;
+        to_pair(v[8 * c8 + i], e, a, b);
+        hi[i] = a;
+        lo[i] = b;
       }
+      *reinterpret_cast<h8*>(&Rth[col * RT_STRIDE + rg * RPT + 8 * c8]) = hi;
+      *reinterpret_cast<h8*>(&Rtl[col * RT_STRIDE + rg * RPT + 8 * c8]) = lo;
     }
     __syncthreads();
     stamp(wgi, 2);
@@ -542,9 +538,11 @@ __global__ __launch_bounds__(BNT) void k_block_prolong(BlockGeom G, BlockFactors
                                                        BlockDot dt) {
   constexpr int BW = BNC * NCT;
   constexpr int NL = LEV > 0 ? LEV : 1;
+  constexpr int NS = (NL + 1) / 2;                                             // levels of a stage, at most
+  __shared__ float Hs[NS * RANK * BW];                                         // [l - l0][rank][col]
   __shared__ __attribute__((aligned(16))) _Float16 Phh[NL * BW * PH_STRIDE];   // [l][col][rank]
   __shared__ __attribute__((aligned(16))) _Float16 Phl[NL * BW * PH_STRIDE];
-  __shared__ int emax[NL * BW];                                                // largest |H| bits
+  __shared__ int eH[NL * BW];                                                  // exponent per (l, col)
   __shared__ double red[DOT ? NWAVE * BW : 1];
   const BItem it = bitem(G);
   stamp((int)blockIdx.x, 8);
@@ -577,29 +575,41 @@ __global__ __launch_bounds__(BNT) void k_block_prolong(BlockGeom G, BlockFactors
       hv[u] = H[q_index(G, it.s, l, (it.k >> l) ^ 1, row) + c0 + col];
     }
   };
-  // the column maxima of levels [l0, l0 + nl) (as the bits of positive floats)
-  auto max_h = [&](const float* hv, int l0, int nl) {
+  // levels [l0, l0 + nl): the half sums into LDS as they are laid out (fp32;
+  // the two stages take turns in one buffer), then a column pass: a thread per
+  // (level, column), its 32 values' exponent and their pairs, eight per
+  // 16-byte store
+  auto stage_h = [&](const float* hv, int l0, int nl) {
 #pragma unroll
-    for (int u = 0; u < nl * PE; ++u) {
-      const int e = tid + u * BNT;
-      const int l = l0 + e / (RANK * BW), rem = e % (RANK * BW);
-      const int col = rem % BW;
-      atomicMax(&emax[l * BW + col], __float_as_int(fabsf(hv[u])));
+    for (int u = 0; u < nl * PE; ++u) Hs[tid + u * BNT] = hv[u];
+  };
+  auto pair_h = [&](int l0, int nl) {
+    for (int p = tid; p < nl * BW; p += BNT) {
+      const int l = l0 + p / BW, col = p % BW;
+      float v[RANK];
+      float m = 0.f;
+#pragma unroll
+      for (int i = 0; i < RANK; ++i) {
+        v[i] = Hs[((l - l0) * RANK + i) * BW + col];
+        m = fmaxf(m, fabsf(v[i]));
+      }
+      const int e = pair_exponent(m);
+      eH[l * BW + col] = e;
+#pragma unroll
+      for (int c8 = 0; c8 < RANK / 8; ++c8) {
+        h8 hi, lo;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          _Float16 a, b;
+          to_pair(v[8 * c8 + i], e, a, b);
+          hi[i] = a;
+          lo[i] = b;
+        }
+        *reinterpret_cast<h8*>(&Phh[(l * BW + col) * PH_STRIDE + 8 * c8]) = hi;
+        *reinterpret_cast<h8*>(&Phl[(l * BW + col) * PH_STRIDE + 8 * c8]) = lo;
+      }
     }
   };
-  auto store_h = [&](const float* hv, int l0, int nl) {
-#pragma unroll
-    for (int u = 0; u < nl * PE; ++u) {
-      const int e = tid + u * BNT;
-      const int l = l0 + e / (RANK * BW), rem = e % (RANK * BW);
-      const int row = rem / BW, col = rem - row * BW;
-      _Float16 hi, lo;
-      to_pair(hv[u], pair_exponent(__int_as_float(emax[l * BW + col])), hi, lo);
-      Phh[(l * BW + col) * PH_STRIDE + row] = hi;
-      Phl[(l * BW + col) * PH_STRIDE + row] = lo;
-    }
-  };
-  for (int e = tid; e < LEV * BW; e += BNT) emax[e] = 0;
   // accumulators start from the leaf stage's Y
   mf4 ya[NCT], yb[NCT];
 #pragma unroll
@@ -621,7 +631,7 @@ __global__ __launch_bounds__(BNT) void k_block_prolong(BlockGeom G, BlockFactors
         const mf4 z = {0, 0, 0, 0};
         const mf4 pa = mfma_pair(wa_h[l], wa_l[l], bh, bl, z);
         const mf4 pb = mfma_pair(wb_h[l], wb_l[l], bh, bl, z);
-        const float sc = ldexpf(1.f, -(eW[l] + pair_exponent(__int_as_float(emax[l * BW + col]))));
+        const float sc = ldexpf(1.f, -(eW[l] + eH[l * BW + col]));
         ya[j] += pa * sc;
         yb[j] += pb * sc;
       }
@@ -644,17 +654,16 @@ __global__ __launch_bounds__(BNT) void k_block_prolong(BlockGeom G, BlockFactors
       }
     }
   }
-  __syncthreads();                 // emax cleared
-  max_h(ha, 0, LA);
+  stage_h(ha, 0, LA);
   __syncthreads();
-  store_h(ha, 0, LA);
+  pair_h(0, LA);
   __syncthreads();
   stamp((int)blockIdx.x, 9);
   products(0, LA);
   if constexpr (LB > 0) {
-    max_h(hb, LA, LB);
+    stage_h(hb, LA, LB);
     __syncthreads();
-    store_h(hb, LA, LB);
+    pair_h(LA, LB);
     __syncthreads();
     products(LA, LEV);
   }
