@@ -1129,7 +1129,7 @@ hpcg_status launch_block_apply(hpcg_ctx* h, int32_t nrhs, const float* d_R, floa
   }
   if (h->G.levels > 0) {
     size_t sys_total = 0;
-    for (int l = 0; l < h->G.levels; ++l) sys_total += (size_t)(h->G.K >> l) * RANK * nrhs;
+    for (int l = 0; l < h->G.levels; ++l) sys_total += (size_t)(h->G.K >> l) * RANK * nrhs * halfsum_runs(l);
     hipLaunchKernelGGL(k_block_halfsum, dim3((unsigned)((sys_total + 255) / 256), (unsigned)std::min(h->G.B, 65535)),
                        dim3(256), 0, stream, bg, Q, H);
 #define HPCG_BLOCK_PROLONG_N(LV, N)                                                                     \
@@ -1261,16 +1261,15 @@ hpcg_status block_iteration(hpcg_ctx* h, int32_t nrhs, char* wk, const BlockSolv
   ColState* cs = reinterpret_cast<ColState*>(wk + L.cs);
   const int rblocks = G.n / BS_ROWS;   // row blocks per system
   const dim3 rows_grid((unsigned)(G.B * rblocks), (unsigned)((nrhs + BS_COLS - 1) / BS_COLS));
-  const int ncol = G.B * nrhs;
-  const dim3 sc_grid((unsigned)((ncol + BS_SC_COLS - 1) / BS_SC_COLS));
-  hipLaunchKernelGGL(k_bs_spmv_dot, rows_grid, dim3(BS_SPMV_NT), 0, stream, h->B.row_ptr, h->B.col, h->B.val, P, Q,
+  const dim3 spmv_grid((unsigned)(G.B * G.K), (unsigned)((nrhs + BS_SPMV_COLS - 1) / BS_SPMV_COLS));
+  const dim3 dir_grid((unsigned)(G.B * G.K), (unsigned)((nrhs + BS_DIR_COLS - 1) / BS_DIR_COLS));
+  // Q = A P and the p.q partials per leaf
+  hipLaunchKernelGGL(k_bs_spmv_dot, spmv_grid, dim3(BS_SPMV_NT), 0, stream, h->B.row_ptr, h->B.col, h->B.val, P, Q,
                      part, nrhs);
-  hipLaunchKernelGGL(k_bs_scalars<BS_PQ>, sc_grid, dim3(64 * BS_SC_COLS), 0, stream, cs, part, G.B, nrhs, rblocks, tol, maxit,
-                     (const double*)nullptr, 0);
-  // R -= alpha Q and the r.r partials in the leaf stage; the r.z partials in
-  // the prolongation (per leaf), or, without tile levels, by a pass of their own
-  static_assert(sizeof(ColState) % sizeof(double) == 0, "ColState holds whole doubles");
-  const BlockUpd upd{&cs[0].alpha, (int)(sizeof(ColState) / sizeof(double)), Q, R, part2};
+  // the PQ step, R -= alpha Q and the r.r partials in the leaf stage; the r.z
+  // partials in the prolongation (per leaf), or, without tile levels, by a pass
+  // of their own
+  const BlockUpd upd{cs, part, Q, R, part2};
   const BlockDot dot{R, part};
   hpcg_status s = launch_block_apply(h, nrhs, R, Z, reinterpret_cast<float*>(wk + L.scratchQ),
                                      reinterpret_cast<float*>(wk + L.scratchH), stream, &upd, &dot);
@@ -1280,9 +1279,9 @@ hpcg_status block_iteration(hpcg_ctx* h, int32_t nrhs, char* wk, const BlockSolv
     hipLaunchKernelGGL(k_bs_dot, rows_grid, dim3(BS_NT), 0, stream, R, Z, part, nrhs);
     rz_blocks = rblocks;
   }
-  hipLaunchKernelGGL(k_bs_scalars<BS_RRZ>, sc_grid, dim3(64 * BS_SC_COLS), 0, stream, cs, part, G.B, nrhs, rz_blocks,
-                     tol, maxit, (const double*)part2, G.K);
-  hipLaunchKernelGGL(k_bs_direction, rows_grid, dim3(BS_NT), 0, stream, cs, Z, P, d_X, nrhs, rblocks);
+  // the RRZ step, X += alpha P and P = Z + beta P
+  const BsRrz rrz{part, rz_blocks, part2, G.K, tol, maxit};
+  hipLaunchKernelGGL(k_bs_direction<true>, dir_grid, dim3(BS_DIR_NT), 0, stream, cs, Z, P, d_X, nrhs, G.K, rrz);
   return HPCG_OK;
 }
 
@@ -1319,7 +1318,7 @@ hpcg_status hpcg_solve_block(hpcg_handle h, const float* d_B, double* d_X, int32
   const int rblocks = G.n / BS_ROWS;   // row blocks per system
   const dim3 rows_grid((unsigned)(G.B * rblocks), (unsigned)((nrhs + BS_COLS - 1) / BS_COLS));
   const int ncol = G.B * nrhs;
-  const dim3 sc_grid((unsigned)((ncol + BS_SC_COLS - 1) / BS_SC_COLS));
+  const dim3 sc_grid((unsigned)(G.B * (nrhs / BS_SC_C)));
 
   // the recorded iterations depend on the buffers, nrhs, tol, maxit, the unroll
   // and the block split
@@ -1354,15 +1353,14 @@ hpcg_status hpcg_solve_block(hpcg_handle h, const float* d_B, double* d_X, int32
   __atomic_store_n(hflag, 0, __ATOMIC_RELEASE);
   hipLaunchKernelGGL(k_bs_reset, dim3(1), dim3(64), 0, h->stream, ctr, dflag);
   hipLaunchKernelGGL(k_bs_init, rows_grid, dim3(BS_NT), 0, h->stream, d_B, R, d_X, part, nrhs);
-  hipLaunchKernelGGL(k_bs_scalars<BS_INIT>, sc_grid, dim3(64 * BS_SC_COLS), 0, h->stream, cs, part, G.B, nrhs, rblocks, tol, maxit,
-                     (const double*)nullptr, 0);
+  hipLaunchKernelGGL(k_bs_scalars<BS_INIT>, sc_grid, dim3(BS_SC_C * BS_SC_G), 0, h->stream, cs, part, G.B, nrhs, rblocks);
   hpcg_status s = launch_block_apply(h, nrhs, R, Z, reinterpret_cast<float*>(wk + L.scratchQ),
                                      reinterpret_cast<float*>(wk + L.scratchH), h->stream);
   if (s != HPCG_OK) return s;
   hipLaunchKernelGGL(k_bs_dot, rows_grid, dim3(BS_NT), 0, h->stream, R, Z, part, nrhs);
-  hipLaunchKernelGGL(k_bs_scalars<BS_RZ0>, sc_grid, dim3(64 * BS_SC_COLS), 0, h->stream, cs, part, G.B, nrhs, rblocks, tol, maxit,
-                     (const double*)nullptr, 0);
-  hipLaunchKernelGGL(k_bs_direction, rows_grid, dim3(BS_NT), 0, h->stream, cs, Z, P, d_X, nrhs, rblocks);
+  hipLaunchKernelGGL(k_bs_scalars<BS_RZ0>, sc_grid, dim3(BS_SC_C * BS_SC_G), 0, h->stream, cs, part, G.B, nrhs, rblocks);
+  const dim3 dir_grid((unsigned)(G.B * G.K), (unsigned)((nrhs + BS_DIR_COLS - 1) / BS_DIR_COLS));
+  hipLaunchKernelGGL(k_bs_direction<false>, dir_grid, dim3(BS_DIR_NT), 0, h->stream, cs, Z, P, d_X, nrhs, G.K, BsRrz{});
   s = check_launch(h, "block solve setup launch");
   if (s != HPCG_OK) return s;
 

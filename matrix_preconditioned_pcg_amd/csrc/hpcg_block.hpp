@@ -29,7 +29,7 @@
 // and (3) its r.z partials (BlockUpd, BlockDot), so that neither needs a pass
 // of its own over the block.
 #pragma once
-#include "hpcg_device.hpp"
+#include "hpcg_colstate.hpp"
 
 namespace hpcg {
 
@@ -126,13 +126,14 @@ __device__ __forceinline__ size_t q_index(const BlockGeom& G, int s, int l, int 
 }
 
 // The block solve's residual update, taken by the leaf stage as it loads R
-// (UPD): R <- R - alpha_c (A P) column by column, in fp64 and rounded to fp32
-// once, a column whose alpha is 0 keeping its R; the new R is written back and
-// the apply runs on it, and the workgroup leaves its (system, leaf, column)
-// partials of the new R . R.
+// (UPD): first the PQ step of the workgroup's columns (hpcg_colstate.hpp) from
+// the p.q partials, then R <- R - alpha_c (A P) column by column, in fp64 and
+// rounded to fp32 once, a column whose alpha is 0 keeping its R; the new R is
+// written back and the apply runs on it, and the workgroup leaves its (system,
+// leaf, column) partials of the new R . R.
 struct BlockUpd {
-  const double* alpha;   // alpha of (system s, column c) at alpha[(s nrhs + c) stride]
-  int stride;
+  ColState* cs;          // [B][nrhs]; leaf 0's workgroups store the PQ step
+  const double* pq;      // [B][K][nrhs] partials of P . A P
   const float* AP;       // A P, node-major like R
   float* R;              // where the new R goes (the buffer R is read from)
   double* rr;            // [B][K][nrhs] partials of the new R . R
@@ -254,6 +255,8 @@ __global__ __launch_bounds__(BNT, 2) void k_block_restrict(BlockGeom G, BlockFac
   __shared__ int eR[BW];                                                    // exponent per column
   __shared__ float cmax[BNT];                                               // per (row group, column)
   __shared__ double red[UPD ? NWAVE * BW : 1];
+  __shared__ double pq_red[UPD ? BNT : 1];                                  // p.q group sums
+  __shared__ double alpha_s[UPD ? BW : 1];
   int role = 0;
   const BItem it = SPLIT ? bitem2(G, role) : bitem(G);
   const bool leaf_role = !SPLIT || role == 0;      // leaf stage, gate, write-back
@@ -313,6 +316,19 @@ __global__ __launch_bounds__(BNT, 2) void k_block_restrict(BlockGeom G, BlockFac
       if (par < LEV) load_slot(0, par);
     }
   };
+  // UPD: the column's state as the PQ step reads it, loaded before anything else
+  constexpr int GP = BNT / BW;               // threads per column
+  const int pcol = tid % BW, gp = tid / BW;
+  double rz_col = 0.0;
+  int st_col = 0, it_col = 0;
+  if constexpr (UPD) {
+    if (gp == 0) {
+      const ColState* cp = up.cs + (size_t)it.s * G.nrhs + c0 + pcol;
+      rz_col = cp->rz;
+      st_col = cp->status;
+      it_col = cp->iters;
+    }
+  }
   // R tile: 128 rows x 4 BW bytes, straight into LDS
   dma_to_lds(Rs, LEAF * BW / 4, [&](int c) {
     return R + (size_t)(it.leaf0 + c / (BW / 4)) * G.nrhs + c0 + 4 * (c % (BW / 4));
@@ -324,13 +340,42 @@ __global__ __launch_bounds__(BNT, 2) void k_block_restrict(BlockGeom G, BlockFac
   mf4 ap[UPD ? CH : 1];
   if constexpr (UPD) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) al[v] = up.alpha[((size_t)it.s * G.nrhs + cc + v) * up.stride];
-#pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int row = (tid + BNT * i) / C4;
       ap[i] = *reinterpret_cast<const mf4*>(up.AP + (size_t)(it.leaf0 + row) * G.nrhs + cc);
     }
   }
+  // UPD: the PQ step of the tile's columns while the tile is in flight: thread
+  // (gp, col) adds its partials in leaf order, thread (0, col) the GP group
+  // sums in order
+  auto take_alpha = [&]() {
+    if constexpr (UPD) {
+      const int col = pcol;
+      const size_t idx = (size_t)it.s * G.nrhs + c0 + col;
+      pq_red[tid] = bs_strided_sum(up.pq + (size_t)it.s * G.K * G.nrhs + c0 + col, G.K, G.nrhs, gp, GP);
+      __syncthreads();
+      if (gp == 0) {
+        double pq = pq_red[col];
+#pragma unroll
+        for (int k = 1; k < GP; ++k) pq += pq_red[k * BW + col];
+        ColState st;
+        st.rz = rz_col;
+        st.status = st_col;
+        st.iters = it_col;
+        bs_step_pq(st, pq);
+        alpha_s[col] = st.alpha;
+        if (it.k == 0 && leaf_role) {
+          up.cs[idx].alpha = st.alpha;
+          up.cs[idx].rz_prev = st.rz_prev;
+          up.cs[idx].iters = st.iters;
+          up.cs[idx].status_pq = st.status_pq;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int v = 0; v < 4; ++v) al[v] = alpha_s[4 * (tid % C4) + v];
+    }
+  };
   // every load so far has landed; the UPD update of the R tile, the columns'
   // exponents and the R^T pairs
   auto wait_update = [&]() {
@@ -472,12 +517,14 @@ __global__ __launch_bounds__(BNT, 2) void k_block_restrict(BlockGeom G, BlockFac
   };
   if (SPLIT && role == 1) {        // the restriction alone
     load_restr();
+    take_alpha();
     wait_update();
     restriction();
     return;
   }
   load_leaf();
   if constexpr (!SPLIT) load_restr();
+  take_alpha();
   wait_update();
   leaf_stage();
   if constexpr (!SPLIT) restriction();
@@ -489,39 +536,46 @@ __global__ __launch_bounds__(BNT, 2) void k_block_restrict(BlockGeom G, BlockFac
   }
 }
 
-// (2) half sums: H_l[h] = sum of Q_l[k] over the 2^l leaves k of half h, summed
-// in leaf order.  Same layout as Q (half index in place of the leaf index).
-// Grid: x over a system's (level, half, element) triples, y over the systems
-// (a stride of gridDim.y past 65535 systems); the index arithmetic is 32-bit
-// (a system's triples are far fewer than 2^31).
-__global__ void k_block_halfsum(BlockGeom G, const float* __restrict__ Q, float* __restrict__ H) {
-  constexpr int HB = 8;                            // loads in flight per batch
+// (2) half sums: H_l[h] = sum of Q_l[k] over the 2^l leaves k of half h.  Same
+// layout as Q (half index in place of the leaf index).  A thread adds a run of
+// at most eight consecutive leaves (its loads all in flight at once, added in
+// leaf order); the P = 2^l / 8 runs of a half's element sit in one wave, 64 / P
+// lanes apart, and are combined pairwise in leaf order, adjacent runs first
+// (a fixed tree: one order, every call).  A level's threads come in whole
+// waves (RANK * nrhs is a multiple of 64).
+// Grid: x over a system's (level, half, element, run) quadruples, y over the
+// systems (a stride of gridDim.y past 65535 systems); the index arithmetic is
+// 32-bit (a system's quadruples are far fewer than 2^31).
+constexpr int HS_RUN = 8;
+__host__ __device__ inline unsigned halfsum_runs(int l) { return (1 << l) > HS_RUN ? (1u << l) / HS_RUN : 1u; }
+__global__ __launch_bounds__(256) void k_block_halfsum(BlockGeom G, const float* __restrict__ Q,
+                                                       float* __restrict__ H) {
   const unsigned per = (unsigned)RANK * (unsigned)G.nrhs;   // elements per (level, leaf)
   unsigned rem = blockIdx.x * blockDim.x + threadIdx.x;
   int l = 0;
-  unsigned level_elems = (unsigned)G.K * per;      // l = 0
-  while (l < G.levels && rem >= level_elems) {
-    rem -= level_elems;
+  unsigned level_threads = (unsigned)G.K * per;    // l = 0: one run per element
+  while (l < G.levels && rem >= level_threads) {
+    rem -= level_threads;
     ++l;
-    level_elems = (unsigned)(G.K >> l) * per;
+    level_threads = (unsigned)(G.K >> l) * per * halfsum_runs(l);
   }
-  if (l >= G.levels) return;
-  const unsigned h = rem / per, e = rem - h * per;
+  if (l >= G.levels) return;                       // whole waves
   const int span = 1 << l;
+  const unsigned P = halfsum_runs(l), gap = 64u / P, lane = threadIdx.x & 63u;
+  const int n = span / (int)P;                     // leaves of a run, at most HS_RUN
+  const unsigned idx = (rem / 64u) * gap + lane % gap, run = lane / gap;
+  const unsigned h = idx / per, e = idx - h * per;
   for (int s = (int)blockIdx.y; s < G.B; s += (int)gridDim.y) {
-    const float* src = Q + q_index(G, s, l, (int)h * span, 0) + e;
-    // the sum keeps leaf order
-    float a = 0.f;
-    int i = 0;
-    for (; i + HB <= span; i += HB) {
-      float v[HB];
+    const float* src = Q + q_index(G, s, l, (int)h * span + (int)run * n, 0) + e;
+    float v[HS_RUN];
 #pragma unroll
-      for (int u = 0; u < HB; ++u) v[u] = src[(size_t)(i + u) * per];
+    for (int u = 0; u < HS_RUN; ++u) v[u] = u < n ? src[(size_t)u * per] : 0.f;
+    float a = v[0];
 #pragma unroll
-      for (int u = 0; u < HB; ++u) a += v[u];
-    }
-    for (; i < span; ++i) a += src[(size_t)i * per];
-    H[q_index(G, s, l, (int)h, 0) + e] = a;
+    for (int u = 1; u < HS_RUN; ++u)
+      if (u < n) a += v[u];
+    for (unsigned o = gap; o < 64u; o <<= 1) a += __shfl_xor(a, (int)o);
+    if (run == 0) H[q_index(G, s, l, (int)h, 0) + e] = a;
   }
 }
 

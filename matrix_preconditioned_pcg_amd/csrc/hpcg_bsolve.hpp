@@ -16,23 +16,24 @@
 // The test is taken with beta, after Z = M R: a column that has just
 // converged costs one unused column of the block apply, and its count and x
 // are those of the textbook loop, with one launch fewer per iteration.
-// Six launches per iteration (eight with the block apply's three): the SpMV
-// leaves the p.q partials; the apply's leaf stage takes R -= alpha Q and
-// leaves the r.r partials, its prolongation the r.z partials; X += alpha P
-// waits for the direction step, which reads P anyway.
+// Five launches per iteration: the SpMV leaves the p.q partials; the apply's
+// leaf stage takes the PQ step (alpha) and R -= alpha Q and leaves the r.r
+// partials; the halfsums; the prolongation leaves the r.z partials; the
+// direction step takes the RRZ step (the test and beta), X += alpha P (it
+// reads P anyway) and P = Z + beta P.  The steps sit in the kernels that use
+// their results (hpcg_colstate.hpp), so no launch is spent on a few scalars.
 // R, Z, P, Q are fp32 (the block apply's arithmetic), X and every scalar fp64.
 // A finished column gets alpha = beta = 0 from then on, so its X and R stay
 // as they were while the others continue.
 //
 // Dot products: every product is taken in fp64 and every partial is a sum in
-// a fixed order: p.q per 32-row block (the SpMV's workgroups, which own 32 rows
-// and 64 columns), r.r and r.z per leaf (the block apply's workgroups), and
-// the setup's b.b and r.z per 32-row block (k_bs_init, k_bs_dot).  The
-// partials of a system are added by one wave per (system, column) in a fixed
-// order (lane-strided, then a fixed butterfly): every sum has one order, so a
-// solve is bitwise reproducible.
+// a fixed order: p.q, r.r and r.z per leaf (the SpMV's and the block apply's
+// workgroups), and the setup's b.b and r.z per 32-row block (k_bs_init,
+// k_bs_dot).  The partials of a system are added in a fixed order (interleaved
+// groups, each in order, then the groups in order): every sum has one order,
+// so a solve is bitwise reproducible.
 #pragma once
-#include "hpcg_device.hpp"
+#include "hpcg_colstate.hpp"
 
 namespace hpcg {
 
@@ -40,18 +41,7 @@ constexpr int BS_ROWS = 32;     // rows per workgroup (n is a multiple of 128)
 constexpr int BS_COLS = 64;     // columns per workgroup
 constexpr int BS_NT = 256;      // threads per workgroup
 
-struct ColState {
-  double bnorm;    // ||B_j||
-  double rz;       // R_j . Z_j of the last completed iteration
-  double alpha;
-  double beta;
-  double relres;   // ||R_j|| / ||B_j|| after the last update
-  int status;      // ST_*
-  int iters;
-  int pad[2];
-};
-
-enum : int { BS_INIT = 0, BS_RZ0 = 1, BS_PQ = 2, BS_RRZ = 3 };
+enum : int { BS_INIT = 0, BS_RZ0 = 1 };
 
 // Workgroup (leaf rb, column tile) -> thread's column c, row group rg.
 __device__ __forceinline__ double bs_rowgroup_reduce(double acc, double* red) {
@@ -104,17 +94,18 @@ __global__ __launch_bounds__(BS_NT) void k_bs_init(const float* __restrict__ Bm,
   if (rg == 0 && c < nrhs) part[rb * nrhs + c] = s;
 }
 
-// Q = A P and the block's partials of P . Q (the layout of k_bs_dot).  A
-// workgroup of 512 takes a 32-row block and a 64-column tile: thread (rr, g)
-// row rr and columns 4g..4g+3, the row's entries four at a time, their indices
-// and then their P rows all in flight together (two rows per thread, in 256,
-// were slower).  A row's sum is taken in fp64 and rounded to fp32 once:
-// R -= alpha Q moves R away from B - A X by alpha (A P - Q) every step, and a
-// sum of the stencil's cancelling terms rounded at every step moved it by
-// several times tol on long, stiff grids.  The partial of a column adds the
-// rows' products (with the stored, rounded Q) over the four row groups of a
-// wave (fixed butterfly) and then the eight waves in order.
-constexpr int BS_SPMV_NT = 512;
+// Q = A P and the leaf's partials of P . Q, part[s][k][c].  A workgroup of
+// 1024 takes a leaf (128 rows) and a 32-column tile: thread (rr, g) row rr and
+// columns 4g..4g+3 (a row's 32 columns are one 128-byte line), the row's
+// entries four at a time, their indices and then their P rows all in flight
+// together.  A row's sum is taken in fp64 and rounded to fp32 once: R -= alpha
+// Q moves R away from B - A X by alpha (A P - Q) every step, and a sum of the
+// stencil's cancelling terms rounded at every step moved it by several times
+// tol on long, stiff grids.  The partial of a column adds the rows' products
+// (with the stored, rounded Q) over the eight rows of a wave (fixed butterfly)
+// and then the sixteen waves in order.
+constexpr int BS_SPMV_NT = 1024;
+constexpr int BS_SPMV_COLS = 32;
 __global__ __launch_bounds__(BS_SPMV_NT) void k_bs_spmv_dot(const int* __restrict__ row_ptr,
                                                             const int* __restrict__ col,
                                                             const float* __restrict__ val,
@@ -122,14 +113,15 @@ __global__ __launch_bounds__(BS_SPMV_NT) void k_bs_spmv_dot(const int* __restric
                                                             double* __restrict__ part, int nrhs) {
   typedef float f4 __attribute__((ext_vector_type(4)));
   constexpr int NWV = BS_SPMV_NT / 64;
-  __shared__ double red[NWV * BS_COLS];
+  constexpr int CG = BS_SPMV_COLS / 4;       // column groups of a row (8)
+  __shared__ double red[NWV * BS_SPMV_COLS];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int g = tid & 15, rr = tid >> 4;
-  const int c4 = blockIdx.y * BS_COLS + 4 * g;
-  const size_t rb = blockIdx.x;
+  const int g = tid % CG, rr = tid / CG;
+  const int c4 = blockIdx.y * BS_SPMV_COLS + 4 * g;
+  const size_t leaf = blockIdx.x;            // over the B K leaves of the batch
   double d[4] = {0.0, 0.0, 0.0, 0.0};
   if (c4 < nrhs) {
-    const int row = (int)(rb * BS_ROWS) + rr;
+    const int row = (int)(leaf * LEAF) + rr;
     const int e0 = row_ptr[row], e1 = row_ptr[row + 1];
     const f4 pv = *reinterpret_cast<const f4*>(P + (size_t)row * nrhs + c4);
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
@@ -160,110 +152,145 @@ __global__ __launch_bounds__(BS_SPMV_NT) void k_bs_spmv_dot(const int* __restric
   }
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    d[t] += __shfl_xor(d[t], 16);
-    d[t] += __shfl_xor(d[t], 32);
-  }
-  if (lane < 16) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) red[w * BS_COLS + 4 * lane + t] = d[t];
+    for (int o = CG; o < 64; o <<= 1) d[t] += __shfl_xor(d[t], o);
+  }
+  if (lane < CG) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) red[w * BS_SPMV_COLS + 4 * lane + t] = d[t];
   }
   __syncthreads();
-  const int c = blockIdx.y * BS_COLS + tid;
-  if (tid < BS_COLS && c < nrhs) {
+  const int c = blockIdx.y * BS_SPMV_COLS + tid;
+  if (tid < BS_SPMV_COLS && c < nrhs) {
     double sum = red[tid];
 #pragma unroll
-    for (int k = 1; k < NWV; ++k) sum += red[k * BS_COLS + tid];
-    part[rb * nrhs + c] = sum;
+    for (int k = 1; k < NWV; ++k) sum += red[k * BS_SPMV_COLS + tid];
+    part[leaf * nrhs + c] = sum;
   }
 }
 
 // X += alpha P, then P = Z + beta P (alpha and beta per column of the row's
 // system).  alpha = 0 (the setup, and every step of a finished column) leaves X
 // as it is; beta = 0 (the first step, and every step of a finished column)
-// takes P = Z without reading P, which holds no value before the first step.
-__global__ __launch_bounds__(BS_NT) void k_bs_direction(const ColState* __restrict__ cs, const float* __restrict__ Z,
-                                                        float* __restrict__ P, double* __restrict__ X, int nrhs,
-                                                        int blocks_per_system) {
-  const int tid = threadIdx.x, rg = tid / BS_COLS;
-  const int c = blockIdx.y * BS_COLS + (tid & (BS_COLS - 1));
-  const size_t rb = blockIdx.x;
-  const int s = (int)(rb / blocks_per_system);
-  if (c >= nrhs) return;
-  const double alpha = cs[(size_t)s * nrhs + c].alpha;
-  const double beta = cs[(size_t)s * nrhs + c].beta;
+// takes P = Z without using P, which holds no value before the first step.
+// A workgroup of 512 takes a leaf (128 rows) and a 64-column tile: thread
+// (rg, c) rows rg, rg + 8, ... of column c.  RRZ: the workgroup first takes the
+// RRZ step of its columns (hpcg_colstate.hpp) from the r.z and r.r partials,
+// thread (rg, c) adding every eighth partial in order and then the eight
+// groups in order, its rows' P, Z (and X) loads already in flight and its X
+// stores (which need alpha only) issued; the workgroups of leaf 0 store the
+// state.  Without RRZ (the setup) beta is the stored one.
+struct BsRrz {
+  const double* rz;   // [B][rz_blocks][nrhs] partials of R . Z
+  int rz_blocks;
+  const double* rr;   // [B][rr_blocks][nrhs] partials of R . R
+  int rr_blocks;
+  double tol;
+  int maxit;
+};
+constexpr int BS_DIR_NT = 512;
+constexpr int BS_DIR_COLS = 64;
+template <bool RRZ>
+__global__ __launch_bounds__(BS_DIR_NT) void k_bs_direction(ColState* __restrict__ cs, const float* __restrict__ Z,
+                                                            float* __restrict__ P, double* __restrict__ X, int nrhs,
+                                                            int K, BsRrz st) {
+  constexpr int NG = BS_DIR_NT / BS_DIR_COLS;   // row groups (8)
+  constexpr int RPT = LEAF / NG;                // rows per thread (16)
+  __shared__ double red[2 * NG * BS_DIR_COLS];
+  __shared__ double beta_s[BS_DIR_COLS];
+  const int tid = threadIdx.x, cl = tid % BS_DIR_COLS, rg = tid / BS_DIR_COLS;
+  const int c = blockIdx.y * BS_DIR_COLS + cl;
+  const size_t leaf = blockIdx.x;            // over the B K leaves of the batch
+  const int s = (int)(leaf / K);
+  const bool live = c < nrhs;
+  const size_t idx = (size_t)s * nrhs + (live ? c : 0);
+  const double alpha = live ? cs[idx].alpha : 0.0;
+  float pv[RPT], zv[RPT];
+  double xv[RPT];
+  if (live) {
 #pragma unroll
-  for (int r = rg; r < BS_ROWS; r += BS_NT / BS_COLS) {
-    const size_t i = (rb * BS_ROWS + r) * nrhs + c;
-    if (alpha != 0.0) {
-      const float p = P[i];
-      X[i] = fma(alpha, (double)p, X[i]);
-      P[i] = beta == 0.0 ? Z[i] : (float)((double)Z[i] + beta * (double)p);
-    } else {
-      P[i] = beta == 0.0 ? Z[i] : (float)((double)Z[i] + beta * (double)P[i]);
+    for (int u = 0; u < RPT; ++u) {
+      const size_t i = (leaf * LEAF + rg + NG * u) * nrhs + c;
+      pv[u] = P[i];
+      zv[u] = Z[i];
+      xv[u] = alpha != 0.0 ? X[i] : 0.0;
     }
+    if (alpha != 0.0) {
+#pragma unroll
+      for (int u = 0; u < RPT; ++u) X[(leaf * LEAF + rg + NG * u) * nrhs + c] = fma(alpha, (double)pv[u], xv[u]);
+    }
+  }
+  double beta;
+  if constexpr (RRZ) {
+    red[tid] = live ? bs_strided_sum(st.rz + (size_t)s * st.rz_blocks * nrhs + c, st.rz_blocks, nrhs, rg, NG) : 0.0;
+    red[NG * BS_DIR_COLS + tid] =
+        live ? bs_strided_sum(st.rr + (size_t)s * st.rr_blocks * nrhs + c, st.rr_blocks, nrhs, rg, NG) : 0.0;
+    __syncthreads();
+    if (rg == 0 && live) {
+      double rz = red[cl], rr = red[NG * BS_DIR_COLS + cl];
+#pragma unroll
+      for (int k = 1; k < NG; ++k) {
+        rz += red[k * BS_DIR_COLS + cl];
+        rr += red[(NG + k) * BS_DIR_COLS + cl];
+      }
+      ColState cst = cs[idx];
+      bs_step_rrz(cst, rz, rr, st.tol, st.maxit);
+      beta_s[cl] = cst.beta;
+      if (leaf % K == 0) {
+        cs[idx].status = cst.status;
+        cs[idx].rz = cst.rz;
+        cs[idx].beta = cst.beta;
+        cs[idx].relres = cst.relres;
+      }
+    }
+    __syncthreads();
+    beta = live ? beta_s[cl] : 0.0;
+  } else {
+    beta = live ? cs[idx].beta : 0.0;
+  }
+  if (!live) return;
+#pragma unroll
+  for (int u = 0; u < RPT; ++u) {
+    const size_t i = (leaf * LEAF + rg + NG * u) * nrhs + c;
+    P[i] = beta == 0.0 ? zv[u] : (float)((double)zv[u] + beta * (double)pv[u]);
   }
 }
 
-// One wave per (system, column): lane l adds the system's per-block partials
-// l, l + 64, ... and the lanes are combined by the fixed butterfly of
-// wave_sum (one order, every call); lane 0 takes the step the mode names.
-constexpr int BS_SC_COLS = 4;   // columns (waves) per workgroup
-// RRZ takes the convergence test on part2 (r.r) and then beta on part (r.z).
-// part holds blocks_per_system partials per (system, column), part2 (RRZ only)
-// blocks2 of them.
+// The setup's steps (INIT: ||B_j|| and the state; RZ0: the first r.z) from
+// per-block partials.  A workgroup per (system, 16-column tile): thread (g, c)
+// adds the partials g, g + 16, ... of its column in order (the 16 columns of a
+// partial row are one 128-byte line), then thread (0, c) adds the 16 group
+// sums in order.  Grid: systems * nrhs / 16 workgroups (nrhs a multiple of 16).
+constexpr int BS_SC_C = 16;     // columns per workgroup
+constexpr int BS_SC_G = 16;     // partial groups per column
 template <int MODE>
-__global__ __launch_bounds__(64 * BS_SC_COLS) void k_bs_scalars(ColState* __restrict__ cs,
-                                                                const double* __restrict__ part, int systems,
-                                                                int nrhs, int blocks_per_system, double tol,
-                                                                int maxit, const double* __restrict__ part2,
-                                                                int blocks2) {
-  const int idx = blockIdx.x * BS_SC_COLS + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (idx >= systems * nrhs) return;     // whole waves leave together
-  const int s = idx / nrhs, c = idx - s * nrhs;
-  double v = 0.0, v2 = 0.0;
-  for (int k = lane; k < blocks_per_system; k += 64) v += part[((size_t)s * blocks_per_system + k) * nrhs + c];
-  if constexpr (MODE == BS_RRZ) {
-    for (int k = lane; k < blocks2; k += 64) v2 += part2[((size_t)s * blocks2 + k) * nrhs + c];
-  }
-  const double sum = wave_sum(v);
-  double sum2 = 0.0;
-  if constexpr (MODE == BS_RRZ) sum2 = wave_sum(v2);
-  if (lane != 0) return;
+__global__ __launch_bounds__(BS_SC_C * BS_SC_G) void k_bs_scalars(ColState* __restrict__ cs,
+                                                                  const double* __restrict__ part, int systems,
+                                                                  int nrhs, int blocks_per_system) {
+  __shared__ double red[BS_SC_G * BS_SC_C];
+  const int tid = threadIdx.x, cl = tid % BS_SC_C, g = tid / BS_SC_C;
+  const int tiles = nrhs / BS_SC_C;
+  const int s = (int)blockIdx.x / tiles, c = ((int)blockIdx.x - s * tiles) * BS_SC_C + cl;
+  if (s >= systems) return;        // whole workgroups leave together
+  red[tid] = bs_strided_sum(part + (size_t)s * blocks_per_system * nrhs + c, blocks_per_system, nrhs, g, BS_SC_G);
+  __syncthreads();
+  if (g != 0) return;
+  double sum = red[cl];
+#pragma unroll
+  for (int k = 1; k < BS_SC_G; ++k) sum += red[k * BS_SC_C + cl];
+  const size_t idx = (size_t)s * nrhs + c;
   ColState st = cs[idx];
   if constexpr (MODE == BS_INIT) {
     st.bnorm = sqrt(sum);
-    st.rz = st.alpha = st.beta = 0.0;
+    st.rz = st.rz_prev = st.alpha = st.beta = 0.0;
     st.iters = 0;
-    st.status = sum == 0.0 ? ST_CONVERGED : ST_RUNNING;
+    st.status = st.status_pq = sum == 0.0 ? ST_CONVERGED : ST_RUNNING;
     st.relres = sum == 0.0 ? 0.0 : 1.0;
-  } else if constexpr (MODE == BS_RZ0) {
+  } else {   // BS_RZ0
     st.beta = 0.0;
     if (st.status == ST_RUNNING) {
       if (!(sum > 0.0) || !isfinite(sum)) st.status = ST_BREAKDOWN;
       else st.rz = sum;
-    }
-  } else if constexpr (MODE == BS_PQ) {
-    st.alpha = 0.0;
-    if (st.status == ST_RUNNING) {
-      st.iters += 1;
-      if (!(sum > 0.0) || !isfinite(sum)) st.status = ST_BREAKDOWN;
-      else st.alpha = st.rz / sum;
-    }
-  } else {   // BS_RRZ
-    if (st.status == ST_RUNNING) {
-      st.relres = sqrt(sum2) / st.bnorm;
-      if (st.relres <= tol) st.status = ST_CONVERGED;
-      else if (st.iters >= maxit) st.status = ST_NOT_CONVERGED;
-    }
-    st.beta = 0.0;
-    if (st.status == ST_RUNNING) {
-      if (!(sum > 0.0) || !isfinite(sum)) {
-        st.status = ST_BREAKDOWN;
-      } else {
-        st.beta = sum / st.rz;
-        st.rz = sum;
-      }
     }
   }
   cs[idx] = st;
