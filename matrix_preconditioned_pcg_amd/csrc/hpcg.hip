@@ -1128,18 +1128,19 @@ hpcg_status launch_block_apply(hpcg_ctx* h, int32_t nrhs, const float* d_R, floa
     default: return fail(h, HPCG_ERR_SHAPE, "levels out of range");
   }
   if (h->G.levels > 0) {
-    size_t sys_total = 0;
-    for (int l = 0; l < h->G.levels; ++l) sys_total += (size_t)(h->G.K >> l) * RANK * nrhs * halfsum_runs(l);
-    hipLaunchKernelGGL(k_block_halfsum, dim3((unsigned)((sys_total + 255) / 256), (unsigned)std::min(h->G.B, 65535)),
-                       dim3(256), 0, stream, bg, Q, H);
+    size_t sys_total = 0;   // level 0 needs no half sums
+    for (int l = 1; l < h->G.levels; ++l) sys_total += (size_t)(h->G.K >> l) * RANK * nrhs * halfsum_runs(l);
+    if (sys_total > 0)
+      hipLaunchKernelGGL(k_block_halfsum, dim3((unsigned)((sys_total + 255) / 256), (unsigned)std::min(h->G.B, 65535)),
+                         dim3(256), 0, stream, bg, Q, H);
 #define HPCG_BLOCK_PROLONG_N(LV, N)                                                                     \
   do {                                                                                                  \
     if (dot)                                                                                            \
-      hipLaunchKernelGGL((k_block_prolong<LV, N, true>), dim3(grid), dim3(BNT), 0, stream, bg, f16, H,    \
+      hipLaunchKernelGGL((k_block_prolong<LV, N, true>), dim3(grid), dim3(BNT), 0, stream, bg, f16, Q, H, \
                          d_Y, dt);                                                                      \
     else                                                                                                \
-      hipLaunchKernelGGL((k_block_prolong<LV, N, false>), dim3(grid), dim3(BNT), 0, stream, bg, f16, H,   \
-                         d_Y, dt);                                                                      \
+      hipLaunchKernelGGL((k_block_prolong<LV, N, false>), dim3(grid), dim3(BNT), 0, stream, bg, f16, Q,   \
+                         H, d_Y, dt);                                                                   \
   } while (0)
     switch (h->G.levels) {
 #define HPCG_BLOCK_PROLONG(LV)                                                                          \

@@ -536,12 +536,13 @@ __global__ __launch_bounds__(BNT, 2) void k_block_restrict(BlockGeom G, BlockFac
   }
 }
 
-// (2) half sums: H_l[h] = sum of Q_l[k] over the 2^l leaves k of half h.  Same
-// layout as Q (half index in place of the leaf index).  A thread adds a run of
-// at most eight consecutive leaves (its loads all in flight at once, added in
-// leaf order); the P = 2^l / 8 runs of a half's element sit in one wave, 64 / P
-// lanes apart, and are combined pairwise in leaf order, adjacent runs first
-// (a fixed tree: one order, every call).  A level's threads come in whole
+// (2) half sums: H_l[h] = sum of Q_l[k] over the 2^l leaves k of half h, for
+// levels 1 and up (a level-0 half is one leaf: the prolongation reads its Q_0
+// itself).  Same layout as Q (half index in place of the leaf index).  A
+// thread adds a run of at most eight consecutive leaves (its loads all in
+// flight at once, added in leaf order); the P = 2^l / 8 runs of a half's
+// element sit in one wave, 64 / P lanes apart, and are combined pairwise in
+// leaf order, adjacent runs first (a fixed tree: one order, every call).  A level's threads come in whole
 // waves (RANK * nrhs is a multiple of 64).
 // Grid: x over a system's (level, half, element, run) quadruples, y over the
 // systems (a stride of gridDim.y past 65535 systems); the index arithmetic is
@@ -552,8 +553,8 @@ __global__ __launch_bounds__(256) void k_block_halfsum(BlockGeom G, const float*
                                                        float* __restrict__ H) {
   const unsigned per = (unsigned)RANK * (unsigned)G.nrhs;   // elements per (level, leaf)
   unsigned rem = blockIdx.x * blockDim.x + threadIdx.x;
-  int l = 0;
-  unsigned level_threads = (unsigned)G.K * per;    // l = 0: one run per element
+  int l = 1;
+  unsigned level_threads = (unsigned)(G.K >> 1) * per;   // l = 1: one run per element
   while (l < G.levels && rem >= level_threads) {
     rem -= level_threads;
     ++l;
@@ -588,8 +589,8 @@ __global__ __launch_bounds__(256) void k_block_halfsum(BlockGeom G, const float*
 constexpr int PH_STRIDE = 40;   // half-sum pair rows in LDS, halfs (80 B)
 template <int LEV, int NCT, bool DOT = false>
 __global__ __launch_bounds__(BNT) void k_block_prolong(BlockGeom G, BlockFactors16 fw,
-                                                       const float* __restrict__ H, float* __restrict__ Y,
-                                                       BlockDot dt) {
+                                                       const float* __restrict__ Q, const float* __restrict__ H,
+                                                       float* __restrict__ Y, BlockDot dt) {
   constexpr int BW = BNC * NCT;
   constexpr int NL = LEV > 0 ? LEV : 1;
   constexpr int NS = (NL + 1) / 2;                                             // levels of a stage, at most
@@ -626,7 +627,8 @@ __global__ __launch_bounds__(BNT) void k_block_prolong(BlockGeom G, BlockFactors
       const int e = tid + u * BNT;
       const int l = l0 + e / (RANK * BW), rem = e % (RANK * BW);
       const int row = rem / BW, col = rem - row * BW;
-      hv[u] = H[q_index(G, it.s, l, (it.k >> l) ^ 1, row) + c0 + col];
+      // level 0's halves are single leaves: the partner's restriction itself
+      hv[u] = (l == 0 ? Q : H)[q_index(G, it.s, l, (it.k >> l) ^ 1, row) + c0 + col];
     }
   };
   // levels [l0, l0 + nl): the half sums into LDS as they are laid out (fp32;
