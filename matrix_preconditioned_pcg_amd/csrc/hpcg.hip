@@ -460,7 +460,7 @@ hpcg_status run_resident(hpcg_ctx* h, bool& ran) {
   // CSR rows, the partner stages of W^T r and W^T q, z and p by leaf-local
   // column (own rows, then the halo), the halo's column list
   const size_t dyn = ((size_t)h->max_leaf_nnz * 8 + (LEAF + 1) * 4 + 15) / 16 * 16 +
-                     2 * (size_t)std::max(G.K - 1, 1) * RANK * sizeof(T) +
+                     2 * (size_t)partner_rows(G) * RANK * sizeof(T) +
                      2 * ((size_t)LEAF + h->max_halo) * sizeof(T) + (size_t)h->max_halo * 4;
   if (dyn + sizeof(RSmem<T>) > kMaxLds) return HPCG_OK;
   hpcg_status s = allow_lds(h, fn, dyn);
@@ -817,7 +817,7 @@ hpcg_status run_bridge_apply(hpcg_ctx* h, const float* d_r, float* d_y, bool& ra
   const Geom G = h->G;
   const int items = G.B * G.K;
   if (G.levels < 1 || !h->bridge_set || G.K > h->num_cu) return HPCG_OK;
-  const size_t dyn = ((size_t)std::max(G.K - 1, 1) * RANK + (size_t)G.levels * RANK * CSTRIDE) * sizeof(float);
+  const size_t dyn = ((size_t)partner_rows(G) * RANK + (size_t)G.levels * RANK * CSTRIDE) * sizeof(float);
   if (dyn + sizeof(RSmem<float>) > kMaxLds) return HPCG_OK;
   const bool split = h->split_apply && 4 * (int64_t)items <= h->num_cu;
   const void* fn = bridge_apply_kernel(G.levels, split);
@@ -855,7 +855,7 @@ hpcg_status run_fused_apply(hpcg_ctx* h, const float* d_r, float* d_y, bool& ran
   const float* ra = d_r;
   float* ya = d_y;
   void* args[] = {&Ga, &Ba, &ra, &ya};
-  const size_t dyn = (size_t)std::max(G.K - 1, 1) * RANK * sizeof(float);
+  const size_t dyn = (size_t)partner_rows(G) * RANK * sizeof(float);
   // two workgroups per leaf (diagonal / off-diagonal roles) while the batch
   // has at most a quarter as many leaves as the device has compute units and
   // every workgroup can be resident at once.  Measured: n = 1,024 / 4,096 /

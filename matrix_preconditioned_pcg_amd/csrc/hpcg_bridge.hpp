@@ -184,8 +184,8 @@ __global__ __launch_bounds__(NTR) void k_apply_bridge(Geom G, Bufs B, const floa
   static_assert(LEV >= 1, "the bridge apply needs tile levels");
   __shared__ RSmem<float> sm;
   extern __shared__ int4 bdyn4[];
-  float* stR = reinterpret_cast<float*>(bdyn4);                  // (K - 1) x R partner values
-  float* cores = stR + (size_t)(G.K > 1 ? G.K - 1 : 1) * RANK;  // LEV x R x CSTRIDE
+  float* stR = reinterpret_cast<float*>(bdyn4);                  // partner_rows x R partner values
+  float* cores = stR + (size_t)partner_rows(G) * RANK;             // LEV x R x CSTRIDE
   const int tid = threadIdx.x;
   const int item = item0 + (SPLIT ? (int)(blockIdx.x >> 1) : (int)blockIdx.x);
   const bool diag_role = SPLIT && (blockIdx.x & 1) == 0;

@@ -422,6 +422,13 @@ __device__ __forceinline__ int load_state(const SysState* st) {
   return v;
 }
 
+// Rows of R values that stage a leaf's partner-half restrictions: level l
+// (l < levels) at rows 2^l - 1 .. 2^(l+1) - 2, one per leaf of the partner
+// half; 2^levels - 1 in all (K - 1 for a full hierarchy), at least one.
+__host__ __device__ inline int partner_rows(const Geom& G) {
+  return G.levels > 0 ? (1 << G.levels) - 1 : 1;
+}
+
 // Dynamic-LDS bytes of the restriction and prolongation stages.
 __host__ __device__ inline int levels_of_slot(const Geom& G, int j) {
   return j < G.levels ? (G.levels - 1 - j) / G.bpl + 1 : 0;
@@ -432,7 +439,7 @@ __host__ __device__ inline size_t restrict_lds_bytes(const Geom& G) {
 template <typename T>
 __host__ __device__ inline size_t prolong_lds_bytes(const Geom& G) {
   const size_t factors = (size_t)4 * (size_t)G.levels * G.RB * RANK;
-  return factors + (size_t)(G.K - 1) * RANK * sizeof(T);
+  return factors + (size_t)partner_rows(G) * RANK * sizeof(T);
 }
 
 // ---------------------------------------------------------------------------

@@ -488,7 +488,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
   int* colL = reinterpret_cast<int*>(rdyn4);              // leaf-local columns (own, then halo)
   float* valL = reinterpret_cast<float*>(colL + max_leaf_nnz);
   int* rpL = reinterpret_cast<int*>(valL + max_leaf_nnz);
-  const int stage_rows = G.K > 1 ? G.K - 1 : 1;
+  const int stage_rows = partner_rows(G);
   T* stR = reinterpret_cast<T*>(rdyn4 + (2 * max_leaf_nnz + LEAF + 1 + 3) / 4);
   T* stQ = stR + (size_t)stage_rows * RANK;
   // z and p of the previous step by leaf-local column: own rows, then the halo

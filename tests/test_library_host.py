@@ -52,6 +52,15 @@ def test_workspace_bytes_rejects_bad_partitions(hp, kw):
     assert hp.hpcg_workspace_bytes(part, 100) == 0
 
 
+@pytest.mark.parametrize("n,levels", [(32768, 8), (65536, 8), (65536, 5), (1 << 20, 8), (1 << 20, 0)])
+def test_workspace_bytes_accepts_large_partitions(hp, n, levels):
+    # more leaves than the full eight levels cover (a partial hierarchy): the
+    # partner stages hold 2^levels - 1 rows, not one per leaf, so the
+    # partition fits a compute unit's LDS and is accepted
+    part = hp.hpcg_partition(n, 128, 32, levels, 1)
+    assert hp.hpcg_workspace_bytes(part, 7 * n) > n * (128 + 32 * levels) * 4
+
+
 def test_workspace_bytes_covers_the_buffers(hp):
     part = hp.partition(16384)
     nnz = 110592
