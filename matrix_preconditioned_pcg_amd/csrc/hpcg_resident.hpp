@@ -26,7 +26,8 @@
 //           convergence test on ||r_{it-1}||; beta; p = z + beta p;
 //           q = A p (CSR rows, z and p in LDS); publish W_l[k]^T q and the
 //           partial p.q; then U_k U_k^T q while those words travel
-//   BC(it): poll the partners' W^T q and the p.q partials; alpha;
+//   BC(it): poll the partners' W^T q (each thread adding its words per level
+//           as they land: nothing is staged) and the p.q partials; alpha;
 //           x += alpha p; r -= alpha q; z = U_k U_k^T r_new + sum_l W_l[k] P_l
 //           + g r_new with P_l = partner-half sum of (W^T r - alpha W^T q);
 //           at a refresh W^T r_new and U_k U_k^T r_new; publish z and the
@@ -222,22 +223,6 @@ __device__ __forceinline__ void leaf_apply(const Resident<T, LEV>& F, const T* v
   diag_times<T, LEV>(F, tmp, y);
 }
 
-// z = M r_new on the leaf's rows into sm.z, with the leaf stage already in
-// hand: U_k U_k^T r_new = sm.yr - alpha sm.yq.  Needs sm.r (= r_new) and the
-// staged partner restrictions of q (stQ) and of r (stR; with r_from_prev
-// their sums are the previous sm.P instead).
-template <typename T, int LEV>
-__device__ __forceinline__ void r_prolong_split(const Resident<T, LEV>& F, RSmem<T>& sm, const T* stR, const T* stQ,
-                                                double alpha, float gate, bool r_from_prev) {
-  const int tid = tid_of<kFresh<T, LEV>>();
-  if constexpr (LEV > 0) prolong_strips<T, LEV>(sm, stR, stQ, alpha, r_from_prev);
-  prolong_offdiag<T, LEV>(F, sm);
-  __syncthreads();
-  if (tid < LEAF)
-    sm.z[tid] = (T)((double)sm.yr[tid] - alpha * (double)sm.yq[tid]) + sm.yoff[tid] + (T)gate * sm.r[tid];
-  __syncthreads();
-}
-
 // z = M r_new on the leaf's rows into sm.z.  Needs sm.t (= U_k^T r_new), sm.r
 // (= r_new) and the staged partner restrictions of r (stR) and q (stQ):
 // P_l = sum(stR) - alpha sum(stQ).  With stQ == nullptr, P_l = sum(stR).
@@ -384,58 +369,8 @@ __device__ __forceinline__ void r_restrict_q_ll(const Geom& G, const Bufs& B, in
   __syncthreads();
 }
 
-// The partner halves' W^T q of step it (every level; level l at stage row
-// 2^l - 1, its i-th leaf at row 2^l - 1 + i) polled from their flagged words
-// into `stage` by the first NST threads (the last wave polls the p.q partials
-// meanwhile).  Every word is loaded at once and the late ones re-polled
-// together, so a late partner costs one round trip, not one per word.
+// The last wave's first thread (it holds the p.q partials' sum).
 constexpr int NST = NTR - 64;
-template <typename T, int LEV>
-__device__ __forceinline__ void ll_stage_q(const Geom& G, const Bufs& B, int s, int k, int par, unsigned tag,
-                                           unsigned e, T* stage, int& bad) {
-  if constexpr (LEV > 0) {
-    constexpr int NWORDS = RANK * ((1 << LEV) - 1);
-    constexpr int WPT = (NWORDS + NST - 1) / NST;
-    static_assert(WPT <= 32, "poll mask");
-    const int tid = tid_of<kFresh<T, LEV>>();
-    const unsigned long long* base =
-        B.qll + (size_t)par * G.B * G.levels * G.K * RANK + (size_t)s * G.levels * G.K * RANK;
-    int off[WPT];
-    unsigned long long v[WPT];
-    unsigned pending = 0;
-#pragma unroll
-    for (int j = 0; j < WPT; ++j) {
-      const int w = tid + j * NST;
-      off[j] = 0;
-      if (w < NWORDS) {
-        const int row = w / RANK, c = w - row * RANK;
-        const int l = 31 - __clz(row + 1);
-        const int kp = (((k >> l) ^ 1) << l) + (row + 1 - (1 << l));
-        off[j] = (l * G.K + kp) * RANK + c;
-        v[j] = ld_c(base + off[j]);
-        pending |= 1u << j;
-      }
-    }
-    for (unsigned polls = 0;; ++polls) {
-#pragma unroll
-      for (int j = 0; j < WPT; ++j)
-        if ((pending & (1u << j)) && q_ready<T>(v[j], tag, e)) {
-          stage[tid + j * NST] = q_value<T>(v[j]);
-          pending &= ~(1u << j);
-        }
-      if (!pending) break;
-      if (polls > B.poll_limit || ((polls & 1023u) == 1023u && ld_c(B.abort_flag))) {
-        st_c(B.abort_flag, 1);
-        bad = 1;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-      for (int j = 0; j < WPT; ++j)
-        if (pending & (1u << j)) v[j] = ld_c(base + off[j]);
-    }
-  }
-}
 
 // The system's K flagged p.q partials of epoch e (parity par), summed by one
 // wave in the fixed order of sum_partials_r.
@@ -464,6 +399,173 @@ __device__ __forceinline__ double ll_get_pq(const Bufs& B, int s, int K, size_t 
   return wave_sum(a);
 }
 
+// Phase BC's poll of the partners' W^T q words, summed as they land.  Thread
+// (column c = tid % 32, group g = tid / 32 of 16) polls, for every level l,
+// the words of the partner half's leaves g, g + 16, ... and adds them in that
+// order; the two groups of a wave are folded, and the wave's partial of each
+// (level, column) goes to sm.redW[wave][MAX_LEVELS * RANK + l * RANK + c]:
+// the values, slots and order in which prolong_strips sums staged words, so
+// the partner sums are bitwise the same, without staging the words in LDS
+// and reading them back.  Every word is loaded at once and the late ones
+// re-polled together.  The last wave also polls the system's p.q partials and
+// sums them in the order of ll_get_pq into sm.dsc[3].  No barrier.
+template <int LEV>
+constexpr int q_slot0(int l) {
+  int n = 0;
+  for (int i = 0; i < l; ++i) n += ((1 << i) + 15) / 16;
+  return n;
+}
+
+template <typename T, int LEV>
+__device__ __forceinline__ void ll_q_strips(const Geom& G, const Bufs& B, int s, int k, int par, unsigned tag,
+                                            unsigned e, size_t BK, RSmem<T>& sm, int& bad) {
+  static_assert(LEV > 0, "levels only");
+  constexpr int NS = q_slot0<LEV>(LEV);
+  static_assert(NS <= 32, "poll mask");
+  const int tid = tid_of<kFresh<T, LEV>>(), lane = tid & 63, wave = tid >> 6;
+  const int c = tid & 31, g = tid >> 5;
+  const bool hi = (lane & 32) != 0;
+  const unsigned long long* base =
+      B.qll + (size_t)par * G.B * G.levels * G.K * RANK + (size_t)s * G.levels * G.K * RANK;
+  auto addr = [&](int l, int i) { return base + ((size_t)l * G.K + (((k >> l) ^ 1) << l) + i) * RANK + c; };
+  unsigned long long v[NS];
+  unsigned pending = 0;
+#pragma unroll
+  for (int l = 0; l < LEV; ++l)
+#pragma unroll
+    for (int m = 0; m < ((1 << l) + 15) / 16; ++m) {
+      const int i = g + 16 * m, j = q_slot0<LEV>(l) + m;
+      if (i < (1 << l)) {
+        v[j] = ld_c(addr(l, i));
+        pending |= 1u << j;
+      }
+    }
+  // the last wave: the p.q partial of leaf j = lane (and lane + 64) as its two words
+  const bool pqw = wave == NWR - 1;
+  const unsigned long long* pq = B.pqll + ((size_t)par * BK + (size_t)s * G.K) * 2;
+  unsigned long long w0 = 0, w1 = 0, w2 = 0, w3 = 0;
+  unsigned ppend = 0;
+  if (pqw) {
+    if (lane < G.K) { w0 = ld_c(pq + 2 * lane); w1 = ld_c(pq + 2 * lane + 1); ppend |= 1u; }
+    if (lane + 64 < G.K) { w2 = ld_c(pq + 2 * lane + 128); w3 = ld_c(pq + 2 * lane + 129); ppend |= 2u; }
+  }
+  for (unsigned polls = 0;; ++polls) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+      if ((pending & (1u << j)) && q_ready<T>(v[j], tag, e)) pending &= ~(1u << j);
+    if ((ppend & 1u) && ll_ready(w0, e) && ll_ready(w1, e)) ppend &= ~1u;
+    if ((ppend & 2u) && ll_ready(w2, e) && ll_ready(w3, e)) ppend &= ~2u;
+    if (!pending && !ppend) break;
+    if (polls > B.poll_limit || ((polls & 1023u) == 1023u && ld_c(B.abort_flag))) {
+      st_c(B.abort_flag, 1);
+      bad = 1;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int l = 0; l < LEV; ++l)
+#pragma unroll
+      for (int m = 0; m < ((1 << l) + 15) / 16; ++m) {
+        const int j = q_slot0<LEV>(l) + m;
+        if (pending & (1u << j)) v[j] = ld_c(addr(l, g + 16 * m));
+      }
+    if (ppend & 1u) { w0 = ld_c(pq + 2 * lane); w1 = ld_c(pq + 2 * lane + 1); }
+    if (ppend & 2u) { w2 = ld_c(pq + 2 * lane + 128); w3 = ld_c(pq + 2 * lane + 129); }
+  }
+  T b[LEV];
+#pragma unroll
+  for (int l = 0; l < LEV; ++l) {
+    b[l] = 0;
+#pragma unroll
+    for (int m = 0; m < ((1 << l) + 15) / 16; ++m)
+      if (g + 16 * m < (1 << l)) b[l] += q_value<T>(v[q_slot0<LEV>(l) + m]);
+  }
+  T* dQ = &sm.redW[wave][MAX_LEVELS * RANK + c];
+#pragma unroll
+  for (int l = 0; l + 1 < LEV; l += 2) dQ[(hi ? l + 1 : l) * RANK] = fold_x32(b[l], b[l + 1]);
+  if constexpr (LEV % 2 == 1) {
+    const T f = b[LEV - 1] + lane_x32(b[LEV - 1]);
+    if (!hi) dQ[(LEV - 1) * RANK] = f;
+  }
+  if (pqw) {
+    double a = 0.0;
+    if (lane < G.K) a += __hiloint2double((int)(unsigned)w1, (int)(unsigned)w0);
+    if (lane + 64 < G.K) a += __hiloint2double((int)(unsigned)w3, (int)(unsigned)w2);
+    for (int j = lane + 128; j < G.K && !bad; j += 64) {   // systems of more than 128 leaves
+      const unsigned long long* p = pq + 2 * j;
+      for (unsigned polls = 0;; ++polls) {
+        const unsigned long long x0 = ld_c(p), x1 = ld_c(p + 1);
+        if (ll_ready(x0, e) && ll_ready(x1, e)) {
+          a += __hiloint2double((int)(unsigned)x1, (int)(unsigned)x0);
+          break;
+        }
+        if (polls > B.poll_limit || ((polls & 1023u) == 1023u && ld_c(B.abort_flag))) {
+          st_c(B.abort_flag, 1);
+          bad = 1;
+          break;
+        }
+      }
+    }
+    const double sum = wave_sum(a);
+    if (lane == 0) sm.dsc[3] = sum;
+  }
+}
+
+// z = M r_new on the leaf's rows into sm.z after ll_q_strips: the waves'
+// partials of the partner sums of W^T q are in sm.redW; with r_from_prev the
+// partner sums of W^T r are the previous sm.P, else they are summed from the
+// staged words stR here (prolong_strips' order).  P_l = (sum of W^T r) - alpha
+// (sum of W^T q); then z = (sm.yr - alpha sm.yq) + sum_l W_l[k] P_l + g r_new
+// (U_k U_k^T r_new by the linear update of the leaf stage).
+template <typename T, int LEV>
+__device__ __forceinline__ void r_prolong_split_q(const Resident<T, LEV>& F, RSmem<T>& sm, const T* stR,
+                                                  double alpha, float gate, bool r_from_prev) {
+  const int tid = tid_of<kFresh<T, LEV>>();
+  if constexpr (LEV > 0) {
+    if (!r_from_prev) {
+      const int lane = tid & 63, wave = tid >> 6, c = tid & 31, g = tid >> 5;
+      const bool hi = (lane & 32) != 0;
+      T a[LEV];
+#pragma unroll
+      for (int l = 0; l < LEV; ++l) {
+        const T* vr = stR + (size_t)((1 << l) - 1) * RANK + c;
+        a[l] = 0;
+#pragma unroll
+        for (int m = 0; m < ((1 << l) + 15) / 16; ++m)
+          if (g + 16 * m < (1 << l)) a[l] += vr[(g + 16 * m) * RANK];
+      }
+      T* dR = &sm.redW[wave][c];
+#pragma unroll
+      for (int l = 0; l + 1 < LEV; l += 2) dR[(hi ? l + 1 : l) * RANK] = fold_x32(a[l], a[l + 1]);
+      if constexpr (LEV % 2 == 1) {
+        const T f = a[LEV - 1] + lane_x32(a[LEV - 1]);
+        if (!hi) dR[(LEV - 1) * RANK] = f;
+      }
+      __syncthreads();
+    }
+    if (tid < LEV * RANK) {
+      T a;
+      if (r_from_prev) {
+        a = sm.P[tid];
+      } else {
+        a = sm.redW[0][tid];
+#pragma unroll
+        for (int w = 1; w < NWR; ++w) a += sm.redW[w][tid];
+      }
+      T b = sm.redW[0][MAX_LEVELS * RANK + tid];
+#pragma unroll
+      for (int w = 1; w < NWR; ++w) b += sm.redW[w][MAX_LEVELS * RANK + tid];
+      sm.P[tid] = (T)((double)a - alpha * (double)b);
+    }
+    __syncthreads();
+  }
+  prolong_offdiag<T, LEV>(F, sm);
+  __syncthreads();
+  if (tid < LEAF)
+    sm.z[tid] = (T)((double)sm.yr[tid] - alpha * (double)sm.yq[tid]) + sm.yoff[tid] + (T)gate * sm.r[tid];
+  __syncthreads();
+}
+
 // The grid covers systems s0 .. s0 + gridDim.x / K - 1 (a batch with more
 // leaves than CUs is solved in groups of whole systems, one launch each).
 //
@@ -490,9 +592,8 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
   int* rpL = reinterpret_cast<int*>(valL + max_leaf_nnz);
   const int stage_rows = partner_rows(G);
   T* stR = reinterpret_cast<T*>(rdyn4 + (2 * max_leaf_nnz + LEAF + 1 + 3) / 4);
-  T* stQ = stR + (size_t)stage_rows * RANK;
   // z and p of the previous step by leaf-local column: own rows, then the halo
-  T* zc = stQ + (size_t)stage_rows * RANK;
+  T* zc = stR + (size_t)stage_rows * RANK;
   T* pc = zc + LEAF + max_halo;
   int* hcolL = reinterpret_cast<int*>(pc + LEAF + max_halo);   // halo global columns
   const int tid = threadIdx.x;
@@ -716,9 +817,9 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
         if (!r_from_prev) r_stage_partners<T, LEV>(G, pR[rbuf], s, k, stR);
       }
       int bad = 0;
-      if (tid < NST) {
-        ll_stage_q<T, LEV>(G, B, s, k, it & 1, q_tag(it), B.ep_base + (unsigned)it, stQ, bad);
-      } else {
+      if constexpr (LEV > 0) {
+        ll_q_strips<T, LEV>(G, B, s, k, it & 1, q_tag(it), B.ep_base + (unsigned)it, BK, sm, bad);
+      } else if (tid >= NST) {
         const double pqs = ll_get_pq(B, s, G.K, BK, it & 1, B.ep_base + (unsigned)it, bad);
         if (tid == NST) sm.dsc[3] = pqs;
       }
@@ -741,8 +842,8 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
       if constexpr (JAC) {
         if (tid < LEAF) sm.z[tid] = (T)(dinv * (double)sm.r[tid]);
       } else {
-        // (r_prolong_split synchronizes before it reads sm.r)
-        r_prolong_split<T, LEV>(F, sm, stR, stQ, alpha, gate, r_from_prev);
+        // (r_prolong_split_q synchronizes before it reads sm.r)
+        r_prolong_split_q<T, LEV>(F, sm, stR, alpha, gate, r_from_prev);
       }
       stamp_it(it, 6);
       if constexpr (SQ) {
