@@ -817,7 +817,7 @@ hpcg_status run_bridge_apply(hpcg_ctx* h, const float* d_r, float* d_y, bool& ra
   const Geom G = h->G;
   const int items = G.B * G.K;
   if (G.levels < 1 || !h->bridge_set || G.K > h->num_cu) return HPCG_OK;
-  const size_t dyn = ((size_t)partner_rows(G) * RANK + (size_t)G.levels * RANK * CSTRIDE) * sizeof(float);
+  const size_t dyn = (size_t)G.levels * RANK * CSTRIDE * sizeof(float);   // the leaf's tiles' cores
   if (dyn + sizeof(RSmem<float>) > kMaxLds) return HPCG_OK;
   const bool split = h->split_apply && 4 * (int64_t)items <= h->num_cu;
   const void* fn = bridge_apply_kernel(G.levels, split);
@@ -855,7 +855,7 @@ hpcg_status run_fused_apply(hpcg_ctx* h, const float* d_r, float* d_y, bool& ran
   const float* ra = d_r;
   float* ya = d_y;
   void* args[] = {&Ga, &Ba, &ra, &ya};
-  const size_t dyn = (size_t)partner_rows(G) * RANK * sizeof(float);
+  const size_t dyn = 0;   // the partner words are summed as they land: no stage in LDS
   // two workgroups per leaf (diagonal / off-diagonal roles) while the batch
   // has at most a quarter as many leaves as the device has compute units and
   // every workgroup can be resident at once.  Measured: n = 1,024 / 4,096 /

@@ -72,62 +72,114 @@ __global__ __launch_bounds__(NT) void k_spmv(const int* __restrict__ row_ptr, co
 // which stays set until the host reads it, and finishes with whatever words
 // it has, so the output is undefined but every workgroup exits and every
 // leaf's epoch still advances by one (the next call is consistent).
+
+// The partners' restriction words polled and summed per level as they land:
+// thread (column c = tid % 32, group g = tid / 32 of 16) loads, for every
+// level l, the words of the partner half's leaves g, g + 16, ... at once, adds
+// them in that order, and the two groups of a wave are folded into the wave's
+// partial of each (level, column), stored at sm.redW[wave][MAX_LEVELS * RANK +
+// l * RANK + c] (the half of redW the restriction does not use, so no barrier
+// is needed before it): the first stage of prolong_strips over staged words,
+// without staging them.  DIAG: also the leaf's diagonal-stage words (LEAF of
+// them at B.lly[item], from its diagonal workgroup) into ydiag, in the same
+// poll rounds.  No barrier.
 template <int LEV>
-__device__ __forceinline__ void gather_partners_ll(const Geom& G, const Bufs& B, int s, int k, unsigned want,
-                                                   float* stage) {
-  if constexpr (LEV > 0) {
-    // word w = row * RANK + c, row = 2^l - 1 + i: column c of the i-th leaf of
-    // level l's partner half, staged at the same position
-    constexpr int NWORDS = RANK * ((1 << LEV) - 1);
-    constexpr int WPT = (NWORDS + NTR - 1) / NTR;
-    const int tid = threadIdx.x;
-    const unsigned long long* src[WPT];
-    unsigned long long v[WPT];
+constexpr int strip_slot0(int l) {
+  int n = 0;
+  for (int i = 0; i < l; ++i) n += ((1 << i) + 15) / 16;
+  return n;
+}
+
+template <int LEV, bool DIAG>
+__device__ __forceinline__ void gather_sum_ll(const Geom& G, const Bufs& B, int s, int k, int item, unsigned want,
+                                              RSmem<float>& sm, float* ydiag) {
+  static_assert(LEV > 0, "levels only");
+  constexpr int NS = strip_slot0<LEV>(LEV);
+  static_assert(NS <= 31, "poll mask");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = tid & 31, g = tid >> 5;
+  const bool hi = (lane & 32) != 0;
+  const unsigned long long* base = B.llw + (size_t)s * G.levels * G.K * RANK;
+  auto addr = [&](int l, int i) { return base + ((size_t)l * G.K + (((k >> l) ^ 1) << l) + i) * RANK + c; };
+  unsigned long long v[NS];
+  unsigned pending = 0;
 #pragma unroll
-    for (int j = 0; j < WPT; ++j) {
-      const int w = tid + j * NTR;
-      src[j] = nullptr;
-      if (w < NWORDS) {
-        const int row = w / RANK, c = w - row * RANK;
-        const int l = 31 - __clz(row + 1);
-        const int kp = (((k >> l) ^ 1) << l) + (row + 1 - (1 << l));
-        src[j] = B.llw + (((size_t)s * G.levels + l) * G.K + kp) * RANK + c;
-        v[j] = ld_c(src[j]);
+  for (int l = 0; l < LEV; ++l)
+#pragma unroll
+    for (int m = 0; m < ((1 << l) + 15) / 16; ++m) {
+      const int i = g + 16 * m, j = strip_slot0<LEV>(l) + m;
+      if (i < (1 << l)) {
+        v[j] = ld_c(addr(l, i));
+        pending |= 1u << j;
       }
     }
-    // re-poll every word still short of its epoch together, so that a late
-    // partner costs one round trip, not one per word
-    unsigned pending = 0;
-#pragma unroll
-    for (int j = 0; j < WPT; ++j)
-      if (src[j] && (unsigned)(v[j] >> 32) != want) pending |= 1u << j;
-    stamp(blockIdx.x, 10);
-    unsigned polls = 0;
-    while (pending) {
-      __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-      for (int j = 0; j < WPT; ++j)
-        if (pending & (1u << j)) v[j] = ld_c(src[j]);
-#pragma unroll
-      for (int j = 0; j < WPT; ++j)
-        if ((pending & (1u << j)) && (unsigned)(v[j] >> 32) == want) pending &= ~(1u << j);
-      if (pending && ++polls > B.apply_poll_limit) {
-        st_c(B.apply_abort, 1);
-        break;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < WPT; ++j)
-      if (src[j]) stage[tid + j * NTR] = __uint_as_float((unsigned)v[j]);
+  const unsigned long long* dsrc = B.lly + (size_t)item * LEAF + tid;
+  unsigned long long dv = 0;
+  if (DIAG && tid < LEAF) {
+    dv = ld_c(dsrc);
+    pending |= 1u << NS;
   }
+  auto settle = [&]() {
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+      if ((pending & (1u << j)) && (unsigned)(v[j] >> 32) == want) pending &= ~(1u << j);
+    if (DIAG && (pending & (1u << NS)) && (unsigned)(dv >> 32) == want) pending &= ~(1u << NS);
+  };
+  settle();
+  stamp(blockIdx.x, 10);
+  unsigned polls = 0;
+  while (pending) {
+    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int l = 0; l < LEV; ++l)
+#pragma unroll
+      for (int m = 0; m < ((1 << l) + 15) / 16; ++m) {
+        const int j = strip_slot0<LEV>(l) + m;
+        if (pending & (1u << j)) v[j] = ld_c(addr(l, g + 16 * m));
+      }
+    if (DIAG && (pending & (1u << NS))) dv = ld_c(dsrc);
+    settle();
+    if (pending && ++polls > B.apply_poll_limit) {
+      st_c(B.apply_abort, 1);
+      break;
+    }
+  }
+  float a[LEV];
+#pragma unroll
+  for (int l = 0; l < LEV; ++l) {
+    a[l] = 0.f;
+#pragma unroll
+    for (int m = 0; m < ((1 << l) + 15) / 16; ++m)
+      if (g + 16 * m < (1 << l)) a[l] += __uint_as_float((unsigned)v[strip_slot0<LEV>(l) + m]);
+  }
+  float* d = &sm.redW[wave][MAX_LEVELS * RANK + c];
+#pragma unroll
+  for (int l = 0; l + 1 < LEV; l += 2) d[(hi ? l + 1 : l) * RANK] = fold_x32(a[l], a[l + 1]);
+  if constexpr (LEV % 2 == 1) {
+    const float f = a[LEV - 1] + lane_x32(a[LEV - 1]);
+    if (!hi) d[(LEV - 1) * RANK] = f;
+  }
+  if (DIAG && tid < LEAF) ydiag[tid] = __uint_as_float((unsigned)dv);
+}
+
+// Strip aggregation after gather_sum_ll (after a barrier): P_l[c] = the sum of
+// the waves' partials.  One barrier.
+template <int LEV>
+__device__ __forceinline__ void strips_from_partials(RSmem<float>& sm) {
+  const int tid = threadIdx.x;
+  if (tid < LEV * RANK) {
+    float a = sm.redW[0][MAX_LEVELS * RANK + tid];
+#pragma unroll
+    for (int w = 1; w < NWR; ++w) a += sm.redW[w][MAX_LEVELS * RANK + tid];
+    sm.P[tid] = a;
+  }
+  __syncthreads();
 }
 
 template <int LEV>
 __global__ __launch_bounds__(NTR) void k_apply_fused(Geom G, Bufs B, const float* __restrict__ rin,
                                                      float* __restrict__ yout, int item0) {
   __shared__ RSmem<float> sm;
-  extern __shared__ int4 fdyn4[];
-  float* stR = reinterpret_cast<float*>(fdyn4);
   const int tid = threadIdx.x;
   const int item = item0 + (int)blockIdx.x;
   const int s = item / G.K, k = item - s * G.K;
@@ -177,10 +229,10 @@ __global__ __launch_bounds__(NTR) void k_apply_fused(Geom G, Bufs B, const float
   // partners' words are in flight
   prolong_diag<float, LEV>(F, sm);
   stamp(blockIdx.x, 4);
-  gather_partners_ll<LEV>(G, B, s, k, want, stR);
+  if constexpr (LEV > 0) gather_sum_ll<LEV, false>(G, B, s, k, item, want, sm, nullptr);
   __syncthreads();
   stamp(blockIdx.x, 5);
-  if constexpr (LEV > 0) prolong_strips<float, LEV, true>(sm, stR, (const float*)nullptr, 0.0);
+  if constexpr (LEV > 0) strips_from_partials<LEV>(sm);
   stamp(blockIdx.x, 8);
   prolong_offdiag<float, LEV>(F, sm);
   stamp(blockIdx.x, 9);
@@ -193,59 +245,6 @@ __global__ __launch_bounds__(NTR) void k_apply_fused(Geom G, Bufs B, const float
   __syncthreads();
   stamp(blockIdx.x, 7);
 #endif
-}
-
-// gather_partners_ll plus the leaf's own diagonal stage U_k U_k^T r published
-// by its diagonal workgroup (LEAF words at B.lly[item]) into ydiag, in the
-// same poll rounds.
-template <int LEV>
-__device__ __forceinline__ void gather_partners_diag_ll(const Geom& G, const Bufs& B, int s, int k, int item,
-                                                        unsigned want, float* stage, float* ydiag) {
-  constexpr int NP = RANK * ((1 << LEV) - 1);
-  constexpr int NWORDS = NP + LEAF;
-  constexpr int WPT = (NWORDS + NTR - 1) / NTR;
-  static_assert(WPT <= 32, "poll mask");
-  const int tid = threadIdx.x;
-  const unsigned long long* src[WPT];
-  unsigned long long v[WPT];
-#pragma unroll
-  for (int j = 0; j < WPT; ++j) {
-    const int w = tid + j * NTR;
-    src[j] = nullptr;
-    if (w < NP) {
-      const int row = w / RANK, c = w - row * RANK;
-      const int l = 31 - __clz(row + 1);
-      const int kp = (((k >> l) ^ 1) << l) + (row + 1 - (1 << l));
-      src[j] = B.llw + (((size_t)s * G.levels + l) * G.K + kp) * RANK + c;
-    } else if (w < NWORDS) {
-      src[j] = B.lly + (size_t)item * LEAF + (w - NP);
-    }
-    if (src[j]) v[j] = ld_c(src[j]);
-  }
-  unsigned pending = 0;
-#pragma unroll
-  for (int j = 0; j < WPT; ++j)
-    if (src[j] && (unsigned)(v[j] >> 32) != want) pending |= 1u << j;
-  unsigned polls = 0;
-  while (pending) {
-    __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-    for (int j = 0; j < WPT; ++j)
-      if (pending & (1u << j)) v[j] = ld_c(src[j]);
-#pragma unroll
-    for (int j = 0; j < WPT; ++j)
-      if ((pending & (1u << j)) && (unsigned)(v[j] >> 32) == want) pending &= ~(1u << j);
-    if (pending && ++polls > B.apply_poll_limit) {
-      st_c(B.apply_abort, 1);
-      break;
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < WPT; ++j) {
-    const int w = tid + j * NTR;
-    if (w < NP) stage[w] = __uint_as_float((unsigned)v[j]);
-    else if (w < NWORDS) ydiag[w - NP] = __uint_as_float((unsigned)v[j]);
-  }
 }
 
 // Single-pass apply with two workgroups per leaf, by role, so that twice as
@@ -262,8 +261,6 @@ __global__ __launch_bounds__(NTR) void k_apply_split(Geom G, Bufs B, const float
                                                      float* __restrict__ yout) {
   static_assert(LEV > 0, "the split needs tile levels");
   __shared__ RSmem<float> sm;
-  extern __shared__ int4 fdyn4[];
-  float* stR = reinterpret_cast<float*>(fdyn4);
   const int tid = threadIdx.x;
   const int item = blockIdx.x >> 1;
   const bool diag_role = (blockIdx.x & 1) == 0;
@@ -313,10 +310,10 @@ __global__ __launch_bounds__(NTR) void k_apply_split(Geom G, Bufs B, const float
          ((unsigned long long)want << 32) | __float_as_uint(a));
   }
   stamp(blockIdx.x, 2);
-  gather_partners_diag_ll<LEV>(G, B, s, k, item, want, stR, sm.yleaf);
+  gather_sum_ll<LEV, true>(G, B, s, k, item, want, sm, sm.yleaf);
   __syncthreads();
   stamp(blockIdx.x, 5);
-  prolong_strips<float, LEV, true>(sm, stR, (const float*)nullptr, 0.0);
+  strips_from_partials<LEV>(sm);
   prolong_offdiag<float, LEV>(F, sm);
   __syncthreads();
   stamp(blockIdx.x, 6);

@@ -125,37 +125,13 @@ __device__ __forceinline__ void couple_and_publish(const Geom& G, const Bufs& B,
   }
 }
 
-// Strip aggregation of the gathered coupled values (stage row 2^l - 1 + i:
-// level l, i-th leaf of the partner half), summed per side: sm.P[0, R) = the
+// Strip aggregation of the gathered coupled values per side, from the waves'
+// partials that gather_sum_ll leaves (level l, column c): sm.P[0, R) = the
 // levels where k is in the row half (they multiply U~_k), sm.P[R, 2R) = the
-// others (V~_k).  16 groups of threads per column, then across waves and
-// levels in a fixed order; two barriers.
+// others (V~_k), across waves and levels in a fixed order.  One barrier.
 template <int LEV>
-__device__ __forceinline__ void bridge_strip_sides(RSmem<float>& sm, const float* stR, int k) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = tid & 31, g = tid >> 5;
-  const bool hi = (lane & 32) != 0;
-  float a[LEV];
-#pragma unroll
-  for (int l = 0; l < LEV; ++l) {
-    const float* vr = stR + (size_t)((1 << l) - 1) * RANK + c;
-    a[l] = 0.f;
-#pragma unroll
-    for (int m = 0; m < ((1 << l) + 15) / 16; ++m) {
-      const int i = g + 16 * m;
-      const bool ok = (1 << l) >= 16 || i < (1 << l);
-      const float v = vr[(ok ? i : 0) * RANK];
-      a[l] += ok ? v : 0.f;
-    }
-  }
-  float* d = &sm.redW[wave][c];
-#pragma unroll
-  for (int l = 0; l + 1 < LEV; l += 2) d[(hi ? l + 1 : l) * RANK] = fold_x32(a[l], a[l + 1]);
-  if constexpr (LEV % 2 == 1) {
-    const float f = a[LEV - 1] + lane_x32(a[LEV - 1]);
-    if (!hi) d[(LEV - 1) * RANK] = f;
-  }
-  __syncthreads();
+__device__ __forceinline__ void bridge_sides_from_partials(RSmem<float>& sm, int k) {
+  const int tid = threadIdx.x;
   if (tid < 2 * RANK) {
     const int side = tid / RANK, cc = tid - side * RANK;
     float p = 0.f;
@@ -163,9 +139,9 @@ __device__ __forceinline__ void bridge_strip_sides(RSmem<float>& sm, const float
     // at once); the other side's levels add zero
 #pragma unroll
     for (int l = 0; l < LEV; ++l) {
-      float q = sm.redW[0][l * RANK + cc];
+      float q = sm.redW[0][MAX_LEVELS * RANK + l * RANK + cc];
 #pragma unroll
-      for (int w = 1; w < NWR; ++w) q += sm.redW[w][l * RANK + cc];
+      for (int w = 1; w < NWR; ++w) q += sm.redW[w][MAX_LEVELS * RANK + l * RANK + cc];
       p += ((k >> l) & 1) == side ? q : 0.f;
     }
     sm.P[tid] = p;
@@ -184,8 +160,7 @@ __global__ __launch_bounds__(NTR) void k_apply_bridge(Geom G, Bufs B, const floa
   static_assert(LEV >= 1, "the bridge apply needs tile levels");
   __shared__ RSmem<float> sm;
   extern __shared__ int4 bdyn4[];
-  float* stR = reinterpret_cast<float*>(bdyn4);                  // partner_rows x R partner values
-  float* cores = stR + (size_t)partner_rows(G) * RANK;             // LEV x R x CSTRIDE
+  float* cores = reinterpret_cast<float*>(bdyn4);                 // LEV x R x CSTRIDE
   const int tid = threadIdx.x;
   const int item = item0 + (SPLIT ? (int)(blockIdx.x >> 1) : (int)blockIdx.x);
   const bool diag_role = SPLIT && (blockIdx.x & 1) == 0;
@@ -246,11 +221,10 @@ __global__ __launch_bounds__(NTR) void k_apply_bridge(Geom G, Bufs B, const floa
     prolong_diag<float, 2>(F, sm);
     stamp(blockIdx.x, 4);
   }
-  if constexpr (SPLIT) gather_partners_diag_ll<LEV>(G, B, s, k, item, want, stR, sm.yleaf);
-  else gather_partners_ll<LEV>(G, B, s, k, want, stR);
+  gather_sum_ll<LEV, SPLIT>(G, B, s, k, item, want, sm, sm.yleaf);
   __syncthreads();
   stamp(blockIdx.x, 5);
-  bridge_strip_sides<LEV>(sm, stR, k);
+  bridge_sides_from_partials<LEV>(sm, k);
   stamp(blockIdx.x, 8);
   prolong_offdiag<float, 2>(F, sm);
   __syncthreads();
