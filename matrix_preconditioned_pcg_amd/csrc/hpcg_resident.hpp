@@ -727,7 +727,7 @@ __global__ __launch_bounds__(NTR) void k_resident(Geom G, Bufs B, int max_leaf_n
 
   double pend_rel = 0.0;
   // timeline build: stamps of one iteration (empty otherwise)
-  constexpr int kTraceIt = 65;   // an iteration without the exact refresh
+  constexpr int kTraceIt = 66;   // a plain iteration: no exact refresh, no restaging of W^T r
   auto stamp_it = [&](int it, int slot) {
     if (it == kTraceIt) stamp(blockIdx.x, slot);
   };

@@ -67,7 +67,7 @@ def main(argv=None):
     ap.add_argument("--calls", type=int, default=200)
     ap.add_argument("--build", action="store_true")
     ap.add_argument("--bridge", action="store_true", help="factors in the bridge format (native bridge apply)")
-    ap.add_argument("--solve", action="store_true", help="also one resident solve: its 65th iteration")
+    ap.add_argument("--solve", action="store_true", help="also one resident solve: its 66th iteration")
     ap.add_argument("--block", type=int, default=0, metavar="NRHS",
                     help="instead: the block apply's leaf stage and prolongation on NRHS columns, in a "
                          "replayed graph of block applies and in the last iteration of a block solve")
@@ -157,11 +157,11 @@ def main(argv=None):
             hpcg.hpcg_trace_read(0, clear=True)
             res = solver.solve(b)
             torch.cuda.synchronize()
-        if hpcg.hpcg_last_engine(solver.handle) == hpcg.HPCG_ENGINE_PERSISTENT and min(res.iterations) > 65:
+        if hpcg.hpcg_last_engine(solver.handle) == hpcg.HPCG_ENGINE_PERSISTENT and min(res.iterations) > 66:
             nwg = min(items, ncu)
             rs = np.array(hpcg.hpcg_trace_read(nwg * SLOTS), dtype=np.uint64).reshape(nwg, SLOTS)
             t0 = int(rs[:, 0].astype(np.int64).min())
-            out += ["", table(f"resident solve, iteration 65 of {res.iterations[0]} (first launch)", rs,
+            out += ["", table(f"resident solve, iteration 66 of {res.iterations[0]} (first launch)", rs,
                               RESIDENT, t0)]
             d = np.diff(rs[:, [0, 1, 2, 3, 4, 5, 6, 7, 8]].astype(np.int64), axis=1) * TICK_US
             names = list(RESIDENT.values())

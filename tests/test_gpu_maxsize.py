@@ -81,9 +81,8 @@ def test_max_truncated_solve(system, n, engine):
 
 
 def test_max_solve_parity(system):
-    # fp64 vectors: the resident engine's partner stages of 255 rows do not fit
-    # in LDS beside its other arrays, so AUTO runs the graph engine; fp32
-    # vectors: the resident engine at its widest (256 workgroups, one per CU)
+    # both vector precisions on the resident engine at its widest (256
+    # workgroups, one per CU, with the 255-row partner stage of W^T r in LDS)
     batch = system(32768)
     _log("max-size solve n=32768 (oracle solve takes ~15 s)")
     sy = batch.system(0)
@@ -97,8 +96,7 @@ def test_max_solve_parity(system):
         grid, lds = hpcg.hpcg_last_launch_info(s.handle)
         _log(f"  precision {prec}: engine {s.last_engine} (grid {grid}, LDS {lds}), "
              f"{res.iterations[0]} iterations (oracle {ref.iterations})")
-        if prec == hpcg.HPCG_PREC_VEC32:
-            assert s.last_engine == hpcg.HPCG_ENGINE_PERSISTENT and grid == 256
+        assert s.last_engine == hpcg.HPCG_ENGINE_PERSISTENT and grid == 256
         assert abs(res.iterations[0] - ref.iterations) <= ITER_TOL, (res.iterations[0], ref.iterations)
         assert res.relres[0] <= batch.tol
         tr = oracle.true_relres(sy.row_ptr, sy.col, sy.val, sy.b, res.x[0].cpu().numpy())
