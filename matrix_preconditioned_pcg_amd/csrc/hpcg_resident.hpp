@@ -440,10 +440,21 @@ __device__ __forceinline__ void ll_q_strips(const Geom& G, const Bufs& B, int s,
         pending |= 1u << j;
       }
     }
-  // the last wave: the p.q partial of leaf j = lane (and lane + 64) as its two words
+  // the last wave: the p.q partial of leaf j = lane (and lane + 64) as its two
+  // words.  From seven levels on (where registers run short) they take the
+  // slots of levels 0 .. 3, which that wave's groups (14 and 15) never fill
   const bool pqw = wave == NWR - 1;
   const unsigned long long* pq = B.pqll + ((size_t)par * BK + (size_t)s * G.K) * 2;
-  unsigned long long w0 = 0, w1 = 0, w2 = 0, w3 = 0;
+  constexpr bool PQ_IN_SLOTS = LEV >= 7;
+  unsigned long long wx[4];
+  auto pw = [&](int i) -> unsigned long long& {
+    if constexpr (PQ_IN_SLOTS) return v[i];
+    else return wx[i];
+  };
+  unsigned long long& w0 = pw(0);
+  unsigned long long& w1 = pw(1);
+  unsigned long long& w2 = pw(2);
+  unsigned long long& w3 = pw(3);
   unsigned ppend = 0;
   if (pqw) {
     if (lane < G.K) { w0 = ld_c(pq + 2 * lane); w1 = ld_c(pq + 2 * lane + 1); ppend |= 1u; }
