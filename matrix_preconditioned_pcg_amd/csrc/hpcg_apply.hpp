@@ -101,6 +101,13 @@ __device__ __forceinline__ void gather_sum_ll(const Geom& G, const Bufs& B, int 
   const bool hi = (lane & 32) != 0;
   const unsigned long long* base = B.llw + (size_t)s * G.levels * G.K * RANK;
   auto addr = [&](int l, int i) { return base + ((size_t)l * G.K + (((k >> l) ^ 1) << l) + i) * RANK + c; };
+  // The split kernel's off-diagonal workgroup reaches this poll right after
+  // publishing its own words, before most partners' words can be visible: a
+  // first round then finds few of them, and the rest cost a second round
+  // trip.  A short wait first (12 x 64 clocks, ~0.3 us) lets one round find
+  // nearly all of them (measured: N8k 5.92 -> 5.24 us, tet4k 5.30 -> 4.78;
+  // with fewer than five levels no gain, so no wait).
+  if constexpr (DIAG && LEV >= 5) __builtin_amdgcn_s_sleep(12);
   unsigned long long v[NS];
   unsigned pending = 0;
 #pragma unroll
