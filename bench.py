@@ -207,11 +207,11 @@ def cpu_baseline(batch, budget_s=25.0):
 
 def single_pass_kernel(batch):
     """Which single-pass apply kernel AUTO launches: two workgroups per leaf
-    (diagonal / off-diagonal roles) when the batch has at most a quarter as
-    many leaves as the device has CUs, else one per leaf."""
+    (diagonal / off-diagonal roles) when the batch has at most half as many
+    leaves as the device has CUs, else one per leaf."""
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    if 4 * batch.batch * batch.K <= cus:
+    if 2 * batch.batch * batch.K <= cus:
         return f"M-apply (k_apply_split<{batch.levels}>: one launch, two workgroups per leaf, factors read once)"
     return f"M-apply (k_apply_fused<{batch.levels}>: one launch, one workgroup per leaf, factors read once)"
 

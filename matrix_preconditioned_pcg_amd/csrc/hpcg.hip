@@ -857,11 +857,13 @@ hpcg_status run_fused_apply(hpcg_ctx* h, const float* d_r, float* d_y, bool& ran
   void* args[] = {&Ga, &Ba, &ra, &ya};
   const size_t dyn = 0;   // the partner words are summed as they land: no stage in LDS
   // two workgroups per leaf (diagonal / off-diagonal roles) while the batch
-  // has at most a quarter as many leaves as the device has compute units and
+  // has at most half as many leaves as the device has compute units and
   // every workgroup can be resident at once.  Measured: n = 1,024 / 4,096 /
-  // 8,192 gain 9 / 4 / 3%; at 128 leaves (half the CUs already busy) the
-  // split gains nothing warm and loses 4% with the factors in HBM.
-  const bool split = h->split_apply && 4 * (int64_t)items <= h->num_cu;
+  // 8,192 gain 9 / 4 / 3%; at 128 leaves (n = 16,384), with the off-diagonal
+  // workgroup's short wait before its first poll, 6.57 -> 6.16 us warm and
+  // 9.66 -> 9.39 us with the factors in HBM (without the wait it gained
+  // nothing warm and lost 4% cold).
+  const bool split = h->split_apply && 2 * (int64_t)items <= h->num_cu;
   if (const void* fs = split ? split_apply_kernel(G.levels) : nullptr) {
     hpcg_status s = allow_lds(h, fs, dyn);
     if (s != HPCG_OK) return s;

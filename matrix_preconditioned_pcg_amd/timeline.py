@@ -126,7 +126,7 @@ def main(argv=None):
     items = batch.batch * batch.K
     st = np.array(hpcg.hpcg_trace_read(4096 * SLOTS), dtype=np.uint64).reshape(4096, SLOTS)
     single = path in (hpcg.HPCG_APPLY_FUSED, hpcg.HPCG_APPLY_BRIDGE)
-    if single and 4 * items <= ncu:
+    if single and 2 * items <= ncu:
         wg = st[:2 * items]
         t0 = int(wg[:, 0].astype(np.int64).min())
         out.append(table("single-pass apply, two workgroups per leaf: diagonal role", wg[0::2], SPLIT_DIAG, t0))
