@@ -810,8 +810,9 @@ const void* bridge_apply_kernel(int levels, bool split) {
 
 // The native bridge-format apply (factors from hpcg_set_factors_bridge): one
 // launch per group of whole systems whose leaves all get a compute unit, two
-// workgroups per leaf while a quarter of the CUs hold the batch's leaves (as
-// the slab apply).  ran = false when it does not fit.
+// workgroups per leaf while the batch has at most half as many leaves as the
+// device has CUs (as the slab apply; N16k 6.92 -> 6.81 us).  ran = false when
+// it does not fit.
 hpcg_status run_bridge_apply(hpcg_ctx* h, const float* d_r, float* d_y, bool& ran) {
   ran = false;
   const Geom G = h->G;
@@ -819,7 +820,7 @@ hpcg_status run_bridge_apply(hpcg_ctx* h, const float* d_r, float* d_y, bool& ra
   if (G.levels < 1 || !h->bridge_set || G.K > h->num_cu) return HPCG_OK;
   const size_t dyn = (size_t)G.levels * RANK * CSTRIDE * sizeof(float);   // the leaf's tiles' cores
   if (dyn + sizeof(RSmem<float>) > kMaxLds) return HPCG_OK;
-  const bool split = h->split_apply && 4 * (int64_t)items <= h->num_cu;
+  const bool split = h->split_apply && 2 * (int64_t)items <= h->num_cu;
   const void* fn = bridge_apply_kernel(G.levels, split);
   if (!fn) return HPCG_OK;
   hpcg_status s = allow_lds(h, fn, dyn);
