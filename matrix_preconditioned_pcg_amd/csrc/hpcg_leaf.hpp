@@ -154,13 +154,11 @@ __device__ __forceinline__ void load_factors(const Geom& G, const Bufs& B, int s
 // alpha sum(stQ), or sum(stR) with stQ == nullptr.  With r_from_prev the
 // partner sums of r are not staged: sm.P still holds them (the previous
 // P, by linearity) and becomes sm.P - alpha sum(stQ).  16 groups of threads
-// per column, then across waves; two barriers.  BATCH issues every read
-// unconditionally (levels with fewer than 16 partner leaves read leaf 0 in
-// the idle groups and add zero instead), so that all of them are in flight
-// before the first wait: measured faster in the single-pass apply (N16k 7.08
-// -> 6.92 us) and slower in the resident solve (N8k 1.91 -> 1.96 ms), which
-// keeps the branches.
-template <typename T, int LEV, bool BATCH = false>
+// per column (group g adds the partner leaves g, g + 16, ... in that order),
+// then across waves; two barriers.  (The single-pass apply and the resident
+// solve's iterations add the partner words in this order as they land
+// instead of staging them; this form serves the set-up and the squared form.)
+template <typename T, int LEV>
 __device__ __forceinline__ void prolong_strips(RSmem<T>& sm, const T* stR, const T* stQ, double alpha,
                                                bool r_from_prev = false) {
   const int tid = tid_of<kFresh<T, LEV>>(), lane = tid & 63, wave = tid >> 6;
@@ -176,18 +174,7 @@ __device__ __forceinline__ void prolong_strips(RSmem<T>& sm, const T* stR, const
 #pragma unroll
     for (int m = 0; m < ((1 << l) + 15) / 16; ++m) {
       const int i = g + 16 * m;
-      if constexpr (BATCH) {
-        const bool ok = (1 << l) >= 16 || i < (1 << l);
-        const int ic = ok ? i : 0;
-        if (!r_from_prev) {
-          const T v = vr[ic * RANK];
-          a[l] += ok ? v : T(0);
-        }
-        if (stQ) {
-          const T v = stQ[(size_t)((1 << l) - 1) * RANK + c + ic * RANK];
-          b[l] += ok ? v : T(0);
-        }
-      } else if (i < (1 << l)) {
+      if (i < (1 << l)) {
         if (!r_from_prev) a[l] += vr[i * RANK];
         if (stQ) b[l] += stQ[(size_t)((1 << l) - 1) * RANK + c + i * RANK];
       }
