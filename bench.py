@@ -170,7 +170,7 @@ def cpu_model() -> str:
 
 def cpu_baseline(batch, budget_s=25.0):
     """The plain C fp64 oracle (oracle/c/pcg_oracle.c) solving the workload on
-    host cores: median of up to 5 timed solves after one warm-up, at one
+    host cores: median of up to 21 timed solves after one warm-up, at one
     thread and at every thread OpenMP gets (the box's share of cores); the
     number of solves shrinks so that the whole leg stays near budget_s."""
     from oracle import c_oracle
@@ -184,7 +184,7 @@ def cpu_baseline(batch, budget_s=25.0):
         t0 = time.perf_counter()
         _x, it, st, _rel = c_oracle.pcg(*args)          # warm-up
         first = time.perf_counter() - t0
-        reps = int(max(1, min(5, (budget_s / 2 - first) // max(first, 1e-3))))
+        reps = int(max(1, min(21, (budget_s / 2 - first) // max(first, 1e-3))))
         ts = []
         for _ in range(reps):
             t0 = time.perf_counter()
